@@ -1,0 +1,266 @@
+"""Plain fp64 CPU oracle for paged KV append + PagedAttention forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+path (``paged_kv_cache_append_amd/csrc``) and imports nothing from it.
+
+It writes out the plain definition of what the op computes, slowly and
+visibly:
+
+1. append: every new token's K/V row is stored at its derived slot;
+2. gather: each sequence's K/V are collected from the block pool via its
+   block-table row, up-cast to fp64;
+3. scores: the full ``[q_len, kv_len]`` score matrix per query head;
+4. softcap, then the causal / local-window mask as exclusion;
+5. softmax over the admitted keys (max-subtracted) and ``P @ V``.
+
+Sources (page title, section):
+
+* PagedAttention -- CUDA Design Document, §4.3-§4.8 (contract, positions
+  ``past_seqlens[b] + j``), §5.1 (derived write slot), §4.5 and §9 (window of W
+  positions including the current one), §8.5 implementation note (softcap
+  ``softcap * tanh(qk * scale / softcap)``; window ``[kv_len - W, kv_len)``),
+  §12.6 (default scale ``1/sqrt(head_size)``), §18.2 (tokens past
+  ``cumulative_sequence_length[batch_size]`` own nothing).
+* Design: WebGPU PagedAttention, §4.1 (per-batch causal length
+  ``past + q_idx + 1``, GQA grouping ``n_reps = num_heads / kv_num_heads``) and
+  §7 (scatter before attention).
+* GroupQueryAttention CPU Implementation Notes, "Naive Path" (QK GEMM, then
+  masking/softcap/softmax, then SV GEMM, with the full score matrix).
+
+Readings where the pages are silent (each also listed in the design notes):
+
+* q head ``h`` reads kv head ``h // (num_heads // kv_num_heads)``.
+* softcap is applied to the scaled score first; masked keys are then
+  excluded (they never enter the softmax).
+* RoPE (formula not printed on the pages): rotate-half pairs ``(i, i + r/2)``
+  when not interleaved, ``(2i, 2i+1)`` when interleaved, angle index ``i``,
+  ``x' = x*c - y*s``, ``y' = y*c + x*s``; channels ``>= r`` pass through.
+  The rotated K that is stored in the fp16 pool is ``fp16(fp32(x*c - y*s))``
+  (both products of fp16 numbers are exact in fp32; one fp32 rounding of the
+  exact result, then one fp16 rounding).  The direction of rotation is
+  parity unpinned: the pages print no formula, the tests only pin
+  self-consistency properties.
+* A query row with no admitted key (impossible with causal + W >= 1) is 0.
+* Output rows of tokens owned by no sequence are 0.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# a1 / a2: token -> (sequence, position) -> slot
+# PagedAttention -- CUDA Design Document, §5.1 (derived write slot) and §18.2.
+# ---------------------------------------------------------------------------
+
+def locate_token(cum: np.ndarray, t: int):
+    """Return ``(b, j)`` for packed token ``t``: the sequence ``b`` with
+    ``cum[b] <= t < cum[b+1]`` and its offset ``j = t - cum[b]``; ``None`` when
+    ``t >= cum[batch_size]`` (the token belongs to no sequence)."""
+    B = len(cum) - 1
+    for b in range(B):                       # plain scan, no search trick
+        if int(cum[b]) <= t < int(cum[b + 1]):
+            return b, t - int(cum[b])
+    return None
+
+
+def token_position(past: np.ndarray, b: int, j: int) -> int:
+    """Position of the j-th new token of sequence b: ``past[b] + j``
+    (PagedAttention -- CUDA Design Document, §4.8)."""
+    return int(past[b]) + j
+
+
+def derived_slot(block_table: np.ndarray, b: int, pos: int, block_size: int):
+    """``(physical block, offset)`` holding position ``pos`` of sequence ``b``:
+    ``block_table[b, pos // block_size]`` and ``pos % block_size``
+    (PagedAttention -- CUDA Design Document, §5.1)."""
+    return int(block_table[b, pos // block_size]), pos % block_size
+
+
+# ---------------------------------------------------------------------------
+# a3: rotary embedding (formula not printed on the pages -- see header)
+# ---------------------------------------------------------------------------
+
+def _rotary_pairs(rotary_dim: int, interleaved: bool):
+    """List of ``(first, second, angle index)`` channel pairs."""
+    half = rotary_dim // 2
+    if interleaved:
+        return [(2 * i, 2 * i + 1, i) for i in range(half)]
+    return [(i, i + half, i) for i in range(half)]
+
+
+def rope_key_fp16(x16: np.ndarray, pos: int, cos16: np.ndarray, sin16: np.ndarray,
+                  interleaved: bool) -> np.ndarray:
+    """Rotate one fp16 head row ``x16 [D]`` at ``pos`` and round it the way it
+    is stored in the fp16 pool: exact products, one fp32 rounding of their
+    difference, one fp16 rounding."""
+    rotary_dim = 2 * cos16.shape[1]
+    out = x16.copy()
+    for a, b, i in _rotary_pairs(rotary_dim, interleaved):
+        x = float(x16[a])
+        y = float(x16[b])
+        c = float(cos16[pos, i])
+        s = float(sin16[pos, i])
+        # products of two fp16 values are exact in fp64; the fp64 difference
+        # rounded to fp32 equals the fp32-rounded exact difference (53 >= 2*24+2).
+        first = np.float32(x * c - y * s)
+        second = np.float32(y * c + x * s)
+        out[a] = np.float16(first)
+        out[b] = np.float16(second)
+    return out
+
+
+def rope_query_fp64(x: np.ndarray, pos: int, cos: np.ndarray, sin: np.ndarray,
+                    interleaved: bool) -> np.ndarray:
+    """Rotate one head row in fp64 with no rounding (used for queries, which
+    are never stored)."""
+    rotary_dim = 2 * cos.shape[1]
+    out = np.array(x, dtype=np.float64, copy=True)
+    for a, b, i in _rotary_pairs(rotary_dim, interleaved):
+        c = float(cos[pos, i])
+        s = float(sin[pos, i])
+        out[a] = float(x[a]) * c - float(x[b]) * s
+        out[b] = float(x[b]) * c + float(x[a]) * s
+    return out
+
+
+# ---------------------------------------------------------------------------
+# a4: KV append (scatter new tokens into the pool, in place semantics)
+# Design: WebGPU PagedAttention §7 (scatter before attention);
+# PagedAttention -- CUDA Design Document §4.4 (cache outputs alias inputs).
+# ---------------------------------------------------------------------------
+
+def append_kv(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
+              value: np.ndarray, cum: np.ndarray, past: np.ndarray,
+              block_table: np.ndarray, *, kv_num_heads: int, head_size: int,
+              cos_cache: Optional[np.ndarray] = None, sin_cache: Optional[np.ndarray] = None,
+              rotary_interleaved: bool = False):
+    """Return new ``(key_cache, value_cache)`` copies with every new token's
+    K (rotated if a rotary table is given) and V stored at its derived slot.
+    Slots that no token maps to are left byte-identical."""
+    kc = key_cache.copy()
+    vc = value_cache.copy()
+    block_size = kc.shape[1]
+    Hkv, D = kv_num_heads, head_size
+    T = key.shape[0]
+    for t in range(T):
+        owner = locate_token(cum, t)
+        if owner is None:
+            continue
+        b, j = owner
+        pos = token_position(past, b, j)
+        blk, off = derived_slot(block_table, b, pos, block_size)
+        for h in range(Hkv):
+            krow = key[t, h * D:(h + 1) * D]
+            if cos_cache is not None:
+                krow = rope_key_fp16(krow, pos, cos_cache, sin_cache, rotary_interleaved)
+            kc[blk, off, h, :] = krow
+            vc[blk, off, h, :] = value[t, h * D:(h + 1) * D]
+    return kc, vc
+
+
+# ---------------------------------------------------------------------------
+# a5 / a7: attention over the paged context
+# ---------------------------------------------------------------------------
+
+def gather_sequence(cache: np.ndarray, block_table: np.ndarray, b: int, kv_len: int) -> np.ndarray:
+    """fp64 ``[kv_len, Hkv, D]``: position ``tau`` of sequence ``b`` read from
+    block ``block_table[b, tau // bs]``, offset ``tau % bs``."""
+    bs = cache.shape[1]
+    out = np.empty((kv_len, cache.shape[2], cache.shape[3]), np.float64)
+    for tau in range(kv_len):
+        blk, off = derived_slot(block_table, b, tau, bs)
+        out[tau] = cache[blk, off]
+    return out
+
+
+def effective_scale(scale: float, head_size: int) -> float:
+    """``scale == 0`` selects ``1/sqrt(head_size)`` (PagedAttention -- CUDA
+    Design Document, §12.6)."""
+    return float(scale) if scale != 0.0 else 1.0 / math.sqrt(head_size)
+
+
+def admitted(tau: np.ndarray, pos: int, local_window_size: int) -> np.ndarray:
+    """Keys a query at ``pos`` may attend: ``tau <= pos`` (causal, bottom-right
+    aligned) and, with a window ``W >= 1``, ``tau >= pos - W + 1`` (W positions
+    including the current one)."""
+    ok = tau <= pos
+    if local_window_size >= 1:
+        ok &= tau >= pos - local_window_size + 1
+    return ok
+
+
+def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
+            cum: np.ndarray, past: np.ndarray, block_table: np.ndarray, *,
+            num_heads: int, kv_num_heads: int, head_size: int, scale: float = 0.0,
+            softcap: float = 0.0, local_window_size: int = -1,
+            cos_cache: Optional[np.ndarray] = None, sin_cache: Optional[np.ndarray] = None,
+            rotary_interleaved: bool = False, rows: Optional[Iterable[int]] = None,
+            return_probs: bool = False):
+    """Attention output in fp64.
+
+    ``key_cache``/``value_cache`` must already hold the new tokens (run
+    :func:`append_kv` first).  Returns ``[T, H*D]`` for all tokens, or
+    ``[len(rows), H*D]`` in the given order when ``rows`` is set.  With
+    ``return_probs`` also returns ``{(t, h): probabilities over keys}``."""
+    T = query.shape[0]
+    H, Hkv, D = num_heads, kv_num_heads, head_size
+    g = H // Hkv
+    sigma = effective_scale(scale, D)
+    row_list = list(range(T)) if rows is None else [int(r) for r in rows]
+    out = np.zeros((len(row_list), H * D), np.float64)
+    probs = {}
+
+    # group the requested rows by owning sequence so each context is gathered once
+    by_seq = {}
+    for n, t in enumerate(row_list):
+        owner = locate_token(cum, t)
+        if owner is None:
+            continue                          # owned by no sequence: row stays 0
+        b, j = owner
+        by_seq.setdefault(b, []).append((n, t, j))
+
+    for b, items in by_seq.items():
+        q_len = int(cum[b + 1]) - int(cum[b])
+        kv_len = int(past[b]) + q_len
+        K = gather_sequence(key_cache, block_table, b, kv_len)
+        V = gather_sequence(value_cache, block_table, b, kv_len)
+        tau = np.arange(kv_len)
+        n_idx = [n for n, _, _ in items]
+        positions = [token_position(past, b, j) for _, _, j in items]
+        # queries [n_rows, H, D] in fp64, rotated at their position if asked
+        Q = np.empty((len(items), H, D), np.float64)
+        for r, (_, t, _) in enumerate(items):
+            qrow = query[t].astype(np.float64).reshape(H, D)
+            if cos_cache is not None:
+                for h in range(H):
+                    qrow[h] = rope_query_fp64(qrow[h], positions[r], cos_cache, sin_cache,
+                                              rotary_interleaved)
+            Q[r] = qrow
+        mask = np.stack([admitted(tau, p, local_window_size) for p in positions])
+        for h in range(H):
+            kvh = h // g
+            S = sigma * (Q[:, h, :] @ K[:, kvh, :].T)          # full score matrix
+            if softcap > 0.0:
+                S = softcap * np.tanh(S / softcap)
+            S = np.where(mask, S, -np.inf)                     # exclusion
+            O = np.zeros((len(items), D), np.float64)
+            for r in range(len(items)):
+                if not mask[r].any():
+                    continue                                   # fully masked -> 0
+                m = S[r].max()
+                e = np.exp(S[r] - m)
+                p = e / e.sum()
+                assert abs(p.sum() - 1.0) < 1e-12
+                O[r] = p @ V[:, kvh, :]
+                if return_probs:
+                    probs[(items[r][1], h)] = p
+            out[n_idx, h * D:(h + 1) * D] = O
+    if return_probs:
+        return out, probs
+    return out

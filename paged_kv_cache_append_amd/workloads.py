@@ -1,0 +1,329 @@
+"""Seeded synthetic inputs for paged KV append + PagedAttention forward.
+
+This module only *draws* inputs: lengths, block tables, new Q/K/V tokens,
+block-pool contents and rotary tables.  It holds none of the attention
+arithmetic, so that both the fp64 oracle (``oracle/``) and the HIP path can
+consume the very same host arrays without sharing any code of the method.
+
+Input contract being populated (PagedAttention -- CUDA Design Document, §4 and
+§4.3; Design: WebGPU PagedAttention, §3.3 "GenAI runtime contract"):
+
+* ``query``  fp16 ``[token_count, num_heads * head_size]`` packed over requests
+* ``key``/``value`` fp16 ``[token_count, kv_num_heads * head_size]``
+* ``key_cache``/``value_cache`` fp16 ``[num_blocks, block_size, kv_num_heads, head_size]``
+* ``block_table`` int32 ``[batch_size, max_blocks_per_seq]`` (entry i holds the
+  block of positions ``[i*block_size, (i+1)*block_size)``; padding is -1)
+* ``cumulative_sequence_lengths`` int32 ``[batch_size + 1]``
+* ``past_sequence_lengths`` int32 ``[batch_size]``
+* ``cos_cache``/``sin_cache`` fp16 ``[rows, rotary_dim / 2]`` when rotary is on.
+
+Pool contents are generated per physical block from a counter-keyed numpy
+generator ``default_rng([seed, kind, block])`` so any subset of blocks can be
+re-drawn without materialising the whole pool (the 256-sequence decode pool is
+about 10 GB).
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+
+KIND_K = 0
+KIND_V = 1
+
+
+@dataclass
+class Workload:
+    """One batch of synthetic inputs for an append + forward step."""
+
+    name: str
+    seed: int
+    num_heads: int
+    kv_num_heads: int
+    head_size: int
+    block_size: int
+    scale: float
+    softcap: float
+    local_window_size: int
+    do_rotary: int
+    rotary_interleaved: int
+    cum: np.ndarray            # int32 [B+1]
+    past: np.ndarray           # int32 [B]
+    block_table: np.ndarray    # int32 [B, max_blocks_per_seq]
+    num_blocks: int
+    query: np.ndarray          # fp16 [T, H*D]
+    key: np.ndarray            # fp16 [T, Hkv*D]
+    value: np.ndarray          # fp16 [T, Hkv*D]
+    cos_cache: Optional[np.ndarray] = None   # fp16 [rows, rot/2]
+    sin_cache: Optional[np.ndarray] = None
+    kv_sigma: float = 1.0
+    # blocks whose contents are NaN before the append ("poisoned" pool):
+    # every slot that the runtime has not filled yet.
+    poison: bool = False
+    description: str = ""
+    extra: dict = field(default_factory=dict)
+
+    # ---- shape helpers -------------------------------------------------
+    @property
+    def batch_size(self) -> int:
+        return int(self.past.shape[0])
+
+    @property
+    def token_count(self) -> int:
+        return int(self.query.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def q_lens(self) -> np.ndarray:
+        return np.diff(self.cum.astype(np.int64))
+
+    @property
+    def rotary_dim(self) -> int:
+        return 0 if self.cos_cache is None else 2 * int(self.cos_cache.shape[1])
+
+    @property
+    def rotary_rows(self) -> int:
+        return 0 if self.cos_cache is None else int(self.cos_cache.shape[0])
+
+    def pool_shape(self):
+        return (self.num_blocks, self.block_size, self.kv_num_heads, self.head_size)
+
+    # ---- pool contents -------------------------------------------------
+    def pool_blocks(self, kind: int, ids: Sequence[int]) -> np.ndarray:
+        """fp16 contents of physical blocks ``ids`` of the K (kind 0) or V
+        (kind 1) pool, before the append."""
+        ids = [int(i) for i in ids]
+        out = np.empty((len(ids), self.block_size, self.kv_num_heads, self.head_size),
+                       np.float16)
+        for n, p in enumerate(ids):
+            out[n] = _draw_block(self.seed, kind, p, out.shape[1:], self.kv_sigma)
+        if self.poison:
+            filled = self._filled_tokens()
+            for n, p in enumerate(ids):
+                f = filled.get(p, 0)
+                out[n, f:] = np.float16(np.nan)
+        return out
+
+    def full_pool(self, kind: int, threads: Optional[int] = None,
+                  chunk: int = 512) -> np.ndarray:
+        """The whole pool of one kind, drawn block by block (threaded)."""
+        pool = np.empty(self.pool_shape(), np.float16)
+        fill_pool_chunks(self, kind, pool, threads=threads, chunk=chunk)
+        return pool
+
+    def _filled_tokens(self) -> dict:
+        """Physical block -> number of leading slots that hold cached tokens
+        (the runtime's bookkeeping of what it has written so far)."""
+        if "_filled" in self.extra:
+            return self.extra["_filled"]
+        filled = {}
+        bs = self.block_size
+        for b in range(self.batch_size):
+            n_past = int(self.past[b])
+            for i in range(self.max_blocks_per_seq):
+                blk = int(self.block_table[b, i])
+                if blk < 0:
+                    continue
+                n = min(max(n_past - i * bs, 0), bs)
+                filled[blk] = max(filled.get(blk, 0), n)
+        self.extra["_filled"] = filled
+        return filled
+
+
+def _draw_block(seed: int, kind: int, p: int, shape, sigma: float) -> np.ndarray:
+    rng = np.random.default_rng([seed, kind, p])
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return x.astype(np.float16)
+
+
+def fill_pool_chunks(w: Workload, kind: int, out: np.ndarray,
+                     threads: Optional[int] = None, chunk: int = 512,
+                     sink=None) -> None:
+    """Draw every block of one pool kind into ``out`` (host array).  If
+    ``sink`` is given it is called as ``sink(start, array)`` per chunk (used to
+    stream the pool to device memory without holding it all on the host)."""
+    nb = w.num_blocks
+    threads = threads or min(16, os.cpu_count() or 1)
+
+    def work(start):
+        stop = min(nb, start + chunk)
+        arr = w.pool_blocks(kind, range(start, stop))
+        return start, arr
+
+    with ThreadPoolExecutor(threads) as ex:
+        for start, arr in ex.map(work, range(0, nb, chunk)):
+            if out is not None:
+                out[start:start + arr.shape[0]] = arr
+            if sink is not None:
+                sink(start, arr)
+
+
+def rope_tables(rows: int, rotary_dim: int, base: float = 10000.0):
+    """fp16 cos/sin tables ``[rows, rotary_dim/2]`` for the standard inverse
+    frequency ``base**(-2i/rotary_dim)``, evaluated in fp64 then rounded."""
+    half = rotary_dim // 2
+    inv = base ** (-(2.0 * np.arange(half, dtype=np.float64)) / rotary_dim)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float16), np.sin(ang).astype(np.float16)
+
+
+def build_case(name: str, seed: int, *, q_lens: Sequence[int], past: Sequence[int],
+               num_heads: int, kv_num_heads: int, head_size: int, block_size: int,
+               scale: float = 0.0, softcap: float = 0.0, local_window_size: int = -1,
+               do_rotary: int = 0, rotary_interleaved: int = 0, rotary_dim: int = 0,
+               rotary_base: float = 10000.0, q_sigma: float = 1.0, kv_sigma: float = 1.0,
+               num_blocks: Optional[int] = None, pool_slack: float = 1.1,
+               extra_blocks_per_seq: int = 0, rng: Optional[np.random.Generator] = None,
+               shuffle: bool = True, poison: bool = False, description: str = "",
+               extra_tokens: int = 0) -> Workload:
+    """Assemble a workload from explicit per-sequence lengths.
+
+    Block allocation mimics a serving runtime: each sequence gets
+    ``ceil((past + q_len) / block_size)`` physical blocks taken in batch order
+    from a seeded permutation of the pool; unused table entries are -1.
+    ``extra_tokens`` appends rows to the packed Q/K/V beyond the last
+    sequence (tokens owned by no sequence)."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    past = np.asarray(past, dtype=np.int64)
+    B = len(q_lens)
+    assert len(past) == B
+    kv_lens = past + q_lens
+    nblk = (kv_lens + block_size - 1) // block_size
+    used = int(nblk.sum())
+    if num_blocks is None:
+        num_blocks = max(1, int(math.ceil(pool_slack * used)))
+    assert num_blocks >= used, "pool too small"
+    maxblk = max(1, int(nblk.max()) + extra_blocks_per_seq) if B else 1
+    perm = rng.permutation(num_blocks) if shuffle else np.arange(num_blocks)
+    table = np.full((B, maxblk), -1, np.int32)
+    o = 0
+    for b in range(B):
+        n = int(nblk[b])
+        table[b, :n] = perm[o:o + n]
+        o += n
+    cum = np.zeros(B + 1, np.int32)
+    cum[1:] = np.cumsum(q_lens)
+    T = int(cum[-1]) + extra_tokens
+    H, Hkv, D = num_heads, kv_num_heads, head_size
+    q = rng.standard_normal((T, H * D), dtype=np.float32)
+    if q_sigma != 1.0:
+        q *= np.float32(q_sigma)
+    k = rng.standard_normal((T, Hkv * D), dtype=np.float32) * np.float32(kv_sigma)
+    v = rng.standard_normal((T, Hkv * D), dtype=np.float32) * np.float32(kv_sigma)
+    cos = sin = None
+    if do_rotary:
+        rd = rotary_dim or D
+        rows = maxblk * block_size
+        cos, sin = rope_tables(rows, rd, rotary_base)
+    return Workload(name=name, seed=seed, num_heads=H, kv_num_heads=Hkv, head_size=D,
+                    block_size=block_size, scale=float(scale), softcap=float(softcap),
+                    local_window_size=int(local_window_size), do_rotary=int(do_rotary),
+                    rotary_interleaved=int(rotary_interleaved), cum=cum,
+                    past=past.astype(np.int32), block_table=table, num_blocks=int(num_blocks),
+                    query=q.astype(np.float16), key=k.astype(np.float16),
+                    value=v.astype(np.float16), cos_cache=cos, sin_cache=sin,
+                    kv_sigma=float(kv_sigma), poison=poison, description=description)
+
+
+# ---------------------------------------------------------------------------
+# The five benchmark workloads (seed 1000 + index, draws in a fixed order:
+# past lengths, block permutation, Q, K, V; pool per block).
+# ---------------------------------------------------------------------------
+
+CONFIG_NAMES = (
+    "tiny_decode",
+    "llama3_8b_mixed",
+    "decode_heavy_256",
+    "gemma2_prefill_window",
+    "long_context_decode_rope",
+)
+
+
+def make_workload(name: str, poison: bool = False) -> Workload:
+    idx = CONFIG_NAMES.index(name)
+    seed = 1000 + idx
+    rng = np.random.default_rng(seed)
+    if name == "tiny_decode":
+        # 2 sequences, one new token each on 37 / 50 cached tokens; pool of 16
+        # blocks whose table rows are a seeded permutation (all 8 entries valid).
+        w = build_case(name, seed, q_lens=[1, 1], past=[37, 50], num_heads=4,
+                       kv_num_heads=2, head_size=64, block_size=16, scale=0.125,
+                       num_blocks=16, rng=rng, shuffle=True, poison=poison,
+                       description="2 seqs x 1 token, past 37/50, H=4 Hkv=2 D=64 bs=16")
+        perm = np.random.default_rng([seed, 7]).permutation(16).astype(np.int32)
+        w.block_table = perm.reshape(2, 8)
+        w.extra.pop("_filled", None)
+        return w
+    if name == "llama3_8b_mixed":
+        past_dec = rng.integers(128, 4096, size=64, endpoint=True)
+        q_lens = [1] * 64 + [512, 512]
+        past = list(past_dec) + [0, 1024]
+        return build_case(name, seed, q_lens=q_lens, past=past, num_heads=32, kv_num_heads=8,
+                          head_size=128, block_size=16, scale=1.0 / math.sqrt(128), rng=rng,
+                          poison=poison,
+                          description="64 decode seqs (past U[128,4096]) + 2x512-token "
+                                      "prefill chunks (past 0, 1024); H=32 Hkv=8 D=128 bs=16")
+    if name == "decode_heavy_256":
+        past = rng.integers(1024, 16384, size=256, endpoint=True)
+        return build_case(name, seed, q_lens=[1] * 256, past=past, num_heads=32,
+                          kv_num_heads=8, head_size=128, block_size=32,
+                          scale=1.0 / math.sqrt(128), kv_sigma=0.5, rng=rng, poison=poison,
+                          description="256 decode seqs, past U[1024,16384]; H=32 Hkv=8 "
+                                      "D=128 bs=32; K/V ~ N(0, 0.5)")
+    if name == "gemma2_prefill_window":
+        return build_case(name, seed, q_lens=[2048] * 8, past=[2048] * 8, num_heads=16,
+                          kv_num_heads=8, head_size=256, block_size=16, scale=1.0 / 16.0,
+                          softcap=50.0, local_window_size=4096, rng=rng, poison=poison,
+                          description="8 seqs x 2048 new tokens on 2048 cached; H=16 Hkv=8 "
+                                      "D=256 bs=16; window 4096, softcap 50")
+    if name == "long_context_decode_rope":
+        past_small = rng.integers(512, 8192, size=7, endpoint=True)
+        past = [131072] + list(past_small)
+        return build_case(name, seed, q_lens=[1] * 8, past=past, num_heads=64, kv_num_heads=8,
+                          head_size=64, block_size=64, scale=0.125, do_rotary=1,
+                          rotary_interleaved=0, rotary_dim=64, rng=rng, poison=poison,
+                          description="1 seq on 131072 cached + 7 on U[512,8192]; H=64 "
+                                      "Hkv=8 D=64 bs=64; rotary base 10000")
+    raise KeyError(name)
+
+
+def scaled_down(name: str, poison: bool = False) -> Workload:
+    """A small stand-in with the same head layout, block size and features as
+    benchmark workload ``name`` (lengths cut so the oracle finishes in
+    seconds while still spanning several tiles and a ragged tail)."""
+    idx = CONFIG_NAMES.index(name)
+    seed = 2000 + idx
+    rng = np.random.default_rng(seed)
+    if name == "tiny_decode":
+        return make_workload(name, poison)
+    if name == "llama3_8b_mixed":
+        past = list(rng.integers(1, 700, size=6, endpoint=True)) + [0, 75]
+        return build_case(name + "_small", seed, q_lens=[1] * 6 + [130, 77], past=past,
+                          num_heads=32, kv_num_heads=8, head_size=128, block_size=16,
+                          scale=1.0 / math.sqrt(128), rng=rng, poison=poison)
+    if name == "decode_heavy_256":
+        past = rng.integers(1, 1500, size=12, endpoint=True)
+        return build_case(name + "_small", seed, q_lens=[1] * 12, past=past, num_heads=32,
+                          kv_num_heads=8, head_size=128, block_size=32,
+                          scale=1.0 / math.sqrt(128), kv_sigma=0.5, rng=rng, poison=poison)
+    if name == "gemma2_prefill_window":
+        return build_case(name + "_small", seed, q_lens=[150, 67], past=[200, 0], num_heads=16,
+                          kv_num_heads=8, head_size=256, block_size=16, scale=1.0 / 16.0,
+                          softcap=50.0, local_window_size=96, rng=rng, poison=poison)
+    if name == "long_context_decode_rope":
+        past = [3000] + list(rng.integers(10, 400, size=3, endpoint=True))
+        return build_case(name + "_small", seed, q_lens=[1] * 4, past=past, num_heads=64,
+                          kv_num_heads=8, head_size=64, block_size=64, scale=0.125,
+                          do_rotary=1, rotary_interleaved=0, rotary_dim=64, rng=rng,
+                          poison=poison)
+    raise KeyError(name)

@@ -1,0 +1,533 @@
+"""Pins for the fp64 oracle, checked against things other than itself:
+a hand-worked example, torch's own fp64 attention on contiguous (non-paged)
+tensors, closed forms and invariants.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_append_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# helpers: build a paged case FROM contiguous per-sequence tensors
+# (the inverse of the oracle's gather, written independently)
+# ---------------------------------------------------------------------------
+
+def paged_from_contiguous(rng, q_lens, past, H, Hkv, D, bs, extra_blocks=3, kv_sigma=1.0):
+    """Draw contiguous K/V per sequence, scatter the cached part into a pool
+    through a shuffled table, and return the new tokens as packed rows."""
+    B = len(q_lens)
+    kv_lens = [p + q for p, q in zip(past, q_lens)]
+    nblk = [(L + bs - 1) // bs for L in kv_lens]
+    num_blocks = sum(nblk) + extra_blocks
+    perm = rng.permutation(num_blocks)
+    maxblk = max(nblk) if B else 1
+    table = np.full((B, max(1, maxblk)), -1, np.int32)
+    o = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[o:o + nblk[b]]
+        o += nblk[b]
+    # pool starts as garbage that must never be read
+    kc = (rng.standard_normal((num_blocks, bs, Hkv, D)) * 100).astype(np.float16)
+    vc = (rng.standard_normal((num_blocks, bs, Hkv, D)) * 100).astype(np.float16)
+    Kc, Vc, Qs = [], [], []
+    for b in range(B):
+        K = (rng.standard_normal((kv_lens[b], Hkv, D)) * kv_sigma).astype(np.float16)
+        V = (rng.standard_normal((kv_lens[b], Hkv, D)) * kv_sigma).astype(np.float16)
+        Q = rng.standard_normal((q_lens[b], H, D)).astype(np.float16)
+        Kc.append(K); Vc.append(V); Qs.append(Q)
+        for i in range(nblk[b]):                   # cached part, block by block
+            lo, hi = i * bs, min((i + 1) * bs, past[b])
+            if hi > lo:
+                kc[table[b, i], :hi - lo] = K[lo:hi]
+                vc[table[b, i], :hi - lo] = V[lo:hi]
+    cum = np.zeros(B + 1, np.int32)
+    cum[1:] = np.cumsum(q_lens)
+    key = np.concatenate([Kc[b][past[b]:].reshape(q_lens[b], Hkv * D) for b in range(B)]) \
+        if cum[-1] else np.zeros((0, Hkv * D), np.float16)
+    value = np.concatenate([Vc[b][past[b]:].reshape(q_lens[b], Hkv * D) for b in range(B)]) \
+        if cum[-1] else np.zeros((0, Hkv * D), np.float16)
+    query = np.concatenate([Qs[b].reshape(q_lens[b], H * D) for b in range(B)]) \
+        if cum[-1] else np.zeros((0, H * D), np.float16)
+    return dict(kc=kc, vc=vc, table=table, cum=cum, past=np.asarray(past, np.int32),
+                key=key, value=value, query=query, K=Kc, V=Vc, Q=Qs)
+
+
+def run_oracle(c, H, Hkv, D, **kw):
+    kc, vc = oracle.append_kv(c["kc"], c["vc"], c["key"], c["value"], c["cum"], c["past"],
+                              c["table"], kv_num_heads=Hkv, head_size=D)
+    return oracle.forward(c["query"], kc, vc, c["cum"], c["past"], c["table"], num_heads=H,
+                          kv_num_heads=Hkv, head_size=D, **kw)
+
+
+def torch_reference(c, H, Hkv, D, scale, window=-1):
+    """torch fp64 scaled_dot_product_attention on contiguous K/V, with the
+    library's own causal mask (tril) shifted by the cached length."""
+    g = H // Hkv
+    outs = []
+    for b in range(len(c["Q"])):
+        q_len = c["Q"][b].shape[0]
+        if q_len == 0:
+            continue
+        past = int(c["past"][b])
+        kv_len = past + q_len
+        q = torch.from_numpy(c["Q"][b].astype(np.float64)).permute(1, 0, 2)[None]
+        k = torch.from_numpy(c["K"][b].astype(np.float64)).permute(1, 0, 2)
+        v = torch.from_numpy(c["V"][b].astype(np.float64)).permute(1, 0, 2)
+        k = k.repeat_interleave(g, dim=0)[None]
+        v = v.repeat_interleave(g, dim=0)[None]
+        mask = torch.ones(q_len, kv_len, dtype=torch.bool).tril(diagonal=past)
+        if window >= 1:
+            mask &= ~torch.ones(q_len, kv_len, dtype=torch.bool).tril(diagonal=past - window)
+        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask,
+                                                             scale=scale)
+        outs.append(o[0].permute(1, 0, 2).reshape(q_len, H * D).numpy())
+    return np.concatenate(outs)
+
+
+# ---------------------------------------------------------------------------
+# slot derivation: hand-worked example
+# ---------------------------------------------------------------------------
+
+def test_slot_derivation_golden():
+    g = json.load(open(os.path.join(GOLDEN, "slot_derivation.json")))
+    cum = np.array(g["cum"], np.int32)
+    past = np.array(g["past"], np.int32)
+    table = np.array(g["block_table"], np.int32)
+    bs = g["block_size"]
+    for e in g["expected"]:
+        owner = oracle.locate_token(cum, e["t"])
+        if e["b"] is None:
+            assert owner is None
+            continue
+        b, j = owner
+        pos = oracle.token_position(past, b, j)
+        blk, off = oracle.derived_slot(table, b, pos, bs)
+        assert (b, j, pos, blk, off, blk * bs + off) == \
+            (e["b"], e["j"], e["pos"], e["block"], e["offset"], e["slot"])
+
+
+def test_append_writes_exactly_the_golden_slots():
+    g = json.load(open(os.path.join(GOLDEN, "slot_derivation.json")))
+    bs, Hkv, D = g["block_size"], 2, 8
+    cum = np.array(g["cum"], np.int32)
+    past = np.array(g["past"], np.int32)
+    table = np.array(g["block_table"], np.int32)
+    T = g["token_count"]
+    rng = np.random.default_rng(5)
+    kc = rng.standard_normal((8, bs, Hkv, D)).astype(np.float16)
+    vc = rng.standard_normal((8, bs, Hkv, D)).astype(np.float16)
+    key = rng.standard_normal((T, Hkv * D)).astype(np.float16)
+    val = rng.standard_normal((T, Hkv * D)).astype(np.float16)
+    nk, nv = oracle.append_kv(kc, vc, key, val, cum, past, table, kv_num_heads=Hkv, head_size=D)
+    expect_k = kc.reshape(-1, Hkv, D).copy()
+    expect_v = vc.reshape(-1, Hkv, D).copy()
+    for e in g["expected"]:
+        if e["b"] is None:
+            continue
+        expect_k[e["slot"]] = key[e["t"]].reshape(Hkv, D)
+        expect_v[e["slot"]] = val[e["t"]].reshape(Hkv, D)
+    assert nk.reshape(-1, Hkv, D).tobytes() == expect_k.tobytes()
+    assert nv.reshape(-1, Hkv, D).tobytes() == expect_v.tobytes()
+
+
+# ---------------------------------------------------------------------------
+# paged oracle == torch fp64 attention on contiguous tensors
+# ---------------------------------------------------------------------------
+
+SWEEP = [
+    # q_lens, past, H, Hkv, D, bs, window
+    ([1, 1], [37, 50], 4, 2, 64, 16, -1),
+    ([1, 1, 1], [0, 15, 40], 8, 8, 16, 16, -1),          # MHA
+    ([1, 1], [16, 17], 8, 1, 8, 16, -1),                  # MQA
+    ([5, 17], [0, 0], 2, 1, 16, 16, -1),                  # fresh prefill
+    ([5, 2, 17], [1, 16, 40], 4, 2, 16, 32, -1),          # chunked prefill
+    ([17, 1, 0, 2], [15, 3, 9, 0], 4, 4, 8, 16, -1),      # ragged incl. q_len 0
+    ([9, 1], [20, 33], 4, 2, 16, 16, 5),                  # window
+    ([6, 3], [0, 40], 2, 2, 8, 16, 2),
+    ([4], [10], 2, 1, 8, 16, 1000),                        # window >= context
+]
+
+
+@pytest.mark.parametrize("case", SWEEP)
+def test_oracle_matches_torch_contiguous(case):
+    q_lens, past, H, Hkv, D, bs, W = case
+    rng = np.random.default_rng(abs(hash(str(case))) % (2 ** 31))
+    c = paged_from_contiguous(rng, q_lens, past, H, Hkv, D, bs)
+    scale = 1.0 / math.sqrt(D)
+    got = run_oracle(c, H, Hkv, D, scale=0.0, local_window_size=W)   # 0 -> 1/sqrt(D)
+    ref = torch_reference(c, H, Hkv, D, scale, window=W)
+    assert got.shape == ref.shape
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_fresh_prefill_matches_torch_is_causal():
+    """past = 0 prefill against torch's built-in causal flag (no mask typed here)."""
+    rng = np.random.default_rng(11)
+    H, Hkv, D, bs = 4, 2, 16, 16
+    c = paged_from_contiguous(rng, [23], [0], H, Hkv, D, bs)
+    got = run_oracle(c, H, Hkv, D, scale=0.25)
+    q = torch.from_numpy(c["Q"][0].astype(np.float64)).permute(1, 0, 2)[None]
+    k = torch.from_numpy(c["K"][0].astype(np.float64)).permute(1, 0, 2).repeat_interleave(2, 0)[None]
+    v = torch.from_numpy(c["V"][0].astype(np.float64)).permute(1, 0, 2).repeat_interleave(2, 0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=0.25)
+    np.testing.assert_allclose(got, ref[0].permute(1, 0, 2).reshape(23, H * D).numpy(),
+                               rtol=0, atol=1e-12)
+
+
+def test_decode_matches_unmasked_torch():
+    """one new token attends every cached key: no mask at all."""
+    rng = np.random.default_rng(12)
+    H, Hkv, D, bs = 8, 2, 32, 16
+    c = paged_from_contiguous(rng, [1], [70], H, Hkv, D, bs)
+    got = run_oracle(c, H, Hkv, D, scale=0.0)
+    q = torch.from_numpy(c["Q"][0].astype(np.float64)).permute(1, 0, 2)[None]
+    k = torch.from_numpy(c["K"][0].astype(np.float64)).permute(1, 0, 2).repeat_interleave(4, 0)[None]
+    v = torch.from_numpy(c["V"][0].astype(np.float64)).permute(1, 0, 2).repeat_interleave(4, 0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+    np.testing.assert_allclose(got, ref[0].permute(1, 0, 2).reshape(1, H * D).numpy(),
+                               rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# invariants and special cases
+# ---------------------------------------------------------------------------
+
+def _small_case(seed=3, **kw):
+    args = dict(q_lens=[1, 4, 1, 7], past=[30, 0, 63, 12], num_heads=4, kv_num_heads=2,
+                head_size=16, block_size=16, scale=0.0)
+    args.update(kw)
+    return wl.build_case("t", seed, **args)
+
+
+def _oracle_on(w, kc=None, vc=None, table=None, **over):
+    table = w.block_table if table is None else table
+    kc = w.pool_blocks(0, range(w.num_blocks)) if kc is None else kc
+    vc = w.pool_blocks(1, range(w.num_blocks)) if vc is None else vc
+    rot = dict(cos_cache=w.cos_cache, sin_cache=w.sin_cache,
+               rotary_interleaved=bool(w.rotary_interleaved)) if w.do_rotary else {}
+    nk, nv = oracle.append_kv(kc, vc, w.key, w.value, w.cum, w.past, table,
+                              kv_num_heads=w.kv_num_heads, head_size=w.head_size, **rot)
+    args = dict(num_heads=w.num_heads, kv_num_heads=w.kv_num_heads, head_size=w.head_size,
+                scale=w.scale, softcap=w.softcap, local_window_size=w.local_window_size)
+    args.update(rot)
+    args.update(over)
+    return oracle.forward(w.query, nk, nv, w.cum, w.past, table, **args), nk, nv
+
+
+def test_physical_block_permutation_invariance():
+    w = _small_case()
+    out, _, _ = _oracle_on(w)
+    kc = w.pool_blocks(0, range(w.num_blocks))
+    vc = w.pool_blocks(1, range(w.num_blocks))
+    perm = np.random.default_rng(9).permutation(w.num_blocks)     # new home of block p
+    kc2 = np.empty_like(kc); vc2 = np.empty_like(vc)
+    kc2[perm] = kc; vc2[perm] = vc
+    table2 = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    out2, _, _ = _oracle_on(w, kc2, vc2, table2)
+    assert np.array_equal(out, out2)
+
+
+def test_single_visible_key_returns_v():
+    # first token of a past-0 prefill sees only itself
+    w = _small_case(q_lens=[5], past=[0])
+    out, _, _ = _oracle_on(w)
+    np.testing.assert_array_equal(out[0].reshape(4, 16)[::2], w.value[0].reshape(2, 16).astype(np.float64))
+    # window of 1: every token sees only itself
+    w = _small_case(local_window_size=1)
+    out, _, _ = _oracle_on(w)
+    g = w.num_heads // w.kv_num_heads
+    for t in range(w.token_count):
+        v = w.value[t].reshape(w.kv_num_heads, 1, w.head_size).astype(np.float64)
+        np.testing.assert_array_equal(out[t].reshape(w.kv_num_heads, g, w.head_size),
+                                      np.broadcast_to(v, (w.kv_num_heads, g, w.head_size)))
+
+
+def test_zero_query_gives_mean_of_admitted_values():
+    w = _small_case(local_window_size=6)
+    w.query[:] = 0
+    out, _, nv = _oracle_on(w)
+    b, j = 3, 4                                   # token cum[3] + 4, pos 12 + 4 = 16
+    t = int(w.cum[b]) + j
+    pos = int(w.past[b]) + j
+    vals = [nv[w.block_table[b, p // 16], p % 16].astype(np.float64) for p in range(pos - 5, pos + 1)]
+    mean = np.mean(vals, axis=0)                  # [Hkv, D]
+    np.testing.assert_allclose(out[t].reshape(2, 2, 16), np.repeat(mean[:, None], 2, 1),
+                               rtol=0, atol=1e-12)
+
+
+def test_constant_values_give_that_constant():
+    w = _small_case(softcap=3.0, local_window_size=4)
+    kc = w.pool_blocks(0, range(w.num_blocks))
+    vc = np.full_like(kc, np.float16(0.375))
+    w.value[:] = np.float16(0.375)
+    out, _, _ = _oracle_on(w, vc=vc)
+    np.testing.assert_allclose(out, 0.375, rtol=0, atol=1e-15)
+
+
+def test_two_key_closed_form_and_softcap():
+    """One head, D = 8: keys k0 = 0 (or k0 * e0), k1 = e0; q = e0; V rows e0, e1.
+    Scores are 0 and s, so the output is (1 - sigmoid(s), sigmoid(s)).
+    With a softcap c the second score becomes c * tanh(s / c); choosing
+    s = c * atanh(ln 3 / c) gives weights exactly 1/4, 3/4."""
+    def case(scale, softcap, k0=0.0):
+        D = 8
+        cum = np.array([0, 1], np.int32); past = np.array([1], np.int32)
+        table = np.array([[0]], np.int32)
+        kc = np.zeros((1, 16, 1, D), np.float16); vc = np.zeros_like(kc)
+        vc[0, 0, 0, 0] = 1.0                    # v0 = e0 (cached)
+        kc[0, 0, 0, 0] = k0                     # k0 = k0 * e0 (cached)
+        key = np.zeros((1, D), np.float16); key[0, 0] = 1.0
+        val = np.zeros((1, D), np.float16); val[0, 1] = 1.0
+        q = np.zeros((1, D), np.float16); q[0, 0] = 1.0
+        nk, nv = oracle.append_kv(kc, vc, key, val, cum, past, table, kv_num_heads=1, head_size=D)
+        return oracle.forward(q, nk, nv, cum, past, table, num_heads=1, kv_num_heads=1,
+                              head_size=D, scale=scale, softcap=softcap)[0]
+    o = case(1.0, 0.0)
+    sig = 1.0 / (1.0 + math.exp(-1.0))
+    np.testing.assert_allclose(o[:2], [1 - sig, sig], rtol=0, atol=1e-15)
+    c = 2.0
+    s = c * math.atanh(math.log(3.0) / c)
+    o = case(s, c)
+    np.testing.assert_allclose(o[:2], [0.25, 0.75], rtol=0, atol=1e-14)
+    o = case(s, 1e12)                            # huge cap == no cap
+    sig = 1.0 / (1.0 + math.exp(-s))
+    np.testing.assert_allclose(o[:2], [1 - sig, sig], rtol=0, atol=1e-12)
+    o = case(1000.0, 1.0, k0=0.5)                # scores 500, 1000: saturated cap -> uniform
+    np.testing.assert_allclose(o[:2], [0.5, 0.5], rtol=0, atol=1e-12)
+
+
+def test_window_at_least_context_is_no_window():
+    w = _small_case()
+    a, _, _ = _oracle_on(w, local_window_size=-1)
+    b, _, _ = _oracle_on(w, local_window_size=int(w.past.max() + 8))
+    assert np.array_equal(a, b)
+
+
+def test_window_is_sharp():
+    """W = 2 differs from W = 3 on a token with >= 3 visible keys, and equals
+    the average of exactly two values when the query is zero."""
+    w = _small_case(local_window_size=2)
+    w.query[:] = 0
+    out, _, nv = _oracle_on(w)
+    t = int(w.cum[1]) + 3                         # seq 1, j = 3, pos 3: keys {2, 3}
+    vals = [nv[w.block_table[1, p // 16], p % 16].astype(np.float64) for p in (2, 3)]
+    np.testing.assert_allclose(out[t].reshape(2, 2, 16),
+                               np.repeat(np.mean(vals, 0)[:, None], 2, 1), rtol=0, atol=1e-15)
+
+
+def test_gqa_equals_mha_on_expanded_cache():
+    w = _small_case(num_heads=4, kv_num_heads=2)
+    out, nk, nv = _oracle_on(w)
+    g = 2
+    nk2 = np.repeat(nk, g, axis=2); nv2 = np.repeat(nv, g, axis=2)
+    o2 = oracle.forward(w.query, nk2, nv2, w.cum, w.past, w.block_table, num_heads=4,
+                        kv_num_heads=4, head_size=16, scale=w.scale)
+    np.testing.assert_array_equal(out, o2)
+
+
+def test_chunked_prefill_equals_one_shot_and_decode():
+    """Same positions computed as one 9-token prefill, as chunks 4 + 5, and as
+    9 single-token decode steps give the same rows."""
+    rng = np.random.default_rng(21)
+    H, Hkv, D, bs = 4, 2, 16, 16
+    past0, n = 11, 9
+    c = paged_from_contiguous(rng, [n], [past0], H, Hkv, D, bs)
+    one = run_oracle(c, H, Hkv, D)
+    kc, vc = c["kc"], c["vc"]
+
+    def step(kc, vc, lo, hi):
+        cum = np.array([0, hi - lo], np.int32); past = np.array([past0 + lo], np.int32)
+        nk, nv = oracle.append_kv(kc, vc, c["key"][lo:hi], c["value"][lo:hi], cum, past,
+                                  c["table"], kv_num_heads=Hkv, head_size=D)
+        o = oracle.forward(c["query"][lo:hi], nk, nv, cum, past, c["table"], num_heads=H,
+                           kv_num_heads=Hkv, head_size=D)
+        return nk, nv, o
+    k1, v1, o1 = step(kc, vc, 0, 4)
+    _, _, o2 = step(k1, v1, 4, 9)
+    np.testing.assert_allclose(np.concatenate([o1, o2]), one, rtol=0, atol=1e-13)
+    outs = []
+    kk, vv = kc, vc
+    for i in range(n):
+        kk, vv, o = step(kk, vv, i, i + 1)
+        outs.append(o)
+    np.testing.assert_allclose(np.concatenate(outs), one, rtol=0, atol=1e-13)
+
+
+def test_batch_order_permutation_invariance():
+    w = _small_case()
+    out, nk, nv = _oracle_on(w)
+    order = [2, 0, 3, 1]
+    ql = w.q_lens
+    rows = np.concatenate([np.arange(w.cum[b], w.cum[b + 1]) for b in order])
+    cum2 = np.zeros(5, np.int32); cum2[1:] = np.cumsum(ql[order])
+    o2 = oracle.forward(w.query[rows], nk, nv, cum2, w.past[order], w.block_table[order],
+                        num_heads=4, kv_num_heads=2, head_size=16)
+    np.testing.assert_array_equal(o2, out[rows])
+
+
+def test_rows_subset_equals_full():
+    w = _small_case(softcap=5.0, local_window_size=7)
+    full, nk, nv = _oracle_on(w)
+    rows = [9, 0, 4, 2]
+    sub = oracle.forward(w.query, nk, nv, w.cum, w.past, w.block_table, num_heads=4,
+                         kv_num_heads=2, head_size=16, softcap=5.0, local_window_size=7,
+                         rows=rows)
+    np.testing.assert_array_equal(sub, full[rows])
+
+
+def test_softmax_rows_sum_to_one_and_respect_mask():
+    w = _small_case(softcap=1.0, local_window_size=3)
+    kc = w.pool_blocks(0, range(w.num_blocks)); vc = w.pool_blocks(1, range(w.num_blocks))
+    nk, nv = oracle.append_kv(kc, vc, w.key, w.value, w.cum, w.past, w.block_table,
+                              kv_num_heads=2, head_size=16)
+    _, probs = oracle.forward(w.query, nk, nv, w.cum, w.past, w.block_table, num_heads=4,
+                              kv_num_heads=2, head_size=16, softcap=1.0, local_window_size=3,
+                              return_probs=True)
+    for (t, h), p in probs.items():
+        b, j = oracle.locate_token(w.cum, t)
+        pos = int(w.past[b]) + j
+        assert abs(p.sum() - 1) < 1e-12
+        nz = np.nonzero(p)[0]
+        assert nz.min() >= pos - 2 and nz.max() <= pos
+
+
+def test_orphan_tokens_write_nothing_and_output_zero():
+    w = wl.build_case("t", 4, q_lens=[2, 1], past=[5, 9], num_heads=2, kv_num_heads=1,
+                      head_size=8, block_size=16, extra_tokens=3)
+    kc = w.pool_blocks(0, range(w.num_blocks)); vc = w.pool_blocks(1, range(w.num_blocks))
+    nk, nv = oracle.append_kv(kc, vc, w.key, w.value, w.cum, w.past, w.block_table,
+                              kv_num_heads=1, head_size=8)
+    changed = np.argwhere((nk != kc).any(axis=(2, 3)))
+    assert len(changed) <= 3                       # only the 3 owned tokens' slots
+    out = oracle.forward(w.query, nk, nv, w.cum, w.past, w.block_table, num_heads=2,
+                         kv_num_heads=1, head_size=8)
+    assert np.all(out[3:] == 0) and np.all(np.isfinite(out[:3]))
+
+
+# ---------------------------------------------------------------------------
+# rotary
+# ---------------------------------------------------------------------------
+
+def test_rope_position_zero_is_identity():
+    cos, sin = wl.rope_tables(4, 16)
+    x = np.random.default_rng(1).standard_normal(16).astype(np.float16)
+    for inter in (False, True):
+        assert oracle.rope_key_fp16(x, 0, cos, sin, inter).tobytes() == x.tobytes()
+
+
+def test_rope_relative_position_property():
+    """<R_p q, R_p' k> depends only on p - p' (exact fp64 tables)."""
+    D = 16
+    inv = 10000.0 ** (-(2.0 * np.arange(D // 2)) / D)
+    ang = np.arange(64)[:, None] * inv[None, :]
+    cos, sin = np.cos(ang), np.sin(ang)
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal(D); k = rng.standard_normal(D)
+    for inter in (False, True):
+        d1 = oracle.rope_query_fp64(q, 20, cos, sin, inter) @ oracle.rope_query_fp64(k, 13, cos, sin, inter)
+        d2 = oracle.rope_query_fp64(q, 40, cos, sin, inter) @ oracle.rope_query_fp64(k, 33, cos, sin, inter)
+        d3 = oracle.rope_query_fp64(q, 40, cos, sin, inter) @ oracle.rope_query_fp64(k, 34, cos, sin, inter)
+        assert abs(d1 - d2) < 1e-12 and abs(d1 - d3) > 1e-6
+        # rotation preserves the norm of every pair
+        r = oracle.rope_query_fp64(q, 29, cos, sin, inter)
+        assert abs(np.linalg.norm(r) - np.linalg.norm(q)) < 1e-12
+
+
+def test_rope_interleaved_is_channel_permutation_of_rotate_half():
+    D = 16
+    cos, sin = wl.rope_tables(8, D)
+    x = np.random.default_rng(3).standard_normal(D).astype(np.float16)
+    h = D // 2
+    perm = np.array([2 * i for i in range(h)] + [2 * i + 1 for i in range(h)])  # y = x[perm]
+    a = oracle.rope_key_fp16(x, 5, cos, sin, True)
+    b = oracle.rope_key_fp16(x[perm], 5, cos, sin, False)
+    assert a.tobytes() == b[np.argsort(perm)].tobytes()
+
+
+def test_rope_partial_rotary_dim_passes_tail_through():
+    cos, sin = wl.rope_tables(8, 8)                     # rotary_dim 8 of D = 16
+    x = np.random.default_rng(4).standard_normal(16).astype(np.float16)
+    r = oracle.rope_key_fp16(x, 3, cos, sin, False)
+    assert r[8:].tobytes() == x[8:].tobytes() and r[:8].tobytes() != x[:8].tobytes()
+
+
+def test_rope_fp16_rounding_matches_fp32_evaluation():
+    """The stored rotated K equals torch's float32 evaluation of the same
+    pair formula (exact products, one fp32 rounding) then a cast to fp16."""
+    D, rows = 64, 300
+    cos, sin = wl.rope_tables(rows, D)
+    rng = np.random.default_rng(8)
+    X = rng.standard_normal((rows, D)).astype(np.float16)
+    X[::7] *= np.float16(300)                          # spread of magnitudes
+    h = D // 2
+    for p in range(rows):
+        got = oracle.rope_key_fp16(X[p], p, cos, sin, False)
+        x = torch.from_numpy(X[p, :h]).float(); y = torch.from_numpy(X[p, h:]).float()
+        c = torch.from_numpy(cos[p]).float(); s = torch.from_numpy(sin[p]).float()
+        first = (x * c - y * s).half().numpy(); second = (y * c + x * s).half().numpy()
+        assert got.tobytes() == np.concatenate([first, second]).tobytes(), p
+
+
+def test_rotary_forward_matches_torch_on_rotated_inputs():
+    """Forward with in-op rotary equals plain attention on inputs rotated
+    beforehand (queries in fp64, keys as stored in fp16)."""
+    rng = np.random.default_rng(31)
+    H, Hkv, D, bs = 4, 2, 16, 16
+    w = wl.build_case("r", 31, q_lens=[3, 1], past=[0, 20], num_heads=H, kv_num_heads=Hkv,
+                      head_size=D, block_size=bs, do_rotary=1, rotary_dim=D, rng=rng)
+    out, nk, nv = _oracle_on(w)
+    # rotate keys of the cached part too? cached keys were written un-rotated by the
+    # generator; only the new tokens are rotated on append.  Compare per token:
+    for t in range(w.token_count):
+        b, j = oracle.locate_token(w.cum, t)
+        pos = int(w.past[b]) + j
+        kv_len = int(w.past[b]) + int(w.q_lens[b])
+        K = oracle.gather_sequence(nk, w.block_table, b, kv_len)
+        V = oracle.gather_sequence(nv, w.block_table, b, kv_len)
+        q = w.query[t].astype(np.float64).reshape(H, D)
+        qr = np.stack([oracle.rope_query_fp64(q[h], pos, w.cos_cache, w.sin_cache, False)
+                       for h in range(H)])
+        qt = torch.from_numpy(qr)[None, :, None, :]
+        kt = torch.from_numpy(K[:pos + 1]).permute(1, 0, 2).repeat_interleave(2, 0)[None]
+        vt = torch.from_numpy(V[:pos + 1]).permute(1, 0, 2).repeat_interleave(2, 0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[0, :, 0, :]
+        np.testing.assert_allclose(out[t], ref.reshape(-1).numpy(), rtol=0, atol=1e-12)
+        # and the stored new key is the rotated fp16 key
+        blk, off = oracle.derived_slot(w.block_table, b, pos, bs)
+        for h in range(Hkv):
+            exp = oracle.rope_key_fp16(w.key[t, h * D:(h + 1) * D], pos, w.cos_cache,
+                                       w.sin_cache, False)
+            assert nk[blk, off, h].tobytes() == exp.tobytes()
+
+
+# ---------------------------------------------------------------------------
+# the log-sum-exp merge the split-KV design relies on
+# ---------------------------------------------------------------------------
+
+def test_lse_merge_of_any_partition_equals_direct_softmax():
+    """GroupQueryAttention CPU Implementation Notes, "Flash Decoding": merging
+    per-chunk (m, l, o) with exp(m_c - M) weights equals one softmax."""
+    rng = np.random.default_rng(6)
+    s = rng.standard_normal(97) * 4
+    v = rng.standard_normal((97, 8))
+    p = np.exp(s - s.max()); direct = (p / p.sum()) @ v
+    for cuts in ([0, 97], [0, 13, 50, 97], [0, 1, 2, 96, 97], [0, 40, 40, 97]):
+        parts = []
+        for lo, hi in zip(cuts[:-1], cuts[1:]):
+            if hi == lo:
+                parts.append((-np.finfo(np.float32).max, 0.0, np.zeros(8)))   # empty split
+                continue
+            m = s[lo:hi].max(); e = np.exp(s[lo:hi] - m)
+            parts.append((m, e.sum(), e @ v[lo:hi]))
+        M = max(m for m, _, _ in parts)
+        num = sum(math.exp(m - M) * o for m, _, o in parts)
+        den = sum(math.exp(m - M) * l for m, l, _ in parts)
+        np.testing.assert_allclose(num / den, direct, rtol=0, atol=1e-13)
