@@ -1,0 +1,183 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged KV append + PagedAttention forward.
+ *
+ * Operation (PagedAttention -- CUDA Design Document, section 4 "Schema -- The
+ * Compatible Contract", and Design: WebGPU PagedAttention, section 3 "Op
+ * contract"): causal grouped-query attention over packed variable-length
+ * queries.  Query tokens of all in-flight requests are packed along one axis
+ * and delimited by cumulative_sequence_length; request b owns tokens
+ * [cum[b], cum[b+1]) and its j-th new token sits at position past_seqlens[b] + j.
+ * K/V of every position live in a shared fp16 block pool
+ * [num_blocks, block_size, kv_num_heads, head_size]; block_table[b][i] names the
+ * physical block holding positions [i*block_size, (i+1)*block_size) of request b.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer unless it says "host".  The
+ *     caller owns and allocates every buffer; the library allocates nothing per
+ *     call, never synchronizes, and never reads device memory on the host.
+ *   - fp16 tensors are IEEE binary16, row-major, and must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *     enqueued on it, in order; results are ready when the stream reaches them.
+ *   - Errors: a non-PA_OK status means nothing was enqueued.  pa_last_error()
+ *     returns a thread-local message naming the offending argument and the
+ *     value expected.  Device-resident values (lengths, table entries) cannot be
+ *     checked on the host; out-of-range device values never cause an
+ *     out-of-bounds access (they are clamped or the token is skipped) but give
+ *     unspecified results.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1, /* malformed request (validation rules)      */
+  PA_ERR_UNSUPPORTED = 2,      /* well formed, but not served by a kernel   */
+  PA_ERR_DEVICE = 3            /* a HIP runtime call failed                 */
+} pa_status;
+
+/* Attributes (PagedAttention -- CUDA Design Document, section 4.5; Design:
+ * WebGPU PagedAttention, section 3.1).  Host struct. */
+typedef struct {
+  int32_t num_heads;          /* query heads H, > 0                                    */
+  int32_t kv_num_heads;       /* K/V heads Hkv, > 0, H % Hkv == 0; q head h reads
+                                 kv head h / (H / Hkv)                                 */
+  int32_t head_size;          /* D; multiple of 8; kernels serve 64, 128, 256          */
+  int32_t block_size;         /* tokens per pool block; power of two >= 16             */
+  float scale;                /* 0 -> 1/sqrt(head_size) (section 12.6); finite         */
+  float softcap;              /* 0 -> off; > 0 -> s = softcap*tanh(s_scaled/softcap),
+                                 applied before masking (section 8.5 note); finite     */
+  int32_t local_window_size;  /* -1 -> off; W >= 1 admits the W positions ending at
+                                 the query's own (section 4.5, section 9)              */
+  int32_t do_rotary;          /* 0/1: rotate new K (pa_append_kv) and Q (pa_forward)
+                                 at their absolute position                            */
+  int32_t rotary_interleaved; /* 0: pairs (i, i + r/2); 1: pairs (2i, 2i+1)            */
+  int32_t path;               /* kernel routing, 0 = auto (token_count <= batch_size
+                                 -> decode kernel only, else decode + prefill kernels);
+                                 1 = decode kernel for every token; 2 = decode kernel
+                                 for q_len == 1 requests, prefill kernel for the rest.
+                                 Results are the same up to rounding.                  */
+  int32_t split_tokens;       /* 0 = auto; else decode KV split length in tokens, a
+                                 multiple of 64 (testing hook; rounding may differ)    */
+} pa_attn_params;
+
+/* The paged cache and the per-step request layout.  Host struct holding
+ * device pointers. */
+typedef struct {
+  void *key_cache;                          /* fp16 [num_blocks, block_size, Hkv, D]  */
+  void *value_cache;                        /* same shape; both mutated in place by
+                                               pa_append_kv (cache outputs alias the
+                                               inputs, section 4.4)                   */
+  int64_t num_blocks;                       /* > 0                                   */
+  const int32_t *block_table;               /* int32 [batch_size, max_blocks_per_seq]
+                                               row-major; entries past a request's
+                                               length are never read                 */
+  int32_t max_blocks_per_seq;               /* > 0; capacity = this * block_size     */
+  const int32_t *cumulative_sequence_length;/* int32 [batch_size + 1], cum[0] = 0,
+                                               non-decreasing, cum[batch] <= tokens  */
+  const int32_t *past_seqlens;              /* int32 [batch_size], >= 0              */
+  int32_t batch_size;                       /* > 0                                   */
+  int32_t token_count;                      /* T >= 0; rows of query/key/value/out   */
+} pa_paged_kv;
+
+/*
+ * pa_append_kv -- scatter the new tokens' K/V into their pool slots
+ * (PagedAttention -- CUDA Design Document, section 5.1 "derived write slot";
+ * section 7.2 / 12.5 for rotary applied to K before the write).
+ *
+ *   key, value : fp16 [token_count, kv_num_heads * head_size]
+ *   cos_cache, sin_cache : fp16 [rotary_rows, rotary_dim / 2]; both non-NULL iff
+ *                params->do_rotary; rotary_dim even, <= head_size;
+ *                rotary_rows >= max_blocks_per_seq * block_size.
+ *
+ * Token t of request b (cum[b] <= t < cum[b+1], j = t - cum[b]) at position
+ * p = past[b] + j is written to block block_table[b][p / block_size], offset
+ * p % block_size, for every kv head.  With rotary the stored K is
+ * fp16(fp32(x*cos - y*sin)) of its channel pair.  Tokens t >= cum[batch_size]
+ * write nothing; every other slot keeps its bytes.  Enqueue before
+ * pa_forward on the same stream.
+ */
+pa_status pa_append_kv(const pa_attn_params *params, const pa_paged_kv *kv,
+                       const void *key, const void *value,
+                       const void *cos_cache, const void *sin_cache,
+                       int32_t rotary_rows, int32_t rotary_dim, void *stream);
+
+/*
+ * pa_forward_workspace_bytes -- device workspace pa_forward needs for these
+ * static shapes and optional replay-wide bounds (host call, writes *bytes).
+ *
+ *   max_query_len_bound : 0 = unknown, else an upper bound on any request's
+ *                         new-token count for every step it will serve
+ *   max_kv_len_bound    : 0 = unknown, else an upper bound on any request's
+ *                         past + new length
+ * (PagedAttention -- CUDA Design Document, section 4.7: bounds only size
+ * launches and workspace, never a mask; 0 falls back to token_count and to
+ * max_blocks_per_seq * block_size; over-large bounds are clamped.)
+ */
+pa_status pa_forward_workspace_bytes(const pa_attn_params *params, const pa_paged_kv *kv,
+                                     int32_t max_query_len_bound, int32_t max_kv_len_bound,
+                                     size_t *bytes);
+
+/*
+ * pa_forward -- attention output of every packed token
+ * (PagedAttention -- CUDA Design Document, section 4; GroupQueryAttention CPU
+ * Implementation Notes, "Flash Decoding" for the split-KV merge).
+ *
+ *   query     : fp16 [token_count, num_heads * head_size]
+ *   cos_cache, sin_cache, rotary_rows, rotary_dim : as for pa_append_kv; Q is
+ *               rotated at its position on load (never written back)
+ *   workspace : device scratch of >= pa_forward_workspace_bytes() bytes for the
+ *               same shapes and bounds (may be NULL when that is 0); contents
+ *               on entry are irrelevant; not shared with a concurrent call
+ *   out       : fp16 [token_count, num_heads * head_size]
+ *
+ * out[t, h*D:(h+1)*D] = sum_tau softmax_tau(cap(scale * q_t,h . k_tau)) v_tau over
+ * positions tau of t's request with tau <= p_t and (W < 0 or tau > p_t - W), K/V
+ * read from the pool (so pa_append_kv must run first).  Rows of tokens
+ * t >= cum[batch_size] are written as 0.  A bound smaller than a real length
+ * violates the contract: work is omitted, memory stays safe.
+ */
+pa_status pa_forward(const pa_attn_params *params, const pa_paged_kv *kv,
+                     const void *query,
+                     const void *cos_cache, const void *sin_cache,
+                     int32_t rotary_rows, int32_t rotary_dim,
+                     int32_t max_query_len_bound, int32_t max_kv_len_bound,
+                     void *workspace, size_t workspace_bytes,
+                     void *out, void *stream);
+
+/* Thread-local text of the last error on this thread ("" if none). */
+const char *pa_last_error(void);
+
+/*
+ * pa_describe_plan -- host call; writes into `buf` (host, `len` bytes) a one-line
+ * description of the launches pa_forward would make for these shapes and
+ * bounds (path, grids, split length).  For logs and tests.
+ */
+pa_status pa_describe_plan(const pa_attn_params *params, const pa_paged_kv *kv,
+                           int32_t max_query_len_bound, int32_t max_kv_len_bound,
+                           char *buf, size_t len);
+
+/*
+ * Per-kernel timing on the launch stream, for benchmarks.  While enabled, the
+ * library records a HIP event pair around every kernel it launches (on the
+ * same stream) and pa_timing_read() sums their elapsed times per stage
+ * (synchronizing on the recorded events).  Enabling creates the events
+ * (2 * max_launches); it is not meant for graph capture.
+ *   stage: 0 = append, 1 = decode, 2 = split merge, 3 = prefill.
+ */
+enum { PA_STAGE_APPEND = 0, PA_STAGE_DECODE = 1, PA_STAGE_MERGE = 2, PA_STAGE_PREFILL = 3,
+       PA_NUM_STAGES = 4 };
+pa_status pa_timing_enable(int32_t max_launches);
+pa_status pa_timing_disable(void);
+pa_status pa_timing_read(int32_t stage, double *total_ms, int32_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H_ */

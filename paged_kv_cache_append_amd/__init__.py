@@ -1,5 +1,199 @@
 """MI355X-native paged KV append + PagedAttention forward (HIP, gfx950).
 
-The compute lives in ``libpa.so`` (built from ``csrc/``) behind a C ABI
-declared in ``include/pa.h``; this package only marshals arguments to it.
+The compute lives in ``libpa.so`` (built from ``csrc/`` by ``build.py``)
+behind the C ABI of ``include/pa.h``.  This module only marshals torch tensors
+(device memory) and the current HIP stream into those calls; there is no
+other implementation, and calling it without the built library raises.
+
+Names mirror the C entry points: :func:`append_kv` (``pa_append_kv``),
+:func:`forward` (``pa_forward``), :func:`forward_workspace_bytes`,
+:func:`describe_plan`, :func:`last_error`, and the ``timing_*`` helpers.
 """
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+from . import _lib
+
+__all__ = ["PAError", "Attn", "append_kv", "forward", "forward_workspace_bytes",
+           "describe_plan", "last_error", "timing_enable", "timing_disable", "timing_read",
+           "library_path"]
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+@dataclass
+class Attn:
+    """Attributes of the op (``pa_attn_params``)."""
+    num_heads: int
+    kv_num_heads: int
+    head_size: int
+    block_size: int
+    scale: float = 0.0
+    softcap: float = 0.0
+    local_window_size: int = -1
+    do_rotary: int = 0
+    rotary_interleaved: int = 0
+    path: int = 0
+    split_tokens: int = 0
+
+    def c(self) -> _lib.AttnParams:
+        return _lib.AttnParams(self.num_heads, self.kv_num_heads, self.head_size,
+                               self.block_size, float(self.scale), float(self.softcap),
+                               self.local_window_size, self.do_rotary,
+                               self.rotary_interleaved, self.path, self.split_tokens)
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def last_error() -> str:
+    return _lib.load().pa_last_error().decode()
+
+
+def _check(status: int):
+    if status != _lib.PA_OK:
+        raise PAError(status, last_error())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype, shape=None):
+    import torch
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _kv(key_cache, value_cache, block_table, cum, past, token_count) -> _lib.PagedKV:
+    import torch
+    _need(key_cache, "key_cache", torch.float16)
+    _need(value_cache, "value_cache", torch.float16, key_cache.shape)
+    _need(block_table, "block_table", torch.int32)
+    _need(cum, "cumulative_sequence_length", torch.int32, (block_table.shape[0] + 1,))
+    _need(past, "past_seqlens", torch.int32, (block_table.shape[0],))
+    if key_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("key_cache must be rank 4 and block_table rank 2")
+    return _lib.PagedKV(key_cache.data_ptr(), value_cache.data_ptr(), key_cache.shape[0],
+                        block_table.data_ptr(), block_table.shape[1], cum.data_ptr(),
+                        past.data_ptr(), block_table.shape[0], token_count)
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _rot(attn: Attn, cos_cache, sin_cache):
+    import torch
+    if cos_cache is None:
+        return None, None, 0, 0
+    _need(cos_cache, "cos_cache", torch.float16)
+    _need(sin_cache, "sin_cache", torch.float16, cos_cache.shape)
+    return cos_cache.data_ptr(), sin_cache.data_ptr(), cos_cache.shape[0], 2 * cos_cache.shape[1]
+
+
+def append_kv(attn: Attn, key, value, key_cache, value_cache, block_table, cum, past,
+              cos_cache=None, sin_cache=None, stream=None) -> None:
+    """``pa_append_kv``: scatter new K/V rows ``[T, Hkv*D]`` into the pools
+    (in place)."""
+    import torch
+    T = key.shape[0]
+    _need(key, "key", torch.float16, (T, attn.kv_num_heads * attn.head_size))
+    _need(value, "value", torch.float16, (T, attn.kv_num_heads * attn.head_size))
+    lib = _lib.load()
+    p = attn.c()
+    kv = _kv(key_cache, value_cache, block_table, cum, past, T)
+    c, s, rows, rd = _rot(attn, cos_cache, sin_cache)
+    _check(lib.pa_append_kv(ctypes.byref(p), ctypes.byref(kv), key.data_ptr(), value.data_ptr(),
+                            c, s, rows, rd, _stream(stream)))
+
+
+def forward_workspace_bytes(attn: Attn, key_cache, value_cache, block_table, cum, past,
+                            token_count: int, max_query_len_bound: int = 0,
+                            max_kv_len_bound: int = 0) -> int:
+    lib = _lib.load()
+    p = attn.c()
+    kv = _kv(key_cache, value_cache, block_table, cum, past, token_count)
+    n = ctypes.c_size_t(0)
+    _check(lib.pa_forward_workspace_bytes(ctypes.byref(p), ctypes.byref(kv), max_query_len_bound,
+                                          max_kv_len_bound, ctypes.byref(n)))
+    return int(n.value)
+
+
+def describe_plan(attn: Attn, key_cache, value_cache, block_table, cum, past, token_count: int,
+                  max_query_len_bound: int = 0, max_kv_len_bound: int = 0) -> str:
+    lib = _lib.load()
+    p = attn.c()
+    kv = _kv(key_cache, value_cache, block_table, cum, past, token_count)
+    buf = ctypes.create_string_buffer(512)
+    _check(lib.pa_describe_plan(ctypes.byref(p), ctypes.byref(kv), max_query_len_bound,
+                                max_kv_len_bound, buf, 512))
+    return buf.value.decode()
+
+
+def forward(attn: Attn, query, key_cache, value_cache, block_table, cum, past, cos_cache=None,
+            sin_cache=None, max_query_len_bound: int = 0, max_kv_len_bound: int = 0,
+            workspace=None, out=None, stream=None):
+    """``pa_forward``: attention output ``[T, H*D]`` fp16 for packed queries
+    ``[T, H*D]``.  ``workspace``/``out`` are allocated with torch when not
+    given."""
+    import torch
+    T = query.shape[0]
+    HD = attn.num_heads * attn.head_size
+    _need(query, "query", torch.float16, (T, HD))
+    lib = _lib.load()
+    p = attn.c()
+    kv = _kv(key_cache, value_cache, block_table, cum, past, T)
+    if out is None:
+        out = torch.empty((T, HD), dtype=torch.float16, device=query.device)
+    _need(out, "out", torch.float16, (T, HD))
+    n = ctypes.c_size_t(0)
+    _check(lib.pa_forward_workspace_bytes(ctypes.byref(p), ctypes.byref(kv), max_query_len_bound,
+                                          max_kv_len_bound, ctypes.byref(n)))
+    need = int(n.value)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = _ptr(workspace)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c, s, rows, rd = _rot(attn, cos_cache, sin_cache)
+    _check(lib.pa_forward(ctypes.byref(p), ctypes.byref(kv), query.data_ptr(), c, s, rows, rd,
+                          max_query_len_bound, max_kv_len_bound, ws_ptr, ws_len, out.data_ptr(),
+                          _stream(stream)))
+    return out
+
+
+def timing_enable(max_launches: int) -> None:
+    _check(_lib.load().pa_timing_enable(max_launches))
+
+
+def timing_disable() -> None:
+    _check(_lib.load().pa_timing_disable())
+
+
+def timing_read(stage: str):
+    """(total milliseconds, launches) recorded for ``stage`` in
+    {append, decode, merge, prefill}."""
+    lib = _lib.load()
+    ms = ctypes.c_double(0)
+    n = ctypes.c_int32(0)
+    _check(lib.pa_timing_read(_lib.STAGES[stage], ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

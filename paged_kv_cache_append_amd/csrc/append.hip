@@ -1,0 +1,60 @@
+// KV append: scatter every new token's K/V row into its pool slot
+// (PagedAttention -- CUDA Design Document, section 5.1 "derived write slot";
+// Design: WebGPU PagedAttention, section 5 Phase 1 item 3 for the one-lane-per-
+// vector dispatch over token_count * kv_hidden).
+//
+// One lane moves one 16-byte chunk (8 channels) of one (token, kv head) for
+// both K and V.  Lanes of a wave cover consecutive chunks of a token row, so
+// the NHD pool layout turns every token into one contiguous Hkv*D*2-byte run:
+// fully coalesced reads and writes.  The owning request is found by binary
+// search over cumulative_sequence_length (same-address loads across the
+// wave, served by the cache); tokens at or past cum[B] own nothing (the
+// out-of-bounds defect of section 18.2 cannot occur).
+#include "pa_device.h"
+
+namespace pa {
+
+__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
+  const int chunks = a.head_size >> 3;
+  const int64_t per_tok = (int64_t)a.kv_heads * chunks;
+  const int64_t items = (int64_t)a.s.tokens * per_tok;
+  const int bs = 1 << a.s.block_shift;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += stride) {
+    const int t = (int)(it / per_tok);
+    const int rem = (int)(it - (int64_t)t * per_tok);
+    const int kvh = rem / chunks;
+    const int c = rem - kvh * chunks;
+    const int b = find_request(a.s.cum, a.s.batch, t);
+    if (b < 0) continue;
+    const int pos = a.s.past[b] + (t - a.s.cum[b]);
+    if (pos < 0) continue;
+    const int bi = pos >> a.s.block_shift;
+    if (bi >= a.s.maxblk) continue;
+    const int64_t blk = a.s.block_table[(int64_t)b * a.s.maxblk + bi];
+    if (blk < 0 || blk >= a.s.num_blocks) continue;  // unmapped: nothing to write
+    const int off = pos & (bs - 1);
+    const int64_t dst = slot_base(blk, off, kvh, bs, a.kv_heads, a.head_size) + 8 * c;
+    const int64_t src_row = (int64_t)t * a.kv_heads * a.head_size + (int64_t)kvh * a.head_size;
+    store16(a.value_cache + dst, load16(a.value + src_row + 8 * c));
+    u32x4 k = load16(a.key + src_row + 8 * c);
+    if (a.rotary_dim > 0 && 8 * c < a.rotary_dim) {
+      float r[8];
+      rotate_chunk(a.key + src_row, k, c, pos, a.cos, a.sin, a.rotary_dim,
+                   a.rotary_interleaved, a.rotary_rows, r);
+      k = pack8(r);
+    }
+    store16(a.key_cache + dst, k);
+  }
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
+  const int64_t items = (int64_t)a.s.tokens * a.kv_heads * (a.head_size >> 3);
+  if (items == 0) return hipSuccess;
+  int64_t blocks = (items + 255) / 256;
+  if (blocks > (1 << 20)) blocks = 1 << 20;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,485 @@
+// Host side of the C ABI: validation, launch planning and kernel launches.
+//
+// Validation follows the consolidated rules of PagedAttention -- CUDA Design
+// Document, section 15 (every violation names the offending argument and the
+// expected value); planning follows section 4.7: only static shapes,
+// attributes and the optional replay-wide bounds choose kernels and size
+// grids/workspace -- device-resident lengths never reach the host, so a
+// captured stream stays valid while lengths change.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int log2_exact(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+// ---- per-kernel timing (benchmarks) ---------------------------------------
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<hipEvent_t> events;   // pairs
+  std::vector<int> stage;           // per pair
+  size_t used = 0;                  // pairs recorded
+};
+Timing g_timing;
+
+struct StageScope {
+  hipStream_t st;
+  int slot = -1;
+  StageScope(int stg, hipStream_t s) : st(s) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (!g_timing.enabled || g_timing.used >= g_timing.stage.size()) return;
+    slot = (int)g_timing.used++;
+    g_timing.stage[slot] = stg;
+    hipEventRecord(g_timing.events[2 * slot], st);
+  }
+  ~StageScope() {
+    if (slot >= 0) hipEventRecord(g_timing.events[2 * slot + 1], st);
+  }
+};
+
+// ---- validation --------------------------------------------------------------
+pa_status check_common(const pa_attn_params* p, const pa_paged_kv* kv) {
+  if (!p) return fail(PA_ERR_INVALID_ARGUMENT, "params: expected non-NULL");
+  if (!kv) return fail(PA_ERR_INVALID_ARGUMENT, "kv: expected non-NULL");
+  if (p->num_heads <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_heads: expected > 0, got %d", p->num_heads);
+  if (p->kv_num_heads <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "kv_num_heads: expected > 0, got %d", p->kv_num_heads);
+  if (p->num_heads % p->kv_num_heads != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "num_heads: expected a multiple of kv_num_heads (%d), got %d", p->kv_num_heads,
+                p->num_heads);
+  if (p->head_size <= 0 || p->head_size % 8 != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "head_size: expected a positive multiple of 8, got %d",
+                p->head_size);
+  if (p->block_size < 16 || (p->block_size & (p->block_size - 1)) != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "block_size: expected a power of two >= 16, got %d",
+                p->block_size);
+  if (!std::isfinite(p->scale))
+    return fail(PA_ERR_INVALID_ARGUMENT, "scale: expected a finite value");
+  if (!std::isfinite(p->softcap) || p->softcap < 0.f)
+    return fail(PA_ERR_INVALID_ARGUMENT, "softcap: expected a finite value >= 0, got %g",
+                (double)p->softcap);
+  if (p->local_window_size != -1 && p->local_window_size < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "local_window_size: expected -1 or >= 1, got %d",
+                p->local_window_size);
+  if (p->do_rotary != 0 && p->do_rotary != 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "do_rotary: expected 0 or 1, got %d", p->do_rotary);
+  if (p->rotary_interleaved != 0 && p->rotary_interleaved != 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "rotary_interleaved: expected 0 or 1, got %d",
+                p->rotary_interleaved);
+  if (p->path < 0 || p->path > 2)
+    return fail(PA_ERR_INVALID_ARGUMENT, "path: expected 0, 1 or 2, got %d", p->path);
+  if (p->num_heads > 65535)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_heads: expected <= 65535, got %d", p->num_heads);
+  if (p->split_tokens < 0 || p->split_tokens % 64 != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "split_tokens: expected 0 or a multiple of 64, got %d",
+                p->split_tokens);
+  if (kv->batch_size <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "batch_size: expected > 0, got %d", kv->batch_size);
+  if (kv->token_count < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "token_count: expected >= 0, got %d", kv->token_count);
+  if (kv->num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks: expected > 0, got %lld",
+                (long long)kv->num_blocks);
+  if (kv->max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq: expected > 0, got %d",
+                kv->max_blocks_per_seq);
+  if ((int64_t)kv->max_blocks_per_seq * p->block_size > (int64_t)1 << 30)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "max_blocks_per_seq * block_size: expected <= 2^30 positions");
+  if (!kv->key_cache) return fail(PA_ERR_INVALID_ARGUMENT, "key_cache: expected non-NULL");
+  if (!kv->value_cache) return fail(PA_ERR_INVALID_ARGUMENT, "value_cache: expected non-NULL");
+  if (!aligned16(kv->key_cache) || !aligned16(kv->value_cache))
+    return fail(PA_ERR_INVALID_ARGUMENT, "key_cache/value_cache: expected 16-byte alignment");
+  if (!kv->block_table) return fail(PA_ERR_INVALID_ARGUMENT, "block_table: expected non-NULL");
+  if (!kv->cumulative_sequence_length)
+    return fail(PA_ERR_INVALID_ARGUMENT, "cumulative_sequence_length: expected non-NULL");
+  if (!kv->past_seqlens) return fail(PA_ERR_INVALID_ARGUMENT, "past_seqlens: expected non-NULL");
+  return PA_OK;
+}
+
+pa_status check_rotary(const pa_attn_params* p, const pa_paged_kv* kv, const void* cos_cache,
+                       const void* sin_cache, int32_t rows, int32_t dim) {
+  if ((cos_cache == nullptr) != (sin_cache == nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "cos_cache/sin_cache: expected both or neither");
+  if (p->do_rotary) {
+    if (!cos_cache)
+      return fail(PA_ERR_INVALID_ARGUMENT, "cos_cache/sin_cache: required when do_rotary = 1");
+    if (dim <= 0 || dim % 2 != 0 || dim > p->head_size)
+      return fail(PA_ERR_INVALID_ARGUMENT,
+                  "rotary_dim: expected an even value in [2, head_size=%d], got %d",
+                  p->head_size, dim);
+    const int64_t need = (int64_t)kv->max_blocks_per_seq * p->block_size;
+    if (rows < need)
+      return fail(PA_ERR_INVALID_ARGUMENT,
+                  "rotary_rows: expected >= max_blocks_per_seq * block_size = %lld, got %d",
+                  (long long)need, rows);
+  } else if (cos_cache) {
+    return fail(PA_ERR_INVALID_ARGUMENT, "cos_cache/sin_cache: given but do_rotary = 0");
+  }
+  return PA_OK;
+}
+
+pa_status check_kernel_support(const pa_attn_params* p) {
+  if (p->head_size != 64 && p->head_size != 128 && p->head_size != 256)
+    return fail(PA_ERR_UNSUPPORTED,
+                "head_size %d: the kernels serve head_size 64, 128 and 256", p->head_size);
+  return PA_OK;
+}
+
+// ---- planning ----------------------------------------------------------------
+constexpr int kTargetWorkgroups = 4096;  // decode workgroups aimed at (256 CUs)
+
+struct Plan {
+  bool token_mode = true;    // decode rows are tokens (else requests with q_len == 1)
+  bool prefill = false;
+  int rows = 0;
+  int g = 1, g_chunk = 1, head_chunks = 1;
+  int split_tokens = 256;
+  int max_splits = 1;
+  int prefill_tiles = 0;     // tile slots (grid.x = tiles + 1)
+  size_t ws_bytes = 0;
+};
+
+Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32_t mk) {
+  Plan pl;
+  const int T = kv->token_count, B = kv->batch_size;
+  pl.g = p->num_heads / p->kv_num_heads;
+  pl.g_chunk = pl.g % 8 == 0 ? 8 : pl.g % 4 == 0 ? 4 : pl.g % 2 == 0 ? 2 : 1;
+  pl.head_chunks = pl.g / pl.g_chunk;
+  if (p->path == 1)
+    pl.token_mode = true;
+  else if (p->path == 2)
+    pl.token_mode = false;
+  else
+    pl.token_mode = T <= B;   // static shape test: a heuristic, never a correctness input
+  pl.prefill = !pl.token_mode;
+  pl.rows = pl.token_mode ? T : B;
+
+  const int64_t cap = (int64_t)kv->max_blocks_per_seq * p->block_size;
+  int64_t span = cap;                                   // static key-range extent
+  if (p->local_window_size > 0 && p->local_window_size < span) span = p->local_window_size;
+  if (p->split_tokens > 0) {
+    pl.split_tokens = p->split_tokens;
+  } else {
+    // split length from static shapes only, so results do not depend on the bounds
+    const int64_t pairs = std::max<int64_t>(1, (int64_t)pl.rows * p->kv_num_heads * pl.head_chunks);
+    const int64_t want = std::max<int64_t>(1, (kTargetWorkgroups + pairs - 1) / pairs);
+    int64_t st = (span + want - 1) / want;
+    st = (st + 63) / 64 * 64;
+    pl.split_tokens = (int)std::max<int64_t>(256, std::min<int64_t>(st, 1 << 30));
+  }
+  int64_t kv_ext = mk > 0 ? std::min<int64_t>(mk, cap) : cap;   // bound only trims the grid
+  if (p->local_window_size > 0) kv_ext = std::min<int64_t>(kv_ext, p->local_window_size);
+  pl.max_splits = (int)std::max<int64_t>(1, (kv_ext + pl.split_tokens - 1) / pl.split_tokens);
+  if (pl.max_splits > 1) {
+    const size_t per = (size_t)pl.rows * p->num_heads * pl.max_splits;
+    size_t o_bytes = per * p->head_size * sizeof(float);
+    o_bytes = (o_bytes + 255) / 256 * 256;
+    pl.ws_bytes = o_bytes + per * 2 * sizeof(float);
+  }
+  if (pl.prefill) {
+    const int64_t mql = mq > 0 ? std::min<int64_t>(mq, T) : T;
+    const int64_t per_req = (mql * pl.g + pa::kPrefillRows - 1) / pa::kPrefillRows;
+    const int64_t by_tokens = ((int64_t)T * pl.g + pa::kPrefillRows - 1) / pa::kPrefillRows + B;
+    pl.prefill_tiles = (int)std::min<int64_t>(std::min<int64_t>((int64_t)B * per_req, by_tokens),
+                                              (int64_t)1 << 30);
+  }
+  return pl;
+}
+
+pa_status check_plan(const Plan& pl) {
+  if (pl.max_splits > 65535)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "split_tokens: %d gives %d splits; expected at most 65535", pl.split_tokens,
+                pl.max_splits);
+  return PA_OK;
+}
+
+pa::SeqLayout layout(const pa_attn_params* p, const pa_paged_kv* kv) {
+  pa::SeqLayout s;
+  s.cum = kv->cumulative_sequence_length;
+  s.past = kv->past_seqlens;
+  s.block_table = kv->block_table;
+  s.batch = kv->batch_size;
+  s.tokens = kv->token_count;
+  s.maxblk = kv->max_blocks_per_seq;
+  s.block_shift = log2_exact(p->block_size);
+  s.num_blocks = kv->num_blocks;
+  return s;
+}
+
+pa_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PA_OK;
+  return fail(PA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_error.c_str(); }
+
+pa_status pa_append_kv(const pa_attn_params* params, const pa_paged_kv* kv, const void* key,
+                       const void* value, const void* cos_cache, const void* sin_cache,
+                       int32_t rotary_rows, int32_t rotary_dim, void* stream) {
+  g_error.clear();
+  pa_status st = check_common(params, kv);
+  if (st != PA_OK) return st;
+  if ((st = check_rotary(params, kv, cos_cache, sin_cache, rotary_rows, rotary_dim)) != PA_OK)
+    return st;
+  if (kv->token_count == 0) return PA_OK;
+  if (!key || !value) return fail(PA_ERR_INVALID_ARGUMENT, "key/value: expected non-NULL");
+  if (!aligned16(key) || !aligned16(value))
+    return fail(PA_ERR_INVALID_ARGUMENT, "key/value: expected 16-byte alignment");
+  pa::AppendArgs a;
+  a.s = layout(params, kv);
+  a.key = static_cast<const uint16_t*>(key);
+  a.value = static_cast<const uint16_t*>(value);
+  a.key_cache = static_cast<uint16_t*>(kv->key_cache);
+  a.value_cache = static_cast<uint16_t*>(kv->value_cache);
+  a.cos = static_cast<const uint16_t*>(cos_cache);
+  a.sin = static_cast<const uint16_t*>(sin_cache);
+  a.kv_heads = params->kv_num_heads;
+  a.head_size = params->head_size;
+  a.rotary_dim = params->do_rotary ? rotary_dim : 0;
+  a.rotary_interleaved = params->rotary_interleaved;
+  a.rotary_rows = params->do_rotary ? rotary_rows : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StageScope scope(PA_STAGE_APPEND, s);
+  return device_status(pa::launch_append(a, s), "append kernel launch");
+}
+
+pa_status pa_forward_workspace_bytes(const pa_attn_params* params, const pa_paged_kv* kv,
+                                     int32_t mq, int32_t mk, size_t* bytes) {
+  g_error.clear();
+  if (!bytes) return fail(PA_ERR_INVALID_ARGUMENT, "bytes: expected non-NULL");
+  *bytes = 0;
+  pa_status st = check_common(params, kv);
+  if (st != PA_OK) return st;
+  if (mq < 0 || mk < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_query_len_bound/max_kv_len_bound: expected >= 0");
+  if (kv->token_count == 0) return PA_OK;
+  const Plan pl = make_plan(params, kv, mq, mk);
+  if ((st = check_plan(pl)) != PA_OK) return st;
+  *bytes = pl.ws_bytes;
+  return PA_OK;
+}
+
+pa_status pa_describe_plan(const pa_attn_params* params, const pa_paged_kv* kv, int32_t mq,
+                           int32_t mk, char* buf, size_t len) {
+  g_error.clear();
+  pa_status st = check_common(params, kv);
+  if (st != PA_OK) return st;
+  if (!buf || len == 0) return fail(PA_ERR_INVALID_ARGUMENT, "buf: expected non-NULL, len > 0");
+  const Plan pl = make_plan(params, kv, mq, mk);
+  snprintf(buf, len,
+           "mode=%s decode_grid=(%d,%d,%d) g=%d g_chunk=%d split_tokens=%d max_splits=%d "
+           "merge=%d prefill_grid=(%d,%d) workspace=%zu",
+           pl.token_mode ? "token" : "request", pl.rows, params->kv_num_heads * pl.head_chunks,
+           pl.max_splits, pl.g, pl.g_chunk, pl.split_tokens, pl.max_splits,
+           pl.max_splits > 1 ? 1 : 0, pl.prefill ? pl.prefill_tiles + 1 : 0,
+           pl.prefill ? params->kv_num_heads : 0, pl.ws_bytes);
+  return PA_OK;
+}
+
+pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const void* query,
+                     const void* cos_cache, const void* sin_cache, int32_t rotary_rows,
+                     int32_t rotary_dim, int32_t mq, int32_t mk, void* workspace,
+                     size_t workspace_bytes, void* out, void* stream) {
+  g_error.clear();
+  pa_status st = check_common(params, kv);
+  if (st != PA_OK) return st;
+  if ((st = check_rotary(params, kv, cos_cache, sin_cache, rotary_rows, rotary_dim)) != PA_OK)
+    return st;
+  if (mq < 0 || mk < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_query_len_bound/max_kv_len_bound: expected >= 0");
+  if (kv->token_count == 0) return PA_OK;
+  if ((st = check_kernel_support(params)) != PA_OK) return st;
+  if (!query) return fail(PA_ERR_INVALID_ARGUMENT, "query: expected non-NULL");
+  if (!out) return fail(PA_ERR_INVALID_ARGUMENT, "out: expected non-NULL");
+  if (!aligned16(query) || !aligned16(out))
+    return fail(PA_ERR_INVALID_ARGUMENT, "query/out: expected 16-byte alignment");
+  const Plan pl = make_plan(params, kv, mq, mk);
+  if ((st = check_plan(pl)) != PA_OK) return st;
+  if (workspace_bytes < pl.ws_bytes)
+    return fail(PA_ERR_INVALID_ARGUMENT, "workspace_bytes: expected >= %zu, got %zu",
+                pl.ws_bytes, workspace_bytes);
+  if (pl.ws_bytes > 0 && (!workspace || !aligned16(workspace)))
+    return fail(PA_ERR_INVALID_ARGUMENT, "workspace: expected a 16-byte aligned pointer");
+
+  const int D = params->head_size;
+  const float scale = params->scale != 0.f ? params->scale : 1.0f / std::sqrt((float)D);
+  const bool cap = params->softcap > 0.f;
+  const float log2e = 1.4426950408889634f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const pa::SeqLayout sl = layout(params, kv);
+
+  pa::DecodeArgs d;
+  d.s = sl;
+  d.query = static_cast<const uint16_t*>(query);
+  d.key_cache = static_cast<const uint16_t*>(kv->key_cache);
+  d.value_cache = static_cast<const uint16_t*>(kv->value_cache);
+  d.cos = static_cast<const uint16_t*>(cos_cache);
+  d.sin = static_cast<const uint16_t*>(sin_cache);
+  d.out = static_cast<uint16_t*>(out);
+  d.part_o = static_cast<float*>(workspace);
+  size_t o_bytes = (size_t)pl.rows * params->num_heads * pl.max_splits * D * sizeof(float);
+  o_bytes = (o_bytes + 255) / 256 * 256;
+  d.part_ml = pl.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes)
+                          : nullptr;
+  d.num_heads = params->num_heads;
+  d.kv_heads = params->kv_num_heads;
+  d.group = pl.g;
+  d.head_chunks = pl.head_chunks;
+  d.token_mode = pl.token_mode ? 1 : 0;
+  d.split_tokens = pl.split_tokens;
+  d.max_splits = pl.max_splits;
+  d.window = params->local_window_size;
+  d.rotary_dim = params->do_rotary ? rotary_dim : 0;
+  d.rotary_interleaved = params->rotary_interleaved;
+  d.rotary_rows = params->do_rotary ? rotary_rows : 0;
+  d.score_scale = scale * log2e;
+  d.cap_in = cap ? scale / params->softcap : 0.f;
+  d.cap_out = cap ? params->softcap * log2e : 0.f;
+  d.use_softcap = cap ? 1 : 0;
+
+  if (pl.rows > 0) {
+    const dim3 grid(pl.rows, params->kv_num_heads * pl.head_chunks, pl.max_splits);
+    {
+      StageScope scope(PA_STAGE_DECODE, s);
+      if ((st = device_status(pa::launch_decode(d, D, pl.g_chunk, grid, s),
+                              "decode kernel launch")) != PA_OK)
+        return st;
+    }
+    if (pl.max_splits > 1) {
+      pa::MergeArgs mg;
+      mg.s = sl;
+      mg.part_o = d.part_o;
+      mg.part_ml = d.part_ml;
+      mg.out = d.out;
+      mg.num_heads = params->num_heads;
+      mg.head_size = D;
+      mg.token_mode = d.token_mode;
+      mg.split_tokens = pl.split_tokens;
+      mg.max_splits = pl.max_splits;
+      mg.window = params->local_window_size;
+      StageScope scope(PA_STAGE_MERGE, s);
+      if ((st = device_status(pa::launch_merge(mg, pl.rows, s), "merge kernel launch")) != PA_OK)
+        return st;
+    }
+  }
+  if (pl.prefill) {
+    pa::PrefillArgs f;
+    f.s = sl;
+    f.query = d.query;
+    f.key_cache = d.key_cache;
+    f.value_cache = d.value_cache;
+    f.cos = d.cos;
+    f.sin = d.sin;
+    f.out = d.out;
+    f.num_heads = params->num_heads;
+    f.kv_heads = params->kv_num_heads;
+    f.group = pl.g;
+    f.window = params->local_window_size;
+    f.rotary_dim = d.rotary_dim;
+    f.rotary_interleaved = d.rotary_interleaved;
+    f.rotary_rows = d.rotary_rows;
+    f.tiles = pl.prefill_tiles;
+    f.score_scale = d.score_scale;
+    f.cap_in = d.cap_in;
+    f.cap_out = d.cap_out;
+    f.use_softcap = d.use_softcap;
+    const dim3 grid(pl.prefill_tiles + 1, params->kv_num_heads);
+    StageScope scope(PA_STAGE_PREFILL, s);
+    if ((st = device_status(pa::launch_prefill(f, D, grid, s), "prefill kernel launch")) != PA_OK)
+      return st;
+  }
+  return PA_OK;
+}
+
+pa_status pa_timing_enable(int32_t max_launches) {
+  g_error.clear();
+  if (max_launches <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_launches: expected > 0, got %d", max_launches);
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (hipEvent_t e : g_timing.events) hipEventDestroy(e);
+  g_timing.events.assign(2 * (size_t)max_launches, nullptr);
+  g_timing.stage.assign(max_launches, -1);
+  g_timing.used = 0;
+  for (auto& e : g_timing.events) {
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      g_timing.enabled = false;
+      return fail(PA_ERR_DEVICE, "hipEventCreate: %s", hipGetErrorString(err));
+    }
+  }
+  g_timing.enabled = true;
+  return PA_OK;
+}
+
+pa_status pa_timing_disable(void) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (hipEvent_t e : g_timing.events) hipEventDestroy(e);
+  g_timing.events.clear();
+  g_timing.stage.clear();
+  g_timing.used = 0;
+  g_timing.enabled = false;
+  return PA_OK;
+}
+
+pa_status pa_timing_read(int32_t stage, double* total_ms, int32_t* launches) {
+  g_error.clear();
+  if (!total_ms || !launches)
+    return fail(PA_ERR_INVALID_ARGUMENT, "total_ms/launches: expected non-NULL");
+  if (stage < 0 || stage >= PA_NUM_STAGES)
+    return fail(PA_ERR_INVALID_ARGUMENT, "stage: expected 0..%d, got %d", PA_NUM_STAGES - 1, stage);
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  double tot = 0.0;
+  int n = 0;
+  for (size_t i = 0; i < g_timing.used; ++i) {
+    if (g_timing.stage[i] != stage) continue;
+    hipError_t e = hipEventSynchronize(g_timing.events[2 * i + 1]);
+    if (e != hipSuccess) return fail(PA_ERR_DEVICE, "hipEventSynchronize: %s", hipGetErrorString(e));
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_timing.events[2 * i], g_timing.events[2 * i + 1]);
+    if (e != hipSuccess) return fail(PA_ERR_DEVICE, "hipEventElapsedTime: %s", hipGetErrorString(e));
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return PA_OK;
+}
+
+}  // extern "C"

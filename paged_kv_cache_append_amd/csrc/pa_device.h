@@ -1,0 +1,136 @@
+// Device helpers for the gfx950 kernels: fp16 packing, fast exp2 / tanh,
+// wave reductions, and token -> request resolution.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// tanh from its exponential form: tanh|x| = 1 - 2 / (exp(2|x|) + 1).
+// Absolute error ~1e-7, which the softcap multiplies by at most `softcap`.
+__device__ __forceinline__ float tanh_fast(float x) {
+  float e = exp2_fast(fabsf(x) * (2.0f * kLog2e));
+  float r = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  return copysignf(r, x);
+}
+
+__device__ __forceinline__ float h2f(uint16_t b) {
+  _Float16 h;
+  __builtin_memcpy(&h, &b, 2);
+  return (float)h;
+}
+
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default mode).
+__device__ __forceinline__ uint16_t f2h(float f) {
+  _Float16 h = (_Float16)f;
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+
+__device__ __forceinline__ h8 as_h8(u32x4 v) {
+  h8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void store16(uint16_t* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Which request owns packed token t: the largest b with cum[b] <= t.
+// Returns -1 when t >= cum[B] (PagedAttention -- CUDA Design Document,
+// section 18.2: such tokens own nothing).
+__device__ __forceinline__ int find_request(const int32_t* cum, int B, int t) {
+  if (t >= cum[B]) return -1;
+  int lo = 0, hi = B - 1;  // invariant: cum[lo] <= t (cum[0] = 0 by contract)
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cum[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Pool element offset of (block, offset-in-block, kv head, channel 0).
+__device__ __forceinline__ int64_t slot_base(int64_t blk, int off, int kvh, int block_size,
+                                             int kv_heads, int head_size) {
+  return ((blk * block_size + off) * kv_heads + kvh) * (int64_t)head_size;
+}
+
+// Rotary embedding of channels [8c, 8c+8) of one head row at position `pos`.
+// `row` points at channel 0 of the head (global fp16), `own` holds the chunk.
+// Pairs are (i, i + r/2) (rotate-half) or (2i, 2i+1) (interleaved) with angle
+// index i; first' = x*cos - y*sin, second' = y*cos + x*sin; channels >= r pass
+// through.  Both products of fp16 values are exact in fp32, so the fused
+// multiply-add below rounds the exact result once -- the stored key is then
+// fp16(fp32(exact)).  Positions outside the table are not rotated (memory
+// safety for out-of-contract device lengths).
+__device__ __forceinline__ void rotate_chunk(const uint16_t* row, u32x4 own, int c, int pos,
+                                             const uint16_t* cos_t, const uint16_t* sin_t,
+                                             int rot, int interleaved, int rot_rows,
+                                             float out[8]) {
+  uint16_t x16[8];
+  __builtin_memcpy(x16, &own, 16);
+  const int half = rot >> 1;
+  const bool in_table = pos >= 0 && pos < rot_rows;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = 8 * c + e;
+    const float x = h2f(x16[e]);
+    if (d >= rot || !in_table) {
+      out[e] = x;
+      continue;
+    }
+    int i;
+    bool second;
+    float y;
+    if (interleaved) {
+      i = d >> 1;
+      second = (d & 1) != 0;
+      y = h2f(x16[e ^ 1]);
+    } else {
+      second = d >= half;
+      i = second ? d - half : d;
+      y = h2f(row[second ? d - half : d + half]);
+    }
+    const int64_t ti = (int64_t)pos * half + i;
+    const float cs = h2f(cos_t[ti]);
+    const float sn = h2f(sin_t[ti]);
+    const float ys = y * sn;  // exact
+    out[e] = second ? __builtin_fmaf(x, cs, ys) : __builtin_fmaf(x, cs, -ys);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float f[8]) {
+  uint16_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = f2h(f[e]);
+  u32x4 r;
+  __builtin_memcpy(&r, h, 16);
+  return r;
+}
+
+template <int W>
+__device__ __forceinline__ float xor_sum(float v) {
+#pragma unroll
+  for (int m = W / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+}  // namespace pa

@@ -327,3 +327,73 @@ def scaled_down(name: str, poison: bool = False) -> Workload:
                           do_rotary=1, rotary_interleaved=0, rotary_dim=64, rng=rng,
                           poison=poison)
     raise KeyError(name)
+
+
+# ---------------------------------------------------------------------------
+# device upload (PyTorch is only the memory allocator here)
+# ---------------------------------------------------------------------------
+
+def to_device(w: Workload, device="cuda", pools: bool = True, threads: Optional[int] = None):
+    """Copy a workload's host arrays to device tensors.  Pools are streamed
+    chunk by chunk so the host never holds a whole pool."""
+    import torch
+    d = {
+        "query": torch.from_numpy(w.query).to(device),
+        "key": torch.from_numpy(w.key).to(device),
+        "value": torch.from_numpy(w.value).to(device),
+        "cum": torch.from_numpy(w.cum).to(device),
+        "past": torch.from_numpy(w.past).to(device),
+        "block_table": torch.from_numpy(np.ascontiguousarray(w.block_table)).to(device),
+        "cos": None,
+        "sin": None,
+    }
+    if w.cos_cache is not None:
+        d["cos"] = torch.from_numpy(w.cos_cache).to(device)
+        d["sin"] = torch.from_numpy(w.sin_cache).to(device)
+    if pools:
+        for kind, name in ((KIND_K, "key_cache"), (KIND_V, "value_cache")):
+            dev = torch.empty(w.pool_shape(), dtype=torch.float16, device=device)
+
+            def sink(start, arr, dev=dev):
+                dev[start:start + arr.shape[0]].copy_(torch.from_numpy(arr))
+
+            fill_pool_chunks(w, kind, None, threads=threads, sink=sink)
+            d[name] = dev
+    return d
+
+
+def subset(w: Workload, seqs: Sequence[int]) -> Workload:
+    """A workload holding only requests ``seqs`` of ``w`` with their blocks
+    renumbered into a compact pool (contents re-drawn from ``w``'s generator,
+    so they are identical).  Used to run the oracle on a sample of a large
+    workload."""
+    seqs = [int(s) for s in seqs]
+    ids = sorted({int(x) for s in seqs for x in w.block_table[s] if x >= 0})
+    remap = {old: new for new, old in enumerate(ids)}
+    table = np.full((len(seqs), w.max_blocks_per_seq), -1, np.int32)
+    for r, s in enumerate(seqs):
+        for i, x in enumerate(w.block_table[s]):
+            if x >= 0:
+                table[r, i] = remap[int(x)]
+    q_lens = w.q_lens[seqs]
+    cum = np.zeros(len(seqs) + 1, np.int32)
+    cum[1:] = np.cumsum(q_lens)
+    rows = np.concatenate([np.arange(w.cum[s], w.cum[s + 1]) for s in seqs]) if len(seqs) else \
+        np.zeros(0, np.int64)
+    sub = Workload(name=w.name + "_subset", seed=w.seed, num_heads=w.num_heads,
+                   kv_num_heads=w.kv_num_heads, head_size=w.head_size, block_size=w.block_size,
+                   scale=w.scale, softcap=w.softcap, local_window_size=w.local_window_size,
+                   do_rotary=w.do_rotary, rotary_interleaved=w.rotary_interleaved, cum=cum,
+                   past=w.past[seqs].copy(), block_table=table, num_blocks=max(1, len(ids)),
+                   query=w.query[rows], key=w.key[rows], value=w.value[rows],
+                   cos_cache=w.cos_cache, sin_cache=w.sin_cache, kv_sigma=w.kv_sigma,
+                   poison=w.poison)
+    parent = w
+
+    def pool_blocks(kind, bid, _ids=ids, _p=parent):
+        return _p.pool_blocks(kind, [_ids[i] for i in bid])
+
+    sub.pool_blocks = pool_blocks
+    sub.extra["parent_rows"] = rows
+    sub.extra["parent_block_ids"] = ids
+    return sub

@@ -1,0 +1,188 @@
+"""C-ABI tests that need no GPU: the library loads, exports every entry point
+declared in include/pa.h, and rejects each malformed request with the status
+and message the header documents (PagedAttention -- CUDA Design Document,
+section 15: every violation names the offending argument).  No call here
+reaches a HIP runtime function: only validation and host planning run."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_append_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # 16-byte aligned address, never dereferenced on the host
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libpa.so not built (run __graft_entry__.build())")
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:pa_status|size_t|const char \*)\s*(pa_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for name in ("pa_append_kv", "pa_forward", "pa_forward_workspace_bytes", "pa_last_error"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert set(header_functions()) == set(_lib.EXPORTED)
+
+
+def params(**kw):
+    d = dict(num_heads=8, kv_num_heads=2, head_size=64, block_size=16, scale=0.0, softcap=0.0,
+             local_window_size=-1, do_rotary=0, rotary_interleaved=0, path=0, split_tokens=0)
+    d.update(kw)
+    return _lib.AttnParams(*[d[f] for f, _ in _lib.AttnParams._fields_])
+
+
+def paged(**kw):
+    d = dict(key_cache=FAKE, value_cache=FAKE, num_blocks=32, block_table=FAKE,
+             max_blocks_per_seq=8, cumulative_sequence_length=FAKE, past_seqlens=FAKE,
+             batch_size=4, token_count=4)
+    d.update(kw)
+    return _lib.PagedKV(*[d[f] for f, _ in _lib.PagedKV._fields_])
+
+
+def call_forward(p, kv, query=FAKE, cos=None, sin=None, rows=0, rdim=0, mq=0, mk=0, ws=None,
+                 ws_len=0, out=FAKE):
+    lib = _lib.load()
+    return lib.pa_forward(ctypes.byref(p), ctypes.byref(kv), query, cos, sin, rows, rdim, mq, mk,
+                          ws, ws_len, out, None)
+
+
+def call_append(p, kv, key=FAKE, value=FAKE, cos=None, sin=None, rows=0, rdim=0):
+    lib = _lib.load()
+    return lib.pa_append_kv(ctypes.byref(p), ctypes.byref(kv), key, value, cos, sin, rows, rdim,
+                            None)
+
+
+def err():
+    return _lib.load().pa_last_error().decode()
+
+
+NEGATIVE = [
+    # (params overrides, kv overrides, expected status, message fragment)
+    (dict(num_heads=0), {}, 1, "num_heads"),
+    (dict(kv_num_heads=0), {}, 1, "kv_num_heads"),
+    (dict(num_heads=6, kv_num_heads=4), {}, 1, "multiple of kv_num_heads"),
+    (dict(head_size=60), {}, 1, "head_size"),
+    (dict(block_size=24), {}, 1, "block_size"),
+    (dict(block_size=8), {}, 1, "block_size"),
+    (dict(scale=float("inf")), {}, 1, "scale"),
+    (dict(softcap=-1.0), {}, 1, "softcap"),
+    (dict(softcap=float("nan")), {}, 1, "softcap"),
+    (dict(local_window_size=0), {}, 1, "local_window_size"),
+    (dict(local_window_size=-2), {}, 1, "local_window_size"),
+    (dict(do_rotary=2), {}, 1, "do_rotary"),
+    (dict(rotary_interleaved=3), {}, 1, "rotary_interleaved"),
+    (dict(path=3), {}, 1, "path"),
+    (dict(split_tokens=100), {}, 1, "split_tokens"),
+    ({}, dict(batch_size=0), 1, "batch_size"),
+    ({}, dict(token_count=-1), 1, "token_count"),
+    ({}, dict(num_blocks=0), 1, "num_blocks"),
+    ({}, dict(max_blocks_per_seq=0), 1, "max_blocks_per_seq"),
+    ({}, dict(key_cache=None), 1, "key_cache"),
+    ({}, dict(value_cache=FAKE + 8), 1, "16-byte"),
+    ({}, dict(block_table=None), 1, "block_table"),
+    ({}, dict(cumulative_sequence_length=None), 1, "cumulative_sequence_length"),
+    ({}, dict(past_seqlens=None), 1, "past_seqlens"),
+]
+
+
+@pytest.mark.parametrize("pk,kk,status,frag", NEGATIVE)
+def test_validation_rule(pk, kk, status, frag):
+    for call in (call_forward, call_append):
+        st = call(params(**pk), paged(**kk))
+        assert st == status, (call.__name__, err())
+        assert frag in err(), err()
+
+
+def test_rotary_rules():
+    kv = paged()
+    p = params(do_rotary=1)
+    assert call_forward(p, kv) == 1 and "required when do_rotary" in err()
+    assert call_append(p, kv, cos=FAKE) == 1 and "both or neither" in err()
+    assert call_forward(p, kv, cos=FAKE, sin=FAKE, rows=128, rdim=66) == 1 and "rotary_dim" in err()
+    assert call_forward(p, kv, cos=FAKE, sin=FAKE, rows=128, rdim=7) == 1 and "rotary_dim" in err()
+    assert call_forward(p, kv, cos=FAKE, sin=FAKE, rows=127, rdim=64) == 1 and "rotary_rows" in err()
+    assert call_append(params(), kv, cos=FAKE, sin=FAKE, rows=128, rdim=64) == 1 \
+        and "do_rotary = 0" in err()
+
+
+def test_forward_buffer_rules():
+    kv = paged()
+    assert call_forward(params(), kv, query=None) == 1 and "query" in err()
+    assert call_forward(params(), kv, out=None) == 1 and "out" in err()
+    assert call_forward(params(), kv, query=FAKE + 2) == 1 and "16-byte" in err()
+    assert call_append(params(), kv, key=None) == 1 and "key/value" in err()
+    assert call_forward(params(), kv, mq=-1) == 1 and "bound" in err()
+
+
+def test_unsupported_head_size_is_reported():
+    assert call_forward(params(head_size=96), paged()) == 2
+    assert "head_size 96" in err()
+
+
+def test_workspace_must_cover_the_plan():
+    lib = _lib.load()
+    p, kv = params(), paged(token_count=64, batch_size=64, max_blocks_per_seq=1024)
+    n = ctypes.c_size_t(0)
+    assert lib.pa_forward_workspace_bytes(ctypes.byref(p), ctypes.byref(kv), 0, 0,
+                                          ctypes.byref(n)) == 0
+    assert n.value > 0
+    assert call_forward(p, kv, ws=FAKE, ws_len=n.value - 1) == 1 and "workspace_bytes" in err()
+    assert call_forward(p, kv, ws=None, ws_len=n.value) == 1 and "workspace" in err()
+
+
+def test_zero_tokens_is_a_no_op():
+    kv = paged(token_count=0)
+    assert call_forward(params(), kv, query=None, out=None) == 0
+    assert call_append(params(), kv, key=None, value=None) == 0
+
+
+def plan(p, kv, mq=0, mk=0):
+    lib = _lib.load()
+    buf = ctypes.create_string_buffer(512)
+    assert lib.pa_describe_plan(ctypes.byref(p), ctypes.byref(kv), mq, mk, buf, 512) == 0, err()
+    return dict(kv.split("=", 1) for kv in buf.value.decode().split())
+
+
+def test_plan_static_shape_test():
+    """token_count <= batch_size selects the decode kernel for every token;
+    otherwise requests of one token go to decode and the rest to prefill."""
+    assert plan(params(), paged(token_count=4, batch_size=4))["mode"] == "token"
+    pl = plan(params(), paged(token_count=40, batch_size=4))
+    assert pl["mode"] == "request" and pl["prefill_grid"] != "(0,0)"
+    assert plan(params(path=1), paged(token_count=40, batch_size=4))["mode"] == "token"
+    assert plan(params(path=2), paged(token_count=4, batch_size=4))["mode"] == "request"
+
+
+def test_plan_split_length_ignores_bounds():
+    """Bounds only trim the grid and workspace: the split length (and so the
+    arithmetic of every row) is the same with no, tight or loose bounds."""
+    p, kv = params(), paged(token_count=8, batch_size=8, max_blocks_per_seq=512)
+    a, b, c = plan(p, kv), plan(p, kv, 1, 3000), plan(p, kv, 10 ** 6, 10 ** 8)
+    assert a["split_tokens"] == b["split_tokens"] == c["split_tokens"]
+    assert int(b["max_splits"]) <= int(a["max_splits"]) == int(c["max_splits"])
+
+
+def test_plan_window_caps_splits():
+    p = params(local_window_size=100)
+    pl = plan(p, paged(token_count=2, batch_size=2, max_blocks_per_seq=4096))
+    assert int(pl["max_splits"]) * int(pl["split_tokens"]) < 100 + int(pl["split_tokens"])
+
+
+def test_plan_group_chunks():
+    pl = plan(params(num_heads=24, kv_num_heads=2), paged())      # g = 12 -> chunks of 4
+    assert pl["g"] == "12" and pl["g_chunk"] == "4"
+    pl = plan(params(num_heads=64, kv_num_heads=2), paged())      # g = 32 -> chunks of 8
+    assert pl["g_chunk"] == "8"

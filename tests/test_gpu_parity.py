@@ -1,0 +1,127 @@
+"""GPU parity of the HIP path against the fp64 oracle on sizes the oracle
+finishes in seconds (several tiles, ragged tails): the append must be
+bit-exact (the whole pool, written and untouched slots) and every output row
+within 2e-3 max-abs of the oracle.  Each case runs on the three routings of
+pa_forward (automatic, decode kernel for every token, decode + prefill)."""
+import numpy as np
+import pytest
+
+from paged_kv_cache_append_amd import workloads as wl
+
+from pa_harness import TOL, gpu_forward, gpu_step, max_err, oracle_append, oracle_forward
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [0, 1, 2]
+
+
+def check(w, path=0, rows=None, **over):
+    print(f"\n[case] {w.name} B={w.batch_size} T={w.token_count} H={w.num_heads} "
+          f"Hkv={w.kv_num_heads} D={w.head_size} bs={w.block_size} W={w.local_window_size} "
+          f"softcap={w.softcap} rot={w.do_rotary}/{w.rotary_interleaved} path={path} {over}",
+          flush=True)
+    dev, out = gpu_step(w, path=path, **over)
+    nk, nv = oracle_append(w)
+    gk = dev["key_cache"].cpu().numpy()
+    gv = dev["value_cache"].cpu().numpy()
+    assert gk.tobytes() == nk.tobytes(), "key pool differs from the oracle append"
+    assert gv.tobytes() == nv.tobytes(), "value pool differs from the oracle append"
+    ref = oracle_forward(w, nk, nv)
+    err = max_err(out, ref)
+    print(f"[case] max_abs_err={err:.3e}", flush=True)
+    assert err <= TOL, err
+    return out, ref
+
+
+@pytest.mark.parametrize("name", wl.CONFIG_NAMES)
+@pytest.mark.parametrize("path", PATHS)
+def test_scaled_configs(name, path):
+    check(wl.scaled_down(name), path)
+
+
+SWEEP = [
+    # q_lens, past, H, Hkv, D, bs, extra kwargs
+    ([1, 1, 1], [0, 15, 40], 8, 8, 64, 16, {}),                          # MHA (g = 1)
+    ([1, 1], [16, 17], 8, 1, 64, 16, {}),                                # MQA (g = 8)
+    ([5, 17], [0, 0], 4, 2, 128, 16, {}),                                # fresh prefill
+    ([5, 2, 17], [1, 16, 40], 4, 2, 64, 32, {}),                         # chunked prefill
+    ([17, 1, 0, 2], [15, 3, 9, 0], 4, 4, 64, 16, {}),                    # ragged, q_len 0
+    ([9, 1], [20, 33], 4, 2, 128, 16, dict(local_window_size=5)),
+    ([130, 1, 3], [300, 1000, 64], 6, 2, 256, 16,                        # g = 3 (chunks of 1)
+     dict(local_window_size=200, softcap=5.0)),
+    ([1, 1, 1, 1, 1], [900, 1, 77, 600, 2], 24, 2, 128, 16, dict(softcap=1.0)),   # g = 12
+    ([3, 1, 40], [70, 129, 0], 8, 2, 64, 16,
+     dict(do_rotary=1, rotary_interleaved=1, rotary_dim=32)),
+    ([3, 1, 40], [70, 129, 0], 8, 2, 64, 16, dict(do_rotary=1, rotary_dim=20)),
+    ([200], [0], 2, 1, 64, 64, dict(local_window_size=1)),
+    ([1, 1, 1, 70], [5000, 20, 0, 3000], 8, 2, 64, 16, {}),              # several splits
+    ([64, 1], [4000, 7000], 16, 8, 256, 16, dict(local_window_size=4096, softcap=50.0)),
+    ([33, 2, 1], [1, 2, 3], 32, 8, 128, 128, dict(scale=0.3)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SWEEP)))
+@pytest.mark.parametrize("path", PATHS)
+def test_sweep(case, path):
+    q_lens, past, H, Hkv, D, bs, kw = SWEEP[case]
+    w = wl.build_case(f"sweep{case}", 500 + case, q_lens=q_lens, past=past, num_heads=H,
+                      kv_num_heads=Hkv, head_size=D, block_size=bs, **kw)
+    check(w, path)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_poisoned_pool(path):
+    """Every slot the runtime has not filled is NaN (and unused blocks are
+    NaN): reading any key past a request's length, or weighting a NaN value
+    row by zero, shows up as a non-finite or wrong output."""
+    w = wl.build_case("poison", 77, q_lens=[1, 9, 1, 33], past=[45, 17, 300, 0], num_heads=8,
+                      kv_num_heads=2, head_size=128, block_size=16, extra_blocks_per_seq=2,
+                      poison=True, softcap=20.0)
+    check(w, path)
+
+
+@pytest.mark.parametrize("path", [0, 2])
+def test_tokens_owned_by_no_request(path):
+    w = wl.build_case("orphans", 78, q_lens=[2, 1, 5], past=[10, 40, 0], num_heads=4,
+                      kv_num_heads=2, head_size=64, block_size=16, extra_tokens=3)
+    out, ref = check(w, path)
+    assert np.all(out[-3:] == 0)
+
+
+def test_split_length_changes_only_rounding():
+    w = wl.build_case("splits", 79, q_lens=[1, 1, 1], past=[6000, 1500, 90], num_heads=8,
+                      kv_num_heads=1, head_size=64, block_size=32)
+    outs = [check(w, 1, split_tokens=st)[0] for st in (0, 64, 192, 1024, 8192)]
+    for o in outs[1:]:
+        assert np.max(np.abs(o.astype(np.float64) - outs[0])) <= 1e-3
+
+
+def test_bounds_do_not_change_results():
+    """No bounds, tight bounds and loose bounds give bitwise-identical output
+    (bounds only size launches and workspace)."""
+    import torch
+    w = wl.build_case("bounds", 80, q_lens=[1, 1, 20, 1], past=[3000, 10, 700, 1200], num_heads=8,
+                      kv_num_heads=2, head_size=128, block_size=16)
+    dev, base = gpu_step(w, path=2)
+    mq = int(w.q_lens.max())
+    mk = int((w.past + w.q_lens).max())
+    for bq, bk in ((mq, mk), (10 * mq, 10 * mk), (0, mk), (mq, 0)):
+        o = gpu_forward(w, dev, mq=bq, mk=bk, path=2)
+        torch.cuda.synchronize()
+        assert o.cpu().numpy().tobytes() == base.tobytes(), (bq, bk)
+
+
+def test_batch_order_permutation():
+    w = wl.build_case("perm", 81, q_lens=[1, 7, 1, 3], past=[100, 30, 5, 64], num_heads=4,
+                      kv_num_heads=2, head_size=64, block_size=16)
+    _, out = gpu_step(w, path=2)
+    order = [2, 0, 3, 1]
+    rows = np.concatenate([np.arange(w.cum[b], w.cum[b + 1]) for b in order])
+    w2 = wl.build_case("perm", 81, q_lens=[1, 7, 1, 3], past=[100, 30, 5, 64], num_heads=4,
+                       kv_num_heads=2, head_size=64, block_size=16)
+    w2.cum = np.concatenate([[0], np.cumsum(w.q_lens[order])]).astype(np.int32)
+    w2.past = w.past[order].copy()
+    w2.block_table = w.block_table[order].copy()
+    w2.query, w2.key, w2.value = w.query[rows], w.key[rows], w.value[rows]
+    _, out2 = gpu_step(w2, path=2)
+    assert np.max(np.abs(out2.astype(np.float64) - out[rows])) <= 1e-3
