@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of one paged-attention step (KV append + forward) on one GPU.
+
+A step is the whole hot path over one batch: token -> request resolution,
+slot derivation, rotary (when the workload has it), the KV append, the
+split-KV decode + merge and the MFMA prefill.  Inputs are synthetic and
+already resident in device memory when the timed region starts.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+Prints ONE JSON line.  ``value`` is the decode KV throughput of the whole
+step (algorithmic decode bytes / step time).  ``roofline`` describes the
+dominant kernel (per-launch algorithmic bytes or FLOPs over its average
+launch time, from HIP events recorded around each launch on its stream).
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode KV GB/s (% HBM peak); prefill attention TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16 MFMA
+DEFAULT_CONFIG = "llama3_8b_mixed"
+
+
+def algorithmic_work(w):
+    """Decode bytes (K+V of every decode row's admitted keys, once per kv head,
+    plus its Q and O rows) and prefill FLOPs (4*D*H per admitted pair)."""
+    H, Hkv, D = w.num_heads, w.kv_num_heads, w.head_size
+    q_lens = w.q_lens
+    dec_bytes = 0
+    pf_pairs = 0
+    n_dec = 0
+    W = w.local_window_size
+    for b in range(w.batch_size):
+        ql = int(q_lens[b])
+        past = int(w.past[b])
+        if ql == 1:
+            kv = past + 1
+            if W > 0:
+                kv = min(kv, W)
+            dec_bytes += kv * Hkv * D * 2 * 2 + 2 * H * D * 2
+            n_dec += 1
+        elif ql > 1:
+            for j in range(ql):
+                pos = past + j
+                lo = max(0, pos - W + 1) if W > 0 else 0
+                pf_pairs += pos + 1 - lo
+    return dec_bytes, 4.0 * D * H * pf_pairs, n_dec
+
+
+def traffic_from_profiles(kernel_tag: str, src_hash: str):
+    """HBM bytes per launch measured by rocprofv3 counters (committed summary),
+    or None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data.get(kernel_tag)
+        if not ent or ent.get("source_sha256") != src_hash:
+            return None
+        return ent.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_append_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=96):
+    """fp64 oracle on a bounded sample of the workload: the decode requests
+    (GB/s of decode K/V bytes) or, for a prefill-only batch, the last rows of
+    the first request (GFLOP/s).  Also returns the max-abs error of the GPU
+    rows the sample covers."""
+    import threadpoolctl
+
+    import oracle
+    from paged_kv_cache_append_amd import workloads as wl
+    dec = [b for b in range(w.batch_size) if int(w.q_lens[b]) == 1][:decode_rows_sample]
+    prefill = not dec
+    seqs = dec if dec else [0]
+    sub = wl.subset(w, seqs)
+    kc = sub.pool_blocks(wl.KIND_K, range(sub.num_blocks))
+    vc = sub.pool_blocks(wl.KIND_V, range(sub.num_blocks))
+    rot = dict(cos_cache=sub.cos_cache, sin_cache=sub.sin_cache,
+               rotary_interleaved=bool(sub.rotary_interleaved)) if sub.do_rotary else {}
+    nk, nv = oracle.append_kv(kc, vc, sub.key, sub.value, sub.cum, sub.past, sub.block_table,
+                              kv_num_heads=sub.kv_num_heads, head_size=sub.head_size, **rot)
+    threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
+                  if i.get("user_api") == "blas") or 1
+    rows = None
+    if prefill:
+        ql = int(sub.q_lens[0])
+        rows = list(range(max(0, ql - prefill_rows_sample), ql))
+    t0 = time.perf_counter()
+    ref = oracle.forward(sub.query, nk, nv, sub.cum, sub.past, sub.block_table,
+                         num_heads=sub.num_heads, kv_num_heads=sub.kv_num_heads,
+                         head_size=sub.head_size, scale=sub.scale, softcap=sub.softcap,
+                         local_window_size=sub.local_window_size, rows=rows, **rot)
+    dt = time.perf_counter() - t0
+    prow = sub.extra["parent_rows"]
+    if prefill:
+        W = sub.local_window_size
+        pairs = 0
+        for j in rows:
+            pos = int(sub.past[0]) + j
+            pairs += pos + 1 - (max(0, pos - W + 1) if W > 0 else 0)
+        flops = 4.0 * sub.head_size * sub.num_heads * pairs
+        err = float(np.max(np.abs(gpu_out[prow[rows]].astype(np.float64) - ref)))
+        return {"value": round(flops / dt / 1e9, 4), "unit": "GFLOP/s", "cores": int(threads),
+                "kind": "oracle",
+                "sample": f"last {len(rows)} query rows of request 0 of {w.name} "
+                          f"({flops / 1e9:.2f} GFLOP over admitted pairs), full fp64 score "
+                          f"rows + softmax + PV, {dt:.1f} s"}, err
+    nbytes, _, _ = algorithmic_work(sub)
+    err = float(np.max(np.abs(gpu_out[prow].astype(np.float64) - ref)))
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(dec)} decode requests of {w.name} ({nbytes / 1e6:.1f} MB of K/V+Q/O), "
+                      f"gather + full scores + softmax + PV in fp64, {dt:.1f} s"}, err
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_append_amd as pa
+    from paged_kv_cache_append_amd import workloads as wl
+
+    w = wl.make_workload(args.config)
+    dev = wl.to_device(w)
+    a = pa.Attn(num_heads=w.num_heads, kv_num_heads=w.kv_num_heads, head_size=w.head_size,
+                block_size=w.block_size, scale=w.scale, softcap=w.softcap,
+                local_window_size=w.local_window_size, do_rotary=w.do_rotary,
+                rotary_interleaved=w.rotary_interleaved)
+    T = w.token_count
+    out = torch.empty((T, w.num_heads * w.head_size), dtype=torch.float16, device="cuda")
+    nws = pa.forward_workspace_bytes(a, dev["key_cache"], dev["value_cache"], dev["block_table"],
+                                     dev["cum"], dev["past"], T)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    plan = pa.describe_plan(a, dev["key_cache"], dev["value_cache"], dev["block_table"],
+                            dev["cum"], dev["past"], T)
+
+    def step():
+        pa.append_kv(a, dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
+                     dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"])
+        pa.forward(a, dev["query"], dev["key_cache"], dev["value_cache"], dev["block_table"],
+                   dev["cum"], dev["past"], dev["cos"], dev["sin"], workspace=ws, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    pa.timing_enable(8 * args.steps + 16)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    stages = {s: pa.timing_read(s) for s in ("append", "decode", "merge", "prefill")}
+    pa.timing_disable()
+    ms_step = ms_total / args.steps
+
+    dec_bytes, pf_flops, n_dec = algorithmic_work(w)
+    per = {s: (ms / n * 1e3 if n else 0.0) for s, (ms, n) in stages.items()}   # us per launch
+    if dec_bytes:
+        value, unit = dec_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
+    else:
+        value, unit = pf_flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
+    kernels = {f"{s}_us": round(v, 3) for s, v in per.items()}
+    if per["decode"]:
+        kernels["decode_kernel_gbs"] = round(dec_bytes / (per["decode"] * 1e-6) / 1e9, 1)
+    if per["prefill"] and pf_flops:
+        kernels["prefill_kernel_tflops"] = round(pf_flops / (per["prefill"] * 1e-6) / 1e12, 2)
+    step_frac = (dec_bytes / (HBM_PEAK_GBS * 1e9) + pf_flops / (MFMA_F16_PEAK_TFS * 1e12)) / \
+        (ms_step * 1e-3)
+
+    # dominant kernel: the one with the larger roofline time
+    src_hash = kernel_source_hash()
+    if dec_bytes / (HBM_PEAK_GBS * 1e9) >= pf_flops / (MFMA_F16_PEAK_TFS * 1e12):
+        achieved = dec_bytes / (per["decode"] * 1e-6) / 1e9 if per["decode"] else None
+        roof = {"bound": "hbm", "kernel": "decode", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+                "traffic": traffic_from_profiles(f"decode:{w.name}", src_hash),
+                "algorithmic_bytes_per_launch": dec_bytes}
+    else:
+        achieved = pf_flops / (per["prefill"] * 1e-6) / 1e12 if per["prefill"] else None
+        roof = {"bound": "mfma", "kernel": "prefill", "achieved": achieved,
+                "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": (achieved / MFMA_F16_PEAK_TFS) if achieved else None,
+                "traffic": traffic_from_profiles(f"prefill:{w.name}", src_hash),
+                "algorithmic_flops_per_launch": pf_flops}
+    for k in ("achieved", "frac"):
+        if roof[k] is not None:
+            roof[k] = round(roof[k], 4)
+
+    cpu, err = (None, None)
+    if not args.no_cpu_baseline:
+        cpu, err = cpu_baseline(w, out.cpu().numpy())
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch_size, "tokens": T,
+                   "num_heads": w.num_heads, "kv_num_heads": w.kv_num_heads,
+                   "head_size": w.head_size, "block_size": w.block_size,
+                   "decode_requests": n_dec, "decode_bytes": dec_bytes,
+                   "prefill_flops": pf_flops, "plan": plan},
+        "roofline": roof,
+        "step_roofline_frac": round(step_frac, 4),
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "parity_max_abs_err_sampled": err,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
