@@ -169,10 +169,11 @@ pa_status pa_describe_plan(const pa_attn_params *params, const pa_paged_kv *kv,
  * same stream) and pa_timing_read() sums their elapsed times per stage
  * (synchronizing on the recorded events).  Enabling creates the events
  * (2 * max_launches); it is not meant for graph capture.
- *   stage: 0 = append, 1 = decode, 2 = split merge, 3 = prefill.
+ *   stage: 0 = append, 1 = decode, 2 = split merge, 3 = prefill,
+ *          4 = decode work-list planning.
  */
 enum { PA_STAGE_APPEND = 0, PA_STAGE_DECODE = 1, PA_STAGE_MERGE = 2, PA_STAGE_PREFILL = 3,
-       PA_NUM_STAGES = 4 };
+       PA_STAGE_PLAN = 4, PA_NUM_STAGES = 5 };
 pa_status pa_timing_enable(int32_t max_launches);
 pa_status pa_timing_disable(void);
 pa_status pa_timing_read(int32_t stage, double *total_ms, int32_t *launches);

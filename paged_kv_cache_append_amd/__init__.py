@@ -191,7 +191,7 @@ def timing_disable() -> None:
 
 def timing_read(stage: str):
     """(total milliseconds, launches) recorded for ``stage`` in
-    {append, decode, merge, prefill}."""
+    {append, decode, merge, prefill, plan}."""
     lib = _lib.load()
     ms = ctypes.c_double(0)
     n = ctypes.c_int32(0)

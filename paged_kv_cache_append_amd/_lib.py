@@ -12,7 +12,7 @@ PA_ERR_INVALID_ARGUMENT = 1
 PA_ERR_UNSUPPORTED = 2
 PA_ERR_DEVICE = 3
 
-STAGES = {"append": 0, "decode": 1, "merge": 2, "prefill": 3}
+STAGES = {"append": 0, "decode": 1, "merge": 2, "prefill": 3, "plan": 4}
 
 EXPORTED = ("pa_append_kv", "pa_forward_workspace_bytes", "pa_forward", "pa_last_error",
             "pa_describe_plan", "pa_timing_enable", "pa_timing_disable", "pa_timing_read")

@@ -1,26 +1,30 @@
-// Split-KV decode over the paged pool, plus the log-sum-exp merge of splits.
+// Split-KV decode over the paged pool, its work-list planner and the
+// log-sum-exp merge of splits.
 //
 // Work decomposition (GroupQueryAttention CPU Implementation Notes, "Flash
 // Decoding": partials (m, l, o) per KV chunk, merged with exp(m_c - M)
 // weights; PagedAttention -- CUDA Design Document, section 8.5 implementation
-// note: the decode kernel resolves each token's request on the device and reads
-// pages in place; section 9.3.4 item 2: splits laid over the window-clamped
-// interval [max(0, kv_len - W), kv_len)).
+// note: each token's request is resolved on the device and pages are read in
+// place; section 9.3.4 item 2: splits laid over the window-clamped interval
+// [max(0, kv_len - W), kv_len); section 4.7: empty splits never reach the host).
 //
-// One workgroup (4 waves) owns (row, kv head, split) and serves all G query
-// heads of the group, so each K/V byte of the split is read from HBM exactly
-// once.  A token's D-channel row is spread over D/8 lanes, each holding one
-// 16-byte chunk; a wave therefore covers 64/(D/8) tokens per load instruction
-// and every token row is a contiguous 2*D-byte run of the NHD pool.  The lane
-// keeps its G query chunks in registers (fp16 pairs for v_dot2_f32_f16), the
-// per-token partial dot products are summed across the D/8 lanes with DPP row
-// operations, and each lane group runs its own online softmax (running max,
-// sum and unnormalised output for its 8 channels).  The block-table slice of
-// the split is staged in LDS; K/V loads for the next group of tokens are
-// issued before the current group is consumed.  At the end the lane groups and
-// waves are merged (LDS), and the split either writes the fp16 row (single
-// split) or its partial (m, l, o) for the merge kernel.  Scores are kept in
-// log2 units (scale * log2 e folded in) so every exponential is one exp2.
+// Each wave is an independent worker that owns one item: (row, kv head, head
+// chunk, split).  It serves up to 16 query heads of the kv head's group at
+// once, so every K/V byte of the split is read from HBM once.  Per tile of 32
+// keys the wave computes, on the matrix cores,
+//   S^T[key][head] = K[key][:] . Q[head][:]   (v_mfma_f32_16x16x32_f16)
+//   O^T[d][head]  += V^T[d][key] . P^T[key][head]
+// K goes straight from global memory (coalesced 64-byte runs of each key row)
+// into the A operand; V tiles are loaded coalesced (whole rows), transposed in
+// registers four keys at a time and staged in the wave's own LDS region, from
+// which the PV operand is read with 16-byte loads.  The score accumulator
+// already has the B-operand layout of the PV product (keys ordered to match),
+// so probabilities never leave registers.  A head's running max is shared by
+// the four lanes that hold it with two cross-lane swaps per tile; the lane
+// holding an output column also holds that head's max, so rescaling is local.
+// Scores are in log2 units (scale * log2 e folded in).  Each register set is
+// refilled with the next tile's K (resp. V) as soon as the MFMA (resp. the LDS
+// store) has consumed it, so loads stay in flight during the rest of the tile.
 #include "pa_device.h"
 
 namespace pa {
@@ -28,30 +32,16 @@ namespace pa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over aligned groups of LPT lanes; every lane of a group gets the total.
-template <int LPT>
-__device__ __forceinline__ float group_sum(float v) {
-  v += dpp<0xB1>(v);            // quad_perm [1,0,3,2]
-  v += dpp<0x4E>(v);            // quad_perm [2,3,0,1]
-  if (LPT >= 8) v += dpp<0x141>(v);   // row_half_mirror: quad 0 <-> quad 1
-  if (LPT >= 16) v += dpp<0x140>(v);  // row_mirror: half-row 0 <-> half-row 1
-  if (LPT >= 32) v += __shfl_xor(v, 16, 64);
-  return v;
-}
+constexpr float kRescaleSlack = 8.0f;   // log2 units
+typedef float f4 __attribute__((ext_vector_type(4)));
 
 struct RowInfo {
   int t, b, pos, lo, hi, nsplit;
 };
 
 // Resolve the query token a decode row stands for and the split layout of its
-// admitted key interval [lo, hi).  Identical in the decode and merge kernels.
-// Returns false when the row has no work for this kernel.
+// admitted key interval [lo, hi).  Identical in the plan, decode and merge
+// kernels.  Returns false when the row has no work for the decode kernel.
 __device__ __forceinline__ bool resolve_row(const SeqLayout& s, int token_mode, int row,
                                             int window, int split_tokens, int max_splits,
                                             RowInfo& r, bool& orphan) {
@@ -80,318 +70,474 @@ __device__ __forceinline__ bool resolve_row(const SeqLayout& s, int token_mode, 
   return true;
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
-  constexpr int LPT = D / 8;         // lanes per token row
-  constexpr int TPW = 64 / LPT;      // tokens per wave per pass
-  constexpr int NW = 4;              // waves per workgroup
-  constexpr int U = 4;               // passes per load group
-  constexpr int STEP = NW * TPW;     // tokens per pass over the workgroup
-  constexpr int SEG = 256;           // block-table entries staged per segment
+__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
 
-  __shared__ int32_t s_blk[SEG];
-  __shared__ float s_o[NW][G][D];
-  __shared__ float s_m[NW][G];
-  __shared__ float s_l[NW][G];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int sub = lane / LPT;
-  const int c = lane % LPT;
-  const int row = blockIdx.x;
-  const int kvh = blockIdx.y / a.head_chunks;
-  const int hc = blockIdx.y - kvh * a.head_chunks;
-  const int split = blockIdx.z;
-  const int h0 = kvh * a.group + hc * G;
-  const int64_t HD = (int64_t)a.num_heads * D;
-  const SeqLayout& sl = a.s;
-
-  RowInfo r;
-  bool orphan;
-  if (!resolve_row(sl, a.token_mode, row, a.window, a.split_tokens, a.max_splits, r, orphan)) {
-    if (orphan && split == 0 && row < sl.tokens) {   // token owned by no request: zero row
-      for (int i = threadIdx.x; i < G * LPT; i += 256)
-        store16(a.out + row * HD + (int64_t)(h0 + i / LPT) * D + 8 * (i % LPT), u32x4{0, 0, 0, 0});
+// ---------------------------------------------------------------------------
+// plan: one workgroup lists (row, split) entries; zeroes orphan token rows
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void plan_kernel(const PlanArgs a) {
+  __shared__ int s_wave[16];
+  __shared__ int s_sum;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  int total = 0;
+  for (int r0 = 0; r0 < a.rows; r0 += 1024) {
+    const int row = r0 + tid;
+    int n = 0;
+    if (row < a.rows) {
+      RowInfo r;
+      bool orphan;
+      if (resolve_row(a.s, a.token_mode, row, a.window, a.split_tokens, a.max_splits, r, orphan))
+        n = r.nsplit;
+      else if (orphan)
+        for (int i = 0; i < a.row_width; i += 8)
+          store16(a.out + (int64_t)row * a.row_width + i, u32x4{0, 0, 0, 0});
     }
-    return;
-  }
-  if (split >= max(r.nsplit, 1)) return;
-
-  const int k_lo = r.lo + split * a.split_tokens;
-  const int k_hi = r.nsplit > 0 ? min(r.hi, k_lo + a.split_tokens) : k_lo;
-
-  // query chunks (rotated at the token's position, rounded to fp16)
-  h2 q[G][4];
+    int incl = n;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint16_t* qrow = a.query + (int64_t)r.t * HD + (int64_t)(h0 + h) * D;
-    u32x4 qv = load16(qrow + 8 * c);
-    if (a.rotary_dim > 0 && 8 * c < a.rotary_dim) {
-      float rr[8];
-      rotate_chunk(qrow, qv, c, r.pos, a.cos, a.sin, a.rotary_dim, a.rotary_interleaved,
-                   a.rotary_rows, rr);
-      qv = pack8(rr);
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
     }
-    __builtin_memcpy(&q[h][0], &qv, 16);
-  }
-
-  float m[G], l[G], o[G][8];
+    if (lane == 63) s_wave[wv] = incl;
+    __syncthreads();
+    if (wv == 0) {
+      int v = lane < 16 ? s_wave[lane] : 0;
+      int sc = v;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+      for (int off = 1; off < 16; off <<= 1) {
+        const int y = __shfl_up(sc, off, 64);
+        if (lane >= off) sc += y;
+      }
+      if (lane < 16) s_wave[lane] = sc - v;
+      if (lane == 15) s_sum = sc;
+    }
+    __syncthreads();
+    const int first = total + s_wave[wv] + incl - n;
+    for (int sp = 0; sp < n; ++sp) a.entries[first + sp] = make_int2(row, sp);
+    total += s_sum;
+    __syncthreads();
   }
+  if (tid == 0) *a.entry_count = total;
+}
 
-  const int shift = sl.block_shift;
+// ---------------------------------------------------------------------------
+// decode workers
+// ---------------------------------------------------------------------------
+template <int D>
+struct DecodeCfg {
+  static constexpr int KT = 32;          // keys per tile
+  static constexpr int KS = D / 32;      // QK k-steps over the head dim
+  static constexpr int DB = D / 16;      // 16-channel output blocks
+  static constexpr int CPR = D / 8;      // 16-byte chunks per key row
+  static constexpr int KPL = D / 16;     // V keys per lane per tile
+  static constexpr int VLD = KT + 8;     // LDS row stride of V^T (halves)
+  static constexpr int TBL = 256;        // block-table entries staged per segment
+};
+
+// Position of tile key k in the V^T rows: the PV operand of lane group q
+// (8 consecutive halves at 8q) must hold keys {4q..4q+3, 16+4q..16+4q+3}, the
+// keys of the score accumulator rows that lane group holds.
+__device__ __forceinline__ int vt_pos(int k) {
+  return 8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3);
+}
+
+// K rows of the tile for the QK A operand.  A masked key (past the segment or
+// in an unmapped block) reads block 0 instead; its score is replaced by -inf
+// with a select, so whatever it holds never reaches the softmax.
+template <int D>
+__device__ __forceinline__ void load_k(const uint16_t* kb, const int32_t* tbl, int first_bi,
+                                       int shift, int64_t tok_stride, int k0, int seg_hi,
+                                       int lane, u32x4 (&kr)[2][DecodeCfg<D>::KS]) {
+  using C = DecodeCfg<D>;
   const int bmask = (1 << shift) - 1;
-  const int64_t tok_stride = (int64_t)a.kv_heads * D;
-  const uint16_t* kbase = a.key_cache + (int64_t)kvh * D + 8 * c;
-  const uint16_t* vbase = a.value_cache + (int64_t)kvh * D + 8 * c;
-  const int32_t* bt = sl.block_table + (int64_t)r.b * sl.maxblk;
-  const bool softcap = a.use_softcap != 0;
-
-  for (int seg_lo = k_lo; seg_lo < k_hi;) {
-    const int first_bi = seg_lo >> shift;
-    const int seg_hi = min(k_hi, (first_bi + SEG) << shift);
-    const int last_bi = (seg_hi - 1) >> shift;
-    __syncthreads();
-    if (threadIdx.x < SEG) {
-      const int bi = first_bi + (int)threadIdx.x;
-      int v = -1;
-      if (bi <= last_bi && bi < sl.maxblk) {
-        v = bt[bi];
-        if (v >= sl.num_blocks) v = -1;
-      }
-      s_blk[threadIdx.x] = v;
-    }
-    __syncthreads();
-
-    const int npass = (seg_hi - seg_lo + STEP - 1) / STEP;
-    const int tok0 = seg_lo + wave * TPW + sub;
-
-    u32x4 kc[U], vc[U];
-    bool okc[U];
+  const int q = lane >> 4, l16 = lane & 15;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tau = tok0 + u * STEP;
-      okc[u] = false;
-      kc[u] = vc[u] = u32x4{0, 0, 0, 0};
-      if (tau < seg_hi) {
-        const int blk = s_blk[(tau >> shift) - first_bi];
-        if (blk >= 0) {
-          const int64_t idx = ((int64_t)blk * (bmask + 1) + (tau & bmask)) * tok_stride;
-          kc[u] = load16(kbase + idx);
-          vc[u] = load16(vbase + idx);
-          okc[u] = true;
-        }
-      }
-    }
-
-    for (int p0 = 0; p0 < npass; p0 += U) {
-      // issue the next group's loads before consuming this one
-      u32x4 kn[U], vn[U];
-      bool okn[U];
-      const bool more = p0 + U < npass;
+  for (int s = 0; s < 2; ++s) {
+    const int key = k0 + 16 * s + l16;
+    const bool in = key < seg_hi;
+    const int blk = tbl[in ? (key >> shift) - first_bi : 0];
+    const int64_t off = ((int64_t)(in && blk >= 0 ? blk : 0) * (bmask + 1) + (key & bmask)) * tok_stride;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        okn[u] = false;
-        kn[u] = vn[u] = u32x4{0, 0, 0, 0};
-        const int tau = tok0 + (p0 + U + u) * STEP;
-        if (more && tau < seg_hi) {
-          const int blk = s_blk[(tau >> shift) - first_bi];
-          if (blk >= 0) {
-            const int64_t idx = ((int64_t)blk * (bmask + 1) + (tau & bmask)) * tok_stride;
-            kn[u] = load16(kbase + idx);
-            vn[u] = load16(vbase + idx);
-            okn[u] = true;
-          }
-        }
-      }
-
-      float sc[U][G];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const h8 kk = as_h8(kc[u]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float acc = 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            h2 kp;
-            kp[0] = kk[2 * i];
-            kp[1] = kk[2 * i + 1];
-            acc = __builtin_amdgcn_fdot2(q[h][i], kp, acc, false);
-          }
-          acc = group_sum<LPT>(acc);
-          const float s = softcap ? tanh_fast(acc * a.cap_in) * a.cap_out : acc * a.score_scale;
-          sc[u][h] = okc[u] ? s : kNegInf;
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float mx = sc[0][h];
-#pragma unroll
-        for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][h]);
-        const float mn = fmaxf(m[h], mx);
-        const float mu = mn == kNegInf ? 0.f : mn;
-        const float alpha = exp2_fast(m[h] - mu);
-        m[h] = mn;
-        l[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float p = exp2_fast(sc[u][h] - mu);
-          l[h] += p;
-          const h8 vv = as_h8(vc[u]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[h][e] = __builtin_fmaf(p, (float)vv[e], o[h][e]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        kc[u] = kn[u];
-        vc[u] = vn[u];
-        okc[u] = okn[u];
-      }
-    }
-    seg_lo = seg_hi;
-  }
-
-  // merge the lane groups of this wave (same channels, different tokens)
-#pragma unroll
-  for (int msk = LPT; msk < 64; msk <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], msk, 64);
-      const float lo_ = __shfl_xor(l[h], msk, 64);
-      const float mn = fmaxf(m[h], mo);
-      const float mu = mn == kNegInf ? 0.f : mn;
-      const float fa = exp2_fast(m[h] - mu);
-      const float fb = exp2_fast(mo - mu);
-      l[h] = l[h] * fa + lo_ * fb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float oo = __shfl_xor(o[h][e], msk, 64);
-        o[h][e] = o[h][e] * fa + oo * fb;
-      }
-      m[h] = mn;
-    }
-  }
-  if (sub == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[wave][h][8 * c + e] = o[h][e];
-      if (c == 0) {
-        s_m[wave][h] = m[h];
-        s_l[wave][h] = l[h];
-      }
-    }
-  }
-  __syncthreads();
-
-  // merge the waves; write the row (single split) or this split's partial
-  if ((int)threadIdx.x < G * LPT) {
-    const int h = threadIdx.x / LPT;
-    const int cc = threadIdx.x % LPT;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
-    const float mu = M == kNegInf ? 0.f : M;
-    float den = 0.f, num[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) num[e] = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = exp2_fast(s_m[w][h] - mu);
-      den += f * s_l[w][h];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) num[e] += f * s_o[w][h][8 * cc + e];
-    }
-    if (r.nsplit <= 1) {
-      const float inv = den > 0.f ? 1.0f / den : 0.f;
-      float res[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) res[e] = num[e] * inv;
-      store16(a.out + (int64_t)r.t * HD + (int64_t)(h0 + h) * D + 8 * cc, pack8(res));
-    } else {
-      const int64_t pidx = ((int64_t)row * a.num_heads + h0 + h) * a.max_splits + split;
-      float* po = a.part_o + pidx * D + 8 * cc;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) po[e] = num[e];
-      if (cc == 0) {
-        a.part_ml[2 * pidx] = M;
-        a.part_ml[2 * pidx + 1] = den;
-      }
-    }
+    for (int ks = 0; ks < C::KS; ++ks) kr[s][ks] = load16(kb + off + 8 * q + 32 * ks);
   }
 }
 
-__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
-  const int row = blockIdx.x;
-  RowInfo r;
-  bool orphan;
-  if (!resolve_row(a.s, a.token_mode, row, a.window, a.split_tokens, a.max_splits, r, orphan))
-    return;
-  if (r.nsplit <= 1) return;   // the decode kernel wrote this row directly
-  const int D = a.head_size;
-  const int chunks = D >> 3;
-  const int items = a.num_heads * chunks;
-  const int64_t HD = (int64_t)a.num_heads * D;
-  for (int i = threadIdx.x; i < items; i += blockDim.x) {
-    const int h = i / chunks;
-    const int cc = i - h * chunks;
-    const int64_t base = ((int64_t)row * a.num_heads + h) * a.max_splits;
-    float M = kNegInf;
-    for (int s = 0; s < r.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * (base + s)]);
-    const float mu = M == kNegInf ? 0.f : M;
-    float den = 0.f, num[8];
+// V rows of the tile (whole 16-byte chunks, coalesced).  Masked keys read
+// block 0; bit i of the returned mask says whether key i is real, and the
+// LDS store writes zeros for the others (a zero probability times a
+// non-finite value would otherwise poison the PV product).
+template <int D>
+__device__ __forceinline__ uint32_t load_v(const uint16_t* vb, const int32_t* tbl, int first_bi,
+                                           int shift, int64_t tok_stride, int k0, int seg_hi,
+                                           int lane, u32x4 (&vr)[DecodeCfg<D>::KPL]) {
+  using C = DecodeCfg<D>;
+  const int bmask = (1 << shift) - 1;
+  const int qv = lane / C::CPR, c = lane % C::CPR;
+  uint32_t okm = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) num[e] = 0.f;
-    for (int s = 0; s < r.nsplit; ++s) {
-      const float f = exp2_fast(a.part_ml[2 * (base + s)] - mu);
-      den += f * a.part_ml[2 * (base + s) + 1];
-      const float* po = a.part_o + (base + s) * D + 8 * cc;
+  for (int i = 0; i < C::KPL; ++i) {
+    const int key = k0 + qv * C::KPL + i;
+    const bool in = key < seg_hi;
+    const int blk = tbl[in ? (key >> shift) - first_bi : 0];
+    const bool ok = in && blk >= 0;
+    okm |= (uint32_t)ok << i;
+    const int64_t off = ((int64_t)(ok ? blk : 0) * (bmask + 1) + (key & bmask)) * tok_stride;
+    vr[i] = load16(vb + off + 8 * c);
+  }
+  return okm;
+}
+
+// Write four keys' 8-channel chunks (k0..k3, one u32x4 each) as the 8 rows
+// d = 8c + e of V^T: row e gets the 4 halves {k0[e], k1[e], k2[e], k3[e]}.
+__device__ __forceinline__ void store_vt4(uint16_t* vt, int ld, int c, int p0, u32x4 k0, u32x4 k1,
+                                          u32x4 k2, u32x4 k3, uint32_t ok4) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) num[e] += f * po[e];
-    }
-    const float inv = den > 0.f ? 1.0f / den : 0.f;
-    float res[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) res[e] = num[e] * inv;
-    store16(a.out + (int64_t)r.t * HD + (int64_t)h * D + 8 * cc, pack8(res));
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t a0 = (ok4 & 1) ? k0[w] : 0u, a1 = (ok4 & 2) ? k1[w] : 0u;
+    const uint32_t a2 = (ok4 & 4) ? k2[w] : 0u, a3 = (ok4 & 8) ? k3[w] : 0u;
+    uint2 lo, hi;
+    lo.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // {k0.lo, k1.lo}
+    lo.y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+    hi.x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // {k0.hi, k1.hi}
+    hi.y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+    *reinterpret_cast<uint2*>(&vt[(8 * c + 2 * w) * ld + p0]) = lo;
+    *reinterpret_cast<uint2*>(&vt[(8 * c + 2 * w + 1) * ld + p0]) = hi;
   }
 }
 
 template <int D>
-hipError_t launch_decode_d(const DecodeArgs& a, int g_chunk, dim3 grid, hipStream_t st) {
-  switch (g_chunk) {
-    case 1: hipLaunchKernelGGL((decode_kernel<D, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<D, 4>), grid, dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<D, 8>), grid, dim3(256), 0, st, a); break;
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : D <= 128 ? 2 : 1)))
+void decode_kernel(const DecodeArgs a) {
+  using C = DecodeCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[kDecodeWaves][D * C::VLD];
+  __shared__ int32_t s_tbl[kDecodeWaves][C::TBL];
+
+  // the wave index is uniform across the wave: saying so keeps every per-item
+  // value (row, split, key range, pointers) and loop bound in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4;
+  const int l16 = lane & 15;
+  const SeqLayout& sl = a.s;
+  const int HC = a.kv_heads * a.head_chunks;
+  const int64_t HD = (int64_t)a.num_heads * D;
+  const int total = a.listed ? (*a.entry_count) * HC : a.rows * HC;
+  const int nworkers = gridDim.x * kDecodeWaves;
+  uint16_t* vt = s_vt[wave];
+  int32_t* tbl = s_tbl[wave];
+  const int shift = sl.block_shift;
+  const int64_t tok_stride = (int64_t)a.kv_heads * D;
+  const bool softcap = a.use_softcap != 0;
+
+  for (int item = blockIdx.x * kDecodeWaves + wave; item < total; item += nworkers) {
+    const int e = item / HC;
+    const int kvhc = item - e * HC;
+    int row, split;
+    if (a.listed) {
+      const int2 en = a.entries[e];
+      row = en.x;
+      split = en.y;
+    } else {
+      row = e;
+      split = 0;
+    }
+    const int kvh = kvhc / a.head_chunks;
+    const int h0 = kvh * a.group + (kvhc - kvh * a.head_chunks) * a.chunk_heads;
+
+    RowInfo r;
+    bool orphan;
+    if (!resolve_row(sl, a.token_mode, row, a.window, a.split_tokens, a.max_splits, r, orphan)) {
+      if (orphan && !a.listed && row < sl.tokens) {   // token owned by no request: zero
+        for (int i = lane; i < a.chunk_heads * (D / 8); i += 64)
+          store16(a.out + row * HD + (int64_t)h0 * D + 8 * i, u32x4{0, 0, 0, 0});
+      }
+      continue;
+    }
+    if (split >= max(r.nsplit, 1)) continue;
+    const int k_lo = r.lo + split * a.split_tokens;
+    const int k_hi = r.nsplit > 0 ? min(r.hi, k_lo + a.split_tokens) : k_lo;
+
+    // Q as the B operand: lane (q, l16) holds head l16, channels 32ks + 8q + [0,8)
+    const bool head_ok = l16 < a.chunk_heads;
+    h8 qf[C::KS];
+    {
+      const uint16_t* qrow = a.query + (int64_t)r.t * HD + (int64_t)(h0 + l16) * D;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        u32x4 v = u32x4{0, 0, 0, 0};
+        const int c = 4 * ks + q;
+        if (head_ok) {
+          v = load16(qrow + 8 * c);
+          if (a.rotary_dim > 0 && 8 * c < a.rotary_dim) {
+            float rr[8];
+            rotate_chunk(qrow, v, c, r.pos, a.cos, a.sin, a.rotary_dim, a.rotary_interleaved,
+                         a.rotary_rows, rr);
+            v = pack8(rr);
+          }
+        }
+        qf[ks] = as_h8(v);
+        __builtin_amdgcn_sched_barrier(0);   // one chunk at a time: keeps the prologue small
+      }
+    }
+
+    f4 acc[C::DB];
+#pragma unroll
+    for (int i = 0; i < C::DB; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, lsum = 0.f;
+    const uint16_t* kb = a.key_cache + (int64_t)kvh * D;
+    const uint16_t* vb = a.value_cache + (int64_t)kvh * D;
+    const int32_t* bt = sl.block_table + (int64_t)r.b * sl.maxblk;
+
+    for (int seg_lo = k_lo; seg_lo < k_hi;) {
+      const int first_bi = seg_lo >> shift;
+      const int seg_hi = min(k_hi, (first_bi + C::TBL) << shift);
+      const int n_bi = ((seg_hi - 1) >> shift) - first_bi + 1;
+      bool hole = false;
+      for (int i = lane; i < n_bi; i += 64) {
+        const int bi = first_bi + i;
+        int v = bi < sl.maxblk ? bt[bi] : -1;
+        if (v >= sl.num_blocks) v = -1;
+        hole |= v < 0;
+        tbl[i] = v;
+      }
+      const bool any_hole = __any(hole);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      const int ntile = (seg_hi - seg_lo + C::KT - 1) / C::KT;
+      u32x4 kr[2][C::KS], vr[C::KPL];
+      load_k<D>(kb, tbl, first_bi, shift, tok_stride, seg_lo, seg_hi, lane, kr);
+      uint32_t vok = load_v<D>(vb, tbl, first_bi, shift, tok_stride, seg_lo, seg_hi, lane, vr);
+      for (int it = 0; it < ntile; ++it) {
+        const int k0 = seg_lo + it * C::KT;
+        const bool more = it + 1 < ntile;
+
+        // ---- S^T = K . Q^T: two 16-key blocks ----
+        f4 s[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          s[sb] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks)
+            s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kr[sb][ks]), qf[ks], s[sb], 0, 0, 0);
+        }
+        // K registers are free again: fetch the next tile's keys now (the
+        // scheduling barriers keep the refill after the last use, so the two
+        // tiles never hold registers at the same time)
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) load_k<D>(kb, tbl, first_bi, shift, tok_stride, k0 + C::KT, seg_hi, lane, kr);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- scores (log2 units), mask, running max ----
+        const bool edge = any_hole || k0 + C::KT > seg_hi;
+        float x[8];
+        float mx = kNegInf;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            float v = s[sb][rr];
+            v = softcap ? tanh_fast(v * a.cap_in) * a.cap_out : v * a.score_scale;
+            if (edge) {
+              const int key = k0 + 16 * sb + 4 * q + rr;
+              const bool ok = key < seg_hi && tbl[(key >> shift) - first_bi] >= 0;
+              v = ok ? v : kNegInf;
+            }
+            x[4 * sb + rr] = v;
+            mx = fmaxf(mx, v);
+          }
+        }
+        mx = xor_max(xor_max(mx, 16), 32);
+        // lazy rescale: keep the running max unless the tile exceeds it by more
+        // than kRescaleSlack (probabilities then stay below 2^kRescaleSlack),
+        // so most tiles skip touching the accumulators
+        if (__any(mx > m + kRescaleSlack)) {
+          const float mn = mx > m + kRescaleSlack ? mx : m;
+          const float alpha = exp2_fast(m - (mn == kNegInf ? 0.f : mn));
+          m = mn;
+          lsum *= alpha;
+#pragma unroll
+          for (int i = 0; i < C::DB; ++i) acc[i] *= alpha;
+        }
+        const float mu = m == kNegInf ? 0.f : m;
+        h8 pf;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p = exp2_fast(x[i] - mu);
+          lsum += p;
+          pf[i] = (_Float16)p;
+        }
+
+        // ---- V tile -> LDS, transposed (four keys per 8-byte write) ----
+        {
+          const int qv = lane / C::CPR, c = lane % C::CPR;
+#pragma unroll
+          for (int g4 = 0; g4 < C::KPL / 4; ++g4)
+            store_vt4(vt, C::VLD, c, vt_pos(qv * C::KPL + 4 * g4), vr[4 * g4], vr[4 * g4 + 1],
+                      vr[4 * g4 + 2], vr[4 * g4 + 3], (vok >> (4 * g4)) & 15u);
+        }
+        // V registers are free again: fetch the next tile's values now
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) vok = load_v<D>(vb, tbl, first_bi, shift, tok_stride, k0 + C::KT, seg_hi, lane, vr);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // ---- O^T += V^T . P^T ----
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const h8 va = *reinterpret_cast<const h8*>(&vt[(16 * db + l16) * C::VLD + 8 * q]);
+          acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf, acc[db], 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      seg_lo = seg_hi;
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---- epilogue: lane (q, l16) holds head l16, channels 16db + 4q + [0,4) ----
+    float lt = lsum + __shfl_xor(lsum, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (head_ok) {
+      const int h = h0 + l16;
+      if (r.nsplit <= 1) {
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        uint16_t* orow = a.out + (int64_t)r.t * HD + (int64_t)h * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          uint2 w;
+          w.x = (uint32_t)f2h(acc[db][0] * inv) | ((uint32_t)f2h(acc[db][1] * inv) << 16);
+          w.y = (uint32_t)f2h(acc[db][2] * inv) | ((uint32_t)f2h(acc[db][3] * inv) << 16);
+          *reinterpret_cast<uint2*>(orow + 16 * db + 4 * q) = w;
+        }
+      } else {
+        const int64_t pidx = ((int64_t)row * a.num_heads + h) * a.max_splits + split;
+        float* po = a.part_o + pidx * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) *reinterpret_cast<f4*>(po + 16 * db + 4 * q) = acc[db];
+        if (q == 0) {
+          a.part_ml[2 * pidx] = m;
+          a.part_ml[2 * pidx + 1] = lt;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge: one workgroup per (row, head) with more than one split.  Threads
+// first run over splits (max, weights exp2(m_s - M), denominator), then over
+// (4-channel group, split group) pairs, and the split groups are summed in LDS.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* s_tmp) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float o = __shfl_xor(v, off, 64);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  const int wv = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_tmp[wv] = v;
+  __syncthreads();
+  float r = s_tmp[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i) r = is_max ? fmaxf(r, s_tmp[i]) : r + s_tmp[i];
+  return r;
+}
+
+__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
+  __shared__ float s_w[kDecodeMaxSplits];
+  __shared__ f4 s_red[256];
+  __shared__ float s_tmp[4];
+  const int row = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  RowInfo r;
+  bool orphan;
+  if (!resolve_row(a.s, a.token_mode, row, a.window, a.split_tokens, a.max_splits, r, orphan))
+    return;
+  if (r.nsplit <= 1) return;   // the decode worker wrote this row directly
+  const int n = r.nsplit;
+  const int D = a.head_size;
+  const int64_t base = ((int64_t)row * a.num_heads + h) * a.max_splits;
+  float M = kNegInf;
+  for (int s = tid; s < n; s += 256) M = fmaxf(M, a.part_ml[2 * (base + s)]);
+  M = block_reduce(M, true, s_tmp);
+  const float mu = M == kNegInf ? 0.f : M;
+  float den = 0.f;
+  for (int s = tid; s < n; s += 256) {
+    const float w = exp2_fast(a.part_ml[2 * (base + s)] - mu);
+    s_w[s] = w;
+    den += w * a.part_ml[2 * (base + s) + 1];
+  }
+  den = block_reduce(den, false, s_tmp);   // (its barriers also publish s_w)
+  const int nq = D >> 2;                   // 4-channel groups
+  const int dq = tid % nq;
+  const int sg = tid / nq;
+  const int nsg = 256 / nq;
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  const float* po = a.part_o + base * D + 4 * dq;
+  for (int s = sg; s < n; s += nsg) acc += s_w[s] * *reinterpret_cast<const f4*>(po + (int64_t)s * D);
+  s_red[tid] = acc;
+  __syncthreads();
+  if (sg == 0) {
+    for (int g = 1; g < nsg; ++g) acc += s_red[g * nq + dq];
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    uint2 w;
+    w.x = (uint32_t)f2h(acc[0] * inv) | ((uint32_t)f2h(acc[1] * inv) << 16);
+    w.y = (uint32_t)f2h(acc[2] * inv) | ((uint32_t)f2h(acc[3] * inv) << 16);
+    *reinterpret_cast<uint2*>(a.out + (int64_t)r.t * a.num_heads * D + (int64_t)h * D + 4 * dq) = w;
+  }
+}
+
+template <int D>
+int occupancy_wg() {
+  static int cached = 0;
+  if (!cached) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D>, 256, 0) != hipSuccess ||
+        n <= 0)
+      n = 1;
+    cached = n;
+  }
+  return cached;
+}
+
+}  // namespace
+
+int decode_workgroups_per_cu(int head_size) {
+  switch (head_size) {
+    case 64: return occupancy_wg<64>();
+    case 128: return occupancy_wg<128>();
+    case 256: return occupancy_wg<256>();
+    default: return 1;
+  }
+}
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int head_size, int workgroups, hipStream_t st) {
+  const dim3 grid(workgroups), block(64 * kDecodeWaves);
+  switch (head_size) {
+    case 64: hipLaunchKernelGGL(decode_kernel<64>, grid, block, 0, st, a); break;
+    case 128: hipLaunchKernelGGL(decode_kernel<128>, grid, block, 0, st, a); break;
+    case 256: hipLaunchKernelGGL(decode_kernel<256>, grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_decode(const DecodeArgs& a, int head_size, int g_chunk, dim3 grid,
-                         hipStream_t st) {
-  switch (head_size) {
-    case 64: return launch_decode_d<64>(a, g_chunk, grid, st);
-    case 128: return launch_decode_d<128>(a, g_chunk, grid, st);
-    case 256: return launch_decode_d<256>(a, g_chunk, grid, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_merge(const MergeArgs& a, int rows, hipStream_t st) {
-  hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(256), 0, st, a);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(merge_kernel, dim3(a.rows, a.num_heads), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

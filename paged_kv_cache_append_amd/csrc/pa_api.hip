@@ -144,6 +144,8 @@ pa_status check_rotary(const pa_attn_params* p, const pa_paged_kv* kv, const voi
       return fail(PA_ERR_INVALID_ARGUMENT,
                   "rotary_rows: expected >= max_blocks_per_seq * block_size = %lld, got %d",
                   (long long)need, rows);
+    if (!aligned16(cos_cache) || !aligned16(sin_cache))
+      return fail(PA_ERR_INVALID_ARGUMENT, "cos_cache/sin_cache: expected 16-byte alignment");
   } else if (cos_cache) {
     return fail(PA_ERR_INVALID_ARGUMENT, "cos_cache/sin_cache: given but do_rotary = 0");
   }
@@ -158,25 +160,33 @@ pa_status check_kernel_support(const pa_attn_params* p) {
 }
 
 // ---- planning ----------------------------------------------------------------
-constexpr int kTargetWorkgroups = 4096;  // decode workgroups aimed at (256 CUs)
+constexpr int64_t kTargetItems = 16384;   // decode work items aimed at (split length choice)
 
 struct Plan {
   bool token_mode = true;    // decode rows are tokens (else requests with q_len == 1)
   bool prefill = false;
+  bool listed = false;       // decode items come from the device-built list
   int rows = 0;
-  int g = 1, g_chunk = 1, head_chunks = 1;
+  int g = 1, chunk_heads = 1, head_chunks = 1;
   int split_tokens = 256;
   int max_splits = 1;
   int prefill_tiles = 0;     // tile slots (grid.x = tiles + 1)
+  size_t off_ml = 0, off_entries = 0, off_count = 0;
   size_t ws_bytes = 0;
 };
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32_t mk) {
   Plan pl;
   const int T = kv->token_count, B = kv->batch_size;
   pl.g = p->num_heads / p->kv_num_heads;
-  pl.g_chunk = pl.g % 8 == 0 ? 8 : pl.g % 4 == 0 ? 4 : pl.g % 2 == 0 ? 2 : 1;
-  pl.head_chunks = pl.g / pl.g_chunk;
+  for (int c = std::min(pl.g, pa::kDecodeMaxHeads); c >= 1; --c)
+    if (pl.g % c == 0) {
+      pl.chunk_heads = c;
+      break;
+    }
+  pl.head_chunks = pl.g / pl.chunk_heads;
   if (p->path == 1)
     pl.token_mode = true;
   else if (p->path == 2)
@@ -193,20 +203,22 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
     pl.split_tokens = p->split_tokens;
   } else {
     // split length from static shapes only, so results do not depend on the bounds
-    const int64_t pairs = std::max<int64_t>(1, (int64_t)pl.rows * p->kv_num_heads * pl.head_chunks);
-    const int64_t want = std::max<int64_t>(1, (kTargetWorkgroups + pairs - 1) / pairs);
-    int64_t st = (span + want - 1) / want;
+    const int64_t items = std::max<int64_t>(1, (int64_t)pl.rows * p->kv_num_heads * pl.head_chunks);
+    int64_t st = (items * span + kTargetItems - 1) / kTargetItems;
+    st = std::max<int64_t>(st, (span + pa::kDecodeMaxSplits - 1) / pa::kDecodeMaxSplits);
     st = (st + 63) / 64 * 64;
     pl.split_tokens = (int)std::max<int64_t>(256, std::min<int64_t>(st, 1 << 30));
   }
   int64_t kv_ext = mk > 0 ? std::min<int64_t>(mk, cap) : cap;   // bound only trims the grid
   if (p->local_window_size > 0) kv_ext = std::min<int64_t>(kv_ext, p->local_window_size);
   pl.max_splits = (int)std::max<int64_t>(1, (kv_ext + pl.split_tokens - 1) / pl.split_tokens);
-  if (pl.max_splits > 1) {
+  pl.listed = pl.max_splits > 1;
+  if (pl.listed) {
     const size_t per = (size_t)pl.rows * p->num_heads * pl.max_splits;
-    size_t o_bytes = per * p->head_size * sizeof(float);
-    o_bytes = (o_bytes + 255) / 256 * 256;
-    pl.ws_bytes = o_bytes + per * 2 * sizeof(float);
+    pl.off_ml = align256(per * p->head_size * sizeof(float));
+    pl.off_entries = pl.off_ml + align256(per * 2 * sizeof(float));
+    pl.off_count = pl.off_entries + align256((size_t)pl.rows * pl.max_splits * 2 * sizeof(int32_t));
+    pl.ws_bytes = pl.off_count + 256;
   }
   if (pl.prefill) {
     const int64_t mql = mq > 0 ? std::min<int64_t>(mq, T) : T;
@@ -218,11 +230,24 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
   return pl;
 }
 
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 pa_status check_plan(const Plan& pl) {
-  if (pl.max_splits > 65535)
+  if (pl.max_splits > pa::kDecodeMaxSplits)
     return fail(PA_ERR_INVALID_ARGUMENT,
-                "split_tokens: %d gives %d splits; expected at most 65535", pl.split_tokens,
-                pl.max_splits);
+                "split_tokens: %d gives %d splits; expected at most %d", pl.split_tokens,
+                pl.max_splits, pa::kDecodeMaxSplits);
   return PA_OK;
 }
 
@@ -304,12 +329,12 @@ pa_status pa_describe_plan(const pa_attn_params* params, const pa_paged_kv* kv, 
   if (!buf || len == 0) return fail(PA_ERR_INVALID_ARGUMENT, "buf: expected non-NULL, len > 0");
   const Plan pl = make_plan(params, kv, mq, mk);
   snprintf(buf, len,
-           "mode=%s decode_grid=(%d,%d,%d) g=%d g_chunk=%d split_tokens=%d max_splits=%d "
-           "merge=%d prefill_grid=(%d,%d) workspace=%zu",
+           "mode=%s rows=%d head_chunks=%d g=%d chunk_heads=%d split_tokens=%d max_splits=%d "
+           "listed=%d prefill_grid=(%d,%d) workspace=%zu",
            pl.token_mode ? "token" : "request", pl.rows, params->kv_num_heads * pl.head_chunks,
-           pl.max_splits, pl.g, pl.g_chunk, pl.split_tokens, pl.max_splits,
-           pl.max_splits > 1 ? 1 : 0, pl.prefill ? pl.prefill_tiles + 1 : 0,
-           pl.prefill ? params->kv_num_heads : 0, pl.ws_bytes);
+           pl.g, pl.chunk_heads, pl.split_tokens, pl.max_splits, pl.listed ? 1 : 0,
+           pl.prefill ? pl.prefill_tiles + 1 : 0, pl.prefill ? params->kv_num_heads : 0,
+           pl.ws_bytes);
   return PA_OK;
 }
 
@@ -353,15 +378,18 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
   d.cos = static_cast<const uint16_t*>(cos_cache);
   d.sin = static_cast<const uint16_t*>(sin_cache);
   d.out = static_cast<uint16_t*>(out);
-  d.part_o = static_cast<float*>(workspace);
-  size_t o_bytes = (size_t)pl.rows * params->num_heads * pl.max_splits * D * sizeof(float);
-  o_bytes = (o_bytes + 255) / 256 * 256;
-  d.part_ml = pl.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes)
-                          : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  d.part_o = pl.listed ? reinterpret_cast<float*>(ws) : nullptr;
+  d.part_ml = pl.listed ? reinterpret_cast<float*>(ws + pl.off_ml) : nullptr;
+  d.entries = pl.listed ? reinterpret_cast<const int2*>(ws + pl.off_entries) : nullptr;
+  d.entry_count = pl.listed ? reinterpret_cast<const int32_t*>(ws + pl.off_count) : nullptr;
+  d.listed = pl.listed ? 1 : 0;
+  d.rows = pl.rows;
   d.num_heads = params->num_heads;
   d.kv_heads = params->kv_num_heads;
   d.group = pl.g;
   d.head_chunks = pl.head_chunks;
+  d.chunk_heads = pl.chunk_heads;
   d.token_mode = pl.token_mode ? 1 : 0;
   d.split_tokens = pl.split_tokens;
   d.max_splits = pl.max_splits;
@@ -375,19 +403,41 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
   d.use_softcap = cap ? 1 : 0;
 
   if (pl.rows > 0) {
-    const dim3 grid(pl.rows, params->kv_num_heads * pl.head_chunks, pl.max_splits);
+    const int64_t hc = (int64_t)params->kv_num_heads * pl.head_chunks;
+    int64_t wgs;
+    if (pl.listed) {
+      pa::PlanArgs pa_;
+      pa_.s = sl;
+      pa_.entries = reinterpret_cast<int2*>(ws + pl.off_entries);
+      pa_.entry_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
+      pa_.out = d.out;
+      pa_.rows = pl.rows;
+      pa_.token_mode = d.token_mode;
+      pa_.split_tokens = pl.split_tokens;
+      pa_.max_splits = pl.max_splits;
+      pa_.window = params->local_window_size;
+      pa_.row_width = params->num_heads * D;
+      StageScope scope(PA_STAGE_PLAN, s);
+      if ((st = device_status(pa::launch_plan(pa_, s), "plan kernel launch")) != PA_OK) return st;
+      const int64_t bound = (int64_t)pl.rows * pl.max_splits * hc;
+      const int64_t resident = (int64_t)pa::decode_workgroups_per_cu(D) * device_cus();
+      wgs = std::min<int64_t>((bound + pa::kDecodeWaves - 1) / pa::kDecodeWaves, resident);
+    } else {
+      wgs = ((int64_t)pl.rows * hc + pa::kDecodeWaves - 1) / pa::kDecodeWaves;
+    }
     {
       StageScope scope(PA_STAGE_DECODE, s);
-      if ((st = device_status(pa::launch_decode(d, D, pl.g_chunk, grid, s),
+      if ((st = device_status(pa::launch_decode(d, D, (int)std::max<int64_t>(wgs, 1), s),
                               "decode kernel launch")) != PA_OK)
         return st;
     }
-    if (pl.max_splits > 1) {
+    if (pl.listed) {
       pa::MergeArgs mg;
       mg.s = sl;
       mg.part_o = d.part_o;
       mg.part_ml = d.part_ml;
       mg.out = d.out;
+      mg.rows = pl.rows;
       mg.num_heads = params->num_heads;
       mg.head_size = D;
       mg.token_mode = d.token_mode;
@@ -395,7 +445,7 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
       mg.max_splits = pl.max_splits;
       mg.window = params->local_window_size;
       StageScope scope(PA_STAGE_MERGE, s);
-      if ((st = device_status(pa::launch_merge(mg, pl.rows, s), "merge kernel launch")) != PA_OK)
+      if ((st = device_status(pa::launch_merge(mg, s), "merge kernel launch")) != PA_OK)
         return st;
     }
   }

@@ -81,39 +81,60 @@ __device__ __forceinline__ int64_t slot_base(int64_t blk, int off, int kvh, int 
 // multiply-add below rounds the exact result once -- the stored key is then
 // fp16(fp32(exact)).  Positions outside the table are not rotated (memory
 // safety for out-of-contract device lengths).
+__device__ __forceinline__ float rot_pair(float x, float y, float cs, float sn, bool second) {
+  const float ys = y * sn;  // exact
+  return second ? __builtin_fmaf(x, cs, ys) : __builtin_fmaf(x, cs, -ys);
+}
+
 __device__ __forceinline__ void rotate_chunk(const uint16_t* row, u32x4 own, int c, int pos,
                                              const uint16_t* cos_t, const uint16_t* sin_t,
                                              int rot, int interleaved, int rot_rows,
                                              float out[8]) {
   uint16_t x16[8];
   __builtin_memcpy(x16, &own, 16);
-  const int half = rot >> 1;
-  const bool in_table = pos >= 0 && pos < rot_rows;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int d = 8 * c + e;
-    const float x = h2f(x16[e]);
-    if (d >= rot || !in_table) {
-      out[e] = x;
-      continue;
+  for (int e = 0; e < 8; ++e) out[e] = h2f(x16[e]);
+  const int d0 = 8 * c;
+  if (pos < 0 || pos >= rot_rows || d0 >= rot) return;
+  const int half = rot >> 1;
+  const int64_t tb = (int64_t)pos * half;
+  if (!interleaved && (half & 7) == 0) {
+    // the chunk lies in one half: partner chunk and 8 consecutive angles
+    const bool second = d0 >= half;
+    const int i0 = second ? d0 - half : d0;
+    uint16_t y16[8], c16[8], s16[8];
+    const u32x4 pv = load16(row + (second ? d0 - half : d0 + half));
+    const u32x4 cv = load16(cos_t + tb + i0);
+    const u32x4 sv = load16(sin_t + tb + i0);
+    __builtin_memcpy(y16, &pv, 16);
+    __builtin_memcpy(c16, &cv, 16);
+    __builtin_memcpy(s16, &sv, 16);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      out[e] = rot_pair(h2f(x16[e]), h2f(y16[e]), h2f(c16[e]), h2f(s16[e]), second);
+  } else if (interleaved && (half & 7) == 0) {
+    // pairs (2i, 2i+1) inside the chunk: 4 consecutive angles
+    uint16_t c16[4], s16[4];
+    const uint2 cv = *reinterpret_cast<const uint2*>(cos_t + tb + (d0 >> 1));
+    const uint2 sv = *reinterpret_cast<const uint2*>(sin_t + tb + (d0 >> 1));
+    __builtin_memcpy(c16, &cv, 8);
+    __builtin_memcpy(s16, &sv, 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      out[e] = rot_pair(h2f(x16[e]), h2f(x16[e ^ 1]), h2f(c16[e >> 1]), h2f(s16[e >> 1]),
+                        (e & 1) != 0);
+  } else {
+    // general layout: one channel at a time (kept rolled to stay small)
+#pragma unroll 1
+    for (int e = 0; e < 8; ++e) {
+      const int d = d0 + e;
+      if (d >= rot) break;
+      const bool second = interleaved ? (d & 1) != 0 : d >= half;
+      const int i = interleaved ? (d >> 1) : (second ? d - half : d);
+      const int partner = interleaved ? (d ^ 1) : (second ? d - half : d + half);
+      out[e] = rot_pair(h2f(x16[e]), h2f(row[partner]), h2f(cos_t[tb + i]), h2f(sin_t[tb + i]),
+                        second);
     }
-    int i;
-    bool second;
-    float y;
-    if (interleaved) {
-      i = d >> 1;
-      second = (d & 1) != 0;
-      y = h2f(x16[e ^ 1]);
-    } else {
-      second = d >= half;
-      i = second ? d - half : d;
-      y = h2f(row[second ? d - half : d + half]);
-    }
-    const int64_t ti = (int64_t)pos * half + i;
-    const float cs = h2f(cos_t[ti]);
-    const float sn = h2f(sin_t[ti]);
-    const float ys = y * sn;  // exact
-    out[e] = second ? __builtin_fmaf(x, cs, ys) : __builtin_fmaf(x, cs, -ys);
   }
 }
 

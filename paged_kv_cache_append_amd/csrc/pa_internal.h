@@ -37,8 +37,11 @@ struct AppendArgs {
   int32_t rotary_rows;    // rows of cos/sin (positions beyond are not rotated)
 };
 
-// Decode kernel: one workgroup per (row, kv head [x head chunk], KV split).
-// row = packed token (token mode) or request (request mode, q_len == 1 only).
+// Decode work is a list of items (row, split) x (kv head, head chunk).  A row
+// is a packed token (token mode) or a request with q_len == 1 (request mode);
+// a split is a run of at most split_tokens keys of the row's admitted interval.
+// With more than one possible split per row the list is built on the device
+// by the plan kernel ("listed" mode); otherwise item = (row, split 0).
 struct DecodeArgs {
   SeqLayout s;
   const uint16_t* query;        // fp16 [T, H*D]
@@ -49,13 +52,18 @@ struct DecodeArgs {
   uint16_t* out;                // fp16 [T, H*D]
   float* part_o;                // [rows, H, S, D]   unnormalised split outputs
   float* part_ml;               // [rows, H, S, 2]   (max in log2 units, sum)
+  const int2* entries;          // listed mode: (row, split) per entry
+  const int32_t* entry_count;   // listed mode: number of entries
+  int32_t listed;
+  int32_t rows;
   int32_t num_heads;
   int32_t kv_heads;
   int32_t group;                // H / Hkv
-  int32_t head_chunks;          // group is covered in head_chunks chunks of G heads
+  int32_t head_chunks;          // the group is covered in chunks of <= 16 heads
+  int32_t chunk_heads;          // heads per chunk
   int32_t token_mode;           // 1: row = token; 0: row = request with q_len == 1
   int32_t split_tokens;         // KV tokens per split
-  int32_t max_splits;           // S (grid z and workspace extent)
+  int32_t max_splits;           // S (workspace extent)
   int32_t window;               // -1 or W >= 1
   int32_t rotary_dim;
   int32_t rotary_interleaved;
@@ -66,12 +74,28 @@ struct DecodeArgs {
   int32_t use_softcap;
 };
 
-// Split merge: one workgroup per (row), threads over (head, 8-channel chunk).
+// Plan kernel (one workgroup): lists (row, split) entries of every row with
+// work, and zeroes output rows of tokens owned by no request (token mode).
+struct PlanArgs {
+  SeqLayout s;
+  int2* entries;
+  int32_t* entry_count;
+  uint16_t* out;
+  int32_t rows;
+  int32_t token_mode;
+  int32_t split_tokens;
+  int32_t max_splits;
+  int32_t window;
+  int32_t row_width;            // H * D elements of an output row
+};
+
+// Split merge: one wave per (row, head) of rows with more than one split.
 struct MergeArgs {
   SeqLayout s;
   const float* part_o;
   const float* part_ml;
   uint16_t* out;
+  int32_t rows;
   int32_t num_heads;
   int32_t head_size;
   int32_t token_mode;
@@ -106,11 +130,15 @@ struct PrefillArgs {
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
-hipError_t launch_decode(const DecodeArgs& a, int head_size, int g_chunk, dim3 grid,
-                         hipStream_t st);
-hipError_t launch_merge(const MergeArgs& a, int rows, hipStream_t st);
+hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int head_size, int workgroups, hipStream_t st);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
+int decode_workgroups_per_cu(int head_size);   // resident decode workgroups per CU
 hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st);
 
 constexpr int kPrefillRows = 128;   // query rows (token x head) per prefill workgroup
+constexpr int kDecodeWaves = 4;     // independent decode workers per workgroup
+constexpr int kDecodeMaxHeads = 16; // query heads served by one decode worker
+constexpr int kDecodeMaxSplits = 2048;
 
 }  // namespace pa

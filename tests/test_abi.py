@@ -182,7 +182,9 @@ def test_plan_window_caps_splits():
 
 
 def test_plan_group_chunks():
-    pl = plan(params(num_heads=24, kv_num_heads=2), paged())      # g = 12 -> chunks of 4
-    assert pl["g"] == "12" and pl["g_chunk"] == "4"
-    pl = plan(params(num_heads=64, kv_num_heads=2), paged())      # g = 32 -> chunks of 8
-    assert pl["g_chunk"] == "8"
+    pl = plan(params(num_heads=24, kv_num_heads=2), paged())      # g = 12: one chunk
+    assert pl["g"] == "12" and pl["chunk_heads"] == "12" and pl["head_chunks"] == "2"
+    pl = plan(params(num_heads=64, kv_num_heads=2), paged())      # g = 32: chunks of 16
+    assert pl["chunk_heads"] == "16" and pl["head_chunks"] == "4"
+    pl = plan(params(num_heads=40, kv_num_heads=2), paged())      # g = 20: chunks of 10
+    assert pl["chunk_heads"] == "10"
