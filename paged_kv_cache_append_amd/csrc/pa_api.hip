@@ -467,7 +467,7 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     f.rotary_rows = d.rotary_rows;
     f.tiles = pl.prefill_tiles;
     f.score_scale = d.score_scale;
-    f.cap_in = d.cap_in;
+    f.cap_in2 = 2.0f * log2e * d.cap_in;
     f.cap_out = d.cap_out;
     f.use_softcap = d.use_softcap;
     const dim3 grid(pl.prefill_tiles + 1, params->kv_num_heads);

@@ -122,9 +122,9 @@ struct PrefillArgs {
   int32_t rotary_interleaved;
   int32_t rotary_rows;
   int32_t tiles;                // grid.x - 1: tile slots; the last x zeroes orphan rows
-  float score_scale;
-  float cap_in;
-  float cap_out;
+  float score_scale;            // scale * log2(e)
+  float cap_in2;                // 2 * log2(e) * scale / softcap  (tanh via exp2)
+  float cap_out;                // softcap * log2(e)
   int32_t use_softcap;
 };
 

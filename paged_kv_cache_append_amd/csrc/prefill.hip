@@ -6,21 +6,25 @@
 // accumulate, 1/l at the end) with softcap applied to the scaled score before
 // masking (PagedAttention -- CUDA Design Document, section 8.5 note) and the
 // window of W positions ending at the query (section 4.5).  Tiles address the
-// pool one key row at a time through block_table, so a tile may straddle pages
-// of any power-of-two block size (the straddling limit of section 18.1 does
-// not arise).
+// pool one key row at a time through the block table, so a tile may straddle
+// pages of any power-of-two block size (the straddling limit of section 18.1
+// does not arise).
 //
 // One workgroup = 4 waves = 128 query rows of one kv head; a row is a (query
 // token, head-in-group) pair, token-major, so every K/V tile staged in LDS is
-// shared by all G heads of the group.  Each wave owns 32 rows and computes
+// shared by all heads of the group.  Each wave owns 32 rows and computes
 //   S^T[key][row] = K[key][:] . Q[row][:]          (v_mfma_f32_32x32x16_f16)
-// so that the score accumulator already has the B-operand layout of the PV
-// product O^T[d][row] += V^T[d][key] P^T[key][row]: the probabilities go from
-// registers to the MFMA without an LDS round trip.  V is stored transposed in
-// LDS (with the key order of the accumulator layout: bits 2 and 3 of the key
-// index swapped inside each 16-key group) so that both MFMA operands are plain
-// 16-byte LDS reads.  Scores are in log2 units; the row max is shared by the
-// two lanes holding a row with one cross-lane swap per tile.
+// so that the score accumulator already has the B-operand layout of
+//   O^T[d][row] += V^T[d][key] . P^T[key][row]
+// and the probabilities go from registers to the MFMA without an LDS round
+// trip.  V is stored transposed in LDS with the key order of the accumulator
+// layout (bits 2 and 3 of the key index swapped).  K and V^T tiles are double
+// buffered: the next tile's global loads are issued before the current tile's
+// MFMAs and land in LDS after them, so one barrier per tile suffices and the
+// memory latency hides behind the matrix work.  The block-table slice of the
+// workgroup's key range is staged in LDS.  Scores are in log2 units; the
+// running max is shared by the two lanes of a row with one swap per tile and
+// is only raised when a tile exceeds it by more than 8 (lazy rescale).
 #include "pa_device.h"
 
 namespace pa {
@@ -28,30 +32,41 @@ namespace pa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescaleSlack = 8.0f;   // log2 units
 
 __device__ __forceinline__ int swap23(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
-  constexpr int ROWS = kPrefillRows;  // 128 rows = 4 waves x 32
-  constexpr int KT = 64;              // keys per tile
-  constexpr int KS = D / 16;          // MFMA k-steps over the head dim
-  constexpr int DB = D / 32;          // 32-channel output blocks
-  constexpr int CH = D / 8;           // 16-byte chunks per row
-  constexpr int KLD = D + 8;          // LDS row stride of K (halves)
-  constexpr int VLD = KT + 8;         // LDS row stride of V^T (halves)
+struct PrefillCfg {
+  static constexpr int ROWS = kPrefillRows;  // 128 rows = 4 waves x 32
+  static constexpr int KT = 64;              // keys per tile
+  static constexpr int KS = D / 16;          // QK k-steps over the head dim
+  static constexpr int DB = D / 32;          // 32-channel output blocks
+  static constexpr int CH = D / 8;           // 16-byte chunks per key row
+  static constexpr int KLD = D + 8;          // LDS row stride of K (halves)
+  static constexpr int VLD = KT + 8;         // LDS row stride of V^T (halves)
+  static constexpr int SEGT = 512;           // block-table entries staged per segment
+  static constexpr int KLOADS = CH / 4;                // K chunks per thread per tile (a
+                                                      // quarter of one key row)
+  static constexpr int VG_TOTAL = (KT / 4) * CH;       // 4-key V groups per tile
+  static constexpr int VGROUPS = (VG_TOTAL + 255) / 256; // ... per thread
+};
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VLD];
-  __shared__ uint8_t key_ok[KT];
-  __shared__ int sh_b, sh_tile, sh_ntiles, sh_hole;
+template <int D>
+__global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
+  using C = PrefillCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::KT * C::KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VLD];
+  __shared__ int32_t s_tbl[C::SEGT];
+  __shared__ uint8_t key_ok[2][C::KT];
+  __shared__ int sh_b, sh_tile;
 
   const SeqLayout& sl = a.s;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int l32 = lane & 31;
   const int hf = lane >> 5;
   const int kvh = blockIdx.y;
@@ -61,7 +76,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   if ((int)blockIdx.x == a.tiles) {
     // tokens owned by no request get zero rows (this kv head's columns)
     const int t0 = max(sl.cum[sl.batch], 0);
-    const int width = g * CH;
+    const int width = g * C::CH;
     for (int64_t i = tid; i < (int64_t)(sl.tokens - min(t0, sl.tokens)) * width; i += 256) {
       const int t = t0 + (int)(i / width);
       const int cc = (int)(i % width);
@@ -79,7 +94,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
       int nt = 0;
       if (bb < sl.batch) {
         const int ql = sl.cum[bb + 1] - sl.cum[bb];
-        if (ql >= 2) nt = (ql * g + ROWS - 1) / ROWS;
+        if (ql >= 2) nt = (ql * g + C::ROWS - 1) / C::ROWS;
       }
       int incl = nt;
 #pragma unroll
@@ -102,13 +117,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     if (lane == 0) {
       sh_b = fb;
       sh_tile = fn - 1 - ft;   // later (longer) tiles of a request are dispatched first
-      sh_ntiles = fn;
     }
   }
   __syncthreads();
-  const int b = sh_b;
+  const int b = __builtin_amdgcn_readfirstlane(sh_b);          // uniform per workgroup
   if (b < 0) return;
-  const int tile = sh_tile;
+  const int tile = __builtin_amdgcn_readfirstlane(sh_tile);
 
   const int t_begin = sl.cum[b];
   const int q_len = sl.cum[b + 1] - t_begin;
@@ -122,7 +136,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const uint16_t* vbase = a.value_cache + (int64_t)kvh * D;
 
   // this lane's query row
-  const int R = tile * ROWS + wave * 32 + l32;
+  const int R = tile * C::ROWS + wave * 32 + l32;
   const int j = R / g;
   const int hh = R - j * g;
   const bool row_ok = j < q_len && t_begin + j < sl.tokens;
@@ -130,21 +144,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const int t = t_begin + j;
   const int head = kvh * g + hh;
 
-  // key range of the whole tile
-  const int j_first = (tile * ROWS) / g;
-  const int j_last = min(q_len - 1, (tile * ROWS + ROWS - 1) / g);
+  // key range of the whole tile, and of this wave's rows (fast path)
+  const int j_first = (tile * C::ROWS) / g;
+  const int j_last = min(q_len - 1, (tile * C::ROWS + C::ROWS - 1) / g);
   const int hi = min(past + j_last + 1, cap);
   const int lo = a.window > 0 ? max(0, past + j_first + 1 - a.window) : 0;
-  // range of this wave's rows (for the unmasked-tile fast path)
-  const int wj0 = min((tile * ROWS + wave * 32) / g, q_len - 1);
-  const int wj1 = min((tile * ROWS + wave * 32 + 31) / g, q_len - 1);
+  const int wj0 = min((tile * C::ROWS + wave * 32) / g, q_len - 1);
+  const int wj1 = min((tile * C::ROWS + wave * 32 + 31) / g, q_len - 1);
   const int wpos_min = past + wj0;
   const int wpos_max = past + wj1;
 
   // Q fragments (B operand): row l32, channels 16*ks + 8*hf .. +7
-  h8 qf[KS];
+  h8 qf[C::KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
+  for (int ks = 0; ks < C::KS; ++ks) {
     u32x4 v = u32x4{0, 0, 0, 0};
     if (row_ok) {
       const uint16_t* qrow = a.query + (int64_t)t * HD + (int64_t)head * D;
@@ -160,64 +173,134 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     qf[ks] = as_h8(v);
   }
 
-  f16v acc[DB];
+  f16v acc[C::DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
   float m = kNegInf, lsum = 0.f;
   const bool softcap = a.use_softcap != 0;
 
-  for (int kt0 = lo & ~(KT - 1); kt0 < hi; kt0 += KT) {
+  const int kt_begin = lo & ~(C::KT - 1);
+  const int ntiles = hi > kt_begin ? (hi - kt_begin + C::KT - 1) / C::KT : 0;
+  int seg_first = -1;      // first block index staged in s_tbl
+  bool wg_hole = false;    // some key in [lo, hi) lives in an unmapped block
+
+  // Stage the block-table slice that starts at the block of key `k`.
+  auto stage_table = [&](int k) {
     __syncthreads();
-    if (tid == 0) sh_hole = 0;
-    __syncthreads();
-    // ---- stage K tile [KT][D] ----
-    for (int i = tid; i < KT * CH; i += 256) {
-      const int kk = i / CH;
-      const int cc = i - kk * CH;
-      const int tau = kt0 + kk;
-      u32x4 v = u32x4{0, 0, 0, 0};
-      bool ok = false;
-      if (tau >= lo && tau < hi) {
-        const int blk = bt[tau >> shift];
-        if (blk >= 0 && blk < sl.num_blocks) {
-          v = load16(kbase + ((int64_t)blk * (bmask + 1) + (tau & bmask)) * tok_stride + 8 * cc);
-          ok = true;
-        } else if (cc == 0) {
-          sh_hole = 1;
-        }
+    seg_first = k >> shift;
+    const int last_bi = (hi - 1) >> shift;
+    bool hole = false;
+    for (int i = tid; i < C::SEGT; i += 256) {
+      const int bi = seg_first + i;
+      int v = -1;
+      if (bi <= last_bi && bi < sl.maxblk) {
+        v = bt[bi];
+        if (v >= sl.num_blocks) v = -1;
+        const int k0 = bi << shift;
+        if (v < 0 && k0 + bmask >= lo && k0 < hi) hole = true;
       }
-      if (cc == 0) key_ok[kk] = ok;
-      store16(&Ks[kk * KLD + 8 * cc], v);
+      s_tbl[i] = v;
     }
-    // ---- stage V^T tile [D][KT] (groups of 4 keys, transposed in registers) ----
-    for (int i = tid; i < (KT / 4) * CH; i += 256) {
-      const int kg = i / CH;
-      const int cc = i - kg * CH;
-      const int kk0 = 4 * kg;
-      uint16_t vv[4][8];
+    wg_hole = __syncthreads_or(hole) || wg_hole;
+  };
+
+  // Global loads of one tile into registers (masked keys read block 0 and are
+  // zeroed when stored).
+  u32x4 kst[C::KLOADS];
+  u32x4 vst[C::VGROUPS][4];
+  uint32_t kok = 0, vok = 0;
+  auto load_tile = [&](int kt0) {
+    kok = 0;
+    vok = 0;
+    {
+      // K: thread = (key tid/4, lane-of-four tid%4 taking chunks 4i + tid%4): one
+      // table lookup, and four neighbouring lanes move 64 contiguous bytes
+      const int kk = tid >> 2, qq = tid & 3;
+      const int tau = kt0 + kk;
+      const bool in = tau >= lo && tau < hi;
+      const int blk = s_tbl[in ? (tau >> shift) - seg_first : 0];
+      const bool ok = in && blk >= 0;
+      kok = ok ? 1u : 0u;
+      const uint16_t* src = kbase + ((int64_t)(ok ? blk : 0) * (bmask + 1) + (tau & bmask)) * tok_stride +
+                            8 * qq;
+#pragma unroll
+      for (int i = 0; i < C::KLOADS; ++i) kst[i] = load16(src + 32 * i);   // chunk 4i + qq
+    }
+    {
+      // V: thread = (4-key group tid%16, chunk tid/16 [+16 per round]); the four
+      // keys share one block (tiles start at multiples of 64, blocks hold >= 16)
+      const int kg = tid % (C::KT / 4);
+      const int tau0 = kt0 + 4 * kg;
+      const int blk = s_tbl[tau0 >= lo && tau0 < hi ? (tau0 >> shift) - seg_first : 0];
+      const int64_t row0 = (int64_t)(blk >= 0 ? blk : 0) * (bmask + 1) + (tau0 & bmask);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int tau = kt0 + kk0 + r;
-        u32x4 v = u32x4{0, 0, 0, 0};
-        if (tau >= lo && tau < hi) {
-          const int blk = bt[tau >> shift];
-          if (blk >= 0 && blk < sl.num_blocks)
-            v = load16(vbase + ((int64_t)blk * (bmask + 1) + (tau & bmask)) * tok_stride + 8 * cc);
-        }
-        __builtin_memcpy(vv[r], &v, 16);
+        const int tau = tau0 + r;
+        vok |= (uint32_t)(tau >= lo && tau < hi && blk >= 0) << r;
       }
-      const int p0 = swap23(kk0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint2 w;
-        w.x = (uint32_t)vv[0][e] | ((uint32_t)vv[1][e] << 16);
-        w.y = (uint32_t)vv[2][e] | ((uint32_t)vv[3][e] << 16);
-        *reinterpret_cast<uint2*>(&Vt[(8 * cc + e) * VLD + p0]) = w;
+      for (int i = 0; i < C::VGROUPS; ++i) {
+        const int idx = tid + 256 * i;
+        if (idx >= C::VG_TOTAL) break;
+        const int cc = idx / (C::KT / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vst[i][r] = load16(vbase + (row0 + r) * tok_stride + 8 * cc);
       }
     }
+  };
+  // Store the loaded tile into LDS buffer `buf` (V transposed, key order swap23).
+  auto store_tile = [&](int buf) {
+    {
+      const int kk = tid >> 2, qq = tid & 3;
+      const bool ok = kok != 0;
+#pragma unroll
+      for (int i = 0; i < C::KLOADS; ++i)
+        store16(&Ks[buf][kk * C::KLD + 8 * (4 * i + qq)], ok ? kst[i] : u32x4{0, 0, 0, 0});
+      if (qq == 0) key_ok[buf][kk] = ok;
+    }
+#pragma unroll
+    for (int i = 0; i < C::VGROUPS; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx >= C::VG_TOTAL) break;
+      const int kg = idx % (C::KT / 4), cc = idx / (C::KT / 4);
+      const int p0 = swap23(4 * kg);
+      const uint32_t ok4 = vok;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t a0 = (ok4 & 1) ? vst[i][0][w] : 0u, a1 = (ok4 & 2) ? vst[i][1][w] : 0u;
+        const uint32_t a2 = (ok4 & 4) ? vst[i][2][w] : 0u, a3 = (ok4 & 8) ? vst[i][3][w] : 0u;
+        uint2 lo2, hi2;
+        lo2.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+        lo2.y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+        hi2.x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+        hi2.y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+        *reinterpret_cast<uint2*>(&Vt[buf][(8 * cc + 2 * w) * C::VLD + p0]) = lo2;
+        *reinterpret_cast<uint2*>(&Vt[buf][(8 * cc + 2 * w + 1) * C::VLD + p0]) = hi2;
+      }
+    }
+  };
+  auto need_segment = [&](int kt0) {
+    const int last = min(kt0 + C::KT, hi) - 1;
+    return (last >> shift) >= seg_first + C::SEGT;
+  };
+
+  if (ntiles > 0) {
+    stage_table(max(kt_begin, lo));
+    load_tile(kt_begin);
+    store_tile(0);
     __syncthreads();
+  }
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    const int kt0 = kt_begin + it * C::KT;
+    const bool more = it + 1 < ntiles;
+    if (more) {
+      if (need_segment(kt0 + C::KT)) stage_table(kt0 + C::KT);
+      load_tile(kt0 + C::KT);   // in flight during this tile's matrix work
+    }
 
     // ---- S^T = K . Q^T for two 32-key blocks ----
     f16v s[2];
@@ -226,64 +309,83 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const h8 ka = *reinterpret_cast<const h8*>(&Ks[(kb * 32 + l32) * KLD + 16 * ks + 8 * hf]);
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const h8 ka = *reinterpret_cast<const h8*>(&Ks[cur][(kb * 32 + l32) * C::KLD + 16 * ks + 8 * hf]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[ks], s[kb], 0, 0, 0);
       }
     }
 
-    // ---- scale / softcap / mask (log2 units) ----
-    const bool full = sh_hole == 0 && kt0 + KT - 1 <= wpos_min &&
-                      (a.window <= 0 || kt0 >= wpos_max - a.window + 1) && kt0 + KT <= hi &&
-                      kt0 >= lo;
+    // ---- mask, running max (on raw scores: scale and softcap are monotone) ----
+    const bool full = !wg_hole && kt0 >= lo && kt0 + C::KT <= hi && kt0 + C::KT - 1 <= wpos_min &&
+                      (a.window <= 0 || kt0 >= wpos_max - a.window + 1);
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x = s[kb][r];
-        x = softcap ? tanh_fast(x * a.cap_in) * a.cap_out : x * a.score_scale;
         if (!full) {
           const int kk = kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
           const int tau = kt0 + kk;
-          bool adm = tau <= pos && key_ok[kk];
+          bool adm = tau <= pos && (!wg_hole || key_ok[cur][kk]);
           if (a.window > 0) adm = adm && tau >= pos - a.window + 1;
           x = adm ? x : kNegInf;
+          s[kb][r] = x;
         }
-        s[kb][r] = x;
         mx = fmaxf(mx, x);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);
-    const float mu = mn == kNegInf ? 0.f : mn;
-    const float alpha = exp2_fast(m - mu);
-    m = mn;
-    lsum *= alpha;
+    // tile max in log2 units
+    mx = mx == kNegInf ? kNegInf
+                       : (softcap ? a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(
+                                                            exp2_fast(mx * a.cap_in2) + 1.0f))
+                                  : mx * a.score_scale);
+    if (__any(mx > m + kRescaleSlack)) {
+      const float mn = mx > m + kRescaleSlack ? mx : m;
+      const float alpha = exp2_fast(m - (mn == kNegInf ? 0.f : mn));
+      m = mn;
+      lsum *= alpha;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    }
+    const float mu = m == kNegInf ? 0.f : m;
 
     // ---- P (fp16) as B operand; O^T += V^T . P^T ----
+    // p = exp2(scale*log2e*s - m), or with softcap exp2(cap*log2e*tanh(s*scale/cap) - m)
+    // where tanh(y) = 1 - 2/(exp(2y) + 1) (exact limits +-1 for large |y|)
     h8 pf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(s[kb][r] - mu);
+        const float x = s[kb][r];
+        float e;
+        if (softcap) {
+          const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * a.cap_in2) + 1.0f);
+          e = __builtin_fmaf(th, a.cap_out, -mu);
+        } else {
+          e = __builtin_fmaf(x, a.score_scale, -mu);
+        }
+        float p = exp2_fast(e);
+        if (!full) p = x == kNegInf ? 0.f : p;   // masked (the softcap maps -inf to -cap)
         lsum += p;
         pf[2 * kb + (r >> 3)][r & 7] = (_Float16)p;
       }
     }
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const h8 va = *reinterpret_cast<const h8*>(&Vt[(db * 32 + l32) * VLD + 16 * ks + 8 * hf]);
+        const h8 va = *reinterpret_cast<const h8*>(&Vt[cur][(db * 32 + l32) * C::VLD + 16 * ks + 8 * hf]);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[ks], acc[db], 0, 0, 0);
       }
     }
+
+    if (more) store_tile(cur ^ 1);
+    __syncthreads();
   }
 
   // ---- normalise and store ----
@@ -292,7 +394,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   if (row_ok) {
     uint16_t* orow = a.out + (int64_t)t * HD + (int64_t)head * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = db * 32 + 8 * q4 + 4 * hf;
