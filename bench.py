@@ -7,6 +7,8 @@ split-KV decode + merge and the MFMA prefill.  Inputs are synthetic and
 already resident in device memory when the timed region starts.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+                    [--copy-calibration-mib N]
+    python bench.py --summarize-pmc counter_collection.csv ...
 
 Prints ONE JSON line.  ``value`` is the decode KV throughput of the whole
 step (algorithmic decode bytes / step time).  ``roofline`` describes the
@@ -76,17 +78,26 @@ def traffic_from_profiles(kernel_tag: str, src_hash: str):
         return None
 
 
-def kernel_source_hash() -> str:
+KERNEL_SOURCES = {
+    "decode": ("decode.hip", "pa_api.hip", "pa_device.h", "pa_internal.h"),
+    "prefill": ("prefill.hip", "pa_api.hip", "pa_device.h", "pa_internal.h"),
+}
+
+
+def kernel_source_hash(kind: str) -> str:
+    """Hash of the sources that decide one kernel's memory traffic (its own
+    file, the shared device helpers and the host planning code)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_append_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[kind]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()
 
 
-def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=96):
+def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=1024,
+                 target_seconds=10.0):
     """fp64 oracle on a bounded sample of the workload: the decode requests
     (GB/s of decode K/V bytes) or, for a prefill-only batch, the last rows of
     the first request (GFLOP/s).  Also returns the max-abs error of the GPU
@@ -111,12 +122,18 @@ def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=96):
     if prefill:
         ql = int(sub.q_lens[0])
         rows = list(range(max(0, ql - prefill_rows_sample), ql))
+    # the same sample is run until about target_seconds of CPU work have passed
+    reps = 0
     t0 = time.perf_counter()
-    ref = oracle.forward(sub.query, nk, nv, sub.cum, sub.past, sub.block_table,
-                         num_heads=sub.num_heads, kv_num_heads=sub.kv_num_heads,
-                         head_size=sub.head_size, scale=sub.scale, softcap=sub.softcap,
-                         local_window_size=sub.local_window_size, rows=rows, **rot)
-    dt = time.perf_counter() - t0
+    while True:
+        ref = oracle.forward(sub.query, nk, nv, sub.cum, sub.past, sub.block_table,
+                             num_heads=sub.num_heads, kv_num_heads=sub.kv_num_heads,
+                             head_size=sub.head_size, scale=sub.scale, softcap=sub.softcap,
+                             local_window_size=sub.local_window_size, rows=rows, **rot)
+        reps += 1
+        if time.perf_counter() - t0 >= target_seconds:
+            break
+    dt = (time.perf_counter() - t0) / reps
     prow = sub.extra["parent_rows"]
     if prefill:
         W = sub.local_window_size
@@ -130,13 +147,85 @@ def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=96):
                 "kind": "oracle",
                 "sample": f"last {len(rows)} query rows of request 0 of {w.name} "
                           f"({flops / 1e9:.2f} GFLOP over admitted pairs), full fp64 score "
-                          f"rows + softmax + PV, {dt:.1f} s"}, err
+                          f"rows + softmax + PV, {dt:.2f} s per pass, {reps} passes"}, err
     nbytes, _, _ = algorithmic_work(sub)
     err = float(np.max(np.abs(gpu_out[prow].astype(np.float64) - ref)))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{len(dec)} decode requests of {w.name} ({nbytes / 1e6:.1f} MB of K/V+Q/O), "
-                      f"gather + full scores + softmax + PV in fp64, {dt:.1f} s"}, err
+                      f"gather + full scores + softmax + PV in fp64, {dt:.2f} s per pass, "
+                      f"{reps} passes"}, err
+
+
+def _strip_params(name: str) -> str:
+    """Kernel name without its trailing parameter list."""
+    if not name.endswith(")"):
+        return name
+    depth = 0
+    for i in range(len(name) - 1, -1, -1):
+        depth += {")": 1, "(": -1}.get(name[i], 0)
+        if depth == 0:
+            return name[:i]
+    return name
+
+
+COPY_KERNEL = "neg_kernel"
+
+
+def _pmc_means(path):
+    import csv
+    from collections import defaultdict
+    acc = defaultdict(list)
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            acc[(_strip_params(row.get("Kernel_Name", "?")), row["Counter_Name"])].append(
+                float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def record_traffic(tag, kernel, fetch_csv, write_csv, copy_mib):
+    """HBM bytes per launch = FETCH_SIZE * (copy bytes / copy FETCH_SIZE)
+    + WRITE_SIZE * (copy bytes / copy WRITE_SIZE), each counter in KiB per
+    dispatch, the copy kernel reading and writing COPY_MIB MiB."""
+    copy_kib = float(copy_mib) * 1024.0
+    out = {}
+    for ctr, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        means = _pmc_means(path)
+        cal = [v for (k, c), v in means.items() if COPY_KERNEL in k and c == ctr]
+        val = [v for (k, c), v in means.items() if kernel in k and c == ctr]
+        if len(cal) != 1 or len(val) != 1:
+            raise SystemExit(f"{path}: expected one copy kernel and one '{kernel}' kernel "
+                             f"with {ctr}, found {len(cal)} and {len(val)}")
+        out[ctr] = (val[0], copy_kib / cal[0])
+    nbytes = sum(v * f for v, f in out.values()) * 1024.0
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[tag] = {"source_sha256": kernel_source_hash(tag.split(":")[0]),
+                 "bytes_per_launch": round(nbytes),
+                 "fetch_kib": round(out["FETCH_SIZE"][0], 1),
+                 "fetch_scale": round(out["FETCH_SIZE"][1], 5),
+                 "write_kib": round(out["WRITE_SIZE"][0], 1),
+                 "write_scale": round(out["WRITE_SIZE"][1], 5)}
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({tag: data[tag]}))
+
+
+def summarize_pmc(paths):
+    """Mean of each counter per kernel over the dispatches of rocprofv3
+    ``counter_collection.csv`` files (values as the profiler reports them)."""
+    import csv
+    from collections import defaultdict
+    acc = defaultdict(list)
+    for path in paths:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                short = _strip_params(row.get("Kernel_Name", "?"))[:90]
+                acc[(short, row["Counter_Name"])].append(float(row["Counter_Value"]))
+    print(f"{'kernel':90s} {'counter':28s} {'dispatches':>10s} {'mean':>16s}")
+    for (k, c), v in sorted(acc.items()):
+        print(f"{k:90s} {c:28s} {len(v):10d} {sum(v) / len(v):16.1f}")
 
 
 def main():
@@ -146,7 +235,25 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain fp16 copy kernel over this many MiB (read N, "
+                         "write N), three times, to scale HBM byte counters")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="print per-kernel mean counter values of rocprofv3 counter "
+                         "CSV files and exit (no GPU use)")
+    ap.add_argument("--record-traffic", nargs=5,
+                    metavar=("TAG", "KERNEL", "FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
+                    help="store HBM bytes per launch of KERNEL (substring of the kernel "
+                         "name) under TAG in profiles/traffic.json, from a FETCH_SIZE and a "
+                         "WRITE_SIZE counter run that both include the copy calibration of "
+                         "COPY_MIB MiB, and exit (no GPU use)")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
@@ -156,6 +263,22 @@ def main():
 
     import paged_kv_cache_append_amd as pa
     from paged_kv_cache_append_amd import workloads as wl
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for i in range(3):
+            ev[i].record()
+            torch.neg(src, out=dst)
+        ev[3].record()
+        torch.cuda.synchronize()
+        ms = ev[2].elapsed_time(ev[3])   # the last launch, caches warm
+        print(f"copy calibration: {args.copy_calibration_mib} MiB read + "
+              f"{args.copy_calibration_mib} MiB written per launch, "
+              f"{2 * n * 2 / (ms * 1e-3) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+        del src, dst
 
     w = wl.make_workload(args.config)
     dev = wl.to_device(w)
@@ -209,19 +332,18 @@ def main():
         (ms_step * 1e-3)
 
     # dominant kernel: the one with the larger roofline time
-    src_hash = kernel_source_hash()
     if dec_bytes / (HBM_PEAK_GBS * 1e9) >= pf_flops / (MFMA_F16_PEAK_TFS * 1e12):
         achieved = dec_bytes / (per["decode"] * 1e-6) / 1e9 if per["decode"] else None
         roof = {"bound": "hbm", "kernel": "decode", "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-                "traffic": traffic_from_profiles(f"decode:{w.name}", src_hash),
+                "traffic": traffic_from_profiles(f"decode:{w.name}", kernel_source_hash("decode")),
                 "algorithmic_bytes_per_launch": dec_bytes}
     else:
         achieved = pf_flops / (per["prefill"] * 1e-6) / 1e12 if per["prefill"] else None
         roof = {"bound": "mfma", "kernel": "prefill", "achieved": achieved,
                 "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": (achieved / MFMA_F16_PEAK_TFS) if achieved else None,
-                "traffic": traffic_from_profiles(f"prefill:{w.name}", src_hash),
+                "traffic": traffic_from_profiles(f"prefill:{w.name}", kernel_source_hash("prefill")),
                 "algorithmic_flops_per_launch": pf_flops}
     for k in ("achieved", "frac"):
         if roof[k] is not None:
