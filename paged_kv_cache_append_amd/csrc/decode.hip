@@ -70,7 +70,24 @@ __device__ __forceinline__ bool resolve_row(const SeqLayout& s, int token_mode, 
   return true;
 }
 
-__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
+// max / sum of a value and the one 16 (resp. 32) lanes away: one lane-swap
+// instruction instead of a trip through the LDS crossbar
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // ---------------------------------------------------------------------------
 // plan: one workgroup lists (row, split) entries; zeroes orphan token rows
@@ -207,7 +224,7 @@ __device__ __forceinline__ void store_vt4(uint16_t* vt, int ld, int c, int p0, u
   }
 }
 
-template <int D>
+template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : D <= 128 ? 2 : 1)))
 void decode_kernel(const DecodeArgs a) {
@@ -230,7 +247,6 @@ void decode_kernel(const DecodeArgs a) {
   int32_t* tbl = s_tbl[wave];
   const int shift = sl.block_shift;
   const int64_t tok_stride = (int64_t)a.kv_heads * D;
-  const bool softcap = a.use_softcap != 0;
 
   for (int item = blockIdx.x * kDecodeWaves + wave; item < total; item += nworkers) {
     const int e = item / HC;
@@ -341,7 +357,10 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             float v = s[sb][rr];
-            v = softcap ? tanh_fast(v * a.cap_in) * a.cap_out : v * a.score_scale;
+            if constexpr (SOFTCAP)
+              v = tanh_fast(v * a.cap_in) * a.cap_out;
+            else
+              v = v * a.score_scale;
             if (edge) {
               const int key = k0 + 16 * sb + 4 * q + rr;
               const bool ok = key < seg_hi && tbl[(key >> shift) - first_bi] >= 0;
@@ -351,7 +370,7 @@ void decode_kernel(const DecodeArgs a) {
             mx = fmaxf(mx, v);
           }
         }
-        mx = xor_max(xor_max(mx, 16), 32);
+        mx = xor32_max(xor16_max(mx));
         // lazy rescale: keep the running max unless the tile exceeds it by more
         // than kRescaleSlack (probabilities then stay below 2^kRescaleSlack),
         // so most tiles skip touching the accumulators
@@ -402,8 +421,7 @@ void decode_kernel(const DecodeArgs a) {
     }
 
     // ---- epilogue: lane (q, l16) holds head l16, channels 16db + 4q + [0,4) ----
-    float lt = lsum + __shfl_xor(lsum, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = xor32_sum(xor16_sum(lsum));
     if (head_ok) {
       const int h = h0 + l16;
       if (r.nsplit <= 1) {
@@ -496,12 +514,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   }
 }
 
-template <int D>
+template <int D, bool SOFTCAP>
 int occupancy_wg() {
   static int cached = 0;
   if (!cached) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, SOFTCAP>, 256, 0) != hipSuccess ||
         n <= 0)
       n = 1;
     cached = n;
@@ -509,13 +527,21 @@ int occupancy_wg() {
   return cached;
 }
 
+template <int D>
+void launch_decode_variant(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t st) {
+  if (a.use_softcap)
+    hipLaunchKernelGGL((decode_kernel<D, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, false>), grid, block, 0, st, a);
+}
+
 }  // namespace
 
-int decode_workgroups_per_cu(int head_size) {
+int decode_workgroups_per_cu(int head_size, bool softcap) {
   switch (head_size) {
-    case 64: return occupancy_wg<64>();
-    case 128: return occupancy_wg<128>();
-    case 256: return occupancy_wg<256>();
+    case 64: return softcap ? occupancy_wg<64, true>() : occupancy_wg<64, false>();
+    case 128: return softcap ? occupancy_wg<128, true>() : occupancy_wg<128, false>();
+    case 256: return softcap ? occupancy_wg<256, true>() : occupancy_wg<256, false>();
     default: return 1;
   }
 }
@@ -528,9 +554,9 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
 hipError_t launch_decode(const DecodeArgs& a, int head_size, int workgroups, hipStream_t st) {
   const dim3 grid(workgroups), block(64 * kDecodeWaves);
   switch (head_size) {
-    case 64: hipLaunchKernelGGL(decode_kernel<64>, grid, block, 0, st, a); break;
-    case 128: hipLaunchKernelGGL(decode_kernel<128>, grid, block, 0, st, a); break;
-    case 256: hipLaunchKernelGGL(decode_kernel<256>, grid, block, 0, st, a); break;
+    case 64: launch_decode_variant<64>(a, grid, block, st); break;
+    case 128: launch_decode_variant<128>(a, grid, block, st); break;
+    case 256: launch_decode_variant<256>(a, grid, block, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

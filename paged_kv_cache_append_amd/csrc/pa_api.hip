@@ -420,7 +420,8 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
       StageScope scope(PA_STAGE_PLAN, s);
       if ((st = device_status(pa::launch_plan(pa_, s), "plan kernel launch")) != PA_OK) return st;
       const int64_t bound = (int64_t)pl.rows * pl.max_splits * hc;
-      const int64_t resident = (int64_t)pa::decode_workgroups_per_cu(D) * device_cus();
+      const int64_t resident =
+          (int64_t)pa::decode_workgroups_per_cu(D, d.use_softcap != 0) * device_cus();
       wgs = std::min<int64_t>((bound + pa::kDecodeWaves - 1) / pa::kDecodeWaves, resident);
     } else {
       wgs = ((int64_t)pl.rows * hc + pa::kDecodeWaves - 1) / pa::kDecodeWaves;

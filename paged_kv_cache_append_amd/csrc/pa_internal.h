@@ -133,7 +133,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int head_size, int workgroups, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
-int decode_workgroups_per_cu(int head_size);   // resident decode workgroups per CU
+int decode_workgroups_per_cu(int head_size, bool softcap);   // resident decode workgroups per CU
 hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st);
 
 constexpr int kPrefillRows = 128;   // query rows (token x head) per prefill workgroup

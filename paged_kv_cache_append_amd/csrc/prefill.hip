@@ -54,7 +54,17 @@ struct PrefillCfg {
   static constexpr int VGROUPS = (VG_TOTAL + 255) / 256; // ... per thread
 };
 
-template <int D>
+// max / sum of a value with the one 32 lanes away (one lane-swap instruction)
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   using C = PrefillCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::KT * C::KLD];
@@ -179,7 +189,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
   float m = kNegInf, lsum = 0.f;
-  const bool softcap = a.use_softcap != 0;
 
   const int kt_begin = lo & ~(C::KT - 1);
   const int ntiles = hi > kt_begin ? (hi - kt_begin + C::KT - 1) / C::KT : 0;
@@ -303,13 +312,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     }
 
     // ---- S^T = K . Q^T for two 32-key blocks ----
+    // (the two 32-key blocks alternate so consecutive MFMAs are independent)
     f16v s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
+    for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         const h8 ka = *reinterpret_cast<const h8*>(&Ks[cur][(kb * 32 + l32) * C::KLD + 16 * ks + 8 * hf]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[ks], s[kb], 0, 0, 0);
       }
@@ -318,27 +330,34 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     // ---- mask, running max (on raw scores: scale and softcap are monotone) ----
     const bool full = !wg_hole && kt0 >= lo && kt0 + C::KT <= hi && kt0 + C::KT - 1 <= wpos_min &&
                       (a.window <= 0 || kt0 >= wpos_max - a.window + 1);
-    float mx = kNegInf;
+    if (!full) {
+      // branch-free admission test; unmapped blocks only matter when the
+      // workgroup's key range has a hole (a uniform, rare branch)
+      const int wlo = a.window > 0 ? pos - a.window + 1 : INT32_MIN;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kb][r];
-        if (!full) {
-          const int kk = kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const int tau = kt0 + kk;
-          bool adm = tau <= pos && (!wg_hole || key_ok[cur][kk]);
-          if (a.window > 0) adm = adm && tau >= pos - a.window + 1;
-          x = adm ? x : kNegInf;
-          s[kb][r] = x;
+        for (int r = 0; r < 16; ++r) {
+          const int tau = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          s[kb][r] = (tau <= pos) & (tau >= wlo) ? s[kb][r] : kNegInf;
         }
-        mx = fmaxf(mx, x);
+      if (wg_hole) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!key_ok[cur][kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)]) s[kb][r] = kNegInf;
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = xor32_max(mx);
     // tile max in log2 units
     mx = mx == kNegInf ? kNegInf
-                       : (softcap ? a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(
+                       : (SOFTCAP ? a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(
                                                             exp2_fast(mx * a.cap_in2) + 1.0f))
                                   : mx * a.score_scale);
     if (__any(mx > m + kRescaleSlack)) {
@@ -363,14 +382,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
       for (int r = 0; r < 16; ++r) {
         const float x = s[kb][r];
         float e;
-        if (softcap) {
+        if constexpr (SOFTCAP) {
           const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * a.cap_in2) + 1.0f);
           e = __builtin_fmaf(th, a.cap_out, -mu);
+          e = x == kNegInf ? kNegInf : e;   // masked (the softcap maps -inf to -cap)
         } else {
-          e = __builtin_fmaf(x, a.score_scale, -mu);
+          e = __builtin_fmaf(x, a.score_scale, -mu);   // -inf for a masked key
         }
-        float p = exp2_fast(e);
-        if (!full) p = x == kNegInf ? 0.f : p;   // masked (the softcap maps -inf to -cap)
+        const float p = exp2_fast(e);
         lsum += p;
         pf[2 * kb + (r >> 3)][r & 7] = (_Float16)p;
       }
@@ -389,7 +408,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   }
 
   // ---- normalise and store ----
-  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  const float lt = xor32_sum(lsum);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (row_ok) {
     uint16_t* orow = a.out + (int64_t)t * HD + (int64_t)head * D;
@@ -407,13 +426,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   }
 }
 
+template <int D>
+void launch_variant(const PrefillArgs& a, dim3 grid, hipStream_t st) {
+  if (a.use_softcap)
+    hipLaunchKernelGGL((prefill_kernel<D, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, false>), grid, dim3(256), 0, st, a);
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st) {
   switch (head_size) {
-    case 64: hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(256), 0, st, a); break;
-    case 256: hipLaunchKernelGGL(prefill_kernel<256>, grid, dim3(256), 0, st, a); break;
+    case 64: launch_variant<64>(a, grid, st); break;
+    case 128: launch_variant<128>(a, grid, st); break;
+    case 256: launch_variant<256>(a, grid, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
