@@ -3,7 +3,8 @@
     python -m paged_kv_cache_append_amd.build [-v]
 
 Every call recompiles (objects go to ``_build/``, the library next to this
-file).  Device code is compiled with packed-fp32 instruction selection off.
+file).  Device code is compiled with packed-fp32 instruction selection off
+and with MFMA accumulators in VGPRs.
 """
 from __future__ import annotations
 
@@ -32,7 +33,10 @@ def hipcc() -> str:
 def compile_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep MFMA accumulators in ordinary VGPRs: otherwise loop-carried
+            # accumulators are copied between register files on every tile
+            "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _run(cmd, verbose):
