@@ -48,11 +48,27 @@ struct PrefillCfg {
   static constexpr int KLD = D + 8;          // LDS row stride of K (halves)
   static constexpr int VLD = KT + 8;         // LDS row stride of V^T (halves)
   static constexpr int SEGT = 512;           // block-table entries staged per segment
+  static constexpr int PIPE = KS < 4 ? KS : 4;   // operand reads in flight (k-steps)
   static constexpr int KLOADS = CH / 4;                // K chunks per thread per tile (a
                                                       // quarter of one key row)
   static constexpr int VG_TOTAL = (KT / 4) * CH;       // 4-key V groups per tile
   static constexpr int VGROUPS = (VG_TOTAL + 255) / 256; // ... per thread
 };
+
+// Scheduling order of a block of N MFMAs fed by N LDS reads: the first AHEAD
+// reads, then one MFMA per further read, then the remaining MFMAs, so every
+// operand is requested AHEAD MFMA issue slots before its use.  The compiler
+// otherwise pulls each read down next to its MFMA to save registers.
+template <int AHEAD, int N>
+__device__ __forceinline__ void pipeline_order() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);   // DS reads
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
 
 // max / sum of a value with the one 32 lanes away (one lane-swap instruction)
 __device__ __forceinline__ float xor32_max(float x) {
@@ -182,6 +198,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     }
     qf[ks] = as_h8(v);
   }
+  // Let the query loads land here: otherwise the first MFMA of every tile
+  // would wait for them with a full vmcnt(0), i.e. also for the next tile's
+  // loads that were just issued.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   f16v acc[C::DB];
 #pragma unroll
@@ -312,19 +332,33 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     }
 
     // ---- S^T = K . Q^T for two 32-key blocks ----
-    // (the two 32-key blocks alternate so consecutive MFMAs are independent)
+    // The two 32-key blocks alternate so consecutive MFMAs are independent,
+    // and the LDS operand reads run PIPE steps ahead of the MFMAs that use
+    // them (a read's latency is several MFMA issue slots).
     f16v s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    {
+      const uint16_t* kt = &Ks[cur][l32 * C::KLD + 8 * hf];
+      auto kread = [&](int ks, int kb) {
+        return *reinterpret_cast<const h8*>(kt + kb * 32 * C::KLD + 16 * ks);
+      };
+      h8 kf[C::PIPE][2];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
+      for (int i = 0; i < C::PIPE; ++i)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const h8 ka = *reinterpret_cast<const h8*>(&Ks[cur][(kb * 32 + l32) * C::KLD + 16 * ks + 8 * hf]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[ks], s[kb], 0, 0, 0);
+        for (int kb = 0; kb < 2; ++kb) kf[i][kb] = kread(i, kb);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks % C::PIPE][kb], qf[ks], s[kb], 0, 0, 0);
+          if (ks + C::PIPE < C::KS) kf[ks % C::PIPE][kb] = kread(ks + C::PIPE, kb);
+        }
       }
+      pipeline_order<2 * C::PIPE, 2 * C::KS>();
     }
 
     // ---- mask, running max (on raw scores: scale and softcap are monotone) ----
@@ -394,13 +428,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
         pf[2 * kb + (r >> 3)][r & 7] = (_Float16)p;
       }
     }
+    {
+      // same pipelining; the DB output blocks alternate inside each k-step
+      constexpr int NV = 4 * C::DB;
+      const uint16_t* vt = &Vt[cur][l32 * C::VLD + 8 * hf];
+      auto vread = [&](int i) {
+        return *reinterpret_cast<const h8*>(vt + (i % C::DB) * 32 * C::VLD + 16 * (i / C::DB));
+      };
+      h8 vf[2 * C::PIPE];
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
+      for (int i = 0; i < 2 * C::PIPE; ++i) vf[i] = vread(i);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const h8 va = *reinterpret_cast<const h8*>(&Vt[cur][(db * 32 + l32) * C::VLD + 16 * ks + 8 * hf]);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[ks], acc[db], 0, 0, 0);
+      for (int i = 0; i < NV; ++i) {
+        const int db = i % C::DB, ks = i / C::DB;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % (2 * C::PIPE)], pf[ks], acc[db], 0, 0, 0);
+        if (i + 2 * C::PIPE < NV) vf[i % (2 * C::PIPE)] = vread(i + 2 * C::PIPE);
       }
+      pipeline_order<2 * C::PIPE, NV>();
     }
 
     if (more) store_tile(cur ^ 1);
