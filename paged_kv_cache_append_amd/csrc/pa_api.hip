@@ -59,10 +59,17 @@ struct StageScope {
     if (!g_timing.enabled || g_timing.used >= g_timing.stage.size()) return;
     slot = (int)g_timing.used++;
     g_timing.stage[slot] = stg;
-    hipEventRecord(g_timing.events[2 * slot], st);
+    if (hipEventRecord(g_timing.events[2 * slot], st) != hipSuccess) {
+      g_timing.stage[slot] = -1;   // not counted
+      slot = -1;
+    }
   }
   ~StageScope() {
-    if (slot >= 0) hipEventRecord(g_timing.events[2 * slot + 1], st);
+    if (slot < 0) return;
+    if (hipEventRecord(g_timing.events[2 * slot + 1], st) != hipSuccess) {
+      std::lock_guard<std::mutex> lk(g_timing.mu);
+      g_timing.stage[slot] = -1;
+    }
   }
 };
 
@@ -484,7 +491,7 @@ pa_status pa_timing_enable(int32_t max_launches) {
   if (max_launches <= 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "max_launches: expected > 0, got %d", max_launches);
   std::lock_guard<std::mutex> lk(g_timing.mu);
-  for (hipEvent_t e : g_timing.events) hipEventDestroy(e);
+  for (hipEvent_t e : g_timing.events) (void)hipEventDestroy(e);
   g_timing.events.assign(2 * (size_t)max_launches, nullptr);
   g_timing.stage.assign(max_launches, -1);
   g_timing.used = 0;
@@ -501,7 +508,7 @@ pa_status pa_timing_enable(int32_t max_launches) {
 
 pa_status pa_timing_disable(void) {
   std::lock_guard<std::mutex> lk(g_timing.mu);
-  for (hipEvent_t e : g_timing.events) hipEventDestroy(e);
+  for (hipEvent_t e : g_timing.events) (void)hipEventDestroy(e);
   g_timing.events.clear();
   g_timing.stage.clear();
   g_timing.used = 0;

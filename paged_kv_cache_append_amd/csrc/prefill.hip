@@ -17,14 +17,17 @@
 // so that the score accumulator already has the B-operand layout of
 //   O^T[d][row] += V^T[d][key] . P^T[key][row]
 // and the probabilities go from registers to the MFMA without an LDS round
-// trip.  V is stored transposed in LDS with the key order of the accumulator
-// layout (bits 2 and 3 of the key index swapped).  K and V^T tiles are double
-// buffered: the next tile's global loads are issued before the current tile's
-// MFMAs and land in LDS after them, so one barrier per tile suffices and the
-// memory latency hides behind the matrix work.  The block-table slice of the
-// workgroup's key range is staged in LDS.  Scores are in log2 units; the
-// running max is shared by the two lanes of a row with one swap per tile and
-// is only raised when a tile exceeds it by more than 8 (lazy rescale).
+// trip.  K and V tiles of 64 keys move from the pool straight into LDS with
+// direct loads (no staging registers), double buffered: the next tile streams
+// in while the current one is multiplied, and one barrier per tile suffices.
+// V keeps its natural row layout in LDS; the V^T operand comes from
+// transposing LDS reads.  Operand reads are issued a few MFMAs ahead of their
+// use.  The block-table slice of the workgroup's key range is staged in LDS.
+// Scores are in log2 units; the running max is shared by the two lanes of a
+// row with one lane swap per tile and is only raised when a tile exceeds it by
+// more than 8 (lazy rescale).
+#include <type_traits>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -33,10 +36,7 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;   // log2 units
-
-__device__ __forceinline__ int swap23(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct PrefillCfg {
@@ -45,27 +45,51 @@ struct PrefillCfg {
   static constexpr int KS = D / 16;          // QK k-steps over the head dim
   static constexpr int DB = D / 32;          // 32-channel output blocks
   static constexpr int CH = D / 8;           // 16-byte chunks per key row
-  static constexpr int KLD = D + 8;          // LDS row stride of K (halves)
-  static constexpr int VLD = KT + 8;         // LDS row stride of V^T (halves)
+  static constexpr int RPS = 64 / CH;        // key rows per 1 KB slot (one direct load)
+  static constexpr int NS = 32 / RPS;        // slots per 32-key block
+  static constexpr int SLOTS = KT / RPS;     // slots per tile
+  static constexpr int KSLOT = 1024 + 16;    // K slot stride (bytes): rows read together
+                                             // by 8 lanes fall 16 bytes apart
+  static constexpr int VSLOT = 1024 + 64;    // V slot stride: the 4 rows of a transposing
+                                             // read fall 64 bytes apart
+  static constexpr int DMA = SLOTS / 4;      // direct loads per wave per tile (K or V)
   static constexpr int SEGT = 512;           // block-table entries staged per segment
   static constexpr int PIPE = KS < 4 ? KS : 4;   // operand reads in flight (k-steps)
-  static constexpr int KLOADS = CH / 4;                // K chunks per thread per tile (a
-                                                      // quarter of one key row)
-  static constexpr int VG_TOTAL = (KT / 4) * CH;       // 4-key V groups per tile
-  static constexpr int VGROUPS = (VG_TOTAL + 255) / 256; // ... per thread
 };
 
-// Scheduling order of a block of N MFMAs fed by N LDS reads: the first AHEAD
-// reads, then one MFMA per further read, then the remaining MFMAs, so every
-// operand is requested AHEAD MFMA issue slots before its use.  The compiler
-// otherwise pulls each read down next to its MFMA to save registers.
-template <int AHEAD, int N>
+// Tile layout in LDS: key row r (0..63) of the tile lives in slot
+// (r / 32) * NS + (r % NS) at row position ((r % 32) / NS) within the slot;
+// a slot is one contiguous 1 KB direct load plus padding, and every operand
+// address is a base register plus an immediate offset.
+template <int D>
+__device__ __forceinline__ int row_byte(int r, int slot_bytes) {
+  using C = PrefillCfg<D>;
+  return ((r >> 5) * C::NS + (r % C::NS)) * slot_bytes + ((r & 31) / C::NS) * (2 * D);
+}
+
+// Source of the rows that must read as zero (never written).
+__device__ __attribute__((aligned(16))) uint16_t g_zero_row[256];
+
+__device__ __forceinline__ void dma16(const uint16_t* src, char* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// vmcnt(0), no wait on the LDS/scalar counter
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Scheduling order of a block of N MFMAs fed by RPM LDS reads each: the
+// reads of the first AHEAD MFMAs, then one MFMA per further group of reads,
+// then the remaining MFMAs, so every operand is requested AHEAD MFMA issue
+// slots before its use.  The compiler otherwise pulls each read down next to
+// its MFMA to save registers.
+template <int AHEAD, int N, int RPM>
 __device__ __forceinline__ void pipeline_order() {
-  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);   // DS reads
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * RPM, 0);   // DS reads
 #pragma unroll
   for (int i = 0; i < N - AHEAD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);         // DS reads
   }
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
@@ -83,10 +107,12 @@ __device__ __forceinline__ float xor32_sum(float x) {
 template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   using C = PrefillCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::KT * C::KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VLD];
+  __shared__ __attribute__((aligned(1024))) char K0[C::SLOTS * C::KSLOT];
+  __shared__ __attribute__((aligned(1024))) char K1[C::SLOTS * C::KSLOT];
+  __shared__ __attribute__((aligned(1024))) char V0[C::SLOTS * C::VSLOT];
+  __shared__ __attribute__((aligned(1024))) char V1[C::SLOTS * C::VSLOT];
   __shared__ int32_t s_tbl[C::SEGT];
-  __shared__ uint8_t key_ok[2][C::KT];
+  __shared__ uint8_t ok0[C::KT], ok1[C::KT];
   __shared__ int sh_b, sh_tile;
 
   const SeqLayout& sl = a.s;
@@ -235,79 +261,27 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     wg_hole = __syncthreads_or(hole) || wg_hole;
   };
 
-  // Global loads of one tile into registers (masked keys read block 0 and are
-  // zeroed when stored).
-  u32x4 kst[C::KLOADS];
-  u32x4 vst[C::VGROUPS][4];
-  uint32_t kok = 0, vok = 0;
-  auto load_tile = [&](int kt0) {
-    kok = 0;
-    vok = 0;
-    {
-      // K: thread = (key tid/4, lane-of-four tid%4 taking chunks 4i + tid%4): one
-      // table lookup, and four neighbouring lanes move 64 contiguous bytes
-      const int kk = tid >> 2, qq = tid & 3;
-      const int tau = kt0 + kk;
+  // Direct loads of one tile into LDS buffer B: wave w fills slots w, w + 4,
+  // ...; lane i of a slot load moves chunk i % CH of key row i / CH of that
+  // slot.  Keys outside [lo, hi) or in an unmapped block read a zero row.
+  auto kbuf = [&](auto B) -> char* { if constexpr (B() == 0) return K0; else return K1; };
+  auto vbuf = [&](auto B) -> char* { if constexpr (B() == 0) return V0; else return V1; };
+  auto okbuf = [&](auto B) -> uint8_t* { if constexpr (B() == 0) return ok0; else return ok1; };
+  auto dma_tile = [&](int kt0, auto B) {
+#pragma unroll
+    for (int mi = 0; mi < C::DMA; ++mi) {
+      const int slot = wave + 4 * mi;
+      const int row = (slot / C::NS) * 32 + (slot % C::NS) + C::NS * (lane / C::CH);
+      const int chunk = lane % C::CH;
+      const int tau = kt0 + row;
       const bool in = tau >= lo && tau < hi;
       const int blk = s_tbl[in ? (tau >> shift) - seg_first : 0];
       const bool ok = in && blk >= 0;
-      kok = ok ? 1u : 0u;
-      const uint16_t* src = kbase + ((int64_t)(ok ? blk : 0) * (bmask + 1) + (tau & bmask)) * tok_stride +
-                            8 * qq;
-#pragma unroll
-      for (int i = 0; i < C::KLOADS; ++i) kst[i] = load16(src + 32 * i);   // chunk 4i + qq
-    }
-    {
-      // V: thread = (4-key group tid%16, chunk tid/16 [+16 per round]); the four
-      // keys share one block (tiles start at multiples of 64, blocks hold >= 16)
-      const int kg = tid % (C::KT / 4);
-      const int tau0 = kt0 + 4 * kg;
-      const int blk = s_tbl[tau0 >= lo && tau0 < hi ? (tau0 >> shift) - seg_first : 0];
-      const int64_t row0 = (int64_t)(blk >= 0 ? blk : 0) * (bmask + 1) + (tau0 & bmask);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tau = tau0 + r;
-        vok |= (uint32_t)(tau >= lo && tau < hi && blk >= 0) << r;
-      }
-#pragma unroll
-      for (int i = 0; i < C::VGROUPS; ++i) {
-        const int idx = tid + 256 * i;
-        if (idx >= C::VG_TOTAL) break;
-        const int cc = idx / (C::KT / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vst[i][r] = load16(vbase + (row0 + r) * tok_stride + 8 * cc);
-      }
-    }
-  };
-  // Store the loaded tile into LDS buffer `buf` (V transposed, key order swap23).
-  auto store_tile = [&](int buf) {
-    {
-      const int kk = tid >> 2, qq = tid & 3;
-      const bool ok = kok != 0;
-#pragma unroll
-      for (int i = 0; i < C::KLOADS; ++i)
-        store16(&Ks[buf][kk * C::KLD + 8 * (4 * i + qq)], ok ? kst[i] : u32x4{0, 0, 0, 0});
-      if (qq == 0) key_ok[buf][kk] = ok;
-    }
-#pragma unroll
-    for (int i = 0; i < C::VGROUPS; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx >= C::VG_TOTAL) break;
-      const int kg = idx % (C::KT / 4), cc = idx / (C::KT / 4);
-      const int p0 = swap23(4 * kg);
-      const uint32_t ok4 = vok;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a0 = (ok4 & 1) ? vst[i][0][w] : 0u, a1 = (ok4 & 2) ? vst[i][1][w] : 0u;
-        const uint32_t a2 = (ok4 & 4) ? vst[i][2][w] : 0u, a3 = (ok4 & 8) ? vst[i][3][w] : 0u;
-        uint2 lo2, hi2;
-        lo2.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-        lo2.y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-        hi2.x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-        hi2.y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-        *reinterpret_cast<uint2*>(&Vt[buf][(8 * cc + 2 * w) * C::VLD + p0]) = lo2;
-        *reinterpret_cast<uint2*>(&Vt[buf][(8 * cc + 2 * w + 1) * C::VLD + p0]) = hi2;
-      }
+      const int64_t off =
+          ((int64_t)(ok ? blk : 0) * (bmask + 1) + (tau & bmask)) * tok_stride + 8 * chunk;
+      dma16(ok ? kbase + off : g_zero_row + 8 * chunk, kbuf(B) + slot * C::KSLOT);
+      dma16(ok ? vbase + off : g_zero_row + 8 * chunk, vbuf(B) + slot * C::VSLOT);
+      if (chunk == 0) okbuf(B)[row] = ok;
     }
   };
   auto need_segment = [&](int kt0) {
@@ -315,25 +289,29 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     return (last >> shift) >= seg_first + C::SEGT;
   };
 
+  using Buf0 = std::integral_constant<int, 0>;
+  using Buf1 = std::integral_constant<int, 1>;
   if (ntiles > 0) {
     stage_table(max(kt_begin, lo));
-    load_tile(kt_begin);
-    store_tile(0);
+    dma_tile(kt_begin, Buf0{});
+    wait_vmem();
     __syncthreads();
   }
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
+  // One key tile from buffer B while the next tile streams into the other
+  // buffer.  Both buffers are separate LDS objects named statically, so the
+  // compiler can tell the direct loads into one from the reads of the other
+  // and does not wait for the prefetch before computing on the current tile.
+  auto step = [&](int it, auto B) {
     const int kt0 = kt_begin + it * C::KT;
-    const bool more = it + 1 < ntiles;
-    if (more) {
+    if (it + 1 < ntiles) {
       if (need_segment(kt0 + C::KT)) stage_table(kt0 + C::KT);
-      load_tile(kt0 + C::KT);   // in flight during this tile's matrix work
+      dma_tile(kt0 + C::KT, std::integral_constant<int, 1 - B()>{});
     }
 
     // ---- S^T = K . Q^T for two 32-key blocks ----
     // The two 32-key blocks alternate so consecutive MFMAs are independent,
-    // and the LDS operand reads run PIPE steps ahead of the MFMAs that use
+    // and the LDS operand reads run PIPE k-steps ahead of the MFMAs that use
     // them (a read's latency is several MFMA issue slots).
     f16v s[2];
 #pragma unroll
@@ -341,9 +319,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
     {
-      const uint16_t* kt = &Ks[cur][l32 * C::KLD + 8 * hf];
+      const char* kt = kbuf(B) + 16 * hf;
       auto kread = [&](int ks, int kb) {
-        return *reinterpret_cast<const h8*>(kt + kb * 32 * C::KLD + 16 * ks);
+        return *reinterpret_cast<const h8*>(kt + row_byte<D>(kb * 32 + l32, C::KSLOT) + 32 * ks);
       };
       h8 kf[C::PIPE][2];
 #pragma unroll
@@ -358,7 +336,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
           if (ks + C::PIPE < C::KS) kf[ks % C::PIPE][kb] = kread(ks + C::PIPE, kb);
         }
       }
-      pipeline_order<2 * C::PIPE, 2 * C::KS>();
+      pipeline_order<2 * C::PIPE, 2 * C::KS, 1>();
     }
 
     // ---- mask, running max (on raw scores: scale and softcap are monotone) ----
@@ -373,14 +351,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int tau = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          s[kb][r] = (tau <= pos) & (tau >= wlo) ? s[kb][r] : kNegInf;
+          s[kb][r] = ((tau <= pos) & (tau >= wlo)) ? s[kb][r] : kNegInf;
         }
       if (wg_hole) {
+        const uint8_t* key_ok = okbuf(B);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (!key_ok[cur][kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)]) s[kb][r] = kNegInf;
+            if (!key_ok[kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)]) s[kb][r] = kNegInf;
       }
     }
     float mx = kNegInf;
@@ -408,7 +387,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 
     // ---- P (fp16) as B operand; O^T += V^T . P^T ----
     // p = exp2(scale*log2e*s - m), or with softcap exp2(cap*log2e*tanh(s*scale/cap) - m)
-    // where tanh(y) = 1 - 2/(exp(2y) + 1) (exact limits +-1 for large |y|)
+    // where tanh(y) = 1 - 2/(exp(2y) + 1) (exact limits +-1 for large |y|).
+    // k-step ks of the product covers the keys of accumulator rows
+    // 8*(ks & 1) .. +7 of 32-key block ks / 2.
     h8 pf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -429,11 +410,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
       }
     }
     {
-      // same pipelining; the DB output blocks alternate inside each k-step
+      // V^T operand by transposing LDS reads: lane k of each 16-lane group
+      // points at 4 channels of one key; lane i then receives channel i of
+      // four keys.  Two reads give the 8 keys of k-step ks that the P operand
+      // of this lane holds: 16*ks + 8*rr + 4*hf + (0..3), rr = 0, 1.
       constexpr int NV = 4 * C::DB;
-      const uint16_t* vt = &Vt[cur][l32 * C::VLD + 8 * hf];
+      const int li = lane & 15;
+      const char* vt = vbuf(B) + 2 * (16 * ((lane >> 4) & 1) + 4 * (li & 3));
       auto vread = [&](int i) {
-        return *reinterpret_cast<const h8*>(vt + (i % C::DB) * 32 * C::VLD + 16 * (i / C::DB));
+        const int db = i % C::DB, ks = i / C::DB;
+        v4s part[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+          part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(
+                  vt + row_byte<D>(16 * ks + 8 * rr + 4 * hf + (li >> 2), C::VSLOT) + 64 * db));
+        h8 v;
+        __builtin_memcpy(&v, part, 16);
+        return v;
       };
       h8 vf[2 * C::PIPE];
 #pragma unroll
@@ -444,11 +438,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % (2 * C::PIPE)], pf[ks], acc[db], 0, 0, 0);
         if (i + 2 * C::PIPE < NV) vf[i % (2 * C::PIPE)] = vread(i + 2 * C::PIPE);
       }
-      pipeline_order<2 * C::PIPE, NV>();
+      pipeline_order<2 * C::PIPE, NV, 2>();
     }
 
-    if (more) store_tile(cur ^ 1);
-    __syncthreads();
+    wait_vmem();        // this wave's loads of the next tile have landed
+    __syncthreads();    // ... and everyone's, and nobody reads this tile any more
+  };
+
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, Buf0{});
+    if (it + 1 < ntiles) step(it + 1, Buf1{});
   }
 
   // ---- normalise and store ----
