@@ -184,6 +184,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const int bmask = (1 << shift) - 1;
   const int32_t* bt = sl.block_table + (int64_t)b * sl.maxblk;
   const int64_t tok_stride = (int64_t)a.kv_heads * D;
+  const uint32_t tok_stride32 = (uint32_t)tok_stride;   // Hkv * D < 2^24
   const uint16_t* kbase = a.key_cache + (int64_t)kvh * D;
   const uint16_t* vbase = a.value_cache + (int64_t)kvh * D;
 
@@ -268,20 +269,26 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   auto vbuf = [&](auto B) -> char* { if constexpr (B() == 0) return V0; else return V1; };
   auto okbuf = [&](auto B) -> uint8_t* { if constexpr (B() == 0) return ok0; else return ok1; };
   auto dma_tile = [&](int kt0, auto B) {
+    // all table lookups first (one LDS round trip), then the address
+    // arithmetic in 32 x 32 -> 64-bit products, then the loads
+    int tau[C::DMA], blk[C::DMA];
 #pragma unroll
     for (int mi = 0; mi < C::DMA; ++mi) {
       const int slot = wave + 4 * mi;
-      const int row = (slot / C::NS) * 32 + (slot % C::NS) + C::NS * (lane / C::CH);
-      const int chunk = lane % C::CH;
-      const int tau = kt0 + row;
-      const bool in = tau >= lo && tau < hi;
-      const int blk = s_tbl[in ? (tau >> shift) - seg_first : 0];
-      const bool ok = in && blk >= 0;
-      const int64_t off =
-          ((int64_t)(ok ? blk : 0) * (bmask + 1) + (tau & bmask)) * tok_stride + 8 * chunk;
+      tau[mi] = kt0 + (slot / C::NS) * 32 + (slot % C::NS) + C::NS * (lane / C::CH);
+      const bool in = tau[mi] >= lo && tau[mi] < hi;
+      blk[mi] = in ? s_tbl[(tau[mi] >> shift) - seg_first] : -1;
+    }
+    const int chunk = lane % C::CH;
+#pragma unroll
+    for (int mi = 0; mi < C::DMA; ++mi) {
+      const int slot = wave + 4 * mi;
+      const bool ok = blk[mi] >= 0;
+      const uint32_t slot_row = ((uint32_t)blk[mi] << shift) | (uint32_t)(tau[mi] & bmask);
+      const uint64_t off = (uint64_t)(ok ? slot_row : 0u) * tok_stride32 + 8 * chunk;
       dma16(ok ? kbase + off : g_zero_row + 8 * chunk, kbuf(B) + slot * C::KSLOT);
       dma16(ok ? vbase + off : g_zero_row + 8 * chunk, vbuf(B) + slot * C::VSLOT);
-      if (chunk == 0) okbuf(B)[row] = ok;
+      if (chunk == 0) okbuf(B)[tau[mi] - kt0] = ok;
     }
   };
   auto need_segment = [&](int kt0) {

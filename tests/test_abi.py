@@ -89,6 +89,7 @@ NEGATIVE = [
     ({}, dict(batch_size=0), 1, "batch_size"),
     ({}, dict(token_count=-1), 1, "token_count"),
     ({}, dict(num_blocks=0), 1, "num_blocks"),
+    ({}, dict(num_blocks=(1 << 28) + 1), 1, "2^32 slots"),
     ({}, dict(max_blocks_per_seq=0), 1, "max_blocks_per_seq"),
     ({}, dict(key_cache=None), 1, "key_cache"),
     ({}, dict(value_cache=FAKE + 8), 1, "16-byte"),
