@@ -11,9 +11,11 @@ already resident in device memory when the timed region starts.
     python bench.py --summarize-pmc counter_collection.csv ...
 
 Prints ONE JSON line.  ``value`` is the decode KV throughput of the whole
-step (algorithmic decode bytes / step time).  ``roofline`` describes the
-dominant kernel (per-launch algorithmic bytes or FLOPs over its average
-launch time, from HIP events recorded around each launch on its stream).
+step (algorithmic decode bytes / step time) over K timed steps with nothing
+else on the stream.  The same K steps then run again with every launch's
+dispatch timestamped on its stream (start/stop events of the launch itself);
+``roofline`` describes the dominant kernel from those durations (per-launch
+algorithmic bytes or FLOPs over its average launch time).
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the workload.
 """
 from __future__ import annotations
@@ -300,22 +302,28 @@ def main():
         pa.forward(a, dev["query"], dev["key_cache"], dev["value_cache"], dev["block_table"],
                    dev["cum"], dev["past"], dev["cos"], dev["sin"], workspace=ws, out=out)
 
+    def timed(k):
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(k):
+            step()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # K timed steps, nothing else on the stream: the throughput figure
+    ms_step = timed(args.steps) / args.steps
+    # the same K steps again with every kernel's dispatch timestamped (start
+    # and end of each launch on its stream): the per-kernel durations
     pa.timing_enable(8 * args.steps + 16)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
-    stages = {s: pa.timing_read(s) for s in ("append", "decode", "merge", "prefill")}
+    ms_step_instrumented = timed(args.steps) / args.steps
+    stages = {s: pa.timing_read(s) for s in ("append", "decode", "merge", "prefill", "plan")}
     pa.timing_disable()
-    ms_step = ms_total / args.steps
 
     dec_bytes, pf_flops, n_dec = algorithmic_work(w)
     per = {s: (ms / n * 1e3 if n else 0.0) for s, (ms, n) in stages.items()}   # us per launch
@@ -366,6 +374,7 @@ def main():
         "roofline": roof,
         "step_roofline_frac": round(step_frac, 4),
         "kernels": kernels,
+        "ms_per_step_instrumented": round(ms_step_instrumented, 5),
         "cpu_baseline": cpu,
         "parity_max_abs_err_sampled": err,
     }

@@ -53,7 +53,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   if (items == 0) return hipSuccess;
   int64_t blocks = (items + 255) / 256;
   if (blocks > (1 << 20)) blocks = 1 << 20;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  launch_kernel(append_kernel, dim3((unsigned)blocks), dim3(256), st, a);
   return hipGetLastError();
 }
 

@@ -530,9 +530,9 @@ int occupancy_wg() {
 template <int D>
 void launch_decode_variant(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t st) {
   if (a.use_softcap)
-    hipLaunchKernelGGL((decode_kernel<D, true>), grid, block, 0, st, a);
+    launch_kernel(decode_kernel<D, true>, grid, block, st, a);
   else
-    hipLaunchKernelGGL((decode_kernel<D, false>), grid, block, 0, st, a);
+    launch_kernel(decode_kernel<D, false>, grid, block, st, a);
 }
 
 }  // namespace
@@ -547,7 +547,7 @@ int decode_workgroups_per_cu(int head_size, bool softcap) {
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, a);
+  launch_kernel(plan_kernel, dim3(1), dim3(1024), st, a);
   return hipGetLastError();
 }
 
@@ -563,7 +563,7 @@ hipError_t launch_decode(const DecodeArgs& a, int head_size, int workgroups, hip
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(merge_kernel, dim3(a.rows, a.num_heads), dim3(256), 0, st, a);
+  launch_kernel(merge_kernel, dim3(a.rows, a.num_heads), dim3(256), st, a);
   return hipGetLastError();
 }
 

@@ -50,27 +50,24 @@ struct Timing {
   size_t used = 0;                  // pairs recorded
 };
 Timing g_timing;
+}  // namespace
+
+namespace pa {
+thread_local LaunchEvents g_launch_events;
+}  // namespace pa
+
+namespace {
 
 struct StageScope {
-  hipStream_t st;
   int slot = -1;
-  StageScope(int stg, hipStream_t s) : st(s) {
+  StageScope(int stg, hipStream_t) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
     if (!g_timing.enabled || g_timing.used >= g_timing.stage.size()) return;
     slot = (int)g_timing.used++;
     g_timing.stage[slot] = stg;
-    if (hipEventRecord(g_timing.events[2 * slot], st) != hipSuccess) {
-      g_timing.stage[slot] = -1;   // not counted
-      slot = -1;
-    }
+    pa::g_launch_events = {g_timing.events[2 * slot], g_timing.events[2 * slot + 1]};
   }
-  ~StageScope() {
-    if (slot < 0) return;
-    if (hipEventRecord(g_timing.events[2 * slot + 1], st) != hipSuccess) {
-      std::lock_guard<std::mutex> lk(g_timing.mu);
-      g_timing.stage[slot] = -1;
-    }
-  }
+  ~StageScope() { pa::g_launch_events = {}; }
 };
 
 // ---- validation --------------------------------------------------------------

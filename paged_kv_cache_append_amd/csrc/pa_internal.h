@@ -2,6 +2,7 @@
 // gfx950 kernels (append.hip, decode.hip, prefill.hip).  Not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -127,6 +128,26 @@ struct PrefillArgs {
   float cap_out;                // softcap * log2(e)
   int32_t use_softcap;
 };
+
+// Kernel start/stop events of the launch being made on this thread (set by
+// the host planner while per-kernel timing is on, else null).  With events,
+// the launch goes through hipExtLaunchKernelGGL, which timestamps the
+// dispatch itself instead of inserting separate event packets around it.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+extern thread_local LaunchEvents g_launch_events;
+
+template <typename... Args, typename... Params>
+inline void launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t st,
+                          Args... args) {
+  if (g_launch_events.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, g_launch_events.start, g_launch_events.stop,
+                          0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);

@@ -479,9 +479,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 template <int D>
 void launch_variant(const PrefillArgs& a, dim3 grid, hipStream_t st) {
   if (a.use_softcap)
-    hipLaunchKernelGGL((prefill_kernel<D, true>), grid, dim3(256), 0, st, a);
+    launch_kernel(prefill_kernel<D, true>, grid, dim3(256), st, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, false>), grid, dim3(256), 0, st, a);
+    launch_kernel(prefill_kernel<D, false>, grid, dim3(256), st, a);
 }
 
 }  // namespace
