@@ -322,7 +322,8 @@ def main():
     # and end of each launch on its stream): the per-kernel durations
     pa.timing_enable(8 * args.steps + 16)
     ms_step_instrumented = timed(args.steps) / args.steps
-    stages = {s: pa.timing_read(s) for s in ("append", "decode", "merge", "prefill", "plan")}
+    stages = {s: pa.timing_read(s)
+              for s in ("append", "decode", "merge", "prefill", "prefill_merge", "plan")}
     pa.timing_disable()
 
     dec_bytes, pf_flops, n_dec = algorithmic_work(w)

@@ -65,6 +65,9 @@ typedef struct {
                                  Results are the same up to rounding.                  */
   int32_t split_tokens;       /* 0 = auto; else decode KV split length in tokens, a
                                  multiple of 64 (testing hook; rounding may differ)    */
+  int32_t prefill_pieces;     /* 0 = auto; else 1..4: workgroups sharing one prefill
+                                 tile's key range, merged on the device (testing
+                                 hook; rounding may differ)                            */
 } pa_attn_params;
 
 /* The paged cache and the per-step request layout.  Host struct holding
@@ -165,15 +168,15 @@ pa_status pa_describe_plan(const pa_attn_params *params, const pa_paged_kv *kv,
 
 /*
  * Per-kernel timing on the launch stream, for benchmarks.  While enabled, the
- * library records a HIP event pair around every kernel it launches (on the
- * same stream) and pa_timing_read() sums their elapsed times per stage
- * (synchronizing on the recorded events).  Enabling creates the events
- * (2 * max_launches); it is not meant for graph capture.
- *   stage: 0 = append, 1 = decode, 2 = split merge, 3 = prefill,
- *          4 = decode work-list planning.
+ * library launches every kernel with a start/stop event pair that the
+ * dispatch itself timestamps, and pa_timing_read() sums their elapsed times
+ * per stage (synchronizing on the recorded events).  Enabling creates the
+ * events (2 * max_launches); it is not meant for graph capture.
+ *   stage: 0 = append, 1 = decode, 2 = decode split merge, 3 = prefill,
+ *          4 = decode work-list planning, 5 = prefill piece merge.
  */
 enum { PA_STAGE_APPEND = 0, PA_STAGE_DECODE = 1, PA_STAGE_MERGE = 2, PA_STAGE_PREFILL = 3,
-       PA_STAGE_PLAN = 4, PA_NUM_STAGES = 5 };
+       PA_STAGE_PLAN = 4, PA_STAGE_PREFILL_MERGE = 5, PA_NUM_STAGES = 6 };
 pa_status pa_timing_enable(int32_t max_launches);
 pa_status pa_timing_disable(void);
 pa_status pa_timing_read(int32_t stage, double *total_ms, int32_t *launches);

@@ -42,12 +42,14 @@ class Attn:
     rotary_interleaved: int = 0
     path: int = 0
     split_tokens: int = 0
+    prefill_pieces: int = 0
 
     def c(self) -> _lib.AttnParams:
         return _lib.AttnParams(self.num_heads, self.kv_num_heads, self.head_size,
                                self.block_size, float(self.scale), float(self.softcap),
                                self.local_window_size, self.do_rotary,
-                               self.rotary_interleaved, self.path, self.split_tokens)
+                               self.rotary_interleaved, self.path, self.split_tokens,
+                               self.prefill_pieces)
 
 
 def library_path() -> str:
@@ -191,7 +193,7 @@ def timing_disable() -> None:
 
 def timing_read(stage: str):
     """(total milliseconds, launches) recorded for ``stage`` in
-    {append, decode, merge, prefill, plan}."""
+    {append, decode, merge, prefill, plan, prefill_merge}."""
     lib = _lib.load()
     ms = ctypes.c_double(0)
     n = ctypes.c_int32(0)

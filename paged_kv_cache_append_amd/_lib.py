@@ -12,7 +12,7 @@ PA_ERR_INVALID_ARGUMENT = 1
 PA_ERR_UNSUPPORTED = 2
 PA_ERR_DEVICE = 3
 
-STAGES = {"append": 0, "decode": 1, "merge": 2, "prefill": 3, "plan": 4}
+STAGES = {"append": 0, "decode": 1, "merge": 2, "prefill": 3, "plan": 4, "prefill_merge": 5}
 
 EXPORTED = ("pa_append_kv", "pa_forward_workspace_bytes", "pa_forward", "pa_last_error",
             "pa_describe_plan", "pa_timing_enable", "pa_timing_disable", "pa_timing_read")
@@ -24,7 +24,7 @@ class AttnParams(ctypes.Structure):
                 ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
                 ("local_window_size", ctypes.c_int32), ("do_rotary", ctypes.c_int32),
                 ("rotary_interleaved", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("split_tokens", ctypes.c_int32)]
+                ("split_tokens", ctypes.c_int32), ("prefill_pieces", ctypes.c_int32)]
 
 
 class PagedKV(ctypes.Structure):

@@ -98,6 +98,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const PlanArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
+  for (int i = tid; i < a.zero_count; i += 1024) a.zero[i] = 0;
   int total = 0;
   for (int r0 = 0; r0 < a.rows; r0 += 1024) {
     const int row = r0 + tid;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const PlanArgs a) {
     total += s_sum;
     __syncthreads();
   }
-  if (tid == 0) *a.entry_count = total;
+  if (tid == 0 && a.entry_count) *a.entry_count = total;
 }
 
 // ---------------------------------------------------------------------------

@@ -105,6 +105,9 @@ pa_status check_common(const pa_attn_params* p, const pa_paged_kv* kv) {
     return fail(PA_ERR_INVALID_ARGUMENT, "path: expected 0, 1 or 2, got %d", p->path);
   if (p->num_heads > 65535)
     return fail(PA_ERR_INVALID_ARGUMENT, "num_heads: expected <= 65535, got %d", p->num_heads);
+  if (p->prefill_pieces < 0 || p->prefill_pieces > pa::kPrefillChunks)
+    return fail(PA_ERR_INVALID_ARGUMENT, "prefill_pieces: expected 0..%d, got %d",
+                pa::kPrefillChunks, p->prefill_pieces);
   if (p->split_tokens < 0 || p->split_tokens % 64 != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "split_tokens: expected 0 or a multiple of 64, got %d",
                 p->split_tokens);
@@ -178,8 +181,10 @@ struct Plan {
   int g = 1, chunk_heads = 1, head_chunks = 1;
   int split_tokens = 256;
   int max_splits = 1;
-  int prefill_tiles = 0;     // tile slots (grid.x = tiles + 1)
+  int prefill_tiles = 0;     // tile slots (grid.x = tiles * prefill_chunks + 1)
+  int prefill_chunks = 1;    // key-range pieces per prefill tile
   size_t off_ml = 0, off_entries = 0, off_count = 0;
+  size_t off_pf_o = 0, off_pf_ml = 0;
   size_t ws_bytes = 0;
 };
 
@@ -221,20 +226,39 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
   if (p->local_window_size > 0) kv_ext = std::min<int64_t>(kv_ext, p->local_window_size);
   pl.max_splits = (int)std::max<int64_t>(1, (kv_ext + pl.split_tokens - 1) / pl.split_tokens);
   pl.listed = pl.max_splits > 1;
+  size_t cur = 0;
   if (pl.listed) {
     const size_t per = (size_t)pl.rows * p->num_heads * pl.max_splits;
     pl.off_ml = align256(per * p->head_size * sizeof(float));
     pl.off_entries = pl.off_ml + align256(per * 2 * sizeof(float));
     pl.off_count = pl.off_entries + align256((size_t)pl.rows * pl.max_splits * 2 * sizeof(int32_t));
-    pl.ws_bytes = pl.off_count + 256;
+    cur = pl.off_count + 256;
   }
   if (pl.prefill) {
     const int64_t mql = mq > 0 ? std::min<int64_t>(mq, T) : T;
     const int64_t per_req = (mql * pl.g + pa::kPrefillRows - 1) / pa::kPrefillRows;
     const int64_t by_tokens = ((int64_t)T * pl.g + pa::kPrefillRows - 1) / pa::kPrefillRows + B;
     pl.prefill_tiles = (int)std::min<int64_t>(std::min<int64_t>((int64_t)B * per_req, by_tokens),
-                                              (int64_t)1 << 30);
+                                              (int64_t)1 << 28);
+    // Few (tile, kv head) items leave most of the chip idle while each tile
+    // walks its whole key range: then long tiles' key ranges are cut into
+    // pieces of about kPrefillPieceTiles key tiles (at most kPrefillChunks),
+    // computed by separate workgroups and combined by a merge kernel.  Static
+    // shapes decide whether pieces are allowed; the device cuts by length.
+    const int64_t est_items =
+        ((int64_t)T * pl.g + pa::kPrefillRows - 1) / pa::kPrefillRows * p->kv_num_heads;
+    const bool long_keys = cap >= 4 * pa::kPrefillPieceTiles * 64;
+    pl.prefill_chunks = p->prefill_pieces > 0 ? p->prefill_pieces
+                        : est_items < pa::kPrefillSplitItems && long_keys ? pa::kPrefillChunks
+                                                                          : 1;
+    if (pl.prefill_chunks > 1) {
+      const size_t rows = (size_t)T * p->num_heads * pl.prefill_chunks;
+      pl.off_pf_o = cur;
+      pl.off_pf_ml = pl.off_pf_o + align256(rows * p->head_size * sizeof(float));
+      cur = pl.off_pf_ml + align256(rows * 2 * sizeof(float));
+    }
   }
+  pl.ws_bytes = cur;
   return pl;
 }
 
@@ -338,11 +362,11 @@ pa_status pa_describe_plan(const pa_attn_params* params, const pa_paged_kv* kv, 
   const Plan pl = make_plan(params, kv, mq, mk);
   snprintf(buf, len,
            "mode=%s rows=%d head_chunks=%d g=%d chunk_heads=%d split_tokens=%d max_splits=%d "
-           "listed=%d prefill_grid=(%d,%d) workspace=%zu",
+           "listed=%d prefill_grid=(%d,%d) prefill_chunks=%d workspace=%zu",
            pl.token_mode ? "token" : "request", pl.rows, params->kv_num_heads * pl.head_chunks,
            pl.g, pl.chunk_heads, pl.split_tokens, pl.max_splits, pl.listed ? 1 : 0,
-           pl.prefill ? pl.prefill_tiles + 1 : 0, pl.prefill ? params->kv_num_heads : 0,
-           pl.ws_bytes);
+           pl.prefill ? pl.prefill_tiles * pl.prefill_chunks + 1 : 0,
+           pl.prefill ? params->kv_num_heads : 0, pl.prefill ? pl.prefill_chunks : 0, pl.ws_bytes);
   return PA_OK;
 }
 
@@ -410,23 +434,27 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
   d.cap_out = cap ? params->softcap * log2e : 0.f;
   d.use_softcap = cap ? 1 : 0;
 
+  if (pl.listed) {
+    pa::PlanArgs pa_;
+    pa_.s = sl;
+    pa_.entries = reinterpret_cast<int2*>(ws + pl.off_entries);
+    pa_.entry_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
+    pa_.out = d.out;
+    pa_.rows = pl.rows;
+    pa_.token_mode = d.token_mode;
+    pa_.split_tokens = pl.split_tokens;
+    pa_.max_splits = pl.max_splits;
+    pa_.window = params->local_window_size;
+    pa_.row_width = params->num_heads * D;
+    pa_.zero = nullptr;
+    pa_.zero_count = 0;
+    StageScope scope(PA_STAGE_PLAN, s);
+    if ((st = device_status(pa::launch_plan(pa_, s), "plan kernel launch")) != PA_OK) return st;
+  }
   if (pl.rows > 0) {
     const int64_t hc = (int64_t)params->kv_num_heads * pl.head_chunks;
     int64_t wgs;
     if (pl.listed) {
-      pa::PlanArgs pa_;
-      pa_.s = sl;
-      pa_.entries = reinterpret_cast<int2*>(ws + pl.off_entries);
-      pa_.entry_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
-      pa_.out = d.out;
-      pa_.rows = pl.rows;
-      pa_.token_mode = d.token_mode;
-      pa_.split_tokens = pl.split_tokens;
-      pa_.max_splits = pl.max_splits;
-      pa_.window = params->local_window_size;
-      pa_.row_width = params->num_heads * D;
-      StageScope scope(PA_STAGE_PLAN, s);
-      if ((st = device_status(pa::launch_plan(pa_, s), "plan kernel launch")) != PA_OK) return st;
       const int64_t bound = (int64_t)pl.rows * pl.max_splits * hc;
       const int64_t resident =
           (int64_t)pa::decode_workgroups_per_cu(D, d.use_softcap != 0) * device_cus();
@@ -475,14 +503,25 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     f.rotary_interleaved = d.rotary_interleaved;
     f.rotary_rows = d.rotary_rows;
     f.tiles = pl.prefill_tiles;
+    f.chunks = pl.prefill_chunks;
+    f.piece_tiles = params->prefill_pieces > 0 ? 0 : pa::kPrefillPieceTiles;
+    f.part_o = pl.prefill_chunks > 1 ? reinterpret_cast<float*>(ws + pl.off_pf_o) : nullptr;
+    f.part_ml = pl.prefill_chunks > 1 ? reinterpret_cast<float*>(ws + pl.off_pf_ml) : nullptr;
     f.score_scale = d.score_scale;
     f.cap_in2 = 2.0f * log2e * d.cap_in;
     f.cap_out = d.cap_out;
     f.use_softcap = d.use_softcap;
-    const dim3 grid(pl.prefill_tiles + 1, params->kv_num_heads);
-    StageScope scope(PA_STAGE_PREFILL, s);
-    if ((st = device_status(pa::launch_prefill(f, D, grid, s), "prefill kernel launch")) != PA_OK)
-      return st;
+    const dim3 grid(pl.prefill_tiles * pl.prefill_chunks + 1, params->kv_num_heads);
+    {
+      StageScope scope(PA_STAGE_PREFILL, s);
+      if ((st = device_status(pa::launch_prefill(f, D, grid, s), "prefill kernel launch")) != PA_OK)
+        return st;
+    }
+    if (pl.prefill_chunks > 1) {
+      StageScope scope(PA_STAGE_PREFILL_MERGE, s);
+      if ((st = device_status(pa::launch_prefill_merge(f, D, s), "prefill merge launch")) != PA_OK)
+        return st;
+    }
   }
   return PA_OK;
 }

@@ -88,6 +88,8 @@ struct PlanArgs {
   int32_t max_splits;
   int32_t window;
   int32_t row_width;            // H * D elements of an output row
+  int32_t* zero;                // words cleared before anything else runs (or null)
+  int32_t zero_count;
 };
 
 // Split merge: one wave per (row, head) of rows with more than one split.
@@ -122,7 +124,13 @@ struct PrefillArgs {
   int32_t rotary_dim;
   int32_t rotary_interleaved;
   int32_t rotary_rows;
-  int32_t tiles;                // grid.x - 1: tile slots; the last x zeroes orphan rows
+  int32_t tiles;                // tile slots; grid.x = tiles * chunks + 1 (the last x zeroes
+                                // orphan rows)
+  int32_t chunks;               // at most this many key-range pieces per tile
+  int32_t piece_tiles;          // > 0: pieces of about this many 64-key tiles; 0: `chunks`
+                                // equal pieces
+  float* part_o;                // chunks > 1: [T, H, chunks, D] unnormalised outputs
+  float* part_ml;               // [T, H, chunks, 2] (max in log2 units, sum)
   float score_scale;            // scale * log2(e)
   float cap_in2;                // 2 * log2(e) * scale / softcap  (tanh via exp2)
   float cap_out;                // softcap * log2(e)
@@ -156,10 +164,14 @@ hipError_t launch_decode(const DecodeArgs& a, int head_size, int workgroups, hip
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 int decode_workgroups_per_cu(int head_size, bool softcap);   // resident decode workgroups per CU
 hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st);
+hipError_t launch_prefill_merge(const PrefillArgs& a, int head_size, hipStream_t st);
 
 constexpr int kPrefillRows = 128;   // query rows (token x head) per prefill workgroup
 constexpr int kDecodeWaves = 4;     // independent decode workers per workgroup
 constexpr int kDecodeMaxHeads = 16; // query heads served by one decode worker
 constexpr int kDecodeMaxSplits = 2048;
+constexpr int kPrefillChunks = 4;        // key-range pieces of a prefill tile in small batches
+constexpr int kPrefillPieceTiles = 32;   // ... each about this many 64-key tiles
+constexpr int kPrefillSplitItems = 1024; // ... used below this many (tile, kv head) items
 
 }  // namespace pa

@@ -37,6 +37,7 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct PrefillCfg {
@@ -94,6 +95,67 @@ __device__ __forceinline__ void pipeline_order() {
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
 
+// Tile slot -> (request b, tile) over requests with q_len >= 2, tiles of
+// kPrefillRows rows (token x head-in-group) each; later (longer) tiles of a
+// request come first.  b = -1 past the last tile.  Called by a whole wave;
+// the results are the same in every lane.
+__device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, int lane, int& fb,
+                                          int& ft) {
+  int base = 0;
+  fb = -1;
+  ft = 0;
+  for (int b0 = 0; b0 < sl.batch; b0 += 64) {
+    const int bb = b0 + lane;
+    int nt = 0;
+    if (bb < sl.batch) {
+      const int ql = sl.cum[bb + 1] - sl.cum[bb];
+      if (ql >= 2) nt = (ql * g + kPrefillRows - 1) / kPrefillRows;
+    }
+    int incl = nt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const int total = __shfl(incl, 63, 64);
+    if (slot < base + total) {
+      const bool mine = nt > 0 && slot >= base + incl - nt && slot < base + incl;
+      const unsigned long long bal = __ballot(mine);
+      const int src = __builtin_ctzll(bal);
+      fb = b0 + src;
+      const int fn = __shfl(nt, src, 64);
+      ft = fn - 1 - (slot - (base + __shfl(incl - nt, src, 64)));
+      return;
+    }
+    base += total;
+  }
+}
+
+// Key range [lo, hi) that tile `tile` of a request (q_len, past) needs, and
+// how it is cut into pieces of whole 64-key tiles for `chunks` workgroups.
+struct TileKeys {
+  int lo, hi;              // admitted keys of any row of the tile
+  int all_begin, all_tiles;
+  int per_piece, pieces;
+};
+__device__ __forceinline__ TileKeys tile_keys(int tile, int q_len, int past, int g, int window,
+                                              int cap, int chunks, int piece_tiles) {
+  TileKeys k;
+  const int j_first = (tile * kPrefillRows) / g;
+  const int j_last = min(q_len - 1, (tile * kPrefillRows + kPrefillRows - 1) / g);
+  k.hi = min(past + j_last + 1, cap);
+  k.lo = window > 0 ? max(0, past + j_first + 1 - window) : 0;
+  k.all_begin = k.lo & ~63;
+  k.all_tiles = k.hi > k.all_begin ? (k.hi - k.all_begin + 63) / 64 : 0;
+  // piece_tiles > 0: pieces of about piece_tiles key tiles (short tiles stay
+  // whole), at most `chunks`; else `chunks` equal pieces
+  const int want = piece_tiles > 0 ? (k.all_tiles + piece_tiles - 1) / piece_tiles : chunks;
+  const int n = max(1, min(chunks, want));
+  k.per_piece = (k.all_tiles + n - 1) / n;
+  k.pieces = k.per_piece > 0 ? (k.all_tiles + k.per_piece - 1) / k.per_piece : 1;
+  return k;
+}
+
 // max / sum of a value with the one 32 lanes away (one lane-swap instruction)
 __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -125,7 +187,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const int g = a.group;
   const int64_t HD = (int64_t)a.num_heads * D;
 
-  if ((int)blockIdx.x == a.tiles) {
+  if ((int)blockIdx.x == a.tiles * a.chunks) {
     // tokens owned by no request get zero rows (this kv head's columns)
     const int t0 = max(sl.cum[sl.batch], 0);
     const int width = g * C::CH;
@@ -139,36 +201,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 
   // Map this workgroup to (request, tile) over requests with q_len >= 2.
   if (wave == 0) {
-    const int slot = blockIdx.x;
-    int base = 0, fb = -1, ft = 0, fn = 0;
-    for (int b0 = 0; b0 < sl.batch; b0 += 64) {
-      const int bb = b0 + lane;
-      int nt = 0;
-      if (bb < sl.batch) {
-        const int ql = sl.cum[bb + 1] - sl.cum[bb];
-        if (ql >= 2) nt = (ql * g + C::ROWS - 1) / C::ROWS;
-      }
-      int incl = nt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-      }
-      const int total = __shfl(incl, 63, 64);
-      if (slot < base + total) {
-        const bool mine = nt > 0 && slot >= base + incl - nt && slot < base + incl;
-        const unsigned long long bal = __ballot(mine);
-        const int src = __builtin_ctzll(bal);
-        fb = b0 + src;
-        ft = slot - (base + __shfl(incl - nt, src, 64));
-        fn = __shfl(nt, src, 64);
-        break;
-      }
-      base += total;
-    }
+    int fb, ft;
+    find_tile(sl, g, blockIdx.x / a.chunks, lane, fb, ft);
     if (lane == 0) {
       sh_b = fb;
-      sh_tile = fn - 1 - ft;   // later (longer) tiles of a request are dispatched first
+      sh_tile = ft;
     }
   }
   __syncthreads();
@@ -198,10 +235,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const int head = kvh * g + hh;
 
   // key range of the whole tile, and of this wave's rows (fast path)
-  const int j_first = (tile * C::ROWS) / g;
-  const int j_last = min(q_len - 1, (tile * C::ROWS + C::ROWS - 1) / g);
-  const int hi = min(past + j_last + 1, cap);
-  const int lo = a.window > 0 ? max(0, past + j_first + 1 - a.window) : 0;
+  const TileKeys tk = tile_keys(tile, q_len, past, g, a.window, cap, a.chunks, a.piece_tiles);
+  const int piece = blockIdx.x - (blockIdx.x / a.chunks) * a.chunks;
+  const int pieces = tk.pieces;
+  if (piece >= pieces) return;
+  const int hi = tk.hi;
+  const int lo = tk.lo;
   const int wj0 = min((tile * C::ROWS + wave * 32) / g, q_len - 1);
   const int wj1 = min((tile * C::ROWS + wave * 32 + 31) / g, q_len - 1);
   const int wpos_min = past + wj0;
@@ -237,8 +276,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
   float m = kNegInf, lsum = 0.f;
 
-  const int kt_begin = lo & ~(C::KT - 1);
-  const int ntiles = hi > kt_begin ? (hi - kt_begin + C::KT - 1) / C::KT : 0;
+  // This workgroup's piece of the key range: the tile's key tiles split into
+  // a.chunks nearly equal runs (pieces past the end have nothing to do).
+  const int kt_begin = tk.all_begin + piece * tk.per_piece * C::KT;
+  const int ntiles = min(tk.per_piece, tk.all_tiles - piece * tk.per_piece);
   int seg_first = -1;      // first block index staged in s_tbl
   bool wg_hole = false;    // some key in [lo, hi) lives in an unmapped block
 
@@ -457,8 +498,27 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     if (it + 1 < ntiles) step(it + 1, Buf1{});
   }
 
-  // ---- normalise and store ----
   const float lt = xor32_sum(lsum);
+  if (pieces > 1) {
+    // ---- one piece of several: store (m, l, unnormalised O) ----
+    const int64_t pr = ((int64_t)t * a.num_heads + head) * a.chunks;
+    if (row_ok) {
+      if (hf == 0) {
+        a.part_ml[2 * (pr + piece)] = m;
+        a.part_ml[2 * (pr + piece) + 1] = lt;
+      }
+      float* po = a.part_o + (pr + piece) * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f4*>(po + db * 32 + 8 * q4 + 4 * hf) =
+              f4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
+    }
+    return;   // the merge kernel combines the pieces
+  }
+
+  // ---- normalise and store ----
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (row_ok) {
     uint16_t* orow = a.out + (int64_t)t * HD + (int64_t)head * D;
@@ -476,6 +536,64 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   }
 }
 
+// Combine the pieces of every prefill tile cut into several: one workgroup
+// per (tile slot, kv head); thread pairs own a row, each half of its channels.
+// o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c, with M = max_c m_c
+// (GroupQueryAttention CPU Implementation Notes, "Flash Decoding" merge).
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a) {
+  __shared__ int sh_b, sh_tile;
+  const SeqLayout& sl = a.s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int g = a.group;
+  if (tid < 64) {
+    int fb, ft;
+    find_tile(sl, g, blockIdx.x, lane, fb, ft);
+    if (lane == 0) {
+      sh_b = fb;
+      sh_tile = ft;
+    }
+  }
+  __syncthreads();
+  const int b = __builtin_amdgcn_readfirstlane(sh_b);
+  if (b < 0) return;
+  const int tile = __builtin_amdgcn_readfirstlane(sh_tile);
+  const int t_begin = sl.cum[b];
+  const int q_len = sl.cum[b + 1] - t_begin;
+  const TileKeys tk = tile_keys(tile, q_len, sl.past[b], g, a.window, sl.maxblk << sl.block_shift,
+                                a.chunks, a.piece_tiles);
+  if (tk.pieces <= 1) return;
+  const int R = tile * kPrefillRows + (tid >> 1);
+  const int j = R / g;
+  if (j >= q_len || t_begin + j >= sl.tokens) return;
+  const int t = t_begin + j;
+  const int head = blockIdx.y * g + (R - j * g);
+  const int64_t pr = ((int64_t)t * a.num_heads + head) * a.chunks;
+  float w[kPrefillChunks];
+  float mm = kNegInf, ll = 0.f;
+#pragma unroll
+  for (int c = 0; c < kPrefillChunks; ++c)
+    if (c < tk.pieces) mm = fmaxf(mm, a.part_ml[2 * (pr + c)]);
+#pragma unroll
+  for (int c = 0; c < kPrefillChunks; ++c) {
+    w[c] = c < tk.pieces && mm != kNegInf ? exp2_fast(a.part_ml[2 * (pr + c)] - mm) : 0.f;
+    if (c < tk.pieces) ll += w[c] * a.part_ml[2 * (pr + c) + 1];
+  }
+  const float inv = ll > 0.f ? 1.0f / ll : 0.f;
+  uint16_t* orow = a.out + (int64_t)t * a.num_heads * D + (int64_t)head * D;
+#pragma unroll 4
+  for (int d0 = (tid & 1) * (D / 2); d0 < (tid & 1) * (D / 2) + D / 2; d0 += 4) {
+    f4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kPrefillChunks; ++c)
+      if (c < tk.pieces) o += w[c] * *reinterpret_cast<const f4*>(a.part_o + (pr + c) * D + d0);
+    uint2 v;
+    v.x = (uint32_t)f2h(o[0] * inv) | ((uint32_t)f2h(o[1] * inv) << 16);
+    v.y = (uint32_t)f2h(o[2] * inv) | ((uint32_t)f2h(o[3] * inv) << 16);
+    *reinterpret_cast<uint2*>(orow + d0) = v;
+  }
+}
+
 template <int D>
 void launch_variant(const PrefillArgs& a, dim3 grid, hipStream_t st) {
   if (a.use_softcap)
@@ -485,6 +603,17 @@ void launch_variant(const PrefillArgs& a, dim3 grid, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_prefill_merge(const PrefillArgs& a, int head_size, hipStream_t st) {
+  const dim3 grid(a.tiles, a.kv_heads);
+  switch (head_size) {
+    case 64: launch_kernel(prefill_merge_kernel<64>, grid, dim3(256), st, a); break;
+    case 128: launch_kernel(prefill_merge_kernel<128>, grid, dim3(256), st, a); break;
+    case 256: launch_kernel(prefill_merge_kernel<256>, grid, dim3(256), st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st) {
   switch (head_size) {

@@ -39,7 +39,8 @@ def test_library_exports_every_declared_function():
 
 def params(**kw):
     d = dict(num_heads=8, kv_num_heads=2, head_size=64, block_size=16, scale=0.0, softcap=0.0,
-             local_window_size=-1, do_rotary=0, rotary_interleaved=0, path=0, split_tokens=0)
+             local_window_size=-1, do_rotary=0, rotary_interleaved=0, path=0, split_tokens=0,
+             prefill_pieces=0)
     d.update(kw)
     return _lib.AttnParams(*[d[f] for f, _ in _lib.AttnParams._fields_])
 
@@ -86,6 +87,8 @@ NEGATIVE = [
     (dict(rotary_interleaved=3), {}, 1, "rotary_interleaved"),
     (dict(path=3), {}, 1, "path"),
     (dict(split_tokens=100), {}, 1, "split_tokens"),
+    (dict(prefill_pieces=5), {}, 1, "prefill_pieces"),
+    (dict(prefill_pieces=-1), {}, 1, "prefill_pieces"),
     ({}, dict(batch_size=0), 1, "batch_size"),
     ({}, dict(token_count=-1), 1, "token_count"),
     ({}, dict(num_blocks=0), 1, "num_blocks"),

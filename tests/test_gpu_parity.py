@@ -57,6 +57,7 @@ SWEEP = [
     ([1, 1, 1, 70], [5000, 20, 0, 3000], 8, 2, 64, 16, {}),              # several splits
     ([64, 1], [4000, 7000], 16, 8, 256, 16, dict(local_window_size=4096, softcap=50.0)),
     ([33, 2, 1], [1, 2, 3], 32, 8, 128, 128, dict(scale=0.3)),
+    ([100, 1], [9000, 4000], 8, 2, 128, 16, {}),        # long keys, few tiles: auto pieces
 ]
 
 
@@ -94,6 +95,26 @@ def test_split_length_changes_only_rounding():
     outs = [check(w, 1, split_tokens=st)[0] for st in (0, 64, 192, 1024, 8192)]
     for o in outs[1:]:
         assert np.max(np.abs(o.astype(np.float64) - outs[0])) <= 1e-3
+
+
+PIECE_CASES = [
+    # q_lens, past, H, Hkv, D, bs, extra kwargs: prefill tiles whose key range
+    # spans several 64-key tiles, cut into 1..4 pieces merged on the device
+    ([130, 1, 77], [500, 900, 0], 8, 2, 128, 16, {}),
+    ([64, 3], [1500, 40], 16, 8, 256, 16, dict(local_window_size=700, softcap=50.0)),
+    ([200, 9], [300, 0], 8, 1, 64, 32, dict(do_rotary=1, rotary_dim=64)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PIECE_CASES)))
+@pytest.mark.parametrize("pieces", [1, 2, 3, 4])
+def test_prefill_pieces(case, pieces):
+    """Every split of a prefill tile's key range over workgroups matches the
+    oracle (the pieces only change the summation order)."""
+    q_lens, past, H, Hkv, D, bs, kw = PIECE_CASES[case]
+    w = wl.build_case(f"pieces{case}", 600 + case, q_lens=q_lens, past=past, num_heads=H,
+                      kv_num_heads=Hkv, head_size=D, block_size=bs, **kw)
+    check(w, 2, prefill_pieces=pieces)
 
 
 def test_bounds_do_not_change_results():
