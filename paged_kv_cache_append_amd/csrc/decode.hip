@@ -95,6 +95,7 @@ __device__ __forceinline__ float xor32_sum(float v) {
 __global__ __launch_bounds__(1024) void plan_kernel(const PlanArgs a) {
   __shared__ int s_wave[16];
   __shared__ int s_sum;
+  __shared__ int s_first[1024];   // entry offset of each row of the chunk
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -132,8 +133,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(const PlanArgs a) {
       if (lane == 15) s_sum = sc;
     }
     __syncthreads();
-    const int first = total + s_wave[wv] + incl - n;
-    for (int sp = 0; sp < n; ++sp) a.entries[first + sp] = make_int2(row, sp);
+    // every thread writes entries: entry e of the chunk belongs to the last
+    // row whose first entry is <= e (one row can own thousands of splits)
+    s_first[tid] = s_wave[wv] + incl - n;
+    __syncthreads();
+    const int chunk_rows = min(1024, a.rows - r0);
+    for (int e = tid; e < s_sum; e += 1024) {
+      int lo = 0, hi = chunk_rows - 1;   // invariant: s_first[lo] <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_first[mid] <= e) lo = mid; else hi = mid - 1;
+      }
+      a.entries[total + e] = make_int2(r0 + lo, e - s_first[lo]);
+    }
     total += s_sum;
     __syncthreads();
   }

@@ -171,7 +171,7 @@ pa_status check_kernel_support(const pa_attn_params* p) {
 }
 
 // ---- planning ----------------------------------------------------------------
-constexpr int64_t kTargetItems = 16384;   // decode work items aimed at (split length choice)
+constexpr int64_t kTargetItems = 32768;   // decode work items aimed at (split length choice)
 
 struct Plan {
   bool token_mode = true;    // decode rows are tokens (else requests with q_len == 1)
@@ -220,7 +220,7 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
     int64_t st = (items * span + kTargetItems - 1) / kTargetItems;
     st = std::max<int64_t>(st, (span + pa::kDecodeMaxSplits - 1) / pa::kDecodeMaxSplits);
     st = (st + 63) / 64 * 64;
-    pl.split_tokens = (int)std::max<int64_t>(256, std::min<int64_t>(st, 1 << 30));
+    pl.split_tokens = (int)std::max<int64_t>(128, std::min<int64_t>(st, 1 << 30));
   }
   int64_t kv_ext = mk > 0 ? std::min<int64_t>(mk, cap) : cap;   // bound only trims the grid
   if (p->local_window_size > 0) kv_ext = std::min<int64_t>(kv_ext, p->local_window_size);
