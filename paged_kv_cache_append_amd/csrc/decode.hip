@@ -34,6 +34,7 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 struct RowInfo {
   int t, b, pos, lo, hi, nsplit;
@@ -160,81 +161,42 @@ struct DecodeCfg {
   static constexpr int KT = 32;          // keys per tile
   static constexpr int KS = D / 32;      // QK k-steps over the head dim
   static constexpr int DB = D / 16;      // 16-channel output blocks
-  static constexpr int CPR = D / 8;      // 16-byte chunks per key row
-  static constexpr int KPL = D / 16;     // V keys per lane per tile
-  static constexpr int VLD = KT + 8;     // LDS row stride of V^T (halves)
+  static constexpr int CH = D / 8;       // 16-byte chunks per key row
+  static constexpr int RPI = 64 / CH;    // key rows per 1 KB load instruction
+  static constexpr int NI = KT / RPI;    // load instructions per tile (K, and again V)
+  static constexpr int KLD = D + 8;      // LDS row stride of K (halves): the 16 rows an
+                                         // operand read touches sit 4 banks apart
+  static constexpr int VLD = D + 16;     // LDS row stride of V: the 4 rows of a
+                                         // transposing read sit 8 banks apart
   static constexpr int TBL = 256;        // block-table entries staged per segment
 };
 
-// Position of tile key k in the V^T rows: the PV operand of lane group q
-// (8 consecutive halves at 8q) must hold keys {4q..4q+3, 16+4q..16+4q+3}, the
-// keys of the score accumulator rows that lane group holds.
-__device__ __forceinline__ int vt_pos(int k) {
-  return 8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3);
-}
-
-// K rows of the tile for the QK A operand.  A masked key (past the segment or
-// in an unmapped block) reads block 0 instead; its score is replaced by -inf
-// with a select, so whatever it holds never reaches the softmax.
+// Whole key rows of one tile, K and V (1 KB per instruction: RPI rows of 2D
+// bytes; lane l moves chunk l % CH of row l / CH).  Bit i of the returned mask
+// says whether the row of instruction i is a real key; the others read block
+// 0 and are zeroed when stored, so nothing non-finite reaches the products.
 template <int D>
-__device__ __forceinline__ void load_k(const uint16_t* kb, const int32_t* tbl, int first_bi,
-                                       int shift, int64_t tok_stride, int k0, int seg_hi,
-                                       int lane, u32x4 (&kr)[2][DecodeCfg<D>::KS]) {
+__device__ __forceinline__ uint32_t load_tile(const uint16_t* kb, const uint16_t* vb,
+                                              const int32_t* tbl, int first_bi, int shift,
+                                              int64_t tok_stride, int k0, int seg_hi, int lane,
+                                              u32x4 (&kr)[DecodeCfg<D>::NI],
+                                              u32x4 (&vr)[DecodeCfg<D>::NI]) {
   using C = DecodeCfg<D>;
   const int bmask = (1 << shift) - 1;
-  const int q = lane >> 4, l16 = lane & 15;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int key = k0 + 16 * s + l16;
-    const bool in = key < seg_hi;
-    const int blk = tbl[in ? (key >> shift) - first_bi : 0];
-    const int64_t off = ((int64_t)(in && blk >= 0 ? blk : 0) * (bmask + 1) + (key & bmask)) * tok_stride;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) kr[s][ks] = load16(kb + off + 8 * q + 32 * ks);
-  }
-}
-
-// V rows of the tile (whole 16-byte chunks, coalesced).  Masked keys read
-// block 0; bit i of the returned mask says whether key i is real, and the
-// LDS store writes zeros for the others (a zero probability times a
-// non-finite value would otherwise poison the PV product).
-template <int D>
-__device__ __forceinline__ uint32_t load_v(const uint16_t* vb, const int32_t* tbl, int first_bi,
-                                           int shift, int64_t tok_stride, int k0, int seg_hi,
-                                           int lane, u32x4 (&vr)[DecodeCfg<D>::KPL]) {
-  using C = DecodeCfg<D>;
-  const int bmask = (1 << shift) - 1;
-  const int qv = lane / C::CPR, c = lane % C::CPR;
+  const int c = lane % C::CH;
   uint32_t okm = 0;
 #pragma unroll
-  for (int i = 0; i < C::KPL; ++i) {
-    const int key = k0 + qv * C::KPL + i;
+  for (int i = 0; i < C::NI; ++i) {
+    const int key = k0 + i * C::RPI + lane / C::CH;
     const bool in = key < seg_hi;
     const int blk = tbl[in ? (key >> shift) - first_bi : 0];
     const bool ok = in && blk >= 0;
     okm |= (uint32_t)ok << i;
-    const int64_t off = ((int64_t)(ok ? blk : 0) * (bmask + 1) + (key & bmask)) * tok_stride;
-    vr[i] = load16(vb + off + 8 * c);
+    const int64_t off = ((int64_t)(ok ? blk : 0) * (bmask + 1) + (key & bmask)) * tok_stride + 8 * c;
+    kr[i] = load16(kb + off);
+    vr[i] = load16(vb + off);
   }
   return okm;
-}
-
-// Write four keys' 8-channel chunks (k0..k3, one u32x4 each) as the 8 rows
-// d = 8c + e of V^T: row e gets the 4 halves {k0[e], k1[e], k2[e], k3[e]}.
-__device__ __forceinline__ void store_vt4(uint16_t* vt, int ld, int c, int p0, u32x4 k0, u32x4 k1,
-                                          u32x4 k2, u32x4 k3, uint32_t ok4) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t a0 = (ok4 & 1) ? k0[w] : 0u, a1 = (ok4 & 2) ? k1[w] : 0u;
-    const uint32_t a2 = (ok4 & 4) ? k2[w] : 0u, a3 = (ok4 & 8) ? k3[w] : 0u;
-    uint2 lo, hi;
-    lo.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // {k0.lo, k1.lo}
-    lo.y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-    hi.x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // {k0.hi, k1.hi}
-    hi.y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-    *reinterpret_cast<uint2*>(&vt[(8 * c + 2 * w) * ld + p0]) = lo;
-    *reinterpret_cast<uint2*>(&vt[(8 * c + 2 * w + 1) * ld + p0]) = hi;
-  }
 }
 
 template <int D, bool SOFTCAP>
@@ -242,7 +204,8 @@ __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : D <= 128 ? 2 : 1)))
 void decode_kernel(const DecodeArgs a) {
   using C = DecodeCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[kDecodeWaves][D * C::VLD];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kDecodeWaves][C::KT * C::KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kDecodeWaves][C::KT * C::VLD];
   __shared__ int32_t s_tbl[kDecodeWaves][C::TBL];
 
   // the wave index is uniform across the wave: saying so keeps every per-item
@@ -256,7 +219,8 @@ void decode_kernel(const DecodeArgs a) {
   const int64_t HD = (int64_t)a.num_heads * D;
   const int total = a.listed ? (*a.entry_count) * HC : a.rows * HC;
   const int nworkers = gridDim.x * kDecodeWaves;
-  uint16_t* vt = s_vt[wave];
+  uint16_t* kt = s_k[wave];
+  uint16_t* vt = s_v[wave];
   int32_t* tbl = s_tbl[wave];
   const int shift = sl.block_shift;
   const int64_t tok_stride = (int64_t)a.kv_heads * D;
@@ -338,12 +302,33 @@ void decode_kernel(const DecodeArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
       const int ntile = (seg_hi - seg_lo + C::KT - 1) / C::KT;
-      u32x4 kr[2][C::KS], vr[C::KPL];
-      load_k<D>(kb, tbl, first_bi, shift, tok_stride, seg_lo, seg_hi, lane, kr);
-      uint32_t vok = load_v<D>(vb, tbl, first_bi, shift, tok_stride, seg_lo, seg_hi, lane, vr);
+      u32x4 kr[C::NI], vr[C::NI];
+      uint32_t okm = load_tile<D>(kb, vb, tbl, first_bi, shift, tok_stride, seg_lo, seg_hi, lane,
+                                  kr, vr);
       for (int it = 0; it < ntile; ++it) {
         const int k0 = seg_lo + it * C::KT;
         const bool more = it + 1 < ntile;
+
+        // ---- this tile's rows into the wave's LDS tiles (zeros for masked
+        // keys), then the next tile's loads go out into the freed registers ----
+        {
+          const int c = lane % C::CH;
+#pragma unroll
+          for (int i = 0; i < C::NI; ++i) {
+            const int rw = i * C::RPI + lane / C::CH;
+            const bool ok = (okm >> i) & 1u;
+            store16(kt + rw * C::KLD + 8 * c, ok ? kr[i] : u32x4{0, 0, 0, 0});
+            store16(vt + rw * C::VLD + 8 * c, ok ? vr[i] : u32x4{0, 0, 0, 0});
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more)
+          okm = load_tile<D>(kb, vb, tbl, first_bi, shift, tok_stride, k0 + C::KT, seg_hi, lane,
+                             kr, vr);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         // ---- S^T = K . Q^T: two 16-key blocks ----
         f4 s[2];
@@ -351,15 +336,11 @@ void decode_kernel(const DecodeArgs a) {
         for (int sb = 0; sb < 2; ++sb) {
           s[sb] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks)
-            s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kr[sb][ks]), qf[ks], s[sb], 0, 0, 0);
+          for (int ks = 0; ks < C::KS; ++ks) {
+            const h8 ka = *reinterpret_cast<const h8*>(kt + (16 * sb + l16) * C::KLD + 32 * ks + 8 * q);
+            s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[ks], s[sb], 0, 0, 0);
+          }
         }
-        // K registers are free again: fetch the next tile's keys now (the
-        // scheduling barriers keep the refill after the last use, so the two
-        // tiles never hold registers at the same time)
-        __builtin_amdgcn_sched_barrier(0);
-        if (more) load_k<D>(kb, tbl, first_bi, shift, tok_stride, k0 + C::KT, seg_hi, lane, kr);
-        __builtin_amdgcn_sched_barrier(0);
 
         // ---- scores (log2 units), mask, running max ----
         const bool edge = any_hole || k0 + C::KT > seg_hi;
@@ -396,7 +377,7 @@ void decode_kernel(const DecodeArgs a) {
           for (int i = 0; i < C::DB; ++i) acc[i] *= alpha;
         }
         const float mu = m == kNegInf ? 0.f : m;
-        h8 pf;
+        h8 pf;   // keys 4q + (0..3) of both 16-key blocks, in that order
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float p = exp2_fast(x[i] - mu);
@@ -404,25 +385,20 @@ void decode_kernel(const DecodeArgs a) {
           pf[i] = (_Float16)p;
         }
 
-        // ---- V tile -> LDS, transposed (four keys per 8-byte write) ----
-        {
-          const int qv = lane / C::CPR, c = lane % C::CPR;
-#pragma unroll
-          for (int g4 = 0; g4 < C::KPL / 4; ++g4)
-            store_vt4(vt, C::VLD, c, vt_pos(qv * C::KPL + 4 * g4), vr[4 * g4], vr[4 * g4 + 1],
-                      vr[4 * g4 + 2], vr[4 * g4 + 3], (vok >> (4 * g4)) & 15u);
-        }
-        // V registers are free again: fetch the next tile's values now
-        __builtin_amdgcn_sched_barrier(0);
-        if (more) vok = load_v<D>(vb, tbl, first_bi, shift, tok_stride, k0 + C::KT, seg_hi, lane, vr);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // ---- O^T += V^T . P^T ----
+        // ---- O^T += V^T . P^T: the V^T operand by transposing LDS reads;
+        // lane k of 16-lane group q points at 4 channels of key 4q + k / 4
+        // (then 16 + 4q + k / 4), and lane i receives channel i of those four
+        // keys -- the keys of this lane group's P values ----
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const h8 va = *reinterpret_cast<const h8*>(&vt[(16 * db + l16) * C::VLD + 8 * q]);
+          v4s part[2];
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb)
+            part[sb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s*)(
+                    vt + (16 * sb + 4 * q + (l16 >> 2)) * C::VLD + 16 * db + 4 * (l16 & 3)));
+          h8 va;
+          __builtin_memcpy(&va, part, 16);
           acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf, acc[db], 0, 0, 0);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
