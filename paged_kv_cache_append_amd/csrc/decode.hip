@@ -97,10 +97,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const PlanArgs a) {
   __shared__ int s_wave[16];
   __shared__ int s_sum;
   __shared__ int s_first[1024];   // entry offset of each row of the chunk
+  __shared__ RowInfo s_info[1024];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  for (int i = tid; i < a.zero_count; i += 1024) a.zero[i] = 0;
   int total = 0;
   for (int r0 = 0; r0 < a.rows; r0 += 1024) {
     const int row = r0 + tid;
@@ -108,11 +108,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(const PlanArgs a) {
     if (row < a.rows) {
       RowInfo r;
       bool orphan;
-      if (resolve_row(a.s, a.token_mode, row, a.window, a.split_tokens, a.max_splits, r, orphan))
+      if (resolve_row(a.s, a.token_mode, row, a.window, a.split_tokens, a.max_splits, r, orphan)) {
         n = r.nsplit;
-      else if (orphan)
+        s_info[tid] = r;
+      } else if (orphan) {
         for (int i = 0; i < a.row_width; i += 8)
           store16(a.out + (int64_t)row * a.row_width + i, u32x4{0, 0, 0, 0});
+      }
     }
     int incl = n;
 #pragma unroll
@@ -145,7 +147,17 @@ __global__ __launch_bounds__(1024) void plan_kernel(const PlanArgs a) {
         const int mid = (lo + hi + 1) >> 1;
         if (s_first[mid] <= e) lo = mid; else hi = mid - 1;
       }
-      a.entries[total + e] = make_int2(r0 + lo, e - s_first[lo]);
+      const RowInfo& r = s_info[lo];
+      DecodeEntry en;
+      en.row = r0 + lo;
+      en.split = e - s_first[lo];
+      en.k_lo = r.lo + en.split * a.split_tokens;
+      en.k_hi = min(r.hi, en.k_lo + a.split_tokens);
+      en.t = r.t;
+      en.b = r.b;
+      en.pos = r.pos;
+      en.nsplit = r.nsplit;
+      a.entries[total + e] = en;
     }
     total += s_sum;
     __syncthreads();
@@ -228,30 +240,35 @@ void decode_kernel(const DecodeArgs a) {
   for (int item = blockIdx.x * kDecodeWaves + wave; item < total; item += nworkers) {
     const int e = item / HC;
     const int kvhc = item - e * HC;
-    int row, split;
-    if (a.listed) {
-      const int2 en = a.entries[e];
-      row = en.x;
-      split = en.y;
-    } else {
-      row = e;
-      split = 0;
-    }
     const int kvh = kvhc / a.head_chunks;
     const int h0 = kvh * a.group + (kvhc - kvh * a.head_chunks) * a.chunk_heads;
 
+    int row, split, k_lo, k_hi;
     RowInfo r;
-    bool orphan;
-    if (!resolve_row(sl, a.token_mode, row, a.window, a.split_tokens, a.max_splits, r, orphan)) {
-      if (orphan && !a.listed && row < sl.tokens) {   // token owned by no request: zero
-        for (int i = lane; i < a.chunk_heads * (D / 8); i += 64)
-          store16(a.out + row * HD + (int64_t)h0 * D + 8 * i, u32x4{0, 0, 0, 0});
+    if (a.listed) {
+      const DecodeEntry en = a.entries[e];
+      row = en.row;
+      split = en.split;
+      k_lo = en.k_lo;
+      k_hi = en.k_hi;
+      r.t = en.t;
+      r.b = en.b;
+      r.pos = en.pos;
+      r.nsplit = en.nsplit;
+    } else {
+      row = e;
+      split = 0;
+      bool orphan;
+      if (!resolve_row(sl, a.token_mode, row, a.window, a.split_tokens, a.max_splits, r, orphan)) {
+        if (orphan && row < sl.tokens) {   // token owned by no request: zero
+          for (int i = lane; i < a.chunk_heads * (D / 8); i += 64)
+            store16(a.out + row * HD + (int64_t)h0 * D + 8 * i, u32x4{0, 0, 0, 0});
+        }
+        continue;
       }
-      continue;
+      k_lo = r.lo;
+      k_hi = r.nsplit > 0 ? min(r.hi, k_lo + a.split_tokens) : k_lo;
     }
-    if (split >= max(r.nsplit, 1)) continue;
-    const int k_lo = r.lo + split * a.split_tokens;
-    const int k_hi = r.nsplit > 0 ? min(r.hi, k_lo + a.split_tokens) : k_lo;
 
     // Q as the B operand: lane (q, l16) holds head l16, channels 32ks + 8q + [0,8)
     const bool head_ok = l16 < a.chunk_heads;

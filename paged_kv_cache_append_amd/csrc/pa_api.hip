@@ -231,7 +231,7 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
     const size_t per = (size_t)pl.rows * p->num_heads * pl.max_splits;
     pl.off_ml = align256(per * p->head_size * sizeof(float));
     pl.off_entries = pl.off_ml + align256(per * 2 * sizeof(float));
-    pl.off_count = pl.off_entries + align256((size_t)pl.rows * pl.max_splits * 2 * sizeof(int32_t));
+    pl.off_count = pl.off_entries + align256((size_t)pl.rows * pl.max_splits * sizeof(pa::DecodeEntry));
     cur = pl.off_count + 256;
   }
   if (pl.prefill) {
@@ -413,7 +413,7 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
   char* ws = static_cast<char*>(workspace);
   d.part_o = pl.listed ? reinterpret_cast<float*>(ws) : nullptr;
   d.part_ml = pl.listed ? reinterpret_cast<float*>(ws + pl.off_ml) : nullptr;
-  d.entries = pl.listed ? reinterpret_cast<const int2*>(ws + pl.off_entries) : nullptr;
+  d.entries = pl.listed ? reinterpret_cast<const pa::DecodeEntry*>(ws + pl.off_entries) : nullptr;
   d.entry_count = pl.listed ? reinterpret_cast<const int32_t*>(ws + pl.off_count) : nullptr;
   d.listed = pl.listed ? 1 : 0;
   d.rows = pl.rows;
@@ -434,10 +434,47 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
   d.cap_out = cap ? params->softcap * log2e : 0.f;
   d.use_softcap = cap ? 1 : 0;
 
+  if (pl.prefill) {
+    pa::PrefillArgs f;
+    f.s = sl;
+    f.query = d.query;
+    f.key_cache = d.key_cache;
+    f.value_cache = d.value_cache;
+    f.cos = d.cos;
+    f.sin = d.sin;
+    f.out = d.out;
+    f.num_heads = params->num_heads;
+    f.kv_heads = params->kv_num_heads;
+    f.group = pl.g;
+    f.window = params->local_window_size;
+    f.rotary_dim = d.rotary_dim;
+    f.rotary_interleaved = d.rotary_interleaved;
+    f.rotary_rows = d.rotary_rows;
+    f.tiles = pl.prefill_tiles;
+    f.chunks = pl.prefill_chunks;
+    f.piece_tiles = params->prefill_pieces > 0 ? 0 : pa::kPrefillPieceTiles;
+    f.part_o = pl.prefill_chunks > 1 ? reinterpret_cast<float*>(ws + pl.off_pf_o) : nullptr;
+    f.part_ml = pl.prefill_chunks > 1 ? reinterpret_cast<float*>(ws + pl.off_pf_ml) : nullptr;
+    f.score_scale = d.score_scale;
+    f.cap_in2 = 2.0f * log2e * d.cap_in;
+    f.cap_out = d.cap_out;
+    f.use_softcap = d.use_softcap;
+    const dim3 grid(pl.prefill_tiles * pl.prefill_chunks + 1, params->kv_num_heads);
+    {
+      StageScope scope(PA_STAGE_PREFILL, s);
+      if ((st = device_status(pa::launch_prefill(f, D, grid, s), "prefill kernel launch")) != PA_OK)
+        return st;
+    }
+    if (pl.prefill_chunks > 1) {
+      StageScope scope(PA_STAGE_PREFILL_MERGE, s);
+      if ((st = device_status(pa::launch_prefill_merge(f, D, s), "prefill merge launch")) != PA_OK)
+        return st;
+    }
+  }
   if (pl.listed) {
     pa::PlanArgs pa_;
     pa_.s = sl;
-    pa_.entries = reinterpret_cast<int2*>(ws + pl.off_entries);
+    pa_.entries = reinterpret_cast<pa::DecodeEntry*>(ws + pl.off_entries);
     pa_.entry_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
     pa_.out = d.out;
     pa_.rows = pl.rows;
@@ -446,8 +483,6 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     pa_.max_splits = pl.max_splits;
     pa_.window = params->local_window_size;
     pa_.row_width = params->num_heads * D;
-    pa_.zero = nullptr;
-    pa_.zero_count = 0;
     StageScope scope(PA_STAGE_PLAN, s);
     if ((st = device_status(pa::launch_plan(pa_, s), "plan kernel launch")) != PA_OK) return st;
   }
@@ -483,43 +518,6 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
       mg.window = params->local_window_size;
       StageScope scope(PA_STAGE_MERGE, s);
       if ((st = device_status(pa::launch_merge(mg, s), "merge kernel launch")) != PA_OK)
-        return st;
-    }
-  }
-  if (pl.prefill) {
-    pa::PrefillArgs f;
-    f.s = sl;
-    f.query = d.query;
-    f.key_cache = d.key_cache;
-    f.value_cache = d.value_cache;
-    f.cos = d.cos;
-    f.sin = d.sin;
-    f.out = d.out;
-    f.num_heads = params->num_heads;
-    f.kv_heads = params->kv_num_heads;
-    f.group = pl.g;
-    f.window = params->local_window_size;
-    f.rotary_dim = d.rotary_dim;
-    f.rotary_interleaved = d.rotary_interleaved;
-    f.rotary_rows = d.rotary_rows;
-    f.tiles = pl.prefill_tiles;
-    f.chunks = pl.prefill_chunks;
-    f.piece_tiles = params->prefill_pieces > 0 ? 0 : pa::kPrefillPieceTiles;
-    f.part_o = pl.prefill_chunks > 1 ? reinterpret_cast<float*>(ws + pl.off_pf_o) : nullptr;
-    f.part_ml = pl.prefill_chunks > 1 ? reinterpret_cast<float*>(ws + pl.off_pf_ml) : nullptr;
-    f.score_scale = d.score_scale;
-    f.cap_in2 = 2.0f * log2e * d.cap_in;
-    f.cap_out = d.cap_out;
-    f.use_softcap = d.use_softcap;
-    const dim3 grid(pl.prefill_tiles * pl.prefill_chunks + 1, params->kv_num_heads);
-    {
-      StageScope scope(PA_STAGE_PREFILL, s);
-      if ((st = device_status(pa::launch_prefill(f, D, grid, s), "prefill kernel launch")) != PA_OK)
-        return st;
-    }
-    if (pl.prefill_chunks > 1) {
-      StageScope scope(PA_STAGE_PREFILL_MERGE, s);
-      if ((st = device_status(pa::launch_prefill_merge(f, D, s), "prefill merge launch")) != PA_OK)
         return st;
     }
   }

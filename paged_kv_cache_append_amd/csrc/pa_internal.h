@@ -43,6 +43,14 @@ struct AppendArgs {
 // a split is a run of at most split_tokens keys of the row's admitted interval.
 // With more than one possible split per row the list is built on the device
 // by the plan kernel ("listed" mode); otherwise item = (row, split 0).
+// One work-list entry: a (row, split) pair with what the decode workers need
+// of the row already resolved (query token, request, position, split count)
+// and the split's key interval [k_lo, k_hi).
+struct DecodeEntry {
+  int32_t row, split, k_lo, k_hi;
+  int32_t t, b, pos, nsplit;
+};
+
 struct DecodeArgs {
   SeqLayout s;
   const uint16_t* query;        // fp16 [T, H*D]
@@ -53,7 +61,7 @@ struct DecodeArgs {
   uint16_t* out;                // fp16 [T, H*D]
   float* part_o;                // [rows, H, S, D]   unnormalised split outputs
   float* part_ml;               // [rows, H, S, 2]   (max in log2 units, sum)
-  const int2* entries;          // listed mode: (row, split) per entry
+  const DecodeEntry* entries;   // listed mode: work list
   const int32_t* entry_count;   // listed mode: number of entries
   int32_t listed;
   int32_t rows;
@@ -79,7 +87,7 @@ struct DecodeArgs {
 // work, and zeroes output rows of tokens owned by no request (token mode).
 struct PlanArgs {
   SeqLayout s;
-  int2* entries;
+  DecodeEntry* entries;
   int32_t* entry_count;
   uint16_t* out;
   int32_t rows;
@@ -88,8 +96,6 @@ struct PlanArgs {
   int32_t max_splits;
   int32_t window;
   int32_t row_width;            // H * D elements of an output row
-  int32_t* zero;                // words cleared before anything else runs (or null)
-  int32_t zero_count;
 };
 
 // Split merge: one wave per (row, head) of rows with more than one split.
