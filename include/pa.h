@@ -77,7 +77,7 @@ typedef struct {
   void *value_cache;                        /* same shape; both mutated in place by
                                                pa_append_kv (cache outputs alias the
                                                inputs, section 4.4)                   */
-  int64_t num_blocks;                       /* > 0; num_blocks * block_size <= 2^32  */
+  int64_t num_blocks;                       /* > 0; num_blocks * block_size < 2^32   */
   const int32_t *block_table;               /* int32 [batch_size, max_blocks_per_seq]
                                                row-major; entries past a request's
                                                length are never read                 */

@@ -118,9 +118,9 @@ pa_status check_common(const pa_attn_params* p, const pa_paged_kv* kv) {
   if (kv->num_blocks <= 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks: expected > 0, got %lld",
                 (long long)kv->num_blocks);
-  if (kv->num_blocks > ((int64_t)1 << 32) / p->block_size)
+  if (kv->num_blocks > (((int64_t)1 << 32) - 1) / p->block_size)
     return fail(PA_ERR_INVALID_ARGUMENT,
-                "num_blocks: expected num_blocks * block_size <= 2^32 slots, got %lld blocks",
+                "num_blocks: expected num_blocks * block_size < 2^32 slots, got %lld blocks",
                 (long long)kv->num_blocks);
   if (kv->max_blocks_per_seq <= 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq: expected > 0, got %d",

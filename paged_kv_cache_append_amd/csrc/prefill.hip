@@ -55,7 +55,7 @@ struct PrefillCfg {
                                              // read fall 64 bytes apart
   static constexpr int DMA = SLOTS / 4;      // direct loads per wave per tile (K or V)
   static constexpr int SEGT = 512;           // block-table entries staged per segment
-  static constexpr int PIPE = KS < 4 ? KS : 4;   // operand reads in flight (k-steps)
+  static constexpr int PIPE = KS < 2 ? KS : 2;   // operand reads in flight (k-steps)
 };
 
 // Tile layout in LDS: key row r (0..63) of the tile lives in slot
@@ -181,6 +181,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  __builtin_assume(wave >= 0 && wave < 4);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
   const int kvh = blockIdx.y;
@@ -303,199 +304,354 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     wg_hole = __syncthreads_or(hole) || wg_hole;
   };
 
-  // Direct loads of one tile into LDS buffer B: wave w fills slots w, w + 4,
-  // ...; lane i of a slot load moves chunk i % CH of key row i / CH of that
-  // slot.  Keys outside [lo, hi) or in an unmapped block read a zero row.
   auto kbuf = [&](auto B) -> char* { if constexpr (B() == 0) return K0; else return K1; };
   auto vbuf = [&](auto B) -> char* { if constexpr (B() == 0) return V0; else return V1; };
-  auto okbuf = [&](auto B) -> uint8_t* { if constexpr (B() == 0) return ok0; else return ok1; };
-  auto dma_tile = [&](int kt0, auto B) {
-    // all table lookups first (one LDS round trip), then the address
-    // arithmetic in 32 x 32 -> 64-bit products, then the loads
-    int tau[C::DMA], blk[C::DMA];
+  auto kt_of = [&](int t) { return kt_begin + t * C::KT; };
+
+  // Key rows this wave moves for key tile t (wave w fills slots w, w + 4,
+  // ...; lane i of a slot load moves chunk i % CH of key row i / CH of the
+  // slot) and their pool blocks: -1 for keys outside [lo, hi), in an unmapped
+  // block, or in a tile past this workgroup's range (those read a zero row).
+  // Branch-free, so it can share a scheduling region with the matrix work.
+  auto lookup = [&](int t, int (&tau)[C::DMA], int (&blk)[C::DMA]) {
+    const int kt0 = kt_of(t);
+    const bool valid = t < ntiles;
 #pragma unroll
     for (int mi = 0; mi < C::DMA; ++mi) {
       const int slot = wave + 4 * mi;
       tau[mi] = kt0 + (slot / C::NS) * 32 + (slot % C::NS) + C::NS * (lane / C::CH);
-      const bool in = tau[mi] >= lo && tau[mi] < hi;
-      blk[mi] = in ? s_tbl[(tau[mi] >> shift) - seg_first] : -1;
-    }
-    const int chunk = lane % C::CH;
-#pragma unroll
-    for (int mi = 0; mi < C::DMA; ++mi) {
-      const int slot = wave + 4 * mi;
-      const bool ok = blk[mi] >= 0;
-      const uint32_t slot_row = ((uint32_t)blk[mi] << shift) | (uint32_t)(tau[mi] & bmask);
-      const uint64_t off = (uint64_t)(ok ? slot_row : 0u) * tok_stride32 + 8 * chunk;
-      dma16(ok ? kbase + off : g_zero_row + 8 * chunk, kbuf(B) + slot * C::KSLOT);
-      dma16(ok ? vbase + off : g_zero_row + 8 * chunk, vbuf(B) + slot * C::VSLOT);
-      if (chunk == 0) okbuf(B)[tau[mi] - kt0] = ok;
+      // bitwise tests and an OR with 0 / -1 (not a select of the loaded
+      // value) keep this free of branches
+      const bool in = valid & (tau[mi] >= lo) & (tau[mi] < hi);
+      const int v = s_tbl[in ? (tau[mi] >> shift) - seg_first : 0];
+      blk[mi] = v | (in ? 0 : -1);
     }
   };
-  auto need_segment = [&](int kt0) {
-    const int last = min(kt0 + C::KT, hi) - 1;
+  // The same for one load: the pool row (block * block_size + offset) of the
+  // key row this lane moves with load mi of tile t, or ~0 for a zero row (pools
+  // hold fewer than 2^32 rows).
+  auto row_of = [&](int t, int mi) -> uint32_t {
+    const int slot = wave + 4 * mi;
+    const int tau = kt_of(t) + (slot / C::NS) * 32 + (slot % C::NS) + C::NS * (lane / C::CH);
+    const bool in = (t < ntiles) & (tau >= lo) & (tau < hi);
+    const int v = s_tbl[in ? (tau >> shift) - seg_first : 0] | (in ? 0 : -1);
+    return v < 0 ? ~0u : ((uint32_t)v << shift) | (uint32_t)(tau & bmask);
+  };
+  const int chunk = lane % C::CH;
+  const uint16_t* zrow = g_zero_row + 8 * chunk;
+  auto issue_row = [&](uint32_t row, const uint16_t* base, char* buf, int slot_bytes, int mi) {
+    const int slot = wave + 4 * mi;
+    // one source pointer, base + a selected element offset (a select between
+    // two pointers makes the compiler split the load in two exec-masked halves)
+    const int64_t off =
+        row != ~0u ? (int64_t)((uint64_t)row * tok_stride32 + 8 * chunk) : zrow - base;
+    dma16(base + off, buf + slot * slot_bytes);
+  };
+  auto issue_one = [&](int tau, int blk, const uint16_t* base, char* buf, int slot_bytes,
+                       int mi) {
+    const uint32_t row = blk < 0 ? ~0u : ((uint32_t)blk << shift) | (uint32_t)(tau & bmask);
+    issue_row(row, base, buf, slot_bytes, mi);
+  };
+  auto issue = [&](const int (&tau)[C::DMA], const int (&blk)[C::DMA], const uint16_t* base,
+                   char* buf, int slot_bytes) {
+#pragma unroll
+    for (int mi = 0; mi < C::DMA; ++mi) issue_one(tau[mi], blk[mi], base, buf, slot_bytes, mi);
+  };
+  // the last key tile a staged table slice must cover is within reach
+  auto need_segment = [&](int t) {
+    const int last = min(kt_of(t) + C::KT, hi) - 1;
     return (last >> shift) >= seg_first + C::SEGT;
   };
 
-  using Buf0 = std::integral_constant<int, 0>;
-  using Buf1 = std::integral_constant<int, 1>;
-  if (ntiles > 0) {
-    stage_table(max(kt_begin, lo));
-    dma_tile(kt_begin, Buf0{});
-    wait_vmem();
-    __syncthreads();
-  }
+  // S^T = K . Q^T for two 32-key blocks of the tile in K buffer B.  The two
+  // blocks alternate so consecutive MFMAs are independent; operand reads run
+  // PIPE k-steps ahead (their order is fixed by the caller's schedule).
+  // Per-lane parts of the operand addresses, made opaque so every operand
+  // read is one variable base plus a constant: the compiler otherwise splits
+  // them into long address chains whose reads lose the information that they
+  // cannot overlap the loads streaming into the other buffers (and then wait
+  // for those loads).  row_byte(c + x) = row_byte(c) + row_byte(x) for c a
+  // multiple of 8 and x < 8.
+  int koff = 16 * hf + row_byte<D>(l32, C::KSLOT);
+  int voff = 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) +
+             row_byte<D>(4 * hf + ((lane & 15) >> 2), C::VSLOT);
+  asm("" : "+v"(koff), "+v"(voff));
 
-  // One key tile from buffer B while the next tile streams into the other
-  // buffer.  Both buffers are separate LDS objects named statically, so the
-  // compiler can tell the direct loads into one from the reads of the other
-  // and does not wait for the prefetch before computing on the current tile.
-  auto step = [&](int it, auto B) {
-    const int kt0 = kt_begin + it * C::KT;
-    if (it + 1 < ntiles) {
-      if (need_segment(kt0 + C::KT)) stage_table(kt0 + C::KT);
-      dma_tile(kt0 + C::KT, std::integral_constant<int, 1 - B()>{});
-    }
-
-    // ---- S^T = K . Q^T for two 32-key blocks ----
-    // The two 32-key blocks alternate so consecutive MFMAs are independent,
-    // and the LDS operand reads run PIPE k-steps ahead of the MFMAs that use
-    // them (a read's latency is several MFMA issue slots).
-    f16v s[2];
+  auto qk = [&](auto B, f16v (&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    const char* kt = kbuf(B) + koff;
+    auto kread = [&](int ks, int kb) {
+      return *reinterpret_cast<const h8*>(kt + row_byte<D>(kb * 32, C::KSLOT) + 32 * ks);
+    };
+    h8 kf[C::PIPE][2];
+#pragma unroll
+    for (int i = 0; i < C::PIPE; ++i)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) kf[i][kb] = kread(i, kb);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks % C::PIPE][kb], qf[ks], s[kb], 0, 0, 0);
+        if (ks + C::PIPE < C::KS) kf[ks % C::PIPE][kb] = kread(ks + C::PIPE, kb);
+      }
+    }
+  };
+
+  // Raw score -> log2-unit logit: scale, or softcap * tanh(scale * s / softcap)
+  // with tanh(y) = 1 - 2 / (exp(2y) + 1) (exact limits +-1 for large |y|).
+  auto logit = [&](float x) {
+    if constexpr (SOFTCAP)
+      return a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * a.cap_in2) + 1.0f));
+    else
+      return x * a.score_scale;
+  };
+  // A row's tile maximum in log2 units (scale and softcap are monotone, so
+  // the maximum is taken on raw scores); the row's two lanes agree.
+  auto tile_max = [&](const f16v (&s)[2]) {
+    float mq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      mq[q] = fmaxf(fmaxf(s[q >> 1][8 * (q & 1)], s[q >> 1][8 * (q & 1) + 1]),
+                    fmaxf(s[q >> 1][8 * (q & 1) + 2], s[q >> 1][8 * (q & 1) + 3]));
+#pragma unroll
+      for (int r = 4; r < 8; ++r) mq[q] = fmaxf(mq[q], s[q >> 1][8 * (q & 1) + r]);
+    }
+    const float mx = xor32_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
+    return mx == kNegInf ? kNegInf : logit(mx);
+  };
+  // Keys outside the row's causal window; accumulator entry r of block kb
+  // holds key kt0 + 32 kb + 8 (r / 4) + 4 hf + r % 4.
+  auto full_tile = [&](int kt0) {
+    return kt0 >= lo && kt0 + C::KT <= hi && kt0 + C::KT - 1 <= wpos_min &&
+           (a.window <= 0 || kt0 >= wpos_max - a.window + 1);
+  };
+  auto pos_mask = [&](f16v (&s)[2], int kt0) {
+    const int wlo = a.window > 0 ? pos - a.window + 1 : INT32_MIN;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tau = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        s[kb][r] = ((tau <= pos) & (tau >= wlo)) ? s[kb][r] : kNegInf;
+      }
+  };
+  // Keys outside [lo, hi) or in an unmapped block (only when the key range
+  // has a hole; the staged table slice still covers the tile).  A run of four
+  // keys never straddles a block.
+  auto hole_mask = [&](f16v (&s)[2], int kt0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int tau0 = kt0 + kb * 32 + 8 * rq + 4 * hf;
+        const int bi = (tau0 >> shift) - seg_first;
+        const int v = bi >= 0 && bi < C::SEGT ? s_tbl[bi] : -1;
+#pragma unroll
+        for (int r3 = 0; r3 < 4; ++r3) {
+          const int tau = tau0 + r3;
+          if (!(v >= 0 && tau >= lo && tau < hi)) s[kb][4 * rq + r3] = kNegInf;
+        }
+      }
+  };
+
+  // Probabilities p = 2^(logit - mu) of scores f0 .. f0 + n - 1 (f = 16 kb +
+  // r) of a tile, into the fp16 B operand of the PV product (k-step ks covers
+  // accumulator rows 8 (ks & 1) .. +7 of 32-key block ks / 2); their sums
+  // accumulate in part.  A masked score (-inf) gives 0.
+  auto softmax_part = [&](const f16v (&s)[2], float mu, h8 (&pf)[4], float (&part)[4], int f0,
+                          int n) {
+#pragma unroll
+    for (int f = f0; f < f0 + n; ++f) {
+      const int kb = f >> 4, r = f & 15;
+      const float x = s[kb][r];
+      float e;
+      if constexpr (SOFTCAP) {
+        // cap * tanh(y) - mu = (cap - mu) - 2 cap / (2^t + 1), t = 2y log2(e);
+        // a masked score (t = -inf) gets -inf through t * 2^-120, which is
+        // negligible for any finite t
+        const float t = x * a.cap_in2;
+        const float r = __builtin_amdgcn_rcpf(exp2_fast(t) + 1.0f);
+        e = __builtin_fmaf(t, 0x1p-120f, __builtin_fmaf(r, -2.0f * a.cap_out, a.cap_out - mu));
+      } else {
+        e = __builtin_fmaf(x, a.score_scale, -mu);
+      }
+      const float p = exp2_fast(e);
+      part[r & 3] += p;
+      pf[2 * kb + (r >> 3)][r & 7] = (_Float16)p;
+    }
+  };
+
+  // O^T += V^T . P^T (region B of a step) takes the V^T operand from
+  // transposing LDS reads: lane k of each 16-lane group points at 4 channels
+  // of one key; lane i then receives channel i of four keys.  Two reads give
+  // the 8 keys of k-step ks that the P operand of this lane holds:
+  // 16 ks + 8 rr + 4 hf + (0..3), rr = 0, 1.
+  constexpr int NV = 4 * C::DB;
+
+  // ---- prologue: K and V of tile 0 and K of tile 1, then tile 0's scores ----
+  using Buf0 = std::integral_constant<int, 0>;
+  using Buf1 = std::integral_constant<int, 1>;
+  f16v sA[2], sB[2];
+  float mxA = kNegInf, mxB = kNegInf;
+  if (ntiles > 0) {
+    stage_table(max(kt_begin, lo));
+    int t0[C::DMA], b0[C::DMA], t1[C::DMA], b1[C::DMA];
+    lookup(0, t0, b0);
+    lookup(1, t1, b1);
+    issue(t0, b0, kbase, K0, C::KSLOT);
+    issue(t0, b0, vbase, V0, C::VSLOT);
+    issue(t1, b1, kbase, K1, C::KSLOT);
+    wait_vmem();
+    __syncthreads();
+    qk(Buf0{}, sA);
+    pipeline_order<2 * C::PIPE, 2 * C::KS, 1>();
+    if (!full_tile(kt_of(0))) pos_mask(sA, kt_of(0));
+    mxA = tile_max(sA);
+    __syncthreads();   // K buffer 0 is refilled by the first step
+  }
+
+  // One step: the softmax and PV product of key tile `it` (scores in s_cur,
+  // V in buffer B) while tile it + 1's scores are computed (K in buffer 1 - B)
+  // and the loads of tile it + 1's V and tile it + 2's K stream in.  The
+  // softmax, the load issue and the QK product form one scheduling region,
+  // as do the PV product and the next tile's row maximum, so the vector ALU
+  // and the matrix cores work at the same time.
+  auto step = [&](int it, auto B, f16v (&s_cur)[2], f16v (&s_next)[2], float& mx_cur,
+                  float& mx_next) {
+    using NB = std::integral_constant<int, 1 - B()>;
+    if (wg_hole) {   // uniform and rare
+      hole_mask(s_cur, kt_of(it));
+      mx_cur = tile_max(s_cur);
+    }
+    // lazy rescale: the running max is only raised when the tile exceeds it
+    // by more than kRescaleSlack (probabilities then stay below 2^slack)
     {
-      const char* kt = kbuf(B) + 16 * hf;
+      const float mn = mx_cur > m + kRescaleSlack ? mx_cur : m;
+      const float alpha = mn == m ? 1.0f : exp2_fast(m - mn);
+      m = mn;
+      lsum *= alpha;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      }
+    }
+    const float mu = m == kNegInf ? 0.f : m;
+    {
+      const int tl = min(it + 2, ntiles - 1);
+      if (tl > it && need_segment(tl)) stage_table(max(kt_of(it + 1), lo));
+    }
+
+    // ---- region A: QK of tile it + 1, with the softmax of tile it and the
+    // loads of tile it + 1's V and tile it + 2's K spread over its k-steps
+    // (2 DMA = KS direct loads, one per k-step).  Each k-step is fenced so
+    // the vector work stays between the matrix instructions. ----
+    h8 pf[4];
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    {
+      // load j of the step: tile it + 1's V (j < DMA), then tile it + 2's K;
+      // its table lookup is issued one k-step before the load
+      auto row_j = [&](int j) { return j < C::DMA ? row_of(it + 1, j) : row_of(it + 2, j - C::DMA); };
+      uint32_t row_next = row_j(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s_next[kb][i] = 0.f;
+      const char* kt = kbuf(NB{}) + koff;
       auto kread = [&](int ks, int kb) {
-        return *reinterpret_cast<const h8*>(kt + row_byte<D>(kb * 32 + l32, C::KSLOT) + 32 * ks);
+        return *reinterpret_cast<const h8*>(kt + row_byte<D>(kb * 32, C::KSLOT) + 32 * ks);
       };
       h8 kf[C::PIPE][2];
 #pragma unroll
       for (int i = 0; i < C::PIPE; ++i)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) kf[i][kb] = kread(i, kb);
+      // probabilities of the tile's first 16-key k-step (pf[0], scores 0..7
+      // of this lane) here, in pairs at k-steps 0, KS/4, KS/2, 3KS/4; the other
+      // three quarters are computed in region B during the PV MFMAs of the
+      // quarter before
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks % C::PIPE][kb], qf[ks], s[kb], 0, 0, 0);
+          s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks % C::PIPE][kb], qf[ks], s_next[kb], 0, 0, 0);
           if (ks + C::PIPE < C::KS) kf[ks % C::PIPE][kb] = kread(ks + C::PIPE, kb);
         }
-      }
-      pipeline_order<2 * C::PIPE, 2 * C::KS, 1>();
-    }
-
-    // ---- mask, running max (on raw scores: scale and softcap are monotone) ----
-    const bool full = !wg_hole && kt0 >= lo && kt0 + C::KT <= hi && kt0 + C::KT - 1 <= wpos_min &&
-                      (a.window <= 0 || kt0 >= wpos_max - a.window + 1);
-    if (!full) {
-      // branch-free admission test; unmapped blocks only matter when the
-      // workgroup's key range has a hole (a uniform, rare branch)
-      const int wlo = a.window > 0 ? pos - a.window + 1 : INT32_MIN;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tau = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          s[kb][r] = ((tau <= pos) & (tau >= wlo)) ? s[kb][r] : kNegInf;
+        const uint32_t row = row_next;
+        if (ks + 1 < C::KS) row_next = row_j(ks + 1);
+        if (ks < C::DMA)
+          issue_row(row, vbase, vbuf(NB{}), C::VSLOT, ks);
+        else
+          issue_row(row, kbase, kbuf(B), C::KSLOT, ks - C::DMA);
+        if (ks % (C::KS / 4) == 0) {
+          softmax_part(s_cur, mu, pf, part, 2 * (ks / (C::KS / 4)), 2);
+          // anchor: the compiler would otherwise sink the exponentials down
+          // to their use in region B
+          asm volatile("" ::"v"(part[0]), "v"(part[1]), "v"(part[2]), "v"(part[3]));
         }
-      if (wg_hole) {
-        const uint8_t* key_ok = okbuf(B);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!key_ok[kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)]) s[kb][r] = kNegInf;
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = xor32_max(mx);
-    // tile max in log2 units
-    mx = mx == kNegInf ? kNegInf
-                       : (SOFTCAP ? a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(
-                                                            exp2_fast(mx * a.cap_in2) + 1.0f))
-                                  : mx * a.score_scale);
-    if (__any(mx > m + kRescaleSlack)) {
-      const float mn = mx > m + kRescaleSlack ? mx : m;
-      const float alpha = exp2_fast(m - (mn == kNegInf ? 0.f : mn));
-      m = mn;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-    }
-    const float mu = m == kNegInf ? 0.f : m;
-
-    // ---- P (fp16) as B operand; O^T += V^T . P^T ----
-    // p = exp2(scale*log2e*s - m), or with softcap exp2(cap*log2e*tanh(s*scale/cap) - m)
-    // where tanh(y) = 1 - 2/(exp(2y) + 1) (exact limits +-1 for large |y|).
-    // k-step ks of the product covers the keys of accumulator rows
-    // 8*(ks & 1) .. +7 of 32-key block ks / 2.
-    h8 pf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = s[kb][r];
-        float e;
-        if constexpr (SOFTCAP) {
-          const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * a.cap_in2) + 1.0f);
-          e = __builtin_fmaf(th, a.cap_out, -mu);
-          e = x == kNegInf ? kNegInf : e;   // masked (the softcap maps -inf to -cap)
-        } else {
-          e = __builtin_fmaf(x, a.score_scale, -mu);   // -inf for a masked key
-        }
-        const float p = exp2_fast(e);
-        lsum += p;
-        pf[2 * kb + (r >> 3)][r & 7] = (_Float16)p;
-      }
-    }
+    // ---- region B: PV of tile it, with tile it + 1's row maximum spread
+    // over its MFMAs ----
     {
-      // V^T operand by transposing LDS reads: lane k of each 16-lane group
-      // points at 4 channels of one key; lane i then receives channel i of
-      // four keys.  Two reads give the 8 keys of k-step ks that the P operand
-      // of this lane holds: 16*ks + 8*rr + 4*hf + (0..3), rr = 0, 1.
-      constexpr int NV = 4 * C::DB;
-      const int li = lane & 15;
-      const char* vt = vbuf(B) + 2 * (16 * ((lane >> 4) & 1) + 4 * (li & 3));
+      const char* vt = vbuf(B) + voff;
       auto vread = [&](int i) {
         const int db = i % C::DB, ks = i / C::DB;
-        v4s part[2];
+        v4s part2[2];
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr)
-          part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          part2[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) v4s*)(
-                  vt + row_byte<D>(16 * ks + 8 * rr + 4 * hf + (li >> 2), C::VSLOT) + 64 * db));
+                  vt + row_byte<D>(16 * ks + 8 * rr, C::VSLOT) + 64 * db));
         h8 v;
-        __builtin_memcpy(&v, part, 16);
+        __builtin_memcpy(&v, part2, 16);
         return v;
       };
       h8 vf[2 * C::PIPE];
 #pragma unroll
       for (int i = 0; i < 2 * C::PIPE; ++i) vf[i] = vread(i);
+      constexpr int MPC = 32 / NV > 0 ? 32 / NV : 1;   // max operands per MFMA
+      float mxr = kNegInf;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
         const int db = i % C::DB, ks = i / C::DB;
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % (2 * C::PIPE)], pf[ks], acc[db], 0, 0, 0);
         if (i + 2 * C::PIPE < NV) vf[i % (2 * C::PIPE)] = vread(i + 2 * C::PIPE);
+        // pf[ks + 1] in pairs at MFMAs DB/4 apart
+        if (ks + 1 < 4) {
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr)
+            if ((pr * C::DB) / 4 == db) softmax_part(s_cur, mu, pf, part, 8 * (ks + 1) + 2 * pr, 2);
+        }
+#pragma unroll
+        for (int f = i * MPC; f < (i + 1) * MPC && f < 32; ++f)
+          mxr = fmaxf(mxr, s_next[f >> 4][f & 15]);
+        asm volatile("" ::"v"(mxr), "v"(part[0]), "v"(part[1]), "v"(part[2]), "v"(part[3]));
       }
-      pipeline_order<2 * C::PIPE, NV, 2>();
+      __builtin_amdgcn_sched_barrier(0);
+      lsum += (part[0] + part[1]) + (part[2] + part[3]);
+      mxr = xor32_max(mxr);
+      mx_next = mxr == kNegInf ? kNegInf : logit(mxr);
     }
-
-    wait_vmem();        // this wave's loads of the next tile have landed
-    __syncthreads();    // ... and everyone's, and nobody reads this tile any more
+    if (it + 1 < ntiles && !full_tile(kt_of(it + 1))) {   // diagonal / window-edge tiles
+      pos_mask(s_next, kt_of(it + 1));
+      mx_next = tile_max(s_next);
+    }
+    wait_vmem();        // this wave's loads have landed
+    __syncthreads();    // ... and everyone's; buffers B (V) and 1 - B (K) are free
   };
 
   for (int it = 0; it < ntiles; it += 2) {
-    step(it, Buf0{});
-    if (it + 1 < ntiles) step(it + 1, Buf1{});
+    step(it, Buf0{}, sA, sB, mxA, mxB);
+    if (it + 1 < ntiles) step(it + 1, Buf1{}, sB, sA, mxB, mxA);
   }
 
   const float lt = xor32_sum(lsum);
