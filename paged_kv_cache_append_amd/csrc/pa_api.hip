@@ -275,6 +275,42 @@ int device_cus() {
   return cus[dev];
 }
 
+// A second stream per (thread, device): a batch with both prefill and decode
+// rows runs the prefill launches on it, forked from and joined back into the
+// caller's stream by events, so the MFMA-bound prefill tiles share the chip
+// with the HBM-bound decode workers instead of running after them.
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+pa_status side_stream(hipStream_t main, SideStream** out) {
+  thread_local SideStream per_dev[64];
+  int dev = 0;
+  hipError_t e = main ? hipStreamGetDevice(main, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_DEVICE, "stream device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(PA_ERR_DEVICE, "device index %d out of range", dev);
+  SideStream& x = per_dev[dev];
+  if (!x.st) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess || (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(PA_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(e));
+    SideStream n;
+    e = hipStreamCreateWithFlags(&n.st, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+    (void)hipSetDevice(cur);
+    if (e != hipSuccess) {
+      if (n.st) (void)hipStreamDestroy(n.st);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      return fail(PA_ERR_DEVICE, "side stream creation: %s", hipGetErrorString(e));
+    }
+    x = n;
+  }
+  *out = &x;
+  return PA_OK;
+}
+
 pa_status check_plan(const Plan& pl) {
   if (pl.max_splits > pa::kDecodeMaxSplits)
     return fail(PA_ERR_INVALID_ARGUMENT,
@@ -434,6 +470,43 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
   d.cap_out = cap ? params->softcap * log2e : 0.f;
   d.use_softcap = cap ? 1 : 0;
 
+  // prefill first, on the side stream when decode rows run beside it
+  const bool overlap = pl.prefill && pl.rows > 0;
+  if (pl.listed) {
+    pa::PlanArgs pa_;
+    pa_.s = sl;
+    pa_.entries = reinterpret_cast<pa::DecodeEntry*>(ws + pl.off_entries);
+    pa_.entry_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
+    pa_.out = d.out;
+    pa_.rows = pl.rows;
+    pa_.token_mode = d.token_mode;
+    pa_.split_tokens = pl.split_tokens;
+    pa_.max_splits = pl.max_splits;
+    pa_.window = params->local_window_size;
+    pa_.row_width = params->num_heads * D;
+    StageScope scope(PA_STAGE_PLAN, s);
+    if ((st = device_status(pa::launch_plan(pa_, s), "plan kernel launch")) != PA_OK) return st;
+  }
+  hipStream_t ps = s;
+  SideStream* side = nullptr;
+  if (overlap) {
+    if ((st = side_stream(s, &side)) != PA_OK) return st;
+    hipError_t e = hipEventRecord(side->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->st, side->fork, 0);
+    if (e != hipSuccess) return fail(PA_ERR_DEVICE, "stream fork: %s", hipGetErrorString(e));
+    ps = side->st;
+  }
+  // the join is queued whatever happens after the fork, so the caller's
+  // stream never runs ahead of work queued on the side stream
+  auto joined = [&](pa_status r) {
+    if (!side) return r;
+    hipError_t e = hipEventRecord(side->join, side->st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+    side = nullptr;
+    if (e != hipSuccess && r == PA_OK)
+      return fail(PA_ERR_DEVICE, "stream join: %s", hipGetErrorString(e));
+    return r;
+  };
   if (pl.prefill) {
     pa::PrefillArgs f;
     f.s = sl;
@@ -461,38 +534,26 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     f.use_softcap = d.use_softcap;
     const dim3 grid(pl.prefill_tiles * pl.prefill_chunks + 1, params->kv_num_heads);
     {
-      StageScope scope(PA_STAGE_PREFILL, s);
-      if ((st = device_status(pa::launch_prefill(f, D, grid, s), "prefill kernel launch")) != PA_OK)
-        return st;
+      StageScope scope(PA_STAGE_PREFILL, ps);
+      if ((st = device_status(pa::launch_prefill(f, D, grid, ps), "prefill kernel launch")) != PA_OK)
+        return joined(st);
     }
     if (pl.prefill_chunks > 1) {
-      StageScope scope(PA_STAGE_PREFILL_MERGE, s);
-      if ((st = device_status(pa::launch_prefill_merge(f, D, s), "prefill merge launch")) != PA_OK)
-        return st;
+      StageScope scope(PA_STAGE_PREFILL_MERGE, ps);
+      if ((st = device_status(pa::launch_prefill_merge(f, D, ps), "prefill merge launch")) != PA_OK)
+        return joined(st);
     }
-  }
-  if (pl.listed) {
-    pa::PlanArgs pa_;
-    pa_.s = sl;
-    pa_.entries = reinterpret_cast<pa::DecodeEntry*>(ws + pl.off_entries);
-    pa_.entry_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
-    pa_.out = d.out;
-    pa_.rows = pl.rows;
-    pa_.token_mode = d.token_mode;
-    pa_.split_tokens = pl.split_tokens;
-    pa_.max_splits = pl.max_splits;
-    pa_.window = params->local_window_size;
-    pa_.row_width = params->num_heads * D;
-    StageScope scope(PA_STAGE_PLAN, s);
-    if ((st = device_status(pa::launch_plan(pa_, s), "plan kernel launch")) != PA_OK) return st;
   }
   if (pl.rows > 0) {
     const int64_t hc = (int64_t)params->kv_num_heads * pl.head_chunks;
     int64_t wgs;
     if (pl.listed) {
       const int64_t bound = (int64_t)pl.rows * pl.max_splits * hc;
-      const int64_t resident =
-          (int64_t)pa::decode_workgroups_per_cu(D, d.use_softcap != 0) * device_cus();
+      // beside a prefill, one decode workgroup per CU is left out so the
+      // prefill tiles and the decode workers are resident together whichever
+      // kernel is dispatched first
+      const int per_cu = pa::decode_workgroups_per_cu(D, d.use_softcap != 0);
+      const int64_t resident = (int64_t)std::max(1, overlap ? per_cu - 1 : per_cu) * device_cus();
       wgs = std::min<int64_t>((bound + pa::kDecodeWaves - 1) / pa::kDecodeWaves, resident);
     } else {
       wgs = ((int64_t)pl.rows * hc + pa::kDecodeWaves - 1) / pa::kDecodeWaves;
@@ -501,7 +562,7 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
       StageScope scope(PA_STAGE_DECODE, s);
       if ((st = device_status(pa::launch_decode(d, D, (int)std::max<int64_t>(wgs, 1), s),
                               "decode kernel launch")) != PA_OK)
-        return st;
+        return joined(st);
     }
     if (pl.listed) {
       pa::MergeArgs mg;
@@ -518,10 +579,10 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
       mg.window = params->local_window_size;
       StageScope scope(PA_STAGE_MERGE, s);
       if ((st = device_status(pa::launch_merge(mg, s), "merge kernel launch")) != PA_OK)
-        return st;
+        return joined(st);
     }
   }
-  return PA_OK;
+  return joined(PA_OK);
 }
 
 pa_status pa_timing_enable(int32_t max_launches) {
