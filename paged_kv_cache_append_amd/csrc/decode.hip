@@ -14,17 +14,15 @@
 // keys the wave computes, on the matrix cores,
 //   S^T[key][head] = K[key][:] . Q[head][:]   (v_mfma_f32_16x16x32_f16)
 //   O^T[d][head]  += V^T[d][key] . P^T[key][head]
-// K goes straight from global memory (coalesced 64-byte runs of each key row)
-// into the A operand; V tiles are loaded coalesced (whole rows), transposed in
-// registers four keys at a time and staged in the wave's own LDS region, from
-// which the PV operand is read with 16-byte loads.  The score accumulator
-// already has the B-operand layout of the PV product (keys ordered to match),
-// so probabilities never leave registers.  A head's running max is shared by
-// the four lanes that hold it with two cross-lane swaps per tile; the lane
-// holding an output column also holds that head's max, so rescaling is local.
-// Scores are in log2 units (scale * log2 e folded in).  Each register set is
-// refilled with the next tile's K (resp. V) as soon as the MFMA (resp. the LDS
-// store) has consumed it, so loads stay in flight during the rest of the tile.
+// K and V load as whole key rows (1 KB per instruction), one tile ahead in
+// registers, and are stored into the wave's own LDS tiles; the K operand is
+// read back with 16-byte reads and the V^T operand with transposing reads.
+// The score accumulator already has the B-operand layout of the PV product
+// (keys ordered to match), so probabilities never leave registers.  A head's
+// running max is shared by the four lanes that hold it with two cross-lane
+// swaps per tile; the lane holding an output column also holds that head's
+// max, so rescaling is local.  Scores are in log2 units (scale * log2 e
+// folded in).
 #include "pa_device.h"
 
 namespace pa {

@@ -18,14 +18,17 @@
 //   O^T[d][row] += V^T[d][key] . P^T[key][row]
 // and the probabilities go from registers to the MFMA without an LDS round
 // trip.  K and V tiles of 64 keys move from the pool straight into LDS with
-// direct loads (no staging registers), double buffered: the next tile streams
-// in while the current one is multiplied, and one barrier per tile suffices.
-// V keeps its natural row layout in LDS; the V^T operand comes from
-// transposing LDS reads.  Operand reads are issued a few MFMAs ahead of their
-// use.  The block-table slice of the workgroup's key range is staged in LDS.
-// Scores are in log2 units; the running max is shared by the two lanes of a
-// row with one lane swap per tile and is only raised when a tile exceeds it by
-// more than 8 (lazy rescale).
+// direct loads (no staging registers), two buffers each; V keeps its natural
+// row layout and the V^T operand comes from transposing LDS reads.  The tile
+// loop is software-pipelined with K one tile ahead of V: while the QK
+// product of the next tile runs on the matrix cores, the vector ALU computes
+// the current tile's probabilities and issues the next loads, and while the
+// PV product of the current tile runs, it finishes the probabilities and
+// takes the next tile's row maximum.  One barrier per tile.  The block-table
+// slice of the workgroup's key range is staged in LDS.  Scores are in log2
+// units; the running max is shared by the two lanes of a row with one lane
+// swap per tile and is only raised when a tile exceeds it by more than 8
+// (lazy rescale).
 #include <type_traits>
 
 #include "pa_device.h"
