@@ -68,6 +68,11 @@ typedef struct {
   int32_t prefill_pieces;     /* 0 = auto; else 1..4: workgroups sharing one prefill
                                  tile's key range, merged on the device (testing
                                  hook; rounding may differ)                            */
+  int32_t prefill_kernel;     /* 0 = auto; 1 = 4-wave prefill kernel (32 query rows
+                                 per wave); 2 = 8-wave kernel (16 rows per wave),
+                                 head_size 256 with each cache smaller than 4 GiB,
+                                 else PA_ERR_UNSUPPORTED.  Auto takes 2 where it
+                                 applies.  Testing hook; rounding may differ.          */
 } pa_attn_params;
 
 /* The paged cache and the per-step request layout.  Host struct holding

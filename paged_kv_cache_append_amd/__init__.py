@@ -43,13 +43,14 @@ class Attn:
     path: int = 0
     split_tokens: int = 0
     prefill_pieces: int = 0
+    prefill_kernel: int = 0
 
     def c(self) -> _lib.AttnParams:
         return _lib.AttnParams(self.num_heads, self.kv_num_heads, self.head_size,
                                self.block_size, float(self.scale), float(self.softcap),
                                self.local_window_size, self.do_rotary,
                                self.rotary_interleaved, self.path, self.split_tokens,
-                               self.prefill_pieces)
+                               self.prefill_pieces, self.prefill_kernel)
 
 
 def library_path() -> str:

@@ -24,7 +24,8 @@ class AttnParams(ctypes.Structure):
                 ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
                 ("local_window_size", ctypes.c_int32), ("do_rotary", ctypes.c_int32),
                 ("rotary_interleaved", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("split_tokens", ctypes.c_int32), ("prefill_pieces", ctypes.c_int32)]
+                ("split_tokens", ctypes.c_int32), ("prefill_pieces", ctypes.c_int32),
+                ("prefill_kernel", ctypes.c_int32)]
 
 
 class PagedKV(ctypes.Structure):

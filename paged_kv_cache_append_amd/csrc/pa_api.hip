@@ -108,6 +108,9 @@ pa_status check_common(const pa_attn_params* p, const pa_paged_kv* kv) {
   if (p->prefill_pieces < 0 || p->prefill_pieces > pa::kPrefillChunks)
     return fail(PA_ERR_INVALID_ARGUMENT, "prefill_pieces: expected 0..%d, got %d",
                 pa::kPrefillChunks, p->prefill_pieces);
+  if (p->prefill_kernel < 0 || p->prefill_kernel > 2)
+    return fail(PA_ERR_INVALID_ARGUMENT, "prefill_kernel: expected 0, 1 or 2, got %d",
+                p->prefill_kernel);
   if (p->split_tokens < 0 || p->split_tokens % 64 != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "split_tokens: expected 0 or a multiple of 64, got %d",
                 p->split_tokens);
@@ -163,10 +166,21 @@ pa_status check_rotary(const pa_attn_params* p, const pa_paged_kv* kv, const voi
   return PA_OK;
 }
 
-pa_status check_kernel_support(const pa_attn_params* p) {
+// The 8-wave prefill kernel (head_size 256) addresses a cache with 32-bit
+// byte offsets.
+bool rows16_prefill_fits(const pa_attn_params* p, const pa_paged_kv* kv) {
+  return p->head_size == 256 &&
+         kv->num_blocks * p->block_size * p->kv_num_heads * p->head_size * 2 <
+             ((int64_t)1 << 32) - 16;
+}
+
+pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv) {
   if (p->head_size != 64 && p->head_size != 128 && p->head_size != 256)
     return fail(PA_ERR_UNSUPPORTED,
                 "head_size %d: the kernels serve head_size 64, 128 and 256", p->head_size);
+  if (p->prefill_kernel == 2 && !rows16_prefill_fits(p, kv))
+    return fail(PA_ERR_UNSUPPORTED,
+                "prefill_kernel 2: expected head_size 256 and caches smaller than 4 GiB");
   return PA_OK;
 }
 
@@ -418,7 +432,7 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
   if (mq < 0 || mk < 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "max_query_len_bound/max_kv_len_bound: expected >= 0");
   if (kv->token_count == 0) return PA_OK;
-  if ((st = check_kernel_support(params)) != PA_OK) return st;
+  if ((st = check_kernel_support(params, kv)) != PA_OK) return st;
   if (!query) return fail(PA_ERR_INVALID_ARGUMENT, "query: expected non-NULL");
   if (!out) return fail(PA_ERR_INVALID_ARGUMENT, "out: expected non-NULL");
   if (!aligned16(query) || !aligned16(out))
@@ -532,6 +546,8 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     f.cap_in2 = 2.0f * log2e * d.cap_in;
     f.cap_out = d.cap_out;
     f.use_softcap = d.use_softcap;
+    f.rows16 = params->prefill_kernel == 2 ||
+               (params->prefill_kernel == 0 && rows16_prefill_fits(params, kv));
     const dim3 grid(pl.prefill_tiles * pl.prefill_chunks + 1, params->kv_num_heads);
     {
       StageScope scope(PA_STAGE_PREFILL, ps);

@@ -141,6 +141,7 @@ struct PrefillArgs {
   float cap_in2;                // 2 * log2(e) * scale / softcap  (tanh via exp2)
   float cap_out;                // softcap * log2(e)
   int32_t use_softcap;
+  int32_t rows16;               // head_size 256: the 8-wave kernel (16 rows per wave)
 };
 
 // Kernel start/stop events of the launch being made on this thread (set by
@@ -171,6 +172,8 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 int decode_workgroups_per_cu(int head_size, bool softcap);   // resident decode workgroups per CU
 hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st);
 hipError_t launch_prefill_merge(const PrefillArgs& a, int head_size, hipStream_t st);
+// 8-wave prefill kernel of 16 rows per wave (head_size 256); grid as launch_prefill
+hipError_t launch_prefill16(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st);
 
 constexpr int kPrefillRows = 128;   // query rows (token x head) per prefill workgroup
 constexpr int kDecodeWaves = 4;     // independent decode workers per workgroup

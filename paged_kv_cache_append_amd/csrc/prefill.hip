@@ -31,16 +31,11 @@
 // (lazy rescale).
 #include <type_traits>
 
-#include "pa_device.h"
+#include "prefill_common.h"
 
 namespace pa {
 
 namespace {
-
-constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kRescaleSlack = 8.0f;   // log2 units
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef float f4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct PrefillCfg {
@@ -60,114 +55,6 @@ struct PrefillCfg {
   static constexpr int SEGT = 512;           // block-table entries staged per segment
   static constexpr int PIPE = KS < 2 ? KS : 2;   // operand reads in flight (k-steps)
 };
-
-// Tile layout in LDS: key row r (0..63) of the tile lives in slot
-// (r / 32) * NS + (r % NS) at row position ((r % 32) / NS) within the slot;
-// a slot is one contiguous 1 KB direct load plus padding, and every operand
-// address is a base register plus an immediate offset.
-template <int D>
-__device__ __forceinline__ int row_byte(int r, int slot_bytes) {
-  using C = PrefillCfg<D>;
-  return ((r >> 5) * C::NS + (r % C::NS)) * slot_bytes + ((r & 31) / C::NS) * (2 * D);
-}
-
-// Source of the rows that must read as zero (never written).
-__device__ __attribute__((aligned(16))) uint16_t g_zero_row[256];
-
-__device__ __forceinline__ void dma16(const uint16_t* src, char* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-
-// vmcnt(0), no wait on the LDS/scalar counter
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Scheduling order of a block of N MFMAs fed by RPM LDS reads each: the
-// reads of the first AHEAD MFMAs, then one MFMA per further group of reads,
-// then the remaining MFMAs, so every operand is requested AHEAD MFMA issue
-// slots before its use.  The compiler otherwise pulls each read down next to
-// its MFMA to save registers.
-template <int AHEAD, int N, int RPM>
-__device__ __forceinline__ void pipeline_order() {
-  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * RPM, 0);   // DS reads
-#pragma unroll
-  for (int i = 0; i < N - AHEAD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);         // DS reads
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
-}
-
-// Tile slot -> (request b, tile) over requests with q_len >= 2, tiles of
-// kPrefillRows rows (token x head-in-group) each; later (longer) tiles of a
-// request come first.  b = -1 past the last tile.  Called by a whole wave;
-// the results are the same in every lane.
-__device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, int lane, int& fb,
-                                          int& ft) {
-  int base = 0;
-  fb = -1;
-  ft = 0;
-  for (int b0 = 0; b0 < sl.batch; b0 += 64) {
-    const int bb = b0 + lane;
-    int nt = 0;
-    if (bb < sl.batch) {
-      const int ql = sl.cum[bb + 1] - sl.cum[bb];
-      if (ql >= 2) nt = (ql * g + kPrefillRows - 1) / kPrefillRows;
-    }
-    int incl = nt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    const int total = __shfl(incl, 63, 64);
-    if (slot < base + total) {
-      const bool mine = nt > 0 && slot >= base + incl - nt && slot < base + incl;
-      const unsigned long long bal = __ballot(mine);
-      const int src = __builtin_ctzll(bal);
-      fb = b0 + src;
-      const int fn = __shfl(nt, src, 64);
-      ft = fn - 1 - (slot - (base + __shfl(incl - nt, src, 64)));
-      return;
-    }
-    base += total;
-  }
-}
-
-// Key range [lo, hi) that tile `tile` of a request (q_len, past) needs, and
-// how it is cut into pieces of whole 64-key tiles for `chunks` workgroups.
-struct TileKeys {
-  int lo, hi;              // admitted keys of any row of the tile
-  int all_begin, all_tiles;
-  int per_piece, pieces;
-};
-__device__ __forceinline__ TileKeys tile_keys(int tile, int q_len, int past, int g, int window,
-                                              int cap, int chunks, int piece_tiles) {
-  TileKeys k;
-  const int j_first = (tile * kPrefillRows) / g;
-  const int j_last = min(q_len - 1, (tile * kPrefillRows + kPrefillRows - 1) / g);
-  k.hi = min(past + j_last + 1, cap);
-  k.lo = window > 0 ? max(0, past + j_first + 1 - window) : 0;
-  k.all_begin = k.lo & ~63;
-  k.all_tiles = k.hi > k.all_begin ? (k.hi - k.all_begin + 63) / 64 : 0;
-  // piece_tiles > 0: pieces of about piece_tiles key tiles (short tiles stay
-  // whole), at most `chunks`; else `chunks` equal pieces
-  const int want = piece_tiles > 0 ? (k.all_tiles + piece_tiles - 1) / piece_tiles : chunks;
-  const int n = max(1, min(chunks, want));
-  k.per_piece = (k.all_tiles + n - 1) / n;
-  k.pieces = k.per_piece > 0 ? (k.all_tiles + k.per_piece - 1) / k.per_piece : 1;
-  return k;
-}
-
-// max / sum of a value with the one 32 lanes away (one lane-swap instruction)
-__device__ __forceinline__ float xor32_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
@@ -778,7 +665,10 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStr
   switch (head_size) {
     case 64: launch_variant<64>(a, grid, st); break;
     case 128: launch_variant<128>(a, grid, st); break;
-    case 256: launch_variant<256>(a, grid, st); break;
+    case 256:
+      if (a.rows16) return launch_prefill16(a, head_size, grid, st);
+      launch_variant<256>(a, grid, st);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

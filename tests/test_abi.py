@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function():
 def params(**kw):
     d = dict(num_heads=8, kv_num_heads=2, head_size=64, block_size=16, scale=0.0, softcap=0.0,
              local_window_size=-1, do_rotary=0, rotary_interleaved=0, path=0, split_tokens=0,
-             prefill_pieces=0)
+             prefill_pieces=0, prefill_kernel=0)
     d.update(kw)
     return _lib.AttnParams(*[d[f] for f, _ in _lib.AttnParams._fields_])
 
@@ -89,6 +89,8 @@ NEGATIVE = [
     (dict(split_tokens=100), {}, 1, "split_tokens"),
     (dict(prefill_pieces=5), {}, 1, "prefill_pieces"),
     (dict(prefill_pieces=-1), {}, 1, "prefill_pieces"),
+    (dict(prefill_kernel=3), {}, 1, "prefill_kernel"),
+    (dict(prefill_kernel=-1), {}, 1, "prefill_kernel"),
     ({}, dict(batch_size=0), 1, "batch_size"),
     ({}, dict(token_count=-1), 1, "token_count"),
     ({}, dict(num_blocks=0), 1, "num_blocks"),
@@ -134,6 +136,14 @@ def test_forward_buffer_rules():
 def test_unsupported_head_size_is_reported():
     assert call_forward(params(head_size=96), paged()) == 2
     assert "head_size 96" in err()
+
+
+def test_rows16_prefill_kernel_limits():
+    # the 8-wave prefill kernel serves head_size 256 with caches below 4 GiB
+    assert call_forward(params(prefill_kernel=2), paged()) == 2 and "prefill_kernel 2" in err()
+    big = paged(num_blocks=(1 << 32) // (16 * 2 * 256 * 2))   # exactly 4 GiB per cache
+    assert call_forward(params(head_size=256, prefill_kernel=2), big) == 2
+    assert "4 GiB" in err()
 
 
 def test_workspace_must_cover_the_plan():

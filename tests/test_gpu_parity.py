@@ -146,3 +146,30 @@ def test_batch_order_permutation():
     w2.query, w2.key, w2.value = w.query[rows], w.key[rows], w.value[rows]
     _, out2 = gpu_step(w2, path=2)
     assert np.max(np.abs(out2.astype(np.float64) - out[rows])) <= 1e-3
+
+
+WIDE_CASES = [
+    # q_lens, past, H, Hkv, D = 256, bs, extra kwargs: both prefill kernels of
+    # the 256-channel head (4 waves x 32 rows, 8 waves x 16 rows)
+    ([130, 1, 3], [300, 1000, 64], 6, 2, 256, 16, dict(local_window_size=200, softcap=5.0)),
+    ([64, 1], [4000, 7000], 16, 8, 256, 16, dict(local_window_size=4096, softcap=50.0)),
+    ([257, 2, 40], [0, 129, 3000], 8, 4, 256, 32, {}),
+    ([70, 5], [16, 200], 4, 1, 256, 64, dict(do_rotary=1, rotary_dim=128, local_window_size=33)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WIDE_CASES)))
+@pytest.mark.parametrize("kernel", [1, 2])
+def test_wide_head_prefill_kernels(case, kernel):
+    q_lens, past, H, Hkv, D, bs, kw = WIDE_CASES[case]
+    w = wl.build_case(f"wide{case}", 700 + case, q_lens=q_lens, past=past, num_heads=H,
+                      kv_num_heads=Hkv, head_size=D, block_size=bs, **kw)
+    check(w, 2, prefill_kernel=kernel)
+
+
+@pytest.mark.parametrize("kernel", [1, 2])
+def test_wide_head_prefill_kernels_with_pieces(kernel):
+    q_lens, past, H, Hkv, D, bs, kw = PIECE_CASES[1]
+    w = wl.build_case("pieces1", 601, q_lens=q_lens, past=past, num_heads=H,
+                      kv_num_heads=Hkv, head_size=D, block_size=bs, **kw)
+    check(w, 2, prefill_kernel=kernel, prefill_pieces=3)
