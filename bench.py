@@ -82,7 +82,8 @@ def traffic_from_profiles(kernel_tag: str, src_hash: str):
 
 KERNEL_SOURCES = {
     "decode": ("decode.hip", "pa_api.hip", "pa_device.h", "pa_internal.h"),
-    "prefill": ("prefill.hip", "pa_api.hip", "pa_device.h", "pa_internal.h"),
+    "prefill": ("prefill.hip", "prefill16.hip", "prefill_common.h", "pa_api.hip", "pa_device.h",
+                "pa_internal.h"),
 }
 
 

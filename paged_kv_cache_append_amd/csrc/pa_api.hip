@@ -166,12 +166,15 @@ pa_status check_rotary(const pa_attn_params* p, const pa_paged_kv* kv, const voi
   return PA_OK;
 }
 
-// The 8-wave prefill kernel (head_size 256) addresses a cache with 32-bit
-// byte offsets.
+// Each cache is small enough for 32-bit byte offsets (buffer addressing).
+bool pool_fits_32bit(const pa_attn_params* p, const pa_paged_kv* kv) {
+  return kv->num_blocks * p->block_size * p->kv_num_heads * p->head_size * 2 <
+         ((int64_t)1 << 32) - 16;
+}
+// The 8-wave prefill kernel serves head_size 256 and addresses the caches
+// with 32-bit byte offsets.
 bool rows16_prefill_fits(const pa_attn_params* p, const pa_paged_kv* kv) {
-  return p->head_size == 256 &&
-         kv->num_blocks * p->block_size * p->kv_num_heads * p->head_size * 2 <
-             ((int64_t)1 << 32) - 16;
+  return p->head_size == 256 && pool_fits_32bit(p, kv);
 }
 
 pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv) {
@@ -548,6 +551,7 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     f.use_softcap = d.use_softcap;
     f.rows16 = params->prefill_kernel == 2 ||
                (params->prefill_kernel == 0 && rows16_prefill_fits(params, kv));
+    f.pool32 = pool_fits_32bit(params, kv) ? 1 : 0;
     const dim3 grid(pl.prefill_tiles * pl.prefill_chunks + 1, params->kv_num_heads);
     {
       StageScope scope(PA_STAGE_PREFILL, ps);

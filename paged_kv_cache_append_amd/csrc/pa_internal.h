@@ -142,6 +142,7 @@ struct PrefillArgs {
   float cap_out;                // softcap * log2(e)
   int32_t use_softcap;
   int32_t rows16;               // head_size 256: the 8-wave kernel (16 rows per wave)
+  int32_t pool32;               // each cache is smaller than 4 GiB (32-bit byte offsets)
 };
 
 // Kernel start/stop events of the launch being made on this thread (set by

@@ -56,7 +56,11 @@ struct PrefillCfg {
   static constexpr int PIPE = KS < 2 ? KS : 2;   // operand reads in flight (k-steps)
 };
 
-template <int D, bool SOFTCAP>
+// BUF: the tiles move by buffer loads with an LDS destination and 32-bit byte
+// offsets (each cache smaller than 4 GiB), otherwise by global loads with an
+// LDS destination.  The buffer form leaves the compiler free to wait on
+// individual LDS operand reads; with the global form it waits on all of them.
+template <int D, bool SOFTCAP, bool BUF>
 __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   using C = PrefillCfg<D>;
   __shared__ __attribute__((aligned(1024))) char K0[C::SLOTS * C::KSLOT];
@@ -74,11 +78,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   __builtin_assume(wave >= 0 && wave < 4);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
-  const int kvh = blockIdx.y;
+  const LogicalBlock lb = logical_block();   // XCD-aware order
+  const int kvh = lb.y;
   const int g = a.group;
   const int64_t HD = (int64_t)a.num_heads * D;
 
-  if ((int)blockIdx.x == a.tiles * a.chunks) {
+  if (lb.x == a.tiles * a.chunks) {
     // tokens owned by no request get zero rows (this kv head's columns)
     const int t0 = max(sl.cum[sl.batch], 0);
     const int width = g * C::CH;
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   // Map this workgroup to (request, tile) over requests with q_len >= 2.
   if (wave == 0) {
     int fb, ft;
-    find_tile(sl, g, blockIdx.x / a.chunks, lane, fb, ft);
+    find_tile(sl, g, lb.x / a.chunks, lane, fb, ft);
     if (lane == 0) {
       sh_b = fb;
       sh_tile = ft;
@@ -115,6 +120,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const uint32_t tok_stride32 = (uint32_t)tok_stride;   // Hkv * D < 2^24
   const uint16_t* kbase = a.key_cache + (int64_t)kvh * D;
   const uint16_t* vbase = a.value_cache + (int64_t)kvh * D;
+  // buffers over this kv head's part of each pool (bytes from kbase / vbase on)
+  const int64_t pool_bytes = ((sl.num_blocks << shift) * a.kv_heads * D - (int64_t)kvh * D) * 2;
+  const int nrec = (int)(uint32_t)min(pool_bytes, (int64_t)0xFFFFFFFF);
+  const __amdgpu_buffer_rsrc_t ksrd =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vsrd =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nrec, 0x00020000);
 
   // this lane's query row
   const int R = tile * C::ROWS + wave * 32 + l32;
@@ -127,7 +139,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 
   // key range of the whole tile, and of this wave's rows (fast path)
   const TileKeys tk = tile_keys(tile, q_len, past, g, a.window, cap, a.chunks, a.piece_tiles);
-  const int piece = blockIdx.x - (blockIdx.x / a.chunks) * a.chunks;
+  const int piece = lb.x - (lb.x / a.chunks) * a.chunks;
   const int pieces = tk.pieces;
   if (piece >= pieces) return;
   const int hi = tk.hi;
@@ -231,11 +243,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const uint16_t* zrow = g_zero_row + 8 * chunk;
   auto issue_row = [&](uint32_t row, const uint16_t* base, char* buf, int slot_bytes, int mi) {
     const int slot = wave + 4 * mi;
-    // one source pointer, base + a selected element offset (a select between
-    // two pointers makes the compiler split the load in two exec-masked halves)
-    const int64_t off =
-        row != ~0u ? (int64_t)((uint64_t)row * tok_stride32 + 8 * chunk) : zrow - base;
-    dma16(base + off, buf + slot * slot_bytes);
+    if constexpr (BUF) {
+      // a zero row: an offset past the buffer's end reads zeros
+      const uint32_t off = row != ~0u ? (row * tok_stride32 + 8 * chunk) * 2 : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          base == vbase ? vsrd : ksrd,
+          (__attribute__((address_space(3))) void*)(buf + slot * slot_bytes), 16, off, 0, 0, 0);
+    } else {
+      // one source pointer, base + a selected element offset (a select between
+      // two pointers makes the compiler split the load in two exec-masked halves)
+      const int64_t off =
+          row != ~0u ? (int64_t)((uint64_t)row * tok_stride32 + 8 * chunk) : zrow - base;
+      dma16(base + off, buf + slot * slot_bytes);
+    }
   };
   auto issue_one = [&](int tau, int blk, const uint16_t* base, char* buf, int slot_bytes,
                        int mi) {
@@ -640,12 +660,19 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a)
   }
 }
 
-template <int D>
+template <int D, bool BUF>
 void launch_variant(const PrefillArgs& a, dim3 grid, hipStream_t st) {
   if (a.use_softcap)
-    launch_kernel(prefill_kernel<D, true>, grid, dim3(256), st, a);
+    launch_kernel(prefill_kernel<D, true, BUF>, grid, dim3(256), st, a);
   else
-    launch_kernel(prefill_kernel<D, false>, grid, dim3(256), st, a);
+    launch_kernel(prefill_kernel<D, false, BUF>, grid, dim3(256), st, a);
+}
+template <int D>
+void launch_variant(const PrefillArgs& a, dim3 grid, hipStream_t st) {
+  if (a.pool32)
+    launch_variant<D, true>(a, grid, st);
+  else
+    launch_variant<D, false>(a, grid, st);
 }
 
 }  // namespace
@@ -667,7 +694,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStr
     case 128: launch_variant<128>(a, grid, st); break;
     case 256:
       if (a.rows16) return launch_prefill16(a, head_size, grid, st);
-      launch_variant<256>(a, grid, st);
+      launch_variant<256, false>(a, grid, st);
       break;
     default: return hipErrorInvalidValue;
   }

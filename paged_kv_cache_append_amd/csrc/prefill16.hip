@@ -116,11 +116,12 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
   __builtin_assume(wave >= 0 && wave < C::WAVES);
   const int l16 = lane & 15;   // the lane's row within the wave (MFMA layouts)
   const int q4 = lane >> 4;    // the lane's 16-lane group
-  const int kvh = blockIdx.y;
+  const LogicalBlock lb = logical_block();   // XCD-aware order
+  const int kvh = lb.y;
   const int g = a.group;
   const int64_t HD = (int64_t)a.num_heads * D;
 
-  if ((int)blockIdx.x == a.tiles * a.chunks) {
+  if (lb.x == a.tiles * a.chunks) {
     // tokens owned by no request get zero rows (this kv head's columns)
     const int t0 = max(sl.cum[sl.batch], 0);
     const int width = g * (D / 8);
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
 
   if (wave == 0) {
     int fb, ft;
-    find_tile(sl, g, blockIdx.x / a.chunks, lane, fb, ft);
+    find_tile(sl, g, lb.x / a.chunks, lane, fb, ft);
     if (lane == 0) {
       sh_b = fb;
       sh_tile = ft;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
   const int head = kvh * g + hh;
 
   const TileKeys tk = tile_keys(tile, q_len, past, g, a.window, cap, a.chunks, a.piece_tiles);
-  const int piece = blockIdx.x - (blockIdx.x / a.chunks) * a.chunks;
+  const int piece = lb.x - (lb.x / a.chunks) * a.chunks;
   const int pieces = tk.pieces;
   if (piece >= pieces) return;
   const int hi = tk.hi;

@@ -23,6 +23,27 @@ __device__ __forceinline__ int row_byte(int r, int slot_bytes) {
   return ((r >> 5) * NS + (r % NS)) * slot_bytes + ((r & 31) / NS) * (2 * D);
 }
 
+// Workgroup placement: the hardware deals consecutive linear workgroup ids to
+// the chip's 8 XCDs in turn, each XCD with its own L2.  This maps the linear
+// id of a workgroup to a logical id such that the workgroups placed on one XCD
+// take one contiguous range of logical ids (a bijection for any total), so
+// tiles that read the same K/V tiles share that XCD's L2.
+__device__ __forceinline__ int xcd_logical_id(int linear, int total) {
+  constexpr int kXcds = 8;
+  const int q = total / kXcds, r = total % kXcds;
+  const int xcd = linear % kXcds, k = linear / kXcds;
+  return xcd * q + min(xcd, r) + k;
+}
+// (x, y) of this workgroup in the logical order
+struct LogicalBlock {
+  int x, y;
+};
+__device__ __forceinline__ LogicalBlock logical_block() {
+  const int linear = blockIdx.x + blockIdx.y * gridDim.x;
+  const int l = xcd_logical_id(linear, gridDim.x * gridDim.y);
+  return LogicalBlock{l % (int)gridDim.x, l / (int)gridDim.x};
+}
+
 // Source of the rows that must read as zero (never written).
 __device__ __attribute__((aligned(16))) uint16_t g_zero_row[256];
 
