@@ -487,23 +487,9 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
   d.cap_out = cap ? params->softcap * log2e : 0.f;
   d.use_softcap = cap ? 1 : 0;
 
-  // prefill first, on the side stream when decode rows run beside it
+  // prefill first, on the side stream when decode rows run beside it; the
+  // side stream forks before the plan kernel, which only the decode needs
   const bool overlap = pl.prefill && pl.rows > 0;
-  if (pl.listed) {
-    pa::PlanArgs pa_;
-    pa_.s = sl;
-    pa_.entries = reinterpret_cast<pa::DecodeEntry*>(ws + pl.off_entries);
-    pa_.entry_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
-    pa_.out = d.out;
-    pa_.rows = pl.rows;
-    pa_.token_mode = d.token_mode;
-    pa_.split_tokens = pl.split_tokens;
-    pa_.max_splits = pl.max_splits;
-    pa_.window = params->local_window_size;
-    pa_.row_width = params->num_heads * D;
-    StageScope scope(PA_STAGE_PLAN, s);
-    if ((st = device_status(pa::launch_plan(pa_, s), "plan kernel launch")) != PA_OK) return st;
-  }
   hipStream_t ps = s;
   SideStream* side = nullptr;
   if (overlap) {
@@ -524,6 +510,22 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
       return fail(PA_ERR_DEVICE, "stream join: %s", hipGetErrorString(e));
     return r;
   };
+  if (pl.listed) {
+    pa::PlanArgs pa_;
+    pa_.s = sl;
+    pa_.entries = reinterpret_cast<pa::DecodeEntry*>(ws + pl.off_entries);
+    pa_.entry_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
+    pa_.out = d.out;
+    pa_.rows = pl.rows;
+    pa_.token_mode = d.token_mode;
+    pa_.split_tokens = pl.split_tokens;
+    pa_.max_splits = pl.max_splits;
+    pa_.window = params->local_window_size;
+    pa_.row_width = params->num_heads * D;
+    StageScope scope(PA_STAGE_PLAN, s);
+    if ((st = device_status(pa::launch_plan(pa_, s), "plan kernel launch")) != PA_OK)
+      return joined(st);
+  }
   if (pl.prefill) {
     pa::PrefillArgs f;
     f.s = sl;
