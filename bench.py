@@ -327,6 +327,20 @@ def main():
               for s in ("append", "decode", "merge", "prefill", "prefill_merge", "plan")}
     pa.timing_disable()
 
+    # the append alone, with derived slots (from the steps above) and with an
+    # explicit slot mapping (distinct slots scattered over the pool, as a
+    # scheduler that owns placement hands them out): same bytes moved.  Runs
+    # after the timed steps; the output checked below is the last step's.
+    sm = torch.from_numpy(wl.random_slot_mapping(w, 4242)).to("cuda")
+    pa.timing_enable(args.steps + 16)
+    for _ in range(args.steps):
+        pa.append_kv(a, dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
+                     dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"],
+                     slot_mapping=sm)
+    torch.cuda.synchronize()
+    slots_ms, slots_n = pa.timing_read("append")
+    pa.timing_disable()
+
     dec_bytes, pf_flops, n_dec = algorithmic_work(w)
     per = {s: (ms / n * 1e3 if n else 0.0) for s, (ms, n) in stages.items()}   # us per launch
     if dec_bytes:
@@ -334,6 +348,14 @@ def main():
     else:
         value, unit = pf_flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
     kernels = {f"{s}_us": round(v, 3) for s, v in per.items()}
+    app_bytes = 2 * 2 * T * w.kv_num_heads * w.head_size * 2   # K and V, read + written
+    append = {"algorithmic_bytes_per_launch": app_bytes,
+              "derived_slots_us": round(per["append"], 3),
+              "derived_slots_gbs": round(app_bytes / (per["append"] * 1e-6) / 1e9, 1)
+              if per["append"] else None,
+              "slot_mapping_us": round(slots_ms / slots_n * 1e3, 3) if slots_n else None,
+              "slot_mapping_gbs": round(app_bytes / (slots_ms / slots_n * 1e-3) / 1e9, 1)
+              if slots_n else None}
     if per["decode"]:
         kernels["decode_kernel_gbs"] = round(dec_bytes / (per["decode"] * 1e-6) / 1e9, 1)
     if per["prefill"] and pf_flops:
@@ -376,6 +398,7 @@ def main():
         "roofline": roof,
         "step_roofline_frac": round(step_frac, 4),
         "kernels": kernels,
+        "append": append,
         "ms_per_step_instrumented": round(ms_step_instrumented, 5),
         "cpu_baseline": cpu,
         "parity_max_abs_err_sampled": err,

@@ -92,12 +92,16 @@ typedef struct {
   const int32_t *past_seqlens;              /* int32 [batch_size], >= 0              */
   int32_t batch_size;                       /* > 0                                   */
   int32_t token_count;                      /* T >= 0; rows of query/key/value/out   */
+  const int32_t *slot_mapping;              /* NULL, or int32 [token_count], 4-byte
+                                               aligned: the write slot of each new
+                                               token (pa_append_kv only; section 5) */
 } pa_paged_kv;
 
 /*
  * pa_append_kv -- scatter the new tokens' K/V into their pool slots
- * (PagedAttention -- CUDA Design Document, section 5.1 "derived write slot";
- * section 7.2 / 12.5 for rotary applied to K before the write).
+ * (PagedAttention -- CUDA Design Document, section 5.1 "derived write slot",
+ * section 5.2 explicit slot_mapping; section 7.2 / 12.5 for rotary applied
+ * to K before the write).
  *
  *   key, value : fp16 [token_count, kv_num_heads * head_size]
  *   cos_cache, sin_cache : fp16 [rotary_rows, rotary_dim / 2]; both non-NULL iff
@@ -110,6 +114,15 @@ typedef struct {
  * fp16(fp32(x*cos - y*sin)) of its channel pair.  Tokens t >= cum[batch_size]
  * write nothing; every other slot keeps its bytes.  Enqueue before
  * pa_forward on the same stream.
+ *
+ * With kv->slot_mapping (section 5.2) the write slot of token t is
+ * s = slot_mapping[t], the flat index block * block_size + offset: the rows
+ * go to block s / block_size, offset s % block_size, and s = -1 writes
+ * nothing (the token's query still attends; prefix-cached and rejected
+ * speculative tokens).  K is still rotated at the token's position
+ * past[b] + j.  Values outside [-1, num_blocks * block_size) are undefined
+ * by section 5.4; they write nothing here.  block_table, past and cum still
+ * define what pa_forward reads.
  */
 pa_status pa_append_kv(const pa_attn_params *params, const pa_paged_kv *kv,
                        const void *key, const void *value,

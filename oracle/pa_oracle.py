@@ -44,6 +44,13 @@ Readings where the pages are silent (each also listed in the design notes):
   self-consistency properties.
 * A query row with no admitted key (impossible with causal + W >= 1) is 0.
 * Output rows of tokens owned by no sequence are 0.
+* Explicit write slots (PagedAttention -- CUDA Design Document, §5.2): slot
+  ``s`` is block ``s // block_size``, offset ``s % block_size``; ``-1`` writes
+  nothing.  The stored K is still rotated at the token's position
+  ``past[b] + j`` (the slot only says where it goes).  Tokens owned by no
+  sequence write nothing, as on the derived path.  Values outside
+  ``[-1, num_blocks * block_size)`` are undefined by §5.4; here they write
+  nothing.
 """
 from __future__ import annotations
 
@@ -135,14 +142,26 @@ def rope_query_fp64(x: np.ndarray, pos: int, cos: np.ndarray, sin: np.ndarray,
 # PagedAttention -- CUDA Design Document §4.4 (cache outputs alias inputs).
 # ---------------------------------------------------------------------------
 
+def explicit_slot(slot_mapping: np.ndarray, t: int, block_size: int, num_blocks: int):
+    """``(physical block, offset)`` of token ``t`` from an explicit slot
+    mapping (PagedAttention -- CUDA Design Document, §5.2: the flat slot
+    ``block * block_size + offset``), or ``None`` for ``-1`` (no write) and
+    for values outside the pool."""
+    s = int(slot_mapping[t])
+    if s < 0 or s >= num_blocks * block_size:
+        return None
+    return s // block_size, s % block_size
+
+
 def append_kv(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
               value: np.ndarray, cum: np.ndarray, past: np.ndarray,
               block_table: np.ndarray, *, kv_num_heads: int, head_size: int,
               cos_cache: Optional[np.ndarray] = None, sin_cache: Optional[np.ndarray] = None,
-              rotary_interleaved: bool = False):
+              rotary_interleaved: bool = False, slot_mapping: Optional[np.ndarray] = None):
     """Return new ``(key_cache, value_cache)`` copies with every new token's
-    K (rotated if a rotary table is given) and V stored at its derived slot.
-    Slots that no token maps to are left byte-identical."""
+    K (rotated if a rotary table is given) and V stored at its derived slot,
+    or at ``slot_mapping[t]`` when a mapping is given.  Slots that no token
+    maps to are left byte-identical."""
     kc = key_cache.copy()
     vc = value_cache.copy()
     block_size = kc.shape[1]
@@ -154,7 +173,13 @@ def append_kv(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
             continue
         b, j = owner
         pos = token_position(past, b, j)
-        blk, off = derived_slot(block_table, b, pos, block_size)
+        if slot_mapping is None:
+            blk, off = derived_slot(block_table, b, pos, block_size)
+        else:
+            where = explicit_slot(slot_mapping, t, block_size, kc.shape[0])
+            if where is None:
+                continue
+            blk, off = where
         for h in range(Hkv):
             krow = key[t, h * D:(h + 1) * D]
             if cos_cache is not None:

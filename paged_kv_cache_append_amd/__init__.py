@@ -84,7 +84,8 @@ def _need(t, name, dtype, shape=None):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def _kv(key_cache, value_cache, block_table, cum, past, token_count) -> _lib.PagedKV:
+def _kv(key_cache, value_cache, block_table, cum, past, token_count,
+        slot_mapping=None) -> _lib.PagedKV:
     import torch
     _need(key_cache, "key_cache", torch.float16)
     _need(value_cache, "value_cache", torch.float16, key_cache.shape)
@@ -93,9 +94,12 @@ def _kv(key_cache, value_cache, block_table, cum, past, token_count) -> _lib.Pag
     _need(past, "past_seqlens", torch.int32, (block_table.shape[0],))
     if key_cache.dim() != 4 or block_table.dim() != 2:
         raise ValueError("key_cache must be rank 4 and block_table rank 2")
+    if slot_mapping is not None:
+        _need(slot_mapping, "slot_mapping", torch.int32, (token_count,))
     return _lib.PagedKV(key_cache.data_ptr(), value_cache.data_ptr(), key_cache.shape[0],
                         block_table.data_ptr(), block_table.shape[1], cum.data_ptr(),
-                        past.data_ptr(), block_table.shape[0], token_count)
+                        past.data_ptr(), block_table.shape[0], token_count,
+                        _ptr(slot_mapping))
 
 
 def _stream(stream) -> int:
@@ -115,16 +119,17 @@ def _rot(attn: Attn, cos_cache, sin_cache):
 
 
 def append_kv(attn: Attn, key, value, key_cache, value_cache, block_table, cum, past,
-              cos_cache=None, sin_cache=None, stream=None) -> None:
+              cos_cache=None, sin_cache=None, stream=None, slot_mapping=None) -> None:
     """``pa_append_kv``: scatter new K/V rows ``[T, Hkv*D]`` into the pools
-    (in place)."""
+    (in place); ``slot_mapping`` (int32 ``[T]``, -1 = no write) gives the
+    write slots instead of the block table."""
     import torch
     T = key.shape[0]
     _need(key, "key", torch.float16, (T, attn.kv_num_heads * attn.head_size))
     _need(value, "value", torch.float16, (T, attn.kv_num_heads * attn.head_size))
     lib = _lib.load()
     p = attn.c()
-    kv = _kv(key_cache, value_cache, block_table, cum, past, T)
+    kv = _kv(key_cache, value_cache, block_table, cum, past, T, slot_mapping)
     c, s, rows, rd = _rot(attn, cos_cache, sin_cache)
     _check(lib.pa_append_kv(ctypes.byref(p), ctypes.byref(kv), key.data_ptr(), value.data_ptr(),
                             c, s, rows, rd, _stream(stream)))

@@ -34,7 +34,7 @@ class PagedKV(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32),
                 ("cumulative_sequence_length", ctypes.c_void_p),
                 ("past_seqlens", ctypes.c_void_p), ("batch_size", ctypes.c_int32),
-                ("token_count", ctypes.c_int32)]
+                ("token_count", ctypes.c_int32), ("slot_mapping", ctypes.c_void_p)]
 
 
 _lib = None

@@ -1,7 +1,8 @@
 // KV append: scatter every new token's K/V row into its pool slot
-// (PagedAttention -- CUDA Design Document, section 5.1 "derived write slot";
-// Design: WebGPU PagedAttention, section 5 Phase 1 item 3 for the one-lane-per-
-// vector dispatch over token_count * kv_hidden).
+// (PagedAttention -- CUDA Design Document, section 5.1 "derived write slot",
+// section 5.2 explicit slot_mapping; Design: WebGPU PagedAttention, section 5
+// Phase 1 item 3 for the one-lane-per-vector dispatch over token_count *
+// kv_hidden).
 //
 // One lane moves one 16-byte chunk (8 channels) of one (token, kv head) for
 // both K and V.  Lanes of a wave cover consecutive chunks of a token row, so
@@ -9,7 +10,9 @@
 // fully coalesced reads and writes.  The owning request is found by binary
 // search over cumulative_sequence_length (same-address loads across the
 // wave, served by the cache); tokens at or past cum[B] own nothing (the
-// out-of-bounds defect of section 18.2 cannot occur).
+// out-of-bounds defect of section 18.2 cannot occur).  With an explicit slot
+// mapping the slot is read, not derived (-1: no write); the request is then
+// only looked up for the rotary position.
 #include "pa_device.h"
 
 namespace pa {
@@ -25,15 +28,29 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     const int rem = (int)(it - (int64_t)t * per_tok);
     const int kvh = rem / chunks;
     const int c = rem - kvh * chunks;
-    const int b = find_request(a.s.cum, a.s.batch, t);
-    if (b < 0) continue;
-    const int pos = a.s.past[b] + (t - a.s.cum[b]);
-    if (pos < 0) continue;
-    const int bi = pos >> a.s.block_shift;
-    if (bi >= a.s.maxblk) continue;
-    const int64_t blk = a.s.block_table[(int64_t)b * a.s.maxblk + bi];
-    if (blk < 0 || blk >= a.s.num_blocks) continue;  // unmapped: nothing to write
-    const int off = pos & (bs - 1);
+    int64_t blk;
+    int off, pos = -1;
+    if (a.slot_mapping) {
+      if (t >= a.s.cum[a.s.batch]) continue;          // owned by no request
+      const int32_t sm = a.slot_mapping[t];
+      if (sm < 0 || (int64_t)sm >= (a.s.num_blocks << a.s.block_shift)) continue;   // -1: no write
+      blk = sm >> a.s.block_shift;
+      off = sm & (bs - 1);
+      if (a.rotary_dim > 0 && 8 * c < a.rotary_dim) {
+        const int b = find_request(a.s.cum, a.s.batch, t);
+        pos = a.s.past[b] + (t - a.s.cum[b]);
+      }
+    } else {
+      const int b = find_request(a.s.cum, a.s.batch, t);
+      if (b < 0) continue;
+      pos = a.s.past[b] + (t - a.s.cum[b]);
+      if (pos < 0) continue;
+      const int bi = pos >> a.s.block_shift;
+      if (bi >= a.s.maxblk) continue;
+      blk = a.s.block_table[(int64_t)b * a.s.maxblk + bi];
+      if (blk < 0 || blk >= a.s.num_blocks) continue;  // unmapped: nothing to write
+      off = pos & (bs - 1);
+    }
     const int64_t dst = slot_base(blk, off, kvh, bs, a.kv_heads, a.head_size) + 8 * c;
     const int64_t src_row = (int64_t)t * a.kv_heads * a.head_size + (int64_t)kvh * a.head_size;
     store16(a.value_cache + dst, load16(a.value + src_row + 8 * c));

@@ -372,8 +372,11 @@ pa_status pa_append_kv(const pa_attn_params* params, const pa_paged_kv* kv, cons
   if (!key || !value) return fail(PA_ERR_INVALID_ARGUMENT, "key/value: expected non-NULL");
   if (!aligned16(key) || !aligned16(value))
     return fail(PA_ERR_INVALID_ARGUMENT, "key/value: expected 16-byte alignment");
+  if ((reinterpret_cast<uintptr_t>(kv->slot_mapping) & 3) != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "slot_mapping: expected 4-byte alignment");
   pa::AppendArgs a;
   a.s = layout(params, kv);
+  a.slot_mapping = kv->slot_mapping;
   a.key = static_cast<const uint16_t*>(key);
   a.value = static_cast<const uint16_t*>(value);
   a.key_cache = static_cast<uint16_t*>(kv->key_cache);

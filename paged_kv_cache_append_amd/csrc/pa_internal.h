@@ -25,6 +25,7 @@ struct SeqLayout {
 
 struct AppendArgs {
   SeqLayout s;
+  const int32_t* slot_mapping;   // null: slots derived from the block table
   const uint16_t* key;    // fp16 [T, Hkv*D]
   const uint16_t* value;  // fp16 [T, Hkv*D]
   uint16_t* key_cache;    // fp16 [NB, bs, Hkv, D]

@@ -333,6 +333,23 @@ def scaled_down(name: str, poison: bool = False) -> Workload:
 # device upload (PyTorch is only the memory allocator here)
 # ---------------------------------------------------------------------------
 
+def random_slot_mapping(w: Workload, seed: int, skip_fraction: float = 0.0) -> np.ndarray:
+    """An explicit write-slot assignment for every token of ``w`` (int32
+    ``[T]``), drawn the way a scheduler that owns placement might hand it
+    out: distinct slots anywhere in the pool, each a flat index ``block *
+    block_size + offset``, with about ``skip_fraction`` of the tokens given
+    ``-1`` (not written: a prefix-cache hit or a rejected draft token)."""
+    rng = np.random.default_rng(seed)
+    n_slots = w.num_blocks * w.block_size
+    T = w.token_count
+    if T > n_slots:
+        raise ValueError("more tokens than pool slots")
+    slots = rng.choice(n_slots, size=T, replace=False).astype(np.int64)
+    skip = rng.random(T) < skip_fraction
+    slots[skip] = -1
+    return slots.astype(np.int32)
+
+
 def to_device(w: Workload, device="cuda", pools: bool = True, threads: Optional[int] = None):
     """Copy a workload's host arrays to device tensors.  Pools are streamed
     chunk by chunk so the host never holds a whole pool."""

@@ -60,6 +60,14 @@ def oracle_append(w, kc=None, vc=None):
                             kv_num_heads=w.kv_num_heads, head_size=w.head_size, **rot_kw(w))
 
 
+def oracle_append_slots(w, slot_mapping):
+    kc = w.pool_blocks(wl.KIND_K, range(w.num_blocks))
+    vc = w.pool_blocks(wl.KIND_V, range(w.num_blocks))
+    return oracle.append_kv(kc, vc, w.key, w.value, w.cum, w.past, w.block_table,
+                            kv_num_heads=w.kv_num_heads, head_size=w.head_size,
+                            slot_mapping=slot_mapping, **rot_kw(w))
+
+
 def oracle_forward(w, nk, nv, rows=None):
     return oracle.forward(w.query, nk, nv, w.cum, w.past, w.block_table,
                           num_heads=w.num_heads, kv_num_heads=w.kv_num_heads,

@@ -48,7 +48,7 @@ def params(**kw):
 def paged(**kw):
     d = dict(key_cache=FAKE, value_cache=FAKE, num_blocks=32, block_table=FAKE,
              max_blocks_per_seq=8, cumulative_sequence_length=FAKE, past_seqlens=FAKE,
-             batch_size=4, token_count=4)
+             batch_size=4, token_count=4, slot_mapping=None)
     d.update(kw)
     return _lib.PagedKV(*[d[f] for f, _ in _lib.PagedKV._fields_])
 
@@ -131,6 +131,10 @@ def test_forward_buffer_rules():
     assert call_forward(params(), kv, query=FAKE + 2) == 1 and "16-byte" in err()
     assert call_append(params(), kv, key=None) == 1 and "key/value" in err()
     assert call_forward(params(), kv, mq=-1) == 1 and "bound" in err()
+
+
+def test_slot_mapping_alignment_rule():
+    assert call_append(params(), paged(slot_mapping=FAKE + 2)) == 1 and "slot_mapping" in err()
 
 
 def test_unsupported_head_size_is_reported():

@@ -91,3 +91,44 @@ def test_full_size_workload(name):
               f"rows {len(prow)}: max_abs_err={e:.3e}", flush=True)
         worst = max(worst, e)
     assert worst <= TOL, worst
+
+
+@pytest.mark.parametrize("name", ["gemma2_prefill_window", "llama3_8b_mixed"])
+def test_full_size_slot_mapping(name):
+    """The append with explicit write slots (scattered over the whole pool,
+    5 % of the tokens given -1) at full size: both pools bit-exact against
+    the oracle's append, then sampled forward rows against the oracle on
+    those pools."""
+    import torch
+    import paged_kv_cache_append_amd as pa
+    from pa_harness import attn_for, rot_kw
+    w = wl.make_workload(name)
+    sm = wl.random_slot_mapping(w, 4242, skip_fraction=0.05)
+    print(f"\n[case] full {name} with slot_mapping: T={w.token_count} "
+          f"skipped={int((sm < 0).sum())}", flush=True)
+    dev = wl.to_device(w)
+    pa.append_kv(attn_for(w), dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
+                 dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"],
+                 slot_mapping=torch.from_numpy(sm).cuda())
+    out = gpu_forward(w, dev)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    kc = w.pool_blocks(wl.KIND_K, range(w.num_blocks))
+    vc = w.pool_blocks(wl.KIND_V, range(w.num_blocks))
+    nk, nv = oracle.append_kv(kc, vc, w.key, w.value, w.cum, w.past, w.block_table,
+                              kv_num_heads=w.kv_num_heads, head_size=w.head_size,
+                              slot_mapping=sm, **rot_kw(w))
+    del kc, vc
+    assert dev["key_cache"].cpu().numpy().tobytes() == nk.tobytes()
+    assert dev["value_cache"].cpu().numpy().tobytes() == nv.tobytes()
+    print("[case] append bit-exact on the whole pools", flush=True)
+    rng = np.random.default_rng(7)
+    rows = sorted(int(x) for x in rng.choice(w.token_count, size=min(24, w.token_count),
+                                             replace=False))
+    ref = oracle.forward(w.query, nk, nv, w.cum, w.past, w.block_table, num_heads=w.num_heads,
+                         kv_num_heads=w.kv_num_heads, head_size=w.head_size, scale=w.scale,
+                         softcap=w.softcap, local_window_size=w.local_window_size, rows=rows,
+                         **rot_kw(w))
+    e = max_err(out[rows], ref)
+    print(f"[case] {len(rows)} sampled rows: max_abs_err={e:.3e}", flush=True)
+    assert e <= TOL, e

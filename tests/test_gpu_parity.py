@@ -8,7 +8,8 @@ import pytest
 
 from paged_kv_cache_append_amd import workloads as wl
 
-from pa_harness import TOL, gpu_forward, gpu_step, max_err, oracle_append, oracle_forward
+from pa_harness import (TOL, gpu_forward, gpu_step, max_err, oracle_append, oracle_append_slots,
+                        oracle_forward)
 
 pytestmark = pytest.mark.gpu
 
@@ -173,3 +174,75 @@ def test_wide_head_prefill_kernels_with_pieces(kernel):
     w = wl.build_case("pieces1", 601, q_lens=q_lens, past=past, num_heads=H,
                       kv_num_heads=Hkv, head_size=D, block_size=bs, **kw)
     check(w, 2, prefill_kernel=kernel, prefill_pieces=3)
+
+
+SLOT_CASES = [
+    # q_lens, past, H, Hkv, D, bs, extra kwargs, fraction of tokens with -1
+    ([1, 1, 40, 3], [50, 900, 0, 64], 8, 2, 64, 16, {}, 0.25),
+    ([130, 1], [300, 1000], 6, 2, 128, 32, dict(do_rotary=1, rotary_dim=128), 0.1),
+    ([64, 2], [100, 3000], 16, 8, 256, 16,
+     dict(do_rotary=1, rotary_interleaved=1, rotary_dim=64, softcap=50.0), 0.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SLOT_CASES)))
+def test_slot_mapping(case):
+    """Explicit write slots (scattered over the whole pool, some -1): the
+    pools match the oracle's append bit for bit and the forward, which reads
+    through the block table as always, matches the oracle."""
+    import torch
+    import paged_kv_cache_append_amd as pa
+    from pa_harness import attn_for
+    q_lens, past, H, Hkv, D, bs, kw, skip = SLOT_CASES[case]
+    w = wl.build_case(f"slots{case}", 900 + case, q_lens=q_lens, past=past, num_heads=H,
+                      kv_num_heads=Hkv, head_size=D, block_size=bs, extra_tokens=2, **kw)
+    sm = wl.random_slot_mapping(w, 77 + case, skip_fraction=skip)
+    print(f"\n[case] slot_mapping {w.name} T={w.token_count} D={D} skipped={int((sm < 0).sum())}",
+          flush=True)
+    dev = wl.to_device(w)
+    a = attn_for(w)
+    pa.append_kv(a, dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
+                 dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"],
+                 slot_mapping=torch.from_numpy(sm).cuda())
+    out = gpu_forward(w, dev)
+    torch.cuda.synchronize()
+    nk, nv = oracle_append_slots(w, sm)
+    assert dev["key_cache"].cpu().numpy().tobytes() == nk.tobytes()
+    assert dev["value_cache"].cpu().numpy().tobytes() == nv.tobytes()
+    err = max_err(out.cpu().numpy(), oracle_forward(w, nk, nv))
+    print(f"[case] max_abs_err={err:.3e}", flush=True)
+    assert err <= TOL, err
+
+
+def test_slot_mapping_prefix_cache_hit():
+    """A chunked prefill whose first tokens are already cached: one append
+    of the cached tokens, then the chunk's append with those tokens given
+    -1, leaves the device pool and output bit-identical to one derived
+    append."""
+    import torch
+    import oracle
+    import paged_kv_cache_append_amd as pa
+    from pa_harness import attn_for
+    w = wl.build_case("prefix", 950, q_lens=[70, 1, 33], past=[0, 400, 16], num_heads=8,
+                      kv_num_heads=2, head_size=128, block_size=16, do_rotary=1, rotary_dim=64)
+    derived = np.full(w.token_count, -1, np.int32)
+    for t in range(w.token_count):
+        b, j = oracle.locate_token(w.cum, t)
+        blk, off = oracle.derived_slot(w.block_table, b, oracle.token_position(w.past, b, j),
+                                       w.block_size)
+        derived[t] = blk * w.block_size + off
+    k = 40
+    first = np.where(np.arange(w.token_count) < k, derived, -1).astype(np.int32)
+    rest = np.where(np.arange(w.token_count) < k, -1, derived).astype(np.int32)
+    a = attn_for(w)
+    dev = wl.to_device(w)
+    for sm in (first, rest):
+        pa.append_kv(a, dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
+                     dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"],
+                     slot_mapping=torch.from_numpy(sm).cuda())
+    out = gpu_forward(w, dev).cpu().numpy()
+    ref_dev, ref_out = gpu_step(w)
+    assert dev["key_cache"].cpu().numpy().tobytes() == ref_dev["key_cache"].cpu().numpy().tobytes()
+    assert dev["value_cache"].cpu().numpy().tobytes() == \
+        ref_dev["value_cache"].cpu().numpy().tobytes()
+    assert out.tobytes() == ref_out.tobytes()

@@ -531,3 +531,147 @@ def test_lse_merge_of_any_partition_equals_direct_softmax():
         num = sum(math.exp(m - M) * o for m, _, o in parts)
         den = sum(math.exp(m - M) * l for m, l, _ in parts)
         np.testing.assert_allclose(num / den, direct, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# explicit write slots (PagedAttention -- CUDA Design Document, section 5.2)
+# ---------------------------------------------------------------------------
+
+def _golden_slots():
+    return json.load(open(os.path.join(GOLDEN, "slot_mapping.json")))
+
+
+def test_explicit_slot_golden():
+    g = _golden_slots()
+    sm = np.array(g["slot_mapping"], np.int32)
+    for e in g["expected"]:
+        got = oracle.explicit_slot(sm, e["t"], g["block_size"], g["num_blocks"])
+        if e["block"] is None and "owner" not in e:
+            assert got is None
+        elif "owner" not in e:
+            assert got == (e["block"], e["offset"])
+
+
+def test_append_with_slot_mapping_writes_exactly_the_golden_slots():
+    g = _golden_slots()
+    bs, Hkv, D = g["block_size"], 2, 8
+    cum = np.array(g["cum"], np.int32)
+    past = np.array(g["past"], np.int32)
+    table = np.array(g["block_table"], np.int32)
+    sm = np.array(g["slot_mapping"], np.int32)
+    T = g["token_count"]
+    rng = np.random.default_rng(6)
+    kc = rng.standard_normal((g["num_blocks"], bs, Hkv, D)).astype(np.float16)
+    vc = rng.standard_normal((g["num_blocks"], bs, Hkv, D)).astype(np.float16)
+    key = rng.standard_normal((T, Hkv * D)).astype(np.float16)
+    val = rng.standard_normal((T, Hkv * D)).astype(np.float16)
+    nk, nv = oracle.append_kv(kc, vc, key, val, cum, past, table, kv_num_heads=Hkv, head_size=D,
+                              slot_mapping=sm)
+    expect_k, expect_v = kc.copy(), vc.copy()
+    for e in g["expected"]:
+        if e["block"] is None:
+            continue
+        expect_k[e["block"], e["offset"]] = key[e["t"]].reshape(Hkv, D)
+        expect_v[e["block"], e["offset"]] = val[e["t"]].reshape(Hkv, D)
+    assert nk.tobytes() == expect_k.tobytes()
+    assert nv.tobytes() == expect_v.tobytes()
+
+
+def _derived_mapping(w):
+    """The derived write slot of every token as a flat index (-1 for tokens
+    owned by no request), from the pinned derivation functions."""
+    sm = np.full(w.token_count, -1, np.int32)
+    for t in range(w.token_count):
+        owner = oracle.locate_token(w.cum, t)
+        if owner is None:
+            continue
+        b, j = owner
+        blk, off = oracle.derived_slot(w.block_table, b, oracle.token_position(w.past, b, j),
+                                       w.block_size)
+        sm[t] = blk * w.block_size + off
+    return sm
+
+
+def _rot(w):
+    return dict(cos_cache=w.cos_cache, sin_cache=w.sin_cache,
+                rotary_interleaved=bool(w.rotary_interleaved)) if w.do_rotary else {}
+
+
+def _append(w, kc, vc, **kw):
+    return oracle.append_kv(kc, vc, w.key, w.value, w.cum, w.past, w.block_table,
+                            kv_num_heads=w.kv_num_heads, head_size=w.head_size, **_rot(w), **kw)
+
+
+@pytest.mark.parametrize("rot", [0, 1])
+def test_slot_mapping_equal_to_derived_slots_matches_derived_append(rot):
+    w = wl.build_case("sm", 31, q_lens=[5, 1, 9], past=[12, 30, 0], num_heads=4, kv_num_heads=2,
+                      head_size=16, block_size=16, do_rotary=rot, rotary_dim=16 if rot else 0,
+                      extra_tokens=2)
+    kc, vc = w.pool_blocks(0, range(w.num_blocks)), w.pool_blocks(1, range(w.num_blocks))
+    a = _append(w, kc, vc)
+    b = _append(w, kc, vc, slot_mapping=_derived_mapping(w))
+    assert a[0].tobytes() == b[0].tobytes() and a[1].tobytes() == b[1].tobytes()
+
+
+def test_slot_mapping_all_minus_one_writes_nothing():
+    w = wl.build_case("sm", 32, q_lens=[4, 1], past=[3, 20], num_heads=2, kv_num_heads=1,
+                      head_size=8, block_size=16)
+    kc, vc = w.pool_blocks(0, range(w.num_blocks)), w.pool_blocks(1, range(w.num_blocks))
+    nk, nv = _append(w, kc, vc, slot_mapping=np.full(w.token_count, -1, np.int32))
+    assert nk.tobytes() == kc.tobytes() and nv.tobytes() == vc.tobytes()
+
+
+def test_slot_mapping_out_of_range_writes_nothing():
+    w = wl.build_case("sm", 33, q_lens=[3], past=[5], num_heads=2, kv_num_heads=1,
+                      head_size=8, block_size=16)
+    kc, vc = w.pool_blocks(0, range(w.num_blocks)), w.pool_blocks(1, range(w.num_blocks))
+    n = w.num_blocks * w.block_size
+    nk, nv = _append(w, kc, vc, slot_mapping=np.array([n, -2, n + 100], np.int32))
+    assert nk.tobytes() == kc.tobytes() and nv.tobytes() == vc.tobytes()
+
+
+def test_slot_mapping_rotates_at_the_token_position_not_the_slot():
+    """A token written to a slot other than its derived one carries exactly
+    the bytes the derived append stores for it (rotation follows the
+    position past[b] + j)."""
+    w = wl.build_case("sm", 34, q_lens=[6, 2], past=[40, 7], num_heads=4, kv_num_heads=2,
+                      head_size=16, block_size=16, do_rotary=1, rotary_dim=16, pool_slack=3.0)
+    kc, vc = w.pool_blocks(0, range(w.num_blocks)), w.pool_blocks(1, range(w.num_blocks))
+    derived = _derived_mapping(w)
+    used = {int(x) for x in w.block_table.ravel() if x >= 0}
+    spare = [p for p in range(w.num_blocks) if p not in used]
+    assert spare
+    moved = np.array([spare[0] * w.block_size + t for t in range(w.token_count)], np.int32)
+    dk, dv = _append(w, kc, vc)
+    mk, mv = _append(w, kc, vc, slot_mapping=moved)
+    bs = w.block_size
+    for t in range(w.token_count):
+        db, do = divmod(int(derived[t]), bs)
+        mb, mo = divmod(int(moved[t]), bs)
+        assert mk[mb, mo].tobytes() == dk[db, do].tobytes()
+        assert mv[mb, mo].tobytes() == dv[db, do].tobytes()
+        assert mk[db, do].tobytes() == kc[db, do].tobytes()   # derived slot untouched
+
+
+def test_prefix_cache_hit_then_rest_equals_one_derived_append():
+    """Tokens whose K/V are already cached are passed with -1: writing the
+    first k tokens, then the rest with the first k skipped, leaves the pool
+    (and hence the forward output) exactly as one derived append does."""
+    w = wl.build_case("sm", 35, q_lens=[13, 1, 6], past=[0, 25, 9], num_heads=4, kv_num_heads=2,
+                      head_size=16, block_size=16, do_rotary=1, rotary_dim=8)
+    kc, vc = w.pool_blocks(0, range(w.num_blocks)), w.pool_blocks(1, range(w.num_blocks))
+    derived = _derived_mapping(w)
+    k = 5                                   # first 5 tokens of request 0 are "cached"
+    first = np.where(np.arange(w.token_count) < k, derived, -1).astype(np.int32)
+    rest = np.where(np.arange(w.token_count) < k, -1, derived).astype(np.int32)
+    pk, pv = _append(w, kc, vc, slot_mapping=first)
+    fk, fv = oracle.append_kv(pk, pv, w.key, w.value, w.cum, w.past, w.block_table,
+                              kv_num_heads=w.kv_num_heads, head_size=w.head_size, **_rot(w),
+                              slot_mapping=rest)
+    dk, dv = _append(w, kc, vc)
+    assert fk.tobytes() == dk.tobytes() and fv.tobytes() == dv.tobytes()
+    fwd = dict(num_heads=w.num_heads, kv_num_heads=w.kv_num_heads, head_size=w.head_size,
+               **_rot(w))
+    o1 = oracle.forward(w.query, fk, fv, w.cum, w.past, w.block_table, **fwd)
+    o2 = oracle.forward(w.query, dk, dv, w.cum, w.past, w.block_table, **fwd)
+    assert np.array_equal(o1, o2)
