@@ -44,6 +44,14 @@ Readings where the pages are silent (each also listed in the design notes):
   self-consistency properties.
 * A query row with no admitted key (impossible with causal + W >= 1) is 0.
 * Output rows of tokens owned by no sequence are 0.
+* Quantized caches (PagedAttention -- CUDA Design Document, §8.3): the
+  dequantized value of a stored code is ``q * scale`` (zero point 0), with one
+  scale per tensor or one per (kv head, channel).  The pages print no
+  quantizer; the reading here is ``code = saturate(round_half_even(x / scale))``
+  where ``x`` is the fp16 value the unquantized path would store (after
+  rotary) and the division is one fp32 division: int8 saturates to
+  ``[-128, 127]``, float8 e4m3fn (bias 7, no infinities, largest finite 448)
+  to ``+-448``.
 * Explicit write slots (PagedAttention -- CUDA Design Document, §5.2): slot
   ``s`` is block ``s // block_size``, offset ``s % block_size``; ``-1`` writes
   nothing.  The stored K is still rotated at the token's position
@@ -55,6 +63,7 @@ Readings where the pages are silent (each also listed in the design notes):
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 from typing import Iterable, Optional
 
 import numpy as np
@@ -137,6 +146,97 @@ def rope_query_fp64(x: np.ndarray, pos: int, cos: np.ndarray, sin: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# quantized caches: PagedAttention -- CUDA Design Document, §8.2-§8.4
+# (int8 / float8 e4m3fn codes, fp32 scales, symmetric: x = q * scale)
+# ---------------------------------------------------------------------------
+
+CACHE_FP16, CACHE_INT8, CACHE_FP8 = 0, 1, 2
+QUANT_NONE, QUANT_PER_TENSOR, QUANT_PER_CHANNEL = 0, 1, 2
+FP8_MAX = 448.0
+
+
+def fp8_e4m3fn_value(code: int) -> float:
+    """Value of one float8 e4m3fn byte: sign bit, 4 exponent bits (bias 7),
+    3 mantissa bits; exponent 0 is subnormal (m * 2^-9); 0x7f / 0xff is NaN;
+    there are no infinities."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * m * 2.0 ** -9
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def fp8_e4m3fn_code(x: float) -> int:
+    """The float8 e4m3fn byte nearest to ``x`` (ties to an even mantissa),
+    saturating to +-448; exact (rational) arithmetic."""
+    sign = 0x80 if math.copysign(1.0, x) < 0 else 0
+    a = Fraction(abs(x))
+    if a >= FP8_MAX:
+        return sign | 0x7E
+    best = None
+    # all finite non-negative codes in increasing order of value
+    for code in range(0x7F):
+        v = Fraction(fp8_e4m3fn_value(code))
+        d = abs(v - a)
+        if best is None or d < best[0] or (d == best[0] and (code & 1) == 0):
+            best = (d, code)
+    return sign | best[1]
+
+
+def fp8_e4m3fn_codes(y: np.ndarray) -> np.ndarray:
+    """Vectorized :func:`fp8_e4m3fn_code` for float32 values: the nearest of
+    the finite code values (ties to the even code), saturating to +-448."""
+    vals = np.array([fp8_e4m3fn_value(c) for c in range(0x7F)], np.float64)   # increasing
+    mids = (vals[:-1] + vals[1:]) / 2.0                                       # exact in fp64
+    a = np.abs(y.astype(np.float64))
+    idx = np.searchsorted(mids, a, side="left")
+    tie = (idx < mids.shape[0]) & (mids[np.minimum(idx, mids.shape[0] - 1)] == a)
+    idx = np.where(tie & (idx % 2 == 1), idx + 1, idx)
+    idx = np.where(a >= FP8_MAX, 0x7E, idx)
+    sign = np.where(np.signbit(y), 0x80, 0)
+    return (sign | idx).astype(np.uint8)
+
+
+def quant_scale(scale: np.ndarray, quant_type: int, kvh: int, ch: int, head_size: int) -> float:
+    """The fp32 scale of channel ``ch`` of kv head ``kvh``: one value per
+    tensor, or ``scale[kvh * head_size + ch]`` per channel (§8.3: shape
+    ``[kv_num_heads, 1, head_size]``)."""
+    if quant_type == QUANT_PER_TENSOR:
+        return float(scale[0])
+    return float(scale[kvh * head_size + ch])
+
+
+def quantize_row(x16: np.ndarray, cache_dtype: int, scale: np.ndarray, quant_type: int,
+                 kvh: int) -> np.ndarray:
+    """Codes of one fp16 head row (see the header for the rounding)."""
+    D = x16.shape[0]
+    s = np.array([quant_scale(scale, quant_type, kvh, c, D) for c in range(D)], np.float32)
+    y = x16.astype(np.float32) / s                       # one fp32 division per channel
+    if cache_dtype == CACHE_INT8:
+        return np.clip(np.rint(y), -128, 127).astype(np.int8)
+    return fp8_e4m3fn_codes(y)
+
+
+def dequantize(codes: np.ndarray, cache_dtype: int, scale: np.ndarray, quant_type: int,
+               head_size: int) -> np.ndarray:
+    """fp64 values ``q * scale`` of codes ``[..., Hkv, D]`` (§8.3)."""
+    if cache_dtype == CACHE_INT8:
+        q = codes.astype(np.float64)
+    else:
+        table = np.array([fp8_e4m3fn_value(c) for c in range(256)], np.float64)
+        q = table[codes.astype(np.uint8)]
+    Hkv = codes.shape[-2]
+    if quant_type == QUANT_PER_TENSOR:
+        sc = np.full((Hkv, head_size), float(np.float32(scale[0])), np.float64)
+    else:
+        sc = np.asarray(scale, np.float32).astype(np.float64).reshape(Hkv, head_size)
+    return q * sc
+
+
+# ---------------------------------------------------------------------------
 # a4: KV append (scatter new tokens into the pool, in place semantics)
 # Design: WebGPU PagedAttention §7 (scatter before attention);
 # PagedAttention -- CUDA Design Document §4.4 (cache outputs alias inputs).
@@ -157,11 +257,16 @@ def append_kv(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
               value: np.ndarray, cum: np.ndarray, past: np.ndarray,
               block_table: np.ndarray, *, kv_num_heads: int, head_size: int,
               cos_cache: Optional[np.ndarray] = None, sin_cache: Optional[np.ndarray] = None,
-              rotary_interleaved: bool = False, slot_mapping: Optional[np.ndarray] = None):
+              rotary_interleaved: bool = False, slot_mapping: Optional[np.ndarray] = None,
+              cache_dtype: int = CACHE_FP16, k_quant_type: int = QUANT_NONE,
+              v_quant_type: int = QUANT_NONE, k_scale: Optional[np.ndarray] = None,
+              v_scale: Optional[np.ndarray] = None):
     """Return new ``(key_cache, value_cache)`` copies with every new token's
     K (rotated if a rotary table is given) and V stored at its derived slot,
-    or at ``slot_mapping[t]`` when a mapping is given.  Slots that no token
-    maps to are left byte-identical."""
+    or at ``slot_mapping[t]`` when a mapping is given.  With a quantized
+    cache the stored rows are the codes of those fp16 rows (§8.4: quantized
+    as they are scattered).  Slots that no token maps to are left
+    byte-identical."""
     kc = key_cache.copy()
     vc = value_cache.copy()
     block_size = kc.shape[1]
@@ -182,10 +287,14 @@ def append_kv(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
             blk, off = where
         for h in range(Hkv):
             krow = key[t, h * D:(h + 1) * D]
+            vrow = value[t, h * D:(h + 1) * D]
             if cos_cache is not None:
                 krow = rope_key_fp16(krow, pos, cos_cache, sin_cache, rotary_interleaved)
+            if cache_dtype != CACHE_FP16:
+                krow = quantize_row(krow, cache_dtype, k_scale, k_quant_type, h)
+                vrow = quantize_row(vrow, cache_dtype, v_scale, v_quant_type, h)
             kc[blk, off, h, :] = krow
-            vc[blk, off, h, :] = value[t, h * D:(h + 1) * D]
+            vc[blk, off, h, :] = vrow
     return kc, vc
 
 
@@ -198,6 +307,17 @@ def gather_sequence(cache: np.ndarray, block_table: np.ndarray, b: int, kv_len: 
     block ``block_table[b, tau // bs]``, offset ``tau % bs``."""
     bs = cache.shape[1]
     out = np.empty((kv_len, cache.shape[2], cache.shape[3]), np.float64)
+    for tau in range(kv_len):
+        blk, off = derived_slot(block_table, b, tau, bs)
+        out[tau] = cache[blk, off]
+    return out
+
+
+def gather_codes(cache: np.ndarray, block_table: np.ndarray, b: int, kv_len: int) -> np.ndarray:
+    """The stored codes ``[kv_len, Hkv, D]`` of sequence ``b`` (same walk as
+    :func:`gather_sequence`, no conversion)."""
+    bs = cache.shape[1]
+    out = np.empty((kv_len, cache.shape[2], cache.shape[3]), cache.dtype)
     for tau in range(kv_len):
         blk, off = derived_slot(block_table, b, tau, bs)
         out[tau] = cache[blk, off]
@@ -226,11 +346,14 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
             softcap: float = 0.0, local_window_size: int = -1,
             cos_cache: Optional[np.ndarray] = None, sin_cache: Optional[np.ndarray] = None,
             rotary_interleaved: bool = False, rows: Optional[Iterable[int]] = None,
-            return_probs: bool = False):
+            return_probs: bool = False, cache_dtype: int = CACHE_FP16,
+            k_quant_type: int = QUANT_NONE, v_quant_type: int = QUANT_NONE,
+            k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None):
     """Attention output in fp64.
 
     ``key_cache``/``value_cache`` must already hold the new tokens (run
-    :func:`append_kv` first).  Returns ``[T, H*D]`` for all tokens, or
+    :func:`append_kv` first); a quantized cache holds codes, which are
+    dequantized (``q * scale``, §8.3) as they are gathered.  Returns ``[T, H*D]`` for all tokens, or
     ``[len(rows), H*D]`` in the given order when ``rows`` is set.  With
     ``return_probs`` also returns ``{(t, h): probabilities over keys}``."""
     T = query.shape[0]
@@ -255,6 +378,11 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
         kv_len = int(past[b]) + q_len
         K = gather_sequence(key_cache, block_table, b, kv_len)
         V = gather_sequence(value_cache, block_table, b, kv_len)
+        if cache_dtype != CACHE_FP16:
+            K = dequantize(gather_codes(key_cache, block_table, b, kv_len), cache_dtype, k_scale,
+                           k_quant_type, D)
+            V = dequantize(gather_codes(value_cache, block_table, b, kv_len), cache_dtype,
+                           v_scale, v_quant_type, D)
         tau = np.arange(kv_len)
         n_idx = [n for n, _, _ in items]
         positions = [token_position(past, b, j) for _, _, j in items]

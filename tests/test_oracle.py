@@ -675,3 +675,135 @@ def test_prefix_cache_hit_then_rest_equals_one_derived_append():
     o1 = oracle.forward(w.query, fk, fv, w.cum, w.past, w.block_table, **fwd)
     o2 = oracle.forward(w.query, dk, dv, w.cum, w.past, w.block_table, **fwd)
     assert np.array_equal(o1, o2)
+
+
+# ---------------------------------------------------------------------------
+# quantized caches (PagedAttention -- CUDA Design Document, section 8)
+# ---------------------------------------------------------------------------
+
+def _golden_quant():
+    return json.load(open(os.path.join(GOLDEN, "quantize.json")))
+
+
+def test_int8_codes_golden():
+    for e in _golden_quant()["int8"]:
+        row = np.array([e["x"]], np.float16)
+        code = oracle.quantize_row(row, oracle.CACHE_INT8, np.array([e["scale"]], np.float32),
+                                   oracle.QUANT_PER_TENSOR, 0)
+        assert int(code[0]) == e["code"], e
+
+
+def test_fp8_codes_golden_and_brute_force():
+    g = _golden_quant()["fp8_e4m3fn"]
+    for e in g:
+        row = np.array([e["x"]], np.float16) if abs(e["x"]) < 65504 else None
+        want = int(e["code"], 16)
+        assert oracle.fp8_e4m3fn_code(e["x"] / e["scale"]) == want, e
+        if row is not None:
+            code = oracle.quantize_row(row, oracle.CACHE_FP8, np.array([e["scale"]], np.float32),
+                                       oracle.QUANT_PER_TENSOR, 0)
+            assert int(code[0]) == want, e
+    # the vectorized encoder is the brute-force nearest-code search
+    rng = np.random.default_rng(3)
+    y = np.concatenate([rng.standard_normal(2000).astype(np.float32) * s
+                        for s in (1e-3, 0.05, 1.0, 30.0, 600.0)])
+    brute = np.array([oracle.fp8_e4m3fn_code(float(v)) for v in y], np.uint8)
+    assert np.array_equal(oracle.fp8_e4m3fn_codes(y), brute)
+
+
+def test_fp8_code_values_are_the_format():
+    # every finite code decodes to (1 + m/8) 2^(e-7), or m 2^-9 when e = 0
+    vals = [oracle.fp8_e4m3fn_value(c) for c in range(0x7F)]
+    assert vals[0] == 0.0 and vals[1] == 2.0 ** -9 and vals[8] == 2.0 ** -6
+    assert vals[0x7E] == 448.0 and vals[0x38] == 1.0
+    assert all(b > a for a, b in zip(vals, vals[1:]))
+    assert math.isnan(oracle.fp8_e4m3fn_value(0x7F))
+
+
+@pytest.mark.parametrize("dtype", [1, 2])
+def test_dequantized_codes_are_within_half_a_step(dtype):
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal(4096) * 0.7).astype(np.float16)
+    s = np.array([0.011], np.float32)
+    codes = oracle.quantize_row(x, dtype, s, oracle.QUANT_PER_TENSOR, 0)
+    back = oracle.dequantize(codes.reshape(1, 1, -1), dtype, s, oracle.QUANT_PER_TENSOR,
+                             4096).ravel()
+    y = x.astype(np.float64) / float(s[0])
+    if dtype == oracle.CACHE_INT8:
+        inside = np.abs(y) <= 127
+        assert np.all(np.abs(back[inside] / float(s[0]) - y[inside]) <= 0.5 + 1e-6)
+    else:
+        normal = (np.abs(y) >= 2.0 ** -6) & (np.abs(y) <= 448)
+        assert np.all(np.abs(back[normal] / float(s[0]) - y[normal]) <= np.abs(y[normal]) / 16)
+
+
+def _codes(rng, shape, dtype):
+    """Random valid codes: any int8, or any finite float8 e4m3fn byte."""
+    if dtype == oracle.CACHE_INT8:
+        return rng.integers(-128, 128, shape).astype(np.int8)
+    mag = rng.integers(0, 0x7F, shape)                      # 0x7f would be NaN
+    return (mag | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
+
+
+def _quant_case(seed, rot=0):
+    w = wl.build_case("q", seed, q_lens=[1, 7, 1], past=[40, 9, 70], num_heads=4,
+                      kv_num_heads=2, head_size=16, block_size=16, do_rotary=rot,
+                      rotary_dim=16 if rot else 0)
+    rng = np.random.default_rng(seed)
+    nb, bs = w.num_blocks, w.block_size
+    return w, rng
+
+
+@pytest.mark.parametrize("dtype", [1, 2])
+def test_per_channel_with_equal_scales_is_per_tensor(dtype):
+    w, rng = _quant_case(41, rot=1)
+    kc = _codes(rng, (w.num_blocks, w.block_size, 2, 16), dtype)
+    vc = kc.copy()
+    rot = dict(cos_cache=w.cos_cache, sin_cache=w.sin_cache)
+    common = dict(kv_num_heads=2, head_size=16, cache_dtype=dtype, **rot)
+    st = np.array([0.02], np.float32)
+    sc = np.full(2 * 16, 0.02, np.float32)
+    a = oracle.append_kv(kc, vc, w.key, w.value, w.cum, w.past, w.block_table,
+                         k_quant_type=1, v_quant_type=1, k_scale=st, v_scale=st, **common)
+    b = oracle.append_kv(kc, vc, w.key, w.value, w.cum, w.past, w.block_table,
+                         k_quant_type=2, v_quant_type=2, k_scale=sc, v_scale=sc, **common)
+    assert a[0].tobytes() == b[0].tobytes() and a[1].tobytes() == b[1].tobytes()
+    fwd = dict(num_heads=4, kv_num_heads=2, head_size=16, cache_dtype=dtype, **rot)
+    oa = oracle.forward(w.query, a[0], a[1], w.cum, w.past, w.block_table, k_quant_type=1,
+                        v_quant_type=1, k_scale=st, v_scale=st, **fwd)
+    ob = oracle.forward(w.query, b[0], b[1], w.cum, w.past, w.block_table, k_quant_type=2,
+                        v_quant_type=2, k_scale=sc, v_scale=sc, **fwd)
+    assert np.array_equal(oa, ob)
+
+
+@pytest.mark.parametrize("dtype", [1, 2])
+def test_quantized_forward_is_attention_over_the_dequantized_cache(dtype):
+    """The forward over codes equals the plain forward over an fp64 cache
+    holding code * scale (per-channel scales, every head and channel its
+    own)."""
+    w, rng = _quant_case(42)
+    Hkv, D = 2, 16
+    kc = _codes(rng, (w.num_blocks, w.block_size, Hkv, D), dtype)
+    vc = _codes(rng, kc.shape, dtype)
+    ks = rng.uniform(0.005, 0.05, Hkv * D).astype(np.float32)
+    vs = rng.uniform(0.005, 0.05, Hkv * D).astype(np.float32)
+    q = dict(cache_dtype=dtype, k_quant_type=2, v_quant_type=2, k_scale=ks, v_scale=vs)
+    nk, nv = oracle.append_kv(kc, vc, w.key, w.value, w.cum, w.past, w.block_table,
+                              kv_num_heads=Hkv, head_size=D, **q)
+    out = oracle.forward(w.query, nk, nv, w.cum, w.past, w.block_table, num_heads=4,
+                         kv_num_heads=Hkv, head_size=D, **q)
+    fk = oracle.dequantize(nk, dtype, ks, 2, D)
+    fv = oracle.dequantize(nv, dtype, vs, 2, D)
+    ref = oracle.forward(w.query, fk, fv, w.cum, w.past, w.block_table, num_heads=4,
+                         kv_num_heads=Hkv, head_size=D)
+    assert np.array_equal(out, ref)
+    # and the new tokens' codes dequantize to within half a step of their rows
+    for t in range(w.token_count):
+        b, j = oracle.locate_token(w.cum, t)
+        blk, off = oracle.derived_slot(w.block_table, b, oracle.token_position(w.past, b, j), 16)
+        x = w.value[t].astype(np.float64).reshape(Hkv, D)
+        step = vs.reshape(Hkv, D).astype(np.float64)
+        err = np.abs(fv[blk, off] - x)
+        bound = step / 2 + 1e-12 if dtype == 1 else np.abs(x) / 16 + step * 2.0 ** -10
+        inside = np.abs(x / step) <= (127 if dtype == 1 else 448)   # not saturated
+        assert np.all(err[inside] <= bound[inside])
