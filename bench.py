@@ -8,6 +8,7 @@ already resident in device memory when the timed region starts.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
                     [--copy-calibration-mib N]
+                    [--cache int8|fp8 [--k-quant tensor|channel] [--v-quant tensor|channel]]
     python bench.py --summarize-pmc counter_collection.csv ...
 
 Prints ONE JSON line.  ``value`` is the decode KV throughput of the whole
@@ -17,6 +18,9 @@ dispatch timestamped on its stream (start/stop events of the launch itself);
 ``roofline`` describes the dominant kernel from those durations (per-launch
 algorithmic bytes or FLOPs over its average launch time).
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the workload.
+With ``--cache`` the pools hold int8 or float8 e4m3fn codes with fp32 scales
+(decode-only workloads: every request has one new token); the algorithmic
+bytes then count one byte per cached element.
 """
 from __future__ import annotations
 
@@ -38,9 +42,10 @@ MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16 MFMA
 DEFAULT_CONFIG = "llama3_8b_mixed"
 
 
-def algorithmic_work(w):
+def algorithmic_work(w, kv_elem_bytes=2):
     """Decode bytes (K+V of every decode row's admitted keys, once per kv head,
-    plus its Q and O rows) and prefill FLOPs (4*D*H per admitted pair)."""
+    at ``kv_elem_bytes`` per element, plus its fp16 Q and O rows) and prefill
+    FLOPs (4*D*H per admitted pair)."""
     H, Hkv, D = w.num_heads, w.kv_num_heads, w.head_size
     q_lens = w.q_lens
     dec_bytes = 0
@@ -54,7 +59,7 @@ def algorithmic_work(w):
             kv = past + 1
             if W > 0:
                 kv = min(kv, W)
-            dec_bytes += kv * Hkv * D * 2 * 2 + 2 * H * D * 2
+            dec_bytes += kv * Hkv * D * kv_elem_bytes * 2 + 2 * H * D * 2
             n_dec += 1
         elif ql > 1:
             for j in range(ql):
@@ -100,11 +105,12 @@ def kernel_source_hash(kind: str) -> str:
 
 
 def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=1024,
-                 target_seconds=10.0):
+                 target_seconds=10.0, quant=None):
     """fp64 oracle on a bounded sample of the workload: the decode requests
     (GB/s of decode K/V bytes) or, for a prefill-only batch, the last rows of
     the first request (GFLOP/s).  Also returns the max-abs error of the GPU
-    rows the sample covers."""
+    rows the sample covers.  ``quant`` = (cache dtype, K quant type, V quant
+    type, K scales, V scales) runs it on the quantized pool."""
     import threadpoolctl
 
     import oracle
@@ -113,12 +119,20 @@ def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=1024,
     prefill = not dec
     seqs = dec if dec else [0]
     sub = wl.subset(w, seqs)
-    kc = sub.pool_blocks(wl.KIND_K, range(sub.num_blocks))
-    vc = sub.pool_blocks(wl.KIND_V, range(sub.num_blocks))
+    qkw = {}
+    if quant:
+        cd, kq, vq, ks, vs = quant
+        qkw = dict(cache_dtype=cd, k_quant_type=kq, v_quant_type=vq, k_scale=ks, v_scale=vs)
+        kc = sub.code_blocks(wl.KIND_K, range(sub.num_blocks), cd)
+        vc = sub.code_blocks(wl.KIND_V, range(sub.num_blocks), cd)
+    else:
+        kc = sub.pool_blocks(wl.KIND_K, range(sub.num_blocks))
+        vc = sub.pool_blocks(wl.KIND_V, range(sub.num_blocks))
     rot = dict(cos_cache=sub.cos_cache, sin_cache=sub.sin_cache,
                rotary_interleaved=bool(sub.rotary_interleaved)) if sub.do_rotary else {}
     nk, nv = oracle.append_kv(kc, vc, sub.key, sub.value, sub.cum, sub.past, sub.block_table,
-                              kv_num_heads=sub.kv_num_heads, head_size=sub.head_size, **rot)
+                              kv_num_heads=sub.kv_num_heads, head_size=sub.head_size, **rot,
+                              **qkw)
     threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
                   if i.get("user_api") == "blas") or 1
     rows = None
@@ -132,7 +146,7 @@ def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=1024,
         ref = oracle.forward(sub.query, nk, nv, sub.cum, sub.past, sub.block_table,
                              num_heads=sub.num_heads, kv_num_heads=sub.kv_num_heads,
                              head_size=sub.head_size, scale=sub.scale, softcap=sub.softcap,
-                             local_window_size=sub.local_window_size, rows=rows, **rot)
+                             local_window_size=sub.local_window_size, rows=rows, **rot, **qkw)
         reps += 1
         if time.perf_counter() - t0 >= target_seconds:
             break
@@ -151,11 +165,12 @@ def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=1024,
                 "sample": f"last {len(rows)} query rows of request 0 of {w.name} "
                           f"({flops / 1e9:.2f} GFLOP over admitted pairs), full fp64 score "
                           f"rows + softmax + PV, {dt:.2f} s per pass, {reps} passes"}, err
-    nbytes, _, _ = algorithmic_work(sub)
+    nbytes, _, _ = algorithmic_work(sub, 1 if quant else 2)
     err = float(np.max(np.abs(gpu_out[prow].astype(np.float64) - ref)))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{len(dec)} decode requests of {w.name} ({nbytes / 1e6:.1f} MB of K/V+Q/O), "
+            "sample": f"{len(dec)} decode requests of {w.name} ({nbytes / 1e6:.1f} MB of K/V+Q/O"
+                      f"{', quantized pool dequantized on gather' if quant else ''}), "
                       f"gather + full scores + softmax + PV in fp64, {dt:.2f} s per pass, "
                       f"{reps} passes"}, err
 
@@ -238,6 +253,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cache", choices=("fp16", "int8", "fp8"), default="fp16",
+                    help="element type of the paged pools (int8 / fp8: codes + fp32 scales)")
+    ap.add_argument("--k-quant", choices=("tensor", "channel"), default="channel")
+    ap.add_argument("--v-quant", choices=("tensor", "channel"), default="channel")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain fp16 copy kernel over this many MiB (read N, "
                          "write N), three times, to scale HBM byte counters")
@@ -284,24 +303,39 @@ def main():
         del src, dst
 
     w = wl.make_workload(args.config)
-    dev = wl.to_device(w)
+    cd = {"fp16": wl.CACHE_FP16, "int8": wl.CACHE_INT8, "fp8": wl.CACHE_FP8}[args.cache]
+    quant = None
+    sc = {}
+    if cd != wl.CACHE_FP16:
+        if np.any(w.q_lens != 1):
+            print(f"bench.py: --cache {args.cache} measures decode-only workloads (one new "
+                  f"token per request); {w.name} has multi-token requests", file=sys.stderr)
+            sys.exit(2)
+        qt = {"tensor": wl.QUANT_PER_TENSOR, "channel": wl.QUANT_PER_CHANNEL}
+        kq, vq = qt[args.k_quant], qt[args.v_quant]
+        ks = wl.draw_scales(w, wl.KIND_K, cd, kq, 7)
+        vs = wl.draw_scales(w, wl.KIND_V, cd, vq, 7)
+        quant = (cd, kq, vq, ks, vs)
+        sc = dict(k_scale=torch.from_numpy(ks).cuda(), v_scale=torch.from_numpy(vs).cuda())
+    dev = wl.to_device(w, cache_dtype=cd)
     a = pa.Attn(num_heads=w.num_heads, kv_num_heads=w.kv_num_heads, head_size=w.head_size,
                 block_size=w.block_size, scale=w.scale, softcap=w.softcap,
                 local_window_size=w.local_window_size, do_rotary=w.do_rotary,
-                rotary_interleaved=w.rotary_interleaved)
+                rotary_interleaved=w.rotary_interleaved, cache_dtype=cd,
+                k_quant_type=quant[1] if quant else 0, v_quant_type=quant[2] if quant else 0)
     T = w.token_count
     out = torch.empty((T, w.num_heads * w.head_size), dtype=torch.float16, device="cuda")
     nws = pa.forward_workspace_bytes(a, dev["key_cache"], dev["value_cache"], dev["block_table"],
-                                     dev["cum"], dev["past"], T)
+                                     dev["cum"], dev["past"], T, **sc)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
     plan = pa.describe_plan(a, dev["key_cache"], dev["value_cache"], dev["block_table"],
-                            dev["cum"], dev["past"], T)
+                            dev["cum"], dev["past"], T, **sc)
 
     def step():
         pa.append_kv(a, dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
-                     dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"])
+                     dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"], **sc)
         pa.forward(a, dev["query"], dev["key_cache"], dev["value_cache"], dev["block_table"],
-                   dev["cum"], dev["past"], dev["cos"], dev["sin"], workspace=ws, out=out)
+                   dev["cum"], dev["past"], dev["cos"], dev["sin"], workspace=ws, out=out, **sc)
 
     def timed(k):
         start = torch.cuda.Event(enable_timing=True)
@@ -336,19 +370,21 @@ def main():
     for _ in range(args.steps):
         pa.append_kv(a, dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
                      dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"],
-                     slot_mapping=sm)
+                     slot_mapping=sm, **sc)
     torch.cuda.synchronize()
     slots_ms, slots_n = pa.timing_read("append")
     pa.timing_disable()
 
-    dec_bytes, pf_flops, n_dec = algorithmic_work(w)
+    kv_elem = 1 if quant else 2
+    dec_bytes, pf_flops, n_dec = algorithmic_work(w, kv_elem)
     per = {s: (ms / n * 1e3 if n else 0.0) for s, (ms, n) in stages.items()}   # us per launch
     if dec_bytes:
         value, unit = dec_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
     else:
         value, unit = pf_flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
     kernels = {f"{s}_us": round(v, 3) for s, v in per.items()}
-    app_bytes = 2 * 2 * T * w.kv_num_heads * w.head_size * 2   # K and V, read + written
+    # K and V: fp16 rows read, cache elements written
+    app_bytes = 2 * T * w.kv_num_heads * w.head_size * (2 + kv_elem)
     append = {"algorithmic_bytes_per_launch": app_bytes,
               "derived_slots_us": round(per["append"], 3),
               "derived_slots_gbs": round(app_bytes / (per["append"] * 1e-6) / 1e9, 1)
@@ -368,7 +404,9 @@ def main():
         achieved = dec_bytes / (per["decode"] * 1e-6) / 1e9 if per["decode"] else None
         roof = {"bound": "hbm", "kernel": "decode", "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-                "traffic": traffic_from_profiles(f"decode:{w.name}", kernel_source_hash("decode")),
+                "traffic": traffic_from_profiles(
+                    f"decode:{w.name}" + (f":{args.cache}" if quant else ""),
+                    kernel_source_hash("decode")),
                 "algorithmic_bytes_per_launch": dec_bytes}
     else:
         achieved = pf_flops / (per["prefill"] * 1e-6) / 1e12 if per["prefill"] else None
@@ -383,7 +421,7 @@ def main():
 
     cpu, err = (None, None)
     if not args.no_cpu_baseline:
-        cpu, err = cpu_baseline(w, out.cpu().numpy())
+        cpu, err = cpu_baseline(w, out.cpu().numpy(), quant=quant)
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
@@ -393,6 +431,9 @@ def main():
         "config": {"workload": w.name, "batch": w.batch_size, "tokens": T,
                    "num_heads": w.num_heads, "kv_num_heads": w.kv_num_heads,
                    "head_size": w.head_size, "block_size": w.block_size,
+                   "cache": args.cache,
+                   "k_quant": args.k_quant if quant else "none",
+                   "v_quant": args.v_quant if quant else "none",
                    "decode_requests": n_dec, "decode_bytes": dec_bytes,
                    "prefill_flops": pf_flops, "plan": plan},
         "roofline": roof,

@@ -73,12 +73,41 @@ typedef struct {
                                  head_size 256 with each cache smaller than 4 GiB,
                                  else PA_ERR_UNSUPPORTED.  Auto takes 2 where it
                                  applies.  Testing hook; rounding may differ.          */
+  int32_t cache_dtype;        /* element type of both caches (section 8.2):
+                                 PA_CACHE_FP16 (0), PA_CACHE_INT8 (1) or
+                                 PA_CACHE_FP8_E4M3FN (2); see "Quantized caches"     */
+  int32_t k_quant_type;       /* PA_QUANT_NONE (0), PA_QUANT_PER_TENSOR (1) or
+                                 PA_QUANT_PER_CHANNEL (2) for the K cache            */
+  int32_t v_quant_type;       /* the same for the V cache (chosen independently)    */
 } pa_attn_params;
+
+/* Quantized caches (PagedAttention -- CUDA Design Document, section 8).
+ * With cache_dtype != PA_CACHE_FP16 both caches hold one signed byte per
+ * element, [num_blocks, block_size, kv_num_heads, head_size]: int8 two's
+ * complement, or float8 e4m3fn (sign, 4 exponent bits of bias 7, 3 mantissa
+ * bits, no infinities, 0x7f/0xff NaN).  The value of code c is c * s with
+ * zero point 0 (section 8.3.1) and s the fp32 scale of its channel: one value
+ * for the whole cache (PER_TENSOR, k_scale[0]) or one per (kv head, channel)
+ * (PER_CHANNEL, k_scale[kvh * head_size + d], the [kv_num_heads, 1,
+ * head_size] layout of section 8.3).  pa_append_kv stores
+ * saturate(round-half-even(fp32(x) / s)) of the fp16 value x the fp16 cache
+ * would hold (after rotary; one fp32 division): int8 saturates to
+ * [-128, 127], e4m3fn to +-448 (section 8.4, write path).  pa_forward
+ * dequantizes in the kernel (section 8.5, phase 3): a PER_TENSOR K scale is
+ * folded into the score scale, a PER_CHANNEL one into Q (rounded to fp16), and
+ * the V scale is applied to the output accumulator.  Every token of a
+ * quantized forward runs on the decode kernel (path 0 or 1; path 2 is
+ * PA_ERR_UNSUPPORTED).  Validation (section 8.7): a quantized cache_dtype
+ * needs both quant types non-NONE, fp16 needs both NONE; a quant type other
+ * than NONE needs its scale and NONE forbids it. */
+enum { PA_CACHE_FP16 = 0, PA_CACHE_INT8 = 1, PA_CACHE_FP8_E4M3FN = 2 };
+enum { PA_QUANT_NONE = 0, PA_QUANT_PER_TENSOR = 1, PA_QUANT_PER_CHANNEL = 2 };
 
 /* The paged cache and the per-step request layout.  Host struct holding
  * device pointers. */
 typedef struct {
-  void *key_cache;                          /* fp16 [num_blocks, block_size, Hkv, D]  */
+  void *key_cache;                          /* [num_blocks, block_size, Hkv, D] of
+                                               fp16, or of byte codes when quantized */
   void *value_cache;                        /* same shape; both mutated in place by
                                                pa_append_kv (cache outputs alias the
                                                inputs, section 4.4)                   */
@@ -95,6 +124,12 @@ typedef struct {
   const int32_t *slot_mapping;              /* NULL, or int32 [token_count], 4-byte
                                                aligned: the write slot of each new
                                                token (pa_append_kv only; section 5) */
+  const float *k_scale;                     /* fp32 scales of a quantized K cache:
+                                               [1] (PER_TENSOR, 4-byte aligned) or
+                                               [kv_num_heads, head_size]
+                                               (PER_CHANNEL, 16-byte aligned); NULL
+                                               when k_quant_type is NONE             */
+  const float *v_scale;                     /* the same for the V cache              */
 } pa_paged_kv;
 
 /*

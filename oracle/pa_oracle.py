@@ -204,9 +204,10 @@ def quant_scale(scale: np.ndarray, quant_type: int, kvh: int, ch: int, head_size
     """The fp32 scale of channel ``ch`` of kv head ``kvh``: one value per
     tensor, or ``scale[kvh * head_size + ch]`` per channel (§8.3: shape
     ``[kv_num_heads, 1, head_size]``)."""
+    flat = np.asarray(scale, np.float32).reshape(-1)       # [1] or [Hkv, (1,) D]
     if quant_type == QUANT_PER_TENSOR:
-        return float(scale[0])
-    return float(scale[kvh * head_size + ch])
+        return float(flat[0])
+    return float(flat[kvh * head_size + ch])
 
 
 def quantize_row(x16: np.ndarray, cache_dtype: int, scale: np.ndarray, quant_type: int,
@@ -230,7 +231,8 @@ def dequantize(codes: np.ndarray, cache_dtype: int, scale: np.ndarray, quant_typ
         q = table[codes.astype(np.uint8)]
     Hkv = codes.shape[-2]
     if quant_type == QUANT_PER_TENSOR:
-        sc = np.full((Hkv, head_size), float(np.float32(scale[0])), np.float64)
+        sc = np.full((Hkv, head_size), float(np.asarray(scale, np.float32).reshape(-1)[0]),
+                     np.float64)
     else:
         sc = np.asarray(scale, np.float32).astype(np.float64).reshape(Hkv, head_size)
     return q * sc

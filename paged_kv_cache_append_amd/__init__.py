@@ -17,9 +17,15 @@ from typing import Optional
 
 from . import _lib
 
-__all__ = ["PAError", "Attn", "append_kv", "forward", "forward_workspace_bytes",
+__all__ = ["PAError", "Attn", "CACHE_FP16", "CACHE_INT8", "CACHE_FP8_E4M3FN", "QUANT_NONE",
+           "QUANT_PER_TENSOR", "QUANT_PER_CHANNEL", "append_kv", "forward", "forward_workspace_bytes",
            "describe_plan", "last_error", "timing_enable", "timing_disable", "timing_read",
            "library_path"]
+
+
+# cache element types and scale granularities (the ABI enums of pa.h)
+CACHE_FP16, CACHE_INT8, CACHE_FP8_E4M3FN = 0, 1, 2
+QUANT_NONE, QUANT_PER_TENSOR, QUANT_PER_CHANNEL = 0, 1, 2
 
 
 class PAError(RuntimeError):
@@ -44,13 +50,17 @@ class Attn:
     split_tokens: int = 0
     prefill_pieces: int = 0
     prefill_kernel: int = 0
+    cache_dtype: int = CACHE_FP16
+    k_quant_type: int = QUANT_NONE
+    v_quant_type: int = QUANT_NONE
 
     def c(self) -> _lib.AttnParams:
         return _lib.AttnParams(self.num_heads, self.kv_num_heads, self.head_size,
                                self.block_size, float(self.scale), float(self.softcap),
                                self.local_window_size, self.do_rotary,
                                self.rotary_interleaved, self.path, self.split_tokens,
-                               self.prefill_pieces, self.prefill_kernel)
+                               self.prefill_pieces, self.prefill_kernel, self.cache_dtype,
+                               self.k_quant_type, self.v_quant_type)
 
 
 def library_path() -> str:
@@ -84,11 +94,24 @@ def _need(t, name, dtype, shape=None):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def _kv(key_cache, value_cache, block_table, cum, past, token_count,
-        slot_mapping=None) -> _lib.PagedKV:
+def _cache_dtypes(cache_dtype: int):
     import torch
-    _need(key_cache, "key_cache", torch.float16)
-    _need(value_cache, "value_cache", torch.float16, key_cache.shape)
+    if cache_dtype == CACHE_INT8:
+        return (torch.int8,)
+    if cache_dtype == CACHE_FP8_E4M3FN:
+        return (torch.uint8, torch.float8_e4m3fn)
+    return (torch.float16,)
+
+
+def _kv(attn: Attn, key_cache, value_cache, block_table, cum, past, token_count,
+        slot_mapping=None, k_scale=None, v_scale=None) -> _lib.PagedKV:
+    import torch
+    dts = _cache_dtypes(attn.cache_dtype)
+    if key_cache.dtype not in dts:
+        raise ValueError(f"key_cache: expected dtype {dts[0]} for cache_dtype "
+                         f"{attn.cache_dtype}, got {key_cache.dtype}")
+    _need(key_cache, "key_cache", key_cache.dtype)
+    _need(value_cache, "value_cache", key_cache.dtype, key_cache.shape)
     _need(block_table, "block_table", torch.int32)
     _need(cum, "cumulative_sequence_length", torch.int32, (block_table.shape[0] + 1,))
     _need(past, "past_seqlens", torch.int32, (block_table.shape[0],))
@@ -96,10 +119,12 @@ def _kv(key_cache, value_cache, block_table, cum, past, token_count,
         raise ValueError("key_cache must be rank 4 and block_table rank 2")
     if slot_mapping is not None:
         _need(slot_mapping, "slot_mapping", torch.int32, (token_count,))
+    _need(k_scale, "k_scale", torch.float32)
+    _need(v_scale, "v_scale", torch.float32)
     return _lib.PagedKV(key_cache.data_ptr(), value_cache.data_ptr(), key_cache.shape[0],
                         block_table.data_ptr(), block_table.shape[1], cum.data_ptr(),
                         past.data_ptr(), block_table.shape[0], token_count,
-                        _ptr(slot_mapping))
+                        _ptr(slot_mapping), _ptr(k_scale), _ptr(v_scale))
 
 
 def _stream(stream) -> int:
@@ -119,17 +144,21 @@ def _rot(attn: Attn, cos_cache, sin_cache):
 
 
 def append_kv(attn: Attn, key, value, key_cache, value_cache, block_table, cum, past,
-              cos_cache=None, sin_cache=None, stream=None, slot_mapping=None) -> None:
+              cos_cache=None, sin_cache=None, stream=None, slot_mapping=None, k_scale=None,
+              v_scale=None) -> None:
     """``pa_append_kv``: scatter new K/V rows ``[T, Hkv*D]`` into the pools
     (in place); ``slot_mapping`` (int32 ``[T]``, -1 = no write) gives the
-    write slots instead of the block table."""
+    write slots instead of the block table.  Quantized caches
+    (``attn.cache_dtype``) take fp32 ``k_scale``/``v_scale`` (``[1]`` or
+    ``[Hkv, D]``)."""
     import torch
     T = key.shape[0]
     _need(key, "key", torch.float16, (T, attn.kv_num_heads * attn.head_size))
     _need(value, "value", torch.float16, (T, attn.kv_num_heads * attn.head_size))
     lib = _lib.load()
     p = attn.c()
-    kv = _kv(key_cache, value_cache, block_table, cum, past, T, slot_mapping)
+    kv = _kv(attn, key_cache, value_cache, block_table, cum, past, T, slot_mapping, k_scale,
+             v_scale)
     c, s, rows, rd = _rot(attn, cos_cache, sin_cache)
     _check(lib.pa_append_kv(ctypes.byref(p), ctypes.byref(kv), key.data_ptr(), value.data_ptr(),
                             c, s, rows, rd, _stream(stream)))
@@ -137,10 +166,11 @@ def append_kv(attn: Attn, key, value, key_cache, value_cache, block_table, cum, 
 
 def forward_workspace_bytes(attn: Attn, key_cache, value_cache, block_table, cum, past,
                             token_count: int, max_query_len_bound: int = 0,
-                            max_kv_len_bound: int = 0) -> int:
+                            max_kv_len_bound: int = 0, k_scale=None, v_scale=None) -> int:
     lib = _lib.load()
     p = attn.c()
-    kv = _kv(key_cache, value_cache, block_table, cum, past, token_count)
+    kv = _kv(attn, key_cache, value_cache, block_table, cum, past, token_count,
+             k_scale=k_scale, v_scale=v_scale)
     n = ctypes.c_size_t(0)
     _check(lib.pa_forward_workspace_bytes(ctypes.byref(p), ctypes.byref(kv), max_query_len_bound,
                                           max_kv_len_bound, ctypes.byref(n)))
@@ -148,10 +178,12 @@ def forward_workspace_bytes(attn: Attn, key_cache, value_cache, block_table, cum
 
 
 def describe_plan(attn: Attn, key_cache, value_cache, block_table, cum, past, token_count: int,
-                  max_query_len_bound: int = 0, max_kv_len_bound: int = 0) -> str:
+                  max_query_len_bound: int = 0, max_kv_len_bound: int = 0, k_scale=None,
+                  v_scale=None) -> str:
     lib = _lib.load()
     p = attn.c()
-    kv = _kv(key_cache, value_cache, block_table, cum, past, token_count)
+    kv = _kv(attn, key_cache, value_cache, block_table, cum, past, token_count,
+             k_scale=k_scale, v_scale=v_scale)
     buf = ctypes.create_string_buffer(512)
     _check(lib.pa_describe_plan(ctypes.byref(p), ctypes.byref(kv), max_query_len_bound,
                                 max_kv_len_bound, buf, 512))
@@ -160,17 +192,19 @@ def describe_plan(attn: Attn, key_cache, value_cache, block_table, cum, past, to
 
 def forward(attn: Attn, query, key_cache, value_cache, block_table, cum, past, cos_cache=None,
             sin_cache=None, max_query_len_bound: int = 0, max_kv_len_bound: int = 0,
-            workspace=None, out=None, stream=None):
+            workspace=None, out=None, stream=None, k_scale=None, v_scale=None):
     """``pa_forward``: attention output ``[T, H*D]`` fp16 for packed queries
     ``[T, H*D]``.  ``workspace``/``out`` are allocated with torch when not
-    given."""
+    given; quantized caches take ``k_scale``/``v_scale`` as for
+    :func:`append_kv`."""
     import torch
     T = query.shape[0]
     HD = attn.num_heads * attn.head_size
     _need(query, "query", torch.float16, (T, HD))
     lib = _lib.load()
     p = attn.c()
-    kv = _kv(key_cache, value_cache, block_table, cum, past, T)
+    kv = _kv(attn, key_cache, value_cache, block_table, cum, past, T, k_scale=k_scale,
+             v_scale=v_scale)
     if out is None:
         out = torch.empty((T, HD), dtype=torch.float16, device=query.device)
     _need(out, "out", torch.float16, (T, HD))

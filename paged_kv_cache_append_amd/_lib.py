@@ -25,7 +25,8 @@ class AttnParams(ctypes.Structure):
                 ("local_window_size", ctypes.c_int32), ("do_rotary", ctypes.c_int32),
                 ("rotary_interleaved", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("split_tokens", ctypes.c_int32), ("prefill_pieces", ctypes.c_int32),
-                ("prefill_kernel", ctypes.c_int32)]
+                ("prefill_kernel", ctypes.c_int32), ("cache_dtype", ctypes.c_int32),
+                ("k_quant_type", ctypes.c_int32), ("v_quant_type", ctypes.c_int32)]
 
 
 class PagedKV(ctypes.Structure):
@@ -34,7 +35,8 @@ class PagedKV(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32),
                 ("cumulative_sequence_length", ctypes.c_void_p),
                 ("past_seqlens", ctypes.c_void_p), ("batch_size", ctypes.c_int32),
-                ("token_count", ctypes.c_int32), ("slot_mapping", ctypes.c_void_p)]
+                ("token_count", ctypes.c_int32), ("slot_mapping", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 _lib = None

@@ -13,6 +13,10 @@
 // out-of-bounds defect of section 18.2 cannot occur).  With an explicit slot
 // mapping the slot is read, not derived (-1: no write); the request is then
 // only looked up for the rotary position.
+//
+// Quantized caches (section 8.4, write path): the lane turns its 8 channels
+// -- after rotary, as fp16, exactly the values an fp16 cache would hold --
+// into 8 byte codes with the channels' fp32 scales and stores 8 bytes.
 #include "pa_device.h"
 
 namespace pa {
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     }
     const int64_t dst = slot_base(blk, off, kvh, bs, a.kv_heads, a.head_size) + 8 * c;
     const int64_t src_row = (int64_t)t * a.kv_heads * a.head_size + (int64_t)kvh * a.head_size;
-    store16(a.value_cache + dst, load16(a.value + src_row + 8 * c));
+    const u32x4 v = load16(a.value + src_row + 8 * c);
     u32x4 k = load16(a.key + src_row + 8 * c);
     if (a.rotary_dim > 0 && 8 * c < a.rotary_dim) {
       float r[8];
@@ -61,7 +65,18 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
                    a.rotary_interleaved, a.rotary_rows, r);
       k = pack8(r);
     }
-    store16(a.key_cache + dst, k);
+    if (a.cache_dtype == kCacheF16) {
+      store16(a.value_cache + dst, v);
+      store16(a.key_cache + dst, k);
+    } else {
+      float sk[8], sv[8];
+      channel_scales(a.k_scale, a.k_quant, kvh, a.head_size, 8 * c, sk);
+      channel_scales(a.v_scale, a.v_quant, kvh, a.head_size, 8 * c, sv);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(a.value_cache) + dst) =
+          quantize8(v, a.cache_dtype, sv);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(a.key_cache) + dst) =
+          quantize8(k, a.cache_dtype, sk);
+    }
   }
 }
 

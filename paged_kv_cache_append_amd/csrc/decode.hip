@@ -23,6 +23,15 @@
 // swaps per tile; the lane holding an output column also holds that head's
 // max, so rescaling is local.  Scores are in log2 units (scale * log2 e
 // folded in).
+//
+// Quantized caches (PagedAttention -- CUDA Design Document, section 8.5,
+// phase 3): the rows are loaded as byte codes (half the bytes of fp16) and
+// turned into fp16 on their way into the LDS tiles (int8 and e4m3fn values
+// are all fp16 values, so the tiles hold the codes exactly).  The K scale is
+// folded into the score scale (per tensor) or into Q (per channel), the V
+// scale multiplies the output accumulator, so the products run on the codes.
+#include <type_traits>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -181,17 +190,38 @@ struct DecodeCfg {
   static constexpr int TBL = 256;        // block-table entries staged per segment
 };
 
-// Whole key rows of one tile, K and V (1 KB per instruction: RPI rows of 2D
-// bytes; lane l moves chunk l % CH of row l / CH).  Bit i of the returned mask
-// says whether the row of instruction i is a real key; the others read block
-// 0 and are zeroed when stored, so nothing non-finite reaches the products.
-template <int D>
-__device__ __forceinline__ uint32_t load_tile(const uint16_t* kb, const uint16_t* vb,
+// One lane's 8 channels of a key row as loaded: fp16 (16 bytes) or 8 codes.
+template <int CT>
+using RawChunk = typename std::conditional<CT == kCacheF16, u32x4, u32x2>::type;
+
+template <int CT>
+__device__ __forceinline__ RawChunk<CT> load_chunk(const char* p) {
+  return *reinterpret_cast<const RawChunk<CT>*>(p);
+}
+
+// The chunk as 8 fp16 values; rows that are not real keys become zeros.
+template <int CT>
+__device__ __forceinline__ u32x4 chunk_f16(RawChunk<CT> v, bool ok) {
+  if (!ok) return u32x4{0, 0, 0, 0};
+  if constexpr (CT == kCacheF16)
+    return v;
+  else
+    return codes_to_f16<CT>(v);
+}
+
+// Whole key rows of one tile, K and V (RPI rows per instruction; lane l moves
+// chunk l % CH of row l / CH: 1 KB of fp16, or 512 B of codes).  Bit i of the
+// returned mask says whether the row of instruction i is a real key; the
+// others read block 0 and are zeroed when stored, so nothing non-finite
+// reaches the products.
+template <int D, int CT>
+__device__ __forceinline__ uint32_t load_tile(const char* kb, const char* vb,
                                               const int32_t* tbl, int first_bi, int shift,
                                               int64_t tok_stride, int k0, int seg_hi, int lane,
-                                              u32x4 (&kr)[DecodeCfg<D>::NI],
-                                              u32x4 (&vr)[DecodeCfg<D>::NI]) {
+                                              RawChunk<CT> (&kr)[DecodeCfg<D>::NI],
+                                              RawChunk<CT> (&vr)[DecodeCfg<D>::NI]) {
   using C = DecodeCfg<D>;
+  constexpr int ES = CT == kCacheF16 ? 2 : 1;   // bytes per element
   const int bmask = (1 << shift) - 1;
   const int c = lane % C::CH;
   uint32_t okm = 0;
@@ -202,14 +232,15 @@ __device__ __forceinline__ uint32_t load_tile(const uint16_t* kb, const uint16_t
     const int blk = tbl[in ? (key >> shift) - first_bi : 0];
     const bool ok = in && blk >= 0;
     okm |= (uint32_t)ok << i;
-    const int64_t off = ((int64_t)(ok ? blk : 0) * (bmask + 1) + (key & bmask)) * tok_stride + 8 * c;
-    kr[i] = load16(kb + off);
-    vr[i] = load16(vb + off);
+    const int64_t off =
+        (((int64_t)(ok ? blk : 0) * (bmask + 1) + (key & bmask)) * tok_stride + 8 * c) * ES;
+    kr[i] = load_chunk<CT>(kb + off);
+    vr[i] = load_chunk<CT>(vb + off);
   }
   return okm;
 }
 
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, int CT>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : D <= 128 ? 2 : 1)))
 void decode_kernel(const DecodeArgs a) {
@@ -234,6 +265,20 @@ void decode_kernel(const DecodeArgs a) {
   int32_t* tbl = s_tbl[wave];
   const int shift = sl.block_shift;
   const int64_t tok_stride = (int64_t)a.kv_heads * D;
+  constexpr int ES = CT == kCacheF16 ? 2 : 1;   // bytes per cache element
+  // a per-tensor K scale joins the score scale (exact in the dot product:
+  // the zero point is 0); a per-channel one is folded into Q below
+  float score_scale = a.score_scale, cap_in = a.cap_in;
+  bool k_per_channel = false;
+  if constexpr (CT != kCacheF16) {
+    if (a.k_quant == kQuantChannel) {
+      k_per_channel = true;
+    } else {
+      const float ks = a.k_scale[0];
+      score_scale *= ks;
+      cap_in *= ks;
+    }
+  }
 
   for (int item = blockIdx.x * kDecodeWaves + wave; item < total; item += nworkers) {
     const int e = item / HC;
@@ -279,10 +324,17 @@ void decode_kernel(const DecodeArgs a) {
         const int c = 4 * ks + q;
         if (head_ok) {
           v = load16(qrow + 8 * c);
-          if (a.rotary_dim > 0 && 8 * c < a.rotary_dim) {
+          const bool rot = a.rotary_dim > 0 && 8 * c < a.rotary_dim;
+          if (rot || k_per_channel) {
             float rr[8];
-            rotate_chunk(qrow, v, c, r.pos, a.cos, a.sin, a.rotary_dim, a.rotary_interleaved,
-                         a.rotary_rows, rr);
+            rotate_chunk(qrow, v, c, r.pos, a.cos, a.sin, rot ? a.rotary_dim : 0,
+                         a.rotary_interleaved, a.rotary_rows, rr);
+            if (k_per_channel) {
+              float ks[8];
+              channel_scales(a.k_scale, kQuantChannel, kvh, D, 8 * c, ks);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) rr[e] *= ks[e];
+            }
             v = pack8(rr);
           }
         }
@@ -295,8 +347,8 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < C::DB; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
     float m = kNegInf, lsum = 0.f;
-    const uint16_t* kb = a.key_cache + (int64_t)kvh * D;
-    const uint16_t* vb = a.value_cache + (int64_t)kvh * D;
+    const char* kb = reinterpret_cast<const char*>(a.key_cache) + (int64_t)kvh * D * ES;
+    const char* vb = reinterpret_cast<const char*>(a.value_cache) + (int64_t)kvh * D * ES;
     const int32_t* bt = sl.block_table + (int64_t)r.b * sl.maxblk;
 
     for (int seg_lo = k_lo; seg_lo < k_hi;) {
@@ -317,9 +369,9 @@ void decode_kernel(const DecodeArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
       const int ntile = (seg_hi - seg_lo + C::KT - 1) / C::KT;
-      u32x4 kr[C::NI], vr[C::NI];
-      uint32_t okm = load_tile<D>(kb, vb, tbl, first_bi, shift, tok_stride, seg_lo, seg_hi, lane,
-                                  kr, vr);
+      RawChunk<CT> kr[C::NI], vr[C::NI];
+      uint32_t okm = load_tile<D, CT>(kb, vb, tbl, first_bi, shift, tok_stride, seg_lo, seg_hi,
+                                      lane, kr, vr);
       for (int it = 0; it < ntile; ++it) {
         const int k0 = seg_lo + it * C::KT;
         const bool more = it + 1 < ntile;
@@ -332,14 +384,14 @@ void decode_kernel(const DecodeArgs a) {
           for (int i = 0; i < C::NI; ++i) {
             const int rw = i * C::RPI + lane / C::CH;
             const bool ok = (okm >> i) & 1u;
-            store16(kt + rw * C::KLD + 8 * c, ok ? kr[i] : u32x4{0, 0, 0, 0});
-            store16(vt + rw * C::VLD + 8 * c, ok ? vr[i] : u32x4{0, 0, 0, 0});
+            store16(kt + rw * C::KLD + 8 * c, chunk_f16<CT>(kr[i], ok));
+            store16(vt + rw * C::VLD + 8 * c, chunk_f16<CT>(vr[i], ok));
           }
         }
         __builtin_amdgcn_sched_barrier(0);
         if (more)
-          okm = load_tile<D>(kb, vb, tbl, first_bi, shift, tok_stride, k0 + C::KT, seg_hi, lane,
-                             kr, vr);
+          okm = load_tile<D, CT>(kb, vb, tbl, first_bi, shift, tok_stride, k0 + C::KT, seg_hi,
+                                 lane, kr, vr);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -367,9 +419,9 @@ void decode_kernel(const DecodeArgs a) {
           for (int rr = 0; rr < 4; ++rr) {
             float v = s[sb][rr];
             if constexpr (SOFTCAP)
-              v = tanh_fast(v * a.cap_in) * a.cap_out;
+              v = tanh_fast(v * cap_in) * a.cap_out;
             else
-              v = v * a.score_scale;
+              v = v * score_scale;
             if (edge) {
               const int key = k0 + 16 * sb + 4 * q + rr;
               const bool ok = key < seg_hi && tbl[(key >> shift) - first_bi] >= 0;
@@ -428,6 +480,18 @@ void decode_kernel(const DecodeArgs a) {
     const float lt = xor32_sum(xor16_sum(lsum));
     if (head_ok) {
       const int h = h0 + l16;
+      if constexpr (CT != kCacheF16) {
+        // the V scale of channels 16db + 4q + [0, 4): output = scale * sum p code
+        if (a.v_quant == kQuantChannel) {
+          const float* vs = a.v_scale + (int64_t)kvh * D + 4 * q;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) acc[db] *= *reinterpret_cast<const f4*>(vs + 16 * db);
+        } else {
+          const float vs = a.v_scale[0];
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) acc[db] *= vs;
+        }
+      }
       if (r.nsplit <= 1) {
         const float inv = lt > 0.f ? 1.0f / lt : 0.f;
         uint16_t* orow = a.out + (int64_t)r.t * HD + (int64_t)h * D;
@@ -518,12 +582,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   }
 }
 
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, int CT>
 int occupancy_wg() {
   static int cached = 0;
   if (!cached) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, SOFTCAP>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, SOFTCAP, CT>, 256, 0) !=
+            hipSuccess ||
         n <= 0)
       n = 1;
     cached = n;
@@ -531,21 +596,44 @@ int occupancy_wg() {
   return cached;
 }
 
+template <int D, int CT>
+int occupancy_of(bool softcap) {
+  return softcap ? occupancy_wg<D, true, CT>() : occupancy_wg<D, false, CT>();
+}
+
+template <int D>
+int occupancy_of_head(bool softcap, int cache_dtype) {
+  switch (cache_dtype) {
+    case kCacheI8: return occupancy_of<D, kCacheI8>(softcap);
+    case kCacheF8: return occupancy_of<D, kCacheF8>(softcap);
+    default: return occupancy_of<D, kCacheF16>(softcap);
+  }
+}
+
+template <int D, int CT>
+void launch_decode_cache(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t st) {
+  if (a.use_softcap)
+    launch_kernel(decode_kernel<D, true, CT>, grid, block, st, a);
+  else
+    launch_kernel(decode_kernel<D, false, CT>, grid, block, st, a);
+}
+
 template <int D>
 void launch_decode_variant(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t st) {
-  if (a.use_softcap)
-    launch_kernel(decode_kernel<D, true>, grid, block, st, a);
-  else
-    launch_kernel(decode_kernel<D, false>, grid, block, st, a);
+  switch (a.cache_dtype) {
+    case kCacheI8: launch_decode_cache<D, kCacheI8>(a, grid, block, st); break;
+    case kCacheF8: launch_decode_cache<D, kCacheF8>(a, grid, block, st); break;
+    default: launch_decode_cache<D, kCacheF16>(a, grid, block, st); break;
+  }
 }
 
 }  // namespace
 
-int decode_workgroups_per_cu(int head_size, bool softcap) {
+int decode_workgroups_per_cu(int head_size, bool softcap, int cache_dtype) {
   switch (head_size) {
-    case 64: return softcap ? occupancy_wg<64, true>() : occupancy_wg<64, false>();
-    case 128: return softcap ? occupancy_wg<128, true>() : occupancy_wg<128, false>();
-    case 256: return softcap ? occupancy_wg<256, true>() : occupancy_wg<256, false>();
+    case 64: return occupancy_of_head<64>(softcap, cache_dtype);
+    case 128: return occupancy_of_head<128>(softcap, cache_dtype);
+    case 256: return occupancy_of_head<256>(softcap, cache_dtype);
     default: return 1;
   }
 }

@@ -71,6 +71,54 @@ struct StageScope {
 };
 
 // ---- validation --------------------------------------------------------------
+const char* quant_name(int q) {
+  return q == PA_QUANT_NONE ? "NONE" : q == PA_QUANT_PER_TENSOR ? "PER_TENSOR" : "PER_CHANNEL";
+}
+
+// One cache's quant type against its scale (PagedAttention -- CUDA Design
+// Document, section 8.7: a quant type other than NONE needs its scale, NONE
+// forbids one; a per-channel scale is read 16 bytes at a time).
+pa_status check_scale(const char* which, int quant, const float* scale) {
+  if (quant < PA_QUANT_NONE || quant > PA_QUANT_PER_CHANNEL)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "%s_quant_type: expected 0 (NONE), 1 (PER_TENSOR) or 2 (PER_CHANNEL), got %d",
+                which, quant);
+  if (quant == PA_QUANT_NONE && scale)
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s_scale: given but %s_quant_type is NONE", which,
+                which);
+  if (quant != PA_QUANT_NONE && !scale)
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s_scale: required when %s_quant_type is %s", which,
+                which, quant_name(quant));
+  const uintptr_t align = quant == PA_QUANT_PER_CHANNEL ? 16 : 4;
+  if ((reinterpret_cast<uintptr_t>(scale) & (align - 1)) != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s_scale: expected %d-byte alignment for %s", which,
+                (int)align, quant_name(quant));
+  return PA_OK;
+}
+
+// Cache element type against the quant types (section 8.7: a quantized cache
+// needs both quant types other than NONE; an fp16 cache needs both NONE).
+pa_status check_quant(const pa_attn_params* p, const pa_paged_kv* kv) {
+  if (p->cache_dtype < PA_CACHE_FP16 || p->cache_dtype > PA_CACHE_FP8_E4M3FN)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "cache_dtype: expected 0 (fp16), 1 (int8) or 2 (float8 e4m3fn), got %d",
+                p->cache_dtype);
+  pa_status st = check_scale("k", p->k_quant_type, kv->k_scale);
+  if (st == PA_OK) st = check_scale("v", p->v_quant_type, kv->v_scale);
+  if (st != PA_OK) return st;
+  const bool quantized = p->cache_dtype != PA_CACHE_FP16;
+  if (!quantized && (p->k_quant_type != PA_QUANT_NONE || p->v_quant_type != PA_QUANT_NONE))
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "k_quant_type/v_quant_type: expected NONE with an fp16 cache, got %s/%s",
+                quant_name(p->k_quant_type), quant_name(p->v_quant_type));
+  if (quantized && (p->k_quant_type == PA_QUANT_NONE || p->v_quant_type == PA_QUANT_NONE))
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "k_quant_type/v_quant_type: expected PER_TENSOR or PER_CHANNEL with a quantized "
+                "cache_dtype, got %s/%s",
+                quant_name(p->k_quant_type), quant_name(p->v_quant_type));
+  return PA_OK;
+}
+
 pa_status check_common(const pa_attn_params* p, const pa_paged_kv* kv) {
   if (!p) return fail(PA_ERR_INVALID_ARGUMENT, "params: expected non-NULL");
   if (!kv) return fail(PA_ERR_INVALID_ARGUMENT, "kv: expected non-NULL");
@@ -139,7 +187,7 @@ pa_status check_common(const pa_attn_params* p, const pa_paged_kv* kv) {
   if (!kv->cumulative_sequence_length)
     return fail(PA_ERR_INVALID_ARGUMENT, "cumulative_sequence_length: expected non-NULL");
   if (!kv->past_seqlens) return fail(PA_ERR_INVALID_ARGUMENT, "past_seqlens: expected non-NULL");
-  return PA_OK;
+  return check_quant(p, kv);
 }
 
 pa_status check_rotary(const pa_attn_params* p, const pa_paged_kv* kv, const void* cos_cache,
@@ -184,6 +232,9 @@ pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv) {
   if (p->prefill_kernel == 2 && !rows16_prefill_fits(p, kv))
     return fail(PA_ERR_UNSUPPORTED,
                 "prefill_kernel 2: expected head_size 256 and caches smaller than 4 GiB");
+  if (p->cache_dtype != PA_CACHE_FP16 && p->path == 2)
+    return fail(PA_ERR_UNSUPPORTED,
+                "path 2: quantized caches are served by the decode kernel only (path 0 or 1)");
   return PA_OK;
 }
 
@@ -217,8 +268,8 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
       break;
     }
   pl.head_chunks = pl.g / pl.chunk_heads;
-  if (p->path == 1)
-    pl.token_mode = true;
+  if (p->path == 1 || p->cache_dtype != PA_CACHE_FP16)
+    pl.token_mode = true;   // quantized caches: the decode kernel serves every token
   else if (p->path == 2)
     pl.token_mode = false;
   else
@@ -388,6 +439,11 @@ pa_status pa_append_kv(const pa_attn_params* params, const pa_paged_kv* kv, cons
   a.rotary_dim = params->do_rotary ? rotary_dim : 0;
   a.rotary_interleaved = params->rotary_interleaved;
   a.rotary_rows = params->do_rotary ? rotary_rows : 0;
+  a.cache_dtype = params->cache_dtype;
+  a.k_quant = params->k_quant_type;
+  a.v_quant = params->v_quant_type;
+  a.k_scale = kv->k_scale;
+  a.v_scale = kv->v_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   StageScope scope(PA_STAGE_APPEND, s);
   return device_status(pa::launch_append(a, s), "append kernel launch");
@@ -417,9 +473,12 @@ pa_status pa_describe_plan(const pa_attn_params* params, const pa_paged_kv* kv, 
   if (!buf || len == 0) return fail(PA_ERR_INVALID_ARGUMENT, "buf: expected non-NULL, len > 0");
   const Plan pl = make_plan(params, kv, mq, mk);
   snprintf(buf, len,
-           "mode=%s rows=%d head_chunks=%d g=%d chunk_heads=%d split_tokens=%d max_splits=%d "
-           "listed=%d prefill_grid=(%d,%d) prefill_chunks=%d workspace=%zu",
-           pl.token_mode ? "token" : "request", pl.rows, params->kv_num_heads * pl.head_chunks,
+           "mode=%s cache=%s rows=%d head_chunks=%d g=%d chunk_heads=%d split_tokens=%d "
+           "max_splits=%d listed=%d prefill_grid=(%d,%d) prefill_chunks=%d workspace=%zu",
+           pl.token_mode ? "token" : "request",
+           params->cache_dtype == PA_CACHE_INT8  ? "int8"
+           : params->cache_dtype == PA_CACHE_FP8_E4M3FN ? "fp8e4m3fn"
+                                                       : "fp16", pl.rows, params->kv_num_heads * pl.head_chunks,
            pl.g, pl.chunk_heads, pl.split_tokens, pl.max_splits, pl.listed ? 1 : 0,
            pl.prefill ? pl.prefill_tiles * pl.prefill_chunks + 1 : 0,
            pl.prefill ? params->kv_num_heads : 0, pl.prefill ? pl.prefill_chunks : 0, pl.ws_bytes);
@@ -489,6 +548,11 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
   d.cap_in = cap ? scale / params->softcap : 0.f;
   d.cap_out = cap ? params->softcap * log2e : 0.f;
   d.use_softcap = cap ? 1 : 0;
+  d.cache_dtype = params->cache_dtype;
+  d.k_quant = params->k_quant_type;
+  d.v_quant = params->v_quant_type;
+  d.k_scale = kv->k_scale;
+  d.v_scale = kv->v_scale;
 
   // prefill first, on the side stream when decode rows run beside it; the
   // side stream forks before the plan kernel, which only the decode needs
@@ -577,7 +641,7 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
       // beside a prefill, one decode workgroup per CU is left out so the
       // prefill tiles and the decode workers are resident together whichever
       // kernel is dispatched first
-      const int per_cu = pa::decode_workgroups_per_cu(D, d.use_softcap != 0);
+      const int per_cu = pa::decode_workgroups_per_cu(D, d.use_softcap != 0, d.cache_dtype);
       const int64_t resident = (int64_t)std::max(1, overlap ? per_cu - 1 : per_cu) * device_cus();
       wgs = std::min<int64_t>((bound + pa::kDecodeWaves - 1) / pa::kDecodeWaves, resident);
     } else {

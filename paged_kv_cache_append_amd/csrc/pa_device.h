@@ -13,6 +13,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -144,6 +145,94 @@ __device__ __forceinline__ u32x4 pack8(const float f[8]) {
   for (int e = 0; e < 8; ++e) h[e] = f2h(f[e]);
   u32x4 r;
   __builtin_memcpy(&r, h, 16);
+  return r;
+}
+
+// ---- quantized caches (PagedAttention -- CUDA Design Document, section 8):
+// codes are stored with zero point 0, value = code * scale -------------------
+
+// Eight int8 codes -> eight fp16 values (exact).  code + 128 becomes the low
+// mantissa byte of 1024.0 (0x64xx), then one packed subtraction of 1152.
+__device__ __forceinline__ u32x4 int8x8_to_f16(u32x2 c) {
+  const uint32_t x0 = c[0] ^ 0x80808080u, x1 = c[1] ^ 0x80808080u;
+  const uint32_t w[4] = {__builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u),
+                         __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u),
+                         __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u),
+                         __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)};
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h2 v;
+    __builtin_memcpy(&v, &w[i], 4);
+    v -= h2{(_Float16)1152.0f, (_Float16)1152.0f};
+    __builtin_memcpy(&r[i], &v, 4);
+  }
+  return u32x4{r[0], r[1], r[2], r[3]};
+}
+
+// Eight float8 e4m3fn codes -> eight fp16 values (every e4m3fn value, NaN
+// included, is an fp16 value: exact), two codes per conversion.
+__device__ __forceinline__ u32x4 fp8x8_to_f16(u32x2 c) {
+  const h2 v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[0], 1.0f, false),
+                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[0], 1.0f, true),
+                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[1], 1.0f, false),
+                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[1], 1.0f, true)};
+  u32x4 r;
+  __builtin_memcpy(&r, v, 16);
+  return r;
+}
+
+template <int CT>
+__device__ __forceinline__ u32x4 codes_to_f16(u32x2 c) {
+  if constexpr (CT == kCacheI8)
+    return int8x8_to_f16(c);
+  else
+    return fp8x8_to_f16(c);
+}
+
+// The fp32 scale of channels [d0, d0 + 8) of kv head kvh.
+__device__ __forceinline__ void channel_scales(const float* scale, int quant, int kvh,
+                                               int head_size, int d0, float s[8]) {
+  if (quant == kQuantChannel) {
+    const float* p = scale + (int64_t)kvh * head_size + d0;
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
+    s[4] = b.x; s[5] = b.y; s[6] = b.z; s[7] = b.w;
+  } else {
+    const float v = scale[0];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = v;
+  }
+}
+
+// Codes of eight fp16 values: saturate(round-half-even(fp32(x) / s)), one
+// correctly rounded fp32 division per value.  int8 saturates to [-128, 127];
+// e4m3fn to +-448, after which the hardware conversion rounds to nearest even.
+__device__ __forceinline__ u32x2 quantize8(u32x4 x16, int cache_dtype, const float s[8]) {
+  uint16_t h[8];
+  __builtin_memcpy(h, &x16, 16);
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = h2f(h[e]) / s[e];
+  u32x2 r;
+  if (cache_dtype == kCacheI8) {
+    uint32_t b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      b[e] = (uint32_t)(int32_t)fminf(fmaxf(__builtin_rintf(y[e]), -128.0f), 127.0f) & 0xFFu;
+    r[0] = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    r[1] = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(y[e], -448.0f), 448.0f);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * w], y[4 * w + 1], 0, false);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * w + 2], y[4 * w + 3], v, true);
+      r[w] = (uint32_t)v;
+    }
+  }
   return r;
 }
 

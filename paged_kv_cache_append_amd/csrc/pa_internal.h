@@ -8,6 +8,14 @@
 
 namespace pa {
 
+// Cache element types and scale granularities (the values of the ABI enums).
+constexpr int kCacheF16 = 0;    // fp16 elements
+constexpr int kCacheI8 = 1;     // int8 codes
+constexpr int kCacheF8 = 2;     // float8 e4m3fn codes
+constexpr int kQuantNone = 0;
+constexpr int kQuantTensor = 1; // one fp32 scale per cache
+constexpr int kQuantChannel = 2;// one fp32 scale per (kv head, channel)
+
 // Everything a kernel needs to resolve tokens, positions and pool slots on the
 // device.  Lengths are always read on the device (PagedAttention -- CUDA
 // Design Document, section 4.7: host values only select kernels and size
@@ -37,6 +45,10 @@ struct AppendArgs {
   int32_t rotary_dim;     // 0 = off
   int32_t rotary_interleaved;
   int32_t rotary_rows;    // rows of cos/sin (positions beyond are not rotated)
+  int32_t cache_dtype;    // kCache*: with codes the caches are byte arrays
+  int32_t k_quant, v_quant;
+  const float* k_scale;   // [1] or [Hkv, D]
+  const float* v_scale;
 };
 
 // Decode work is a list of items (row, split) x (kv head, head chunk).  A row
@@ -82,6 +94,10 @@ struct DecodeArgs {
   float cap_in;                 // scale / softcap            (softcap > 0)
   float cap_out;                // softcap * log2(e)          (softcap > 0)
   int32_t use_softcap;
+  int32_t cache_dtype;          // kCache*: with codes key_cache/value_cache are byte arrays
+  int32_t k_quant, v_quant;     // kQuant*
+  const float* k_scale;         // [1] or [Hkv, D]
+  const float* v_scale;
 };
 
 // Plan kernel (one workgroup): lists (row, split) entries of every row with
@@ -171,7 +187,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int head_size, int workgroups, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
-int decode_workgroups_per_cu(int head_size, bool softcap);   // resident decode workgroups per CU
+// resident decode workgroups per CU
+int decode_workgroups_per_cu(int head_size, bool softcap, int cache_dtype);
 hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st);
 hipError_t launch_prefill_merge(const PrefillArgs& a, int head_size, hipStream_t st);
 // 8-wave prefill kernel of 16 rows per wave (head_size 256); grid as launch_prefill

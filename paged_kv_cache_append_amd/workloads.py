@@ -111,6 +111,16 @@ class Workload:
                 out[n, f:] = np.float16(np.nan)
         return out
 
+    def code_blocks(self, kind: int, ids: Sequence[int], cache_dtype: int) -> np.ndarray:
+        """Codes of physical blocks ``ids`` of a quantized K (kind 0) or V
+        (kind 1) pool, before the append."""
+        ids = [int(i) for i in ids]
+        shape = (self.block_size, self.kv_num_heads, self.head_size)
+        out = np.empty((len(ids),) + shape, code_dtype(cache_dtype))
+        for n, p in enumerate(ids):
+            out[n] = draw_code_block(self.seed, kind, p, shape, cache_dtype)
+        return out
+
     def full_pool(self, kind: int, threads: Optional[int] = None,
                   chunk: int = 512) -> np.ndarray:
         """The whole pool of one kind, drawn block by block (threaded)."""
@@ -151,12 +161,19 @@ def fill_pool_chunks(w: Workload, kind: int, out: np.ndarray,
     """Draw every block of one pool kind into ``out`` (host array).  If
     ``sink`` is given it is called as ``sink(start, array)`` per chunk (used to
     stream the pool to device memory without holding it all on the host)."""
+    fill_chunks(w, kind, out, lambda ids: w.pool_blocks(kind, ids), threads, chunk, sink)
+
+
+def fill_chunks(w: Workload, kind: int, out, draw, threads: Optional[int] = None,
+                chunk: int = 512, sink=None) -> None:
+    """Run ``draw(block ids)`` over the pool in chunks (threaded), writing
+    into ``out`` and/or handing each chunk to ``sink(start, array)``."""
     nb = w.num_blocks
     threads = threads or min(16, os.cpu_count() or 1)
 
     def work(start):
         stop = min(nb, start + chunk)
-        arr = w.pool_blocks(kind, range(start, stop))
+        arr = draw(range(start, stop))
         return start, arr
 
     with ThreadPoolExecutor(threads) as ex:
@@ -165,6 +182,54 @@ def fill_pool_chunks(w: Workload, kind: int, out: np.ndarray,
                 out[start:start + arr.shape[0]] = arr
             if sink is not None:
                 sink(start, arr)
+
+
+# ---------------------------------------------------------------------------
+# quantized caches: byte codes of the pool and fp32 scales (drawn, never
+# computed from fp16 values -- the quantizer lives on each side separately)
+# ---------------------------------------------------------------------------
+
+CACHE_FP16, CACHE_INT8, CACHE_FP8 = 0, 1, 2
+QUANT_NONE, QUANT_PER_TENSOR, QUANT_PER_CHANNEL = 0, 1, 2
+
+
+def code_dtype(cache_dtype: int):
+    """numpy dtype of a quantized pool: int8 codes, or e4m3fn bytes as uint8."""
+    return np.int8 if cache_dtype == CACHE_INT8 else np.uint8
+
+
+def draw_code_block(seed: int, kind: int, p: int, shape, cache_dtype: int) -> np.ndarray:
+    """Codes of one physical block of a quantized pool.  int8: a rounded
+    normal of standard deviation 36 clipped to the int8 range (a tail of
+    saturated codes included).  e4m3fn: random sign, exponent field drawn
+    around 12.5 with deviation 0.8 (values of about 2^6, tails comparable to a
+    normal's), random mantissa; the NaN bytes 0x7f and 0xff are replaced by
+    the largest finite codes."""
+    rng = np.random.default_rng([seed, kind, p, 100 + cache_dtype])
+    if cache_dtype == CACHE_INT8:
+        x = np.rint(rng.standard_normal(shape) * 36.0)
+        return np.clip(x, -128, 127).astype(np.int8)
+    e = np.clip(np.rint(rng.normal(12.5, 0.8, shape)), 0, 15).astype(np.uint8)
+    m = rng.integers(0, 8, shape, dtype=np.uint8)
+    s = rng.integers(0, 2, shape, dtype=np.uint8)
+    c = (s << 7) | (e << 3) | m
+    c[(c & 0x7F) == 0x7F] -= 1
+    return c.astype(np.uint8)
+
+
+def draw_scales(w: "Workload", kind: int, cache_dtype: int, quant_type: int,
+                seed: int) -> np.ndarray:
+    """fp32 scales of one quantized cache: ``[1]`` (per tensor) or
+    ``[Hkv, D]`` (per channel).  The base puts the new tokens' values
+    (standard deviation ``kv_sigma``) at about 36 int8 steps (so about one in
+    300 saturates) or about 2^6.3 on the e4m3fn grid; per-channel scales
+    spread the base by a factor drawn from [2^-0.5, 2^0.5)."""
+    rng = np.random.default_rng([seed, kind, 200 + cache_dtype, quant_type])
+    base = w.kv_sigma / 36.0 if cache_dtype == CACHE_INT8 else w.kv_sigma / 80.0
+    if quant_type == QUANT_PER_TENSOR:
+        return np.array([base * rng.uniform(0.8, 1.25)], np.float32)
+    f = 2.0 ** rng.uniform(-0.5, 0.5, (w.kv_num_heads, w.head_size))
+    return (base * f).astype(np.float32)
 
 
 def rope_tables(rows: int, rotary_dim: int, base: float = 10000.0):
@@ -350,9 +415,12 @@ def random_slot_mapping(w: Workload, seed: int, skip_fraction: float = 0.0) -> n
     return slots.astype(np.int32)
 
 
-def to_device(w: Workload, device="cuda", pools: bool = True, threads: Optional[int] = None):
+def to_device(w: Workload, device="cuda", pools: bool = True, threads: Optional[int] = None,
+              cache_dtype: int = CACHE_FP16):
     """Copy a workload's host arrays to device tensors.  Pools are streamed
-    chunk by chunk so the host never holds a whole pool."""
+    chunk by chunk so the host never holds a whole pool.  With a quantized
+    ``cache_dtype`` the pools hold drawn codes (int8, or e4m3fn bytes as
+    uint8)."""
     import torch
     d = {
         "query": torch.from_numpy(w.query).to(device),
@@ -368,13 +436,18 @@ def to_device(w: Workload, device="cuda", pools: bool = True, threads: Optional[
         d["cos"] = torch.from_numpy(w.cos_cache).to(device)
         d["sin"] = torch.from_numpy(w.sin_cache).to(device)
     if pools:
+        tdt = {CACHE_FP16: torch.float16, CACHE_INT8: torch.int8}.get(cache_dtype, torch.uint8)
         for kind, name in ((KIND_K, "key_cache"), (KIND_V, "value_cache")):
-            dev = torch.empty(w.pool_shape(), dtype=torch.float16, device=device)
+            dev = torch.empty(w.pool_shape(), dtype=tdt, device=device)
 
             def sink(start, arr, dev=dev):
                 dev[start:start + arr.shape[0]].copy_(torch.from_numpy(arr))
 
-            fill_pool_chunks(w, kind, None, threads=threads, sink=sink)
+            if cache_dtype == CACHE_FP16:
+                fill_pool_chunks(w, kind, None, threads=threads, sink=sink)
+            else:
+                fill_chunks(w, kind, None, lambda ids, k=kind: w.code_blocks(k, ids, cache_dtype),
+                            threads=threads, sink=sink)
             d[name] = dev
     return d
 
@@ -410,7 +483,11 @@ def subset(w: Workload, seqs: Sequence[int]) -> Workload:
     def pool_blocks(kind, bid, _ids=ids, _p=parent):
         return _p.pool_blocks(kind, [_ids[i] for i in bid])
 
+    def code_blocks(kind, bid, cache_dtype, _ids=ids, _p=parent):
+        return _p.code_blocks(kind, [_ids[i] for i in bid], cache_dtype)
+
     sub.pool_blocks = pool_blocks
+    sub.code_blocks = code_blocks
     sub.extra["parent_rows"] = rows
     sub.extra["parent_block_ids"] = ids
     return sub

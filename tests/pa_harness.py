@@ -79,3 +79,53 @@ def max_err(gpu16, ref64):
     g = gpu16.astype(np.float64)
     assert np.all(np.isfinite(g)), "non-finite GPU output"
     return float(np.max(np.abs(g - ref64))) if g.size else 0.0
+
+
+# ---- quantized caches ------------------------------------------------------
+
+def quant_inputs(w, cache_dtype, k_quant, v_quant, seed=7):
+    """Drawn fp32 scales of both caches (host arrays)."""
+    ks = wl.draw_scales(w, wl.KIND_K, cache_dtype, k_quant, seed)
+    vs = wl.draw_scales(w, wl.KIND_V, cache_dtype, v_quant, seed)
+    return ks, vs
+
+
+def quant_kw(cache_dtype, k_quant, v_quant, ks, vs):
+    return dict(cache_dtype=cache_dtype, k_quant_type=k_quant, v_quant_type=v_quant,
+                k_scale=ks, v_scale=vs)
+
+
+def gpu_quant_step(w, cache_dtype, k_quant, v_quant, ks, vs, slot_mapping=None, **over):
+    """Quantized append + forward on the device: (device dict, fp16 out)."""
+    import torch
+    import paged_kv_cache_append_amd as pa
+    dev = wl.to_device(w, cache_dtype=cache_dtype)
+    dev["k_scale"] = torch.from_numpy(ks).cuda()
+    dev["v_scale"] = torch.from_numpy(vs).cuda()
+    a = attn_for(w, cache_dtype=cache_dtype, k_quant_type=k_quant, v_quant_type=v_quant, **over)
+    sm = None if slot_mapping is None else torch.from_numpy(slot_mapping).cuda()
+    pa.append_kv(a, dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
+                 dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"],
+                 slot_mapping=sm, k_scale=dev["k_scale"], v_scale=dev["v_scale"])
+    out = pa.forward(a, dev["query"], dev["key_cache"], dev["value_cache"], dev["block_table"],
+                     dev["cum"], dev["past"], dev["cos"], dev["sin"], k_scale=dev["k_scale"],
+                     v_scale=dev["v_scale"])
+    torch.cuda.synchronize()
+    return dev, out.cpu().numpy()
+
+
+def oracle_append_quant(w, cache_dtype, k_quant, v_quant, ks, vs, slot_mapping=None):
+    kc = w.code_blocks(wl.KIND_K, range(w.num_blocks), cache_dtype)
+    vc = w.code_blocks(wl.KIND_V, range(w.num_blocks), cache_dtype)
+    return oracle.append_kv(kc, vc, w.key, w.value, w.cum, w.past, w.block_table,
+                            kv_num_heads=w.kv_num_heads, head_size=w.head_size,
+                            slot_mapping=slot_mapping,
+                            **quant_kw(cache_dtype, k_quant, v_quant, ks, vs), **rot_kw(w))
+
+
+def oracle_forward_quant(w, nk, nv, cache_dtype, k_quant, v_quant, ks, vs, rows=None):
+    return oracle.forward(w.query, nk, nv, w.cum, w.past, w.block_table,
+                          num_heads=w.num_heads, kv_num_heads=w.kv_num_heads,
+                          head_size=w.head_size, scale=w.scale, softcap=w.softcap,
+                          local_window_size=w.local_window_size, rows=rows,
+                          **quant_kw(cache_dtype, k_quant, v_quant, ks, vs), **rot_kw(w))

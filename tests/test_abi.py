@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function():
 def params(**kw):
     d = dict(num_heads=8, kv_num_heads=2, head_size=64, block_size=16, scale=0.0, softcap=0.0,
              local_window_size=-1, do_rotary=0, rotary_interleaved=0, path=0, split_tokens=0,
-             prefill_pieces=0, prefill_kernel=0)
+             prefill_pieces=0, prefill_kernel=0, cache_dtype=0, k_quant_type=0, v_quant_type=0)
     d.update(kw)
     return _lib.AttnParams(*[d[f] for f, _ in _lib.AttnParams._fields_])
 
@@ -48,7 +48,7 @@ def params(**kw):
 def paged(**kw):
     d = dict(key_cache=FAKE, value_cache=FAKE, num_blocks=32, block_table=FAKE,
              max_blocks_per_seq=8, cumulative_sequence_length=FAKE, past_seqlens=FAKE,
-             batch_size=4, token_count=4, slot_mapping=None)
+             batch_size=4, token_count=4, slot_mapping=None, k_scale=None, v_scale=None)
     d.update(kw)
     return _lib.PagedKV(*[d[f] for f, _ in _lib.PagedKV._fields_])
 
@@ -101,7 +101,27 @@ NEGATIVE = [
     ({}, dict(block_table=None), 1, "block_table"),
     ({}, dict(cumulative_sequence_length=None), 1, "cumulative_sequence_length"),
     ({}, dict(past_seqlens=None), 1, "past_seqlens"),
+    # quantized caches (section 8.7)
+    (dict(cache_dtype=3), {}, 1, "cache_dtype"),
+    (dict(cache_dtype=-1), {}, 1, "cache_dtype"),
+    (dict(k_quant_type=3), {}, 1, "k_quant_type"),
+    (dict(v_quant_type=-1), {}, 1, "v_quant_type"),
+    (dict(k_quant_type=1), dict(k_scale=FAKE), 1, "expected NONE with an fp16 cache"),
+    ({}, dict(k_scale=FAKE), 1, "k_scale: given but k_quant_type is NONE"),
+    ({}, dict(v_scale=FAKE), 1, "v_scale: given but v_quant_type is NONE"),
+    (dict(cache_dtype=1, k_quant_type=1), dict(k_scale=FAKE), 1,
+     "expected PER_TENSOR or PER_CHANNEL"),
+    (dict(cache_dtype=2), {}, 1, "expected PER_TENSOR or PER_CHANNEL"),
+    (dict(cache_dtype=1, k_quant_type=1, v_quant_type=2), dict(k_scale=FAKE), 1,
+     "v_scale: required when v_quant_type is PER_CHANNEL"),
+    (dict(cache_dtype=2, k_quant_type=2, v_quant_type=1), dict(k_scale=FAKE + 4, v_scale=FAKE),
+     1, "k_scale: expected 16-byte alignment for PER_CHANNEL"),
+    (dict(cache_dtype=2, k_quant_type=1, v_quant_type=1), dict(k_scale=FAKE, v_scale=FAKE + 2),
+     1, "v_scale: expected 4-byte alignment"),
 ]
+
+QUANT = dict(cache_dtype=1, k_quant_type=1, v_quant_type=2)
+QUANT_KV = dict(k_scale=FAKE + 4, v_scale=FAKE)     # per tensor: 4-byte; per channel: 16-byte
 
 
 @pytest.mark.parametrize("pk,kk,status,frag", NEGATIVE)
@@ -148,6 +168,19 @@ def test_rows16_prefill_kernel_limits():
     big = paged(num_blocks=(1 << 32) // (16 * 2 * 256 * 2))   # exactly 4 GiB per cache
     assert call_forward(params(head_size=256, prefill_kernel=2), big) == 2
     assert "4 GiB" in err()
+
+
+def test_quantized_cache_takes_the_decode_kernel():
+    # every token of a quantized forward runs on the decode kernel
+    pl = plan(params(**QUANT), paged(token_count=40, batch_size=4, **QUANT_KV))
+    assert pl["mode"] == "token" and pl["cache"] == "int8" and pl["prefill_grid"] == "(0,0)"
+    pl = plan(params(cache_dtype=2, k_quant_type=2, v_quant_type=2),
+              paged(token_count=40, batch_size=4, k_scale=FAKE, v_scale=FAKE))
+    assert pl["mode"] == "token" and pl["cache"] == "fp8e4m3fn"
+    assert plan(params(), paged())["cache"] == "fp16"
+    # path 2 (prefill kernel for multi-token requests) does not serve codes
+    assert call_forward(params(path=2, **QUANT), paged(**QUANT_KV)) == 2
+    assert "quantized caches" in err()
 
 
 def test_workspace_must_cover_the_plan():
