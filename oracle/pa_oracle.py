@@ -52,6 +52,22 @@ Readings where the pages are silent (each also listed in the design notes):
   rotary) and the division is one fp32 division: int8 saturates to
   ``[-128, 127]``, float8 e4m3fn (bias 7, no infinities, largest finite 448)
   to ``+-448``.
+* Attention sink (PagedAttention -- CUDA Design Document, §6.1): the head's
+  sink logit ``s_h`` joins the softmax denominator only,
+  ``p_i = e^(x_i - m) / (e^(s_h - m) + sum_j e^(x_j - m))`` with
+  ``m = max(s_h, max_j x_j)``; ``x`` is the score after scale and softcap
+  (the sink is a logit of its own and is neither scaled nor capped).
+  ``use_smooth_softmax`` without ``head_sink`` is a sink of 0 for every head
+  (the page's schema lists the attribute; its §6.1 says a sink only exists
+  when given, so the attribute is read as a zero-valued sink).
+* QK-Norm (PagedAttention -- CUDA Design Document, §7.1-§7.2): per head,
+  ``x * w / sqrt(mean(x^2) + eps)`` with one fp16 weight vector of
+  ``head_size`` shared by all heads, applied to Q and to the new K before
+  RoPE.  The prologue of §7.2 stages the normalized rows in an fp16 buffer
+  (§7.3), so the normalized value is rounded to fp16 before it is rotated
+  (and before K is quantized).  Computed here in fp64 (§7.1 asks for an fp32
+  sum of squares; the kernels' fp32 result may round to a neighbouring fp16
+  value, one unit in the last place).
 * Explicit write slots (PagedAttention -- CUDA Design Document, §5.2): slot
   ``s`` is block ``s // block_size``, offset ``s % block_size``; ``-1`` writes
   nothing.  The stored K is still rotated at the token's position
@@ -143,6 +159,21 @@ def rope_query_fp64(x: np.ndarray, pos: int, cos: np.ndarray, sin: np.ndarray,
         out[a] = float(x[a]) * c - float(x[b]) * s
         out[b] = float(x[b]) * c + float(x[a]) * s
     return out
+
+
+# ---------------------------------------------------------------------------
+# QK-Norm: PagedAttention -- CUDA Design Document, §7.1
+# ---------------------------------------------------------------------------
+
+QK_NORM_EPSILON = 1e-6     # §7.1 default
+
+
+def rms_norm_fp16(x16: np.ndarray, w16: np.ndarray, eps: float) -> np.ndarray:
+    """RMS-norm of one fp16 head row with an fp16 weight, in fp64, rounded
+    to fp16: ``x[c] * w[c] / sqrt(sum_j x[j]^2 / head_size + eps)``."""
+    x = x16.astype(np.float64)
+    r = 1.0 / math.sqrt(float(np.sum(x * x)) / x.shape[0] + float(eps))
+    return (x * r * w16.astype(np.float64)).astype(np.float16)
 
 
 # ---------------------------------------------------------------------------
@@ -262,13 +293,14 @@ def append_kv(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
               rotary_interleaved: bool = False, slot_mapping: Optional[np.ndarray] = None,
               cache_dtype: int = CACHE_FP16, k_quant_type: int = QUANT_NONE,
               v_quant_type: int = QUANT_NONE, k_scale: Optional[np.ndarray] = None,
-              v_scale: Optional[np.ndarray] = None):
+              v_scale: Optional[np.ndarray] = None, k_norm_weight: Optional[np.ndarray] = None,
+              qk_norm_epsilon: float = QK_NORM_EPSILON):
     """Return new ``(key_cache, value_cache)`` copies with every new token's
-    K (rotated if a rotary table is given) and V stored at its derived slot,
-    or at ``slot_mapping[t]`` when a mapping is given.  With a quantized
-    cache the stored rows are the codes of those fp16 rows (§8.4: quantized
-    as they are scattered).  Slots that no token maps to are left
-    byte-identical."""
+    K (RMS-normed with ``k_norm_weight`` if given, then rotated if a rotary
+    table is given; §7.2 order) and V stored at its derived slot, or at
+    ``slot_mapping[t]`` when a mapping is given.  With a quantized cache the
+    stored rows are the codes of those fp16 rows (§8.4: quantized as they
+    are scattered).  Slots that no token maps to are left byte-identical."""
     kc = key_cache.copy()
     vc = value_cache.copy()
     block_size = kc.shape[1]
@@ -290,6 +322,8 @@ def append_kv(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
         for h in range(Hkv):
             krow = key[t, h * D:(h + 1) * D]
             vrow = value[t, h * D:(h + 1) * D]
+            if k_norm_weight is not None:
+                krow = rms_norm_fp16(krow, k_norm_weight, qk_norm_epsilon)
             if cos_cache is not None:
                 krow = rope_key_fp16(krow, pos, cos_cache, sin_cache, rotary_interleaved)
             if cache_dtype != CACHE_FP16:
@@ -350,14 +384,20 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
             rotary_interleaved: bool = False, rows: Optional[Iterable[int]] = None,
             return_probs: bool = False, cache_dtype: int = CACHE_FP16,
             k_quant_type: int = QUANT_NONE, v_quant_type: int = QUANT_NONE,
-            k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None):
+            k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None,
+            head_sink: Optional[np.ndarray] = None, use_smooth_softmax: bool = False,
+            q_norm_weight: Optional[np.ndarray] = None,
+            qk_norm_epsilon: float = QK_NORM_EPSILON):
     """Attention output in fp64.
 
     ``key_cache``/``value_cache`` must already hold the new tokens (run
     :func:`append_kv` first); a quantized cache holds codes, which are
-    dequantized (``q * scale``, §8.3) as they are gathered.  Returns ``[T, H*D]`` for all tokens, or
-    ``[len(rows), H*D]`` in the given order when ``rows`` is set.  With
-    ``return_probs`` also returns ``{(t, h): probabilities over keys}``."""
+    dequantized (``q * scale``, §8.3) as they are gathered.  ``q_norm_weight``
+    RMS-norms each query head before RoPE (§7); ``head_sink`` (``[H]``) or
+    ``use_smooth_softmax`` adds a denominator-only logit per head (§6.1).
+    Returns ``[T, H*D]`` for all tokens, or ``[len(rows), H*D]`` in the
+    given order when ``rows`` is set.  With ``return_probs`` also returns
+    ``{(t, h): probabilities over keys}``."""
     T = query.shape[0]
     H, Hkv, D = num_heads, kv_num_heads, head_size
     g = H // Hkv
@@ -375,6 +415,12 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
         b, j = owner
         by_seq.setdefault(b, []).append((n, t, j))
 
+    sink = None
+    if head_sink is not None:
+        sink = np.asarray(head_sink).astype(np.float64).reshape(H)
+    elif use_smooth_softmax:
+        sink = np.zeros(H, np.float64)
+
     for b, items in by_seq.items():
         q_len = int(cum[b + 1]) - int(cum[b])
         kv_len = int(past[b]) + q_len
@@ -391,7 +437,12 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
         # queries [n_rows, H, D] in fp64, rotated at their position if asked
         Q = np.empty((len(items), H, D), np.float64)
         for r, (_, t, _) in enumerate(items):
-            qrow = query[t].astype(np.float64).reshape(H, D)
+            if q_norm_weight is not None:
+                qrow = np.stack([rms_norm_fp16(query[t, h * D:(h + 1) * D], q_norm_weight,
+                                               qk_norm_epsilon) for h in range(H)])
+                qrow = qrow.astype(np.float64)
+            else:
+                qrow = query[t].astype(np.float64).reshape(H, D)
             if cos_cache is not None:
                 for h in range(H):
                     qrow[h] = rope_query_fp64(qrow[h], positions[r], cos_cache, sin_cache,
@@ -409,9 +460,13 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
                 if not mask[r].any():
                     continue                                   # fully masked -> 0
                 m = S[r].max()
+                if sink is not None:
+                    m = max(m, sink[h])
                 e = np.exp(S[r] - m)
-                p = e / e.sum()
-                assert abs(p.sum() - 1.0) < 1e-12
+                den = e.sum() + (math.exp(sink[h] - m) if sink is not None else 0.0)
+                p = e / den
+                if sink is None:
+                    assert abs(p.sum() - 1.0) < 1e-12
                 O[r] = p @ V[:, kvh, :]
                 if return_probs:
                     probs[(items[r][1], h)] = p

@@ -807,3 +807,173 @@ def test_quantized_forward_is_attention_over_the_dequantized_cache(dtype):
         bound = step / 2 + 1e-12 if dtype == 1 else np.abs(x) / 16 + step * 2.0 ** -10
         inside = np.abs(x / step) <= (127 if dtype == 1 else 448)   # not saturated
         assert np.all(err[inside] <= bound[inside])
+
+
+# ---------------------------------------------------------------------------
+# attention sink (PagedAttention -- CUDA Design Document, §6.1-§6.2)
+# ---------------------------------------------------------------------------
+
+def _sink_case():
+    return _small_case(seed=11, softcap=4.0, local_window_size=9)
+
+
+def test_sink_is_an_exact_denominator_rescale():
+    """§6.2: with a sink only the denominator changes, so each (token, head)
+    output is the no-sink output times 1 / (1 + e^(s - l)), l the row's
+    log-sum-exp.  The ratio is constant over channels and its logit moves
+    one for one with the sink."""
+    w = _sink_case()
+    H, D = w.num_heads, w.head_size
+    base, _, _ = _oracle_on(w)
+    s1 = np.random.default_rng(4).uniform(-3, 3, H).astype(np.float16)
+    s2 = (s1.astype(np.float64) + 0.75).astype(np.float16)
+    o1, _, _ = _oracle_on(w, head_sink=s1)
+    o2, _, _ = _oracle_on(w, head_sink=s2)
+    for t in range(w.token_count):
+        for h in range(H):
+            b = base[t, h * D:(h + 1) * D]
+            big = np.abs(b) > 1e-3
+            r1 = o1[t, h * D:(h + 1) * D][big] / b[big]
+            r2 = o2[t, h * D:(h + 1) * D][big] / b[big]
+            assert np.ptp(r1) < 1e-12 and np.ptp(r2) < 1e-12
+            assert 0.0 < r1[0] < 1.0 and 0.0 < r2[0] < 1.0
+            lg1 = math.log(r1[0] / (1 - r1[0]))
+            lg2 = math.log(r2[0] / (1 - r2[0]))
+            assert abs((lg1 - lg2) - (float(s2[h]) - float(s1[h]))) < 1e-9
+
+
+def test_sink_of_minus_infinity_is_no_sink_and_a_huge_sink_empties_the_row():
+    w = _sink_case()
+    base, _, _ = _oracle_on(w)
+    off, _, _ = _oracle_on(w, head_sink=np.full(w.num_heads, -np.inf, np.float16))
+    assert np.array_equal(base, off)
+    big, _, _ = _oracle_on(w, head_sink=np.full(w.num_heads, 60000.0, np.float16))
+    assert np.max(np.abs(big)) < 1e-300
+
+
+def test_sink_reaches_only_its_own_head():
+    w = _sink_case()
+    H, D = w.num_heads, w.head_size
+    base, _, _ = _oracle_on(w)
+    s = np.full(H, -np.inf, np.float16)
+    s[1] = 0.5
+    out, _, _ = _oracle_on(w, head_sink=s)
+    for h in range(H):
+        same = np.array_equal(out[:, h * D:(h + 1) * D], base[:, h * D:(h + 1) * D])
+        assert same == (h != 1), h
+
+
+def test_smooth_softmax_is_a_zero_sink_for_every_head():
+    w = _sink_case()
+    a, _, _ = _oracle_on(w, use_smooth_softmax=True)
+    b, _, _ = _oracle_on(w, head_sink=np.zeros(w.num_heads, np.float16))
+    assert np.array_equal(a, b)
+    # an explicit sink takes precedence over the attribute
+    s = np.full(w.num_heads, -1.5, np.float16)
+    c, _, _ = _oracle_on(w, head_sink=s, use_smooth_softmax=True)
+    d, _, _ = _oracle_on(w, head_sink=s)
+    assert np.array_equal(c, d)
+
+
+def test_sink_with_one_visible_key_is_a_sigmoid_of_the_two_logits():
+    """A fresh request's first token sees only itself: o = v * e^x / (e^x +
+    e^s).  With s equal to that score the weight is exactly one half."""
+    w = _small_case(q_lens=[3], past=[0], num_heads=2, kv_num_heads=2, scale=0.25)
+    D = w.head_size
+    q = w.query[0].astype(np.float64).reshape(2, D)
+    k = w.key[0].astype(np.float64).reshape(2, D)
+    x = 0.25 * np.sum(q * k, axis=1)                 # the single score of each head
+    s = x.astype(np.float16)
+    out, _, _ = _oracle_on(w, head_sink=s)
+    v = w.value[0].astype(np.float64).reshape(2, D)
+    for h in range(2):
+        weight = 1.0 / (1.0 + math.exp(float(s[h]) - x[h]))
+        np.testing.assert_allclose(out[0, h * D:(h + 1) * D], weight * v[h], rtol=1e-12, atol=0)
+        assert abs(weight - 0.5) < 1e-3
+
+
+# ---------------------------------------------------------------------------
+# QK-Norm (PagedAttention -- CUDA Design Document, §7.1-§7.2)
+# ---------------------------------------------------------------------------
+
+def test_qk_norm_golden():
+    g = json.load(open(os.path.join(GOLDEN, "qk_norm.json")))
+    for row in g["rows"]:
+        x = np.array(row["x"], np.float16)
+        w = np.array(row["w"], np.float16)
+        y = oracle.rms_norm_fp16(x, w, row["eps"])
+        assert y.dtype == np.float16
+        assert np.array_equal(y.astype(np.float64), np.array(row["y"], np.float64)), row["why"]
+
+
+def _ulps(a16, b16):
+    ia = a16.view(np.int16).astype(np.int32)
+    ib = b16.view(np.int16).astype(np.int32)
+    ia = np.where(ia < 0, -32768 - ia, ia)            # monotone integer order
+    ib = np.where(ib < 0, -32768 - ib, ib)
+    return np.abs(ia - ib)
+
+
+def test_qk_norm_unit_weight_gives_unit_mean_square_and_is_scale_free():
+    rng = np.random.default_rng(21)
+    for D in (64, 128, 256):
+        x = (rng.standard_normal(D) * 3).astype(np.float16)
+        one = np.ones(D, np.float16)
+        y = oracle.rms_norm_fp16(x, one, 1e-6).astype(np.float64)
+        assert abs(np.mean(y * y) - 1.0) < 2e-3
+        # the direction of x is kept: y is x over a positive constant
+        ratio = y[np.abs(x) > 0.1] / x[np.abs(x) > 0.1].astype(np.float64)
+        assert np.ptp(ratio) / ratio.mean() < 2e-3 and ratio.min() > 0
+        for k in (-3, 4):                             # exact power-of-two rescale
+            y2 = oracle.rms_norm_fp16((x * np.float16(2.0 ** k)).astype(np.float16), one, 1e-6)
+            assert np.max(_ulps(y2, y.astype(np.float16))) <= 1
+
+
+def test_qk_norm_weight_is_per_channel_and_shared_by_heads():
+    rng = np.random.default_rng(22)
+    D = 64
+    x = rng.standard_normal(D).astype(np.float16)
+    w = rng.uniform(0.5, 2.0, D).astype(np.float16)
+    y1 = oracle.rms_norm_fp16(x, np.ones(D, np.float16), 1e-6).astype(np.float64)
+    y = oracle.rms_norm_fp16(x, w, 1e-6).astype(np.float64)
+    np.testing.assert_allclose(y, y1 * w.astype(np.float64), rtol=2e-3, atol=1e-6)
+
+
+def _norm_rows(x, w, heads, D, eps=1e-6):
+    return np.stack([np.concatenate([oracle.rms_norm_fp16(r[h * D:(h + 1) * D], w, eps)
+                                     for h in range(heads)]) for r in x])
+
+
+@pytest.mark.parametrize("rot", [0, 1])
+def test_append_normalizes_k_before_rope(rot):
+    kw = dict(do_rotary=1, rotary_dim=16) if rot else {}
+    w = _small_case(seed=23, **kw)
+    kc = w.pool_blocks(0, range(w.num_blocks))
+    vc = w.pool_blocks(1, range(w.num_blocks))
+    kn = np.random.default_rng(5).uniform(0.5, 1.5, w.head_size).astype(np.float16)
+    a = _append(w, kc, vc, k_norm_weight=kn)
+    key0 = w.key
+    w.key = _norm_rows(key0, kn, w.kv_num_heads, w.head_size)
+    b = _append(w, kc, vc)
+    w.key = key0
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    if rot:   # the other order (rotate, then norm) stores something else
+        r = _append(w, kc, vc)[0]
+        pos = [(bb, int(w.past[bb]) + j) for bb in range(w.batch_size)
+               for j in range(int(w.cum[bb + 1] - w.cum[bb]))]
+        rows_a = np.stack([a[0][w.block_table[bb, p // 16], p % 16] for bb, p in pos])
+        rows_r = np.stack([np.stack([oracle.rms_norm_fp16(h, kn, 1e-6) for h in
+                                     r[w.block_table[bb, p // 16], p % 16]]) for bb, p in pos])
+        assert not np.array_equal(rows_a, rows_r)
+
+
+def test_forward_normalizes_q_before_rope_and_composes_with_the_sink():
+    w = _small_case(seed=24, do_rotary=1, rotary_dim=16, softcap=3.0)
+    qn = np.random.default_rng(6).uniform(0.5, 1.5, w.head_size).astype(np.float16)
+    sink = np.random.default_rng(7).uniform(-1, 1, w.num_heads).astype(np.float16)
+    a, _, _ = _oracle_on(w, q_norm_weight=qn, head_sink=sink)
+    q0 = w.query
+    w.query = _norm_rows(q0, qn, w.num_heads, w.head_size)
+    b, _, _ = _oracle_on(w, head_sink=sink)
+    w.query = q0
+    assert np.array_equal(a, b)
