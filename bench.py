@@ -9,6 +9,7 @@ already resident in device memory when the timed region starts.
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
                     [--copy-calibration-mib N]
                     [--cache int8|fp8 [--k-quant tensor|channel] [--v-quant tensor|channel]]
+                    [--head-sink | --smooth-softmax] [--qk-norm]
     python bench.py --summarize-pmc counter_collection.csv ...
 
 Prints ONE JSON line.  ``value`` is the decode KV throughput of the whole
@@ -105,12 +106,13 @@ def kernel_source_hash(kind: str) -> str:
 
 
 def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=1024,
-                 target_seconds=10.0, quant=None):
+                 target_seconds=10.0, quant=None, feat=None):
     """fp64 oracle on a bounded sample of the workload: the decode requests
     (GB/s of decode K/V bytes) or, for a prefill-only batch, the last rows of
     the first request (GFLOP/s).  Also returns the max-abs error of the GPU
     rows the sample covers.  ``quant`` = (cache dtype, K quant type, V quant
-    type, K scales, V scales) runs it on the quantized pool."""
+    type, K scales, V scales) runs it on the quantized pool; ``feat`` holds
+    the sink / QK-Norm inputs (host arrays) of the GPU run."""
     import threadpoolctl
 
     import oracle
@@ -130,9 +132,18 @@ def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=1024,
         vc = sub.pool_blocks(wl.KIND_V, range(sub.num_blocks))
     rot = dict(cos_cache=sub.cos_cache, sin_cache=sub.sin_cache,
                rotary_interleaved=bool(sub.rotary_interleaved)) if sub.do_rotary else {}
+    feat = feat or {}
+    akw, fkw = {}, {}
+    if "k_norm_weight" in feat:
+        akw = dict(k_norm_weight=feat["k_norm_weight"], qk_norm_epsilon=feat["qk_norm_epsilon"])
+        fkw = dict(q_norm_weight=feat["q_norm_weight"], qk_norm_epsilon=feat["qk_norm_epsilon"])
+    if "head_sink" in feat:
+        fkw["head_sink"] = feat["head_sink"]
+    if feat.get("use_smooth_softmax"):
+        fkw["use_smooth_softmax"] = True
     nk, nv = oracle.append_kv(kc, vc, sub.key, sub.value, sub.cum, sub.past, sub.block_table,
                               kv_num_heads=sub.kv_num_heads, head_size=sub.head_size, **rot,
-                              **qkw)
+                              **qkw, **akw)
     threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
                   if i.get("user_api") == "blas") or 1
     rows = None
@@ -146,7 +157,8 @@ def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=1024,
         ref = oracle.forward(sub.query, nk, nv, sub.cum, sub.past, sub.block_table,
                              num_heads=sub.num_heads, kv_num_heads=sub.kv_num_heads,
                              head_size=sub.head_size, scale=sub.scale, softcap=sub.softcap,
-                             local_window_size=sub.local_window_size, rows=rows, **rot, **qkw)
+                             local_window_size=sub.local_window_size, rows=rows, **rot, **qkw,
+                             **fkw)
         reps += 1
         if time.perf_counter() - t0 >= target_seconds:
             break
@@ -257,6 +269,11 @@ def main():
                     help="element type of the paged pools (int8 / fp8: codes + fp32 scales)")
     ap.add_argument("--k-quant", choices=("tensor", "channel"), default="channel")
     ap.add_argument("--v-quant", choices=("tensor", "channel"), default="channel")
+    ap.add_argument("--head-sink", action="store_true",
+                    help="a sink logit per head (drawn from U[-2, 3])")
+    ap.add_argument("--smooth-softmax", action="store_true", help="a zero sink for every head")
+    ap.add_argument("--qk-norm", action="store_true",
+                    help="QK-Norm of Q and new K with drawn weights (U[0.5, 1.5]), eps 1e-6")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain fp16 copy kernel over this many MiB (read N, "
                          "write N), three times, to scale HBM byte counters")
@@ -318,11 +335,23 @@ def main():
         quant = (cd, kq, vq, ks, vs)
         sc = dict(k_scale=torch.from_numpy(ks).cuda(), v_scale=torch.from_numpy(vs).cuda())
     dev = wl.to_device(w, cache_dtype=cd)
+    feat = {}
+    frng = np.random.default_rng([w.seed, 31])
+    if args.head_sink:
+        feat["head_sink"] = torch.from_numpy(
+            frng.uniform(-2.0, 3.0, w.num_heads).astype(np.float16)).cuda()
+    if args.smooth_softmax:
+        feat["use_smooth_softmax"] = 1
+    if args.qk_norm:
+        for k in ("q_norm_weight", "k_norm_weight"):
+            feat[k] = torch.from_numpy(frng.uniform(0.5, 1.5, w.head_size).astype(np.float16)).cuda()
+        feat["qk_norm_epsilon"] = 1e-6
     a = pa.Attn(num_heads=w.num_heads, kv_num_heads=w.kv_num_heads, head_size=w.head_size,
                 block_size=w.block_size, scale=w.scale, softcap=w.softcap,
                 local_window_size=w.local_window_size, do_rotary=w.do_rotary,
                 rotary_interleaved=w.rotary_interleaved, cache_dtype=cd,
-                k_quant_type=quant[1] if quant else 0, v_quant_type=quant[2] if quant else 0)
+                k_quant_type=quant[1] if quant else 0, v_quant_type=quant[2] if quant else 0,
+                **feat)
     T = w.token_count
     out = torch.empty((T, w.num_heads * w.head_size), dtype=torch.float16, device="cuda")
     nws = pa.forward_workspace_bytes(a, dev["key_cache"], dev["value_cache"], dev["block_table"],
@@ -358,7 +387,7 @@ def main():
     pa.timing_enable(8 * args.steps + 16)
     ms_step_instrumented = timed(args.steps) / args.steps
     stages = {s: pa.timing_read(s)
-              for s in ("append", "decode", "merge", "prefill", "prefill_merge", "plan")}
+              for s in ("append", "decode", "merge", "prefill", "prefill_merge", "plan", "q_norm")}
     pa.timing_disable()
 
     # the append alone, with derived slots (from the steps above) and with an
@@ -392,6 +421,9 @@ def main():
               "slot_mapping_us": round(slots_ms / slots_n * 1e3, 3) if slots_n else None,
               "slot_mapping_gbs": round(app_bytes / (slots_ms / slots_n * 1e-3) / 1e9, 1)
               if slots_n else None}
+    if per["q_norm"]:   # the QK-Norm prologue: Q read and staged once
+        kernels["q_norm_gbs"] = round(2 * T * w.num_heads * w.head_size * 2 /
+                                      (per["q_norm"] * 1e-6) / 1e9, 1)
     if per["decode"]:
         kernels["decode_kernel_gbs"] = round(dec_bytes / (per["decode"] * 1e-6) / 1e9, 1)
     if per["prefill"] and pf_flops:
@@ -421,7 +453,9 @@ def main():
 
     cpu, err = (None, None)
     if not args.no_cpu_baseline:
-        cpu, err = cpu_baseline(w, out.cpu().numpy(), quant=quant)
+        cpu, err = cpu_baseline(w, out.cpu().numpy(), quant=quant,
+                                feat={k: (v.cpu().numpy() if hasattr(v, "cpu") else v)
+                                      for k, v in feat.items()})
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
@@ -434,6 +468,9 @@ def main():
                    "cache": args.cache,
                    "k_quant": args.k_quant if quant else "none",
                    "v_quant": args.v_quant if quant else "none",
+                   "head_sink": "drawn" if args.head_sink else
+                   ("zero (smooth softmax)" if args.smooth_softmax else "none"),
+                   "qk_norm": bool(args.qk_norm),
                    "decode_requests": n_dec, "decode_bytes": dec_bytes,
                    "prefill_flops": pf_flops, "plan": plan},
         "roofline": roof,

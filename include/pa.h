@@ -79,6 +79,22 @@ typedef struct {
   int32_t k_quant_type;       /* PA_QUANT_NONE (0), PA_QUANT_PER_TENSOR (1) or
                                  PA_QUANT_PER_CHANNEL (2) for the K cache            */
   int32_t v_quant_type;       /* the same for the V cache (chosen independently)    */
+  const void *head_sink;      /* NULL, or DEVICE fp16 [num_heads], 2-byte aligned: the
+                                 sink logit s_h of each head, which joins the softmax
+                                 denominator only (section 6.1):
+                                 p_i = e^(x_i - m) / (e^(s_h - m) + sum_j e^(x_j - m)),
+                                 x the score after scale and softcap; finite or -inf */
+  int32_t use_smooth_softmax; /* 0/1: with head_sink NULL, a sink of 0 for every head
+                                 (an explicit head_sink takes precedence)           */
+  const void *q_norm_weight;  /* NULL, or DEVICE fp16 [head_size], 16-byte aligned:
+                                 QK-Norm weight of Q (section 7.1), shared by heads  */
+  const void *k_norm_weight;  /* the same for the new K (pa_append_kv); both weights or
+                                 neither; head_size 64, 128 or 256.  Each head row x
+                                 becomes fp16(x * w / sqrt(mean(x^2) + eps)), sum of
+                                 squares in fp32, before RoPE (section 7.2); cached K
+                                 is stored normalized, and pa_forward stages the
+                                 normalized Q in its workspace                       */
+  float qk_norm_epsilon;      /* 0 -> 1e-6 (section 7.1 default); else finite, > 0    */
 } pa_attn_params;
 
 /* Quantized caches (PagedAttention -- CUDA Design Document, section 8).
@@ -146,7 +162,9 @@ typedef struct {
  * Token t of request b (cum[b] <= t < cum[b+1], j = t - cum[b]) at position
  * p = past[b] + j is written to block block_table[b][p / block_size], offset
  * p % block_size, for every kv head.  With rotary the stored K is
- * fp16(fp32(x*cos - y*sin)) of its channel pair.  Tokens t >= cum[batch_size]
+ * fp16(fp32(x*cos - y*sin)) of its channel pair.  With params->k_norm_weight
+ * the K row is first RMS-normed to fp16 (section 7.2: norm, then RoPE, then
+ * write; a quantized cache stores the codes of the result).  Tokens t >= cum[batch_size]
  * write nothing; every other slot keeps its bytes.  Enqueue before
  * pa_forward on the same stream.
  *
@@ -174,7 +192,9 @@ pa_status pa_append_kv(const pa_attn_params *params, const pa_paged_kv *kv,
  *                         past + new length
  * (PagedAttention -- CUDA Design Document, section 4.7: bounds only size
  * launches and workspace, never a mask; 0 falls back to token_count and to
- * max_blocks_per_seq * block_size; over-large bounds are clamped.)
+ * max_blocks_per_seq * block_size; over-large bounds are clamped.)  With
+ * QK-Norm the workspace also stages the normalized queries, token_count *
+ * num_heads * head_size fp16 (section 7.3).
  */
 pa_status pa_forward_workspace_bytes(const pa_attn_params *params, const pa_paged_kv *kv,
                                      int32_t max_query_len_bound, int32_t max_kv_len_bound,
@@ -226,10 +246,11 @@ pa_status pa_describe_plan(const pa_attn_params *params, const pa_paged_kv *kv,
  * per stage (synchronizing on the recorded events).  Enabling creates the
  * events (2 * max_launches); it is not meant for graph capture.
  *   stage: 0 = append, 1 = decode, 2 = decode split merge, 3 = prefill,
- *          4 = decode work-list planning, 5 = prefill piece merge.
+ *          4 = decode work-list planning, 5 = prefill piece merge,
+ *          6 = QK-Norm prologue of the queries.
  */
 enum { PA_STAGE_APPEND = 0, PA_STAGE_DECODE = 1, PA_STAGE_MERGE = 2, PA_STAGE_PREFILL = 3,
-       PA_STAGE_PLAN = 4, PA_STAGE_PREFILL_MERGE = 5, PA_NUM_STAGES = 6 };
+       PA_STAGE_PLAN = 4, PA_STAGE_PREFILL_MERGE = 5, PA_STAGE_Q_NORM = 6, PA_NUM_STAGES = 7 };
 pa_status pa_timing_enable(int32_t max_launches);
 pa_status pa_timing_disable(void);
 pa_status pa_timing_read(int32_t stage, double *total_ms, int32_t *launches);

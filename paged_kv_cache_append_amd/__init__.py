@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import ctypes
 from dataclasses import dataclass
-from typing import Optional
+from typing import Any, Optional
 
 from . import _lib
 
@@ -53,14 +53,25 @@ class Attn:
     cache_dtype: int = CACHE_FP16
     k_quant_type: int = QUANT_NONE
     v_quant_type: int = QUANT_NONE
+    head_sink: Any = None           # fp16 device tensor [num_heads] or None
+    use_smooth_softmax: int = 0
+    q_norm_weight: Any = None       # fp16 device tensors [head_size] or None (both or neither)
+    k_norm_weight: Any = None
+    qk_norm_epsilon: float = 0.0    # 0 -> 1e-6
 
     def c(self) -> _lib.AttnParams:
+        import torch
+        _need(self.head_sink, "head_sink", torch.float16, (self.num_heads,))
+        _need(self.q_norm_weight, "q_norm_weight", torch.float16, (self.head_size,))
+        _need(self.k_norm_weight, "k_norm_weight", torch.float16, (self.head_size,))
         return _lib.AttnParams(self.num_heads, self.kv_num_heads, self.head_size,
                                self.block_size, float(self.scale), float(self.softcap),
                                self.local_window_size, self.do_rotary,
                                self.rotary_interleaved, self.path, self.split_tokens,
                                self.prefill_pieces, self.prefill_kernel, self.cache_dtype,
-                               self.k_quant_type, self.v_quant_type)
+                               self.k_quant_type, self.v_quant_type, _ptr(self.head_sink),
+                               self.use_smooth_softmax, _ptr(self.q_norm_weight),
+                               _ptr(self.k_norm_weight), float(self.qk_norm_epsilon))
 
 
 def library_path() -> str:

@@ -12,7 +12,8 @@ PA_ERR_INVALID_ARGUMENT = 1
 PA_ERR_UNSUPPORTED = 2
 PA_ERR_DEVICE = 3
 
-STAGES = {"append": 0, "decode": 1, "merge": 2, "prefill": 3, "plan": 4, "prefill_merge": 5}
+STAGES = {"append": 0, "decode": 1, "merge": 2, "prefill": 3, "plan": 4, "prefill_merge": 5,
+          "q_norm": 6}
 
 EXPORTED = ("pa_append_kv", "pa_forward_workspace_bytes", "pa_forward", "pa_last_error",
             "pa_describe_plan", "pa_timing_enable", "pa_timing_disable", "pa_timing_read")
@@ -26,7 +27,10 @@ class AttnParams(ctypes.Structure):
                 ("rotary_interleaved", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("split_tokens", ctypes.c_int32), ("prefill_pieces", ctypes.c_int32),
                 ("prefill_kernel", ctypes.c_int32), ("cache_dtype", ctypes.c_int32),
-                ("k_quant_type", ctypes.c_int32), ("v_quant_type", ctypes.c_int32)]
+                ("k_quant_type", ctypes.c_int32), ("v_quant_type", ctypes.c_int32),
+                ("head_sink", ctypes.c_void_p), ("use_smooth_softmax", ctypes.c_int32),
+                ("q_norm_weight", ctypes.c_void_p), ("k_norm_weight", ctypes.c_void_p),
+                ("qk_norm_epsilon", ctypes.c_float)]
 
 
 class PagedKV(ctypes.Structure):

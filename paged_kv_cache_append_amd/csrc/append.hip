@@ -14,6 +14,11 @@
 // mapping the slot is read, not derived (-1: no write); the request is then
 // only looked up for the rotary position.
 //
+// QK-Norm (section 7.2: normalize, then RoPE, then write): the lanes of one
+// (token, kv head) row are D/8 consecutive, aligned lanes of a wave; they sum
+// their squares across the group before any lane leaves for lack of a slot,
+// normalize their own chunk, and normalize the partner chunk RoPE reads.
+//
 // Quantized caches (section 8.4, write path): the lane turns its 8 channels
 // -- after rotary, as fp16, exactly the values an fp16 cache would hold --
 // into 8 byte codes with the channels' fp32 scales and stores 8 bytes.
@@ -32,6 +37,13 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     const int rem = (int)(it - (int64_t)t * per_tok);
     const int kvh = rem / chunks;
     const int c = rem - kvh * chunks;
+    const int64_t src_row = (int64_t)t * a.kv_heads * a.head_size + (int64_t)kvh * a.head_size;
+    u32x4 k = load16(a.key + src_row + 8 * c);
+    float nr = 0.f;
+    if (a.k_norm) {
+      nr = rms_inverse(group_sum(sum_squares8(k), chunks), a.head_size, a.norm_eps);
+      k = norm_chunk(k, nr, a.k_norm, c);
+    }
     int64_t blk;
     int off, pos = -1;
     if (a.slot_mapping) {
@@ -56,13 +68,11 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
       off = pos & (bs - 1);
     }
     const int64_t dst = slot_base(blk, off, kvh, bs, a.kv_heads, a.head_size) + 8 * c;
-    const int64_t src_row = (int64_t)t * a.kv_heads * a.head_size + (int64_t)kvh * a.head_size;
     const u32x4 v = load16(a.value + src_row + 8 * c);
-    u32x4 k = load16(a.key + src_row + 8 * c);
     if (a.rotary_dim > 0 && 8 * c < a.rotary_dim) {
       float r[8];
       rotate_chunk(a.key + src_row, k, c, pos, a.cos, a.sin, a.rotary_dim,
-                   a.rotary_interleaved, a.rotary_rows, r);
+                   a.rotary_interleaved, a.rotary_rows, r, nr, a.k_norm);
       k = pack8(r);
     }
     if (a.cache_dtype == kCacheF16) {
@@ -78,6 +88,32 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
           quantize8(k, a.cache_dtype, sk);
     }
   }
+}
+
+// The prologue of a forward with QK-Norm (section 7.2-7.3): every query head
+// row normalized into an fp16 staging buffer, which the attention kernels
+// then read (and rotate) in place of the query.  One lane per 8 channels;
+// the D/8 lanes of a row are consecutive and aligned.
+__global__ __launch_bounds__(256) void q_norm_kernel(const QNormArgs a) {
+  const int chunks = a.head_size >> 3;
+  const int64_t items = a.rows * chunks;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += stride) {
+    const int64_t row = it / chunks;
+    const int c = (int)(it - row * chunks);
+    const u32x4 x = load16(a.in + row * a.head_size + 8 * c);
+    const float r = rms_inverse(group_sum(sum_squares8(x), chunks), a.head_size, a.eps);
+    store16(a.out + row * a.head_size + 8 * c, norm_chunk(x, r, a.weight, c));
+  }
+}
+
+hipError_t launch_q_norm(const QNormArgs& a, hipStream_t st) {
+  const int64_t items = a.rows * (a.head_size >> 3);
+  if (items == 0) return hipSuccess;
+  int64_t blocks = (items + 255) / 256;
+  if (blocks > (1 << 20)) blocks = 1 << 20;
+  launch_kernel(q_norm_kernel, dim3((unsigned)blocks), dim3(256), st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {

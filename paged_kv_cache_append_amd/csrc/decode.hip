@@ -493,7 +493,8 @@ void decode_kernel(const DecodeArgs a) {
         }
       }
       if (r.nsplit <= 1) {
-        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        const float den = sink_denominator(lt, m, a.use_sink, a.head_sink, h);
+        const float inv = den > 0.f ? 1.0f / den : 0.f;
         uint16_t* orow = a.out + (int64_t)r.t * HD + (int64_t)h * D;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
@@ -563,6 +564,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
     den += w * a.part_ml[2 * (base + s) + 1];
   }
   den = block_reduce(den, false, s_tmp);   // (its barriers also publish s_w)
+  den = sink_denominator(den, M, a.use_sink, a.head_sink, h);
   const int nq = D >> 2;                   // 4-channel groups
   const int dq = tid % nq;
   const int sg = tid / nq;

@@ -119,6 +119,37 @@ pa_status check_quant(const pa_attn_params* p, const pa_paged_kv* kv) {
   return PA_OK;
 }
 
+// Attention sink and QK-Norm (PagedAttention -- CUDA Design Document,
+// section 6.4 and section 7.4: both norm weights or neither, epsilon > 0).
+pa_status check_sink_norm(const pa_attn_params* p) {
+  if (p->use_smooth_softmax != 0 && p->use_smooth_softmax != 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "use_smooth_softmax: expected 0 or 1, got %d",
+                p->use_smooth_softmax);
+  if ((reinterpret_cast<uintptr_t>(p->head_sink) & 1) != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "head_sink: expected 2-byte alignment");
+  if ((p->q_norm_weight == nullptr) != (p->k_norm_weight == nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "q_norm_weight/k_norm_weight: expected both or neither");
+  if (!aligned16(p->q_norm_weight) || !aligned16(p->k_norm_weight))
+    return fail(PA_ERR_INVALID_ARGUMENT, "q_norm_weight/k_norm_weight: expected 16-byte alignment");
+  if (!std::isfinite(p->qk_norm_epsilon) || p->qk_norm_epsilon < 0.f)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "qk_norm_epsilon: expected 0 (default 1e-6) or a finite value > 0, got %g",
+                (double)p->qk_norm_epsilon);
+  return PA_OK;
+}
+
+// QK-Norm sums a head row's squares across D/8 lanes of a wave.
+pa_status check_norm_support(const pa_attn_params* p) {
+  if (p->k_norm_weight && p->head_size != 64 && p->head_size != 128 && p->head_size != 256)
+    return fail(PA_ERR_UNSUPPORTED, "QK-Norm with head_size %d: served for 64, 128 and 256",
+                p->head_size);
+  return PA_OK;
+}
+
+float norm_epsilon(const pa_attn_params* p) {
+  return p->qk_norm_epsilon > 0.f ? p->qk_norm_epsilon : 1e-6f;
+}
+
 pa_status check_common(const pa_attn_params* p, const pa_paged_kv* kv) {
   if (!p) return fail(PA_ERR_INVALID_ARGUMENT, "params: expected non-NULL");
   if (!kv) return fail(PA_ERR_INVALID_ARGUMENT, "kv: expected non-NULL");
@@ -187,6 +218,8 @@ pa_status check_common(const pa_attn_params* p, const pa_paged_kv* kv) {
   if (!kv->cumulative_sequence_length)
     return fail(PA_ERR_INVALID_ARGUMENT, "cumulative_sequence_length: expected non-NULL");
   if (!kv->past_seqlens) return fail(PA_ERR_INVALID_ARGUMENT, "past_seqlens: expected non-NULL");
+  pa_status st = check_sink_norm(p);
+  if (st != PA_OK) return st;
   return check_quant(p, kv);
 }
 
@@ -253,6 +286,8 @@ struct Plan {
   int prefill_chunks = 1;    // key-range pieces per prefill tile
   size_t off_ml = 0, off_entries = 0, off_count = 0;
   size_t off_pf_o = 0, off_pf_ml = 0;
+  size_t off_qn = 0;         // QK-Norm: normalized queries, fp16 [T, H*D]
+  bool q_norm = false;
   size_t ws_bytes = 0;
 };
 
@@ -325,6 +360,11 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
       pl.off_pf_ml = pl.off_pf_o + align256(rows * p->head_size * sizeof(float));
       cur = pl.off_pf_ml + align256(rows * 2 * sizeof(float));
     }
+  }
+  if (p->q_norm_weight) {
+    pl.q_norm = true;
+    pl.off_qn = cur;
+    cur += align256((size_t)T * p->num_heads * p->head_size * sizeof(uint16_t));
   }
   pl.ws_bytes = cur;
   return pl;
@@ -420,6 +460,7 @@ pa_status pa_append_kv(const pa_attn_params* params, const pa_paged_kv* kv, cons
   if ((st = check_rotary(params, kv, cos_cache, sin_cache, rotary_rows, rotary_dim)) != PA_OK)
     return st;
   if (kv->token_count == 0) return PA_OK;
+  if ((st = check_norm_support(params)) != PA_OK) return st;
   if (!key || !value) return fail(PA_ERR_INVALID_ARGUMENT, "key/value: expected non-NULL");
   if (!aligned16(key) || !aligned16(value))
     return fail(PA_ERR_INVALID_ARGUMENT, "key/value: expected 16-byte alignment");
@@ -444,6 +485,8 @@ pa_status pa_append_kv(const pa_attn_params* params, const pa_paged_kv* kv, cons
   a.v_quant = params->v_quant_type;
   a.k_scale = kv->k_scale;
   a.v_scale = kv->v_scale;
+  a.k_norm = static_cast<const uint16_t*>(params->k_norm_weight);
+  a.norm_eps = norm_epsilon(params);
   hipStream_t s = static_cast<hipStream_t>(stream);
   StageScope scope(PA_STAGE_APPEND, s);
   return device_status(pa::launch_append(a, s), "append kernel launch");
@@ -474,14 +517,16 @@ pa_status pa_describe_plan(const pa_attn_params* params, const pa_paged_kv* kv, 
   const Plan pl = make_plan(params, kv, mq, mk);
   snprintf(buf, len,
            "mode=%s cache=%s rows=%d head_chunks=%d g=%d chunk_heads=%d split_tokens=%d "
-           "max_splits=%d listed=%d prefill_grid=(%d,%d) prefill_chunks=%d workspace=%zu",
+           "max_splits=%d listed=%d prefill_grid=(%d,%d) prefill_chunks=%d q_norm=%d "
+           "workspace=%zu",
            pl.token_mode ? "token" : "request",
            params->cache_dtype == PA_CACHE_INT8  ? "int8"
            : params->cache_dtype == PA_CACHE_FP8_E4M3FN ? "fp8e4m3fn"
                                                        : "fp16", pl.rows, params->kv_num_heads * pl.head_chunks,
            pl.g, pl.chunk_heads, pl.split_tokens, pl.max_splits, pl.listed ? 1 : 0,
            pl.prefill ? pl.prefill_tiles * pl.prefill_chunks + 1 : 0,
-           pl.prefill ? params->kv_num_heads : 0, pl.prefill ? pl.prefill_chunks : 0, pl.ws_bytes);
+           pl.prefill ? params->kv_num_heads : 0, pl.prefill ? pl.prefill_chunks : 0,
+           pl.q_norm ? 1 : 0, pl.ws_bytes);
   return PA_OK;
 }
 
@@ -498,6 +543,7 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     return fail(PA_ERR_INVALID_ARGUMENT, "max_query_len_bound/max_kv_len_bound: expected >= 0");
   if (kv->token_count == 0) return PA_OK;
   if ((st = check_kernel_support(params, kv)) != PA_OK) return st;
+  if ((st = check_norm_support(params)) != PA_OK) return st;
   if (!query) return fail(PA_ERR_INVALID_ARGUMENT, "query: expected non-NULL");
   if (!out) return fail(PA_ERR_INVALID_ARGUMENT, "out: expected non-NULL");
   if (!aligned16(query) || !aligned16(out))
@@ -553,6 +599,23 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
   d.v_quant = params->v_quant_type;
   d.k_scale = kv->k_scale;
   d.v_scale = kv->v_scale;
+  d.head_sink = static_cast<const uint16_t*>(params->head_sink);
+  d.use_sink = params->head_sink || params->use_smooth_softmax ? 1 : 0;
+  // QK-Norm prologue (section 7.2): normalized queries staged in the
+  // workspace; every attention kernel reads (and rotates) them from there
+  if (pl.q_norm) {
+    pa::QNormArgs qa;
+    qa.in = static_cast<const uint16_t*>(query);
+    qa.out = reinterpret_cast<uint16_t*>(ws + pl.off_qn);
+    qa.rows = (int64_t)kv->token_count * params->num_heads;
+    qa.head_size = D;
+    qa.weight = static_cast<const uint16_t*>(params->q_norm_weight);
+    qa.eps = norm_epsilon(params);
+    StageScope scope(PA_STAGE_Q_NORM, s);
+    if ((st = device_status(pa::launch_q_norm(qa, s), "QK-Norm prologue launch")) != PA_OK)
+      return st;
+    d.query = qa.out;
+  }
 
   // prefill first, on the side stream when decode rows run beside it; the
   // side stream forks before the plan kernel, which only the decode needs
@@ -621,6 +684,8 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     f.rows16 = params->prefill_kernel == 2 ||
                (params->prefill_kernel == 0 && rows16_prefill_fits(params, kv));
     f.pool32 = pool_fits_32bit(params, kv) ? 1 : 0;
+    f.head_sink = d.head_sink;
+    f.use_sink = d.use_sink;
     const dim3 grid(pl.prefill_tiles * pl.prefill_chunks + 1, params->kv_num_heads);
     {
       StageScope scope(PA_STAGE_PREFILL, ps);
@@ -666,6 +731,8 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
       mg.split_tokens = pl.split_tokens;
       mg.max_splits = pl.max_splits;
       mg.window = params->local_window_size;
+      mg.head_sink = d.head_sink;
+      mg.use_sink = d.use_sink;
       StageScope scope(PA_STAGE_MERGE, s);
       if ((st = device_status(pa::launch_merge(mg, s), "merge kernel launch")) != PA_OK)
         return joined(st);

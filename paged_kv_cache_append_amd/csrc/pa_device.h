@@ -74,8 +74,58 @@ __device__ __forceinline__ int64_t slot_base(int64_t blk, int off, int kvh, int 
   return ((blk * block_size + off) * kv_heads + kvh) * (int64_t)head_size;
 }
 
+// ---- QK-Norm (PagedAttention -- CUDA Design Document, section 7.1) -------
+// x[c] * w[c] / sqrt(mean_j x[j]^2 + eps) per head, the sum of squares in
+// fp32; the result is rounded to fp16 (the staged fp16 rows of section 7.3).
+
+// Sum over the `group` consecutive lanes (a power of two <= 64, aligned)
+// that hold one head row; every lane of the group must be active.
+__device__ __forceinline__ float group_sum(float v, int group) {
+  for (int m = 1; m < group; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float sum_squares8(u32x4 x) {
+  uint16_t h[8];
+  __builtin_memcpy(h, &x, 16);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(h2f(h[e]), h2f(h[e]), ss);
+  return ss;
+}
+
+// 1 / sqrt(sum of squares / head_size + eps), correctly rounded steps.
+__device__ __forceinline__ float rms_inverse(float ss, int head_size, float eps) {
+  return 1.0f / __builtin_sqrtf(ss / (float)head_size + eps);
+}
+
+// One fp16 value normalized: fp16(x * r * w).
+__device__ __forceinline__ float norm_value(float x, float r, uint16_t w) {
+  return (float)(_Float16)(x * r * h2f(w));
+}
+
+// Chunk [8c, 8c + 8) of a head row normalized with inverse rms r and weight w.
+__device__ __forceinline__ u32x4 norm_chunk(u32x4 x, float r, const uint16_t* w, int c) {
+  uint16_t h[8], wv[8];
+  const u32x4 wc = load16(w + 8 * c);
+  __builtin_memcpy(h, &x, 16);
+  __builtin_memcpy(wv, &wc, 16);
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = norm_value(h2f(h[e]), r, wv[e]);
+  u32x4 out;
+  uint16_t o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = f2h(f[e]);
+  __builtin_memcpy(&out, o, 16);
+  return out;
+}
+
 // Rotary embedding of channels [8c, 8c+8) of one head row at position `pos`.
 // `row` points at channel 0 of the head (global fp16), `own` holds the chunk.
+// With a norm weight `nw` (QK-Norm before RoPE) the row in memory is the
+// raw one: partner values read from it are normalized with (nr, nw) first,
+// and `own` must already be normalized.
 // Pairs are (i, i + r/2) (rotate-half) or (2i, 2i+1) (interleaved) with angle
 // index i; first' = x*cos - y*sin, second' = y*cos + x*sin; channels >= r pass
 // through.  Both products of fp16 values are exact in fp32, so the fused
@@ -90,7 +140,8 @@ __device__ __forceinline__ float rot_pair(float x, float y, float cs, float sn, 
 __device__ __forceinline__ void rotate_chunk(const uint16_t* row, u32x4 own, int c, int pos,
                                              const uint16_t* cos_t, const uint16_t* sin_t,
                                              int rot, int interleaved, int rot_rows,
-                                             float out[8]) {
+                                             float out[8], float nr = 0.f,
+                                             const uint16_t* nw = nullptr) {
   uint16_t x16[8];
   __builtin_memcpy(x16, &own, 16);
 #pragma unroll
@@ -104,7 +155,9 @@ __device__ __forceinline__ void rotate_chunk(const uint16_t* row, u32x4 own, int
     const bool second = d0 >= half;
     const int i0 = second ? d0 - half : d0;
     uint16_t y16[8], c16[8], s16[8];
-    const u32x4 pv = load16(row + (second ? d0 - half : d0 + half));
+    const int pc = (second ? d0 - half : d0 + half) >> 3;
+    u32x4 pv = load16(row + 8 * pc);
+    if (nw) pv = norm_chunk(pv, nr, nw, pc);
     const u32x4 cv = load16(cos_t + tb + i0);
     const u32x4 sv = load16(sin_t + tb + i0);
     __builtin_memcpy(y16, &pv, 16);
@@ -133,8 +186,8 @@ __device__ __forceinline__ void rotate_chunk(const uint16_t* row, u32x4 own, int
       const bool second = interleaved ? (d & 1) != 0 : d >= half;
       const int i = interleaved ? (d >> 1) : (second ? d - half : d);
       const int partner = interleaved ? (d ^ 1) : (second ? d - half : d + half);
-      out[e] = rot_pair(h2f(x16[e]), h2f(row[partner]), h2f(cos_t[tb + i]), h2f(sin_t[tb + i]),
-                        second);
+      const float y = nw ? norm_value(h2f(row[partner]), nr, nw[partner]) : h2f(row[partner]);
+      out[e] = rot_pair(h2f(x16[e]), y, h2f(cos_t[tb + i]), h2f(sin_t[tb + i]), second);
     }
   }
 }
@@ -234,6 +287,18 @@ __device__ __forceinline__ u32x2 quantize8(u32x4 x16, int cache_dtype, const flo
     }
   }
   return r;
+}
+
+// ---- attention sink (PagedAttention -- CUDA Design Document, section 6.1) --
+// The head's sink logit s joins the softmax denominator only.  Scores are
+// kept as 2^(x log2 e - m) with running max m (log2 units) and sum l, so the
+// denominator becomes l + 2^(s log2 e - m).  A row with no key at all
+// (m = -inf, l = 0, output 0) keeps l, so a sink of -inf cannot make it NaN.
+__device__ __forceinline__ float sink_denominator(float l, float m, int use_sink,
+                                                  const uint16_t* sink, int h) {
+  if (!use_sink || m == -__builtin_huge_valf()) return l;
+  const float s = sink ? h2f(sink[h]) : 0.f;   // no array: smooth softmax (s = 0)
+  return l + exp2_fast(s * kLog2e - m);
 }
 
 template <int W>

@@ -49,6 +49,19 @@ struct AppendArgs {
   int32_t k_quant, v_quant;
   const float* k_scale;   // [1] or [Hkv, D]
   const float* v_scale;
+  const uint16_t* k_norm; // QK-Norm weight of K (fp16 [D]) or null
+  float norm_eps;
+};
+
+// QK-Norm of the queries into a staging buffer (the prologue): rows of
+// head_size channels, one weight vector shared by all heads.
+struct QNormArgs {
+  const uint16_t* in;     // fp16 [rows, D]
+  uint16_t* out;          // fp16 [rows, D]
+  int64_t rows;           // tokens * heads
+  int32_t head_size;
+  const uint16_t* weight; // fp16 [D]
+  float eps;
 };
 
 // Decode work is a list of items (row, split) x (kv head, head chunk).  A row
@@ -98,6 +111,8 @@ struct DecodeArgs {
   int32_t k_quant, v_quant;     // kQuant*
   const float* k_scale;         // [1] or [Hkv, D]
   const float* v_scale;
+  const uint16_t* head_sink;    // fp16 [H] sink logits, or null (zero sinks)
+  int32_t use_sink;             // 0: no sink term
 };
 
 // Plan kernel (one workgroup): lists (row, split) entries of every row with
@@ -128,6 +143,8 @@ struct MergeArgs {
   int32_t split_tokens;
   int32_t max_splits;
   int32_t window;
+  const uint16_t* head_sink;    // as in DecodeArgs
+  int32_t use_sink;
 };
 
 // Prefill kernel: one workgroup per (q tile of 128 rows, kv head).  Rows of a
@@ -160,6 +177,8 @@ struct PrefillArgs {
   int32_t use_softcap;
   int32_t rows16;               // head_size 256: the 8-wave kernel (16 rows per wave)
   int32_t pool32;               // each cache is smaller than 4 GiB (32-bit byte offsets)
+  const uint16_t* head_sink;    // as in DecodeArgs
+  int32_t use_sink;
 };
 
 // Kernel start/stop events of the launch being made on this thread (set by
@@ -184,6 +203,7 @@ inline void launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipS
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+hipError_t launch_q_norm(const QNormArgs& a, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int head_size, int workgroups, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);

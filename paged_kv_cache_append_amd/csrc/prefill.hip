@@ -585,7 +585,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   }
 
   // ---- normalise and store ----
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float den = sink_denominator(lt, m, a.use_sink, a.head_sink, head);
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
   if (row_ok) {
     uint16_t* orow = a.out + (int64_t)t * HD + (int64_t)head * D;
 #pragma unroll
@@ -645,6 +646,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a)
     w[c] = c < tk.pieces && mm != kNegInf ? exp2_fast(a.part_ml[2 * (pr + c)] - mm) : 0.f;
     if (c < tk.pieces) ll += w[c] * a.part_ml[2 * (pr + c) + 1];
   }
+  ll = sink_denominator(ll, mm, a.use_sink, a.head_sink, head);
   const float inv = ll > 0.f ? 1.0f / ll : 0.f;
   uint16_t* orow = a.out + (int64_t)t * a.num_heads * D + (int64_t)head * D;
 #pragma unroll 4

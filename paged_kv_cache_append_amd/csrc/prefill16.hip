@@ -552,7 +552,8 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
     return;
   }
 
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float den = sink_denominator(lt, m, a.use_sink, a.head_sink, head);
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
   if (row_ok) {
     uint16_t* orow = a.out + (int64_t)t * HD + (int64_t)head * D;
 #pragma unroll

@@ -40,7 +40,9 @@ def test_library_exports_every_declared_function():
 def params(**kw):
     d = dict(num_heads=8, kv_num_heads=2, head_size=64, block_size=16, scale=0.0, softcap=0.0,
              local_window_size=-1, do_rotary=0, rotary_interleaved=0, path=0, split_tokens=0,
-             prefill_pieces=0, prefill_kernel=0, cache_dtype=0, k_quant_type=0, v_quant_type=0)
+             prefill_pieces=0, prefill_kernel=0, cache_dtype=0, k_quant_type=0, v_quant_type=0,
+             head_sink=None, use_smooth_softmax=0, q_norm_weight=None, k_norm_weight=None,
+             qk_norm_epsilon=0.0)
     d.update(kw)
     return _lib.AttnParams(*[d[f] for f, _ in _lib.AttnParams._fields_])
 
@@ -120,6 +122,17 @@ NEGATIVE = [
      1, "v_scale: expected 4-byte alignment"),
 ]
 
+# attention sink and QK-Norm (sections 6.4, 7.4)
+NEGATIVE += [
+    (dict(use_smooth_softmax=2), {}, 1, "use_smooth_softmax"),
+    (dict(head_sink=FAKE + 1), {}, 1, "head_sink: expected 2-byte"),
+    (dict(q_norm_weight=FAKE), {}, 1, "both or neither"),
+    (dict(k_norm_weight=FAKE), {}, 1, "both or neither"),
+    (dict(q_norm_weight=FAKE, k_norm_weight=FAKE + 8), {}, 1, "16-byte alignment"),
+    (dict(qk_norm_epsilon=-1e-6), {}, 1, "qk_norm_epsilon"),
+    (dict(qk_norm_epsilon=float("inf")), {}, 1, "qk_norm_epsilon"),
+]
+
 QUANT = dict(cache_dtype=1, k_quant_type=1, v_quant_type=2)
 QUANT_KV = dict(k_scale=FAKE + 4, v_scale=FAKE)     # per tensor: 4-byte; per channel: 16-byte
 
@@ -181,6 +194,17 @@ def test_quantized_cache_takes_the_decode_kernel():
     # path 2 (prefill kernel for multi-token requests) does not serve codes
     assert call_forward(params(path=2, **QUANT), paged(**QUANT_KV)) == 2
     assert "quantized caches" in err()
+
+
+def test_qk_norm_head_size_limit_and_workspace():
+    norm = dict(q_norm_weight=FAKE, k_norm_weight=FAKE)
+    assert call_forward(params(head_size=96, **norm), paged()) == 2
+    assert call_append(params(head_size=96, **norm), paged()) == 2 and "QK-Norm" in err()
+    # the normalized queries are staged in the workspace: T * H * D fp16
+    a = plan(params(), paged(token_count=4, batch_size=4))
+    b = plan(params(**norm), paged(token_count=4, batch_size=4))
+    assert b["q_norm"] == "1" and a["q_norm"] == "0"
+    assert int(b["workspace"]) - int(a["workspace"]) >= 4 * 8 * 64 * 2
 
 
 def test_workspace_must_cover_the_plan():
