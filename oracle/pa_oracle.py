@@ -68,6 +68,13 @@ Readings where the pages are silent (each also listed in the design notes):
   (and before K is quantized).  Computed here in fp64 (§7.1 asks for an fp32
   sum of squares; the kernels' fp32 result may round to a neighbouring fp16
   value, one unit in the last place).
+* Latent attention (MLA, PagedAttention -- CUDA Design Document, §12.2-§12.5):
+  with ``kv_cache_layout = LATENT`` there is one cache, ``kv_num_heads = 1``;
+  V is the leading ``v_head_size`` channels of each K row (no value input,
+  no value cache) and the output has ``v_head_size`` channels per head.
+  RoPE covers channels ``[rotary_offset, rotary_offset + rotary_dim)`` of a
+  head (§12.5); the pairs and angle index are those of R6 counted from the
+  offset.
 * Explicit write slots (PagedAttention -- CUDA Design Document, §5.2): slot
   ``s`` is block ``s // block_size``, offset ``s % block_size``; ``-1`` writes
   nothing.  The stored K is still rotated at the token's position
@@ -118,22 +125,23 @@ def derived_slot(block_table: np.ndarray, b: int, pos: int, block_size: int):
 # a3: rotary embedding (formula not printed on the pages -- see header)
 # ---------------------------------------------------------------------------
 
-def _rotary_pairs(rotary_dim: int, interleaved: bool):
-    """List of ``(first, second, angle index)`` channel pairs."""
+def _rotary_pairs(rotary_dim: int, interleaved: bool, offset: int = 0):
+    """List of ``(first, second, angle index)`` channel pairs; the rotated
+    channels start at ``offset`` (§12.5)."""
     half = rotary_dim // 2
     if interleaved:
-        return [(2 * i, 2 * i + 1, i) for i in range(half)]
-    return [(i, i + half, i) for i in range(half)]
+        return [(offset + 2 * i, offset + 2 * i + 1, i) for i in range(half)]
+    return [(offset + i, offset + i + half, i) for i in range(half)]
 
 
 def rope_key_fp16(x16: np.ndarray, pos: int, cos16: np.ndarray, sin16: np.ndarray,
-                  interleaved: bool) -> np.ndarray:
+                  interleaved: bool, offset: int = 0) -> np.ndarray:
     """Rotate one fp16 head row ``x16 [D]`` at ``pos`` and round it the way it
     is stored in the fp16 pool: exact products, one fp32 rounding of their
     difference, one fp16 rounding."""
     rotary_dim = 2 * cos16.shape[1]
     out = x16.copy()
-    for a, b, i in _rotary_pairs(rotary_dim, interleaved):
+    for a, b, i in _rotary_pairs(rotary_dim, interleaved, offset):
         x = float(x16[a])
         y = float(x16[b])
         c = float(cos16[pos, i])
@@ -148,12 +156,12 @@ def rope_key_fp16(x16: np.ndarray, pos: int, cos16: np.ndarray, sin16: np.ndarra
 
 
 def rope_query_fp64(x: np.ndarray, pos: int, cos: np.ndarray, sin: np.ndarray,
-                    interleaved: bool) -> np.ndarray:
+                    interleaved: bool, offset: int = 0) -> np.ndarray:
     """Rotate one head row in fp64 with no rounding (used for queries, which
     are never stored)."""
     rotary_dim = 2 * cos.shape[1]
     out = np.array(x, dtype=np.float64, copy=True)
-    for a, b, i in _rotary_pairs(rotary_dim, interleaved):
+    for a, b, i in _rotary_pairs(rotary_dim, interleaved, offset):
         c = float(cos[pos, i])
         s = float(sin[pos, i])
         out[a] = float(x[a]) * c - float(x[b]) * s
@@ -166,6 +174,7 @@ def rope_query_fp64(x: np.ndarray, pos: int, cos: np.ndarray, sin: np.ndarray,
 # ---------------------------------------------------------------------------
 
 QK_NORM_EPSILON = 1e-6     # §7.1 default
+LAYOUT_SEPARATE, LAYOUT_LATENT = 0, 1   # kv_cache_layout (§12.3)
 
 
 def rms_norm_fp16(x16: np.ndarray, w16: np.ndarray, eps: float) -> np.ndarray:
@@ -294,15 +303,19 @@ def append_kv(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
               cache_dtype: int = CACHE_FP16, k_quant_type: int = QUANT_NONE,
               v_quant_type: int = QUANT_NONE, k_scale: Optional[np.ndarray] = None,
               v_scale: Optional[np.ndarray] = None, k_norm_weight: Optional[np.ndarray] = None,
-              qk_norm_epsilon: float = QK_NORM_EPSILON):
+              qk_norm_epsilon: float = QK_NORM_EPSILON, rotary_offset: int = 0,
+              kv_cache_layout: int = LAYOUT_SEPARATE):
     """Return new ``(key_cache, value_cache)`` copies with every new token's
     K (RMS-normed with ``k_norm_weight`` if given, then rotated if a rotary
     table is given; §7.2 order) and V stored at its derived slot, or at
     ``slot_mapping[t]`` when a mapping is given.  With a quantized cache the
     stored rows are the codes of those fp16 rows (§8.4: quantized as they
-    are scattered).  Slots that no token maps to are left byte-identical."""
+    are scattered).  Slots that no token maps to are left byte-identical.
+    With ``kv_cache_layout = LATENT`` only the key cache exists (``value``
+    and ``value_cache`` are None; §12.2) and None is returned for V."""
+    latent = kv_cache_layout == LAYOUT_LATENT
     kc = key_cache.copy()
-    vc = value_cache.copy()
+    vc = None if latent else value_cache.copy()
     block_size = kc.shape[1]
     Hkv, D = kv_num_heads, head_size
     T = key.shape[0]
@@ -321,16 +334,19 @@ def append_kv(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
             blk, off = where
         for h in range(Hkv):
             krow = key[t, h * D:(h + 1) * D]
-            vrow = value[t, h * D:(h + 1) * D]
             if k_norm_weight is not None:
                 krow = rms_norm_fp16(krow, k_norm_weight, qk_norm_epsilon)
             if cos_cache is not None:
-                krow = rope_key_fp16(krow, pos, cos_cache, sin_cache, rotary_interleaved)
+                krow = rope_key_fp16(krow, pos, cos_cache, sin_cache, rotary_interleaved,
+                                     rotary_offset)
             if cache_dtype != CACHE_FP16:
                 krow = quantize_row(krow, cache_dtype, k_scale, k_quant_type, h)
-                vrow = quantize_row(vrow, cache_dtype, v_scale, v_quant_type, h)
             kc[blk, off, h, :] = krow
-            vc[blk, off, h, :] = vrow
+            if not latent:
+                vrow = value[t, h * D:(h + 1) * D]
+                if cache_dtype != CACHE_FP16:
+                    vrow = quantize_row(vrow, cache_dtype, v_scale, v_quant_type, h)
+                vc[blk, off, h, :] = vrow
     return kc, vc
 
 
@@ -387,7 +403,8 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
             k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None,
             head_sink: Optional[np.ndarray] = None, use_smooth_softmax: bool = False,
             q_norm_weight: Optional[np.ndarray] = None,
-            qk_norm_epsilon: float = QK_NORM_EPSILON):
+            qk_norm_epsilon: float = QK_NORM_EPSILON, rotary_offset: int = 0,
+            kv_cache_layout: int = LAYOUT_SEPARATE, v_head_size: int = 0):
     """Attention output in fp64.
 
     ``key_cache``/``value_cache`` must already hold the new tokens (run
@@ -395,15 +412,20 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
     dequantized (``q * scale``, §8.3) as they are gathered.  ``q_norm_weight``
     RMS-norms each query head before RoPE (§7); ``head_sink`` (``[H]``) or
     ``use_smooth_softmax`` adds a denominator-only logit per head (§6.1).
-    Returns ``[T, H*D]`` for all tokens, or ``[len(rows), H*D]`` in the
-    given order when ``rows`` is set.  With ``return_probs`` also returns
-    ``{(t, h): probabilities over keys}``."""
+    With ``kv_cache_layout = LATENT`` (§12.2) V is the leading
+    ``v_head_size`` channels of K (``value_cache`` is not read) and each head
+    outputs ``v_head_size`` channels.
+    Returns ``[T, H*DV]`` for all tokens, or ``[len(rows), H*DV]`` in the
+    given order when ``rows`` is set (``DV = D`` unless latent).  With
+    ``return_probs`` also returns ``{(t, h): probabilities over keys}``."""
     T = query.shape[0]
     H, Hkv, D = num_heads, kv_num_heads, head_size
     g = H // Hkv
     sigma = effective_scale(scale, D)
+    latent = kv_cache_layout == LAYOUT_LATENT
+    DV = v_head_size if latent and v_head_size else D
     row_list = list(range(T)) if rows is None else [int(r) for r in rows]
-    out = np.zeros((len(row_list), H * D), np.float64)
+    out = np.zeros((len(row_list), H * DV), np.float64)
     probs = {}
 
     # group the requested rows by owning sequence so each context is gathered once
@@ -424,13 +446,18 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
     for b, items in by_seq.items():
         q_len = int(cum[b + 1]) - int(cum[b])
         kv_len = int(past[b]) + q_len
-        K = gather_sequence(key_cache, block_table, b, kv_len)
-        V = gather_sequence(value_cache, block_table, b, kv_len)
         if cache_dtype != CACHE_FP16:
             K = dequantize(gather_codes(key_cache, block_table, b, kv_len), cache_dtype, k_scale,
                            k_quant_type, D)
-            V = dequantize(gather_codes(value_cache, block_table, b, kv_len), cache_dtype,
-                           v_scale, v_quant_type, D)
+            if not latent:
+                V = dequantize(gather_codes(value_cache, block_table, b, kv_len), cache_dtype,
+                               v_scale, v_quant_type, D)
+        else:
+            K = gather_sequence(key_cache, block_table, b, kv_len)
+            if not latent:
+                V = gather_sequence(value_cache, block_table, b, kv_len)
+        if latent:
+            V = K[:, :, :DV]                                   # V is a view of K (§12.2)
         tau = np.arange(kv_len)
         n_idx = [n for n, _, _ in items]
         positions = [token_position(past, b, j) for _, _, j in items]
@@ -446,7 +473,7 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
             if cos_cache is not None:
                 for h in range(H):
                     qrow[h] = rope_query_fp64(qrow[h], positions[r], cos_cache, sin_cache,
-                                              rotary_interleaved)
+                                              rotary_interleaved, rotary_offset)
             Q[r] = qrow
         mask = np.stack([admitted(tau, p, local_window_size) for p in positions])
         for h in range(H):
@@ -455,7 +482,7 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
             if softcap > 0.0:
                 S = softcap * np.tanh(S / softcap)
             S = np.where(mask, S, -np.inf)                     # exclusion
-            O = np.zeros((len(items), D), np.float64)
+            O = np.zeros((len(items), DV), np.float64)
             for r in range(len(items)):
                 if not mask[r].any():
                     continue                                   # fully masked -> 0
@@ -470,7 +497,7 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
                 O[r] = p @ V[:, kvh, :]
                 if return_probs:
                     probs[(items[r][1], h)] = p
-            out[n_idx, h * D:(h + 1) * D] = O
+            out[n_idx, h * DV:(h + 1) * DV] = O
     if return_probs:
         return out, probs
     return out

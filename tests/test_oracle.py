@@ -977,3 +977,113 @@ def test_forward_normalizes_q_before_rope_and_composes_with_the_sink():
     b, _, _ = _oracle_on(w, head_sink=sink)
     w.query = q0
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# latent attention (MLA, PagedAttention -- CUDA Design Document, §12)
+# ---------------------------------------------------------------------------
+
+def _contiguous_pool(rows, bs):
+    """A pool [nb, bs, Hkv, D] holding ``rows`` [L, Hkv, D] in blocks 0, 1, ...
+    and the identity table row."""
+    L = rows.shape[0]
+    nb = (L + bs - 1) // bs + 1
+    pool = np.zeros((nb, bs) + rows.shape[1:], rows.dtype)
+    for p in range(L):
+        pool[p // bs, p % bs] = rows[p]
+    return pool, np.arange(nb, dtype=np.int32)[None, :]
+
+
+def test_rotary_offset_rotates_only_its_window():
+    rng = np.random.default_rng(40)
+    x = rng.standard_normal(24).astype(np.float16)
+    cos, sin = wl.rope_tables(16, 8)
+    for inter in (False, True):
+        y = oracle.rope_key_fp16(x, 11, cos, sin, inter, offset=16)
+        assert np.array_equal(y[:16], x[:16])
+        assert np.array_equal(y[16:], oracle.rope_key_fp16(x[16:], 11, cos, sin, inter))
+        q = oracle.rope_query_fp64(x, 11, cos, sin, inter, offset=16)
+        np.testing.assert_array_equal(q[:16], x[:16].astype(np.float64))
+        np.testing.assert_array_equal(q[16:], oracle.rope_query_fp64(x[16:], 11, cos, sin, inter))
+
+
+def test_latent_is_separate_attention_with_v_the_leading_channels_of_k():
+    rng = np.random.default_rng(41)
+    H, D, DV, bs = 4, 24, 16, 16
+    w = _small_case(seed=42, num_heads=H, kv_num_heads=1, head_size=D, block_size=bs,
+                    scale=0.3, softcap=2.0, local_window_size=20)
+    kc = w.pool_blocks(0, range(w.num_blocks))
+    nk, nv = oracle.append_kv(kc, None, w.key, None, w.cum, w.past, w.block_table,
+                              kv_num_heads=1, head_size=D, kv_cache_layout=oracle.LAYOUT_LATENT)
+    assert nv is None
+    lat = oracle.forward(w.query, nk, None, w.cum, w.past, w.block_table, num_heads=H,
+                         kv_num_heads=1, head_size=D, scale=0.3, softcap=2.0,
+                         local_window_size=20, kv_cache_layout=oracle.LAYOUT_LATENT,
+                         v_head_size=DV)
+    vc = nk.copy()
+    vc[..., DV:] = 0                              # V: the leading DV channels, zero-padded
+    sep = oracle.forward(w.query, nk, vc, w.cum, w.past, w.block_table, num_heads=H,
+                         kv_num_heads=1, head_size=D, scale=0.3, softcap=2.0,
+                         local_window_size=20)
+    assert lat.shape == (w.token_count, H * DV)
+    for h in range(H):
+        np.testing.assert_array_equal(lat[:, h * DV:(h + 1) * DV], sep[:, h * D:h * D + DV])
+        assert np.all(sep[:, h * D + DV:(h + 1) * D] == 0)
+
+
+def test_absorbed_mla_equals_non_absorbed_attention():
+    """§12.1: folding W_UK into the query and W_UV into the output is the same
+    attention as decompressing per-head K/V first.  Entries are small
+    multiples of 1/2, so every fp16 input of both forms is exact and the two
+    fp64 results agree to rounding.  RoPE sits at offset R (absorbed row
+    [c, k_pe]) or N (per-head row [k_nope, k_pe])."""
+    rng = np.random.default_rng(43)
+    H, R, N, P, V, L, bs = 2, 16, 8, 8, 8, 37, 16
+    half = lambda *s: (rng.integers(-2, 3, s) * 0.5).astype(np.float16)
+    c = half(L, R)                    # latent rows
+    kpe = half(L, P)                  # rope part (before rotation)
+    W_uk = half(H, R, N)
+    W_uv = half(H, R, V)
+    q_nope = half(L, H, N)
+    q_pe = half(L, H, P)
+    cos, sin = wl.rope_tables(64, P)
+    rot = dict(cos_cache=cos, sin_cache=sin, rotary_interleaved=False)
+    cum = np.array([0, L], np.int32)
+    past = np.array([0], np.int32)
+    scale = 1.0 / math.sqrt(N + P)     # the pre-absorption width (§12.6)
+
+    # absorbed: one latent cache row [c, k_pe] (width R + P), V = c
+    key_lat = np.concatenate([c, kpe], axis=1)                          # [L, R + P]
+    q_abs = np.concatenate([np.einsum("thn,hrn->thr", q_nope.astype(np.float64),
+                                      W_uk.astype(np.float64)), q_pe], axis=2)
+    assert np.array_equal(q_abs, q_abs.astype(np.float16))             # exact in fp16
+    pool, table = _contiguous_pool(np.zeros((L, 1, R + P), np.float16), bs)
+    nk, _ = oracle.append_kv(pool, None, key_lat, None, cum, past, table, kv_num_heads=1,
+                             head_size=R + P, rotary_offset=R,
+                             kv_cache_layout=oracle.LAYOUT_LATENT, **rot)
+    o_lat = oracle.forward(q_abs.reshape(L, H * (R + P)).astype(np.float16), nk, None, cum,
+                           past, table, num_heads=H, kv_num_heads=1, head_size=R + P,
+                           scale=scale, rotary_offset=R, kv_cache_layout=oracle.LAYOUT_LATENT,
+                           v_head_size=R, **rot)
+    o_abs = np.stack([o_lat[:, h * R:(h + 1) * R] @ W_uv[h].astype(np.float64)
+                      for h in range(H)], axis=1)                       # [L, H, V]
+
+    # non-absorbed: per-head K = [c W_uk, k_pe], V = c W_uv (zero-padded to N + P)
+    k_nope = np.einsum("tr,hrn->thn", c.astype(np.float64), W_uk.astype(np.float64))
+    v_full = np.einsum("tr,hrv->thv", c.astype(np.float64), W_uv.astype(np.float64))
+    key_sep = np.concatenate([k_nope, np.repeat(kpe[:, None, :].astype(np.float64), H, 1)], 2)
+    val_sep = np.concatenate([v_full, np.zeros((L, H, N + P - V))], axis=2)
+    assert np.array_equal(key_sep, key_sep.astype(np.float16))
+    assert np.array_equal(val_sep, val_sep.astype(np.float16))
+    zero = np.zeros((L, H, N + P), np.float16)
+    kpool, table2 = _contiguous_pool(zero, bs)
+    vpool, _ = _contiguous_pool(zero, bs)
+    nk2, nv2 = oracle.append_kv(kpool, vpool, key_sep.reshape(L, -1).astype(np.float16),
+                                val_sep.reshape(L, -1).astype(np.float16), cum, past, table2,
+                                kv_num_heads=H, head_size=N + P, rotary_offset=N, **rot)
+    q_sep = np.concatenate([q_nope, q_pe], axis=2).reshape(L, -1)
+    o_sep = oracle.forward(q_sep, nk2, nv2, cum, past, table2, num_heads=H, kv_num_heads=H,
+                           head_size=N + P, scale=scale, rotary_offset=N, **rot)
+    o_sep = o_sep.reshape(L, H, N + P)[:, :, :V]
+    np.testing.assert_allclose(o_abs, o_sep, rtol=0, atol=1e-12)
+    assert np.max(np.abs(o_sep)) > 0.1
