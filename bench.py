@@ -19,6 +19,9 @@ dispatch timestamped on its stream (start/stop events of the launch itself);
 ``roofline`` describes the dominant kernel from those durations (per-launch
 algorithmic bytes or FLOPs over its average launch time).
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the workload.
+``--config mla_decode_tp8`` / ``mla_decode_dp`` runs the latent-attention (MLA)
+step instead: append of 576-channel latent rows + forward on the latent
+kernel (V is the leading 512 channels of K).
 With ``--cache`` the pools hold int8 or float8 e4m3fn codes with fp32 scales
 (decode-only workloads: every request has one new token); the algorithmic
 bytes then count one byte per cached element.
@@ -87,7 +90,8 @@ def traffic_from_profiles(kernel_tag: str, src_hash: str):
 
 
 KERNEL_SOURCES = {
-    "decode": ("decode.hip", "pa_api.hip", "pa_device.h", "pa_internal.h"),
+    "mla": ("mla.hip", "decode_rows.h", "pa_api.hip", "pa_device.h", "pa_internal.h"),
+    "decode": ("decode.hip", "decode_rows.h", "pa_api.hip", "pa_device.h", "pa_internal.h"),
     "prefill": ("prefill.hip", "prefill16.hip", "prefill_common.h", "pa_api.hip", "pa_device.h",
                 "pa_internal.h"),
 }
@@ -258,6 +262,164 @@ def summarize_pmc(paths):
         print(f"{k:90s} {c:28s} {len(v):10d} {sum(v) / len(v):16.1f}")
 
 
+STAGES = ("append", "decode", "merge", "prefill", "prefill_merge", "plan", "q_norm")
+
+
+def measure(step, steps, warmup):
+    """W untimed steps, then K timed steps with nothing else on the stream
+    (the throughput figure), then the same K steps with every kernel's
+    dispatch timestamped on its stream (the per-kernel durations)."""
+    import torch
+
+    import paged_kv_cache_append_amd as pa
+
+    def timed(k):
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(k):
+            step()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step = timed(steps) / steps
+    pa.timing_enable(8 * steps + 16)
+    ms_step_instrumented = timed(steps) / steps
+    stages = {s: pa.timing_read(s) for s in STAGES}
+    pa.timing_disable()
+    return ms_step, ms_step_instrumented, stages
+
+
+def mla_work(w):
+    """Latent attention: bytes (each admitted 576-channel row once -- V is a
+    view of K -- plus the fp16 Q and O rows of every query token) and FLOPs
+    (2 * H * (D + DV) per admitted key of every query token)."""
+    from paged_kv_cache_append_amd import workloads as wl
+    H, D, DV = w.num_heads, w.head_size, wl.MLA_V_HEAD_SIZE
+    W = w.local_window_size
+    nbytes = 0
+    keys = 0
+    for b in range(w.batch_size):
+        for j in range(int(w.q_lens[b])):
+            pos = int(w.past[b]) + j
+            kv = pos + 1 - (max(0, pos - W + 1) if W > 0 else 0)
+            nbytes += kv * D * 2 + H * D * 2 + H * DV * 2
+            keys += kv
+    return nbytes, 2.0 * H * (D + DV) * keys
+
+
+def mla_cpu_baseline(w, gpu_out, sample=16, target_seconds=10.0):
+    """The oracle on the first ``sample`` requests of a latent workload, for
+    about target_seconds: GB/s of the same algorithmic bytes, and the max-abs
+    error of the GPU rows it covers."""
+    import threadpoolctl
+
+    import oracle
+    from paged_kv_cache_append_amd import workloads as wl
+    sub = wl.subset(w, list(range(min(sample, w.batch_size))))
+    rot = dict(cos_cache=sub.cos_cache, sin_cache=sub.sin_cache,
+               rotary_interleaved=bool(sub.rotary_interleaved),
+               rotary_offset=wl.MLA_ROTARY_OFFSET)
+    kc = sub.pool_blocks(wl.KIND_K, range(sub.num_blocks))
+    nk, _ = oracle.append_kv(kc, None, sub.key, None, sub.cum, sub.past, sub.block_table,
+                             kv_num_heads=1, head_size=sub.head_size,
+                             kv_cache_layout=oracle.LAYOUT_LATENT, **rot)
+    threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
+                  if i.get("user_api") == "blas") or 1
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        ref = oracle.forward(sub.query, nk, None, sub.cum, sub.past, sub.block_table,
+                             num_heads=sub.num_heads, kv_num_heads=1, head_size=sub.head_size,
+                             scale=sub.scale, softcap=sub.softcap,
+                             local_window_size=sub.local_window_size,
+                             kv_cache_layout=oracle.LAYOUT_LATENT,
+                             v_head_size=wl.MLA_V_HEAD_SIZE, **rot)
+        reps += 1
+        if time.perf_counter() - t0 >= target_seconds:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    nbytes, _ = mla_work(sub)
+    err = float(np.max(np.abs(gpu_out[sub.extra["parent_rows"]].astype(np.float64) - ref)))
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{sub.batch_size} requests of {w.name} ({nbytes / 1e6:.1f} MB of latent "
+                      f"rows + Q/O), gather + full scores + softmax + PV in fp64, {dt:.2f} s "
+                      f"per pass, {reps} passes"}, err
+
+
+def bench_mla(args):
+    """Latent attention (MLA) step: append of the latent rows + forward on the
+    latent kernel, over an absorbed DeepSeek-shaped decode batch."""
+    import torch
+
+    import paged_kv_cache_append_amd as pa
+    from paged_kv_cache_append_amd import workloads as wl
+    w = wl.make_mla_workload(args.config)
+    dev = wl.to_device(w)
+    a = pa.Attn(num_heads=w.num_heads, kv_num_heads=1, head_size=w.head_size,
+                block_size=w.block_size, scale=w.scale, do_rotary=1,
+                rotary_interleaved=w.rotary_interleaved, kv_cache_layout=pa.LAYOUT_LATENT,
+                v_head_size=wl.MLA_V_HEAD_SIZE, rotary_offset=wl.MLA_ROTARY_OFFSET)
+    T = w.token_count
+    out = torch.empty((T, w.num_heads * wl.MLA_V_HEAD_SIZE), dtype=torch.float16, device="cuda")
+    nws = pa.forward_workspace_bytes(a, dev["key_cache"], None, dev["block_table"], dev["cum"],
+                                     dev["past"], T)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    plan = pa.describe_plan(a, dev["key_cache"], None, dev["block_table"], dev["cum"],
+                            dev["past"], T)
+
+    def step():
+        pa.append_kv(a, dev["key"], None, dev["key_cache"], None, dev["block_table"], dev["cum"],
+                     dev["past"], dev["cos"], dev["sin"])
+        pa.forward(a, dev["query"], dev["key_cache"], None, dev["block_table"], dev["cum"],
+                   dev["past"], dev["cos"], dev["sin"], workspace=ws, out=out)
+
+    ms_step, ms_step_instrumented, stages = measure(step, args.steps, args.warmup)
+    per = {s: (ms / n * 1e3 if n else 0.0) for s, (ms, n) in stages.items()}
+    nbytes, flops = mla_work(w)
+    t = per["decode"] * 1e-6
+    gbs, tfs = nbytes / t / 1e9, flops / t / 1e12
+    hbm_bound = nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_F16_PEAK_TFS * 1e12)
+    roof = {"bound": "hbm" if hbm_bound else "mfma", "kernel": "mla",
+            "achieved": round(gbs if hbm_bound else tfs, 4),
+            "peak": HBM_PEAK_GBS if hbm_bound else MFMA_F16_PEAK_TFS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": round(gbs / HBM_PEAK_GBS if hbm_bound else tfs / MFMA_F16_PEAK_TFS, 4),
+            "traffic": traffic_from_profiles(f"mla:{w.name}", kernel_source_hash("mla")),
+            "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
+            "other_unit_frac": round(tfs / MFMA_F16_PEAK_TFS if hbm_bound
+                                     else gbs / HBM_PEAK_GBS, 4)}
+    kernels = {f"{s}_us": round(v, 3) for s, v in per.items()}
+    kernels["mla_kernel_gbs"] = round(gbs, 1)
+    kernels["mla_kernel_tflops"] = round(tfs, 2)
+    cpu, err = (None, None)
+    if not args.no_cpu_baseline:
+        cpu, err = mla_cpu_baseline(w, out.cpu().numpy())
+    line = {
+        "metric": METRIC, "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch_size, "tokens": T,
+                   "num_heads": w.num_heads, "kv_num_heads": 1, "head_size": w.head_size,
+                   "v_head_size": wl.MLA_V_HEAD_SIZE, "block_size": w.block_size,
+                   "kv_cache_layout": "latent", "rotary_offset": wl.MLA_ROTARY_OFFSET,
+                   "latent_bytes": nbytes, "flops": flops, "plan": plan},
+        "roofline": roof,
+        "kernels": kernels,
+        "ms_per_step_instrumented": round(ms_step_instrumented, 5),
+        "cpu_baseline": cpu,
+        "parity_max_abs_err_sampled": err,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +464,14 @@ def main():
 
     import paged_kv_cache_append_amd as pa
     from paged_kv_cache_append_amd import workloads as wl
+
+    if args.config in wl.MLA_CONFIG_NAMES:
+        if args.cache != "fp16" or args.head_sink or args.smooth_softmax or args.qk_norm:
+            print("bench.py: the latent workloads run with an fp16 cache and no sink or "
+                  "QK-Norm (section 12.10)", file=sys.stderr)
+            sys.exit(2)
+        bench_mla(args)
+        return
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 2
@@ -366,29 +536,7 @@ def main():
         pa.forward(a, dev["query"], dev["key_cache"], dev["value_cache"], dev["block_table"],
                    dev["cum"], dev["past"], dev["cos"], dev["sin"], workspace=ws, out=out, **sc)
 
-    def timed(k):
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(k):
-            step()
-        stop.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # K timed steps, nothing else on the stream: the throughput figure
-    ms_step = timed(args.steps) / args.steps
-    # the same K steps again with every kernel's dispatch timestamped (start
-    # and end of each launch on its stream): the per-kernel durations
-    pa.timing_enable(8 * args.steps + 16)
-    ms_step_instrumented = timed(args.steps) / args.steps
-    stages = {s: pa.timing_read(s)
-              for s in ("append", "decode", "merge", "prefill", "prefill_merge", "plan", "q_norm")}
-    pa.timing_disable()
+    ms_step, ms_step_instrumented, stages = measure(step, args.steps, args.warmup)
 
     # the append alone, with derived slots (from the steps above) and with an
     # explicit slot mapping (distinct slots scattered over the pool, as a

@@ -95,7 +95,28 @@ typedef struct {
                                  is stored normalized, and pa_forward stages the
                                  normalized Q in its workspace                       */
   float qk_norm_epsilon;      /* 0 -> 1e-6 (section 7.1 default); else finite, > 0    */
+  int32_t kv_cache_layout;    /* PA_LAYOUT_SEPARATE (0) or PA_LAYOUT_LATENT (1); see
+                                 "Latent attention"                                  */
+  int32_t v_head_size;        /* 0 = head_size; else 1..head_size, LATENT only: the V
+                                 channels of each row and of each output head         */
+  int32_t rotary_offset;      /* first rotated channel of a head, a multiple of 8;
+                                 RoPE covers [rotary_offset, rotary_offset +
+                                 rotary_dim) (section 12.5); 0 = from channel 0       */
 } pa_attn_params;
+
+/* Latent attention (MLA; PagedAttention -- CUDA Design Document, section 12).
+ * With kv_cache_layout = PA_LAYOUT_LATENT there is one cache: key_cache holds
+ * [num_blocks, block_size, 1, head_size] rows (kv_num_heads = 1), V is the
+ * leading v_head_size channels of each row (section 12.2), value and
+ * value_cache are NULL, and pa_forward writes out as [token_count, num_heads *
+ * v_head_size].  Absorbed DeepSeek-style rows are 576 channels (512 latent +
+ * 64 rotary, rotary_offset 512) with v_head_size 512: the shape the kernel
+ * serves (others: PA_ERR_UNSUPPORTED), for fp16 caches smaller than 4 GiB.
+ * Rules (section 12.10): an explicit scale when v_head_size != head_size
+ * (section 12.6), no head_sink / smooth softmax / QK-Norm, no V quantization,
+ * and RoPE only past the V channels (rotary_offset >= v_head_size).  Every
+ * token runs on the latent kernel (path 2 is PA_ERR_UNSUPPORTED). */
+enum { PA_LAYOUT_SEPARATE = 0, PA_LAYOUT_LATENT = 1 };
 
 /* Quantized caches (PagedAttention -- CUDA Design Document, section 8).
  * With cache_dtype != PA_CACHE_FP16 both caches hold one signed byte per
@@ -126,7 +147,7 @@ typedef struct {
                                                fp16, or of byte codes when quantized */
   void *value_cache;                        /* same shape; both mutated in place by
                                                pa_append_kv (cache outputs alias the
-                                               inputs, section 4.4)                   */
+                                               inputs, section 4.4); NULL when LATENT */
   int64_t num_blocks;                       /* > 0; num_blocks * block_size < 2^32   */
   const int32_t *block_table;               /* int32 [batch_size, max_blocks_per_seq]
                                                row-major; entries past a request's

@@ -17,14 +17,16 @@ from typing import Any, Optional
 
 from . import _lib
 
-__all__ = ["PAError", "Attn", "CACHE_FP16", "CACHE_INT8", "CACHE_FP8_E4M3FN", "QUANT_NONE",
+__all__ = ["PAError", "Attn", "CACHE_FP16", "CACHE_INT8", "CACHE_FP8_E4M3FN", "LAYOUT_SEPARATE",
+           "LAYOUT_LATENT", "QUANT_NONE",
            "QUANT_PER_TENSOR", "QUANT_PER_CHANNEL", "append_kv", "forward", "forward_workspace_bytes",
            "describe_plan", "last_error", "timing_enable", "timing_disable", "timing_read",
            "library_path"]
 
 
-# cache element types and scale granularities (the ABI enums of pa.h)
+# cache element types, scale granularities and cache layouts (the ABI enums of pa.h)
 CACHE_FP16, CACHE_INT8, CACHE_FP8_E4M3FN = 0, 1, 2
+LAYOUT_SEPARATE, LAYOUT_LATENT = 0, 1
 QUANT_NONE, QUANT_PER_TENSOR, QUANT_PER_CHANNEL = 0, 1, 2
 
 
@@ -58,6 +60,16 @@ class Attn:
     q_norm_weight: Any = None       # fp16 device tensors [head_size] or None (both or neither)
     k_norm_weight: Any = None
     qk_norm_epsilon: float = 0.0    # 0 -> 1e-6
+    kv_cache_layout: int = LAYOUT_SEPARATE
+    v_head_size: int = 0            # 0 -> head_size (LATENT: the V view of each row)
+    rotary_offset: int = 0
+
+    @property
+    def out_head_size(self) -> int:
+        """Channels per head of the output (v_head_size with a latent cache)."""
+        if self.kv_cache_layout == LAYOUT_LATENT and self.v_head_size:
+            return self.v_head_size
+        return self.head_size
 
     def c(self) -> _lib.AttnParams:
         import torch
@@ -71,7 +83,8 @@ class Attn:
                                self.prefill_pieces, self.prefill_kernel, self.cache_dtype,
                                self.k_quant_type, self.v_quant_type, _ptr(self.head_sink),
                                self.use_smooth_softmax, _ptr(self.q_norm_weight),
-                               _ptr(self.k_norm_weight), float(self.qk_norm_epsilon))
+                               _ptr(self.k_norm_weight), float(self.qk_norm_epsilon),
+                               self.kv_cache_layout, self.v_head_size, self.rotary_offset)
 
 
 def library_path() -> str:
@@ -122,7 +135,7 @@ def _kv(attn: Attn, key_cache, value_cache, block_table, cum, past, token_count,
         raise ValueError(f"key_cache: expected dtype {dts[0]} for cache_dtype "
                          f"{attn.cache_dtype}, got {key_cache.dtype}")
     _need(key_cache, "key_cache", key_cache.dtype)
-    _need(value_cache, "value_cache", key_cache.dtype, key_cache.shape)
+    _need(value_cache, "value_cache", key_cache.dtype, key_cache.shape)   # None when latent
     _need(block_table, "block_table", torch.int32)
     _need(cum, "cumulative_sequence_length", torch.int32, (block_table.shape[0] + 1,))
     _need(past, "past_seqlens", torch.int32, (block_table.shape[0],))
@@ -132,7 +145,7 @@ def _kv(attn: Attn, key_cache, value_cache, block_table, cum, past, token_count,
         _need(slot_mapping, "slot_mapping", torch.int32, (token_count,))
     _need(k_scale, "k_scale", torch.float32)
     _need(v_scale, "v_scale", torch.float32)
-    return _lib.PagedKV(key_cache.data_ptr(), value_cache.data_ptr(), key_cache.shape[0],
+    return _lib.PagedKV(key_cache.data_ptr(), _ptr(value_cache), key_cache.shape[0],
                         block_table.data_ptr(), block_table.shape[1], cum.data_ptr(),
                         past.data_ptr(), block_table.shape[0], token_count,
                         _ptr(slot_mapping), _ptr(k_scale), _ptr(v_scale))
@@ -165,13 +178,13 @@ def append_kv(attn: Attn, key, value, key_cache, value_cache, block_table, cum, 
     import torch
     T = key.shape[0]
     _need(key, "key", torch.float16, (T, attn.kv_num_heads * attn.head_size))
-    _need(value, "value", torch.float16, (T, attn.kv_num_heads * attn.head_size))
+    _need(value, "value", torch.float16, (T, attn.kv_num_heads * attn.head_size))  # None: latent
     lib = _lib.load()
     p = attn.c()
     kv = _kv(attn, key_cache, value_cache, block_table, cum, past, T, slot_mapping, k_scale,
              v_scale)
     c, s, rows, rd = _rot(attn, cos_cache, sin_cache)
-    _check(lib.pa_append_kv(ctypes.byref(p), ctypes.byref(kv), key.data_ptr(), value.data_ptr(),
+    _check(lib.pa_append_kv(ctypes.byref(p), ctypes.byref(kv), key.data_ptr(), _ptr(value),
                             c, s, rows, rd, _stream(stream)))
 
 
@@ -204,21 +217,22 @@ def describe_plan(attn: Attn, key_cache, value_cache, block_table, cum, past, to
 def forward(attn: Attn, query, key_cache, value_cache, block_table, cum, past, cos_cache=None,
             sin_cache=None, max_query_len_bound: int = 0, max_kv_len_bound: int = 0,
             workspace=None, out=None, stream=None, k_scale=None, v_scale=None):
-    """``pa_forward``: attention output ``[T, H*D]`` fp16 for packed queries
-    ``[T, H*D]``.  ``workspace``/``out`` are allocated with torch when not
+    """``pa_forward``: attention output ``[T, H*DV]`` fp16 (``DV`` =
+    ``attn.out_head_size``) for packed queries ``[T, H*D]``.  ``workspace``/``out`` are allocated with torch when not
     given; quantized caches take ``k_scale``/``v_scale`` as for
     :func:`append_kv`."""
     import torch
     T = query.shape[0]
     HD = attn.num_heads * attn.head_size
+    HO = attn.num_heads * attn.out_head_size
     _need(query, "query", torch.float16, (T, HD))
     lib = _lib.load()
     p = attn.c()
     kv = _kv(attn, key_cache, value_cache, block_table, cum, past, T, k_scale=k_scale,
              v_scale=v_scale)
     if out is None:
-        out = torch.empty((T, HD), dtype=torch.float16, device=query.device)
-    _need(out, "out", torch.float16, (T, HD))
+        out = torch.empty((T, HO), dtype=torch.float16, device=query.device)
+    _need(out, "out", torch.float16, (T, HO))
     n = ctypes.c_size_t(0)
     _check(lib.pa_forward_workspace_bytes(ctypes.byref(p), ctypes.byref(kv), max_query_len_bound,
                                           max_kv_len_bound, ctypes.byref(n)))

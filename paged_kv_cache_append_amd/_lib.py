@@ -30,7 +30,8 @@ class AttnParams(ctypes.Structure):
                 ("k_quant_type", ctypes.c_int32), ("v_quant_type", ctypes.c_int32),
                 ("head_sink", ctypes.c_void_p), ("use_smooth_softmax", ctypes.c_int32),
                 ("q_norm_weight", ctypes.c_void_p), ("k_norm_weight", ctypes.c_void_p),
-                ("qk_norm_epsilon", ctypes.c_float)]
+                ("qk_norm_epsilon", ctypes.c_float), ("kv_cache_layout", ctypes.c_int32),
+                ("v_head_size", ctypes.c_int32), ("rotary_offset", ctypes.c_int32)]
 
 
 class PagedKV(ctypes.Structure):

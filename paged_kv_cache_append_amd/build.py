@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.hip", "append.hip", "decode.hip", "prefill.hip", "prefill16.hip"]
+SOURCES = ["pa_api.hip", "append.hip", "decode.hip", "prefill.hip", "prefill16.hip", "mla.hip"]
 ARCH = "gfx950"
 
 

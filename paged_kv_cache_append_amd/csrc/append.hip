@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
       if (sm < 0 || (int64_t)sm >= (a.s.num_blocks << a.s.block_shift)) continue;   // -1: no write
       blk = sm >> a.s.block_shift;
       off = sm & (bs - 1);
-      if (a.rotary_dim > 0 && 8 * c < a.rotary_dim) {
+      if (chunk_rotated(c, a.rotary_offset, a.rotary_dim)) {
         const int b = find_request(a.s.cum, a.s.batch, t);
         pos = a.s.past[b] + (t - a.s.cum[b]);
       }
@@ -68,15 +68,17 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
       off = pos & (bs - 1);
     }
     const int64_t dst = slot_base(blk, off, kvh, bs, a.kv_heads, a.head_size) + 8 * c;
-    const u32x4 v = load16(a.value + src_row + 8 * c);
-    if (a.rotary_dim > 0 && 8 * c < a.rotary_dim) {
+    // a latent cache (section 12.2) has no V: V is a view of K
+    const u32x4 v = a.value ? load16(a.value + src_row + 8 * c) : u32x4{0, 0, 0, 0};
+    if (chunk_rotated(c, a.rotary_offset, a.rotary_dim)) {
+      const int off = a.rotary_offset;
       float r[8];
-      rotate_chunk(a.key + src_row, k, c, pos, a.cos, a.sin, a.rotary_dim,
-                   a.rotary_interleaved, a.rotary_rows, r, nr, a.k_norm);
+      rotate_chunk(a.key + src_row + off, k, c - off / 8, pos, a.cos, a.sin, a.rotary_dim,
+                   a.rotary_interleaved, a.rotary_rows, r, nr, a.k_norm ? a.k_norm + off : nullptr);
       k = pack8(r);
     }
     if (a.cache_dtype == kCacheF16) {
-      store16(a.value_cache + dst, v);
+      if (a.value_cache) store16(a.value_cache + dst, v);
       store16(a.key_cache + dst, k);
     } else {
       float sk[8], sv[8];

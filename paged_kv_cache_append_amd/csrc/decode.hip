@@ -32,6 +32,7 @@
 // scale multiplies the output accumulator, so the products run on the codes.
 #include <type_traits>
 
+#include "decode_rows.h"
 #include "pa_device.h"
 
 namespace pa {
@@ -42,41 +43,6 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
-
-struct RowInfo {
-  int t, b, pos, lo, hi, nsplit;
-};
-
-// Resolve the query token a decode row stands for and the split layout of its
-// admitted key interval [lo, hi).  Identical in the plan, decode and merge
-// kernels.  Returns false when the row has no work for the decode kernel.
-__device__ __forceinline__ bool resolve_row(const SeqLayout& s, int token_mode, int row,
-                                            int window, int split_tokens, int max_splits,
-                                            RowInfo& r, bool& orphan) {
-  orphan = false;
-  if (token_mode) {
-    r.t = row;
-    r.b = find_request(s.cum, s.batch, row);
-    if (r.b < 0) {
-      orphan = true;
-      return false;
-    }
-    r.pos = s.past[r.b] + (row - s.cum[r.b]);
-  } else {
-    r.b = row;
-    const int c0 = s.cum[row];
-    if (s.cum[row + 1] - c0 != 1) return false;   // served by the prefill kernel
-    r.t = c0;
-    r.pos = s.past[row];
-  }
-  if (r.t < 0 || r.t >= s.tokens) return false;
-  const int cap = s.maxblk << s.block_shift;
-  r.hi = min(r.pos + 1, cap);
-  r.lo = window > 0 ? max(0, r.pos + 1 - window) : 0;
-  const int n = r.hi - r.lo;
-  r.nsplit = n > 0 ? min((n + split_tokens - 1) / split_tokens, max_splits) : 0;
-  return true;
-}
 
 // max / sum of a value and the one 16 (resp. 32) lanes away: one lane-swap
 // instruction instead of a trip through the LDS crossbar
@@ -324,10 +290,11 @@ void decode_kernel(const DecodeArgs a) {
         const int c = 4 * ks + q;
         if (head_ok) {
           v = load16(qrow + 8 * c);
-          const bool rot = a.rotary_dim > 0 && 8 * c < a.rotary_dim;
+          const bool rot = chunk_rotated(c, a.rotary_offset, a.rotary_dim);
           if (rot || k_per_channel) {
+            const int off = rot ? a.rotary_offset : 0;
             float rr[8];
-            rotate_chunk(qrow, v, c, r.pos, a.cos, a.sin, rot ? a.rotary_dim : 0,
+            rotate_chunk(qrow + off, v, c - off / 8, r.pos, a.cos, a.sin, rot ? a.rotary_dim : 0,
                          a.rotary_interleaved, a.rotary_rows, rr);
             if (k_per_channel) {
               float ks[8];

@@ -107,6 +107,17 @@ pa_status check_quant(const pa_attn_params* p, const pa_paged_kv* kv) {
   if (st == PA_OK) st = check_scale("v", p->v_quant_type, kv->v_scale);
   if (st != PA_OK) return st;
   const bool quantized = p->cache_dtype != PA_CACHE_FP16;
+  if (p->kv_cache_layout == PA_LAYOUT_LATENT) {
+    // one physical cache, described by k_scale alone (section 8.3, 12.10)
+    if (p->v_quant_type != PA_QUANT_NONE || kv->v_scale)
+      return fail(PA_ERR_INVALID_ARGUMENT,
+                  "v_quant_type/v_scale: expected NONE/NULL with kv_cache_layout LATENT");
+    if (quantized != (p->k_quant_type != PA_QUANT_NONE))
+      return fail(PA_ERR_INVALID_ARGUMENT,
+                  "k_quant_type: expected %s with this cache_dtype, got %s",
+                  quantized ? "PER_TENSOR or PER_CHANNEL" : "NONE", quant_name(p->k_quant_type));
+    return PA_OK;
+  }
   if (!quantized && (p->k_quant_type != PA_QUANT_NONE || p->v_quant_type != PA_QUANT_NONE))
     return fail(PA_ERR_INVALID_ARGUMENT,
                 "k_quant_type/v_quant_type: expected NONE with an fp16 cache, got %s/%s",
@@ -148,6 +159,52 @@ pa_status check_norm_support(const pa_attn_params* p) {
 
 float norm_epsilon(const pa_attn_params* p) {
   return p->qk_norm_epsilon > 0.f ? p->qk_norm_epsilon : 1e-6f;
+}
+
+// Latent layout (MLA) and offset RoPE (PagedAttention -- CUDA Design
+// Document, section 12.10).
+int effective_v_head_size(const pa_attn_params* p) {
+  return p->kv_cache_layout == PA_LAYOUT_LATENT && p->v_head_size != 0 ? p->v_head_size
+                                                                       : p->head_size;
+}
+
+pa_status check_layout(const pa_attn_params* p, const pa_paged_kv* kv) {
+  if (p->kv_cache_layout != PA_LAYOUT_SEPARATE && p->kv_cache_layout != PA_LAYOUT_LATENT)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "kv_cache_layout: expected 0 (SEPARATE) or 1 (LATENT), got %d",
+                p->kv_cache_layout);
+  if (p->v_head_size < 0 || p->v_head_size > p->head_size)
+    return fail(PA_ERR_INVALID_ARGUMENT, "v_head_size: expected 0..head_size (%d), got %d",
+                p->head_size, p->v_head_size);
+  if (p->rotary_offset < 0 || p->rotary_offset % 8 != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "rotary_offset: expected a non-negative multiple of 8, got %d", p->rotary_offset);
+  if (p->kv_cache_layout == PA_LAYOUT_SEPARATE) {
+    if (p->v_head_size != 0 && p->v_head_size != p->head_size)
+      return fail(PA_ERR_INVALID_ARGUMENT,
+                  "v_head_size: %d != head_size requires kv_cache_layout LATENT", p->v_head_size);
+    if (!kv->value_cache)
+      return fail(PA_ERR_INVALID_ARGUMENT, "value_cache: expected non-NULL");
+    return PA_OK;
+  }
+  if (p->kv_num_heads != 1)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "kv_num_heads: expected 1 with kv_cache_layout LATENT, got %d", p->kv_num_heads);
+  if (kv->value_cache)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "value_cache: expected NULL with kv_cache_layout LATENT (V is a view of K)");
+  if (effective_v_head_size(p) != p->head_size && p->scale == 0.f)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "scale: an explicit scale is required when v_head_size != head_size");
+  if (p->head_sink || p->use_smooth_softmax || p->q_norm_weight || p->k_norm_weight)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "head_sink/use_smooth_softmax/QK-Norm: not allowed with kv_cache_layout LATENT");
+  if (p->do_rotary && p->rotary_offset < effective_v_head_size(p))
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "rotary_offset: expected >= v_head_size (%d) with kv_cache_layout LATENT, so "
+                "that RoPE leaves the V channels alone, got %d",
+                effective_v_head_size(p), p->rotary_offset);
+  return PA_OK;
 }
 
 pa_status check_common(const pa_attn_params* p, const pa_paged_kv* kv) {
@@ -211,7 +268,6 @@ pa_status check_common(const pa_attn_params* p, const pa_paged_kv* kv) {
     return fail(PA_ERR_INVALID_ARGUMENT,
                 "max_blocks_per_seq * block_size: expected <= 2^30 positions");
   if (!kv->key_cache) return fail(PA_ERR_INVALID_ARGUMENT, "key_cache: expected non-NULL");
-  if (!kv->value_cache) return fail(PA_ERR_INVALID_ARGUMENT, "value_cache: expected non-NULL");
   if (!aligned16(kv->key_cache) || !aligned16(kv->value_cache))
     return fail(PA_ERR_INVALID_ARGUMENT, "key_cache/value_cache: expected 16-byte alignment");
   if (!kv->block_table) return fail(PA_ERR_INVALID_ARGUMENT, "block_table: expected non-NULL");
@@ -220,6 +276,7 @@ pa_status check_common(const pa_attn_params* p, const pa_paged_kv* kv) {
   if (!kv->past_seqlens) return fail(PA_ERR_INVALID_ARGUMENT, "past_seqlens: expected non-NULL");
   pa_status st = check_sink_norm(p);
   if (st != PA_OK) return st;
+  if ((st = check_layout(p, kv)) != PA_OK) return st;
   return check_quant(p, kv);
 }
 
@@ -230,10 +287,11 @@ pa_status check_rotary(const pa_attn_params* p, const pa_paged_kv* kv, const voi
   if (p->do_rotary) {
     if (!cos_cache)
       return fail(PA_ERR_INVALID_ARGUMENT, "cos_cache/sin_cache: required when do_rotary = 1");
-    if (dim <= 0 || dim % 2 != 0 || dim > p->head_size)
+    if (dim <= 0 || dim % 2 != 0 || dim + p->rotary_offset > p->head_size)
       return fail(PA_ERR_INVALID_ARGUMENT,
-                  "rotary_dim: expected an even value in [2, head_size=%d], got %d",
-                  p->head_size, dim);
+                  "rotary_dim: expected an even value in [2, head_size - rotary_offset = %d], "
+                  "got %d",
+                  p->head_size - p->rotary_offset, dim);
     const int64_t need = (int64_t)kv->max_blocks_per_seq * p->block_size;
     if (rows < need)
       return fail(PA_ERR_INVALID_ARGUMENT,
@@ -259,6 +317,22 @@ bool rows16_prefill_fits(const pa_attn_params* p, const pa_paged_kv* kv) {
 }
 
 pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv) {
+  if (p->kv_cache_layout == PA_LAYOUT_LATENT) {
+    if (p->head_size != pa::kMlaHeadSize || effective_v_head_size(p) != pa::kMlaVHeadSize)
+      return fail(PA_ERR_UNSUPPORTED,
+                  "kv_cache_layout LATENT: served for head_size %d with v_head_size %d, got "
+                  "%d/%d",
+                  pa::kMlaHeadSize, pa::kMlaVHeadSize, p->head_size, effective_v_head_size(p));
+    if (p->cache_dtype != PA_CACHE_FP16)
+      return fail(PA_ERR_UNSUPPORTED, "kv_cache_layout LATENT: served for fp16 caches");
+    if (p->path == 2)
+      return fail(PA_ERR_UNSUPPORTED,
+                  "path 2: the latent kernel serves every token (path 0 or 1)");
+    if (kv->num_blocks * p->block_size * p->head_size * 2 > (int64_t)pa::kMlaZeroRow)
+      return fail(PA_ERR_UNSUPPORTED,
+                  "kv_cache_layout LATENT: expected a cache of at most 4 GiB - 4 KiB");
+    return PA_OK;
+  }
   if (p->head_size != 64 && p->head_size != 128 && p->head_size != 256)
     return fail(PA_ERR_UNSUPPORTED,
                 "head_size %d: the kernels serve head_size 64, 128 and 256", p->head_size);
@@ -273,6 +347,9 @@ pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv) {
 
 // ---- planning ----------------------------------------------------------------
 constexpr int64_t kTargetItems = 32768;   // decode work items aimed at (split length choice)
+// The latent kernel runs 4 waves per CU and each item's partials are 16 heads
+// x 512 channels: fewer, longer splits (about 4 items per wave slot).
+constexpr int64_t kTargetItemsLatent = 4096;
 
 struct Plan {
   bool token_mode = true;    // decode rows are tokens (else requests with q_len == 1)
@@ -303,8 +380,8 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
       break;
     }
   pl.head_chunks = pl.g / pl.chunk_heads;
-  if (p->path == 1 || p->cache_dtype != PA_CACHE_FP16)
-    pl.token_mode = true;   // quantized caches: the decode kernel serves every token
+  if (p->path == 1 || p->cache_dtype != PA_CACHE_FP16 || p->kv_cache_layout == PA_LAYOUT_LATENT)
+    pl.token_mode = true;   // quantized and latent caches: one kernel serves every token
   else if (p->path == 2)
     pl.token_mode = false;
   else
@@ -320,7 +397,9 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
   } else {
     // split length from static shapes only, so results do not depend on the bounds
     const int64_t items = std::max<int64_t>(1, (int64_t)pl.rows * p->kv_num_heads * pl.head_chunks);
-    int64_t st = (items * span + kTargetItems - 1) / kTargetItems;
+    const int64_t target =
+        p->kv_cache_layout == PA_LAYOUT_LATENT ? kTargetItemsLatent : kTargetItems;
+    int64_t st = (items * span + target - 1) / target;
     st = std::max<int64_t>(st, (span + pa::kDecodeMaxSplits - 1) / pa::kDecodeMaxSplits);
     st = (st + 63) / 64 * 64;
     pl.split_tokens = (int)std::max<int64_t>(128, std::min<int64_t>(st, 1 << 30));
@@ -332,7 +411,7 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
   size_t cur = 0;
   if (pl.listed) {
     const size_t per = (size_t)pl.rows * p->num_heads * pl.max_splits;
-    pl.off_ml = align256(per * p->head_size * sizeof(float));
+    pl.off_ml = align256(per * effective_v_head_size(p) * sizeof(float));
     pl.off_entries = pl.off_ml + align256(per * 2 * sizeof(float));
     pl.off_count = pl.off_entries + align256((size_t)pl.rows * pl.max_splits * sizeof(pa::DecodeEntry));
     cur = pl.off_count + 256;
@@ -461,7 +540,12 @@ pa_status pa_append_kv(const pa_attn_params* params, const pa_paged_kv* kv, cons
     return st;
   if (kv->token_count == 0) return PA_OK;
   if ((st = check_norm_support(params)) != PA_OK) return st;
-  if (!key || !value) return fail(PA_ERR_INVALID_ARGUMENT, "key/value: expected non-NULL");
+  const bool latent = params->kv_cache_layout == PA_LAYOUT_LATENT;
+  if (!key || (!value && !latent))
+    return fail(PA_ERR_INVALID_ARGUMENT, "key/value: expected non-NULL");
+  if (latent && value)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "value: expected NULL with kv_cache_layout LATENT (V is a view of K)");
   if (!aligned16(key) || !aligned16(value))
     return fail(PA_ERR_INVALID_ARGUMENT, "key/value: expected 16-byte alignment");
   if ((reinterpret_cast<uintptr_t>(kv->slot_mapping) & 3) != 0)
@@ -487,6 +571,7 @@ pa_status pa_append_kv(const pa_attn_params* params, const pa_paged_kv* kv, cons
   a.v_scale = kv->v_scale;
   a.k_norm = static_cast<const uint16_t*>(params->k_norm_weight);
   a.norm_eps = norm_epsilon(params);
+  a.rotary_offset = params->do_rotary ? params->rotary_offset : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   StageScope scope(PA_STAGE_APPEND, s);
   return device_status(pa::launch_append(a, s), "append kernel launch");
@@ -601,6 +686,10 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
   d.v_scale = kv->v_scale;
   d.head_sink = static_cast<const uint16_t*>(params->head_sink);
   d.use_sink = params->head_sink || params->use_smooth_softmax ? 1 : 0;
+  d.rotary_offset = params->do_rotary ? params->rotary_offset : 0;
+  const bool latent = params->kv_cache_layout == PA_LAYOUT_LATENT;
+  const int DV = effective_v_head_size(params);
+  d.v_head_size = DV;
   // QK-Norm prologue (section 7.2): normalized queries staged in the
   // workspace; every attention kernel reads (and rotates) them from there
   if (pl.q_norm) {
@@ -651,7 +740,7 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     pa_.split_tokens = pl.split_tokens;
     pa_.max_splits = pl.max_splits;
     pa_.window = params->local_window_size;
-    pa_.row_width = params->num_heads * D;
+    pa_.row_width = params->num_heads * DV;
     StageScope scope(PA_STAGE_PLAN, s);
     if ((st = device_status(pa::launch_plan(pa_, s), "plan kernel launch")) != PA_OK)
       return joined(st);
@@ -686,6 +775,7 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     f.pool32 = pool_fits_32bit(params, kv) ? 1 : 0;
     f.head_sink = d.head_sink;
     f.use_sink = d.use_sink;
+    f.rotary_offset = d.rotary_offset;
     const dim3 grid(pl.prefill_tiles * pl.prefill_chunks + 1, params->kv_num_heads);
     {
       StageScope scope(PA_STAGE_PREFILL, ps);
@@ -706,7 +796,9 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
       // beside a prefill, one decode workgroup per CU is left out so the
       // prefill tiles and the decode workers are resident together whichever
       // kernel is dispatched first
-      const int per_cu = pa::decode_workgroups_per_cu(D, d.use_softcap != 0, d.cache_dtype);
+      const int per_cu = latent ? pa::mla_workgroups_per_cu(d.use_softcap != 0)
+                                : pa::decode_workgroups_per_cu(D, d.use_softcap != 0,
+                                                               d.cache_dtype);
       const int64_t resident = (int64_t)std::max(1, overlap ? per_cu - 1 : per_cu) * device_cus();
       wgs = std::min<int64_t>((bound + pa::kDecodeWaves - 1) / pa::kDecodeWaves, resident);
     } else {
@@ -714,7 +806,8 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     }
     {
       StageScope scope(PA_STAGE_DECODE, s);
-      if ((st = device_status(pa::launch_decode(d, D, (int)std::max<int64_t>(wgs, 1), s),
+      const int n = (int)std::max<int64_t>(wgs, 1);
+      if ((st = device_status(latent ? pa::launch_mla(d, n, s) : pa::launch_decode(d, D, n, s),
                               "decode kernel launch")) != PA_OK)
         return joined(st);
     }
@@ -726,7 +819,7 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
       mg.out = d.out;
       mg.rows = pl.rows;
       mg.num_heads = params->num_heads;
-      mg.head_size = D;
+      mg.head_size = DV;
       mg.token_mode = d.token_mode;
       mg.split_tokens = pl.split_tokens;
       mg.max_splits = pl.max_splits;

@@ -132,6 +132,14 @@ __device__ __forceinline__ u32x4 norm_chunk(u32x4 x, float r, const uint16_t* w,
 // multiply-add below rounds the exact result once -- the stored key is then
 // fp16(fp32(exact)).  Positions outside the table are not rotated (memory
 // safety for out-of-contract device lengths).
+// Whether chunk c (channels [8c, 8c + 8)) of a head row meets the rotary
+// window [off, off + rot) (PagedAttention -- CUDA Design Document, section
+// 12.5: RoPE may cover a suffix; off is a multiple of 8).  Callers then pass
+// the row from channel off and the chunk index c - off / 8.
+__device__ __forceinline__ bool chunk_rotated(int c, int off, int rot) {
+  return rot > 0 && 8 * c >= off && 8 * c < off + rot;
+}
+
 __device__ __forceinline__ float rot_pair(float x, float y, float cs, float sn, bool second) {
   const float ys = y * sn;  // exact
   return second ? __builtin_fmaf(x, cs, ys) : __builtin_fmaf(x, cs, -ys);

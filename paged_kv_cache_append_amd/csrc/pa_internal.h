@@ -51,6 +51,7 @@ struct AppendArgs {
   const float* v_scale;
   const uint16_t* k_norm; // QK-Norm weight of K (fp16 [D]) or null
   float norm_eps;
+  int32_t rotary_offset;  // first rotated channel (multiple of 8)
 };
 
 // QK-Norm of the queries into a staging buffer (the prologue): rows of
@@ -113,6 +114,8 @@ struct DecodeArgs {
   const float* v_scale;
   const uint16_t* head_sink;    // fp16 [H] sink logits, or null (zero sinks)
   int32_t use_sink;             // 0: no sink term
+  int32_t rotary_offset;        // first rotated channel (multiple of 8)
+  int32_t v_head_size;          // output channels per head (latent: the V view of K)
 };
 
 // Plan kernel (one workgroup): lists (row, split) entries of every row with
@@ -179,6 +182,7 @@ struct PrefillArgs {
   int32_t pool32;               // each cache is smaller than 4 GiB (32-bit byte offsets)
   const uint16_t* head_sink;    // as in DecodeArgs
   int32_t use_sink;
+  int32_t rotary_offset;
 };
 
 // Kernel start/stop events of the launch being made on this thread (set by
@@ -213,6 +217,15 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStr
 hipError_t launch_prefill_merge(const PrefillArgs& a, int head_size, hipStream_t st);
 // 8-wave prefill kernel of 16 rows per wave (head_size 256); grid as launch_prefill
 hipError_t launch_prefill16(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st);
+// latent attention (MLA): kv_num_heads 1, head_size 576, V = the leading 512
+// channels of K; every row in token mode, items as for the decode kernel
+hipError_t launch_mla(const DecodeArgs& a, int workgroups, hipStream_t st);
+int mla_workgroups_per_cu(bool softcap);
+constexpr int kMlaHeadSize = 576;
+constexpr int kMlaVHeadSize = 512;
+// byte offset of the latent kernel's zero rows (past the pool; a row read
+// from there ends below 2^32): latent pools hold at most this many bytes
+constexpr uint32_t kMlaZeroRow = 0xFFFFF000u;
 
 constexpr int kPrefillRows = 128;   // query rows (token x head) per prefill workgroup
 constexpr int kDecodeWaves = 4;     // independent decode workers per workgroup

@@ -190,10 +190,11 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
       const uint16_t* qrow = a.query + (int64_t)t * HD + (int64_t)head * D;
       const int c = 4 * ks + q4;
       v = load16(qrow + 8 * c);
-      if (a.rotary_dim > 0 && 8 * c < a.rotary_dim) {
+      if (chunk_rotated(c, a.rotary_offset, a.rotary_dim)) {
+        const int off = a.rotary_offset;
         float rr[8];
-        rotate_chunk(qrow, v, c, pos, a.cos, a.sin, a.rotary_dim, a.rotary_interleaved,
-                     a.rotary_rows, rr);
+        rotate_chunk(qrow + off, v, c - off / 8, pos, a.cos, a.sin, a.rotary_dim,
+                     a.rotary_interleaved, a.rotary_rows, rr);
         v = pack8(rr);
       }
     }

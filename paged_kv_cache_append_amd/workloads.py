@@ -362,6 +362,57 @@ def make_workload(name: str, poison: bool = False) -> Workload:
     raise KeyError(name)
 
 
+# ---------------------------------------------------------------------------
+# Latent attention (MLA) workloads: absorbed DeepSeek-style rows of 576
+# channels (512 latent + 64 rotary at offset 512), one kv head, V = the
+# leading 512 channels (PagedAttention -- CUDA Design Document, section 12).
+# The scale is 1/sqrt(192), the pre-absorption head width (section 12.6).
+# seed 1100 + index; extra["latent"] marks them (value rows are drawn but
+# unused).
+# ---------------------------------------------------------------------------
+
+MLA_CONFIG_NAMES = ("mla_decode_tp8", "mla_decode_dp")
+MLA_HEAD_SIZE, MLA_V_HEAD_SIZE, MLA_ROTARY_OFFSET, MLA_ROTARY_DIM = 576, 512, 512, 64
+MLA_SCALE = 1.0 / math.sqrt(192.0)
+
+
+def _mla_case(name, seed, q_lens, past, num_heads, rng, block_size=64, **kw):
+    w = build_case(name, seed, q_lens=q_lens, past=past, num_heads=num_heads, kv_num_heads=1,
+                   head_size=MLA_HEAD_SIZE, block_size=block_size, scale=MLA_SCALE,
+                   do_rotary=1, rotary_dim=MLA_ROTARY_DIM, rng=rng, **kw)
+    w.extra["latent"] = True
+    w.extra["v_head_size"] = MLA_V_HEAD_SIZE
+    w.extra["rotary_offset"] = MLA_ROTARY_OFFSET
+    return w
+
+
+def make_mla_workload(name: str) -> Workload:
+    idx = MLA_CONFIG_NAMES.index(name)
+    seed = 1100 + idx
+    rng = np.random.default_rng(seed)
+    if name == "mla_decode_tp8":
+        past = rng.integers(1024, 16384, size=128, endpoint=True)
+        return _mla_case(name, seed, [1] * 128, past, 16, rng,
+                         description="128 decode seqs, past U[1024,16384]; H=16 (one GPU's "
+                                     "share of 128 heads), latent 576/512, bs=64")
+    past = rng.integers(1024, 8192, size=64, endpoint=True)
+    return _mla_case(name, seed, [1] * 64, past, 128, rng,
+                     description="64 decode seqs, past U[1024,8192]; H=128, latent 576/512, "
+                                 "bs=64")
+
+
+def scaled_down_mla(name: str) -> Workload:
+    """Small stand-ins for the MLA workloads (the oracle takes seconds)."""
+    idx = MLA_CONFIG_NAMES.index(name)
+    seed = 2100 + idx
+    rng = np.random.default_rng(seed)
+    if name == "mla_decode_tp8":
+        past = list(rng.integers(1, 900, size=5, endpoint=True))
+        return _mla_case(name + "_small", seed, [1] * 5, past, 16, rng)
+    past = list(rng.integers(1, 600, size=3, endpoint=True))
+    return _mla_case(name + "_small", seed, [1] * 3, past, 128, rng)
+
+
 def scaled_down(name: str, poison: bool = False) -> Workload:
     """A small stand-in with the same head layout, block size and features as
     benchmark workload ``name`` (lengths cut so the oracle finishes in
@@ -437,7 +488,10 @@ def to_device(w: Workload, device="cuda", pools: bool = True, threads: Optional[
         d["sin"] = torch.from_numpy(w.sin_cache).to(device)
     if pools:
         tdt = {CACHE_FP16: torch.float16, CACHE_INT8: torch.int8}.get(cache_dtype, torch.uint8)
-        for kind, name in ((KIND_K, "key_cache"), (KIND_V, "value_cache")):
+        kinds = ((KIND_K, "key_cache"),) if w.extra.get("latent") else \
+            ((KIND_K, "key_cache"), (KIND_V, "value_cache"))
+        d["value_cache"] = None          # a latent workload has one cache
+        for kind, name in kinds:
             dev = torch.empty(w.pool_shape(), dtype=tdt, device=device)
 
             def sink(start, arr, dev=dev):

@@ -42,7 +42,7 @@ def params(**kw):
              local_window_size=-1, do_rotary=0, rotary_interleaved=0, path=0, split_tokens=0,
              prefill_pieces=0, prefill_kernel=0, cache_dtype=0, k_quant_type=0, v_quant_type=0,
              head_sink=None, use_smooth_softmax=0, q_norm_weight=None, k_norm_weight=None,
-             qk_norm_epsilon=0.0)
+             qk_norm_epsilon=0.0, kv_cache_layout=0, v_head_size=0, rotary_offset=0)
     d.update(kw)
     return _lib.AttnParams(*[d[f] for f, _ in _lib.AttnParams._fields_])
 
@@ -133,6 +133,24 @@ NEGATIVE += [
     (dict(qk_norm_epsilon=float("inf")), {}, 1, "qk_norm_epsilon"),
 ]
 
+# latent layout (MLA, section 12.10) and offset RoPE
+LAT = dict(kv_cache_layout=1, kv_num_heads=1, num_heads=8, head_size=576, v_head_size=512,
+           scale=0.07)
+LAT_KV = dict(value_cache=None)
+NEGATIVE += [
+    ({}, dict(value_cache=None), 1, "value_cache: expected non-NULL"),
+    (dict(kv_cache_layout=2), {}, 1, "kv_cache_layout"),
+    (dict(v_head_size=-1), {}, 1, "v_head_size: expected 0..head_size"),
+    (dict(v_head_size=32), {}, 1, "requires kv_cache_layout LATENT"),
+    (dict(rotary_offset=4), {}, 1, "rotary_offset"),
+    (dict(LAT, kv_num_heads=2), LAT_KV, 1, "kv_num_heads: expected 1"),
+    (LAT, {}, 1, "value_cache: expected NULL"),
+    (dict(LAT, scale=0.0), LAT_KV, 1, "explicit scale"),
+    (dict(LAT, use_smooth_softmax=1), LAT_KV, 1, "not allowed with kv_cache_layout LATENT"),
+    (dict(LAT, cache_dtype=1, k_quant_type=1, v_quant_type=1), dict(LAT_KV, k_scale=FAKE,
+     v_scale=FAKE), 1, "v_quant_type/v_scale"),
+]
+
 QUANT = dict(cache_dtype=1, k_quant_type=1, v_quant_type=2)
 QUANT_KV = dict(k_scale=FAKE + 4, v_scale=FAKE)     # per tensor: 4-byte; per channel: 16-byte
 
@@ -205,6 +223,28 @@ def test_qk_norm_head_size_limit_and_workspace():
     b = plan(params(**norm), paged(token_count=4, batch_size=4))
     assert b["q_norm"] == "1" and a["q_norm"] == "0"
     assert int(b["workspace"]) - int(a["workspace"]) >= 4 * 8 * 64 * 2
+
+
+def test_latent_rules():
+    kv = paged(**LAT_KV)
+    # RoPE must leave the V channels (the leading 512) alone
+    p = params(**LAT, do_rotary=1, rotary_offset=256)
+    assert call_forward(p, kv, cos=FAKE, sin=FAKE, rows=128, rdim=64) == 1
+    assert "rotary_offset" in err()
+    # offset + rotary_dim within the head
+    p = params(**LAT, do_rotary=1, rotary_offset=544)
+    assert call_forward(p, kv, cos=FAKE, sin=FAKE, rows=128, rdim=64) == 1
+    assert "rotary_dim" in err()
+    # the append takes no value rows
+    assert call_append(params(**LAT), kv) == 1 and "value: expected NULL" in err()
+    # kernel shapes: 576/512 fp16 only; path 2 has no latent kernel
+    assert call_forward(params(**dict(LAT, head_size=64, v_head_size=32)), kv) == 2
+    assert "LATENT: served for head_size 576" in err()
+    assert call_forward(params(**LAT, path=2), kv) == 2 and "latent kernel" in err()
+    big = paged(value_cache=None, num_blocks=(1 << 32) // (16 * 576 * 2) + 1)
+    assert call_forward(params(**LAT), big) == 2 and "4 GiB" in err()
+    pl = plan(params(**LAT), paged(token_count=40, batch_size=4, **LAT_KV))
+    assert pl["mode"] == "token" and pl["prefill_grid"] == "(0,0)"
 
 
 def test_workspace_must_cover_the_plan():
