@@ -465,14 +465,6 @@ def main():
     import paged_kv_cache_append_amd as pa
     from paged_kv_cache_append_amd import workloads as wl
 
-    if args.config in wl.MLA_CONFIG_NAMES:
-        if args.cache != "fp16" or args.head_sink or args.smooth_softmax or args.qk_norm:
-            print("bench.py: the latent workloads run with an fp16 cache and no sink or "
-                  "QK-Norm (section 12.10)", file=sys.stderr)
-            sys.exit(2)
-        bench_mla(args)
-        return
-
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 2
         src = torch.ones(n, dtype=torch.float16, device="cuda")
@@ -488,6 +480,14 @@ def main():
               f"{args.copy_calibration_mib} MiB written per launch, "
               f"{2 * n * 2 / (ms * 1e-3) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
         del src, dst
+
+    if args.config in wl.MLA_CONFIG_NAMES:
+        if args.cache != "fp16" or args.head_sink or args.smooth_softmax or args.qk_norm:
+            print("bench.py: the latent workloads run with an fp16 cache and no sink or "
+                  "QK-Norm (section 12.10)", file=sys.stderr)
+            sys.exit(2)
+        bench_mla(args)
+        return
 
     w = wl.make_workload(args.config)
     cd = {"fp16": wl.CACHE_FP16, "int8": wl.CACHE_INT8, "fp8": wl.CACHE_FP8}[args.cache]
