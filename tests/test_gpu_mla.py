@@ -116,3 +116,14 @@ def test_mla_full_size_sampled(name):
     err = max_err(out[sub.extra["parent_rows"]], ref)
     print(f"[mla] sampled max_abs_err={err:.3e}", flush=True)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("heads", [64, 80])
+def test_mla_shared_tile_head_groups(heads):
+    """64+ heads: the four waves of a workgroup share one tile pair (shared
+    mode); 80 heads leave three waves of the second group with no chunk of
+    their own (they only copy)."""
+    rng = np.random.default_rng(3403 + heads)
+    w = wl._mla_case(f"mla_heads{heads}", 3403 + heads, [1, 1, 5, 1], [900, 33, 200, 2100],
+                     heads, rng, softcap=25.0, local_window_size=1500, extra_tokens=2)
+    check(w)
