@@ -119,6 +119,11 @@ class Workload:
         out = np.empty((len(ids),) + shape, code_dtype(cache_dtype))
         for n, p in enumerate(ids):
             out[n] = draw_code_block(self.seed, kind, p, shape, cache_dtype)
+        if self.poison and cache_dtype == CACHE_FP8:
+            # unfilled slots hold the e4m3fn NaN code (int8 has no NaN)
+            filled = self._filled_tokens()
+            for n, p in enumerate(ids):
+                out[n, filled.get(p, 0):] = 0x7F
         return out
 
     def full_pool(self, kind: int, threads: Optional[int] = None,

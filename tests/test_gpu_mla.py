@@ -67,7 +67,7 @@ def check(w, **over):
     dev = device_inputs(w)
     out = gpu_latent(w, dev, **over)
     nk, ref = oracle_latent(w, w.pool_blocks(wl.KIND_K, range(w.num_blocks)))
-    assert np.array_equal(dev["key_cache"].cpu().numpy(), nk), "latent pool differs"
+    assert dev["key_cache"].cpu().numpy().tobytes() == nk.tobytes(), "latent pool differs"
     err = max_err(out, ref)
     print(f"[mla] max_abs_err={err:.3e}", flush=True)
     assert err <= TOL, err
@@ -127,3 +127,15 @@ def test_mla_shared_tile_head_groups(heads):
     w = wl._mla_case(f"mla_heads{heads}", 3403 + heads, [1, 1, 5, 1], [900, 33, 200, 2100],
                      heads, rng, softcap=25.0, local_window_size=1500, extra_tokens=2)
     check(w)
+
+
+def test_mla_poisoned_pool():
+    """Every slot no request has filled holds NaN: a read outside a row's
+    admitted keys (or a masked key multiplied by zero) would show."""
+    rng = np.random.default_rng(3404)
+    w = wl._mla_case("mla_poison", 3404, [1, 3, 1], [70, 200, 1000], 64, rng, poison=True,
+                     local_window_size=300)
+    check(w)
+    rng = np.random.default_rng(3405)
+    w = wl._mla_case("mla_poison16", 3405, [1, 1, 4], [129, 4000, 63], 16, rng, poison=True)
+    check(w, split_tokens=128)

@@ -107,3 +107,10 @@ def test_quantized_explicit_slots():
     nk, nv = oracle_append_quant(w, F8, PC, PT, ks, vs, slot_mapping=sm)
     assert np.array_equal(dev["key_cache"].cpu().numpy(), nk)
     assert np.array_equal(dev["value_cache"].cpu().numpy(), nv)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_mixed", "long_context_decode_rope"])
+def test_quantized_poisoned_pool(name):
+    """Every slot no request has filled holds the e4m3fn NaN code: a read
+    outside a row's admitted keys would show in the output."""
+    check_quant(wl.scaled_down(name, poison=True), F8, PC, PT)
