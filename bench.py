@@ -265,10 +265,17 @@ def summarize_pmc(paths):
 STAGES = ("append", "decode", "merge", "prefill", "prefill_merge", "plan", "q_norm")
 
 
+WARMUP_SECONDS = 0.5   # default warm-up: at least this long (and 10 steps)
+
+
 def measure(step, steps, warmup):
     """W untimed steps, then K timed steps with nothing else on the stream
     (the throughput figure), then the same K steps with every kernel's
-    dispatch timestamped on its stream (the per-kernel durations)."""
+    dispatch timestamped on its stream (the per-kernel durations).  With
+    ``warmup`` None the warm-up runs until at least WARMUP_SECONDS have passed
+    (and 10 steps): the clocks of an idle GPU take that long to settle, and a
+    short warm-up understates a long step by several percent.  Returns the
+    warm-up step count too."""
     import torch
 
     import paged_kv_cache_append_amd as pa
@@ -284,15 +291,24 @@ def measure(step, steps, warmup):
         torch.cuda.synchronize()
         return start.elapsed_time(stop)
 
-    for _ in range(warmup):
-        step()
+    if warmup is None:
+        warmup = 0
+        t0 = time.perf_counter()
+        while warmup < 10 or time.perf_counter() - t0 < WARMUP_SECONDS:
+            for _ in range(10):
+                step()
+            warmup += 10
+            torch.cuda.synchronize()
+    else:
+        for _ in range(warmup):
+            step()
     torch.cuda.synchronize()
     ms_step = timed(steps) / steps
     pa.timing_enable(8 * steps + 16)
     ms_step_instrumented = timed(steps) / steps
     stages = {s: pa.timing_read(s) for s in STAGES}
     pa.timing_disable()
-    return ms_step, ms_step_instrumented, stages
+    return ms_step, ms_step_instrumented, stages, warmup
 
 
 def mla_work(w):
@@ -380,7 +396,7 @@ def bench_mla(args):
         pa.forward(a, dev["query"], dev["key_cache"], None, dev["block_table"], dev["cum"],
                    dev["past"], dev["cos"], dev["sin"], workspace=ws, out=out)
 
-    ms_step, ms_step_instrumented, stages = measure(step, args.steps, args.warmup)
+    ms_step, ms_step_instrumented, stages, args.warmup = measure(step, args.steps, args.warmup)
     per = {s: (ms / n * 1e3 if n else 0.0) for s, (ms, n) in stages.items()}
     nbytes, flops = mla_work(w)
     t = per["decode"] * 1e-6
@@ -424,7 +440,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: at least "
+                         f"{WARMUP_SECONDS} s of steps, and 10; the count is reported)")
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cache", choices=("fp16", "int8", "fp8"), default="fp16",
@@ -536,7 +554,7 @@ def main():
         pa.forward(a, dev["query"], dev["key_cache"], dev["value_cache"], dev["block_table"],
                    dev["cum"], dev["past"], dev["cos"], dev["sin"], workspace=ws, out=out, **sc)
 
-    ms_step, ms_step_instrumented, stages = measure(step, args.steps, args.warmup)
+    ms_step, ms_step_instrumented, stages, args.warmup = measure(step, args.steps, args.warmup)
 
     # the append alone, with derived slots (from the steps above) and with an
     # explicit slot mapping (distinct slots scattered over the pool, as a
