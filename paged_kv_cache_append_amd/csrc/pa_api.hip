@@ -793,14 +793,16 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     int64_t wgs;
     if (pl.listed) {
       const int64_t bound = (int64_t)pl.rows * pl.max_splits * hc;
-      // beside a prefill, one decode workgroup per CU is left out so the
-      // prefill tiles and the decode workers are resident together whichever
-      // kernel is dispatched first
+      // alone, persistent workers fill the chip; beside a prefill, one
+      // workgroup per four possible items instead (the ones past the list
+      // exit at once), so decode work spreads into the CUs the prefill tiles
+      // free as they finish rather than staying on the share it started with
       const int per_cu = latent ? pa::mla_workgroups_per_cu(d.use_softcap != 0)
                                 : pa::decode_workgroups_per_cu(D, d.use_softcap != 0,
                                                                d.cache_dtype);
-      const int64_t resident = (int64_t)std::max(1, overlap ? per_cu - 1 : per_cu) * device_cus();
-      wgs = std::min<int64_t>((bound + pa::kDecodeWaves - 1) / pa::kDecodeWaves, resident);
+      const int64_t resident = (int64_t)per_cu * device_cus();
+      const int64_t per_item = (bound + pa::kDecodeWaves - 1) / pa::kDecodeWaves;
+      wgs = overlap ? per_item : std::min<int64_t>(per_item, resident);
     } else {
       wgs = ((int64_t)pl.rows * hc + pa::kDecodeWaves - 1) / pa::kDecodeWaves;
     }
