@@ -793,16 +793,21 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     int64_t wgs;
     if (pl.listed) {
       const int64_t bound = (int64_t)pl.rows * pl.max_splits * hc;
-      // alone, persistent workers fill the chip; beside a prefill, one
-      // workgroup per four possible items instead (the ones past the list
-      // exit at once), so decode work spreads into the CUs the prefill tiles
-      // free as they finish rather than staying on the share it started with
+      // One workgroup per four possible items (those past the device list
+      // exit at once) beside a prefill, so decode work spreads into the CUs
+      // the prefill tiles free as they finish, and for long items (>= 256 KB
+      // of K/V each), whose static round-robin over persistent workers leaves
+      // a ragged tail that the hardware's dispatch evens out.  Short items
+      // keep persistent workers: there extra workgroups cost more than they
+      // balance.
       const int per_cu = latent ? pa::mla_workgroups_per_cu(d.use_softcap != 0)
                                 : pa::decode_workgroups_per_cu(D, d.use_softcap != 0,
                                                                d.cache_dtype);
       const int64_t resident = (int64_t)per_cu * device_cus();
       const int64_t per_item = (bound + pa::kDecodeWaves - 1) / pa::kDecodeWaves;
-      wgs = overlap ? per_item : std::min<int64_t>(per_item, resident);
+      const int64_t row_bytes = latent ? 2 * D : 2 * 2 * D;   // K + V (or the latent row)
+      const bool long_items = (int64_t)pl.split_tokens * row_bytes >= (256 << 10);
+      wgs = overlap || long_items ? per_item : std::min<int64_t>(per_item, resident);
     } else {
       wgs = ((int64_t)pl.rows * hc + pa::kDecodeWaves - 1) / pa::kDecodeWaves;
     }
