@@ -246,6 +246,12 @@ void decode_kernel(const DecodeArgs a) {
     }
   }
 
+  // listed mode: the next item's entry is read while this item runs
+  DecodeEntry en_next;
+  {
+    const int first = blockIdx.x * kDecodeWaves + wave;
+    if (a.listed && first < total) en_next = a.entries[first / HC];
+  }
   for (int item = blockIdx.x * kDecodeWaves + wave; item < total; item += nworkers) {
     const int e = item / HC;
     const int kvhc = item - e * HC;
@@ -255,7 +261,8 @@ void decode_kernel(const DecodeArgs a) {
     int row, split, k_lo, k_hi;
     RowInfo r;
     if (a.listed) {
-      const DecodeEntry en = a.entries[e];
+      const DecodeEntry en = en_next;
+      if (item + nworkers < total) en_next = a.entries[(item + nworkers) / HC];
       row = en.row;
       split = en.split;
       k_lo = en.k_lo;
