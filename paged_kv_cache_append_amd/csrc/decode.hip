@@ -246,8 +246,12 @@ void decode_kernel(const DecodeArgs a) {
     }
   }
 
-  // listed mode: the next item's entry is read while this item runs
+  // listed mode: the next item's entry is read while this item runs, and
+  // (once this item's first tile loads are out) the block-table entries of
+  // the next item's first segment, one per lane, when it spans <= 64 blocks
   DecodeEntry en_next;
+  int32_t tbl_next = -1;
+  bool tbl_next_ok = false;
   {
     const int first = blockIdx.x * kDecodeWaves + wave;
     if (a.listed && first < total) en_next = a.entries[first / HC];
@@ -325,17 +329,29 @@ void decode_kernel(const DecodeArgs a) {
     const char* vb = reinterpret_cast<const char*>(a.value_cache) + (int64_t)kvh * D * ES;
     const int32_t* bt = sl.block_table + (int64_t)r.b * sl.maxblk;
 
+    const bool have_next = a.listed && item + nworkers < total;
+    const bool use_prefetch = tbl_next_ok;
+    tbl_next_ok = false;
     for (int seg_lo = k_lo; seg_lo < k_hi;) {
       const int first_bi = seg_lo >> shift;
       const int seg_hi = min(k_hi, (first_bi + C::TBL) << shift);
       const int n_bi = ((seg_hi - 1) >> shift) - first_bi + 1;
       bool hole = false;
-      for (int i = lane; i < n_bi; i += 64) {
-        const int bi = first_bi + i;
-        int v = bi < sl.maxblk ? bt[bi] : -1;
-        if (v >= sl.num_blocks) v = -1;
-        hole |= v < 0;
-        tbl[i] = v;
+      if (use_prefetch && seg_lo == k_lo) {   // staged by the previous item (n_bi <= 64)
+        if (lane < n_bi) {
+          int v = tbl_next;
+          if (v >= sl.num_blocks) v = -1;
+          hole = v < 0;
+          tbl[lane] = v;
+        }
+      } else {
+        for (int i = lane; i < n_bi; i += 64) {
+          const int bi = first_bi + i;
+          int v = bi < sl.maxblk ? bt[bi] : -1;
+          if (v >= sl.num_blocks) v = -1;
+          hole |= v < 0;
+          tbl[i] = v;
+        }
       }
       const bool any_hole = __any(hole);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -346,6 +362,20 @@ void decode_kernel(const DecodeArgs a) {
       RawChunk<CT> kr[C::NI], vr[C::NI];
       uint32_t okm = load_tile<D, CT>(kb, vb, tbl, first_bi, shift, tok_stride, seg_lo, seg_hi,
                                       lane, kr, vr);
+      if (have_next && seg_lo == k_lo) {
+        // the next item's first-segment table, behind this tile's loads
+        const int nlo = en_next.k_lo, nhi = en_next.k_hi;
+        const int nfirst = nlo >> shift;
+        const int nseg_hi = min(nhi, (nfirst + C::TBL) << shift);
+        const int nn = nhi > nlo ? ((nseg_hi - 1) >> shift) - nfirst + 1 : 0;
+        if (nn <= 64) {
+          const int bi = nfirst + lane;
+          tbl_next = lane < nn && bi < sl.maxblk
+                         ? sl.block_table[(int64_t)en_next.b * sl.maxblk + bi]
+                         : -1;
+          tbl_next_ok = true;
+        }
+      }
       for (int it = 0; it < ntile; ++it) {
         const int k0 = seg_lo + it * C::KT;
         const bool more = it + 1 < ntile;
