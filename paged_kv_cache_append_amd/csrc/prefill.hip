@@ -68,7 +68,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char V0[C::SLOTS * C::VSLOT];
   __shared__ __attribute__((aligned(1024))) char V1[C::SLOTS * C::VSLOT];
   __shared__ int32_t s_tbl[C::SEGT];
-  __shared__ uint8_t ok0[C::KT], ok1[C::KT];
   __shared__ int sh_b, sh_tile;
 
   const SeqLayout& sl = a.s;
