@@ -401,8 +401,12 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
         p->kv_cache_layout == PA_LAYOUT_LATENT ? kTargetItemsLatent : kTargetItems;
     int64_t st = (items * span + target - 1) / target;
     st = std::max<int64_t>(st, (span + pa::kDecodeMaxSplits - 1) / pa::kDecodeMaxSplits);
+    // beside a prefill, which holds part of the CUs for most of the decode,
+    // fewer and longer items cost less than finer balance gains (partials,
+    // merge work, per-item start-up)
+    st = std::max<int64_t>(st, pl.prefill ? 256 : 128);
     st = (st + 63) / 64 * 64;
-    pl.split_tokens = (int)std::max<int64_t>(128, std::min<int64_t>(st, 1 << 30));
+    pl.split_tokens = (int)std::min<int64_t>(st, 1 << 30);
   }
   int64_t kv_ext = mk > 0 ? std::min<int64_t>(mk, cap) : cap;   // bound only trims the grid
   if (p->local_window_size > 0) kv_ext = std::min<int64_t>(kv_ext, p->local_window_size);
