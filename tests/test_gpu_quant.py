@@ -16,12 +16,14 @@ pytestmark = pytest.mark.gpu
 
 I8, F8 = wl.CACHE_INT8, wl.CACHE_FP8
 PT, PC = wl.QUANT_PER_TENSOR, wl.QUANT_PER_CHANNEL
-NAMES = {I8: "int8", F8: "fp8", PT: "tensor", PC: "channel"}
+CACHE_NAMES = {I8: "int8", F8: "fp8"}
+QUANT_NAMES = {PT: "tensor", PC: "channel"}
 
 
 def check_quant(w, cd, kq, vq, slot_mapping=None, **over):
     print(f"\n[quant] {w.name} T={w.token_count} H={w.num_heads} Hkv={w.kv_num_heads} "
-          f"D={w.head_size} bs={w.block_size} cache={NAMES[cd]} k={NAMES[kq]} v={NAMES[vq]} "
+          f"D={w.head_size} bs={w.block_size} cache={CACHE_NAMES[cd]} k={QUANT_NAMES[kq]} "
+          f"v={QUANT_NAMES[vq]} "
           f"slots={'explicit' if slot_mapping is not None else 'derived'} {over}", flush=True)
     ks, vs = quant_inputs(w, cd, kq, vq)
     dev, out = gpu_quant_step(w, cd, kq, vq, ks, vs, slot_mapping=slot_mapping, **over)
@@ -55,7 +57,7 @@ QUANT_CASES = [
 
 
 @pytest.mark.parametrize("case", QUANT_CASES, ids=lambda c: "-".join(
-    [c[0]] + [NAMES[x] for x in c[1:]]))
+    [c[0], CACHE_NAMES[c[1]], QUANT_NAMES[c[2]], QUANT_NAMES[c[3]]]))
 def test_quantized_scaled_configs(case):
     name, cd, kq, vq = case
     check_quant(wl.scaled_down(name), cd, kq, vq)
@@ -114,3 +116,57 @@ def test_quantized_poisoned_pool(name):
     """Every slot no request has filled holds the e4m3fn NaN code: a read
     outside a row's admitted keys would show in the output."""
     check_quant(wl.scaled_down(name, poison=True), F8, PC, PT)
+
+
+@pytest.mark.parametrize("cd", [I8, F8], ids=["int8", "fp8"])
+def test_quantized_full_size_sampled(cd):
+    """decode_heavy_256 at full size with per-channel K and V scales, as
+    bench.py --cache times it: the codes of every block that receives a new
+    token equal the oracle's byte for byte, a sample of untouched blocks keeps
+    its codes, and sampled requests (the longest, the shortest and two drawn
+    ones) match the oracle's attention over the dequantized pool, recomputed
+    one request at a time on a compact copy of its blocks."""
+    import torch
+    import oracle
+    from pa_harness import oracle_append_quant, oracle_forward_quant, quant_kw, rot_kw
+    w = wl.make_workload("decode_heavy_256")
+    print(f"\n[quant] full {w.name} B={w.batch_size} blocks={w.num_blocks} "
+          f"cache={CACHE_NAMES[cd]} k=channel v=channel", flush=True)
+    ks, vs = quant_inputs(w, cd, PC, PC)
+    dev, out = gpu_quant_step(w, cd, PC, PC, ks, vs)
+
+    ids = sorted({int(w.block_table[b, (int(w.past[b]) + i) // w.block_size])
+                  for b in range(w.batch_size) for i in range(int(w.q_lens[b]))})
+    remap = {old: new for new, old in enumerate(ids)}
+    table = np.vectorize(lambda x: remap.get(int(x), 0))(w.block_table).astype(np.int32)
+    kc = w.code_blocks(wl.KIND_K, ids, cd)
+    vc = w.code_blocks(wl.KIND_V, ids, cd)
+    nk, nv = oracle.append_kv(kc, vc, w.key, w.value, w.cum, w.past, table,
+                              kv_num_heads=w.kv_num_heads, head_size=w.head_size,
+                              **quant_kw(cd, PC, PC, ks, vs), **rot_kw(w))
+    idx = torch.tensor(ids, device="cuda", dtype=torch.long)
+    assert dev["key_cache"].index_select(0, idx).cpu().numpy().tobytes() == nk.tobytes()
+    assert dev["value_cache"].index_select(0, idx).cpu().numpy().tobytes() == nv.tobytes()
+    rng = np.random.default_rng(17)
+    rest = sorted(set(range(w.num_blocks)) - set(ids))
+    pick = sorted(int(x) for x in rng.choice(rest, size=min(64, len(rest)), replace=False))
+    sel = torch.tensor(pick, device="cuda", dtype=torch.long)
+    assert dev["key_cache"].index_select(0, sel).cpu().numpy().tobytes() == \
+        w.code_blocks(wl.KIND_K, pick, cd).tobytes()
+    assert dev["value_cache"].index_select(0, sel).cpu().numpy().tobytes() == \
+        w.code_blocks(wl.KIND_V, pick, cd).tobytes()
+    print(f"[quant] codes bit-exact on {len(ids)} written blocks", flush=True)
+    del dev
+
+    kv = w.past
+    chosen = {int(np.argmax(kv)), int(np.argmin(kv))}
+    chosen |= {int(x) for x in rng.choice(w.batch_size, size=2, replace=False)}
+    worst = 0.0
+    for b in sorted(chosen):
+        sub = wl.subset(w, [b])
+        snk, snv = oracle_append_quant(sub, cd, PC, PC, ks, vs)
+        ref = oracle_forward_quant(sub, snk, snv, cd, PC, PC, ks, vs)
+        e = max_err(out[sub.extra["parent_rows"]], ref)
+        print(f"[quant] request {b} (past {int(w.past[b])}): max_abs_err={e:.3e}", flush=True)
+        worst = max(worst, e)
+    assert worst <= TOL, worst
