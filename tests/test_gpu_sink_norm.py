@@ -153,3 +153,74 @@ def test_sink_and_norm_with_a_quantized_pool():
     run(w, extras(w), 0, quant=(wl.CACHE_INT8, wl.QUANT_PER_CHANNEL, wl.QUANT_PER_TENSOR))
     w = wl.scaled_down("long_context_decode_rope")
     run(w, extras(w), 0, quant=(wl.CACHE_FP8, wl.QUANT_PER_TENSOR, wl.QUANT_PER_CHANNEL))
+
+
+def test_sink_and_qk_norm_full_size_sampled():
+    """llama3_8b_mixed at full size with a head sink and QK-Norm, as bench.py
+    --head-sink --qk-norm times it (decode beside the prefill, automatic
+    routing): the written V rows bit-exact and the normalized K rows within
+    two fp16 units of the oracle's append, untouched blocks unchanged, and
+    sampled decode requests and prefill rows against the oracle, recomputed
+    one request at a time on a compact copy of its blocks."""
+    import torch
+    import paged_kv_cache_append_amd as pa
+    from test_gpu_fullsize import sample_plan, touched_blocks
+    w = wl.make_workload("llama3_8b_mixed")
+    e = extras(w)
+    print(f"\n[sink/norm] full {w.name} B={w.batch_size} T={w.token_count} "
+          f"blocks={w.num_blocks}", flush=True)
+    dev = wl.to_device(w)
+    t = {k: (torch.from_numpy(v).cuda() if isinstance(v, np.ndarray) else v) for k, v in e.items()}
+    a = attn_for(w, **t)
+    pa.append_kv(a, dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
+                 dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"])
+    out = pa.forward(a, dev["query"], dev["key_cache"], dev["value_cache"], dev["block_table"],
+                     dev["cum"], dev["past"], dev["cos"], dev["sin"])
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    norm = dict(k_norm_weight=e["k_norm_weight"], qk_norm_epsilon=1e-6)
+
+    ids = touched_blocks(w)
+    remap = {old: new for new, old in enumerate(ids)}
+    table = np.vectorize(lambda x: remap.get(int(x), 0))(w.block_table).astype(np.int32)
+    nk, nv = oracle.append_kv(w.pool_blocks(wl.KIND_K, ids), w.pool_blocks(wl.KIND_V, ids),
+                              w.key, w.value, w.cum, w.past, table,
+                              kv_num_heads=w.kv_num_heads, head_size=w.head_size,
+                              **rot_kw(w), **norm)
+    idx = torch.tensor(ids, device="cuda", dtype=torch.long)
+    gk = dev["key_cache"].index_select(0, idx).cpu().numpy()
+    assert dev["value_cache"].index_select(0, idx).cpu().numpy().tobytes() == nv.tobytes()
+    diff = np.abs(gk.astype(np.float64) - nk.astype(np.float64))
+    unit = np.spacing(np.maximum(np.abs(nk.astype(np.float64)), 1.0).astype(np.float16))
+    units = diff / unit.astype(np.float64)
+    print(f"[sink/norm] K rows of {len(ids)} written blocks: max {units.max():.2f} units, "
+          f"{np.count_nonzero(diff) / diff.size:.2e} of elements differ", flush=True)
+    assert units.max() <= 2 and np.count_nonzero(diff) / diff.size < 1e-2
+    rng = np.random.default_rng(23)
+    rest = sorted(set(range(w.num_blocks)) - set(ids))
+    pick = sorted(int(x) for x in rng.choice(rest, size=min(64, len(rest)), replace=False))
+    sel = torch.tensor(pick, device="cuda", dtype=torch.long)
+    assert dev["key_cache"].index_select(0, sel).cpu().numpy().tobytes() == \
+        w.pool_blocks(wl.KIND_K, pick).tobytes()
+    del dev
+
+    fw = dict(head_sink=e["head_sink"], q_norm_weight=e["q_norm_weight"], qk_norm_epsilon=1e-6)
+    worst = 0.0
+    for b, rows in sample_plan(w, rng):
+        sub = wl.subset(w, [b])
+        snk, snv = oracle.append_kv(sub.pool_blocks(wl.KIND_K, range(sub.num_blocks)),
+                                    sub.pool_blocks(wl.KIND_V, range(sub.num_blocks)),
+                                    sub.key, sub.value, sub.cum, sub.past, sub.block_table,
+                                    kv_num_heads=w.kv_num_heads, head_size=w.head_size,
+                                    **rot_kw(sub), **norm)
+        ref = oracle.forward(sub.query, snk, snv, sub.cum, sub.past, sub.block_table,
+                             num_heads=w.num_heads, kv_num_heads=w.kv_num_heads,
+                             head_size=w.head_size, scale=w.scale, softcap=w.softcap,
+                             local_window_size=w.local_window_size, rows=rows,
+                             **rot_kw(sub), **fw)
+        prow = sub.extra["parent_rows"] if rows is None else sub.extra["parent_rows"][rows]
+        err = max_err(out[prow], ref)
+        print(f"[sink/norm] request {b} (past {int(w.past[b])}, q_len {int(w.q_lens[b])}) "
+              f"rows {len(prow)}: max_abs_err={err:.3e}", flush=True)
+        worst = max(worst, err)
+    assert worst <= TOL, worst
