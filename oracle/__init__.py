@@ -7,7 +7,7 @@ from .pa_oracle import (CACHE_FP8, CACHE_FP16, CACHE_INT8, LAYOUT_LATENT, LAYOUT
                         QK_NORM_EPSILON, QUANT_NONE,
                         QUANT_PER_CHANNEL, QUANT_PER_TENSOR, admitted, append_kv, dequantize, derived_slot,
                         effective_scale, explicit_slot, forward, fp8_e4m3fn_code, fp8_e4m3fn_codes,
-                        fp8_e4m3fn_value, gather_codes, gather_sequence, locate_token,
+                        fp8_e4m3fn_value, gather_codes, gather_sequence, locate_token, mapped_keys,
                         quantize_row, rms_norm_fp16, rope_key_fp16, rope_query_fp64,
                         token_position)
 
@@ -16,5 +16,5 @@ __all__ = ["CACHE_FP8", "CACHE_FP16", "CACHE_INT8", "LAYOUT_LATENT", "LAYOUT_SEP
            "QUANT_PER_TENSOR", "admitted", "append_kv", "dequantize", "derived_slot",
            "effective_scale", "explicit_slot", "forward", "fp8_e4m3fn_code", "fp8_e4m3fn_codes",
            "fp8_e4m3fn_value",
-           "gather_codes", "gather_sequence", "locate_token", "quantize_row", "rms_norm_fp16", "rope_key_fp16",
+           "gather_codes", "gather_sequence", "locate_token", "mapped_keys", "quantize_row", "rms_norm_fp16", "rope_key_fp16",
            "rope_query_fp64", "token_position"]

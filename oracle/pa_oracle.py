@@ -42,7 +42,8 @@ Readings where the pages are silent (each also listed in the design notes):
   exact result, then one fp16 rounding).  The direction of rotation is
   parity unpinned: the pages print no formula, the tests only pin
   self-consistency properties.
-* A query row with no admitted key (impossible with causal + W >= 1) is 0.
+* A query row with no admitted key is 0 (causal masking with W >= 1 always
+  admits the query's own position; only unmapped blocks can empty a row).
 * Output rows of tokens owned by no sequence are 0.
 * Quantized caches (PagedAttention -- CUDA Design Document, §8.3): the
   dequantized value of a stored code is ``q * scale`` (zero point 0), with one
@@ -75,6 +76,13 @@ Readings where the pages are silent (each also listed in the design notes):
   RoPE covers channels ``[rotary_offset, rotary_offset + rotary_dim)`` of a
   head (§12.5); the pairs and angle index are those of R6 counted from the
   offset.
+* Unmapped blocks (PagedAttention -- CUDA Design Document, §9.2 item 3,
+  §9.3.1): a ``block_table`` entry of ``-1`` means the block is not mapped;
+  every position in it is masked out of the softmax, and the derived append
+  writes nothing there (as for a ``-1`` slot).  The pages name only ``-1``;
+  an entry that names no block of the pool, and a position past the row's
+  capacity, are read the same way here.  A row left with no admitted key is 0
+  (the convention of the empty split).
 * Explicit write slots (PagedAttention -- CUDA Design Document, §5.2): slot
   ``s`` is block ``s // block_size``, offset ``s % block_size``; ``-1`` writes
   nothing.  The stored K is still rotated at the token's position
@@ -114,11 +122,30 @@ def token_position(past: np.ndarray, b: int, j: int) -> int:
     return int(past[b]) + j
 
 
-def derived_slot(block_table: np.ndarray, b: int, pos: int, block_size: int):
+def derived_slot(block_table: np.ndarray, b: int, pos: int, block_size: int,
+                 num_blocks: Optional[int] = None):
     """``(physical block, offset)`` holding position ``pos`` of sequence ``b``:
     ``block_table[b, pos // block_size]`` and ``pos % block_size``
-    (PagedAttention -- CUDA Design Document, §5.1)."""
-    return int(block_table[b, pos // block_size]), pos % block_size
+    (PagedAttention -- CUDA Design Document, §5.1), or ``None`` when the
+    position is unmapped: its table entry is ``-1`` (§9.2 item 3 and §9.3.1:
+    block not mapped, every position in it masked out), names no block of a
+    pool of ``num_blocks`` blocks, or lies past the row's capacity."""
+    i = pos // block_size
+    if i >= block_table.shape[1]:
+        return None
+    blk = int(block_table[b, i])
+    if blk < 0 or (num_blocks is not None and blk >= num_blocks):
+        return None
+    return blk, pos % block_size
+
+
+def mapped_keys(block_table: np.ndarray, b: int, kv_len: int, block_size: int,
+                num_blocks: int) -> np.ndarray:
+    """bool ``[kv_len]``: whether position ``tau`` of sequence ``b`` has a
+    block (see :func:`derived_slot`).  Unmapped positions are excluded from
+    the softmax like masked keys (§9.2 item 3)."""
+    return np.array([derived_slot(block_table, b, tau, block_size, num_blocks) is not None
+                     for tau in range(kv_len)], dtype=bool)
 
 
 # ---------------------------------------------------------------------------
@@ -326,12 +353,13 @@ def append_kv(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
         b, j = owner
         pos = token_position(past, b, j)
         if slot_mapping is None:
-            blk, off = derived_slot(block_table, b, pos, block_size)
+            # an unmapped block (-1) takes no write, as a -1 slot does (§9.2 item 3)
+            where = derived_slot(block_table, b, pos, block_size, kc.shape[0])
         else:
             where = explicit_slot(slot_mapping, t, block_size, kc.shape[0])
-            if where is None:
-                continue
-            blk, off = where
+        if where is None:
+            continue
+        blk, off = where
         for h in range(Hkv):
             krow = key[t, h * D:(h + 1) * D]
             if k_norm_weight is not None:
@@ -356,23 +384,27 @@ def append_kv(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
 
 def gather_sequence(cache: np.ndarray, block_table: np.ndarray, b: int, kv_len: int) -> np.ndarray:
     """fp64 ``[kv_len, Hkv, D]``: position ``tau`` of sequence ``b`` read from
-    block ``block_table[b, tau // bs]``, offset ``tau % bs``."""
+    block ``block_table[b, tau // bs]``, offset ``tau % bs``.  Unmapped
+    positions (:func:`derived_slot` gives None) are not read and hold 0; the
+    caller excludes them with :func:`mapped_keys`."""
     bs = cache.shape[1]
-    out = np.empty((kv_len, cache.shape[2], cache.shape[3]), np.float64)
+    out = np.zeros((kv_len, cache.shape[2], cache.shape[3]), np.float64)
     for tau in range(kv_len):
-        blk, off = derived_slot(block_table, b, tau, bs)
-        out[tau] = cache[blk, off]
+        where = derived_slot(block_table, b, tau, bs, cache.shape[0])
+        if where is not None:
+            out[tau] = cache[where]
     return out
 
 
 def gather_codes(cache: np.ndarray, block_table: np.ndarray, b: int, kv_len: int) -> np.ndarray:
     """The stored codes ``[kv_len, Hkv, D]`` of sequence ``b`` (same walk as
-    :func:`gather_sequence`, no conversion)."""
+    :func:`gather_sequence`, no conversion; unmapped positions hold code 0)."""
     bs = cache.shape[1]
-    out = np.empty((kv_len, cache.shape[2], cache.shape[3]), cache.dtype)
+    out = np.zeros((kv_len, cache.shape[2], cache.shape[3]), cache.dtype)
     for tau in range(kv_len):
-        blk, off = derived_slot(block_table, b, tau, bs)
-        out[tau] = cache[blk, off]
+        where = derived_slot(block_table, b, tau, bs, cache.shape[0])
+        if where is not None:
+            out[tau] = cache[where]
     return out
 
 
@@ -475,7 +507,9 @@ def forward(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
                     qrow[h] = rope_query_fp64(qrow[h], positions[r], cos_cache, sin_cache,
                                               rotary_interleaved, rotary_offset)
             Q[r] = qrow
-        mask = np.stack([admitted(tau, p, local_window_size) for p in positions])
+        # keys in unmapped blocks are masked out like keys outside the window
+        mapped = mapped_keys(block_table, b, kv_len, key_cache.shape[1], key_cache.shape[0])
+        mask = np.stack([admitted(tau, p, local_window_size) & mapped for p in positions])
         for h in range(H):
             kvh = h // g
             S = sigma * (Q[:, h, :] @ K[:, kvh, :].T)          # full score matrix

@@ -104,6 +104,11 @@ class Workload:
                        np.float16)
         for n, p in enumerate(ids):
             out[n] = _draw_block(self.seed, kind, p, out.shape[1:], self.kv_sigma)
+        dead = self.extra.get("dead_blocks")
+        if dead:
+            for n, p in enumerate(ids):
+                if p in dead:
+                    out[n] = np.float16(np.nan)
         if self.poison:
             filled = self._filled_tokens()
             for n, p in enumerate(ids):
@@ -119,6 +124,12 @@ class Workload:
         out = np.empty((len(ids),) + shape, code_dtype(cache_dtype))
         for n, p in enumerate(ids):
             out[n] = draw_code_block(self.seed, kind, p, shape, cache_dtype)
+        dead = self.extra.get("dead_blocks")
+        if dead:
+            # int8 has no NaN: the largest code, which a wrong read would show
+            for n, p in enumerate(ids):
+                if p in dead:
+                    out[n] = 0x7F
         if self.poison and cache_dtype == CACHE_FP8:
             # unfilled slots hold the e4m3fn NaN code (int8 has no NaN)
             filled = self._filled_tokens()
@@ -295,19 +306,21 @@ def build_case(name: str, seed: int, *, q_lens: Sequence[int], past: Sequence[in
         rd = rotary_dim or D
         rows = maxblk * block_size
         cos, sin = rope_tables(rows, rd, rotary_base)
-    return Workload(name=name, seed=seed, num_heads=H, kv_num_heads=Hkv, head_size=D,
-                    block_size=block_size, scale=float(scale), softcap=float(softcap),
-                    local_window_size=int(local_window_size), do_rotary=int(do_rotary),
-                    rotary_interleaved=int(rotary_interleaved), cum=cum,
-                    past=past.astype(np.int32), block_table=table, num_blocks=int(num_blocks),
-                    query=q.astype(np.float16), key=k.astype(np.float16),
-                    value=v.astype(np.float16), cos_cache=cos, sin_cache=sin,
-                    kv_sigma=float(kv_sigma), poison=poison, description=description)
+    w = Workload(name=name, seed=seed, num_heads=H, kv_num_heads=Hkv, head_size=D,
+                 block_size=block_size, scale=float(scale), softcap=float(softcap),
+                 local_window_size=int(local_window_size), do_rotary=int(do_rotary),
+                 rotary_interleaved=int(rotary_interleaved), cum=cum,
+                 past=past.astype(np.int32), block_table=table, num_blocks=int(num_blocks),
+                 query=q.astype(np.float16), key=k.astype(np.float16),
+                 value=v.astype(np.float16), cos_cache=cos, sin_cache=sin,
+                 kv_sigma=float(kv_sigma), poison=poison, description=description)
+    w.extra["perm"] = perm
+    return w
 
 
 # ---------------------------------------------------------------------------
-# The five benchmark workloads (seed 1000 + index, draws in a fixed order:
-# past lengths, block permutation, Q, K, V; pool per block).
+# The five benchmark workloads C1..C5 (seed 1000 + n for config Cn, draws in a
+# fixed order: past lengths, block permutation, Q, K, V; pool per block).
 # ---------------------------------------------------------------------------
 
 CONFIG_NAMES = (
@@ -321,17 +334,17 @@ CONFIG_NAMES = (
 
 def make_workload(name: str, poison: bool = False) -> Workload:
     idx = CONFIG_NAMES.index(name)
-    seed = 1000 + idx
+    seed = 1001 + idx
     rng = np.random.default_rng(seed)
     if name == "tiny_decode":
         # 2 sequences, one new token each on 37 / 50 cached tokens; pool of 16
-        # blocks whose table rows are a seeded permutation (all 8 entries valid).
+        # blocks; the table rows are the config's own block permutation
+        # reshaped to [2, 8] (all 8 entries valid, 3 and 4 of them in use).
         w = build_case(name, seed, q_lens=[1, 1], past=[37, 50], num_heads=4,
                        kv_num_heads=2, head_size=64, block_size=16, scale=0.125,
                        num_blocks=16, rng=rng, shuffle=True, poison=poison,
                        description="2 seqs x 1 token, past 37/50, H=4 Hkv=2 D=64 bs=16")
-        perm = np.random.default_rng([seed, 7]).permutation(16).astype(np.int32)
-        w.block_table = perm.reshape(2, 8)
+        w.block_table = w.extra["perm"].astype(np.int32).reshape(2, 8)
         w.extra.pop("_filled", None)
         return w
     if name == "llama3_8b_mixed":
@@ -550,3 +563,136 @@ def subset(w: Workload, seqs: Sequence[int]) -> Workload:
     sub.extra["parent_rows"] = rows
     sub.extra["parent_block_ids"] = ids
     return sub
+
+
+# ---------------------------------------------------------------------------
+# Unmapped blocks, shared prefixes and a rolling sliding-window cache: inputs
+# a serving runtime hands the op (PagedAttention -- CUDA Design Document,
+# §9.2 item 3: -1 in block_table is "not mapped, masked out"; §9.3: the
+# bounded-capacity window cache; §17.2: the paging tests).  Table and slot
+# bookkeeping only; no attention arithmetic.
+# ---------------------------------------------------------------------------
+
+def _copy_with_table(w: Workload, table: np.ndarray, dead) -> Workload:
+    import dataclasses
+    extra = {k: v for k, v in w.extra.items() if k != "_filled"}
+    extra["dead_blocks"] = frozenset(int(x) for x in dead) | w.extra.get("dead_blocks",
+                                                                         frozenset())
+    return dataclasses.replace(w, block_table=np.ascontiguousarray(table, np.int32), extra=extra)
+
+
+def cached_block_entries(w: Workload):
+    """(request, block index) pairs of blocks that hold only cached positions
+    (no new token of this step is written there)."""
+    out = []
+    bs = w.block_size
+    for b in range(w.batch_size):
+        past = int(w.past[b])
+        for i in range(past // bs):
+            if int(w.block_table[b, i]) >= 0:
+                out.append((b, i))
+    return out
+
+
+def with_unmapped_blocks(w: Workload, entries) -> Workload:
+    """A copy of ``w`` whose table entries ``(request, block index)`` in
+    ``entries`` are -1.  The physical blocks they named become dead: their
+    contents are NaN (fp16) or the code 0x7F, so a read through a stale entry
+    would show in the output."""
+    table = w.block_table.copy()
+    dead = set()
+    for b, i in entries:
+        blk = int(table[b, i])
+        if blk >= 0:
+            dead.add(blk)
+        table[b, i] = -1
+    still = {int(x) for x in table.reshape(-1) if x >= 0}
+    return _copy_with_table(w, table, dead - still)
+
+
+def random_unmapped_entries(w: Workload, seed: int, fraction: float):
+    """About ``fraction`` of the fully cached blocks of each request, drawn."""
+    rng = np.random.default_rng(seed)
+    ent = cached_block_entries(w)
+    keep = rng.random(len(ent)) < fraction
+    return [e for e, k in zip(ent, keep) if k]
+
+
+def with_shared_prefix(w: Workload, pairs) -> Workload:
+    """A copy of ``w`` in which, for each ``(b1, b2, n)``, request ``b2``
+    reads its first ``n`` blocks from request ``b1``'s blocks (prefix
+    sharing: the blocks are read by both, written by neither; ``n`` blocks
+    must hold only cached positions of both requests).  ``b2``'s former
+    blocks become dead (poisoned)."""
+    table = w.block_table.copy()
+    bs = w.block_size
+    dead = set()
+    for b1, b2, n in pairs:
+        if n * bs > min(int(w.past[b1]), int(w.past[b2])):
+            raise ValueError("shared blocks must hold only cached positions of both requests")
+        for i in range(n):
+            dead.add(int(table[b2, i]))
+            table[b2, i] = table[b1, i]
+    still = {int(x) for x in table.reshape(-1) if x >= 0}
+    return _copy_with_table(w, table, dead - still)
+
+
+class RingBlockAllocator:
+    """The ring-buffer policy of the bounded sliding-window cache (CUDA
+    Design Document, §9.3.2 item 1): request ``b`` owns a ring of
+    ``N = ceil(W / block_size) + 1`` physical blocks; position ``p`` of block
+    index ``i = p // block_size`` is written to slot
+    ``ring[i % N] * block_size + p % block_size`` through ``slot_mapping``,
+    ``block_table[b][i]`` names ``ring[i % N]``, and entries below the window
+    start of the step's earliest query are -1 (§9.3.1: the row stays indexed by
+    absolute position).  Raises if a step would overwrite a block that a query
+    of the same step can still see."""
+
+    def __init__(self, batch: int, window: int, block_size: int, max_blocks_per_seq: int,
+                 seed: int = 0):
+        self.W, self.bs = int(window), int(block_size)
+        self.N = -(-self.W // self.bs) + 1
+        perm = np.random.default_rng(seed).permutation(batch * self.N)
+        self.ring = perm.reshape(batch, self.N).astype(np.int32)
+        self.num_blocks = batch * self.N
+        self.table = np.full((batch, max_blocks_per_seq), -1, np.int32)
+
+    def step(self, past, q_lens):
+        """``(block_table, slot_mapping)`` for one step with these lengths."""
+        slots = []
+        for b, (p0, ql) in enumerate(zip(past, q_lens)):
+            p0, ql = int(p0), int(ql)
+            lo = max(0, p0 - self.W + 1) // self.bs          # first reachable block
+            self.table[b, :lo] = -1
+            for p in range(p0, p0 + ql):
+                i = p // self.bs
+                r = self.ring[b, i % self.N]
+                live = np.nonzero(self.table[b] == r)[0]
+                if any(int(j) != i for j in live):
+                    raise ValueError(f"request {b}: block index {i} would overwrite live "
+                                     f"block index {int(live[0])}")
+                self.table[b, i] = r
+                slots.append(int(r) * self.bs + p % self.bs)
+        return self.table.copy(), np.asarray(slots, np.int32)
+
+
+def full_cache_table(batch: int, max_blocks_per_seq: int, seed: int = 0):
+    """A table that gives every (request, block index) its own physical
+    block, shuffled over a pool of ``batch * max_blocks_per_seq`` blocks."""
+    perm = np.random.default_rng(seed).permutation(batch * max_blocks_per_seq)
+    return perm.reshape(batch, max_blocks_per_seq).astype(np.int32)
+
+
+def step_tokens(seed: int, step: int, q_lens, num_heads: int, kv_num_heads: int,
+                head_size: int):
+    """Packed ``(cum, query, key, value)`` of one step's new tokens (fp16
+    N(0, 1)), drawn from ``default_rng([seed, step])``."""
+    rng = np.random.default_rng([seed, step])
+    q_lens = np.asarray(q_lens, np.int64)
+    cum = np.zeros(len(q_lens) + 1, np.int32)
+    cum[1:] = np.cumsum(q_lens)
+    T = int(cum[-1])
+    q = rng.standard_normal((T, num_heads * head_size), dtype=np.float32).astype(np.float16)
+    k = rng.standard_normal((T, kv_num_heads * head_size), dtype=np.float32).astype(np.float16)
+    v = rng.standard_normal((T, kv_num_heads * head_size), dtype=np.float32).astype(np.float16)
+    return cum, q, k, v
