@@ -1,30 +1,37 @@
 #!/usr/bin/env python3
-"""Benchmark of one paged-attention step (KV append + forward) on one GPU.
+"""Benchmark of the paged-attention step (KV append + forward) on one GPU.
 
 A step is the whole hot path over one batch: token -> request resolution,
 slot derivation, rotary (when the workload has it), the KV append, the
 split-KV decode + merge and the MFMA prefill.  Inputs are synthetic and
 already resident in device memory when the timed region starts.
 
-    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
-                    [--copy-calibration-mib N]
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--prefill-config NAME|none]
+                    [--no-cpu-baseline] [--no-flush] [--copy-calibration-mib N]
                     [--cache int8|fp8 [--k-quant tensor|channel] [--v-quant tensor|channel]]
                     [--head-sink | --smooth-softmax] [--qk-norm]
     python bench.py --summarize-pmc counter_collection.csv ...
+    python bench.py --summarize-mfma KERNEL counter_collection.csv
 
-Prints ONE JSON line.  ``value`` is the decode KV throughput of the whole
-step (algorithmic decode bytes / step time) over K timed steps with nothing
-else on the stream.  The same K steps then run again with every launch's
-dispatch timestamped on its stream (start/stop events of the launch itself);
-``roofline`` describes the dominant kernel from those durations (per-launch
-algorithmic bytes or FLOPs over its average launch time).
-``cpu_baseline`` times the fp64 oracle on a bounded sample of the workload.
-``--config mla_decode_tp8`` / ``mla_decode_dp`` runs the latent-attention (MLA)
-step instead: append of 576-channel latent rows + forward on the latent
-kernel (V is the leading 512 channels of K).
-With ``--cache`` the pools hold int8 or float8 e4m3fn codes with fp32 scales
-(decode-only workloads: every request has one new token); the algorithmic
-bytes then count one byte per cached element.
+Prints ONE JSON line.  By default it is quoted on the decode-heavy batch
+(``decode_heavy_256``: 256 requests, past U[1024, 16384], H=32, Hkv=8,
+D=128, block 32; 9.09 GB of K/V per step): ``value`` is the decode KV
+throughput of the whole step (algorithmic decode bytes / median step time).
+The same line carries a ``prefill`` object for the windowed, softcapped
+prefill batch (``gemma2_prefill_window``: 8 x 2048 new tokens on 2048 past,
+H=16, Hkv=8, D=256; 824.8 GFLOP per step) with its own TFLOP/s, roofline and
+oracle baseline.
+
+Timing protocol, per workload: W untimed warm-up steps, then K steps each
+bracketed by its own event pair on the launch stream, with a 1 GiB scratch
+write (not timed) before every step so that neither the L2s nor the 256 MB
+memory-side cache hold the step's inputs ("cold"; the median and p10/p90 are
+reported), then K back-to-back steps the same way without the scratch write
+(reported under ``warm``), then K cold steps with every launch's dispatch
+timestamped on its stream (the per-kernel durations behind ``roofline``).
+``hbm_ceiling`` is a plain streaming read of a 4 GiB buffer, the practical
+ceiling set beside the 8 TB/s figure.  ``cpu_baseline`` times the fp64
+oracle on a bounded sample of the workload on the host cores.
 """
 from __future__ import annotations
 
@@ -43,7 +50,12 @@ sys.path.insert(0, ROOT)
 METRIC = "decode KV GB/s (% HBM peak); prefill attention TFLOP/s (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16 MFMA
-DEFAULT_CONFIG = "llama3_8b_mixed"
+DEFAULT_CONFIG = "decode_heavy_256"
+DEFAULT_PREFILL_CONFIG = "gemma2_prefill_window"
+FLUSH_BYTES = 1 << 30          # scratch written between cold steps (> 256 MB MALL + L2s)
+CEILING_BYTES = 4 << 30        # streaming-read ceiling buffer
+WARMUP_SECONDS = 0.5           # default warm-up: at least this long (and 10 steps)
+STAGES = ("append", "decode", "merge", "prefill", "prefill_merge", "plan", "q_norm")
 
 
 def algorithmic_work(w, kv_elem_bytes=2):
@@ -109,6 +121,36 @@ def kernel_source_hash(kind: str) -> str:
     return h.hexdigest()
 
 
+def host_cpu():
+    """CPU model and the host CPUs this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return model, n
+
+
+def blas_threads():
+    import threadpoolctl
+    return sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
+               if i.get("user_api") == "blas") or 1
+
+
+def _cpu_entry(value, unit, sample):
+    model, n = host_cpu()
+    return {"value": round(value, 4), "unit": unit, "cores": int(blas_threads()), "kind": "oracle",
+            "sample": sample, "cpu_model": model, "host_cpus": n}
+
+
 def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=1024,
                  target_seconds=10.0, quant=None, feat=None):
     """fp64 oracle on a bounded sample of the workload: the decode requests
@@ -117,8 +159,6 @@ def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=1024,
     rows the sample covers.  ``quant`` = (cache dtype, K quant type, V quant
     type, K scales, V scales) runs it on the quantized pool; ``feat`` holds
     the sink / QK-Norm inputs (host arrays) of the GPU run."""
-    import threadpoolctl
-
     import oracle
     from paged_kv_cache_append_amd import workloads as wl
     dec = [b for b in range(w.batch_size) if int(w.q_lens[b]) == 1][:decode_rows_sample]
@@ -148,8 +188,6 @@ def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=1024,
     nk, nv = oracle.append_kv(kc, vc, sub.key, sub.value, sub.cum, sub.past, sub.block_table,
                               kv_num_heads=sub.kv_num_heads, head_size=sub.head_size, **rot,
                               **qkw, **akw)
-    threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
-                  if i.get("user_api") == "blas") or 1
     rows = None
     if prefill:
         ql = int(sub.q_lens[0])
@@ -176,20 +214,22 @@ def cpu_baseline(w, gpu_out, decode_rows_sample=64, prefill_rows_sample=1024,
             pairs += pos + 1 - (max(0, pos - W + 1) if W > 0 else 0)
         flops = 4.0 * sub.head_size * sub.num_heads * pairs
         err = float(np.max(np.abs(gpu_out[prow[rows]].astype(np.float64) - ref)))
-        return {"value": round(flops / dt / 1e9, 4), "unit": "GFLOP/s", "cores": int(threads),
-                "kind": "oracle",
-                "sample": f"last {len(rows)} query rows of request 0 of {w.name} "
+        return _cpu_entry(flops / dt / 1e9, "GFLOP/s",
+                          f"last {len(rows)} query rows of request 0 of {w.name} "
                           f"({flops / 1e9:.2f} GFLOP over admitted pairs), full fp64 score "
-                          f"rows + softmax + PV, {dt:.2f} s per pass, {reps} passes"}, err
+                          f"rows + softmax + PV, {dt:.2f} s per pass, {reps} passes"), err
     nbytes, _, _ = algorithmic_work(sub, 1 if quant else 2)
     err = float(np.max(np.abs(gpu_out[prow].astype(np.float64) - ref)))
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(dec)} decode requests of {w.name} ({nbytes / 1e6:.1f} MB of K/V+Q/O"
+    return _cpu_entry(nbytes / dt / 1e9, "GB/s",
+                      f"{len(dec)} decode requests of {w.name} ({nbytes / 1e6:.1f} MB of K/V+Q/O"
                       f"{', quantized pool dequantized on gather' if quant else ''}), "
                       f"gather + full scores + softmax + PV in fp64, {dt:.2f} s per pass, "
-                      f"{reps} passes"}, err
+                      f"{reps} passes"), err
 
+
+# ---------------------------------------------------------------------------
+# rocprofv3 counter summaries (no GPU use)
+# ---------------------------------------------------------------------------
 
 def _strip_params(name: str) -> str:
     """Kernel name without its trailing parameter list."""
@@ -262,35 +302,74 @@ def summarize_pmc(paths):
         print(f"{k:90s} {c:28s} {len(v):10d} {sum(v) / len(v):16.1f}")
 
 
-STAGES = ("append", "decode", "merge", "prefill", "prefill_merge", "plan", "q_norm")
+def summarize_mfma(kernel, path, simds=1024, clock_ghz=None):
+    """MFMA utilisation of one kernel from a rocprofv3 counter run holding
+    SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs), GRBM_GUI_ACTIVE (GPU
+    cycles while busy) and SQ_INSTS_VALU_MFMA_MOPS_F16 (units of 512 FLOPs):
+    busy / (active * SIMDs), the profiler's MfmaUtil definition, and the
+    FLOPs the matrix cores executed per dispatch."""
+    means = {c: v for (k, c), v in _pmc_means(path).items() if kernel in k}
+    busy = means.get("SQ_VALU_MFMA_BUSY_CYCLES")
+    active = means.get("GRBM_GUI_ACTIVE")
+    mops = means.get("SQ_INSTS_VALU_MFMA_MOPS_F16")
+    out = {"kernel": kernel, "counters": means}
+    if busy is not None and active:
+        out["mfma_util"] = busy / (active * simds)
+    if mops is not None:
+        out["mfma_flops_per_dispatch"] = mops * 512.0
+    print(json.dumps(out, indent=1))
 
 
-WARMUP_SECONDS = 0.5   # default warm-up: at least this long (and 10 steps)
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+
+def stats(ms):
+    a = np.asarray(ms, np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "mean": round(float(a.mean()), 5),
+            "reps": int(a.size)}
 
 
-def measure(step, steps, warmup):
-    """W untimed steps, then K timed steps with nothing else on the stream
-    (the throughput figure), then the same K steps with every kernel's
-    dispatch timestamped on its stream (the per-kernel durations).  With
+class Flusher:
+    """Writes FLUSH_BYTES of scratch on the current stream: afterwards the L2s
+    and the memory-side cache hold none of the step's inputs."""
+
+    def __init__(self, nbytes=FLUSH_BYTES):
+        import torch
+        self.buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n)
+
+
+def _reps(step, reps, flush):
+    """``reps`` steps, each between its own pair of events on the current
+    stream; ``flush`` (or None) runs before each, outside the pair."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        if flush is not None:
+            flush()
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def measure(step, steps, warmup, flush):
+    """Warm-up, then cold steps (scratch write before each), warm steps (back
+    to back) and cold steps with every kernel's dispatch timestamped.  With
     ``warmup`` None the warm-up runs until at least WARMUP_SECONDS have passed
-    (and 10 steps): the clocks of an idle GPU take that long to settle, and a
-    short warm-up understates a long step by several percent.  Returns the
-    warm-up step count too."""
+    (and 10 steps): an idle GPU's clocks take that long to settle."""
     import torch
 
     import paged_kv_cache_append_amd as pa
-
-    def timed(k):
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(k):
-            step()
-        stop.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop)
-
     if warmup is None:
         warmup = 0
         t0 = time.perf_counter()
@@ -303,219 +382,49 @@ def measure(step, steps, warmup):
         for _ in range(warmup):
             step()
     torch.cuda.synchronize()
-    ms_step = timed(steps) / steps
+    cold = _reps(step, steps, flush)
+    warm = _reps(step, steps, None)
     pa.timing_enable(8 * steps + 16)
-    ms_step_instrumented = timed(steps) / steps
+    _reps(step, steps, flush)
     stages = {s: pa.timing_read(s) for s in STAGES}
     pa.timing_disable()
-    return ms_step, ms_step_instrumented, stages, warmup
+    return {"cold": cold, "warm": warm, "stages": stages, "warmup": warmup}
 
 
-def mla_work(w):
-    """Latent attention: bytes (each admitted 576-channel row once -- V is a
-    view of K -- plus the fp16 Q and O rows of every query token) and FLOPs
-    (2 * H * (D + DV) per admitted key of every query token)."""
-    from paged_kv_cache_append_amd import workloads as wl
-    H, D, DV = w.num_heads, w.head_size, wl.MLA_V_HEAD_SIZE
-    W = w.local_window_size
-    nbytes = 0
-    keys = 0
-    for b in range(w.batch_size):
-        for j in range(int(w.q_lens[b])):
-            pos = int(w.past[b]) + j
-            kv = pos + 1 - (max(0, pos - W + 1) if W > 0 else 0)
-            nbytes += kv * D * 2 + H * D * 2 + H * DV * 2
-            keys += kv
-    return nbytes, 2.0 * H * (D + DV) * keys
-
-
-def mla_cpu_baseline(w, gpu_out, sample=16, target_seconds=10.0):
-    """The oracle on the first ``sample`` requests of a latent workload, for
-    about target_seconds: GB/s of the same algorithmic bytes, and the max-abs
-    error of the GPU rows it covers."""
-    import threadpoolctl
-
-    import oracle
-    from paged_kv_cache_append_amd import workloads as wl
-    sub = wl.subset(w, list(range(min(sample, w.batch_size))))
-    rot = dict(cos_cache=sub.cos_cache, sin_cache=sub.sin_cache,
-               rotary_interleaved=bool(sub.rotary_interleaved),
-               rotary_offset=wl.MLA_ROTARY_OFFSET)
-    kc = sub.pool_blocks(wl.KIND_K, range(sub.num_blocks))
-    nk, _ = oracle.append_kv(kc, None, sub.key, None, sub.cum, sub.past, sub.block_table,
-                             kv_num_heads=1, head_size=sub.head_size,
-                             kv_cache_layout=oracle.LAYOUT_LATENT, **rot)
-    threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
-                  if i.get("user_api") == "blas") or 1
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        ref = oracle.forward(sub.query, nk, None, sub.cum, sub.past, sub.block_table,
-                             num_heads=sub.num_heads, kv_num_heads=1, head_size=sub.head_size,
-                             scale=sub.scale, softcap=sub.softcap,
-                             local_window_size=sub.local_window_size,
-                             kv_cache_layout=oracle.LAYOUT_LATENT,
-                             v_head_size=wl.MLA_V_HEAD_SIZE, **rot)
-        reps += 1
-        if time.perf_counter() - t0 >= target_seconds:
-            break
-    dt = (time.perf_counter() - t0) / reps
-    nbytes, _ = mla_work(sub)
-    err = float(np.max(np.abs(gpu_out[sub.extra["parent_rows"]].astype(np.float64) - ref)))
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{sub.batch_size} requests of {w.name} ({nbytes / 1e6:.1f} MB of latent "
-                      f"rows + Q/O), gather + full scores + softmax + PV in fp64, {dt:.2f} s "
-                      f"per pass, {reps} passes"}, err
-
-
-def bench_mla(args):
-    """Latent attention (MLA) step: append of the latent rows + forward on the
-    latent kernel, over an absorbed DeepSeek-shaped decode batch."""
+def hbm_ceiling(reps=10):
+    """Streaming read of a CEILING_BYTES buffer (larger than every cache):
+    median GB/s over ``reps`` back-to-back reads."""
     import torch
 
     import paged_kv_cache_append_amd as pa
-    from paged_kv_cache_append_amd import workloads as wl
-    w = wl.make_mla_workload(args.config)
-    dev = wl.to_device(w)
-    a = pa.Attn(num_heads=w.num_heads, kv_num_heads=1, head_size=w.head_size,
-                block_size=w.block_size, scale=w.scale, do_rotary=1,
-                rotary_interleaved=w.rotary_interleaved, kv_cache_layout=pa.LAYOUT_LATENT,
-                v_head_size=wl.MLA_V_HEAD_SIZE, rotary_offset=wl.MLA_ROTARY_OFFSET)
-    T = w.token_count
-    out = torch.empty((T, w.num_heads * wl.MLA_V_HEAD_SIZE), dtype=torch.float16, device="cuda")
-    nws = pa.forward_workspace_bytes(a, dev["key_cache"], None, dev["block_table"], dev["cum"],
-                                     dev["past"], T)
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
-    plan = pa.describe_plan(a, dev["key_cache"], None, dev["block_table"], dev["cum"],
-                            dev["past"], T)
-
-    def step():
-        pa.append_kv(a, dev["key"], None, dev["key_cache"], None, dev["block_table"], dev["cum"],
-                     dev["past"], dev["cos"], dev["sin"])
-        pa.forward(a, dev["query"], dev["key_cache"], None, dev["block_table"], dev["cum"],
-                   dev["past"], dev["cos"], dev["sin"], workspace=ws, out=out)
-
-    ms_step, ms_step_instrumented, stages, args.warmup = measure(step, args.steps, args.warmup)
-    per = {s: (ms / n * 1e3 if n else 0.0) for s, (ms, n) in stages.items()}
-    nbytes, flops = mla_work(w)
-    t = per["decode"] * 1e-6
-    gbs, tfs = nbytes / t / 1e9, flops / t / 1e12
-    hbm_bound = nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_F16_PEAK_TFS * 1e12)
-    roof = {"bound": "hbm" if hbm_bound else "mfma", "kernel": "mla",
-            "achieved": round(gbs if hbm_bound else tfs, 4),
-            "peak": HBM_PEAK_GBS if hbm_bound else MFMA_F16_PEAK_TFS,
-            "unit": "GB/s" if hbm_bound else "TFLOP/s",
-            "frac": round(gbs / HBM_PEAK_GBS if hbm_bound else tfs / MFMA_F16_PEAK_TFS, 4),
-            "traffic": traffic_from_profiles(f"mla:{w.name}", kernel_source_hash("mla")),
-            "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
-            "other_unit_frac": round(tfs / MFMA_F16_PEAK_TFS if hbm_bound
-                                     else gbs / HBM_PEAK_GBS, 4)}
-    kernels = {f"{s}_us": round(v, 3) for s, v in per.items()}
-    kernels["mla_kernel_gbs"] = round(gbs, 1)
-    kernels["mla_kernel_tflops"] = round(tfs, 2)
-    cpu, err = (None, None)
-    if not args.no_cpu_baseline:
-        cpu, err = mla_cpu_baseline(w, out.cpu().numpy())
-    line = {
-        "metric": METRIC, "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch_size, "tokens": T,
-                   "num_heads": w.num_heads, "kv_num_heads": 1, "head_size": w.head_size,
-                   "v_head_size": wl.MLA_V_HEAD_SIZE, "block_size": w.block_size,
-                   "kv_cache_layout": "latent", "rotary_offset": wl.MLA_ROTARY_OFFSET,
-                   "latent_bytes": nbytes, "flops": flops, "plan": plan},
-        "roofline": roof,
-        "kernels": kernels,
-        "ms_per_step_instrumented": round(ms_step_instrumented, 5),
-        "cpu_baseline": cpu,
-        "parity_max_abs_err_sampled": err,
-    }
-    print(json.dumps(line), flush=True)
+    buf = torch.ones(CEILING_BYTES // 2, dtype=torch.float16, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    pa.stream_read(buf, sink)
+    ms = _reps(lambda: pa.stream_read(buf, sink), reps, None)
+    del buf
+    gbs = CEILING_BYTES / (float(np.median(ms)) * 1e-3) / 1e9
+    return {"gbs": round(gbs, 1), "bytes": CEILING_BYTES, "frac_of_spec": round(gbs / HBM_PEAK_GBS, 4),
+            "protocol": f"pa_bench_stream_read of a 4 GiB buffer, median of {reps} back-to-back "
+                        "reads, each between its own event pair"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps before the timed ones (default: at least "
-                         f"{WARMUP_SECONDS} s of steps, and 10; the count is reported)")
-    ap.add_argument("--config", default=DEFAULT_CONFIG)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cache", choices=("fp16", "int8", "fp8"), default="fp16",
-                    help="element type of the paged pools (int8 / fp8: codes + fp32 scales)")
-    ap.add_argument("--k-quant", choices=("tensor", "channel"), default="channel")
-    ap.add_argument("--v-quant", choices=("tensor", "channel"), default="channel")
-    ap.add_argument("--head-sink", action="store_true",
-                    help="a sink logit per head (drawn from U[-2, 3])")
-    ap.add_argument("--smooth-softmax", action="store_true", help="a zero sink for every head")
-    ap.add_argument("--qk-norm", action="store_true",
-                    help="QK-Norm of Q and new K with drawn weights (U[0.5, 1.5]), eps 1e-6")
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="first run a plain fp16 copy kernel over this many MiB (read N, "
-                         "write N), three times, to scale HBM byte counters")
-    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
-                    help="print per-kernel mean counter values of rocprofv3 counter "
-                         "CSV files and exit (no GPU use)")
-    ap.add_argument("--record-traffic", nargs=5,
-                    metavar=("TAG", "KERNEL", "FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
-                    help="store HBM bytes per launch of KERNEL (substring of the kernel "
-                         "name) under TAG in profiles/traffic.json, from a FETCH_SIZE and a "
-                         "WRITE_SIZE counter run that both include the copy calibration of "
-                         "COPY_MIB MiB, and exit (no GPU use)")
-    args = ap.parse_args()
-    if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc)
-        return
-    if args.record_traffic:
-        record_traffic(*args.record_traffic)
-        return
-    if args.gpus != 1:
-        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
-        sys.exit(2)
+# ---------------------------------------------------------------------------
+# one workload
+# ---------------------------------------------------------------------------
 
+def run_workload(name, args, flush, ceiling):
+    """Append + forward steps of one workload under the timing protocol;
+    returns the fields of its JSON object."""
     import torch
 
     import paged_kv_cache_append_amd as pa
     from paged_kv_cache_append_amd import workloads as wl
 
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib * (1 << 20) // 2
-        src = torch.ones(n, dtype=torch.float16, device="cuda")
-        dst = torch.empty_like(src)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        for i in range(3):
-            ev[i].record()
-            torch.neg(src, out=dst)
-        ev[3].record()
-        torch.cuda.synchronize()
-        ms = ev[2].elapsed_time(ev[3])   # the last launch, caches warm
-        print(f"copy calibration: {args.copy_calibration_mib} MiB read + "
-              f"{args.copy_calibration_mib} MiB written per launch, "
-              f"{2 * n * 2 / (ms * 1e-3) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
-        del src, dst
-
-    if args.config in wl.MLA_CONFIG_NAMES:
-        if args.cache != "fp16" or args.head_sink or args.smooth_softmax or args.qk_norm:
-            print("bench.py: the latent workloads run with an fp16 cache and no sink or "
-                  "QK-Norm (section 12.10)", file=sys.stderr)
-            sys.exit(2)
-        bench_mla(args)
-        return
-
-    w = wl.make_workload(args.config)
+    w = wl.make_workload(name)
     cd = {"fp16": wl.CACHE_FP16, "int8": wl.CACHE_INT8, "fp8": wl.CACHE_FP8}[args.cache]
     quant = None
     sc = {}
     if cd != wl.CACHE_FP16:
-        if np.any(w.q_lens != 1):
-            print(f"bench.py: --cache {args.cache} measures decode-only workloads (one new "
-                  f"token per request); {w.name} has multi-token requests", file=sys.stderr)
-            sys.exit(2)
         qt = {"tensor": wl.QUANT_PER_TENSOR, "channel": wl.QUANT_PER_CHANNEL}
         kq, vq = qt[args.k_quant], qt[args.v_quant]
         ks = wl.draw_scales(w, wl.KIND_K, cd, kq, 7)
@@ -554,15 +463,17 @@ def main():
         pa.forward(a, dev["query"], dev["key_cache"], dev["value_cache"], dev["block_table"],
                    dev["cum"], dev["past"], dev["cos"], dev["sin"], workspace=ws, out=out, **sc)
 
-    ms_step, ms_step_instrumented, stages, args.warmup = measure(step, args.steps, args.warmup)
+    m = measure(step, args.steps, args.warmup, flush)
+    cold, warm = stats(m["cold"]), stats(m["warm"])
 
-    # the append alone, with derived slots (from the steps above) and with an
-    # explicit slot mapping (distinct slots scattered over the pool, as a
-    # scheduler that owns placement hands them out): same bytes moved.  Runs
-    # after the timed steps; the output checked below is the last step's.
+    # the append alone with an explicit slot mapping (distinct slots scattered
+    # over the pool, as a scheduler that owns placement hands them out): the
+    # same bytes moved as the derived append of the steps above.  Runs after
+    # the timed steps; the output checked below is the last step's.
     sm = torch.from_numpy(wl.random_slot_mapping(w, 4242)).to("cuda")
     pa.timing_enable(args.steps + 16)
     for _ in range(args.steps):
+        flush()
         pa.append_kv(a, dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
                      dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"],
                      slot_mapping=sm, **sc)
@@ -572,13 +483,15 @@ def main():
 
     kv_elem = 1 if quant else 2
     dec_bytes, pf_flops, n_dec = algorithmic_work(w, kv_elem)
-    per = {s: (ms / n * 1e3 if n else 0.0) for s, (ms, n) in stages.items()}   # us per launch
+    per = {s: (ms / n * 1e3 if n else 0.0) for s, (ms, n) in m["stages"].items()}  # us / launch
+    ms_step = cold["median"]
     if dec_bytes:
         value, unit = dec_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
+        warm_value = dec_bytes / (warm["median"] * 1e-3) / 1e9
     else:
         value, unit = pf_flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
+        warm_value = pf_flops / (warm["median"] * 1e-3) / 1e12
     kernels = {f"{s}_us": round(v, 3) for s, v in per.items()}
-    # K and V: fp16 rows read, cache elements written
     app_bytes = 2 * T * w.kv_num_heads * w.head_size * (2 + kv_elem)
     append = {"algorithmic_bytes_per_launch": app_bytes,
               "derived_slots_us": round(per["append"], 3),
@@ -592,6 +505,9 @@ def main():
                                       (per["q_norm"] * 1e-6) / 1e9, 1)
     if per["decode"]:
         kernels["decode_kernel_gbs"] = round(dec_bytes / (per["decode"] * 1e-6) / 1e9, 1)
+        dm = per["decode"] + per["merge"] + per["plan"]
+        kernels["decode_plan_merge_gbs"] = round(dec_bytes / (dm * 1e-6) / 1e9, 1)
+        kernels["decode_plan_merge_frac"] = round(dec_bytes / (dm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     if per["prefill"] and pf_flops:
         kernels["prefill_kernel_tflops"] = round(pf_flops / (per["prefill"] * 1e-6) / 1e12, 2)
     step_frac = (dec_bytes / (HBM_PEAK_GBS * 1e9) + pf_flops / (MFMA_F16_PEAK_TFS * 1e12)) / \
@@ -605,14 +521,16 @@ def main():
                 "traffic": traffic_from_profiles(
                     f"decode:{w.name}" + (f":{args.cache}" if quant else ""),
                     kernel_source_hash("decode")),
-                "algorithmic_bytes_per_launch": dec_bytes}
+                "algorithmic_bytes_per_launch": dec_bytes, "kernel_us": round(per["decode"], 3)}
+        if achieved and ceiling:
+            roof["frac_of_ceiling"] = round(achieved / ceiling["gbs"], 4)
     else:
         achieved = pf_flops / (per["prefill"] * 1e-6) / 1e12 if per["prefill"] else None
         roof = {"bound": "mfma", "kernel": "prefill", "achieved": achieved,
                 "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": (achieved / MFMA_F16_PEAK_TFS) if achieved else None,
                 "traffic": traffic_from_profiles(f"prefill:{w.name}", kernel_source_hash("prefill")),
-                "algorithmic_flops_per_launch": pf_flops}
+                "algorithmic_flops_per_launch": pf_flops, "kernel_us": round(per["prefill"], 3)}
     for k in ("achieved", "frac"):
         if roof[k] is not None:
             roof[k] = round(roof[k], 4)
@@ -622,12 +540,10 @@ def main():
         cpu, err = cpu_baseline(w, out.cpu().numpy(), quant=quant,
                                 feat={k: (v.cpu().numpy() if hasattr(v, "cpu") else v)
                                       for k, v in feat.items()})
-
-    line = {
-        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-        "data": "synthetic",
+    del dev
+    torch.cuda.empty_cache()
+    return {
+        "value": round(value, 2), "unit": unit, "ms_per_step": ms_step,
         "config": {"workload": w.name, "batch": w.batch_size, "tokens": T,
                    "num_heads": w.num_heads, "kv_num_heads": w.kv_num_heads,
                    "head_size": w.head_size, "block_size": w.block_size,
@@ -639,14 +555,264 @@ def main():
                    "qk_norm": bool(args.qk_norm),
                    "decode_requests": n_dec, "decode_bytes": dec_bytes,
                    "prefill_flops": pf_flops, "plan": plan},
+        "timing": {"cold_ms": cold, "warm_ms": warm, "warmup": m["warmup"],
+                   "cold_warm_ratio": round(cold["median"] / warm["median"], 4)},
+        "warm": {"value": round(warm_value, 2), "unit": unit, "ms_per_step": warm["median"],
+                 "note": "back-to-back steps, caches holding what the previous step left"},
         "roofline": roof,
         "step_roofline_frac": round(step_frac, 4),
         "kernels": kernels,
         "append": append,
-        "ms_per_step_instrumented": round(ms_step_instrumented, 5),
         "cpu_baseline": cpu,
         "parity_max_abs_err_sampled": err,
     }
+
+
+# ---------------------------------------------------------------------------
+# latent attention (MLA) workloads
+# ---------------------------------------------------------------------------
+
+def mla_work(w):
+    """Latent attention: bytes (each admitted 576-channel row once -- V is a
+    view of K -- plus the fp16 Q and O rows of every query token) and FLOPs
+    (2 * H * (D + DV) per admitted key of every query token)."""
+    from paged_kv_cache_append_amd import workloads as wl
+    H, D, DV = w.num_heads, w.head_size, wl.MLA_V_HEAD_SIZE
+    W = w.local_window_size
+    nbytes = 0
+    keys = 0
+    for b in range(w.batch_size):
+        for j in range(int(w.q_lens[b])):
+            pos = int(w.past[b]) + j
+            kv = pos + 1 - (max(0, pos - W + 1) if W > 0 else 0)
+            nbytes += kv * D * 2 + H * D * 2 + H * DV * 2
+            keys += kv
+    return nbytes, 2.0 * H * (D + DV) * keys
+
+
+def mla_cpu_baseline(w, gpu_out, sample=16, target_seconds=10.0):
+    """The oracle on the first ``sample`` requests of a latent workload, for
+    about target_seconds: GB/s of the same algorithmic bytes, and the max-abs
+    error of the GPU rows it covers."""
+    import oracle
+    from paged_kv_cache_append_amd import workloads as wl
+    sub = wl.subset(w, list(range(min(sample, w.batch_size))))
+    rot = dict(cos_cache=sub.cos_cache, sin_cache=sub.sin_cache,
+               rotary_interleaved=bool(sub.rotary_interleaved),
+               rotary_offset=wl.MLA_ROTARY_OFFSET)
+    kc = sub.pool_blocks(wl.KIND_K, range(sub.num_blocks))
+    nk, _ = oracle.append_kv(kc, None, sub.key, None, sub.cum, sub.past, sub.block_table,
+                             kv_num_heads=1, head_size=sub.head_size,
+                             kv_cache_layout=oracle.LAYOUT_LATENT, **rot)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        ref = oracle.forward(sub.query, nk, None, sub.cum, sub.past, sub.block_table,
+                             num_heads=sub.num_heads, kv_num_heads=1, head_size=sub.head_size,
+                             scale=sub.scale, softcap=sub.softcap,
+                             local_window_size=sub.local_window_size,
+                             kv_cache_layout=oracle.LAYOUT_LATENT,
+                             v_head_size=wl.MLA_V_HEAD_SIZE, **rot)
+        reps += 1
+        if time.perf_counter() - t0 >= target_seconds:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    nbytes, _ = mla_work(sub)
+    err = float(np.max(np.abs(gpu_out[sub.extra["parent_rows"]].astype(np.float64) - ref)))
+    return _cpu_entry(nbytes / dt / 1e9, "GB/s",
+                      f"{sub.batch_size} requests of {w.name} ({nbytes / 1e6:.1f} MB of latent "
+                      f"rows + Q/O), gather + full scores + softmax + PV in fp64, {dt:.2f} s "
+                      f"per pass, {reps} passes"), err
+
+
+def run_mla(name, args, flush, ceiling):
+    """Latent attention (MLA) step: append of the latent rows + forward on the
+    latent kernel, over an absorbed DeepSeek-shaped decode batch."""
+    import torch
+
+    import paged_kv_cache_append_amd as pa
+    from paged_kv_cache_append_amd import workloads as wl
+    w = wl.make_mla_workload(name)
+    dev = wl.to_device(w)
+    a = pa.Attn(num_heads=w.num_heads, kv_num_heads=1, head_size=w.head_size,
+                block_size=w.block_size, scale=w.scale, do_rotary=1,
+                rotary_interleaved=w.rotary_interleaved, kv_cache_layout=pa.LAYOUT_LATENT,
+                v_head_size=wl.MLA_V_HEAD_SIZE, rotary_offset=wl.MLA_ROTARY_OFFSET)
+    T = w.token_count
+    out = torch.empty((T, w.num_heads * wl.MLA_V_HEAD_SIZE), dtype=torch.float16, device="cuda")
+    nws = pa.forward_workspace_bytes(a, dev["key_cache"], None, dev["block_table"], dev["cum"],
+                                     dev["past"], T)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    plan = pa.describe_plan(a, dev["key_cache"], None, dev["block_table"], dev["cum"],
+                            dev["past"], T)
+
+    def step():
+        pa.append_kv(a, dev["key"], None, dev["key_cache"], None, dev["block_table"], dev["cum"],
+                     dev["past"], dev["cos"], dev["sin"])
+        pa.forward(a, dev["query"], dev["key_cache"], None, dev["block_table"], dev["cum"],
+                   dev["past"], dev["cos"], dev["sin"], workspace=ws, out=out)
+
+    m = measure(step, args.steps, args.warmup, flush)
+    cold, warm = stats(m["cold"]), stats(m["warm"])
+    per = {s: (ms / n * 1e3 if n else 0.0) for s, (ms, n) in m["stages"].items()}
+    nbytes, flops = mla_work(w)
+    t = per["decode"] * 1e-6
+    gbs, tfs = nbytes / t / 1e9, flops / t / 1e12
+    hbm_bound = nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_F16_PEAK_TFS * 1e12)
+    roof = {"bound": "hbm" if hbm_bound else "mfma", "kernel": "mla",
+            "achieved": round(gbs if hbm_bound else tfs, 4),
+            "peak": HBM_PEAK_GBS if hbm_bound else MFMA_F16_PEAK_TFS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": round(gbs / HBM_PEAK_GBS if hbm_bound else tfs / MFMA_F16_PEAK_TFS, 4),
+            "traffic": traffic_from_profiles(f"mla:{w.name}", kernel_source_hash("mla")),
+            "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
+            "kernel_us": round(per["decode"], 3),
+            "other_unit_frac": round(tfs / MFMA_F16_PEAK_TFS if hbm_bound
+                                     else gbs / HBM_PEAK_GBS, 4)}
+    if hbm_bound and ceiling:
+        roof["frac_of_ceiling"] = round(gbs / ceiling["gbs"], 4)
+    kernels = {f"{s}_us": round(v, 3) for s, v in per.items()}
+    kernels["mla_kernel_gbs"] = round(gbs, 1)
+    kernels["mla_kernel_tflops"] = round(tfs, 2)
+    cpu, err = (None, None)
+    if not args.no_cpu_baseline:
+        cpu, err = mla_cpu_baseline(w, out.cpu().numpy())
+    return {
+        "value": round(nbytes / (cold["median"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "ms_per_step": cold["median"],
+        "config": {"workload": w.name, "batch": w.batch_size, "tokens": T,
+                   "num_heads": w.num_heads, "kv_num_heads": 1, "head_size": w.head_size,
+                   "v_head_size": wl.MLA_V_HEAD_SIZE, "block_size": w.block_size,
+                   "kv_cache_layout": "latent", "rotary_offset": wl.MLA_ROTARY_OFFSET,
+                   "latent_bytes": nbytes, "flops": flops, "plan": plan},
+        "timing": {"cold_ms": cold, "warm_ms": warm, "warmup": m["warmup"],
+                   "cold_warm_ratio": round(cold["median"] / warm["median"], 4)},
+        "warm": {"value": round(nbytes / (warm["median"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+                 "ms_per_step": warm["median"]},
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "parity_max_abs_err_sampled": err,
+    }
+
+
+def copy_calibration(mib):
+    """A plain fp16 copy kernel over ``mib`` MiB (read N, write N), three
+    times: the reference the HBM byte counters are scaled by."""
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for i in range(3):
+        ev[i].record()
+        torch.neg(src, out=dst)
+    ev[3].record()
+    torch.cuda.synchronize()
+    ms = ev[2].elapsed_time(ev[3])   # the last launch, caches warm
+    print(f"copy calibration: {mib} MiB read + {mib} MiB written per launch, "
+          f"{2 * n * 2 / (ms * 1e-3) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50,
+                    help="timed steps per pass (cold, warm and per-kernel passes)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: at least "
+                         f"{WARMUP_SECONDS} s of steps, and 10; the count is reported)")
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--prefill-config", default=None,
+                    help=f"workload of the 'prefill' object (default {DEFAULT_PREFILL_CONFIG} "
+                         "with the default --config; 'none' to leave it out)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="no scratch write between the 'cold' steps (they are then warm too)")
+    ap.add_argument("--cache", choices=("fp16", "int8", "fp8"), default="fp16",
+                    help="element type of the paged pools (int8 / fp8: codes + fp32 scales)")
+    ap.add_argument("--k-quant", choices=("tensor", "channel"), default="channel")
+    ap.add_argument("--v-quant", choices=("tensor", "channel"), default="channel")
+    ap.add_argument("--head-sink", action="store_true",
+                    help="a sink logit per head (drawn from U[-2, 3])")
+    ap.add_argument("--smooth-softmax", action="store_true", help="a zero sink for every head")
+    ap.add_argument("--qk-norm", action="store_true",
+                    help="QK-Norm of Q and new K with drawn weights (U[0.5, 1.5]), eps 1e-6")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain fp16 copy kernel over this many MiB (read N, "
+                         "write N), three times, to scale HBM byte counters")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="print per-kernel mean counter values of rocprofv3 counter "
+                         "CSV files and exit (no GPU use)")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("KERNEL", "CSV"),
+                    help="print the MFMA utilisation of KERNEL from a counter CSV and exit")
+    ap.add_argument("--record-traffic", nargs=5,
+                    metavar=("TAG", "KERNEL", "FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
+                    help="store HBM bytes per launch of KERNEL (substring of the kernel "
+                         "name) under TAG in profiles/traffic.json, from a FETCH_SIZE and a "
+                         "WRITE_SIZE counter run that both include the copy calibration of "
+                         "COPY_MIB MiB, and exit (no GPU use)")
+    args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
+        return
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    from paged_kv_cache_append_amd import workloads as wl
+    latent = args.config in wl.MLA_CONFIG_NAMES
+    if latent and (args.cache != "fp16" or args.head_sink or args.smooth_softmax or args.qk_norm):
+        print("bench.py: the latent workloads run with an fp16 cache and no sink or QK-Norm "
+              "(section 12.10)", file=sys.stderr)
+        sys.exit(2)
+    if not latent and args.cache != "fp16":
+        w = wl.make_workload(args.config)
+        if np.any(w.q_lens != 1):
+            print(f"bench.py: --cache {args.cache} measures decode-only workloads (one new "
+                  f"token per request); {w.name} has multi-token requests", file=sys.stderr)
+            sys.exit(2)
+        del w
+    pf_name = args.prefill_config
+    if pf_name is None:
+        pf_name = DEFAULT_PREFILL_CONFIG if (args.config == DEFAULT_CONFIG and
+                                             args.cache == "fp16") else "none"
+
+    import torch
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+    ceiling = hbm_ceiling()
+    flush = (lambda: None) if args.no_flush else Flusher()
+    res = run_mla(args.config, args, flush, ceiling) if latent else \
+        run_workload(args.config, args, flush, ceiling)
+    line = {"metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+            "steps": args.steps, "warmup": res["timing"]["warmup"],
+            "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f16", "data": "synthetic"}
+    line.update({k: v for k, v in res.items() if k not in ("value", "unit", "ms_per_step")})
+    line["timing"]["protocol"] = (
+        "per step: its own event pair on the launch stream; 'cold' steps follow a "
+        f"{FLUSH_BYTES >> 20} MiB scratch write (outside the pair)"
+        if not args.no_flush else "per step: its own event pair; no scratch write (warm)")
+    line["hbm_ceiling"] = ceiling
+    if pf_name != "none":
+        if pf_name in wl.MLA_CONFIG_NAMES:
+            raise SystemExit("--prefill-config takes a prefill workload")
+        args_pf = argparse.Namespace(**vars(args))
+        args_pf.cache, args_pf.head_sink, args_pf.smooth_softmax, args_pf.qk_norm = \
+            "fp16", False, False, False
+        pf = run_workload(pf_name, args_pf, flush, ceiling)
+        line["prefill"] = {"workload": pf_name, "value": pf["value"], "unit": pf["unit"],
+                           "ms_per_step": pf["ms_per_step"],
+                           **{k: v for k, v in pf.items()
+                              if k not in ("value", "unit", "ms_per_step")}}
     print(json.dumps(line), flush=True)
 
 

@@ -58,21 +58,6 @@ typedef struct {
   int32_t do_rotary;          /* 0/1: rotate new K (pa_append_kv) and Q (pa_forward)
                                  at their absolute position                            */
   int32_t rotary_interleaved; /* 0: pairs (i, i + r/2); 1: pairs (2i, 2i+1)            */
-  int32_t path;               /* kernel routing, 0 = auto (token_count <= batch_size
-                                 -> decode kernel only, else decode + prefill kernels);
-                                 1 = decode kernel for every token; 2 = decode kernel
-                                 for q_len == 1 requests, prefill kernel for the rest.
-                                 Results are the same up to rounding.                  */
-  int32_t split_tokens;       /* 0 = auto; else decode KV split length in tokens, a
-                                 multiple of 64 (testing hook; rounding may differ)    */
-  int32_t prefill_pieces;     /* 0 = auto; else 1..4: workgroups sharing one prefill
-                                 tile's key range, merged on the device (testing
-                                 hook; rounding may differ)                            */
-  int32_t prefill_kernel;     /* 0 = auto; 1 = 4-wave prefill kernel (32 query rows
-                                 per wave); 2 = 8-wave kernel (16 rows per wave),
-                                 head_size 256 with each cache smaller than 4 GiB,
-                                 else PA_ERR_UNSUPPORTED.  Auto takes 2 where it
-                                 applies.  Testing hook; rounding may differ.          */
   int32_t cache_dtype;        /* element type of both caches (section 8.2):
                                  PA_CACHE_FP16 (0), PA_CACHE_INT8 (1) or
                                  PA_CACHE_FP8_E4M3FN (2); see "Quantized caches"     */
@@ -115,7 +100,7 @@ typedef struct {
  * Rules (section 12.10): an explicit scale when v_head_size != head_size
  * (section 12.6), no head_sink / smooth softmax / QK-Norm, no V quantization,
  * and RoPE only past the V channels (rotary_offset >= v_head_size).  Every
- * token runs on the latent kernel (path 2 is PA_ERR_UNSUPPORTED). */
+ * token runs on the latent kernel. */
 enum { PA_LAYOUT_SEPARATE = 0, PA_LAYOUT_LATENT = 1 };
 
 /* Quantized caches (PagedAttention -- CUDA Design Document, section 8).
@@ -133,8 +118,7 @@ enum { PA_LAYOUT_SEPARATE = 0, PA_LAYOUT_LATENT = 1 };
  * dequantizes in the kernel (section 8.5, phase 3): a PER_TENSOR K scale is
  * folded into the score scale, a PER_CHANNEL one into Q (rounded to fp16), and
  * the V scale is applied to the output accumulator.  Every token of a
- * quantized forward runs on the decode kernel (path 0 or 1; path 2 is
- * PA_ERR_UNSUPPORTED).  Validation (section 8.7): a quantized cache_dtype
+ * quantized forward runs on the decode kernel.  Validation (section 8.7): a quantized cache_dtype
  * needs both quant types non-NONE, fp16 needs both NONE; a quant type other
  * than NONE needs its scale and NONE forbids it. */
 enum { PA_CACHE_FP16 = 0, PA_CACHE_INT8 = 1, PA_CACHE_FP8_E4M3FN = 2 };
@@ -151,7 +135,12 @@ typedef struct {
   int64_t num_blocks;                       /* > 0; num_blocks * block_size < 2^32   */
   const int32_t *block_table;               /* int32 [batch_size, max_blocks_per_seq]
                                                row-major; entries past a request's
-                                               length are never read                 */
+                                               length are never read.  -1 (or any
+                                               value outside [0, num_blocks)) is an
+                                               unmapped block (section 9.2 item 3,
+                                               section 9.3.1): the derived append
+                                               writes nothing there and the forward
+                                               masks its positions out            */
   int32_t max_blocks_per_seq;               /* > 0; capacity = this * block_size     */
   const int32_t *cumulative_sequence_length;/* int32 [batch_size + 1], cum[0] = 0,
                                                non-decreasing, cum[batch] <= tokens  */
@@ -236,7 +225,9 @@ pa_status pa_forward_workspace_bytes(const pa_attn_params *params, const pa_page
  *
  * out[t, h*D:(h+1)*D] = sum_tau softmax_tau(cap(scale * q_t,h . k_tau)) v_tau over
  * positions tau of t's request with tau <= p_t and (W < 0 or tau > p_t - W), K/V
- * read from the pool (so pa_append_kv must run first).  Rows of tokens
+ * read from the pool (so pa_append_kv must run first).  Positions whose block
+ * is unmapped (block_table entry -1) are masked out like positions outside the
+ * window; a row left with no admitted key is written as 0.  Rows of tokens
  * t >= cum[batch_size] are written as 0.  A bound smaller than a real length
  * violates the contract: work is omitted, memory stays safe.
  */
@@ -250,31 +241,6 @@ pa_status pa_forward(const pa_attn_params *params, const pa_paged_kv *kv,
 
 /* Thread-local text of the last error on this thread ("" if none). */
 const char *pa_last_error(void);
-
-/*
- * pa_describe_plan -- host call; writes into `buf` (host, `len` bytes) a one-line
- * description of the launches pa_forward would make for these shapes and
- * bounds (path, grids, split length).  For logs and tests.
- */
-pa_status pa_describe_plan(const pa_attn_params *params, const pa_paged_kv *kv,
-                           int32_t max_query_len_bound, int32_t max_kv_len_bound,
-                           char *buf, size_t len);
-
-/*
- * Per-kernel timing on the launch stream, for benchmarks.  While enabled, the
- * library launches every kernel with a start/stop event pair that the
- * dispatch itself timestamps, and pa_timing_read() sums their elapsed times
- * per stage (synchronizing on the recorded events).  Enabling creates the
- * events (2 * max_launches); it is not meant for graph capture.
- *   stage: 0 = append, 1 = decode, 2 = decode split merge, 3 = prefill,
- *          4 = decode work-list planning, 5 = prefill piece merge,
- *          6 = QK-Norm prologue of the queries.
- */
-enum { PA_STAGE_APPEND = 0, PA_STAGE_DECODE = 1, PA_STAGE_MERGE = 2, PA_STAGE_PREFILL = 3,
-       PA_STAGE_PLAN = 4, PA_STAGE_PREFILL_MERGE = 5, PA_STAGE_Q_NORM = 6, PA_NUM_STAGES = 7 };
-pa_status pa_timing_enable(int32_t max_launches);
-pa_status pa_timing_disable(void);
-pa_status pa_timing_read(int32_t stage, double *total_ms, int32_t *launches);
 
 #ifdef __cplusplus
 }

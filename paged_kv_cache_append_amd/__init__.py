@@ -7,7 +7,9 @@ other implementation, and calling it without the built library raises.
 
 Names mirror the C entry points: :func:`append_kv` (``pa_append_kv``),
 :func:`forward` (``pa_forward``), :func:`forward_workspace_bytes`,
-:func:`describe_plan`, :func:`last_error`, and the ``timing_*`` helpers.
+:func:`last_error`; and, from ``include/pa_testing.h``, :class:`Routing`
+(``pa_routing``, taken by :func:`forward`, :func:`forward_workspace_bytes` and
+:func:`describe_plan`), the ``timing_*`` helpers and :func:`stream_read`.
 """
 from __future__ import annotations
 
@@ -17,11 +19,11 @@ from typing import Any, Optional
 
 from . import _lib
 
-__all__ = ["PAError", "Attn", "CACHE_FP16", "CACHE_INT8", "CACHE_FP8_E4M3FN", "LAYOUT_SEPARATE",
+__all__ = ["PAError", "Attn", "Routing", "CACHE_FP16", "CACHE_INT8", "CACHE_FP8_E4M3FN", "LAYOUT_SEPARATE",
            "LAYOUT_LATENT", "QUANT_NONE",
            "QUANT_PER_TENSOR", "QUANT_PER_CHANNEL", "append_kv", "forward", "forward_workspace_bytes",
            "describe_plan", "last_error", "timing_enable", "timing_disable", "timing_read",
-           "library_path"]
+           "stream_read", "library_path"]
 
 
 # cache element types, scale granularities and cache layouts (the ABI enums of pa.h)
@@ -48,10 +50,6 @@ class Attn:
     local_window_size: int = -1
     do_rotary: int = 0
     rotary_interleaved: int = 0
-    path: int = 0
-    split_tokens: int = 0
-    prefill_pieces: int = 0
-    prefill_kernel: int = 0
     cache_dtype: int = CACHE_FP16
     k_quant_type: int = QUANT_NONE
     v_quant_type: int = QUANT_NONE
@@ -79,12 +77,26 @@ class Attn:
         return _lib.AttnParams(self.num_heads, self.kv_num_heads, self.head_size,
                                self.block_size, float(self.scale), float(self.softcap),
                                self.local_window_size, self.do_rotary,
-                               self.rotary_interleaved, self.path, self.split_tokens,
-                               self.prefill_pieces, self.prefill_kernel, self.cache_dtype,
+                               self.rotary_interleaved, self.cache_dtype,
                                self.k_quant_type, self.v_quant_type, _ptr(self.head_sink),
                                self.use_smooth_softmax, _ptr(self.q_norm_weight),
                                _ptr(self.k_norm_weight), float(self.qk_norm_epsilon),
                                self.kv_cache_layout, self.v_head_size, self.rotary_offset)
+
+
+@dataclass
+class Routing:
+    """Forced kernel routing (``pa_routing`` of ``include/pa_testing.h``);
+    all zeros is the automatic choice.  For tests: every choice computes the
+    same function, only the rounding may differ."""
+    path: int = 0
+    split_tokens: int = 0
+    prefill_pieces: int = 0
+    prefill_kernel: int = 0
+
+    def c(self) -> _lib.Routing:
+        return _lib.Routing(self.path, self.split_tokens, self.prefill_pieces,
+                            self.prefill_kernel)
 
 
 def library_path() -> str:
@@ -188,39 +200,53 @@ def append_kv(attn: Attn, key, value, key_cache, value_cache, block_table, cum, 
                             c, s, rows, rd, _stream(stream)))
 
 
+def _workspace_bytes(lib, p, kv, routing, mq, mk) -> int:
+    n = ctypes.c_size_t(0)
+    if routing is None:
+        _check(lib.pa_forward_workspace_bytes(ctypes.byref(p), ctypes.byref(kv), mq, mk,
+                                              ctypes.byref(n)))
+    else:
+        r = routing.c()
+        _check(lib.pa_forward_workspace_bytes_routed(ctypes.byref(p), ctypes.byref(kv),
+                                                     ctypes.byref(r), mq, mk, ctypes.byref(n)))
+    return int(n.value)
+
+
 def forward_workspace_bytes(attn: Attn, key_cache, value_cache, block_table, cum, past,
                             token_count: int, max_query_len_bound: int = 0,
-                            max_kv_len_bound: int = 0, k_scale=None, v_scale=None) -> int:
+                            max_kv_len_bound: int = 0, k_scale=None, v_scale=None,
+                            routing: Optional[Routing] = None) -> int:
+    """``pa_forward_workspace_bytes`` (``..._routed`` with a forced ``routing``)."""
     lib = _lib.load()
     p = attn.c()
     kv = _kv(attn, key_cache, value_cache, block_table, cum, past, token_count,
              k_scale=k_scale, v_scale=v_scale)
-    n = ctypes.c_size_t(0)
-    _check(lib.pa_forward_workspace_bytes(ctypes.byref(p), ctypes.byref(kv), max_query_len_bound,
-                                          max_kv_len_bound, ctypes.byref(n)))
-    return int(n.value)
+    return _workspace_bytes(lib, p, kv, routing, max_query_len_bound, max_kv_len_bound)
 
 
 def describe_plan(attn: Attn, key_cache, value_cache, block_table, cum, past, token_count: int,
                   max_query_len_bound: int = 0, max_kv_len_bound: int = 0, k_scale=None,
-                  v_scale=None) -> str:
+                  v_scale=None, routing: Optional[Routing] = None) -> str:
     lib = _lib.load()
     p = attn.c()
     kv = _kv(attn, key_cache, value_cache, block_table, cum, past, token_count,
              k_scale=k_scale, v_scale=v_scale)
     buf = ctypes.create_string_buffer(512)
-    _check(lib.pa_describe_plan(ctypes.byref(p), ctypes.byref(kv), max_query_len_bound,
+    r = None if routing is None else ctypes.byref(routing.c())
+    _check(lib.pa_describe_plan(ctypes.byref(p), ctypes.byref(kv), r, max_query_len_bound,
                                 max_kv_len_bound, buf, 512))
     return buf.value.decode()
 
 
 def forward(attn: Attn, query, key_cache, value_cache, block_table, cum, past, cos_cache=None,
             sin_cache=None, max_query_len_bound: int = 0, max_kv_len_bound: int = 0,
-            workspace=None, out=None, stream=None, k_scale=None, v_scale=None):
+            workspace=None, out=None, stream=None, k_scale=None, v_scale=None,
+            routing: Optional[Routing] = None):
     """``pa_forward``: attention output ``[T, H*DV]`` fp16 (``DV`` =
-    ``attn.out_head_size``) for packed queries ``[T, H*D]``.  ``workspace``/``out`` are allocated with torch when not
-    given; quantized caches take ``k_scale``/``v_scale`` as for
-    :func:`append_kv`."""
+    ``attn.out_head_size``) for packed queries ``[T, H*D]``.  ``workspace``
+    and ``out`` are allocated with torch when not given; quantized caches take
+    ``k_scale``/``v_scale`` as for :func:`append_kv`.  A ``routing`` calls
+    ``pa_forward_routed`` instead."""
     import torch
     T = query.shape[0]
     HD = attn.num_heads * attn.head_size
@@ -233,18 +259,22 @@ def forward(attn: Attn, query, key_cache, value_cache, block_table, cum, past, c
     if out is None:
         out = torch.empty((T, HO), dtype=torch.float16, device=query.device)
     _need(out, "out", torch.float16, (T, HO))
-    n = ctypes.c_size_t(0)
-    _check(lib.pa_forward_workspace_bytes(ctypes.byref(p), ctypes.byref(kv), max_query_len_bound,
-                                          max_kv_len_bound, ctypes.byref(n)))
-    need = int(n.value)
+    need = _workspace_bytes(lib, p, kv, routing, max_query_len_bound, max_kv_len_bound)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_ptr = _ptr(workspace)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     c, s, rows, rd = _rot(attn, cos_cache, sin_cache)
-    _check(lib.pa_forward(ctypes.byref(p), ctypes.byref(kv), query.data_ptr(), c, s, rows, rd,
-                          max_query_len_bound, max_kv_len_bound, ws_ptr, ws_len, out.data_ptr(),
-                          _stream(stream)))
+    if routing is None:
+        _check(lib.pa_forward(ctypes.byref(p), ctypes.byref(kv), query.data_ptr(), c, s, rows, rd,
+                              max_query_len_bound, max_kv_len_bound, ws_ptr, ws_len,
+                              out.data_ptr(), _stream(stream)))
+    else:
+        r = routing.c()
+        _check(lib.pa_forward_routed(ctypes.byref(p), ctypes.byref(kv), ctypes.byref(r),
+                                     query.data_ptr(), c, s, rows, rd, max_query_len_bound,
+                                     max_kv_len_bound, ws_ptr, ws_len, out.data_ptr(),
+                                     _stream(stream)))
     return out
 
 
@@ -256,9 +286,16 @@ def timing_disable() -> None:
     _check(_lib.load().pa_timing_disable())
 
 
+def stream_read(src, sink, stream=None) -> None:
+    """``pa_bench_stream_read``: read every byte of the device tensor ``src``
+    (a multiple of 16 KiB) once; ``sink`` is a device tensor of >= 4 bytes."""
+    n = src.numel() * src.element_size()
+    _check(_lib.load().pa_bench_stream_read(src.data_ptr(), n, sink.data_ptr(), _stream(stream)))
+
+
 def timing_read(stage: str):
     """(total milliseconds, launches) recorded for ``stage`` in
-    {append, decode, merge, prefill, plan, prefill_merge}."""
+    {append, decode, merge, prefill, plan, prefill_merge, q_norm}."""
     lib = _lib.load()
     ms = ctypes.c_double(0)
     n = ctypes.c_int32(0)

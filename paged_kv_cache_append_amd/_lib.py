@@ -1,4 +1,5 @@
-"""ctypes declarations of the C ABI in ``include/pa.h`` (libpa.so)."""
+"""ctypes declarations of the C ABI of libpa.so: the op (``include/pa.h``)
+and the test and measurement entry points (``include/pa_testing.h``)."""
 from __future__ import annotations
 
 import ctypes
@@ -15,8 +16,11 @@ PA_ERR_DEVICE = 3
 STAGES = {"append": 0, "decode": 1, "merge": 2, "prefill": 3, "plan": 4, "prefill_merge": 5,
           "q_norm": 6}
 
-EXPORTED = ("pa_append_kv", "pa_forward_workspace_bytes", "pa_forward", "pa_last_error",
-            "pa_describe_plan", "pa_timing_enable", "pa_timing_disable", "pa_timing_read")
+# entry points of include/pa.h, and of include/pa_testing.h
+EXPORTED = ("pa_append_kv", "pa_forward_workspace_bytes", "pa_forward", "pa_last_error")
+TESTING_EXPORTED = ("pa_forward_workspace_bytes_routed", "pa_forward_routed", "pa_describe_plan",
+                    "pa_timing_enable", "pa_timing_disable", "pa_timing_read",
+                    "pa_bench_stream_read")
 
 
 class AttnParams(ctypes.Structure):
@@ -24,9 +28,7 @@ class AttnParams(ctypes.Structure):
                 ("head_size", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
                 ("local_window_size", ctypes.c_int32), ("do_rotary", ctypes.c_int32),
-                ("rotary_interleaved", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("split_tokens", ctypes.c_int32), ("prefill_pieces", ctypes.c_int32),
-                ("prefill_kernel", ctypes.c_int32), ("cache_dtype", ctypes.c_int32),
+                ("rotary_interleaved", ctypes.c_int32), ("cache_dtype", ctypes.c_int32),
                 ("k_quant_type", ctypes.c_int32), ("v_quant_type", ctypes.c_int32),
                 ("head_sink", ctypes.c_void_p), ("use_smooth_softmax", ctypes.c_int32),
                 ("q_norm_weight", ctypes.c_void_p), ("k_norm_weight", ctypes.c_void_p),
@@ -42,6 +44,11 @@ class PagedKV(ctypes.Structure):
                 ("past_seqlens", ctypes.c_void_p), ("batch_size", ctypes.c_int32),
                 ("token_count", ctypes.c_int32), ("slot_mapping", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
+                ("prefill_pieces", ctypes.c_int32), ("prefill_kernel", ctypes.c_int32)]
 
 
 _lib = None
@@ -73,7 +80,14 @@ def load() -> ctypes.CDLL:
     lib.pa_forward.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
-    lib.pa_describe_plan.argtypes = [P(AttnParams), P(PagedKV), i32, i32, ctypes.c_char_p, sz]
+    lib.pa_forward_workspace_bytes_routed.argtypes = [P(AttnParams), P(PagedKV), P(Routing), i32,
+                                                      i32, P(sz)]
+    lib.pa_forward_workspace_bytes_routed.restype = ctypes.c_int
+    lib.pa_forward_routed.argtypes = [P(AttnParams), P(PagedKV), P(Routing), vp, vp, vp, i32, i32,
+                                      i32, i32, vp, sz, vp, vp]
+    lib.pa_forward_routed.restype = ctypes.c_int
+    lib.pa_describe_plan.argtypes = [P(AttnParams), P(PagedKV), P(Routing), i32, i32,
+                                     ctypes.c_char_p, sz]
     lib.pa_describe_plan.restype = ctypes.c_int
     lib.pa_timing_enable.argtypes = [i32]
     lib.pa_timing_enable.restype = ctypes.c_int
@@ -81,5 +95,7 @@ def load() -> ctypes.CDLL:
     lib.pa_timing_disable.restype = ctypes.c_int
     lib.pa_timing_read.argtypes = [i32, P(ctypes.c_double), P(i32)]
     lib.pa_timing_read.restype = ctypes.c_int
+    lib.pa_bench_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.pa_bench_stream_read.restype = ctypes.c_int
     _lib = lib
     return lib

@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "../../include/pa.h"
+#include "../../include/pa_testing.h"
 #include "pa_internal.h"
 
 namespace {
@@ -237,19 +238,8 @@ pa_status check_common(const pa_attn_params* p, const pa_paged_kv* kv) {
   if (p->rotary_interleaved != 0 && p->rotary_interleaved != 1)
     return fail(PA_ERR_INVALID_ARGUMENT, "rotary_interleaved: expected 0 or 1, got %d",
                 p->rotary_interleaved);
-  if (p->path < 0 || p->path > 2)
-    return fail(PA_ERR_INVALID_ARGUMENT, "path: expected 0, 1 or 2, got %d", p->path);
   if (p->num_heads > 65535)
     return fail(PA_ERR_INVALID_ARGUMENT, "num_heads: expected <= 65535, got %d", p->num_heads);
-  if (p->prefill_pieces < 0 || p->prefill_pieces > pa::kPrefillChunks)
-    return fail(PA_ERR_INVALID_ARGUMENT, "prefill_pieces: expected 0..%d, got %d",
-                pa::kPrefillChunks, p->prefill_pieces);
-  if (p->prefill_kernel < 0 || p->prefill_kernel > 2)
-    return fail(PA_ERR_INVALID_ARGUMENT, "prefill_kernel: expected 0, 1 or 2, got %d",
-                p->prefill_kernel);
-  if (p->split_tokens < 0 || p->split_tokens % 64 != 0)
-    return fail(PA_ERR_INVALID_ARGUMENT, "split_tokens: expected 0 or a multiple of 64, got %d",
-                p->split_tokens);
   if (kv->batch_size <= 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "batch_size: expected > 0, got %d", kv->batch_size);
   if (kv->token_count < 0)
@@ -305,6 +295,29 @@ pa_status check_rotary(const pa_attn_params* p, const pa_paged_kv* kv, const voi
   return PA_OK;
 }
 
+// Forced routing of the testing entry points (pa_testing.h); all zeros is the
+// automatic choice of pa_forward.
+pa_routing auto_routing() {
+  pa_routing r;
+  r.path = r.split_tokens = r.prefill_pieces = r.prefill_kernel = 0;
+  return r;
+}
+
+pa_status check_routing(const pa_routing* r) {
+  if (r->path < 0 || r->path > 2)
+    return fail(PA_ERR_INVALID_ARGUMENT, "path: expected 0, 1 or 2, got %d", r->path);
+  if (r->prefill_pieces < 0 || r->prefill_pieces > pa::kPrefillChunks)
+    return fail(PA_ERR_INVALID_ARGUMENT, "prefill_pieces: expected 0..%d, got %d",
+                pa::kPrefillChunks, r->prefill_pieces);
+  if (r->prefill_kernel < 0 || r->prefill_kernel > 2)
+    return fail(PA_ERR_INVALID_ARGUMENT, "prefill_kernel: expected 0, 1 or 2, got %d",
+                r->prefill_kernel);
+  if (r->split_tokens < 0 || r->split_tokens % 64 != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "split_tokens: expected 0 or a multiple of 64, got %d",
+                r->split_tokens);
+  return PA_OK;
+}
+
 // Each cache is small enough for 32-bit byte offsets (buffer addressing).
 bool pool_fits_32bit(const pa_attn_params* p, const pa_paged_kv* kv) {
   return kv->num_blocks * p->block_size * p->kv_num_heads * p->head_size * 2 <
@@ -316,7 +329,8 @@ bool rows16_prefill_fits(const pa_attn_params* p, const pa_paged_kv* kv) {
   return p->head_size == 256 && pool_fits_32bit(p, kv);
 }
 
-pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv) {
+pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv,
+                               const pa_routing& rt) {
   if (p->kv_cache_layout == PA_LAYOUT_LATENT) {
     if (p->head_size != pa::kMlaHeadSize || effective_v_head_size(p) != pa::kMlaVHeadSize)
       return fail(PA_ERR_UNSUPPORTED,
@@ -325,7 +339,7 @@ pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv) {
                   pa::kMlaHeadSize, pa::kMlaVHeadSize, p->head_size, effective_v_head_size(p));
     if (p->cache_dtype != PA_CACHE_FP16)
       return fail(PA_ERR_UNSUPPORTED, "kv_cache_layout LATENT: served for fp16 caches");
-    if (p->path == 2)
+    if (rt.path == 2)
       return fail(PA_ERR_UNSUPPORTED,
                   "path 2: the latent kernel serves every token (path 0 or 1)");
     if (kv->num_blocks * p->block_size * p->head_size * 2 > (int64_t)pa::kMlaZeroRow)
@@ -336,10 +350,10 @@ pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv) {
   if (p->head_size != 64 && p->head_size != 128 && p->head_size != 256)
     return fail(PA_ERR_UNSUPPORTED,
                 "head_size %d: the kernels serve head_size 64, 128 and 256", p->head_size);
-  if (p->prefill_kernel == 2 && !rows16_prefill_fits(p, kv))
+  if (rt.prefill_kernel == 2 && !rows16_prefill_fits(p, kv))
     return fail(PA_ERR_UNSUPPORTED,
                 "prefill_kernel 2: expected head_size 256 and caches smaller than 4 GiB");
-  if (p->cache_dtype != PA_CACHE_FP16 && p->path == 2)
+  if (p->cache_dtype != PA_CACHE_FP16 && rt.path == 2)
     return fail(PA_ERR_UNSUPPORTED,
                 "path 2: quantized caches are served by the decode kernel only (path 0 or 1)");
   return PA_OK;
@@ -370,7 +384,8 @@ struct Plan {
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32_t mk) {
+Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, const pa_routing& rt, int32_t mq,
+               int32_t mk) {
   Plan pl;
   const int T = kv->token_count, B = kv->batch_size;
   pl.g = p->num_heads / p->kv_num_heads;
@@ -380,9 +395,9 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
       break;
     }
   pl.head_chunks = pl.g / pl.chunk_heads;
-  if (p->path == 1 || p->cache_dtype != PA_CACHE_FP16 || p->kv_cache_layout == PA_LAYOUT_LATENT)
+  if (rt.path == 1 || p->cache_dtype != PA_CACHE_FP16 || p->kv_cache_layout == PA_LAYOUT_LATENT)
     pl.token_mode = true;   // quantized and latent caches: one kernel serves every token
-  else if (p->path == 2)
+  else if (rt.path == 2)
     pl.token_mode = false;
   else
     pl.token_mode = T <= B;   // static shape test: a heuristic, never a correctness input
@@ -392,8 +407,8 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
   const int64_t cap = (int64_t)kv->max_blocks_per_seq * p->block_size;
   int64_t span = cap;                                   // static key-range extent
   if (p->local_window_size > 0 && p->local_window_size < span) span = p->local_window_size;
-  if (p->split_tokens > 0) {
-    pl.split_tokens = p->split_tokens;
+  if (rt.split_tokens > 0) {
+    pl.split_tokens = rt.split_tokens;
   } else {
     // split length from static shapes only, so results do not depend on the bounds
     const int64_t items = std::max<int64_t>(1, (int64_t)pl.rows * p->kv_num_heads * pl.head_chunks);
@@ -434,7 +449,7 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, int32_t mq, int32
     const int64_t est_items =
         ((int64_t)T * pl.g + pa::kPrefillRows - 1) / pa::kPrefillRows * p->kv_num_heads;
     const bool long_keys = cap >= 4 * pa::kPrefillPieceTiles * 64;
-    pl.prefill_chunks = p->prefill_pieces > 0 ? p->prefill_pieces
+    pl.prefill_chunks = rt.prefill_pieces > 0 ? rt.prefill_pieces
                         : est_items < pa::kPrefillSplitItems && long_keys ? pa::kPrefillChunks
                                                                           : 1;
     if (pl.prefill_chunks > 1) {
@@ -581,29 +596,47 @@ pa_status pa_append_kv(const pa_attn_params* params, const pa_paged_kv* kv, cons
   return device_status(pa::launch_append(a, s), "append kernel launch");
 }
 
-pa_status pa_forward_workspace_bytes(const pa_attn_params* params, const pa_paged_kv* kv,
-                                     int32_t mq, int32_t mk, size_t* bytes) {
+static pa_status workspace_bytes_impl(const pa_attn_params* params, const pa_paged_kv* kv,
+                                      const pa_routing* routing, int32_t mq, int32_t mk,
+                                      size_t* bytes) {
   g_error.clear();
   if (!bytes) return fail(PA_ERR_INVALID_ARGUMENT, "bytes: expected non-NULL");
   *bytes = 0;
   pa_status st = check_common(params, kv);
   if (st != PA_OK) return st;
+  if (!routing) return fail(PA_ERR_INVALID_ARGUMENT, "routing: expected non-NULL");
+  if ((st = check_routing(routing)) != PA_OK) return st;
   if (mq < 0 || mk < 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "max_query_len_bound/max_kv_len_bound: expected >= 0");
   if (kv->token_count == 0) return PA_OK;
-  const Plan pl = make_plan(params, kv, mq, mk);
+  const Plan pl = make_plan(params, kv, *routing, mq, mk);
   if ((st = check_plan(pl)) != PA_OK) return st;
   *bytes = pl.ws_bytes;
   return PA_OK;
 }
 
-pa_status pa_describe_plan(const pa_attn_params* params, const pa_paged_kv* kv, int32_t mq,
-                           int32_t mk, char* buf, size_t len) {
+pa_status pa_forward_workspace_bytes(const pa_attn_params* params, const pa_paged_kv* kv,
+                                     int32_t mq, int32_t mk, size_t* bytes) {
+  const pa_routing rt = auto_routing();
+  return workspace_bytes_impl(params, kv, &rt, mq, mk, bytes);
+}
+
+pa_status pa_forward_workspace_bytes_routed(const pa_attn_params* params, const pa_paged_kv* kv,
+                                            const pa_routing* routing, int32_t mq, int32_t mk,
+                                            size_t* bytes) {
+  return workspace_bytes_impl(params, kv, routing, mq, mk, bytes);
+}
+
+pa_status pa_describe_plan(const pa_attn_params* params, const pa_paged_kv* kv,
+                           const pa_routing* routing, int32_t mq, int32_t mk, char* buf,
+                           size_t len) {
   g_error.clear();
   pa_status st = check_common(params, kv);
   if (st != PA_OK) return st;
+  const pa_routing rt = routing ? *routing : auto_routing();
+  if ((st = check_routing(&rt)) != PA_OK) return st;
   if (!buf || len == 0) return fail(PA_ERR_INVALID_ARGUMENT, "buf: expected non-NULL, len > 0");
-  const Plan pl = make_plan(params, kv, mq, mk);
+  const Plan pl = make_plan(params, kv, rt, mq, mk);
   snprintf(buf, len,
            "mode=%s cache=%s rows=%d head_chunks=%d g=%d chunk_heads=%d split_tokens=%d "
            "max_splits=%d listed=%d prefill_grid=(%d,%d) prefill_chunks=%d q_norm=%d "
@@ -619,25 +652,29 @@ pa_status pa_describe_plan(const pa_attn_params* params, const pa_paged_kv* kv, 
   return PA_OK;
 }
 
-pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const void* query,
-                     const void* cos_cache, const void* sin_cache, int32_t rotary_rows,
-                     int32_t rotary_dim, int32_t mq, int32_t mk, void* workspace,
-                     size_t workspace_bytes, void* out, void* stream) {
+static pa_status forward_impl(const pa_attn_params* params, const pa_paged_kv* kv,
+                               const pa_routing* routing, const void* query,
+                               const void* cos_cache, const void* sin_cache, int32_t rotary_rows,
+                               int32_t rotary_dim, int32_t mq, int32_t mk, void* workspace,
+                               size_t workspace_bytes, void* out, void* stream) {
   g_error.clear();
   pa_status st = check_common(params, kv);
   if (st != PA_OK) return st;
+  if (!routing) return fail(PA_ERR_INVALID_ARGUMENT, "routing: expected non-NULL");
+  if ((st = check_routing(routing)) != PA_OK) return st;
+  const pa_routing& rt = *routing;
   if ((st = check_rotary(params, kv, cos_cache, sin_cache, rotary_rows, rotary_dim)) != PA_OK)
     return st;
   if (mq < 0 || mk < 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "max_query_len_bound/max_kv_len_bound: expected >= 0");
   if (kv->token_count == 0) return PA_OK;
-  if ((st = check_kernel_support(params, kv)) != PA_OK) return st;
+  if ((st = check_kernel_support(params, kv, rt)) != PA_OK) return st;
   if ((st = check_norm_support(params)) != PA_OK) return st;
   if (!query) return fail(PA_ERR_INVALID_ARGUMENT, "query: expected non-NULL");
   if (!out) return fail(PA_ERR_INVALID_ARGUMENT, "out: expected non-NULL");
   if (!aligned16(query) || !aligned16(out))
     return fail(PA_ERR_INVALID_ARGUMENT, "query/out: expected 16-byte alignment");
-  const Plan pl = make_plan(params, kv, mq, mk);
+  const Plan pl = make_plan(params, kv, rt, mq, mk);
   if ((st = check_plan(pl)) != PA_OK) return st;
   if (workspace_bytes < pl.ws_bytes)
     return fail(PA_ERR_INVALID_ARGUMENT, "workspace_bytes: expected >= %zu, got %zu",
@@ -767,15 +804,15 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     f.rotary_rows = d.rotary_rows;
     f.tiles = pl.prefill_tiles;
     f.chunks = pl.prefill_chunks;
-    f.piece_tiles = params->prefill_pieces > 0 ? 0 : pa::kPrefillPieceTiles;
+    f.piece_tiles = rt.prefill_pieces > 0 ? 0 : pa::kPrefillPieceTiles;
     f.part_o = pl.prefill_chunks > 1 ? reinterpret_cast<float*>(ws + pl.off_pf_o) : nullptr;
     f.part_ml = pl.prefill_chunks > 1 ? reinterpret_cast<float*>(ws + pl.off_pf_ml) : nullptr;
     f.score_scale = d.score_scale;
     f.cap_in2 = 2.0f * log2e * d.cap_in;
     f.cap_out = d.cap_out;
     f.use_softcap = d.use_softcap;
-    f.rows16 = params->prefill_kernel == 2 ||
-               (params->prefill_kernel == 0 && rows16_prefill_fits(params, kv));
+    f.rows16 = rt.prefill_kernel == 2 ||
+               (rt.prefill_kernel == 0 && rows16_prefill_fits(params, kv));
     f.pool32 = pool_fits_32bit(params, kv) ? 1 : 0;
     f.head_sink = d.head_sink;
     f.use_sink = d.use_sink;
@@ -843,6 +880,37 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
     }
   }
   return joined(PA_OK);
+}
+
+pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const void* query,
+                     const void* cos_cache, const void* sin_cache, int32_t rotary_rows,
+                     int32_t rotary_dim, int32_t mq, int32_t mk, void* workspace,
+                     size_t workspace_bytes, void* out, void* stream) {
+  const pa_routing rt = auto_routing();
+  return forward_impl(params, kv, &rt, query, cos_cache, sin_cache, rotary_rows, rotary_dim, mq,
+                      mk, workspace, workspace_bytes, out, stream);
+}
+
+pa_status pa_forward_routed(const pa_attn_params* params, const pa_paged_kv* kv,
+                            const pa_routing* routing, const void* query,
+                            const void* cos_cache, const void* sin_cache, int32_t rotary_rows,
+                            int32_t rotary_dim, int32_t mq, int32_t mk, void* workspace,
+                            size_t workspace_bytes, void* out, void* stream) {
+  return forward_impl(params, kv, routing, query, cos_cache, sin_cache, rotary_rows, rotary_dim,
+                      mq, mk, workspace, workspace_bytes, out, stream);
+}
+
+pa_status pa_bench_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  g_error.clear();
+  if (!src || !sink) return fail(PA_ERR_INVALID_ARGUMENT, "src/sink: expected non-NULL");
+  // whole 16 KB blocks: every lane's loads then stay inside the buffer
+  if (bytes % 16384 != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "bytes: expected a multiple of 16384, got %zu", bytes);
+  if (!aligned16(src)) return fail(PA_ERR_INVALID_ARGUMENT, "src: expected 16-byte alignment");
+  if (bytes == 0) return PA_OK;
+  return device_status(pa::launch_stream_read(src, (int64_t)bytes, sink,
+                                              static_cast<hipStream_t>(stream)),
+                       "stream read launch");
 }
 
 pa_status pa_timing_enable(int32_t max_launches) {

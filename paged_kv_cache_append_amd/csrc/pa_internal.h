@@ -221,6 +221,8 @@ hipError_t launch_prefill16(const PrefillArgs& a, int head_size, dim3 grid, hipS
 // channels of K; every row in token mode, items as for the decode kernel
 hipError_t launch_mla(const DecodeArgs& a, int workgroups, hipStream_t st);
 int mla_workgroups_per_cu(bool softcap);
+// streaming read of `bytes` bytes (a multiple of 16 KB) for benchmarks
+hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t st);
 constexpr int kMlaHeadSize = 576;
 constexpr int kMlaVHeadSize = 512;
 // byte offset of the latent kernel's zero rows (past the pool; a row read

@@ -10,8 +10,22 @@ from paged_kv_cache_append_amd import workloads as wl
 TOL = 2e-3   # max-abs error of fp16 outputs against the fp64 oracle
 
 
+ROUTING_KEYS = ("path", "split_tokens", "prefill_pieces", "prefill_kernel")
+
+
+def split_routing(over):
+    """(attribute overrides, forced Routing or None) from one keyword dict:
+    the routing keys go to ``pa_routing`` (include/pa_testing.h)."""
+    import paged_kv_cache_append_amd as pa
+    over = dict(over)
+    r = {k: over.pop(k) for k in ROUTING_KEYS if k in over}
+    r = {k: v for k, v in r.items() if v}
+    return over, (pa.Routing(**r) if r else None)
+
+
 def attn_for(w, **over):
     import paged_kv_cache_append_amd as pa
+    assert not set(over) & set(ROUTING_KEYS), "routing goes through split_routing"
     a = pa.Attn(num_heads=w.num_heads, kv_num_heads=w.kv_num_heads, head_size=w.head_size,
                 block_size=w.block_size, scale=w.scale, softcap=w.softcap,
                 local_window_size=w.local_window_size, do_rotary=w.do_rotary,
@@ -23,17 +37,18 @@ def attn_for(w, **over):
 
 def gpu_append(w, dev, **over):
     import paged_kv_cache_append_amd as pa
-    a = attn_for(w, **over)
+    a = attn_for(w, **split_routing(over)[0])
     pa.append_kv(a, dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
                  dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"])
 
 
 def gpu_forward(w, dev, mq=0, mk=0, **over):
     import paged_kv_cache_append_amd as pa
+    over, routing = split_routing(over)
     a = attn_for(w, **over)
     return pa.forward(a, dev["query"], dev["key_cache"], dev["value_cache"], dev["block_table"],
                       dev["cum"], dev["past"], dev["cos"], dev["sin"], max_query_len_bound=mq,
-                      max_kv_len_bound=mk)
+                      max_kv_len_bound=mk, routing=routing)
 
 
 def gpu_step(w, dev=None, **over):
@@ -102,6 +117,7 @@ def gpu_quant_step(w, cache_dtype, k_quant, v_quant, ks, vs, slot_mapping=None, 
     dev = wl.to_device(w, cache_dtype=cache_dtype)
     dev["k_scale"] = torch.from_numpy(ks).cuda()
     dev["v_scale"] = torch.from_numpy(vs).cuda()
+    over, routing = split_routing(over)
     a = attn_for(w, cache_dtype=cache_dtype, k_quant_type=k_quant, v_quant_type=v_quant, **over)
     sm = None if slot_mapping is None else torch.from_numpy(slot_mapping).cuda()
     pa.append_kv(a, dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
@@ -109,7 +125,7 @@ def gpu_quant_step(w, cache_dtype, k_quant, v_quant, ks, vs, slot_mapping=None, 
                  slot_mapping=sm, k_scale=dev["k_scale"], v_scale=dev["v_scale"])
     out = pa.forward(a, dev["query"], dev["key_cache"], dev["value_cache"], dev["block_table"],
                      dev["cum"], dev["past"], dev["cos"], dev["sin"], k_scale=dev["k_scale"],
-                     v_scale=dev["v_scale"])
+                     v_scale=dev["v_scale"], routing=routing)
     torch.cuda.synchronize()
     return dev, out.cpu().numpy()
 

@@ -1,5 +1,5 @@
 """C-ABI tests that need no GPU: the library loads, exports every entry point
-declared in include/pa.h, and rejects each malformed request with the status
+declared in include/pa.h and include/pa_testing.h, and rejects each malformed request with the status
 and message the header documents (PagedAttention -- CUDA Design Document,
 section 15: every violation names the offending argument).  No call here
 reaches a HIP runtime function: only validation and host planning run."""
@@ -18,29 +18,33 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
                                 reason="libpa.so not built (run __graft_entry__.build())")
 
 
-def header_functions():
-    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+def header_functions(header="pa.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     return sorted(set(re.findall(r"^\s*(?:pa_status|size_t|const char \*)\s*(pa_\w+)\s*\(",
                                  text, re.M)))
 
 
 def test_header_declares_the_boundary():
-    fns = header_functions()
-    for name in ("pa_append_kv", "pa_forward", "pa_forward_workspace_bytes", "pa_last_error"):
-        assert name in fns
+    assert set(header_functions()) >= {"pa_append_kv", "pa_forward", "pa_forward_workspace_bytes",
+                                       "pa_last_error"}
+    # the op's attributes carry no testing hook
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    for hook in ("path", "split_tokens", "prefill_pieces", "prefill_kernel"):
+        assert not re.search(rf"\b{hook}\s*;", text), hook
 
 
 def test_library_exports_every_declared_function():
     lib = _lib.load()
-    for name in header_functions():
-        assert hasattr(lib, name), name
-    assert set(header_functions()) == set(_lib.EXPORTED)
+    for header, names in (("pa.h", _lib.EXPORTED), ("pa_testing.h", _lib.TESTING_EXPORTED)):
+        for name in header_functions(header):
+            assert hasattr(lib, name), name
+        assert set(header_functions(header)) == set(names), header
 
 
 def params(**kw):
     d = dict(num_heads=8, kv_num_heads=2, head_size=64, block_size=16, scale=0.0, softcap=0.0,
-             local_window_size=-1, do_rotary=0, rotary_interleaved=0, path=0, split_tokens=0,
-             prefill_pieces=0, prefill_kernel=0, cache_dtype=0, k_quant_type=0, v_quant_type=0,
+             local_window_size=-1, do_rotary=0, rotary_interleaved=0, cache_dtype=0,
+             k_quant_type=0, v_quant_type=0,
              head_sink=None, use_smooth_softmax=0, q_norm_weight=None, k_norm_weight=None,
              qk_norm_epsilon=0.0, kv_cache_layout=0, v_head_size=0, rotary_offset=0)
     d.update(kw)
@@ -55,11 +59,20 @@ def paged(**kw):
     return _lib.PagedKV(*[d[f] for f, _ in _lib.PagedKV._fields_])
 
 
+def routing(**kw):
+    d = dict(path=0, split_tokens=0, prefill_pieces=0, prefill_kernel=0)
+    d.update(kw)
+    return _lib.Routing(*[d[f] for f, _ in _lib.Routing._fields_])
+
+
 def call_forward(p, kv, query=FAKE, cos=None, sin=None, rows=0, rdim=0, mq=0, mk=0, ws=None,
-                 ws_len=0, out=FAKE):
+                 ws_len=0, out=FAKE, rt=None):
     lib = _lib.load()
-    return lib.pa_forward(ctypes.byref(p), ctypes.byref(kv), query, cos, sin, rows, rdim, mq, mk,
-                          ws, ws_len, out, None)
+    if rt is None:
+        return lib.pa_forward(ctypes.byref(p), ctypes.byref(kv), query, cos, sin, rows, rdim, mq,
+                              mk, ws, ws_len, out, None)
+    return lib.pa_forward_routed(ctypes.byref(p), ctypes.byref(kv), ctypes.byref(rt), query, cos,
+                                 sin, rows, rdim, mq, mk, ws, ws_len, out, None)
 
 
 def call_append(p, kv, key=FAKE, value=FAKE, cos=None, sin=None, rows=0, rdim=0):
@@ -87,12 +100,6 @@ NEGATIVE = [
     (dict(local_window_size=-2), {}, 1, "local_window_size"),
     (dict(do_rotary=2), {}, 1, "do_rotary"),
     (dict(rotary_interleaved=3), {}, 1, "rotary_interleaved"),
-    (dict(path=3), {}, 1, "path"),
-    (dict(split_tokens=100), {}, 1, "split_tokens"),
-    (dict(prefill_pieces=5), {}, 1, "prefill_pieces"),
-    (dict(prefill_pieces=-1), {}, 1, "prefill_pieces"),
-    (dict(prefill_kernel=3), {}, 1, "prefill_kernel"),
-    (dict(prefill_kernel=-1), {}, 1, "prefill_kernel"),
     ({}, dict(batch_size=0), 1, "batch_size"),
     ({}, dict(token_count=-1), 1, "token_count"),
     ({}, dict(num_blocks=0), 1, "num_blocks"),
@@ -163,6 +170,37 @@ def test_validation_rule(pk, kk, status, frag):
         assert frag in err(), err()
 
 
+ROUTING_NEGATIVE = [
+    (dict(path=3), "path"),
+    (dict(split_tokens=100), "split_tokens"),
+    (dict(prefill_pieces=5), "prefill_pieces"),
+    (dict(prefill_pieces=-1), "prefill_pieces"),
+    (dict(prefill_kernel=3), "prefill_kernel"),
+    (dict(prefill_kernel=-1), "prefill_kernel"),
+]
+
+
+@pytest.mark.parametrize("rk,frag", ROUTING_NEGATIVE)
+def test_routing_validation_rule(rk, frag):
+    lib = _lib.load()
+    assert call_forward(params(), paged(), rt=routing(**rk)) == 1 and frag in err(), err()
+    n = ctypes.c_size_t(0)
+    r = routing(**rk)
+    assert lib.pa_forward_workspace_bytes_routed(ctypes.byref(params()), ctypes.byref(paged()),
+                                                 ctypes.byref(r), 0, 0, ctypes.byref(n)) == 1
+    buf = ctypes.create_string_buffer(64)
+    assert lib.pa_describe_plan(ctypes.byref(params()), ctypes.byref(paged()), ctypes.byref(r),
+                                0, 0, buf, 64) == 1 and frag in err()
+
+
+def test_stream_read_rules():
+    lib = _lib.load()
+    assert lib.pa_bench_stream_read(FAKE, 1000, FAKE, None) == 1 and "16384" in err()
+    assert lib.pa_bench_stream_read(FAKE + 8, 16384, FAKE, None) == 1 and "src" in err()
+    assert lib.pa_bench_stream_read(None, 16384, FAKE, None) == 1
+    assert lib.pa_bench_stream_read(FAKE, 0, FAKE, None) == 0
+
+
 def test_rotary_rules():
     kv = paged()
     p = params(do_rotary=1)
@@ -195,9 +233,10 @@ def test_unsupported_head_size_is_reported():
 
 def test_rows16_prefill_kernel_limits():
     # the 8-wave prefill kernel serves head_size 256 with caches below 4 GiB
-    assert call_forward(params(prefill_kernel=2), paged()) == 2 and "prefill_kernel 2" in err()
+    rt = routing(prefill_kernel=2)
+    assert call_forward(params(), paged(), rt=rt) == 2 and "prefill_kernel 2" in err()
     big = paged(num_blocks=(1 << 32) // (16 * 2 * 256 * 2))   # exactly 4 GiB per cache
-    assert call_forward(params(head_size=256, prefill_kernel=2), big) == 2
+    assert call_forward(params(head_size=256), big, rt=rt) == 2
     assert "4 GiB" in err()
 
 
@@ -210,7 +249,7 @@ def test_quantized_cache_takes_the_decode_kernel():
     assert pl["mode"] == "token" and pl["cache"] == "fp8e4m3fn"
     assert plan(params(), paged())["cache"] == "fp16"
     # path 2 (prefill kernel for multi-token requests) does not serve codes
-    assert call_forward(params(path=2, **QUANT), paged(**QUANT_KV)) == 2
+    assert call_forward(params(**QUANT), paged(**QUANT_KV), rt=routing(path=2)) == 2
     assert "quantized caches" in err()
 
 
@@ -240,7 +279,7 @@ def test_latent_rules():
     # kernel shapes: 576/512 fp16 only; path 2 has no latent kernel
     assert call_forward(params(**dict(LAT, head_size=64, v_head_size=32)), kv) == 2
     assert "LATENT: served for head_size 576" in err()
-    assert call_forward(params(**LAT, path=2), kv) == 2 and "latent kernel" in err()
+    assert call_forward(params(**LAT), kv, rt=routing(path=2)) == 2 and "latent kernel" in err()
     big = paged(value_cache=None, num_blocks=(1 << 32) // (16 * 576 * 2) + 1)
     assert call_forward(params(**LAT), big) == 2 and "4 GiB" in err()
     pl = plan(params(**LAT), paged(token_count=40, batch_size=4, **LAT_KV))
@@ -264,10 +303,11 @@ def test_zero_tokens_is_a_no_op():
     assert call_append(params(), kv, key=None, value=None) == 0
 
 
-def plan(p, kv, mq=0, mk=0):
+def plan(p, kv, mq=0, mk=0, rt=None):
     lib = _lib.load()
     buf = ctypes.create_string_buffer(512)
-    assert lib.pa_describe_plan(ctypes.byref(p), ctypes.byref(kv), mq, mk, buf, 512) == 0, err()
+    r = None if rt is None else ctypes.byref(rt)
+    assert lib.pa_describe_plan(ctypes.byref(p), ctypes.byref(kv), r, mq, mk, buf, 512) == 0, err()
     return dict(kv.split("=", 1) for kv in buf.value.decode().split())
 
 
@@ -277,8 +317,8 @@ def test_plan_static_shape_test():
     assert plan(params(), paged(token_count=4, batch_size=4))["mode"] == "token"
     pl = plan(params(), paged(token_count=40, batch_size=4))
     assert pl["mode"] == "request" and pl["prefill_grid"] != "(0,0)"
-    assert plan(params(path=1), paged(token_count=40, batch_size=4))["mode"] == "token"
-    assert plan(params(path=2), paged(token_count=4, batch_size=4))["mode"] == "request"
+    assert plan(params(), paged(token_count=40, batch_size=4), rt=routing(path=1))["mode"] == "token"
+    assert plan(params(), paged(token_count=4, batch_size=4), rt=routing(path=2))["mode"] == "request"
 
 
 def test_plan_split_length_ignores_bounds():

@@ -1,8 +1,10 @@
 """Parity at the benchmark workloads' full sizes, in the launch configuration
 bench.py times (automatic routing, no bounds).  The append is checked
 bit-exactly on every block that receives a new token and on a random sample
-of untouched blocks; the forward on sampled rows, recomputed one request at a
-time by the fp64 oracle on a compact copy of that request's blocks."""
+of untouched blocks; the forward on sampled rows (32 decode requests, and
+the first and last 64 rows, the tile edges and drawn rows of every prefill
+request), recomputed one request at a time by the fp64 oracle on a compact
+copy of that request's blocks."""
 import numpy as np
 import pytest
 
@@ -24,8 +26,13 @@ def touched_blocks(w):
     return sorted(ids)
 
 
-def sample_plan(w, rng):
-    """(request, rows within it) pairs to recompute with the oracle."""
+def sample_plan(w, rng, n_decode=32, edge_rows=64):
+    """(request, rows within it) pairs to recompute with the oracle: up to
+    ``n_decode`` decode requests (the longest, the shortest and drawn
+    others), and for every prefill request its first and last
+    ``edge_rows`` rows plus 16 drawn rows and the rows at the query-tile
+    edges that fall between (tiles of 128 rows of (token, head) pairs, so
+    128 / g tokens)."""
     ql = w.q_lens
     dec = [b for b in range(w.batch_size) if ql[b] == 1]
     pre = [b for b in range(w.batch_size) if ql[b] > 1]
@@ -33,12 +40,18 @@ def sample_plan(w, rng):
     if dec:
         kv = w.past[dec]
         chosen = {dec[int(np.argmax(kv))], dec[int(np.argmin(kv))]}
-        chosen |= {int(x) for x in rng.choice(dec, size=min(2, len(dec)), replace=False)}
+        others = [b for b in dec if b not in chosen]
+        k = min(max(0, n_decode - len(chosen)), len(others))
+        chosen |= {int(x) for x in rng.choice(others, size=k, replace=False)}
         picks += [(b, None) for b in sorted(chosen)]
-    for b in pre[:2]:
+    g = w.num_heads // w.kv_num_heads
+    tile = max(1, 128 // g)
+    for b in pre:
         n = int(ql[b])
-        rows = sorted({0, 1, n - 1, n - 2} | {int(x) for x in rng.integers(0, n, 12)})
-        picks.append((b, rows))
+        rows = set(range(min(edge_rows, n))) | set(range(max(0, n - edge_rows), n))
+        rows |= {int(x) for x in rng.integers(0, n, 16)}
+        rows |= {r for t in range(tile, n, tile) for r in (t - 1, t) if r < n}
+        picks.append((b, sorted(rows)))
     return picks
 
 

@@ -9,7 +9,7 @@ import pytest
 import oracle
 from paged_kv_cache_append_amd import workloads as wl
 
-from pa_harness import TOL, attn_for, max_err
+from pa_harness import TOL, attn_for, max_err, split_routing
 
 pytestmark = pytest.mark.gpu
 
@@ -34,11 +34,12 @@ def device_inputs(w):
 def gpu_latent(w, dev, **over):
     import torch
     import paged_kv_cache_append_amd as pa
+    over, routing = split_routing(over)
     a = attn_for(w, **LATENT, **over)
     pa.append_kv(a, dev["key"], None, dev["key_cache"], None, dev["block_table"], dev["cum"],
                  dev["past"], dev["cos"], dev["sin"])
     out = pa.forward(a, dev["query"], dev["key_cache"], None, dev["block_table"], dev["cum"],
-                     dev["past"], dev["cos"], dev["sin"])
+                     dev["past"], dev["cos"], dev["sin"], routing=routing)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 

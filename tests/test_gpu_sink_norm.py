@@ -17,7 +17,7 @@ import pytest
 import oracle
 from paged_kv_cache_append_amd import workloads as wl
 
-from pa_harness import TOL, attn_for, max_err, rot_kw
+from pa_harness import TOL, attn_for, max_err, rot_kw, split_routing
 
 pytestmark = pytest.mark.gpu
 
@@ -54,11 +54,12 @@ def run(w, e, path=0, quant=None, **over):
         sc = dict(k_scale=torch.from_numpy(ks).cuda(), v_scale=torch.from_numpy(vs).cuda())
         qkw = dict(cache_dtype=cd, k_quant_type=kq, v_quant_type=vq, k_scale=ks, v_scale=vs)
         over = dict(over, cache_dtype=cd, k_quant_type=kq, v_quant_type=vq)
-    a = attn_for(w, path=path, **t, **over)
+    over, routing = split_routing(dict(over, path=path))
+    a = attn_for(w, **t, **over)
     pa.append_kv(a, dev["key"], dev["value"], dev["key_cache"], dev["value_cache"],
                  dev["block_table"], dev["cum"], dev["past"], dev["cos"], dev["sin"], **sc)
     out = pa.forward(a, dev["query"], dev["key_cache"], dev["value_cache"], dev["block_table"],
-                     dev["cum"], dev["past"], dev["cos"], dev["sin"], **sc)
+                     dev["cum"], dev["past"], dev["cos"], dev["sin"], routing=routing, **sc)
     torch.cuda.synchronize()
     out = out.cpu().numpy()
     if quant:
