@@ -239,6 +239,31 @@ pa_status pa_forward(const pa_attn_params *params, const pa_paged_kv *kv,
                      void *workspace, size_t workspace_bytes,
                      void *out, void *stream);
 
+/*
+ * pa_forward_noalloc -- pa_forward with the library's own workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, semantics and errors as pa_forward without the workspace
+ * pair; the caller still owns query, out and the cache.  The workspace is a
+ * file-scope device array of PA_NOALLOC_SCRATCH_BYTES (128 MiB) that every GPU
+ * the library runs on holds until the process ends; the call allocates
+ * nothing (no hipMalloc / hipFree, no stream or event creation: all launches
+ * go on `stream`, one after another).  A plan that needs more than
+ * PA_NOALLOC_SCRATCH_BYTES (pa_forward_workspace_bytes with the same shapes
+ * and bounds) returns PA_ERR_UNSUPPORTED before any device call.  Nothing in
+ * the array needs to start at zero (the plan kernel writes every value a
+ * later kernel reads).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other threads) race.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (128u << 20)
+pa_status pa_forward_noalloc(const pa_attn_params *params, const pa_paged_kv *kv,
+                             const void *query,
+                             const void *cos_cache, const void *sin_cache,
+                             int32_t rotary_rows, int32_t rotary_dim,
+                             int32_t max_query_len_bound, int32_t max_kv_len_bound,
+                             void *out, void *stream);
+
 /* Thread-local text of the last error on this thread ("" if none). */
 const char *pa_last_error(void);
 

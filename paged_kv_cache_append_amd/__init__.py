@@ -7,7 +7,7 @@ other implementation, and calling it without the built library raises.
 
 Names mirror the C entry points: :func:`append_kv` (``pa_append_kv``),
 :func:`forward` (``pa_forward``), :func:`forward_workspace_bytes`,
-:func:`last_error`; and, from ``include/pa_testing.h``, :class:`Routing`
+:func:`forward_noalloc` (``pa_forward_noalloc``), :func:`last_error`; and, from ``include/pa_testing.h``, :class:`Routing`
 (``pa_routing``, taken by :func:`forward`, :func:`forward_workspace_bytes` and
 :func:`describe_plan`), the ``timing_*`` helpers and :func:`stream_read`.
 """
@@ -20,7 +20,7 @@ from typing import Any, Optional
 from . import _lib
 
 __all__ = ["PAError", "Attn", "Routing", "CACHE_FP16", "CACHE_INT8", "CACHE_FP8_E4M3FN", "LAYOUT_SEPARATE",
-           "LAYOUT_LATENT", "QUANT_NONE",
+           "LAYOUT_LATENT", "QUANT_NONE", "forward_noalloc",
            "QUANT_PER_TENSOR", "QUANT_PER_CHANNEL", "append_kv", "forward", "forward_workspace_bytes",
            "describe_plan", "last_error", "timing_enable", "timing_disable", "timing_read",
            "stream_read", "library_path"]
@@ -275,6 +275,32 @@ def forward(attn: Attn, query, key_cache, value_cache, block_table, cum, past, c
                                      query.data_ptr(), c, s, rows, rd, max_query_len_bound,
                                      max_kv_len_bound, ws_ptr, ws_len, out.data_ptr(),
                                      _stream(stream)))
+    return out
+
+
+def forward_noalloc(attn: Attn, query, key_cache, value_cache, block_table, cum, past,
+                    cos_cache=None, sin_cache=None, max_query_len_bound: int = 0,
+                    max_kv_len_bound: int = 0, out=None, stream=None, k_scale=None,
+                    v_scale=None):
+    """``pa_forward_noalloc``: :func:`forward` on the library's own scratch
+    array (no workspace argument; the library allocates nothing).  ``out``
+    must be given by callers that allocate nothing themselves."""
+    import torch
+    T = query.shape[0]
+    HD = attn.num_heads * attn.head_size
+    HO = attn.num_heads * attn.out_head_size
+    _need(query, "query", torch.float16, (T, HD))
+    lib = _lib.load()
+    p = attn.c()
+    kv = _kv(attn, key_cache, value_cache, block_table, cum, past, T, k_scale=k_scale,
+             v_scale=v_scale)
+    if out is None:
+        out = torch.empty((T, HO), dtype=torch.float16, device=query.device)
+    _need(out, "out", torch.float16, (T, HO))
+    c, s, rows, rd = _rot(attn, cos_cache, sin_cache)
+    _check(lib.pa_forward_noalloc(ctypes.byref(p), ctypes.byref(kv), query.data_ptr(), c, s, rows,
+                                  rd, max_query_len_bound, max_kv_len_bound, out.data_ptr(),
+                                  _stream(stream)))
     return out
 
 

@@ -17,7 +17,9 @@ STAGES = {"append": 0, "decode": 1, "merge": 2, "prefill": 3, "plan": 4, "prefil
           "q_norm": 6}
 
 # entry points of include/pa.h, and of include/pa_testing.h
-EXPORTED = ("pa_append_kv", "pa_forward_workspace_bytes", "pa_forward", "pa_last_error")
+EXPORTED = ("pa_append_kv", "pa_forward_workspace_bytes", "pa_forward", "pa_forward_noalloc",
+            "pa_last_error")
+NOALLOC_SCRATCH_BYTES = 128 << 20     # PA_NOALLOC_SCRATCH_BYTES
 TESTING_EXPORTED = ("pa_forward_workspace_bytes_routed", "pa_forward_routed", "pa_describe_plan",
                     "pa_timing_enable", "pa_timing_disable", "pa_timing_read",
                     "pa_bench_stream_read")
@@ -78,6 +80,9 @@ def load() -> ctypes.CDLL:
     lib.pa_forward.argtypes = [P(AttnParams), P(PagedKV), vp, vp, vp, i32, i32, i32, i32, vp,
                                sz, vp, vp]
     lib.pa_forward.restype = ctypes.c_int
+    lib.pa_forward_noalloc.argtypes = [P(AttnParams), P(PagedKV), vp, vp, vp, i32, i32, i32, i32,
+                                       vp, vp]
+    lib.pa_forward_noalloc.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_forward_workspace_bytes_routed.argtypes = [P(AttnParams), P(PagedKV), P(Routing), i32,

@@ -543,6 +543,43 @@ pa_status device_status(hipError_t e, const char* what) {
   return fail(PA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// ---- the workspace of pa_forward_noalloc -------------------------------------
+// A file-scope device array: every GPU the library runs on holds its own copy
+// (PA_NOALLOC_SCRATCH_BYTES) until the process ends.  In host code its name is
+// only a stand-in; the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is passed
+// to kernels.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchAddresses {
+  std::mutex mu;
+  void* ptr[64] = {};
+};
+ScratchAddresses g_scratch;
+
+pa_status scratch_address(hipStream_t s, void** out) {
+  int dev = 0;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_DEVICE, "stream device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(PA_ERR_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch.mu);
+  if (!g_scratch.ptr[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess || (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(PA_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = hipSetDevice(cur);
+    if (e != hipSuccess)
+      return fail(PA_ERR_DEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    if (back != hipSuccess) return fail(PA_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(back));
+    if (!p) return fail(PA_ERR_DEVICE, "hipGetSymbolAddress(scratch): null address");
+    g_scratch.ptr[dev] = p;
+  }
+  *out = g_scratch.ptr[dev];
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -656,7 +693,8 @@ static pa_status forward_impl(const pa_attn_params* params, const pa_paged_kv* k
                                const pa_routing* routing, const void* query,
                                const void* cos_cache, const void* sin_cache, int32_t rotary_rows,
                                int32_t rotary_dim, int32_t mq, int32_t mk, void* workspace,
-                               size_t workspace_bytes, void* out, void* stream) {
+                               size_t workspace_bytes, void* out, void* stream,
+                               bool one_stream = false) {
   g_error.clear();
   pa_status st = check_common(params, kv);
   if (st != PA_OK) return st;
@@ -749,7 +787,9 @@ static pa_status forward_impl(const pa_attn_params* params, const pa_paged_kv* k
 
   // prefill first, on the side stream when decode rows run beside it; the
   // side stream forks before the plan kernel, which only the decode needs
-  const bool overlap = pl.prefill && pl.rows > 0;
+  // (pa_forward_noalloc creates nothing, not even the side stream: its launches
+  // all go on the caller's stream, one after the other)
+  const bool overlap = pl.prefill && pl.rows > 0 && !one_stream;
   hipStream_t ps = s;
   SideStream* side = nullptr;
   if (overlap) {
@@ -889,6 +929,29 @@ pa_status pa_forward(const pa_attn_params* params, const pa_paged_kv* kv, const 
   const pa_routing rt = auto_routing();
   return forward_impl(params, kv, &rt, query, cos_cache, sin_cache, rotary_rows, rotary_dim, mq,
                       mk, workspace, workspace_bytes, out, stream);
+}
+
+pa_status pa_forward_noalloc(const pa_attn_params* params, const pa_paged_kv* kv,
+                             const void* query, const void* cos_cache, const void* sin_cache,
+                             int32_t rotary_rows, int32_t rotary_dim, int32_t mq, int32_t mk,
+                             void* out, void* stream) {
+  // validation and the plan first: an oversized plan is rejected before any
+  // device call
+  const pa_routing rt = auto_routing();
+  size_t need = 0;
+  pa_status st = workspace_bytes_impl(params, kv, &rt, mq, mk, &need);
+  if (st != PA_OK) return st;
+  if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_ERR_UNSUPPORTED,
+                "pa_forward_noalloc: this plan needs %zu bytes of workspace, more than the "
+                "%zu-byte scratch array (use pa_forward with a caller workspace)",
+                need, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (kv->token_count > 0) {
+    if ((st = scratch_address(static_cast<hipStream_t>(stream), &ws)) != PA_OK) return st;
+  }
+  return forward_impl(params, kv, &rt, query, cos_cache, sin_cache, rotary_rows, rotary_dim, mq,
+                      mk, ws, (size_t)PA_NOALLOC_SCRATCH_BYTES, out, stream, true);
 }
 
 pa_status pa_forward_routed(const pa_attn_params* params, const pa_paged_kv* kv,

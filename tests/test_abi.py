@@ -343,3 +343,19 @@ def test_plan_group_chunks():
     assert pl["chunk_heads"] == "16" and pl["head_chunks"] == "4"
     pl = plan(params(num_heads=40, kv_num_heads=2), paged())      # g = 20: chunks of 10
     assert pl["chunk_heads"] == "10"
+
+
+def test_noalloc_rejects_a_plan_beyond_its_scratch_before_any_device_call():
+    lib = _lib.load()
+    p = params(num_heads=64, kv_num_heads=8, head_size=256)
+    kv = paged(token_count=64, batch_size=64, max_blocks_per_seq=8192, num_blocks=1 << 16)
+    assert int(plan(p, kv)["workspace"]) > _lib.NOALLOC_SCRATCH_BYTES
+    st = lib.pa_forward_noalloc(ctypes.byref(p), ctypes.byref(kv), FAKE, None, None, 0, 0, 0, 0,
+                                FAKE, None)
+    assert st == 2 and "scratch array" in err(), err()
+    # validation runs first, as for pa_forward
+    st = lib.pa_forward_noalloc(ctypes.byref(params(num_heads=0)), ctypes.byref(paged()), FAKE,
+                                None, None, 0, 0, 0, 0, FAKE, None)
+    assert st == 1 and "num_heads" in err()
+    assert lib.pa_forward_noalloc(ctypes.byref(params()), ctypes.byref(paged(token_count=0)),
+                                  None, None, None, 0, 0, 0, 0, None, None) == 0
