@@ -24,14 +24,18 @@ oracle baseline.
 
 Timing protocol, per workload: W untimed warm-up steps, then K steps each
 bracketed by its own event pair on the launch stream, with a 1 GiB scratch
-write (not timed) before every step so that neither the L2s nor the 256 MB
-memory-side cache hold the step's inputs ("cold"; the median and p10/p90 are
-reported), then K back-to-back steps the same way without the scratch write
-(reported under ``warm``), then K cold steps with every launch's dispatch
-timestamped on its stream (the per-kernel durations behind ``roofline``).
-``hbm_ceiling`` is a plain streaming read of a 4 GiB buffer, the practical
-ceiling set beside the 8 TB/s figure.  ``cpu_baseline`` times the fp64
-oracle on a bounded sample of the workload on the host cores.
+write and then a 1 GiB read of another buffer (not timed) before every step:
+neither the L2s nor the 256 MB memory-side cache hold the step's inputs, and
+the caches hold no dirty lines whose write-back the step would pay for
+("cold"; the median and p10/p90 are reported).  Then K steps after the
+scratch write alone ("cold_dirty", which includes that write-back), K
+back-to-back steps without either (``warm``), and K cold steps with every
+launch's dispatch timestamped on its stream (the per-kernel durations behind
+``roofline``).  ``hbm_ceiling`` is a plain streaming read of a 4 GiB buffer,
+the practical ceiling set beside the 8 TB/s figure; ``roofline.ceiling_at_size``
+is the same read over the decode's own byte count under the cold protocol.
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the workload on
+the host cores.
 """
 from __future__ import annotations
 
@@ -302,21 +306,27 @@ def summarize_pmc(paths):
         print(f"{k:90s} {c:28s} {len(v):10d} {sum(v) / len(v):16.1f}")
 
 
-def summarize_mfma(kernel, path, simds=1024, clock_ghz=None):
+def summarize_mfma(kernel, path, simds=1024, xcds=8, clock_ghz=2.4):
     """MFMA utilisation of one kernel from a rocprofv3 counter run holding
     SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs), GRBM_GUI_ACTIVE (GPU
-    cycles while busy) and SQ_INSTS_VALU_MFMA_MOPS_F16 (units of 512 FLOPs):
-    busy / (active * SIMDs), the profiler's MfmaUtil definition, and the
-    FLOPs the matrix cores executed per dispatch."""
+    cycles while busy, which the profiler sums over the XCDs of the chip)
+    and SQ_INSTS_VALU_MFMA_MOPS_F16 (units of 512 FLOPs): busy cycles over
+    (active cycles of one XCD * SIMDs), and the FLOPs the matrix cores
+    executed per dispatch with the rate they imply over the active time."""
     means = {c: v for (k, c), v in _pmc_means(path).items() if kernel in k}
     busy = means.get("SQ_VALU_MFMA_BUSY_CYCLES")
     active = means.get("GRBM_GUI_ACTIVE")
     mops = means.get("SQ_INSTS_VALU_MFMA_MOPS_F16")
     out = {"kernel": kernel, "counters": means}
+    if active:
+        out["active_cycles_per_xcd"] = active / xcds
+        out["active_us_at_clock"] = active / xcds / (clock_ghz * 1e3)
     if busy is not None and active:
-        out["mfma_util"] = busy / (active * simds)
+        out["mfma_util"] = busy / (active / xcds * simds)
     if mops is not None:
         out["mfma_flops_per_dispatch"] = mops * 512.0
+        if active:
+            out["mfma_tflops_over_active"] = mops * 512.0 / (active / xcds / (clock_ghz * 1e9)) / 1e12
     print(json.dumps(out, indent=1))
 
 
@@ -332,15 +342,29 @@ def stats(ms):
 
 
 class Flusher:
-    """Writes FLUSH_BYTES of scratch on the current stream: afterwards the L2s
-    and the memory-side cache hold none of the step's inputs."""
+    """Run before each cold step, outside its timing: writes FLUSH_BYTES of
+    scratch (afterwards neither the L2s nor the 256 MB memory-side cache hold
+    the step's inputs), then, unless ``dirty``, reads FLUSH_BYTES of another
+    buffer, so the caches hold clean unrelated lines: the step then pays for
+    no write-back of the scratch's dirty lines, which a write alone leaves
+    behind (up to the size of the memory-side cache)."""
 
-    def __init__(self, nbytes=FLUSH_BYTES):
+    def __init__(self, nbytes=FLUSH_BYTES, dirty=False):
         import torch
         self.buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+        self.clean = None if dirty else torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+        self.sink = torch.zeros(4, dtype=torch.int32, device="cuda")
         self.n = 0
 
     def __call__(self):
+        import paged_kv_cache_append_amd as pa
+        self.n += 1
+        self.buf.fill_(self.n)
+        if self.clean is not None:
+            pa.stream_read(self.clean, self.sink)
+
+    def dirty(self):
+        """The scratch write alone (caches left holding dirty lines)."""
         self.n += 1
         self.buf.fill_(self.n)
 
@@ -363,7 +387,8 @@ def _reps(step, reps, flush):
 
 
 def measure(step, steps, warmup, flush):
-    """Warm-up, then cold steps (scratch write before each), warm steps (back
+    """Warm-up, then cold steps (scratch write + clean read before each),
+    cold steps after the scratch write alone ("cold_dirty"), warm steps (back
     to back) and cold steps with every kernel's dispatch timestamped.  With
     ``warmup`` None the warm-up runs until at least WARMUP_SECONDS have passed
     (and 10 steps): an idle GPU's clocks take that long to settle."""
@@ -383,12 +408,29 @@ def measure(step, steps, warmup, flush):
             step()
     torch.cuda.synchronize()
     cold = _reps(step, steps, flush)
+    dirty = _reps(step, steps, getattr(flush, "dirty", None))
     warm = _reps(step, steps, None)
     pa.timing_enable(8 * steps + 16)
     _reps(step, steps, flush)
     stages = {s: pa.timing_read(s) for s in STAGES}
     pa.timing_disable()
-    return {"cold": cold, "warm": warm, "stages": stages, "warmup": warmup}
+    return {"cold": cold, "cold_dirty": dirty, "warm": warm, "stages": stages, "warmup": warmup}
+
+
+def stream_ceiling(nbytes, flush, reps=10):
+    """A plain streaming read of ``nbytes`` (rounded up to 16 KiB) under the
+    cold protocol: the practical HBM ceiling for a read of the step's size
+    (ramp-up and drain included)."""
+    import torch
+
+    import paged_kv_cache_append_amd as pa
+    nbytes = max(16384, (nbytes + 16383) // 16384 * 16384)
+    buf = torch.ones(nbytes // 2, dtype=torch.float16, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    pa.stream_read(buf, sink)
+    ms = float(np.median(_reps(lambda: pa.stream_read(buf, sink), reps, flush)))
+    del buf
+    return {"bytes": nbytes, "us": round(ms * 1e3, 2), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def hbm_ceiling(reps=10):
@@ -524,6 +566,10 @@ def run_workload(name, args, flush, ceiling):
                 "algorithmic_bytes_per_launch": dec_bytes, "kernel_us": round(per["decode"], 3)}
         if achieved and ceiling:
             roof["frac_of_ceiling"] = round(achieved / ceiling["gbs"], 4)
+        if achieved and not args.no_flush:
+            at = stream_ceiling(dec_bytes, flush)
+            roof["ceiling_at_size"] = at
+            roof["frac_of_ceiling_at_size"] = round(achieved / at["gbs"], 4)
     else:
         achieved = pf_flops / (per["prefill"] * 1e-6) / 1e12 if per["prefill"] else None
         roof = {"bound": "mfma", "kernel": "prefill", "achieved": achieved,
@@ -555,7 +601,8 @@ def run_workload(name, args, flush, ceiling):
                    "qk_norm": bool(args.qk_norm),
                    "decode_requests": n_dec, "decode_bytes": dec_bytes,
                    "prefill_flops": pf_flops, "plan": plan},
-        "timing": {"cold_ms": cold, "warm_ms": warm, "warmup": m["warmup"],
+        "timing": {"cold_ms": cold, "cold_dirty_ms": stats(m["cold_dirty"]), "warm_ms": warm,
+                   "warmup": m["warmup"],
                    "cold_warm_ratio": round(cold["median"] / warm["median"], 4)},
         "warm": {"value": round(warm_value, 2), "unit": unit, "ms_per_step": warm["median"],
                  "note": "back-to-back steps, caches holding what the previous step left"},
@@ -671,6 +718,10 @@ def run_mla(name, args, flush, ceiling):
                                      else gbs / HBM_PEAK_GBS, 4)}
     if hbm_bound and ceiling:
         roof["frac_of_ceiling"] = round(gbs / ceiling["gbs"], 4)
+    if hbm_bound and not args.no_flush:
+        at = stream_ceiling(nbytes, flush)
+        roof["ceiling_at_size"] = at
+        roof["frac_of_ceiling_at_size"] = round(gbs / at["gbs"], 4)
     kernels = {f"{s}_us": round(v, 3) for s, v in per.items()}
     kernels["mla_kernel_gbs"] = round(gbs, 1)
     kernels["mla_kernel_tflops"] = round(tfs, 2)
@@ -685,7 +736,8 @@ def run_mla(name, args, flush, ceiling):
                    "v_head_size": wl.MLA_V_HEAD_SIZE, "block_size": w.block_size,
                    "kv_cache_layout": "latent", "rotary_offset": wl.MLA_ROTARY_OFFSET,
                    "latent_bytes": nbytes, "flops": flops, "plan": plan},
-        "timing": {"cold_ms": cold, "warm_ms": warm, "warmup": m["warmup"],
+        "timing": {"cold_ms": cold, "cold_dirty_ms": stats(m["cold_dirty"]), "warm_ms": warm,
+                   "warmup": m["warmup"],
                    "cold_warm_ratio": round(cold["median"] / warm["median"], 4)},
         "warm": {"value": round(nbytes / (warm["median"] * 1e-3) / 1e9, 2), "unit": "GB/s",
                  "ms_per_step": warm["median"]},
@@ -799,7 +851,10 @@ def main():
     line.update({k: v for k, v in res.items() if k not in ("value", "unit", "ms_per_step")})
     line["timing"]["protocol"] = (
         "per step: its own event pair on the launch stream; 'cold' steps follow a "
-        f"{FLUSH_BYTES >> 20} MiB scratch write (outside the pair)"
+        f"{FLUSH_BYTES >> 20} MiB scratch write and a {FLUSH_BYTES >> 20} MiB read of a clean "
+        "buffer (outside the pair: the step's inputs are in no cache and the caches hold no "
+        "dirty lines); 'cold_dirty' steps follow the scratch write alone, and so also pay "
+        "for writing back the dirty lines it leaves in the 256 MB memory-side cache"
         if not args.no_flush else "per step: its own event pair; no scratch write (warm)")
     line["hbm_ceiling"] = ceiling
     if pf_name != "none":
