@@ -88,6 +88,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const PlanArgs a) {
         for (int i = 0; i < a.row_width; i += 8)
           store16(a.out + (int64_t)row * a.row_width + i, u32x4{0, 0, 0, 0});
       }
+      a.row_split[row] = RowSplit{n > 0 ? r.t : -1, n};
     }
     int incl = n;
 #pragma unroll
@@ -522,69 +523,89 @@ void decode_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// merge: one workgroup per (row, head) with more than one split.  Threads
-// first run over splits (max, weights exp2(m_s - M), denominator), then over
-// (4-channel group, split group) pairs, and the split groups are summed in LDS.
+// merge: one workgroup per (row, group of heads) of rows with more than one
+// split.  Thread (head, split group sg, 4-channel group dq) folds splits sg,
+// sg + nsg, ... into a running (max, denominator, output) in one pass -- its
+// loads go out eight splits at a time, ahead of the arithmetic -- and the
+// split groups of each head are then combined pairwise in LDS (log2 nsg
+// steps), each step rescaling both sides to the larger max
+// (GroupQueryAttention CPU Implementation Notes, "Flash Decoding": partials
+// weighted by exp(m_c - M)).  The host sizes nsg to the plan's split count
+// and packs several heads into a workgroup when a head needs few threads.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* s_tmp) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float o = __shfl_xor(v, off, 64);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  const int wv = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) s_tmp[wv] = v;
-  __syncthreads();
-  float r = s_tmp[0];
-#pragma unroll
-  for (int i = 1; i < 4; ++i) r = is_max ? fmaxf(r, s_tmp[i]) : r + s_tmp[i];
-  return r;
+constexpr int kMergeBatch = 8;   // splits whose loads one thread issues together
+
+__device__ __forceinline__ void merge_pair(float& M, float& den, f4& acc, float m2, float d2,
+                                           f4 o2) {
+  const float mn = fmaxf(M, m2);
+  const float mu = mn == kNegInf ? 0.f : mn;
+  const float a1 = exp2_fast(M - mu), a2 = exp2_fast(m2 - mu);
+  acc = acc * a1 + o2 * a2;
+  den = den * a1 + d2 * a2;
+  M = mn;
 }
 
-__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
-  __shared__ float s_w[kDecodeMaxSplits];
-  __shared__ f4 s_red[256];
-  __shared__ float s_tmp[4];
-  const int row = blockIdx.x;
-  const int h = blockIdx.y;
+template <int NT>
+__global__ __launch_bounds__(NT) void merge_kernel(const MergeArgs a, const int hpw) {
+  __shared__ f4 s_o[NT];
+  __shared__ float2 s_md[NT];
+  // workgroup id = row * head groups + head group: consecutive ids (one
+  // row's head groups) land on different XCDs, so a long row's merge work
+  // spreads over the chip
+  const int ngroups = (a.num_heads + hpw - 1) / hpw;
+  const int row = blockIdx.x / ngroups;
+  const int hg = blockIdx.x - row * ngroups;
   const int tid = threadIdx.x;
-  RowInfo r;
-  bool orphan;
-  if (!resolve_row(a.s, a.token_mode, row, a.window, a.split_tokens, a.max_splits, r, orphan))
-    return;
-  if (r.nsplit <= 1) return;   // the decode worker wrote this row directly
-  const int n = r.nsplit;
+  const RowSplit rs = a.row_split[row];
+  if (rs.n <= 1) return;   // not a decode row, or the decode worker wrote it directly
+  const int n = rs.n;
   const int D = a.head_size;
-  const int64_t base = ((int64_t)row * a.num_heads + h) * a.max_splits;
-  float M = kNegInf;
-  for (int s = tid; s < n; s += 256) M = fmaxf(M, a.part_ml[2 * (base + s)]);
-  M = block_reduce(M, true, s_tmp);
-  const float mu = M == kNegInf ? 0.f : M;
-  float den = 0.f;
-  for (int s = tid; s < n; s += 256) {
-    const float w = exp2_fast(a.part_ml[2 * (base + s)] - mu);
-    s_w[s] = w;
-    den += w * a.part_ml[2 * (base + s) + 1];
-  }
-  den = block_reduce(den, false, s_tmp);   // (its barriers also publish s_w)
-  den = sink_denominator(den, M, a.use_sink, a.head_sink, h);
-  const int nq = D >> 2;                   // 4-channel groups
-  const int dq = tid % nq;
-  const int sg = tid / nq;
-  const int nsg = 256 / nq;
+  const int nq = D >> 2;          // 4-channel groups (a power of two)
+  const int per = NT / hpw;       // threads per head (a power-of-two multiple of nq)
+  const int h = hg * hpw + tid / per;
+  const int tl = tid % per;
+  const int dq = tl % nq;
+  const int sg = tl / nq;
+  const int nsg = per / nq;
+  const bool active = h < a.num_heads;
+  float M = kNegInf, den = 0.f;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-  const float* po = a.part_o + base * D + 4 * dq;
-  for (int s = sg; s < n; s += nsg) acc += s_w[s] * *reinterpret_cast<const f4*>(po + (int64_t)s * D);
-  s_red[tid] = acc;
-  __syncthreads();
-  if (sg == 0) {
-    for (int g = 1; g < nsg; ++g) acc += s_red[g * nq + dq];
+  if (active) {
+    const int64_t base = ((int64_t)row * a.num_heads + h) * a.max_splits;
+    const float* po = a.part_o + base * D + 4 * dq;
+    const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + base;
+    for (int s0 = sg; s0 < n; s0 += nsg * kMergeBatch) {
+      float2 ml[kMergeBatch];
+      f4 o[kMergeBatch];
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const int s = s0 + i * nsg;
+        ml[i] = s < n ? pml[s] : make_float2(kNegInf, 0.f);
+        o[i] = s < n ? *reinterpret_cast<const f4*>(po + (int64_t)s * D)
+                     : f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) merge_pair(M, den, acc, ml[i].x, ml[i].y, o[i]);
+    }
+  }
+  s_o[tid] = acc;
+  s_md[tid] = make_float2(M, den);
+  for (int half = nsg >> 1; half >= 1; half >>= 1) {
+    __syncthreads();   // reads below touch groups [half, 2 half), writes [0, half)
+    if (sg < half) {
+      const float2 md = s_md[tid + half * nq];
+      merge_pair(M, den, acc, md.x, md.y, s_o[tid + half * nq]);
+      s_o[tid] = acc;
+      s_md[tid] = make_float2(M, den);
+    }
+  }
+  if (active && sg == 0) {
+    den = sink_denominator(den, M, a.use_sink, a.head_sink, h);
     const float inv = den > 0.f ? 1.0f / den : 0.f;
     uint2 w;
     w.x = (uint32_t)f2h(acc[0] * inv) | ((uint32_t)f2h(acc[1] * inv) << 16);
     w.y = (uint32_t)f2h(acc[2] * inv) | ((uint32_t)f2h(acc[3] * inv) << 16);
-    *reinterpret_cast<uint2*>(a.out + (int64_t)r.t * a.num_heads * D + (int64_t)h * D + 4 * dq) = w;
+    *reinterpret_cast<uint2*>(a.out + (int64_t)rs.t * a.num_heads * D + (int64_t)h * D + 4 * dq) = w;
   }
 }
 
@@ -661,7 +682,24 @@ hipError_t launch_decode(const DecodeArgs& a, int head_size, int workgroups, hip
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
-  launch_kernel(merge_kernel, dim3(a.rows, a.num_heads), dim3(256), st, a);
+  const int nq = a.head_size / 4;
+  if (a.head_size % 4 || nq > 256 || (nq & (nq - 1)) || a.num_heads <= 0) return hipErrorInvalidValue;
+  // split groups per head: enough that one batch of loads covers the plan's
+  // splits (at most 1024 threads per head); heads share a workgroup of 256
+  // threads when each needs fewer
+  int nsg = 1;
+  while (nsg * kMergeBatch < a.max_splits && nq * nsg < 1024) nsg *= 2;
+  const int per = nq * nsg;
+  const int nt = per > 256 ? 1024 : 256;
+  int hpw = nt / per;
+  while (hpw > 1 && hpw / 2 >= a.num_heads) hpw /= 2;   // no more heads than there are
+  const int64_t wgs = (int64_t)a.rows * ((a.num_heads + hpw - 1) / hpw);
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs);
+  if (nt == 1024)
+    launch_kernel(merge_kernel<1024>, grid, dim3(1024), st, a, hpw);
+  else
+    launch_kernel(merge_kernel<256>, grid, dim3(256), st, a, hpw);
   return hipGetLastError();
 }
 

@@ -375,7 +375,7 @@ struct Plan {
   int max_splits = 1;
   int prefill_tiles = 0;     // tile slots (grid.x = tiles * prefill_chunks + 1)
   int prefill_chunks = 1;    // key-range pieces per prefill tile
-  size_t off_ml = 0, off_entries = 0, off_count = 0;
+  size_t off_ml = 0, off_entries = 0, off_count = 0, off_rows = 0;
   size_t off_pf_o = 0, off_pf_ml = 0;
   size_t off_qn = 0;         // QK-Norm: normalized queries, fp16 [T, H*D]
   bool q_norm = false;
@@ -433,7 +433,8 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, const pa_routing&
     pl.off_ml = align256(per * effective_v_head_size(p) * sizeof(float));
     pl.off_entries = pl.off_ml + align256(per * 2 * sizeof(float));
     pl.off_count = pl.off_entries + align256((size_t)pl.rows * pl.max_splits * sizeof(pa::DecodeEntry));
-    cur = pl.off_count + 256;
+    pl.off_rows = pl.off_count + 256;
+    cur = pl.off_rows + align256((size_t)pl.rows * sizeof(pa::RowSplit));
   }
   if (pl.prefill) {
     const int64_t mql = mq > 0 ? std::min<int64_t>(mq, T) : T;
@@ -815,6 +816,7 @@ static pa_status forward_impl(const pa_attn_params* params, const pa_paged_kv* k
     pa_.s = sl;
     pa_.entries = reinterpret_cast<pa::DecodeEntry*>(ws + pl.off_entries);
     pa_.entry_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
+    pa_.row_split = reinterpret_cast<pa::RowSplit*>(ws + pl.off_rows);
     pa_.out = d.out;
     pa_.rows = pl.rows;
     pa_.token_mode = d.token_mode;
@@ -901,17 +903,14 @@ static pa_status forward_impl(const pa_attn_params* params, const pa_paged_kv* k
     }
     if (pl.listed) {
       pa::MergeArgs mg;
-      mg.s = sl;
+      mg.row_split = reinterpret_cast<const pa::RowSplit*>(ws + pl.off_rows);
       mg.part_o = d.part_o;
       mg.part_ml = d.part_ml;
       mg.out = d.out;
       mg.rows = pl.rows;
       mg.num_heads = params->num_heads;
       mg.head_size = DV;
-      mg.token_mode = d.token_mode;
-      mg.split_tokens = pl.split_tokens;
       mg.max_splits = pl.max_splits;
-      mg.window = params->local_window_size;
       mg.head_sink = d.head_sink;
       mg.use_sink = d.use_sink;
       StageScope scope(PA_STAGE_MERGE, s);

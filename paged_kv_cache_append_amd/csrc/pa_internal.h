@@ -120,10 +120,17 @@ struct DecodeArgs {
 
 // Plan kernel (one workgroup): lists (row, split) entries of every row with
 // work, and zeroes output rows of tokens owned by no request (token mode).
+// A decode row's output token and split count, as the plan resolved it
+// (n = 0: not a decode row); the merge reads it instead of resolving again.
+struct RowSplit {
+  int32_t t, n;
+};
+
 struct PlanArgs {
   SeqLayout s;
   DecodeEntry* entries;
   int32_t* entry_count;
+  RowSplit* row_split;          // [rows]
   uint16_t* out;
   int32_t rows;
   int32_t token_mode;
@@ -133,19 +140,16 @@ struct PlanArgs {
   int32_t row_width;            // H * D elements of an output row
 };
 
-// Split merge: one wave per (row, head) of rows with more than one split.
+// Split merge: one workgroup per (row, head) of rows with more than one split.
 struct MergeArgs {
-  SeqLayout s;
+  const RowSplit* row_split;    // written by the plan kernel
   const float* part_o;
   const float* part_ml;
   uint16_t* out;
   int32_t rows;
   int32_t num_heads;
   int32_t head_size;
-  int32_t token_mode;
-  int32_t split_tokens;
   int32_t max_splits;
-  int32_t window;
   const uint16_t* head_sink;    // as in DecodeArgs
   int32_t use_sink;
 };
