@@ -435,19 +435,24 @@ def stream_ceiling(nbytes, flush, reps=10):
 
 def hbm_ceiling(reps=10):
     """Streaming read of a CEILING_BYTES buffer (larger than every cache):
-    median GB/s over ``reps`` back-to-back reads."""
+    median GB/s over ``reps`` back-to-back reads, after WARMUP_SECONDS of
+    reads (an idle GPU's clocks take that long to settle)."""
     import torch
 
     import paged_kv_cache_append_amd as pa
     buf = torch.ones(CEILING_BYTES // 2, dtype=torch.float16, device="cuda")
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
-    pa.stream_read(buf, sink)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < WARMUP_SECONDS:
+        for _ in range(10):
+            pa.stream_read(buf, sink)
+        torch.cuda.synchronize()
     ms = _reps(lambda: pa.stream_read(buf, sink), reps, None)
     del buf
     gbs = CEILING_BYTES / (float(np.median(ms)) * 1e-3) / 1e9
     return {"gbs": round(gbs, 1), "bytes": CEILING_BYTES, "frac_of_spec": round(gbs / HBM_PEAK_GBS, 4),
-            "protocol": f"pa_bench_stream_read of a 4 GiB buffer, median of {reps} back-to-back "
-                        "reads, each between its own event pair"}
+            "protocol": f"pa_bench_stream_read of a 4 GiB buffer after {WARMUP_SECONDS} s of reads, "
+                        f"median of {reps} back-to-back reads, each between its own event pair"}
 
 
 # ---------------------------------------------------------------------------
