@@ -117,8 +117,11 @@ enum { PA_LAYOUT_SEPARATE = 0, PA_LAYOUT_LATENT = 1 };
  * [-128, 127], e4m3fn to +-448 (section 8.4, write path).  pa_forward
  * dequantizes in the kernel (section 8.5, phase 3): a PER_TENSOR K scale is
  * folded into the score scale, a PER_CHANNEL one into Q (rounded to fp16), and
- * the V scale is applied to the output accumulator.  Every token of a
- * quantized forward runs on the decode kernel.  Validation (section 8.7): a quantized cache_dtype
+ * the V scale is applied to the output accumulator.  Decode rows read the
+ * codes in the decode kernel; multi-token requests in the 4-wave prefill
+ * kernel, which turns each lane's codes into fp16 on their way into LDS.
+ * Scales are positive finite values (they are device data and not checked).
+ * Validation (section 8.7): a quantized cache_dtype
  * needs both quant types non-NONE, fp16 needs both NONE; a quant type other
  * than NONE needs its scale and NONE forbids it. */
 enum { PA_CACHE_FP16 = 0, PA_CACHE_INT8 = 1, PA_CACHE_FP8_E4M3FN = 2 };

@@ -21,7 +21,7 @@ typedef struct {
   int32_t path;           /* 0 = auto (token_count <= batch_size -> decode kernel only,
                              else decode + prefill kernels); 1 = decode kernel for every
                              token; 2 = decode kernel for q_len == 1 requests, prefill
-                             kernel for the rest (fp16 SEPARATE caches only, else
+                             kernel for the rest (SEPARATE caches only, else
                              PA_ERR_UNSUPPORTED)                                        */
   int32_t split_tokens;   /* 0 = auto; else the decode KV split length in tokens, a
                              multiple of 64                                             */
@@ -29,7 +29,7 @@ typedef struct {
                              key range, merged on the device                            */
   int32_t prefill_kernel; /* 0 = auto; 1 = 4-wave prefill kernel (32 query rows per
                              wave); 2 = 8-wave kernel (16 rows per wave), head_size 256
-                             with each cache smaller than 4 GiB, else
+                             with fp16 caches each smaller than 4 GiB, else
                              PA_ERR_UNSUPPORTED                                         */
 } pa_routing;
 

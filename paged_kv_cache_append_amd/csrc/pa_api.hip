@@ -323,10 +323,10 @@ bool pool_fits_32bit(const pa_attn_params* p, const pa_paged_kv* kv) {
   return kv->num_blocks * p->block_size * p->kv_num_heads * p->head_size * 2 <
          ((int64_t)1 << 32) - 16;
 }
-// The 8-wave prefill kernel serves head_size 256 and addresses the caches
-// with 32-bit byte offsets.
+// The 8-wave prefill kernel serves head_size 256 over fp16 caches and
+// addresses them with 32-bit byte offsets.
 bool rows16_prefill_fits(const pa_attn_params* p, const pa_paged_kv* kv) {
-  return p->head_size == 256 && pool_fits_32bit(p, kv);
+  return p->head_size == 256 && p->cache_dtype == PA_CACHE_FP16 && pool_fits_32bit(p, kv);
 }
 
 pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv,
@@ -352,10 +352,8 @@ pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv,
                 "head_size %d: the kernels serve head_size 64, 128 and 256", p->head_size);
   if (rt.prefill_kernel == 2 && !rows16_prefill_fits(p, kv))
     return fail(PA_ERR_UNSUPPORTED,
-                "prefill_kernel 2: expected head_size 256 and caches smaller than 4 GiB");
-  if (p->cache_dtype != PA_CACHE_FP16 && rt.path == 2)
-    return fail(PA_ERR_UNSUPPORTED,
-                "path 2: quantized caches are served by the decode kernel only (path 0 or 1)");
+                "prefill_kernel 2: expected head_size 256, an fp16 cache and caches smaller "
+                "than 4 GiB");
   return PA_OK;
 }
 
@@ -395,8 +393,8 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, const pa_routing&
       break;
     }
   pl.head_chunks = pl.g / pl.chunk_heads;
-  if (rt.path == 1 || p->cache_dtype != PA_CACHE_FP16 || p->kv_cache_layout == PA_LAYOUT_LATENT)
-    pl.token_mode = true;   // quantized and latent caches: one kernel serves every token
+  if (rt.path == 1 || p->kv_cache_layout == PA_LAYOUT_LATENT)
+    pl.token_mode = true;   // latent caches: one kernel serves every token
   else if (rt.path == 2)
     pl.token_mode = false;
   else
@@ -859,6 +857,11 @@ static pa_status forward_impl(const pa_attn_params* params, const pa_paged_kv* k
     f.head_sink = d.head_sink;
     f.use_sink = d.use_sink;
     f.rotary_offset = d.rotary_offset;
+    f.cache_dtype = d.cache_dtype;
+    f.k_quant = d.k_quant;
+    f.v_quant = d.v_quant;
+    f.k_scale = d.k_scale;
+    f.v_scale = d.v_scale;
     const dim3 grid(pl.prefill_tiles * pl.prefill_chunks + 1, params->kv_num_heads);
     {
       StageScope scope(PA_STAGE_PREFILL, ps);

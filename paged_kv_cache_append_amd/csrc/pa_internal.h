@@ -187,6 +187,10 @@ struct PrefillArgs {
   const uint16_t* head_sink;    // as in DecodeArgs
   int32_t use_sink;
   int32_t rotary_offset;
+  int32_t cache_dtype;          // kCache*: with codes key_cache/value_cache are byte arrays
+  int32_t k_quant, v_quant;     // kQuant*
+  const float* k_scale;         // [1] or [Hkv, D]
+  const float* v_scale;
 };
 
 // Kernel start/stop events of the launch being made on this thread (set by

@@ -29,6 +29,15 @@
 // units; the running max is shared by the two lanes of a row with one lane
 // swap per tile and is only raised when a tile exceeds it by more than 8
 // (lazy rescale).
+//
+// Quantized pools (PagedAttention -- CUDA Design Document, section 8.5,
+// phase 3, here for multi-token requests too): each lane loads its eight
+// codes of a key row into a register instead of the direct load, and writes
+// them as eight fp16 values (int8 and e4m3fn values are exact in fp16) into
+// the same LDS slot once the step's matrix work is done; the buffers written
+// are the ones no wave reads during the step, as with the direct loads.  A
+// per-tensor K scale joins the score scale, a per-channel one multiplies Q
+// (then rounded to fp16); the V scale multiplies the output accumulator.
 #include <type_traits>
 
 #include "prefill_common.h"
@@ -60,7 +69,10 @@ struct PrefillCfg {
 // offsets (each cache smaller than 4 GiB), otherwise by global loads with an
 // LDS destination.  The buffer form leaves the compiler free to wait on
 // individual LDS operand reads; with the global form it waits on all of them.
-template <int D, bool SOFTCAP, bool BUF>
+//
+// CT: element type of the pools (kCacheF16, or int8 / e4m3fn codes, which
+// take the register path above; BUF is then unused).
+template <int D, bool SOFTCAP, bool BUF, int CT>
 __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   using C = PrefillCfg<D>;
   __shared__ __attribute__((aligned(1024))) char K0[C::SLOTS * C::KSLOT];
@@ -126,6 +138,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nrec, 0x00020000);
   const __amdgpu_buffer_rsrc_t vsrd =
       __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nrec, 0x00020000);
+  // quantized pools: byte arrays of codes, one byte per element
+  constexpr bool kCodes = CT != kCacheF16;
+  const char* kcode = reinterpret_cast<const char*>(a.key_cache) + (int64_t)kvh * D;
+  const char* vcode = reinterpret_cast<const char*>(a.value_cache) + (int64_t)kvh * D;
+  // a per-tensor K scale joins the score scale (and the softcap's input
+  // scale); a per-channel one is folded into Q below
+  float score_scale = a.score_scale, cap_in2 = a.cap_in2;
+  bool k_per_channel = false;
+  if constexpr (kCodes) {
+    if (a.k_quant == kQuantChannel) {
+      k_per_channel = true;
+    } else {
+      const float ks = a.k_scale[0];
+      score_scale *= ks;
+      cap_in2 *= ks;
+    }
+  }
 
   // this lane's query row
   const int R = tile * C::ROWS + wave * 32 + l32;
@@ -157,11 +186,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
       const uint16_t* qrow = a.query + (int64_t)t * HD + (int64_t)head * D;
       const int c = 2 * ks + hf;
       v = load16(qrow + 8 * c);
-      if (chunk_rotated(c, a.rotary_offset, a.rotary_dim)) {
-        const int off = a.rotary_offset;
+      const bool rot = chunk_rotated(c, a.rotary_offset, a.rotary_dim);
+      if (rot || k_per_channel) {
+        const int off = rot ? a.rotary_offset : 0;
         float rr[8];
-        rotate_chunk(qrow + off, v, c - off / 8, pos, a.cos, a.sin, a.rotary_dim,
+        rotate_chunk(qrow + off, v, c - off / 8, pos, a.cos, a.sin, rot ? a.rotary_dim : 0,
                      a.rotary_interleaved, a.rotary_rows, rr);
+        if (k_per_channel) {
+          float ks[8];
+          channel_scales(a.k_scale, kQuantChannel, kvh, D, 8 * c, ks);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rr[e] *= ks[e];
+        }
         v = pack8(rr);
       }
     }
@@ -241,9 +277,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   };
   const int chunk = lane % C::CH;
   const uint16_t* zrow = g_zero_row + 8 * chunk;
+  // quantized pools: this lane's eight codes of a key row (a zero row reads
+  // the zero block: code 0 is +0 in both code types), and their fp16 values
+  // written into the lane's 16 bytes of an LDS slot
+  auto load_codes = [&](uint32_t row, const char* base) -> u32x2 {
+    const int64_t off = row != ~0u ? (int64_t)row * tok_stride + 8 * chunk
+                                   : reinterpret_cast<const char*>(g_zero_row) - base;
+    return *reinterpret_cast<const u32x2*>(base + off);
+  };
+  auto put_codes = [&](u32x2 c, char* buf, int slot_bytes, int mi) {
+    const int slot = wave + 4 * mi;
+    *reinterpret_cast<u32x4*>(buf + slot * slot_bytes + 16 * lane) = codes_to_f16<CT>(c);
+  };
   auto issue_row = [&](uint32_t row, const uint16_t* base, char* buf, int slot_bytes, int mi) {
     const int slot = wave + 4 * mi;
-    if constexpr (BUF) {
+    if constexpr (kCodes) {
+      put_codes(load_codes(row, base == vbase ? vcode : kcode), buf, slot_bytes, mi);
+    } else if constexpr (BUF) {
       // a zero row: an offset past the buffer's end reads zeros
       const uint32_t off = row != ~0u ? (row * tok_stride32 + 8 * chunk) * 2 : 0xFFFFFFF0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -315,9 +365,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   // with tanh(y) = 1 - 2 / (exp(2y) + 1) (exact limits +-1 for large |y|).
   auto logit = [&](float x) {
     if constexpr (SOFTCAP)
-      return a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * a.cap_in2) + 1.0f));
+      return a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * cap_in2) + 1.0f));
     else
-      return x * a.score_scale;
+      return x * score_scale;
   };
   // A row's tile maximum in log2 units (scale and softcap are monotone, so
   // the maximum is taken on raw scores); the row's two lanes agree.
@@ -383,11 +433,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
         // cap * tanh(y) - mu = (cap - mu) - 2 cap / (2^t + 1), t = 2y log2(e);
         // a masked score (t = -inf) gets -inf through t * 2^-120, which is
         // negligible for any finite t
-        const float t = x * a.cap_in2;
+        const float t = x * cap_in2;
         const float r = __builtin_amdgcn_rcpf(exp2_fast(t) + 1.0f);
         e = __builtin_fmaf(t, 0x1p-120f, __builtin_fmaf(r, -2.0f * a.cap_out, a.cap_out - mu));
       } else {
-        e = __builtin_fmaf(x, a.score_scale, -mu);
+        e = __builtin_fmaf(x, score_scale, -mu);
       }
       const float p = exp2_fast(e);
       part[r & 3] += p;
@@ -463,6 +513,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     // the vector work stays between the matrix instructions. ----
     h8 pf[4];
     float part[4] = {0.f, 0.f, 0.f, 0.f};
+    u32x2 codes[kCodes ? C::KS : 1];   // quantized pools: this step's loads, written at its end
     {
       // load j of the step: tile it + 1's V (j < DMA), then tile it + 2's K;
       // its table lookup is issued one k-step before the load
@@ -495,7 +546,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
         }
         const uint32_t row = row_next;
         if (ks + 1 < C::KS) row_next = row_j(ks + 1);
-        if (ks < C::DMA)
+        if constexpr (kCodes)
+          codes[ks] = load_codes(row, ks < C::DMA ? vcode : kcode);
+        else if (ks < C::DMA)
           issue_row(row, vbase, vbuf(NB{}), C::VSLOT, ks);
         else
           issue_row(row, kbase, kbuf(B), C::KSLOT, ks - C::DMA);
@@ -555,6 +608,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
       pos_mask(s_next, kt_of(it + 1));
       mx_next = tile_max(s_next);
     }
+    if constexpr (kCodes) {
+      // tile it + 1's V into buffer 1 - B and tile it + 2's K into buffer B:
+      // neither is read by any wave during this step
+#pragma unroll
+      for (int j = 0; j < C::KS; ++j) {
+        if (j < C::DMA)
+          put_codes(codes[j], vbuf(NB{}), C::VSLOT, j);
+        else
+          put_codes(codes[j], kbuf(B), C::KSLOT, j - C::DMA);
+      }
+    }
     wait_vmem();        // this wave's loads have landed
     __syncthreads();    // ... and everyone's; buffers B (V) and 1 - B (K) are free
   };
@@ -565,6 +629,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   }
 
   const float lt = xor32_sum(lsum);
+  if constexpr (kCodes) {
+    // the V scale of channels db * 32 + 8 q4 + 4 hf + (0..3): output = scale * sum p code
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * hf;
+        const f4 vs = a.v_quant == kQuantChannel
+                          ? *reinterpret_cast<const f4*>(a.v_scale + (int64_t)kvh * D + d0)
+                          : f4{a.v_scale[0], a.v_scale[0], a.v_scale[0], a.v_scale[0]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[db][4 * q4 + e] *= vs[e];
+      }
+  }
   if (pieces > 1) {
     // ---- one piece of several: store (m, l, unnormalised O) ----
     const int64_t pr = ((int64_t)t * a.num_heads + head) * a.chunks;
@@ -662,19 +740,30 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a)
   }
 }
 
-template <int D, bool BUF>
+template <int D, bool BUF, int CT>
 void launch_variant(const PrefillArgs& a, dim3 grid, hipStream_t st) {
   if (a.use_softcap)
-    launch_kernel(prefill_kernel<D, true, BUF>, grid, dim3(256), st, a);
+    launch_kernel(prefill_kernel<D, true, BUF, CT>, grid, dim3(256), st, a);
   else
-    launch_kernel(prefill_kernel<D, false, BUF>, grid, dim3(256), st, a);
+    launch_kernel(prefill_kernel<D, false, BUF, CT>, grid, dim3(256), st, a);
 }
+// quantized pools take the register path; fp16 pools the buffer-form direct
+// loads when each cache is below 4 GiB (never instantiated for D = 256, whose
+// small pools take the 8-wave kernel)
 template <int D>
 void launch_variant(const PrefillArgs& a, dim3 grid, hipStream_t st) {
-  if (a.pool32)
-    launch_variant<D, true>(a, grid, st);
-  else
-    launch_variant<D, false>(a, grid, st);
+  if (a.cache_dtype == kCacheI8)
+    launch_variant<D, false, kCacheI8>(a, grid, st);
+  else if (a.cache_dtype == kCacheF8)
+    launch_variant<D, false, kCacheF8>(a, grid, st);
+  else if constexpr (D != 256) {
+    if (a.pool32)
+      launch_variant<D, true, kCacheF16>(a, grid, st);
+    else
+      launch_variant<D, false, kCacheF16>(a, grid, st);
+  } else {
+    launch_variant<D, false, kCacheF16>(a, grid, st);
+  }
 }
 
 }  // namespace
@@ -696,7 +785,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStr
     case 128: launch_variant<128>(a, grid, st); break;
     case 256:
       if (a.rows16) return launch_prefill16(a, head_size, grid, st);
-      launch_variant<256, false>(a, grid, st);
+      launch_variant<256>(a, grid, st);
       break;
     default: return hipErrorInvalidValue;
   }

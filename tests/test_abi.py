@@ -240,17 +240,24 @@ def test_rows16_prefill_kernel_limits():
     assert "4 GiB" in err()
 
 
-def test_quantized_cache_takes_the_decode_kernel():
-    # every token of a quantized forward runs on the decode kernel
+def test_quantized_cache_routing():
+    # decode rows read codes in the decode kernel; multi-token requests take
+    # the prefill kernel, as with an fp16 cache (the same static shape test)
     pl = plan(params(**QUANT), paged(token_count=40, batch_size=4, **QUANT_KV))
-    assert pl["mode"] == "token" and pl["cache"] == "int8" and pl["prefill_grid"] == "(0,0)"
+    assert pl["mode"] == "request" and pl["cache"] == "int8" and pl["prefill_grid"] != "(0,0)"
     pl = plan(params(cache_dtype=2, k_quant_type=2, v_quant_type=2),
-              paged(token_count=40, batch_size=4, k_scale=FAKE, v_scale=FAKE))
+              paged(token_count=4, batch_size=4, k_scale=FAKE, v_scale=FAKE))
     assert pl["mode"] == "token" and pl["cache"] == "fp8e4m3fn"
     assert plan(params(), paged())["cache"] == "fp16"
-    # path 2 (prefill kernel for multi-token requests) does not serve codes
-    assert call_forward(params(**QUANT), paged(**QUANT_KV), rt=routing(path=2)) == 2
-    assert "quantized caches" in err()
+    # forced routes: every token on the decode kernel, or the prefill kernel
+    pl = plan(params(**QUANT), paged(token_count=40, batch_size=4, **QUANT_KV), rt=routing(path=1))
+    assert pl["mode"] == "token" and pl["prefill_grid"] == "(0,0)"
+    pl = plan(params(**QUANT), paged(token_count=4, batch_size=4, **QUANT_KV), rt=routing(path=2))
+    assert pl["mode"] == "request"
+    # the 8-wave kernel reads fp16 caches only
+    rt = routing(prefill_kernel=2)
+    assert call_forward(params(head_size=256, **QUANT), paged(**QUANT_KV), rt=rt) == 2
+    assert "fp16 cache" in err()
 
 
 def test_qk_norm_head_size_limit_and_workspace():

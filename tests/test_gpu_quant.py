@@ -63,6 +63,36 @@ def test_quantized_scaled_configs(case):
     check_quant(wl.scaled_down(name), cd, kq, vq)
 
 
+MULTI_TOKEN_CASES = [
+    # (workload, cache dtype, K scales, V scales): batches with multi-token requests
+    ("llama3_8b_mixed", I8, PC, PT),
+    ("llama3_8b_mixed", F8, PT, PC),
+    ("gemma2_prefill_window", I8, PT, PC),       # D 256, softcap, window
+    ("gemma2_prefill_window", F8, PC, PC),
+]
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("case", MULTI_TOKEN_CASES, ids=lambda c: "-".join(
+    [c[0], CACHE_NAMES[c[1]], QUANT_NAMES[c[2]], QUANT_NAMES[c[3]]]))
+def test_quantized_multi_token_routes(case, path):
+    """Multi-token requests over a quantized pool on both routes: every token
+    on the decode kernel (path 1), or the 4-wave prefill kernel staging the
+    codes as fp16 in LDS (path 2)."""
+    name, cd, kq, vq = case
+    check_quant(wl.scaled_down(name), cd, kq, vq, path=path)
+
+
+@pytest.mark.parametrize("pieces", [2, 3])
+def test_quantized_prefill_pieces_and_holes(pieces):
+    """The prefill kernel over codes with its key range cut into pieces, and
+    unmapped blocks inside the window (their blocks hold the NaN code)."""
+    w = wl.scaled_down("gemma2_prefill_window")
+    ent = set(wl.random_unmapped_entries(w, 21, 0.2)) | {(0, 7), (0, 9)}
+    w = wl.with_unmapped_blocks(w, sorted(ent))
+    check_quant(w, F8, PC, PT, path=2, prefill_pieces=pieces)
+
+
 def test_quantized_saturation_is_exercised():
     """The int8 scales put about one new value in 300 past the code range:
     the bit-exact check above then covers saturated codes too."""
@@ -83,6 +113,8 @@ QUANT_SWEEP = [
      dict(do_rotary=1, rotary_interleaved=1, rotary_dim=32)),
     ([130, 1, 3], [300, 1000, 64], 6, 2, 256, 16, F8, PC, PT,
      dict(local_window_size=200, softcap=5.0)),
+    ([70, 1, 33], [130, 400, 0], 8, 4, 128, 32, I8, PT, PT,
+     dict(do_rotary=1, rotary_dim=128)),
     ([1, 1, 1, 1, 1], [900, 1, 77, 600, 2], 24, 2, 128, 16, I8, PT, PC, dict(softcap=1.0)),
     ([17, 1, 0, 2], [15, 3, 9, 0], 4, 4, 64, 16, F8, PT, PT, {}),
 ]
