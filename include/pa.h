@@ -118,8 +118,8 @@ enum { PA_LAYOUT_SEPARATE = 0, PA_LAYOUT_LATENT = 1 };
  * dequantizes in the kernel (section 8.5, phase 3): a PER_TENSOR K scale is
  * folded into the score scale, a PER_CHANNEL one into Q (rounded to fp16), and
  * the V scale is applied to the output accumulator.  Decode rows read the
- * codes in the decode kernel; multi-token requests in the 4-wave prefill
- * kernel, which turns each lane's codes into fp16 on their way into LDS.
+ * codes in the decode kernel; multi-token requests in the prefill kernels,
+ * which turn each lane's codes into fp16 on their way into LDS.
  * Scales are positive finite values (they are device data and not checked).
  * Validation (section 8.7): a quantized cache_dtype
  * needs both quant types non-NONE, fp16 needs both NONE; a quant type other

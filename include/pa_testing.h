@@ -29,7 +29,7 @@ typedef struct {
                              key range, merged on the device                            */
   int32_t prefill_kernel; /* 0 = auto; 1 = 4-wave prefill kernel (32 query rows per
                              wave); 2 = 8-wave kernel (16 rows per wave), head_size 256
-                             with fp16 caches each smaller than 4 GiB, else
+                             with each cache smaller than 4 GiB, else
                              PA_ERR_UNSUPPORTED                                         */
 } pa_routing;
 

@@ -323,10 +323,10 @@ bool pool_fits_32bit(const pa_attn_params* p, const pa_paged_kv* kv) {
   return kv->num_blocks * p->block_size * p->kv_num_heads * p->head_size * 2 <
          ((int64_t)1 << 32) - 16;
 }
-// The 8-wave prefill kernel serves head_size 256 over fp16 caches and
-// addresses them with 32-bit byte offsets.
+// The 8-wave prefill kernel serves head_size 256 and addresses the caches
+// with 32-bit byte offsets.
 bool rows16_prefill_fits(const pa_attn_params* p, const pa_paged_kv* kv) {
-  return p->head_size == 256 && p->cache_dtype == PA_CACHE_FP16 && pool_fits_32bit(p, kv);
+  return p->head_size == 256 && pool_fits_32bit(p, kv);
 }
 
 pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv,
@@ -352,8 +352,7 @@ pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv,
                 "head_size %d: the kernels serve head_size 64, 128 and 256", p->head_size);
   if (rt.prefill_kernel == 2 && !rows16_prefill_fits(p, kv))
     return fail(PA_ERR_UNSUPPORTED,
-                "prefill_kernel 2: expected head_size 256, an fp16 cache and caches smaller "
-                "than 4 GiB");
+                "prefill_kernel 2: expected head_size 256 and caches smaller than 4 GiB");
   return PA_OK;
 }
 

@@ -37,6 +37,15 @@
 // QK product of the next tile interleaved with the softmax of the current
 // one, one barrier per tile, scores in log2 units with a lazily raised
 // running max.
+//
+// Quantized pools (PagedAttention -- CUDA Design Document, section 8.5,
+// phase 3): K rows load as byte codes into registers where the fp16 kernel
+// issues its direct loads, and are written into the same LDS slots as fp16
+// values (every int8 and e4m3fn value is an fp16 value) just before the
+// step's barrier; V codes load into registers one step ahead like fp16 V and
+// become fp16 right before their transpose.  A per-tensor K scale joins the
+// score scale, a per-channel one multiplies Q; the V scale multiplies the
+// output accumulator.
 #include <type_traits>
 
 #include "prefill_common.h"
@@ -99,7 +108,8 @@ __device__ __forceinline__ void transpose8x8(u32x4& c0, u32x4& c1) {
   }
 }
 
-template <int D, bool SOFTCAP>
+// CT: element type of the pools (kCacheF16, or int8 / e4m3fn codes).
+template <int D, bool SOFTCAP, int CT>
 __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
   using C = Rows16Cfg<D>;
   __shared__ __attribute__((aligned(1024))) char K0[C::SLOTS * C::KSLOT];
@@ -160,6 +170,23 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
   const int64_t kbytes = ((sl.num_blocks << shift) * a.kv_heads * D - (int64_t)kvh * D) * 2;
   const __amdgpu_buffer_rsrc_t ksrd = __builtin_amdgcn_make_buffer_rsrc(
       (void*)kbase, (short)0, (int)(uint32_t)min(kbytes, (int64_t)0xFFFFFFFF), 0x00020000);
+  // quantized pools: byte arrays of codes, one byte per element
+  constexpr bool kCodes = CT != kCacheF16;
+  const char* kcode = reinterpret_cast<const char*>(a.key_cache) + (int64_t)kvh * D;
+  const char* vcode = reinterpret_cast<const char*>(a.value_cache) + (int64_t)kvh * D;
+  // a per-tensor K scale joins the score scale (and the softcap's input
+  // scale); a per-channel one is folded into Q below
+  float score_scale = a.score_scale, cap_in2 = a.cap_in2;
+  bool k_per_channel = false;
+  if constexpr (kCodes) {
+    if (a.k_quant == kQuantChannel) {
+      k_per_channel = true;
+    } else {
+      const float ks = a.k_scale[0];
+      score_scale *= ks;
+      cap_in2 *= ks;
+    }
+  }
 
   // this lane's query row
   const int R = tile * kPrefillRows + wave * 16 + l16;
@@ -190,11 +217,18 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
       const uint16_t* qrow = a.query + (int64_t)t * HD + (int64_t)head * D;
       const int c = 4 * ks + q4;
       v = load16(qrow + 8 * c);
-      if (chunk_rotated(c, a.rotary_offset, a.rotary_dim)) {
-        const int off = a.rotary_offset;
+      const bool rot = chunk_rotated(c, a.rotary_offset, a.rotary_dim);
+      if (rot || k_per_channel) {
+        const int off = rot ? a.rotary_offset : 0;
         float rr[8];
-        rotate_chunk(qrow + off, v, c - off / 8, pos, a.cos, a.sin, a.rotary_dim,
+        rotate_chunk(qrow + off, v, c - off / 8, pos, a.cos, a.sin, rot ? a.rotary_dim : 0,
                      a.rotary_interleaved, a.rotary_rows, rr);
+        if (k_per_channel) {
+          float ks[8];
+          channel_scales(a.k_scale, kQuantChannel, kvh, D, 8 * c, ks);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rr[e] *= ks[e];
+        }
         v = pack8(rr);
       }
     }
@@ -244,6 +278,18 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
     const int v = s_tbl[in ? (tau >> shift) - seg_first : 0] | (in ? 0 : -1);
     return v < 0 ? ~0u : ((uint32_t)v << shift) | (uint32_t)(tau & bmask);
   };
+  // quantized pools: the lane's eight codes of a K row (a zero row reads the
+  // zero block: code 0 is +0), and their fp16 values written into the lane's
+  // 16 bytes of the slot the direct load would fill
+  auto load_kcode = [&](uint32_t row) -> u32x2 {
+    const int64_t off = row != ~0u ? (int64_t)row * tok_stride32 + 8 * (lane % C::CH)
+                                   : reinterpret_cast<const char*>(g_zero_row) - kcode;
+    return *reinterpret_cast<const u32x2*>(kcode + off);
+  };
+  auto put_k = [&](u32x2 c, char* kb, int mi) {
+    *reinterpret_cast<u32x4*>(kb + (wave + C::WAVES * mi) * C::KSLOT + 16 * lane) =
+        codes_to_f16<CT>(c);
+  };
   auto dma_k = [&](uint32_t row, char* kb, int mi) {
     const uint32_t off = row != ~0u ? (row * tok_stride32 + 8 * (lane % C::CH)) * 2 : 0xFFFFFFF0u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -274,13 +320,31 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
     const int ch = 8 * (lm + 16 * y);
     return row != ~0u ? (int64_t)((uint64_t)row * tok_stride32 + ch) : (g_zero_row + ch) - base;
   };
-  // staged loads: [x][y] = chunk y of key x
+  // staged loads: [x][y] = chunk y of key x (codes: in vcodes until widened)
   u32x4 vreg[2][2];
+  u32x2 vcodes[2][2];
   auto load_v = [&](const uint32_t (&rows)[2]) {
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int y = 0; y < 2; ++y) vreg[x][y] = load16(vbase + chunk_off(rows[x], vbase, y));
+      for (int y = 0; y < 2; ++y) {
+        if constexpr (kCodes) {
+          const int ch = 8 * (lm + 16 * y);
+          const int64_t off = rows[x] != ~0u
+                                  ? (int64_t)((uint64_t)rows[x] * tok_stride32 + ch)
+                                  : reinterpret_cast<const char*>(g_zero_row) - vcode;
+          vcodes[x][y] = *reinterpret_cast<const u32x2*>(vcode + off);
+        } else {
+          vreg[x][y] = load16(vbase + chunk_off(rows[x], vbase, y));
+        }
+      }
+  };
+  // codes of chunk y of both keys as fp16 values, ready for the transpose
+  auto widen_v = [&](int y) {
+    if constexpr (kCodes) {
+      vreg[0][y] = codes_to_f16<CT>(vcodes[0][y]);
+      vreg[1][y] = codes_to_f16<CT>(vcodes[1][y]);
+    }
   };
   // V^T transposed: after the transpose the lane holds channels 2G + x of
   // chunk m + 16 y for the group's 8 keys in slot order
@@ -292,6 +356,7 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
   auto write_v = [&](char* vb) {
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
+      widen_v(y);
       transpose8x8(vreg[0][y], vreg[1][y]);
 #pragma unroll
       for (int x = 0; x < 2; ++x) write_v1(vb, x, y);
@@ -325,9 +390,9 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
 
   auto logit = [&](float x) {
     if constexpr (SOFTCAP)
-      return a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * a.cap_in2) + 1.0f));
+      return a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * cap_in2) + 1.0f));
     else
-      return x * a.score_scale;
+      return x * score_scale;
   };
   // a row's tile maximum in log2 units; the row's four lanes agree
   auto tile_max = [&](const f4 (&s)[4]) {
@@ -381,11 +446,11 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
       if constexpr (SOFTCAP) {
         // cap * tanh(y) - mu = (cap - mu) - 2 cap / (2^t + 1), t = 2y log2(e);
         // a masked score (t = -inf) gets -inf through t * 2^-120
-        const float tt = x * a.cap_in2;
+        const float tt = x * cap_in2;
         const float r = __builtin_amdgcn_rcpf(exp2_fast(tt) + 1.0f);
         e = __builtin_fmaf(tt, 0x1p-120f, __builtin_fmaf(r, -2.0f * a.cap_out, a.cap_out - mu));
       } else {
-        e = __builtin_fmaf(x, a.score_scale, -mu);
+        e = __builtin_fmaf(x, score_scale, -mu);
       }
       const float p = exp2_fast(e);
       part[i] += p;
@@ -401,8 +466,13 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
     stage_table(max(kt_begin, lo));
 #pragma unroll
     for (int mi = 0; mi < C::DMA; ++mi) {
-      dma_k(row_k(0, mi), K0, mi);
-      dma_k(row_k(1, mi), K1, mi);
+      if constexpr (kCodes) {
+        put_k(load_kcode(row_k(0, mi)), K0, mi);
+        put_k(load_kcode(row_k(1, mi)), K1, mi);
+      } else {
+        dma_k(row_k(0, mi), K0, mi);
+        dma_k(row_k(1, mi), K1, mi);
+      }
     }
     const uint32_t r0[2] = {row_v(0, 0), row_v(0, 1)};
     load_v(r0);
@@ -457,6 +527,7 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
     h8 pf[2];
     float part[4] = {0.f, 0.f, 0.f, 0.f};
     uint32_t vrows[2];
+    u32x2 kc[kCodes ? C::DMA : 1];   // quantized pools: this step's K codes, written at its end
     {
       for (int kb = 0; kb < 4; ++kb) s_next[kb] = f4{0.f, 0.f, 0.f, 0.f};
       const char* kt = kbuf(NB{}) + koff;
@@ -477,7 +548,10 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
         if (ks < C::DMA) {
           const uint32_t row = krow_next;
           if (ks + 1 < C::DMA) krow_next = row_k(it + 2, ks + 1);
-          dma_k(row, kbuf(B), ks);
+          if constexpr (kCodes)
+            kc[ks] = load_kcode(row);
+          else
+            dma_k(row, kbuf(B), ks);
         } else if (ks == C::DMA) {
           vrows[0] = row_v(it + 2, 0);
           vrows[1] = row_v(it + 2, 1);
@@ -507,6 +581,7 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
         // loads, issued after them, may still be in flight)
         if (i == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | C::DMA);
         if (i == 17 || i == 21) {
+          widen_v((i - 17) >> 2);
           transpose8x8(vreg[0][(i - 17) >> 2], vreg[1][(i - 17) >> 2]);
         } else if (i >= 18 && i <= 24 && (i & 1) == 0) {
           write_v1(vbuf(NB{}), (i >> 1) & 1, (i - 18) >> 2);
@@ -526,6 +601,11 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
       pos_mask(s_next, kt_of(it + 1));
       mx_next = tile_max(s_next);
     }
+    if constexpr (kCodes) {
+      // tile it + 2's K into buffer B, which no wave reads during this step
+#pragma unroll
+      for (int mi = 0; mi < C::DMA; ++mi) put_k(kc[mi], kbuf(B), mi);
+    }
     // this step's K loads have landed (the V loads issued after them may
     // still be in flight)
     __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
@@ -539,6 +619,16 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
   wait_vmem();   // loads past the last tile (zero rows) drain before the end
 
   const float lt = xor32_sum(xor16_sum(lsum));
+  if constexpr (kCodes) {
+    // the V scale of channels 16 db + 4 q4 + (0..3): output = scale * sum p code
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const f4 vs = a.v_quant == kQuantChannel
+                        ? *reinterpret_cast<const f4*>(a.v_scale + (int64_t)kvh * D + 16 * db + 4 * q4)
+                        : f4{a.v_scale[0], a.v_scale[0], a.v_scale[0], a.v_scale[0]};
+      acc[db] *= vs;
+    }
+  }
   if (pieces > 1) {
     const int64_t pr = ((int64_t)t * a.num_heads + head) * a.chunks;
     if (row_ok) {
@@ -567,14 +657,23 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
   }
 }
 
+template <int CT>
+void launch_prefill16_cache(const PrefillArgs& a, dim3 grid, hipStream_t st) {
+  if (a.use_softcap)
+    launch_kernel(prefill16_kernel<256, true, CT>, grid, dim3(512), st, a);
+  else
+    launch_kernel(prefill16_kernel<256, false, CT>, grid, dim3(512), st, a);
+}
+
 }  // namespace
 
 hipError_t launch_prefill16(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st) {
   if (head_size != 256) return hipErrorInvalidValue;
-  if (a.use_softcap)
-    launch_kernel(prefill16_kernel<256, true>, grid, dim3(512), st, a);
-  else
-    launch_kernel(prefill16_kernel<256, false>, grid, dim3(512), st, a);
+  switch (a.cache_dtype) {
+    case kCacheI8: launch_prefill16_cache<kCacheI8>(a, grid, st); break;
+    case kCacheF8: launch_prefill16_cache<kCacheF8>(a, grid, st); break;
+    default: launch_prefill16_cache<kCacheF16>(a, grid, st); break;
+  }
   return hipGetLastError();
 }
 

@@ -254,10 +254,10 @@ def test_quantized_cache_routing():
     assert pl["mode"] == "token" and pl["prefill_grid"] == "(0,0)"
     pl = plan(params(**QUANT), paged(token_count=4, batch_size=4, **QUANT_KV), rt=routing(path=2))
     assert pl["mode"] == "request"
-    # the 8-wave kernel reads fp16 caches only
-    rt = routing(prefill_kernel=2)
-    assert call_forward(params(head_size=256, **QUANT), paged(**QUANT_KV), rt=rt) == 2
-    assert "fp16 cache" in err()
+    # both prefill kernels read codes: head size 256 takes the 8-wave kernel
+    pl = plan(params(head_size=256, **QUANT), paged(token_count=40, batch_size=4, **QUANT_KV),
+              rt=routing(prefill_kernel=2))
+    assert pl["mode"] == "request" and pl["cache"] == "int8"
 
 
 def test_qk_norm_head_size_limit_and_workspace():
