@@ -52,6 +52,10 @@ constexpr float kRescaleSlack = 8.0f;   // log2 units
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
+// LDS operand reads in flight ahead of the products that use them
+constexpr int kAheadK = 4;
+constexpr int kAheadV = 4;
+
 struct MlaCfg {
   static constexpr int D = kMlaHeadSize;     // 576: latent 512 + rotary 64
   static constexpr int DV = kMlaVHeadSize;   // 512: the V view of a row
@@ -289,19 +293,28 @@ void mla_kernel(const DecodeArgs a) {
         if (chunk_ok) {
 
         // ---- S^T = K . Q^T: two 16-key blocks over the 576 channels ----
-        f4 s[2];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
+        // operand reads run kAheadK products ahead of their MFMAs (the two
+        // 16-key blocks alternate, so consecutive products are independent)
+        f4 s[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+        auto kread = [&](int i) __attribute__((always_inline)) {
+          const int sb = i & 1, ks = i >> 1;
           const int rk = 16 * sb + l16;
-          s[sb] = f4{0.f, 0.f, 0.f, 0.f};
+          const uint16_t* src =
+              ks < C::DV / 32 ? kmain + rk * (C::MAIN / 2) + 32 * ks + 8 * q
+                              : ktail + 8 * tail_slot(rk, 4 * (ks - C::DV / 32) + q);
+          return *reinterpret_cast<const h8*>(src);
+        };
+        {
+          constexpr int NQ = 2 * C::KS;
+          h8 kf[kAheadK];
 #pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) {
-            const uint16_t* src =
-                ks < C::DV / 32
-                    ? kmain + rk * (C::MAIN / 2) + 32 * ks + 8 * q
-                    : ktail + 8 * tail_slot(rk, 4 * (ks - C::DV / 32) + q);
-            const h8 ka = *reinterpret_cast<const h8*>(src);
-            s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[ks], s[sb], 0, 0, 0);
+          for (int i = 0; i < kAheadK; ++i) kf[i] = kread(i);
+#pragma unroll
+          for (int i = 0; i < NQ; ++i) {
+            s[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[i % kAheadK], qf[i >> 1],
+                                                              s[i & 1], 0, 0, 0);
+            if (i + kAheadK < NQ) kf[i % kAheadK] = kread(i + kAheadK);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
 
@@ -346,8 +359,7 @@ void mla_kernel(const DecodeArgs a) {
         }
 
         // ---- O^T += V^T . P^T, V^T read from the K tile (channels < 512) ----
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
+        auto vread = [&](int db) __attribute__((always_inline)) {
           v4s part[2];
 #pragma unroll
           for (int sb = 0; sb < 2; ++sb)
@@ -357,7 +369,18 @@ void mla_kernel(const DecodeArgs a) {
                     4 * (l16 & 3)));
           h8 va;
           __builtin_memcpy(&va, part, 16);
-          acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf, acc[db], 0, 0, 0);
+          return va;
+        };
+        {
+          h8 vf[kAheadV];
+#pragma unroll
+          for (int i = 0; i < kAheadV; ++i) vf[i] = vread(i);
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db % kAheadV], pf, acc[db], 0, 0, 0);
+            if (db + kAheadV < C::DB) vf[db % kAheadV] = vread(db + kAheadV);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
         }   // chunk_ok
         // every read of the tile has returned (the products above consumed
