@@ -84,6 +84,12 @@ __global__ __launch_bounds__(1024) void plan_kernel(const PlanArgs a) {
       if (resolve_row(a.s, a.token_mode, row, a.window, a.split_tokens, a.max_splits, r, orphan)) {
         n = r.nsplit;
         s_info[tid] = r;
+        // no key position to visit (the window starts past the table's
+        // capacity): no item is listed, so the row is written here, as a
+        // row with no admitted key
+        if (n == 0)
+          for (int i = 0; i < a.row_width; i += 8)
+            store16(a.out + (int64_t)r.t * a.row_width + i, u32x4{0, 0, 0, 0});
       } else if (orphan) {
         for (int i = 0; i < a.row_width; i += 8)
           store16(a.out + (int64_t)row * a.row_width + i, u32x4{0, 0, 0, 0});

@@ -85,6 +85,20 @@ def test_unmapped_blocks_with_rotary_and_many_splits():
     check(wl.with_unmapped_blocks(w, sorted(ent)), split_tokens=128)
 
 
+@pytest.mark.parametrize("split_tokens", [0, 64])
+def test_positions_past_the_table_capacity(split_tokens):
+    """A table narrower than a request needs: positions past its capacity
+    read as unmapped, the new token past it is not written, and a row whose
+    window lies wholly past it is 0 (request 0: position 2000, window 100,
+    capacity 512 keys)."""
+    w = wl.build_case("past_capacity", 3301, q_lens=[1, 1, 1], past=[2000, 500, 90],
+                      num_heads=8, kv_num_heads=2, head_size=64, block_size=16,
+                      local_window_size=100)
+    w.block_table = np.ascontiguousarray(w.block_table[:, :32])
+    out, ref = check(w, split_tokens=split_tokens)
+    assert np.all(out[0] == 0) and np.all(ref[0] == 0)
+
+
 def test_unmapped_blocks_int8_pool():
     from pa_harness import gpu_quant_step, oracle_append_quant, oracle_forward_quant, quant_inputs
     w = holes_decode()
