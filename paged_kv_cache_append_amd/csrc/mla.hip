@@ -431,6 +431,284 @@ void mla_kernel(const DecodeArgs a) {
   }
 }
 
+// Shared mode for many heads, in wave pairs: a workgroup of 8 waves takes
+// four head chunks (64 heads) of one (row, split); the two waves of a pair
+// share a head chunk and split its work -- the QK product over the channel
+// halves (k-steps 0..8 and 9..17, whose partial scores are summed through LDS),
+// the PV product over the output channel halves (0..255 and 256..511).  A
+// wave then holds half the Q fragments and half the accumulator, so two
+// waves fit each SIMD and one's softmax and barriers run under the other's
+// products.  Waves 0..3 copy the tiles into the double buffer as in the
+// four-wave shared mode.
+template <bool SOFTCAP>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void mla_pair_kernel(const DecodeArgs a) {
+  using C = MlaCfg;
+  constexpr int KH = C::KS / 2;        // 9 k-steps per half
+  constexpr int DBH = C::DB / 2;       // 16 output blocks per half
+  __shared__ __attribute__((aligned(16))) char s_k[2][C::TILE];
+  __shared__ __attribute__((aligned(16))) f4 s_sx[C::WAVES][2][2][64];   // [pair][half][block][lane]
+  __shared__ int32_t s_tbl[C::TBL];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0..7
+  const int pair = wave >> 1;
+  const int half = wave & 1;
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4;
+  const int l16 = lane & 15;
+  const SeqLayout& sl = a.s;
+  const int HC = a.head_chunks;
+  const int64_t HQ = (int64_t)a.num_heads * C::D;
+  const int64_t HO = (int64_t)a.num_heads * C::DV;
+  const int HG = (HC + C::WAVES - 1) / C::WAVES;   // items per entry: groups of 4 chunks
+  const int total = a.listed ? (*a.entry_count) * HG : a.rows * HG;
+  int32_t* tbl = s_tbl;
+  const int shift = sl.block_shift;
+  const bool copier = wave < C::WAVES;   // waves 0..3 copy a quarter of every tile each
+  const int64_t pool_bytes = (sl.num_blocks << shift) * (int64_t)(2 * C::D);
+  const __amdgpu_buffer_rsrc_t srd = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.key_cache, (short)0, (int)(uint32_t)min(pool_bytes, (int64_t)0xFFFFFFFF),
+      0x00020000);
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int e = item / HG;
+    const int hc = (item - e * HG) * C::WAVES + pair;
+    const bool chunk_ok = hc < HC;   // a pair past the last chunk only helps copy
+    const int h0 = hc * a.chunk_heads;
+
+    int row, split, k_lo, k_hi;
+    RowInfo r;
+    if (a.listed) {
+      const DecodeEntry en = a.entries[e];
+      row = en.row;
+      split = en.split;
+      k_lo = en.k_lo;
+      k_hi = en.k_hi;
+      r.t = en.t;
+      r.b = en.b;
+      r.pos = en.pos;
+      r.nsplit = en.nsplit;
+    } else {
+      row = e;
+      split = 0;
+      bool orphan;
+      if (!resolve_row(sl, 1, row, a.window, a.split_tokens, a.max_splits, r, orphan)) {
+        if (orphan && row < sl.tokens && chunk_ok) {   // token owned by no request: zero
+          for (int i = lane; i < a.chunk_heads * (C::DV / 16); i += 64) {
+            const int hh = i / (C::DV / 16), cc = i % (C::DV / 16);
+            store16(a.out + row * HO + (int64_t)(h0 + hh) * C::DV + half * (C::DV / 2) + 8 * cc,
+                    u32x4{0, 0, 0, 0});
+          }
+        }
+        continue;
+      }
+      k_lo = r.lo;
+      k_hi = r.nsplit > 0 ? min(r.hi, k_lo + a.split_tokens) : k_lo;
+    }
+
+    // this wave's half of Q as the B operand: lane (q, l16) holds head l16,
+    // channels 32 (KH half + j) + 8 q + [0, 8), rotated on its suffix window
+    const bool head_ok = chunk_ok && l16 < a.chunk_heads;
+    h8 qf[KH];
+    {
+      const uint16_t* qrow = a.query + (int64_t)r.t * HQ + (int64_t)(h0 + l16) * C::D;
+#pragma unroll
+      for (int j = 0; j < KH; ++j) {
+        const int ks = KH * half + j;
+        u32x4 v = u32x4{0, 0, 0, 0};
+        const int c = 4 * ks + q;
+        if (head_ok) {
+          v = load16(qrow + 8 * c);
+          // the rotary window lies past the V channels (checked on the host)
+          if (ks >= C::DV / 32 && chunk_rotated(c, a.rotary_offset, a.rotary_dim)) {
+            const int off = a.rotary_offset;
+            float rr[8];
+            rotate_chunk(qrow + off, v, c - off / 8, r.pos, a.cos, a.sin, a.rotary_dim,
+                         a.rotary_interleaved, a.rotary_rows, rr);
+            v = pack8(rr);
+          }
+        }
+        qf[j] = as_h8(v);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    f4 acc[DBH];
+#pragma unroll
+    for (int i = 0; i < DBH; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, lsum = 0.f;
+    const int32_t* bt = sl.block_table + (int64_t)r.b * sl.maxblk;
+
+    for (int seg_lo = k_lo; seg_lo < k_hi;) {
+      const int first_bi = seg_lo >> shift;
+      const int seg_hi = min(k_hi, (first_bi + C::TBL) << shift);
+      const int n_bi = ((seg_hi - 1) >> shift) - first_bi + 1;
+      bool hole = false;
+      for (int i = threadIdx.x; i < n_bi; i += 64 * 2 * C::WAVES) {
+        const int bi = first_bi + i;
+        int v = bi < sl.maxblk ? bt[bi] : -1;
+        if (v >= sl.num_blocks) v = -1;
+        hole |= v < 0;
+        tbl[i] = v;
+      }
+      const bool any_hole = __syncthreads_or(hole);
+
+      const int ntile = (seg_hi - seg_lo + C::KT - 1) / C::KT;
+      auto copy = [&](int t, char* buf) {
+        if (copier)
+          mla_copy_rows<1>(srd, buf, tbl, first_bi, shift, seg_lo + t * C::KT, seg_hi, lane, wave);
+      };
+      copy(0, s_k[0]);
+      if (ntile > 1) copy(1, s_k[1]);
+      for (int it = 0; it < ntile; ++it) {
+        const int k0 = seg_lo + it * C::KT;
+        const bool more = it + 1 < ntile;
+        char* tile = s_k[it & 1];
+        const uint16_t* kmain = reinterpret_cast<const uint16_t*>(tile);
+        const uint16_t* ktail = reinterpret_cast<const uint16_t*>(tile + C::KT * C::MAIN);
+        // this wave's part of tile it has landed (tile it + 1's may be in
+        // flight: 9 instructions), then everyone's
+        if (more)
+          __builtin_amdgcn_s_waitcnt(0x0F79);   // vmcnt(9)
+        else
+          __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();
+
+        // ---- this wave's half of S^T = K . Q^T (k-steps KH half ..) ----
+        f4 s[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+        if (chunk_ok) {
+          auto kread = [&](int i) __attribute__((always_inline)) {
+            const int sb = i & 1, ks = KH * half + (i >> 1);
+            const int rk = 16 * sb + l16;
+            const uint16_t* src =
+                ks < C::DV / 32 ? kmain + rk * (C::MAIN / 2) + 32 * ks + 8 * q
+                                : ktail + 8 * tail_slot(rk, 4 * (ks - C::DV / 32) + q);
+            return *reinterpret_cast<const h8*>(src);
+          };
+          constexpr int NQ = 2 * KH;
+          h8 kf[kAheadK];
+#pragma unroll
+          for (int i = 0; i < kAheadK; ++i) kf[i] = kread(i);
+#pragma unroll
+          for (int i = 0; i < NQ; ++i) {
+            s[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[i % kAheadK], qf[i >> 1],
+                                                              s[i & 1], 0, 0, 0);
+            if (i + kAheadK < NQ) kf[i % kAheadK] = kread(i + kAheadK);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // ---- the pair's partial scores summed through LDS (both waves form
+        // the same sum: fp32 addition commutes) ----
+        s_sx[pair][half][0][lane] = s[0];
+        s_sx[pair][half][1][lane] = s[1];
+        __syncthreads();
+        {
+          const f4 o0 = s_sx[pair][1 - half][0][lane], o1 = s_sx[pair][1 - half][1][lane];
+          s[0] = half == 0 ? s[0] + o0 : o0 + s[0];
+          s[1] = half == 0 ? s[1] + o1 : o1 + s[1];
+        }
+        if (chunk_ok) {
+          // ---- scores (log2 units), mask, running max ----
+          const bool edge = any_hole || k0 + C::KT > seg_hi;
+          float x[8];
+          float mx = kNegInf;
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              float v = s[sb][rr];
+              if constexpr (SOFTCAP)
+                v = tanh_fast(v * a.cap_in) * a.cap_out;
+              else
+                v = v * a.score_scale;
+              if (edge) {
+                const int key = k0 + 16 * sb + 4 * q + rr;
+                const bool ok = key < seg_hi && tbl[(key >> shift) - first_bi] >= 0;
+                v = ok ? v : kNegInf;
+              }
+              x[4 * sb + rr] = v;
+              mx = fmaxf(mx, v);
+            }
+          }
+          mx = lane_max32(lane_max16(mx));
+          if (__any(mx > m + kRescaleSlack)) {
+            const float mn = mx > m + kRescaleSlack ? mx : m;
+            const float alpha = exp2_fast(m - (mn == kNegInf ? 0.f : mn));
+            m = mn;
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < DBH; ++i) acc[i] *= alpha;
+          }
+          const float mu = m == kNegInf ? 0.f : m;
+          h8 pf;   // keys 4q + (0..3) of both 16-key blocks, in that order
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float p = exp2_fast(x[i] - mu);
+            lsum += p;
+            pf[i] = (_Float16)p;
+          }
+
+          // ---- this wave's half of O^T += V^T . P^T (channels 256 half ..) ----
+          auto vread = [&](int db) __attribute__((always_inline)) {
+            v4s part[2];
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+              part[sb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) v4s*)(
+                      kmain + (16 * sb + 4 * q + (l16 >> 2)) * (C::MAIN / 2) +
+                      16 * (DBH * half + db) + 4 * (l16 & 3)));
+            h8 va;
+            __builtin_memcpy(&va, part, 16);
+            return va;
+          };
+          h8 vf[kAheadV];
+#pragma unroll
+          for (int i = 0; i < kAheadV; ++i) vf[i] = vread(i);
+#pragma unroll
+          for (int db = 0; db < DBH; ++db) {
+            acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db % kAheadV], pf, acc[db], 0, 0, 0);
+            if (db + kAheadV < DBH) vf[db % kAheadV] = vread(db + kAheadV);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }   // chunk_ok
+        // every read of the tile (and of the score exchange) has returned: a
+        // later tile's copy may overwrite the tile, the next scores the slots
+        __syncthreads();
+        if (it + 2 < ntile) copy(it + 2, tile);
+      }
+      seg_lo = seg_hi;
+      __syncthreads();   // the table is restaged for the next segment
+    }
+
+    // ---- epilogue: lane (q, l16) holds head l16, channels 256 half + 16 db + 4 q + [0, 4) ----
+    const float lt = lane_sum32(lane_sum16(lsum));
+    if (head_ok) {
+      const int h = h0 + l16;
+      const int cb = (C::DV / 2) * half;
+      if (r.nsplit <= 1) {
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        uint16_t* orow = a.out + (int64_t)r.t * HO + (int64_t)h * C::DV + cb;
+#pragma unroll
+        for (int db = 0; db < DBH; ++db) {
+          uint2 w;
+          w.x = (uint32_t)f2h(acc[db][0] * inv) | ((uint32_t)f2h(acc[db][1] * inv) << 16);
+          w.y = (uint32_t)f2h(acc[db][2] * inv) | ((uint32_t)f2h(acc[db][3] * inv) << 16);
+          *reinterpret_cast<uint2*>(orow + 16 * db + 4 * q) = w;
+        }
+      } else {
+        const int64_t pidx = ((int64_t)row * a.num_heads + h) * a.max_splits + split;
+        float* po = a.part_o + pidx * C::DV + cb;
+#pragma unroll
+        for (int db = 0; db < DBH; ++db) *reinterpret_cast<f4*>(po + 16 * db + 4 * q) = acc[db];
+        if (q == 0 && half == 0) {
+          a.part_ml[2 * pidx] = m;
+          a.part_ml[2 * pidx + 1] = lt;
+        }
+      }
+    }
+  }
+}
+
 template <bool SOFTCAP>
 int mla_occupancy() {
   static int cached = 0;
@@ -456,10 +734,11 @@ hipError_t launch_mla(const DecodeArgs& a, int workgroups, hipStream_t st) {
   // shared mode once a workgroup's four waves each have a head chunk
   const bool shared = a.head_chunks >= MlaCfg::WAVES;
   if (shared) {
+    const dim3 pair_block(2 * 64 * MlaCfg::WAVES);
     if (a.use_softcap)
-      launch_kernel(mla_kernel<true, true>, grid, block, st, a);
+      launch_kernel(mla_pair_kernel<true>, grid, pair_block, st, a);
     else
-      launch_kernel(mla_kernel<false, true>, grid, block, st, a);
+      launch_kernel(mla_pair_kernel<false>, grid, pair_block, st, a);
   } else {
     if (a.use_softcap)
       launch_kernel(mla_kernel<true, false>, grid, block, st, a);
