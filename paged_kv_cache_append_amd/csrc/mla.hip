@@ -32,12 +32,12 @@
 // The head chunks of one (row, split) are consecutive items, taken by waves
 // of one workgroup, so the rows they share come from L2 after the first read.
 //
-// With 64 or more heads (four head chunks or more) the kernel runs in shared
-// mode instead: the four waves of a workgroup take four head chunks of the
-// same (row, split) and share one double-buffered LDS tile pair.  Each wave
-// copies a quarter of every tile (8 rows + their tail), the copy of tile
-// it + 1 lands while all four compute on tile it, and a tile is copied once
-// per 64 heads instead of once per 16.
+// With 64 or more heads (four head chunks or more) a workgroup of 8 waves
+// takes four head chunks of the same (row, split) and shares one
+// double-buffered LDS tile pair; the two waves of a pair split a chunk's
+// products (QK over channel halves, PV over output halves), so each holds
+// half the registers and two waves share every SIMD (mla_pair_kernel).  A
+// tile is copied once per 64 heads instead of once per 16.
 #include <type_traits>
 
 #include "decode_rows.h"
@@ -137,12 +137,12 @@ __device__ __forceinline__ void mla_copy_rows(__amdgpu_buffer_rsrc_t srd, char* 
   }
 }
 
-template <bool SOFTCAP, bool SHARED>
+// Per-wave mode (fewer than four head chunks): each wave an independent
+// worker with its own LDS tile.
+template <bool SOFTCAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void mla_kernel(const DecodeArgs a) {
   using C = MlaCfg;
-  // per-wave mode: one tile per wave; shared mode: tiles 0 and 1 are the
-  // workgroup's double buffer
   __shared__ __attribute__((aligned(16))) char s_k[C::WAVES][C::TILE];
   __shared__ int32_t s_tbl[C::WAVES][C::TBL];
 
@@ -154,11 +154,10 @@ void mla_kernel(const DecodeArgs a) {
   const int HC = a.head_chunks;                       // one kv head
   const int64_t HQ = (int64_t)a.num_heads * C::D;     // query row width
   const int64_t HO = (int64_t)a.num_heads * C::DV;    // output row width
-  // shared mode: an item is (entry, group of WAVES head chunks)
-  const int HG = SHARED ? (HC + C::WAVES - 1) / C::WAVES : HC;
+  const int HG = HC;
   const int total = a.listed ? (*a.entry_count) * HG : a.rows * HG;
-  const int nworkers = SHARED ? gridDim.x : gridDim.x * C::WAVES;
-  int32_t* tbl = s_tbl[SHARED ? 0 : wave];
+  const int nworkers = gridDim.x * C::WAVES;
+  int32_t* tbl = s_tbl[wave];
   const int shift = sl.block_shift;
   // the pool as a buffer: 32-bit byte offsets (the host checks it is < 4 GiB)
   const int64_t pool_bytes = (sl.num_blocks << shift) * (int64_t)(2 * C::D);
@@ -166,11 +165,9 @@ void mla_kernel(const DecodeArgs a) {
       (void*)a.key_cache, (short)0, (int)(uint32_t)min(pool_bytes, (int64_t)0xFFFFFFFF),
       0x00020000);
 
-  for (int item = SHARED ? blockIdx.x : blockIdx.x * C::WAVES + wave; item < total;
-       item += nworkers) {
+  for (int item = blockIdx.x * C::WAVES + wave; item < total; item += nworkers) {
     const int e = item / HG;
-    const int hc = SHARED ? (item - e * HG) * C::WAVES + wave : item - e * HG;
-    const bool chunk_ok = hc < HC;   // shared mode: this wave may only help copy
+    const int hc = item - e * HG;
     const int h0 = hc * a.chunk_heads;
 
     int row, split, k_lo, k_hi;
@@ -190,7 +187,7 @@ void mla_kernel(const DecodeArgs a) {
       split = 0;
       bool orphan;
       if (!resolve_row(sl, 1, row, a.window, a.split_tokens, a.max_splits, r, orphan)) {
-        if (orphan && row < sl.tokens && chunk_ok) {   // token owned by no request: zero
+        if (orphan && row < sl.tokens) {   // token owned by no request: zero
           for (int i = lane; i < a.chunk_heads * (C::DV / 8); i += 64)
             store16(a.out + row * HO + (int64_t)h0 * C::DV + 8 * i, u32x4{0, 0, 0, 0});
         }
@@ -202,7 +199,7 @@ void mla_kernel(const DecodeArgs a) {
 
     // Q as the B operand: lane (q, l16) holds head l16, channels 32 ks + 8 q + [0, 8),
     // rotated on its suffix window
-    const bool head_ok = chunk_ok && l16 < a.chunk_heads;
+    const bool head_ok = l16 < a.chunk_heads;
     h8 qf[C::KS];
     {
       const uint16_t* qrow = a.query + (int64_t)r.t * HQ + (int64_t)(h0 + l16) * C::D;
@@ -237,61 +234,35 @@ void mla_kernel(const DecodeArgs a) {
       const int seg_hi = min(k_hi, (first_bi + C::TBL) << shift);
       const int n_bi = ((seg_hi - 1) >> shift) - first_bi + 1;
       bool hole = false;
-      const int stager = SHARED ? threadIdx.x : lane;
-      for (int i = stager; i < n_bi; i += SHARED ? 64 * C::WAVES : 64) {
+      for (int i = lane; i < n_bi; i += 64) {
         const int bi = first_bi + i;
         int v = bi < sl.maxblk ? bt[bi] : -1;
         if (v >= sl.num_blocks) v = -1;
         hole |= v < 0;
         tbl[i] = v;
       }
-      bool any_hole;
-      if constexpr (SHARED) {
-        any_hole = __syncthreads_or(hole);
-      } else {
-        any_hole = __any(hole);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
+      const bool any_hole = __any(hole);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
       const int ntile = (seg_hi - seg_lo + C::KT - 1) / C::KT;
-      // this wave's copy of tile `t` into buffer `buf`
+      // this wave's copy of tile `t` into its LDS tile
       auto copy = [&](int t, char* buf) {
-        if constexpr (SHARED)
-          mla_copy_rows<1>(srd, buf, tbl, first_bi, shift, seg_lo + t * C::KT, seg_hi, lane, wave);
-        else
-          mla_copy_rows<C::KT / 8>(srd, buf, tbl, first_bi, shift, seg_lo + t * C::KT, seg_hi,
-                                   lane, 0);
+        mla_copy_rows<C::KT / 8>(srd, buf, tbl, first_bi, shift, seg_lo + t * C::KT, seg_hi,
+                                 lane, 0);
       };
-      if constexpr (SHARED) {
-        copy(0, s_k[0]);
-        if (ntile > 1) copy(1, s_k[1]);
-      } else {
-        copy(0, s_k[wave]);
-      }
+      copy(0, s_k[wave]);
       for (int it = 0; it < ntile; ++it) {
         const int k0 = seg_lo + it * C::KT;
         const bool more = it + 1 < ntile;
-        char* tile = SHARED ? s_k[it & 1] : s_k[wave];
+        char* tile = s_k[wave];
         const uint16_t* kmain = reinterpret_cast<const uint16_t*>(tile);
         const uint16_t* ktail = reinterpret_cast<const uint16_t*>(tile + C::KT * C::MAIN);
-        if constexpr (SHARED) {
-          // this wave's part of tile it has landed (tile it + 1's may be in
-          // flight: 9 instructions), then everyone's
-          if (more)
-            __builtin_amdgcn_s_waitcnt(0x0F79);   // vmcnt(9)
-          else
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-          __syncthreads();
-        } else {
-          __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this tile's copy has landed
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-        if (chunk_ok) {
-
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this tile's copy has landed
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // ---- S^T = K . Q^T: two 16-key blocks over the 576 channels ----
         // operand reads run kAheadK products ahead of their MFMAs (the two
         // 16-key blocks alternate, so consecutive products are independent)
@@ -382,25 +353,16 @@ void mla_kernel(const DecodeArgs a) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        }   // chunk_ok
         // every read of the tile has returned (the products above consumed
         // them): a later tile's copy may overwrite it
-        if constexpr (SHARED) {
-          __syncthreads();
-          if (it + 2 < ntile) copy(it + 2, tile);
-        } else {
-          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          if (more) copy(it + 1, tile);
-        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (more) copy(it + 1, tile);
       }
       seg_lo = seg_hi;
-      if constexpr (SHARED)
-        __syncthreads();   // the table is restaged for the next segment
-      else
-        __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_wave_barrier();
     }
 
     // ---- epilogue: lane (q, l16) holds head l16, channels 16 db + 4 q + [0, 4) ----
@@ -714,7 +676,7 @@ int mla_occupancy() {
   static int cached = 0;
   if (!cached) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mla_kernel<SOFTCAP, false>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mla_kernel<SOFTCAP>, 256, 0) !=
             hipSuccess ||
         n <= 0)
       n = 1;
@@ -741,9 +703,9 @@ hipError_t launch_mla(const DecodeArgs& a, int workgroups, hipStream_t st) {
       launch_kernel(mla_pair_kernel<false>, grid, pair_block, st, a);
   } else {
     if (a.use_softcap)
-      launch_kernel(mla_kernel<true, false>, grid, block, st, a);
+      launch_kernel(mla_kernel<true>, grid, block, st, a);
     else
-      launch_kernel(mla_kernel<false, false>, grid, block, st, a);
+      launch_kernel(mla_kernel<false>, grid, block, st, a);
   }
   return hipGetLastError();
 }
