@@ -39,6 +39,9 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     const int c = rem - kvh * chunks;
     const int64_t src_row = (int64_t)t * a.kv_heads * a.head_size + (int64_t)kvh * a.head_size;
     u32x4 k = load16(a.key + src_row + 8 * c);
+    // V goes out with K, ahead of the slot lookup's dependent loads (a latent
+    // cache, section 12.2, has no V: V is a view of K)
+    const u32x4 v = a.value ? load16(a.value + src_row + 8 * c) : u32x4{0, 0, 0, 0};
     float nr = 0.f;
     if (a.k_norm) {
       nr = rms_inverse(group_sum(sum_squares8(k), chunks), a.head_size, a.norm_eps);
@@ -68,8 +71,6 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
       off = pos & (bs - 1);
     }
     const int64_t dst = slot_base(blk, off, kvh, bs, a.kv_heads, a.head_size) + 8 * c;
-    // a latent cache (section 12.2) has no V: V is a view of K
-    const u32x4 v = a.value ? load16(a.value + src_row + 8 * c) : u32x4{0, 0, 0, 0};
     if (chunk_rotated(c, a.rotary_offset, a.rotary_dim)) {
       const int off = a.rotary_offset;
       float r[8];
