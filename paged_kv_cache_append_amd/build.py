@@ -19,8 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.hip", "append.hip", "decode.hip", "prefill.hip", "prefill16.hip", "mla.hip",
-           "measure.hip"]
+SOURCES = ["pa_api.hip", "append.hip", "decode.hip", "prefill.hip", "prefill16.hip", "prefill32.hip",
+           "mla.hip", "measure.hip"]
 ARCH = "gfx950"
 
 

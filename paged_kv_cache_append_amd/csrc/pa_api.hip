@@ -309,8 +309,8 @@ pa_status check_routing(const pa_routing* r) {
   if (r->prefill_pieces < 0 || r->prefill_pieces > pa::kPrefillChunks)
     return fail(PA_ERR_INVALID_ARGUMENT, "prefill_pieces: expected 0..%d, got %d",
                 pa::kPrefillChunks, r->prefill_pieces);
-  if (r->prefill_kernel < 0 || r->prefill_kernel > 2)
-    return fail(PA_ERR_INVALID_ARGUMENT, "prefill_kernel: expected 0, 1 or 2, got %d",
+  if (r->prefill_kernel < 0 || r->prefill_kernel > 3)
+    return fail(PA_ERR_INVALID_ARGUMENT, "prefill_kernel: expected 0..3, got %d",
                 r->prefill_kernel);
   if (r->split_tokens < 0 || r->split_tokens % 64 != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "split_tokens: expected 0 or a multiple of 64, got %d",
@@ -327,6 +327,16 @@ bool pool_fits_32bit(const pa_attn_params* p, const pa_paged_kv* kv) {
 // with 32-bit byte offsets.
 bool rows16_prefill_fits(const pa_attn_params* p, const pa_paged_kv* kv) {
   return p->head_size == 256 && pool_fits_32bit(p, kv);
+}
+// The 8-wave kernel of 32 rows per wave also needs fp16 caches.
+bool rows32_prefill_fits(const pa_attn_params* p, const pa_paged_kv* kv) {
+  return rows16_prefill_fits(p, kv) && p->cache_dtype == PA_CACHE_FP16;
+}
+// Prefill kernel of a forward: 1 = 4-wave, 2 = 8-wave of 16 rows per wave,
+// 3 = 8-wave of 32 rows per wave.
+int prefill_kernel_of(const pa_attn_params* p, const pa_paged_kv* kv, const pa_routing& rt) {
+  if (rt.prefill_kernel > 0) return rt.prefill_kernel;
+  return rows16_prefill_fits(p, kv) ? 2 : 1;
 }
 
 pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv,
@@ -353,6 +363,9 @@ pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv,
   if (rt.prefill_kernel == 2 && !rows16_prefill_fits(p, kv))
     return fail(PA_ERR_UNSUPPORTED,
                 "prefill_kernel 2: expected head_size 256 and caches smaller than 4 GiB");
+  if (rt.prefill_kernel == 3 && !rows32_prefill_fits(p, kv))
+    return fail(PA_ERR_UNSUPPORTED,
+                "prefill_kernel 3: expected head_size 256, fp16 caches smaller than 4 GiB");
   return PA_OK;
 }
 
@@ -372,6 +385,8 @@ struct Plan {
   int max_splits = 1;
   int prefill_tiles = 0;     // tile slots (grid.x = tiles * prefill_chunks + 1)
   int prefill_chunks = 1;    // key-range pieces per prefill tile
+  int prefill_kernel = 1;    // prefill_kernel_of
+  int prefill_rows = pa::kPrefillRows;   // rows of a tile slot
   size_t off_ml = 0, off_entries = 0, off_count = 0, off_rows = 0;
   size_t off_pf_o = 0, off_pf_ml = 0;
   size_t off_qn = 0;         // QK-Norm: normalized queries, fp16 [T, H*D]
@@ -435,8 +450,11 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, const pa_routing&
   }
   if (pl.prefill) {
     const int64_t mql = mq > 0 ? std::min<int64_t>(mq, T) : T;
-    const int64_t per_req = (mql * pl.g + pa::kPrefillRows - 1) / pa::kPrefillRows;
-    const int64_t by_tokens = ((int64_t)T * pl.g + pa::kPrefillRows - 1) / pa::kPrefillRows + B;
+    pl.prefill_kernel = prefill_kernel_of(p, kv, rt);
+    pl.prefill_rows = pl.prefill_kernel == 3 ? 2 * pa::kPrefillRows : pa::kPrefillRows;
+    const int64_t tr = pl.prefill_rows;
+    const int64_t per_req = (mql * pl.g + tr - 1) / tr;
+    const int64_t by_tokens = ((int64_t)T * pl.g + tr - 1) / tr + B;
     pl.prefill_tiles = (int)std::min<int64_t>(std::min<int64_t>((int64_t)B * per_req, by_tokens),
                                               (int64_t)1 << 28);
     // Few (tile, kv head) items leave most of the chip idle while each tile
@@ -444,8 +462,7 @@ Plan make_plan(const pa_attn_params* p, const pa_paged_kv* kv, const pa_routing&
     // pieces of about kPrefillPieceTiles key tiles (at most kPrefillChunks),
     // computed by separate workgroups and combined by a merge kernel.  Static
     // shapes decide whether pieces are allowed; the device cuts by length.
-    const int64_t est_items =
-        ((int64_t)T * pl.g + pa::kPrefillRows - 1) / pa::kPrefillRows * p->kv_num_heads;
+    const int64_t est_items = ((int64_t)T * pl.g + tr - 1) / tr * p->kv_num_heads;
     const bool long_keys = cap >= 4 * pa::kPrefillPieceTiles * 64;
     pl.prefill_chunks = rt.prefill_pieces > 0 ? rt.prefill_pieces
                         : est_items < pa::kPrefillSplitItems && long_keys ? pa::kPrefillChunks
@@ -850,8 +867,10 @@ static pa_status forward_impl(const pa_attn_params* params, const pa_paged_kv* k
     f.cap_in2 = 2.0f * log2e * d.cap_in;
     f.cap_out = d.cap_out;
     f.use_softcap = d.use_softcap;
-    f.rows16 = rt.prefill_kernel == 2 ||
-               (rt.prefill_kernel == 0 && rows16_prefill_fits(params, kv));
+    f.rows16 = pl.prefill_kernel == 2;
+    f.rows32 = pl.prefill_kernel == 3;
+    f.tile_rows = pl.prefill_rows;
+    f.key_tile = pl.prefill_kernel == 3 ? 32 : 64;
     f.pool32 = pool_fits_32bit(params, kv) ? 1 : 0;
     f.head_sink = d.head_sink;
     f.use_sink = d.use_sink;

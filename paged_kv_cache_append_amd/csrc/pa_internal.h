@@ -183,6 +183,10 @@ struct PrefillArgs {
   float cap_out;                // softcap * log2(e)
   int32_t use_softcap;
   int32_t rows16;               // head_size 256: the 8-wave kernel (16 rows per wave)
+  int32_t rows32;               // head_size 256, fp16 pools: the 8-wave kernel of 32 rows per
+                                // wave (tiles of 256 rows and 32 keys)
+  int32_t tile_rows;            // rows of a tile slot (kPrefillRows, or 2x for rows32)
+  int32_t key_tile;             // keys per key tile (64, or 32 for rows32)
   int32_t pool32;               // each cache is smaller than 4 GiB (32-bit byte offsets)
   const uint16_t* head_sink;    // as in DecodeArgs
   int32_t use_sink;
@@ -225,6 +229,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStr
 hipError_t launch_prefill_merge(const PrefillArgs& a, int head_size, hipStream_t st);
 // 8-wave prefill kernel of 16 rows per wave (head_size 256); grid as launch_prefill
 hipError_t launch_prefill16(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st);
+// 8-wave prefill kernel of 32 rows per wave (head_size 256, fp16 pools below 4 GiB)
+hipError_t launch_prefill32(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st);
 // latent attention (MLA): kv_num_heads 1, head_size 576, V = the leading 512
 // channels of K; every row in token mode, items as for the decode kernel
 hipError_t launch_mla(const DecodeArgs& a, int workgroups, hipStream_t st);

@@ -681,34 +681,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   }
 }
 
-// Combine the pieces of every prefill tile cut into several: one workgroup
-// per (tile slot, kv head); thread pairs own a row, each half of its channels.
-// o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c, with M = max_c m_c
-// (GroupQueryAttention CPU Implementation Notes, "Flash Decoding" merge).
+// One row of a tile cut into pieces: combine its pieces' partials.
 template <int D>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a) {
-  __shared__ int sh_b, sh_tile;
+__device__ __forceinline__ void merge_row(const PrefillArgs& a, const TileKeys& tk, int t_begin,
+                                          int q_len, int R, int tid) {
   const SeqLayout& sl = a.s;
-  const int tid = threadIdx.x, lane = tid & 63;
   const int g = a.group;
-  if (tid < 64) {
-    int fb, ft;
-    find_tile(sl, g, blockIdx.x, lane, fb, ft);
-    if (lane == 0) {
-      sh_b = fb;
-      sh_tile = ft;
-    }
-  }
-  __syncthreads();
-  const int b = __builtin_amdgcn_readfirstlane(sh_b);
-  if (b < 0) return;
-  const int tile = __builtin_amdgcn_readfirstlane(sh_tile);
-  const int t_begin = sl.cum[b];
-  const int q_len = sl.cum[b + 1] - t_begin;
-  const TileKeys tk = tile_keys(tile, q_len, sl.past[b], g, a.window, sl.maxblk << sl.block_shift,
-                                a.chunks, a.piece_tiles);
-  if (tk.pieces <= 1) return;
-  const int R = tile * kPrefillRows + (tid >> 1);
   const int j = R / g;
   if (j >= q_len || t_begin + j >= sl.tokens) return;
   const int t = t_begin + j;
@@ -738,6 +716,38 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a)
     v.y = (uint32_t)f2h(o[2] * inv) | ((uint32_t)f2h(o[3] * inv) << 16);
     *reinterpret_cast<uint2*>(orow + d0) = v;
   }
+}
+
+// Combine the pieces of every prefill tile cut into several: one workgroup
+// per (tile slot, kv head); thread pairs own a row, each half of its channels.
+// o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c, with M = max_c m_c
+// (GroupQueryAttention CPU Implementation Notes, "Flash Decoding" merge).
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a) {
+  __shared__ int sh_b, sh_tile;
+  const SeqLayout& sl = a.s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int g = a.group;
+  if (tid < 64) {
+    int fb, ft;
+    find_tile(sl, g, blockIdx.x, lane, fb, ft, a.tile_rows);
+    if (lane == 0) {
+      sh_b = fb;
+      sh_tile = ft;
+    }
+  }
+  __syncthreads();
+  const int b = __builtin_amdgcn_readfirstlane(sh_b);
+  if (b < 0) return;
+  const int tile = __builtin_amdgcn_readfirstlane(sh_tile);
+  const int t_begin = sl.cum[b];
+  const int q_len = sl.cum[b + 1] - t_begin;
+  const TileKeys tk = tile_keys(tile, q_len, sl.past[b], g, a.window, sl.maxblk << sl.block_shift,
+                                a.chunks, a.piece_tiles, a.tile_rows, a.key_tile);
+  if (tk.pieces <= 1) return;
+  // a tile slot of tile_rows rows: thread pairs take rows tid / 2, + 128, ...
+  for (int r0 = 0; r0 < a.tile_rows; r0 += 128)
+    merge_row<D>(a, tk, t_begin, q_len, tile * a.tile_rows + r0 + (tid >> 1), tid);
 }
 
 template <int D, bool BUF, int CT>
@@ -784,6 +794,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_size, dim3 grid, hipStr
     case 64: launch_variant<64>(a, grid, st); break;
     case 128: launch_variant<128>(a, grid, st); break;
     case 256:
+      if (a.rows32) return launch_prefill32(a, head_size, grid, st);
       if (a.rows16) return launch_prefill16(a, head_size, grid, st);
       launch_variant<256>(a, grid, st);
       break;

@@ -72,11 +72,11 @@ __device__ __forceinline__ void pipeline_order() {
 }
 
 // Tile slot -> (request b, tile) over requests with q_len >= 2, tiles of
-// kPrefillRows rows (token x head-in-group) each; later (longer) tiles of a
-// request come first.  b = -1 past the last tile.  Called by a whole wave;
-// the results are the same in every lane.
+// `rows` rows (token x head-in-group) each; later (longer) tiles of a request
+// come first.  b = -1 past the last tile.  Called by a whole wave; the results
+// are the same in every lane.
 __device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, int lane, int& fb,
-                                          int& ft) {
+                                          int& ft, int rows = kPrefillRows) {
   int base = 0;
   fb = -1;
   ft = 0;
@@ -85,7 +85,7 @@ __device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, 
     int nt = 0;
     if (bb < sl.batch) {
       const int ql = sl.cum[bb + 1] - sl.cum[bb];
-      if (ql >= 2) nt = (ql * g + kPrefillRows - 1) / kPrefillRows;
+      if (ql >= 2) nt = (ql * g + rows - 1) / rows;
     }
     int incl = nt;
 #pragma unroll
@@ -107,25 +107,28 @@ __device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, 
   }
 }
 
-// Key range [lo, hi) that tile `tile` of a request (q_len, past) needs, and
-// how it is cut into pieces of whole 64-key tiles for `chunks` workgroups.
+// Key range [lo, hi) that tile `tile` (of `rows` rows) of a request (q_len,
+// past) needs, and how it is cut into pieces of whole key tiles of `kt` keys
+// for `chunks` workgroups.
 struct TileKeys {
   int lo, hi;              // admitted keys of any row of the tile
   int all_begin, all_tiles;
   int per_piece, pieces;
 };
 __device__ __forceinline__ TileKeys tile_keys(int tile, int q_len, int past, int g, int window,
-                                              int cap, int chunks, int piece_tiles) {
+                                              int cap, int chunks, int piece_tiles,
+                                              int rows = kPrefillRows, int kt = 64) {
   TileKeys k;
-  const int j_first = (tile * kPrefillRows) / g;
-  const int j_last = min(q_len - 1, (tile * kPrefillRows + kPrefillRows - 1) / g);
+  const int j_first = (tile * rows) / g;
+  const int j_last = min(q_len - 1, (tile * rows + rows - 1) / g);
   k.hi = min(past + j_last + 1, cap);
   k.lo = window > 0 ? max(0, past + j_first + 1 - window) : 0;
-  k.all_begin = k.lo & ~63;
-  k.all_tiles = k.hi > k.all_begin ? (k.hi - k.all_begin + 63) / 64 : 0;
-  // piece_tiles > 0: pieces of about piece_tiles key tiles (short tiles stay
-  // whole), at most `chunks`; else `chunks` equal pieces
-  const int want = piece_tiles > 0 ? (k.all_tiles + piece_tiles - 1) / piece_tiles : chunks;
+  k.all_begin = k.lo & ~(kt - 1);
+  k.all_tiles = k.hi > k.all_begin ? (k.hi - k.all_begin + kt - 1) / kt : 0;
+  // piece_tiles > 0: pieces of about piece_tiles 64-key tiles (short tiles
+  // stay whole), at most `chunks`; else `chunks` equal pieces
+  const int pt = piece_tiles * 64 / kt;
+  const int want = piece_tiles > 0 ? (k.all_tiles + pt - 1) / pt : chunks;
   const int n = max(1, min(chunks, want));
   k.per_piece = (k.all_tiles + n - 1) / n;
   k.pieces = k.per_piece > 0 ? (k.all_tiles + k.per_piece - 1) / k.per_piece : 1;

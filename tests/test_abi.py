@@ -175,7 +175,7 @@ ROUTING_NEGATIVE = [
     (dict(split_tokens=100), "split_tokens"),
     (dict(prefill_pieces=5), "prefill_pieces"),
     (dict(prefill_pieces=-1), "prefill_pieces"),
-    (dict(prefill_kernel=3), "prefill_kernel"),
+    (dict(prefill_kernel=4), "prefill_kernel"),
     (dict(prefill_kernel=-1), "prefill_kernel"),
 ]
 
@@ -235,6 +235,18 @@ def test_rows16_prefill_kernel_limits():
     # the 8-wave prefill kernel serves head_size 256 with caches below 4 GiB
     rt = routing(prefill_kernel=2)
     assert call_forward(params(), paged(), rt=rt) == 2 and "prefill_kernel 2" in err()
+    big = paged(num_blocks=(1 << 32) // (16 * 2 * 256 * 2))   # exactly 4 GiB per cache
+    assert call_forward(params(head_size=256), big, rt=rt) == 2
+    assert "4 GiB" in err()
+
+
+def test_rows32_prefill_kernel_limits():
+    # the 32-row 8-wave prefill kernel serves head_size 256 with fp16 caches
+    # below 4 GiB
+    rt = routing(prefill_kernel=3)
+    assert call_forward(params(), paged(), rt=rt) == 2 and "prefill_kernel 3" in err()
+    assert call_forward(params(head_size=256, **QUANT), paged(**QUANT_KV), rt=rt) == 2
+    assert "fp16" in err()
     big = paged(num_blocks=(1 << 32) // (16 * 2 * 256 * 2))   # exactly 4 GiB per cache
     assert call_forward(params(head_size=256), big, rt=rt) == 2
     assert "4 GiB" in err()

@@ -150,8 +150,9 @@ def test_batch_order_permutation():
 
 
 WIDE_CASES = [
-    # q_lens, past, H, Hkv, D = 256, bs, extra kwargs: both prefill kernels of
-    # the 256-channel head (4 waves x 32 rows, 8 waves x 16 rows)
+    # q_lens, past, H, Hkv, D = 256, bs, extra kwargs: the prefill kernels of
+    # the 256-channel head (4 waves x 32 rows, 8 waves x 16 rows, 8 waves x 32
+    # rows)
     ([130, 1, 3], [300, 1000, 64], 6, 2, 256, 16, dict(local_window_size=200, softcap=5.0)),
     ([64, 1], [4000, 7000], 16, 8, 256, 16, dict(local_window_size=4096, softcap=50.0)),
     ([257, 2, 40], [0, 129, 3000], 8, 4, 256, 32, {}),
@@ -160,7 +161,7 @@ WIDE_CASES = [
 
 
 @pytest.mark.parametrize("case", range(len(WIDE_CASES)))
-@pytest.mark.parametrize("kernel", [1, 2])
+@pytest.mark.parametrize("kernel", [1, 2, 3])
 def test_wide_head_prefill_kernels(case, kernel):
     q_lens, past, H, Hkv, D, bs, kw = WIDE_CASES[case]
     w = wl.build_case(f"wide{case}", 700 + case, q_lens=q_lens, past=past, num_heads=H,
@@ -168,7 +169,7 @@ def test_wide_head_prefill_kernels(case, kernel):
     check(w, 2, prefill_kernel=kernel)
 
 
-@pytest.mark.parametrize("kernel", [1, 2])
+@pytest.mark.parametrize("kernel", [1, 2, 3])
 def test_wide_head_prefill_kernels_with_pieces(kernel):
     q_lens, past, H, Hkv, D, bs, kw = PIECE_CASES[1]
     w = wl.build_case("pieces1", 601, q_lens=q_lens, past=past, num_heads=H,

@@ -141,8 +141,8 @@ def test_sink_through_decode_splits_and_prefill_pieces():
     run(w, extras(w), 2, prefill_pieces=3)
 
 
-@pytest.mark.parametrize("kernel", [1, 2])
-def test_sink_on_both_wide_head_prefill_kernels(kernel):
+@pytest.mark.parametrize("kernel", [1, 2, 3])
+def test_sink_on_the_wide_head_prefill_kernels(kernel):
     w = wl.build_case("sink_wide", 3302, q_lens=[130, 67, 1], past=[200, 0, 900], num_heads=16,
                       kv_num_heads=8, head_size=256, block_size=16, softcap=50.0,
                       local_window_size=96, do_rotary=1, rotary_dim=64)

@@ -64,7 +64,7 @@ def holes_prefill():
     return wl.with_unmapped_blocks(w, sorted(ent))
 
 
-@pytest.mark.parametrize("kernel", [1, 2])
+@pytest.mark.parametrize("kernel", [1, 2, 3])
 @pytest.mark.parametrize("pieces", [0, 3])
 def test_unmapped_blocks_in_prefill_tiles(kernel, pieces):
     check(holes_prefill(), path=2, prefill_kernel=kernel, prefill_pieces=pieces)
