@@ -336,7 +336,7 @@ bool rows32_prefill_fits(const pa_attn_params* p, const pa_paged_kv* kv) {
 // 3 = 8-wave of 32 rows per wave.
 int prefill_kernel_of(const pa_attn_params* p, const pa_paged_kv* kv, const pa_routing& rt) {
   if (rt.prefill_kernel > 0) return rt.prefill_kernel;
-  return rows16_prefill_fits(p, kv) ? 2 : 1;
+  return rows32_prefill_fits(p, kv) ? 3 : rows16_prefill_fits(p, kv) ? 2 : 1;
 }
 
 pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv,

@@ -383,8 +383,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     const float mx = xor32_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
     return mx == kNegInf ? kNegInf : logit(mx);
   };
-  // Keys outside the row's causal window; accumulator entry r of block kb
-  // holds key kt0 + 32 kb + 8 (r / 4) + 4 hf + r % 4.
+  // Keys outside the row's causal window, or past the table's capacity (hi
+  // is then the capacity); accumulator entry r of block kb holds key
+  // kt0 + 32 kb + 8 (r / 4) + 4 hf + r % 4.
   auto full_tile = [&](int kt0) {
     return kt0 >= lo && kt0 + C::KT <= hi && kt0 + C::KT - 1 <= wpos_min &&
            (a.window <= 0 || kt0 >= wpos_max - a.window + 1);
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tau = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        s[kb][r] = ((tau <= pos) & (tau >= wlo)) ? s[kb][r] : kNegInf;
+        s[kb][r] = ((tau <= pos) & (tau >= wlo) & (tau < hi)) ? s[kb][r] : kNegInf;
       }
   };
   // Keys outside [lo, hi) or in an unmapped block (only when the key range

@@ -406,7 +406,8 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
     return kt0 >= lo && kt0 + C::KT <= hi && kt0 + C::KT - 1 <= wpos_min &&
            (a.window <= 0 || kt0 >= wpos_max - a.window + 1);
   };
-  // accumulator entry i of block kb holds key kt0 + 16 kb + 4 q4 + i
+  // accumulator entry i of block kb holds key kt0 + 16 kb + 4 q4 + i; keys
+  // past the table's capacity (hi is then the capacity) are masked too
   auto pos_mask = [&](f4 (&s)[4], int kt0) {
     const int wlo = a.window > 0 ? pos - a.window + 1 : INT32_MIN;
 #pragma unroll
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(512) void prefill16_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tau = kt0 + 16 * kb + 4 * q4 + i;
-        s[kb][i] = ((tau <= pos) & (tau >= wlo)) ? s[kb][i] : kNegInf;
+        s[kb][i] = ((tau <= pos) & (tau >= wlo) & (tau < hi)) ? s[kb][i] : kNegInf;
       }
   };
   // keys outside [lo, hi) or in an unmapped block (a run of four keys never

@@ -255,7 +255,8 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
     else
       return x * a.score_scale;
   };
-  // accumulator entry r holds key kt0 + 8 (r / 4) + 4 hf + r % 4 of row l32
+  // accumulator entry r holds key kt0 + 8 (r / 4) + 4 hf + r % 4 of row l32;
+  // keys past the table's capacity (hi is then the capacity) are masked too
   auto full_tile = [&](int kt0) {
     return kt0 >= lo && kt0 + C::KT <= hi && kt0 + C::KT - 1 <= wpos_min &&
            (a.window <= 0 || kt0 >= wpos_max - a.window + 1);
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tau = kt0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      s[r] = ((tau <= pos) & (tau >= wlo)) ? s[r] : kNegInf;
+      s[r] = ((tau <= pos) & (tau >= wlo) & (tau < hi)) ? s[r] : kNegInf;
     }
   };
   // keys outside [lo, hi) or in an unmapped block (a run of four keys never

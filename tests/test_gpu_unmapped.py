@@ -99,6 +99,22 @@ def test_positions_past_the_table_capacity(split_tokens):
     assert np.all(out[0] == 0) and np.all(ref[0] == 0)
 
 
+@pytest.mark.parametrize("kernel", [1, 2, 3])
+def test_prefill_positions_past_the_table_capacity(kernel):
+    """Prefill rows whose causal range runs past the table's capacity (32
+    blocks of 16 = 512 keys): the keys past it are unmapped and masked, and
+    the new tokens there are not written.  Request 0 (positions 470..569)
+    straddles the capacity, request 1 (600..629) lies wholly past it: with a
+    window of 64 its rows have no key and are 0."""
+    w = wl.build_case("past_capacity_prefill", 3303, q_lens=[100, 30, 1], past=[470, 600, 40],
+                      num_heads=8, kv_num_heads=4, head_size=256, block_size=16,
+                      local_window_size=64, softcap=30.0)
+    w.block_table = np.ascontiguousarray(w.block_table[:, :32])
+    out, ref = check(w, path=2, prefill_kernel=kernel)
+    t1 = int(w.cum[1])
+    assert np.all(ref[t1:t1 + 30] == 0) and np.all(out[t1:t1 + 30] == 0)
+
+
 def test_unmapped_blocks_int8_pool():
     from pa_harness import gpu_quant_step, oracle_append_quant, oracle_forward_quant, quant_inputs
     w = holes_decode()
