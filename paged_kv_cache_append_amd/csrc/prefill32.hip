@@ -24,10 +24,10 @@
 // product of tile it and the PV product of tile it - 1 (whose probabilities
 // the previous step computed), then the softmax of tile it; K of tile it + 1
 // and V of tile it move into LDS during the step (direct buffer loads, 1 KB
-// per instruction; keys that must read as zero take an offset past the
-// buffer's end).  One barrier per step.  The two waves of a SIMD fill each
-// other's softmax with matrix work.  Scores are in log2 units with a lazily
-// raised running max.
+// per instruction, issued by one wave of each SIMD; keys that must read as
+// zero take an offset past the buffer's end).  One barrier per step.  The two
+// waves of a SIMD fill each other's loads and softmax with matrix work.
+// Scores are in log2 units with a lazily raised running max.
 #include <type_traits>
 
 #include "prefill_common.h"
@@ -45,7 +45,8 @@ struct Rows32Cfg {
   static constexpr int DB = D / 32;           // 32-channel output blocks
   static constexpr int CH = D / 8;            // 16-byte chunks per key row
   static constexpr int SLOTS = KT / 2;        // 1 KB slots (two key rows) per tile
-  static constexpr int DMA = SLOTS / WAVES;   // direct loads per wave per tile (K or V)
+  static constexpr int LOADERS = 4;           // waves that move the tiles (one per SIMD)
+  static constexpr int DMA = SLOTS / LOADERS; // direct loads per loading wave per tile (K or V)
   static constexpr int KSLOT = 1024 + 16;     // K slot stride (bytes)
   static constexpr int VSLOT = 1024 + 64;     // V slot stride: the 4 rows of a transposing
                                               // read fall 64 bytes apart
@@ -202,12 +203,16 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
     return (last >> shift) >= seg_first + C::SEGT;
   };
 
-  // Tile loads: wave w fills slots w and w + 8; lane i of a slot load moves
-  // chunk i % CH of the slot's key row i / CH.  Slot s of a tile holds keys s
-  // and s + 16.  The pool row of that key of tile tt, or ~0 for a zero row
-  // (outside [lo, hi), an unmapped block, or past this workgroup's tiles).
+  // Tile loads: waves 0..3 move every tile, wave w slots w + 4 mi (a wave
+  // that issues direct loads stalls while the load pipe drains them, so the
+  // other wave of each SIMD keeps the matrix core busy meanwhile); lane i of
+  // a slot load moves chunk i % CH of the slot's key row i / CH.  Slot s of a
+  // tile holds keys s and s + 16.  The pool row of that key of tile tt, or ~0
+  // for a zero row (outside [lo, hi), an unmapped block, or past this
+  // workgroup's tiles).
+  const bool loader = wave < C::LOADERS;
   auto row_of = [&](int tt, int mi) -> uint32_t {
-    const int slot = wave + C::WAVES * mi;
+    const int slot = wave + C::LOADERS * mi;
     const int tau = kt_of(tt) + slot + 16 * (lane / C::CH);
     const bool in = (tt < ntiles) & (tau >= lo) & (tau < hi);
     const int v = s_tbl[in ? (tau >> shift) - seg_first : 0] | (in ? 0 : -1);
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
   auto dma = [&](uint32_t row, __amdgpu_buffer_rsrc_t srd, char* buf, int slot_bytes, int mi) {
     const uint32_t off = row != ~0u ? (row * tok_stride32 + 8 * chunk) * 2 : 0xFFFFFFF0u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        srd, (__attribute__((address_space(3))) void*)(buf + (wave + C::WAVES * mi) * slot_bytes),
+        srd, (__attribute__((address_space(3))) void*)(buf + (wave + C::LOADERS * mi) * slot_bytes),
         16, off, 0, 0, 0);
   };
 
@@ -306,12 +311,12 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
       const int tl = min(it + 1, ntiles - 1);
       if (need_segment(tl)) stage_table(max(kt_of(it), lo));
     }
-    const uint32_t krow[2] = {row_of(it + 1, 0), row_of(it + 1, 1)};
-    const uint32_t vrow[2] = {row_of(it, 0), row_of(it, 1)};
+    if (loader) {
 #pragma unroll
-    for (int mi = 0; mi < C::DMA; ++mi) dma(vrow[mi], vsrd, vbuf(B), C::VSLOT, mi);
+      for (int mi = 0; mi < C::DMA; ++mi) dma(row_of(it, mi), vsrd, vbuf(B), C::VSLOT, mi);
 #pragma unroll
-    for (int mi = 0; mi < C::DMA; ++mi) dma(krow[mi], ksrd, kbuf(NB{}), C::KSLOT, mi);
+      for (int mi = 0; mi < C::DMA; ++mi) dma(row_of(it + 1, mi), ksrd, kbuf(NB{}), C::KSLOT, mi);
+    }
 
     // ---- matrix work: QK of tile it interleaved with PV of tile it - 1 ----
     f16v s;
@@ -382,10 +387,9 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
 
   if (ntiles > 0) {
     stage_table(max(kt_begin, lo));
-    {
-      const uint32_t krow[2] = {row_of(0, 0), row_of(0, 1)};
+    if (loader) {
 #pragma unroll
-      for (int mi = 0; mi < C::DMA; ++mi) dma(krow[mi], ksrd, K0, C::KSLOT, mi);
+      for (int mi = 0; mi < C::DMA; ++mi) dma(row_of(0, mi), ksrd, K0, C::KSLOT, mi);
     }
     for (int i = tid; i < C::SLOTS * C::VSLOT / 16; i += 64 * C::WAVES)
       reinterpret_cast<u32x4*>(V1)[i] = u32x4{0, 0, 0, 0};
