@@ -108,8 +108,8 @@ def traffic_from_profiles(kernel_tag: str, src_hash: str):
 KERNEL_SOURCES = {
     "mla": ("mla.hip", "decode_rows.h", "pa_api.hip", "pa_device.h", "pa_internal.h"),
     "decode": ("decode.hip", "decode_rows.h", "pa_api.hip", "pa_device.h", "pa_internal.h"),
-    "prefill": ("prefill.hip", "prefill16.hip", "prefill_common.h", "pa_api.hip", "pa_device.h",
-                "pa_internal.h"),
+    "prefill": ("prefill.hip", "prefill16.hip", "prefill32.hip", "prefill_common.h", "pa_api.hip",
+                "pa_device.h", "pa_internal.h"),
 }
 
 
