@@ -399,9 +399,10 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
       step(it, Buf0{});
       if (it + 1 < ntiles) step(it + 1, Buf1{});
     }
-    // PV of the last tile (its V is in buffer (ntiles - 1) % 2)
-    auto last_pv = [&](auto B) {
-      const char* vt = vbuf(B) + voff;
+    // PV of the last tile (its V is in buffer (ntiles - 1) % 2; no load is
+    // in flight any more, so the buffer may be chosen at run time)
+    {
+      const char* vt = ((ntiles & 1) ? V0 : V1) + voff;
       h8 vf[2];
       vf[0] = vread(vt, 0);
       vf[1] = vread(vt, 1);
@@ -413,11 +414,7 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
         if (i + 2 < C::NPV) vf[i & 1] = vread(vt, i + 2);
       }
       __builtin_amdgcn_sched_barrier(0);
-    };
-    if (ntiles & 1)
-      last_pv(Buf0{});
-    else
-      last_pv(Buf1{});
+    }
   }
 
   const float lt = xor32_sum(lsum);
