@@ -30,8 +30,8 @@ typedef struct {
   int32_t prefill_kernel; /* 0 = auto; 1 = 4-wave prefill kernel (32 query rows per
                              wave); 2 = 8-wave kernel (16 rows per wave), head_size 256
                              with each cache smaller than 4 GiB; 3 = 8-wave kernel of 32
-                             rows per wave (tiles of 256 rows), head_size 256 with fp16
-                             caches smaller than 4 GiB; else PA_ERR_UNSUPPORTED         */
+                             rows per wave (tiles of 256 rows), head_size 256 with
+                             each cache smaller than 4 GiB; else PA_ERR_UNSUPPORTED     */
 } pa_routing;
 
 /* pa_forward_workspace_bytes / pa_forward with a forced routing (non-NULL). */

@@ -328,15 +328,15 @@ bool pool_fits_32bit(const pa_attn_params* p, const pa_paged_kv* kv) {
 bool rows16_prefill_fits(const pa_attn_params* p, const pa_paged_kv* kv) {
   return p->head_size == 256 && pool_fits_32bit(p, kv);
 }
-// The 8-wave kernel of 32 rows per wave also needs fp16 caches.
+// The 8-wave kernel of 32 rows per wave: the same shapes.
 bool rows32_prefill_fits(const pa_attn_params* p, const pa_paged_kv* kv) {
-  return rows16_prefill_fits(p, kv) && p->cache_dtype == PA_CACHE_FP16;
+  return rows16_prefill_fits(p, kv);
 }
-// Prefill kernel of a forward: 1 = 4-wave, 2 = 8-wave of 16 rows per wave,
-// 3 = 8-wave of 32 rows per wave.
+// Prefill kernel of a forward: 1 = 4-wave, 2 = 8-wave of 16 rows per wave
+// (only by the testing hook), 3 = 8-wave of 32 rows per wave.
 int prefill_kernel_of(const pa_attn_params* p, const pa_paged_kv* kv, const pa_routing& rt) {
   if (rt.prefill_kernel > 0) return rt.prefill_kernel;
-  return rows32_prefill_fits(p, kv) ? 3 : rows16_prefill_fits(p, kv) ? 2 : 1;
+  return rows32_prefill_fits(p, kv) ? 3 : 1;
 }
 
 pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv,
@@ -365,7 +365,7 @@ pa_status check_kernel_support(const pa_attn_params* p, const pa_paged_kv* kv,
                 "prefill_kernel 2: expected head_size 256 and caches smaller than 4 GiB");
   if (rt.prefill_kernel == 3 && !rows32_prefill_fits(p, kv))
     return fail(PA_ERR_UNSUPPORTED,
-                "prefill_kernel 3: expected head_size 256, fp16 caches smaller than 4 GiB");
+                "prefill_kernel 3: expected head_size 256 and caches smaller than 4 GiB");
   return PA_OK;
 }
 

@@ -1,5 +1,5 @@
 // Prefill / chunked-prefill attention, 8-wave kernel with 32 query rows per
-// wave for the wide head (D = 256) over fp16 pools below 4 GiB.
+// wave for the wide head (D = 256) over pools below 4 GiB.
 //
 // It computes what the kernels in prefill.hip and prefill16.hip compute:
 // online-softmax tiled attention (GroupQueryAttention CPU Implementation
@@ -28,6 +28,13 @@
 // zero take an offset past the buffer's end).  One barrier per step.  The two
 // waves of a SIMD fill each other's loads and softmax with matrix work.
 // Scores are in log2 units with a lazily raised running max.
+//
+// Quantized pools (PagedAttention -- CUDA Design Document, section 8.5,
+// phase 3): the loading waves read each slot's int8 / e4m3fn codes into
+// registers and write them into the same LDS slots as fp16 values (every
+// such code is an fp16 value).  A per-tensor K scale joins the score scale,
+// a per-channel one multiplies Q before its fp16 rounding; the V scale
+// multiplies the output accumulator.
 #include <type_traits>
 
 #include "prefill_common.h"
@@ -55,7 +62,8 @@ struct Rows32Cfg {
 };
 static_assert(Rows32Cfg::ROWS == 2 * kPrefillRows, "tiles of two 128-row slots");
 
-template <bool SOFTCAP>
+// CT: element type of the pools (kCacheF16, or int8 / e4m3fn codes).
+template <bool SOFTCAP, int CT>
 __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
   using C = Rows32Cfg;
   constexpr int D = C::D;
@@ -120,6 +128,23 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nrec, 0x00020000);
   const __amdgpu_buffer_rsrc_t vsrd =
       __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nrec, 0x00020000);
+  // quantized pools: byte arrays of codes, one byte per element
+  constexpr bool kCodes = CT != kCacheF16;
+  const char* kcode = reinterpret_cast<const char*>(a.key_cache) + (int64_t)kvh * D;
+  const char* vcode = reinterpret_cast<const char*>(a.value_cache) + (int64_t)kvh * D;
+  // a per-tensor K scale joins the score scale (and the softcap's input
+  // scale); a per-channel one is folded into Q below
+  float score_scale = a.score_scale, cap_in2 = a.cap_in2;
+  bool k_per_channel = false;
+  if constexpr (kCodes) {
+    if (a.k_quant == kQuantChannel) {
+      k_per_channel = true;
+    } else {
+      const float ks = a.k_scale[0];
+      score_scale *= ks;
+      cap_in2 *= ks;
+    }
+  }
 
   // this lane's query row
   const int R = tile * C::ROWS + wave * 32 + l32;
@@ -151,10 +176,18 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
       const uint16_t* qrow = a.query + (int64_t)t * HD + (int64_t)head * D;
       const int c = 2 * ks + hf;
       v = load16(qrow + 8 * c);
-      if (chunk_rotated(c, a.rotary_offset, a.rotary_dim)) {
+      const bool rot = chunk_rotated(c, a.rotary_offset, a.rotary_dim);
+      if (rot || k_per_channel) {
+        const int off = rot ? a.rotary_offset : 0;
         float rr[8];
-        rotate_chunk(qrow + a.rotary_offset, v, c - a.rotary_offset / 8, pos, a.cos, a.sin,
-                     a.rotary_dim, a.rotary_interleaved, a.rotary_rows, rr);
+        rotate_chunk(qrow + off, v, c - off / 8, pos, a.cos, a.sin, rot ? a.rotary_dim : 0,
+                     a.rotary_interleaved, a.rotary_rows, rr);
+        if (k_per_channel) {
+          float ks[8];
+          channel_scales(a.k_scale, kQuantChannel, kvh, D, 8 * c, ks);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rr[e] *= ks[e];
+        }
         v = pack8(rr);
       }
     }
@@ -225,6 +258,18 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
         srd, (__attribute__((address_space(3))) void*)(buf + (wave + C::LOADERS * mi) * slot_bytes),
         16, off, 0, 0, 0);
   };
+  // quantized pools: the lane's eight codes of a key row (a zero row reads
+  // the zero block: code 0 is +0 in both code types), and their fp16 values
+  // written into the lane's 16 bytes of the slot a direct load would fill
+  auto load_code = [&](uint32_t row, const char* base) -> u32x2 {
+    const int64_t off = row != ~0u ? (int64_t)row * tok_stride32 + 8 * chunk
+                                   : reinterpret_cast<const char*>(g_zero_row) - base;
+    return *reinterpret_cast<const u32x2*>(base + off);
+  };
+  auto put_code = [&](u32x2 c, char* buf, int slot_bytes, int mi) {
+    *reinterpret_cast<u32x4*>(buf + (wave + C::LOADERS * mi) * slot_bytes + 16 * lane) =
+        codes_to_f16<CT>(c);
+  };
 
   // Per-lane parts of the operand addresses (opaque, so each operand read is
   // one base register plus an immediate).  K (A operand of QK): key l32,
@@ -256,9 +301,9 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
   // with tanh(y) = 1 - 2 / (exp(2y) + 1).
   auto logit = [&](float x) {
     if constexpr (SOFTCAP)
-      return a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * a.cap_in2) + 1.0f));
+      return a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(x * cap_in2) + 1.0f));
     else
-      return x * a.score_scale;
+      return x * score_scale;
   };
   // accumulator entry r holds key kt0 + 8 (r / 4) + 4 hf + r % 4 of row l32;
   // keys past the table's capacity (hi is then the capacity) are masked too
@@ -312,10 +357,24 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
       if (need_segment(tl)) stage_table(max(kt_of(it), lo));
     }
     if (loader) {
+      if constexpr (kCodes) {
+        u32x2 cv[C::DMA], ck[C::DMA];
 #pragma unroll
-      for (int mi = 0; mi < C::DMA; ++mi) dma(row_of(it, mi), vsrd, vbuf(B), C::VSLOT, mi);
+        for (int mi = 0; mi < C::DMA; ++mi) {
+          cv[mi] = load_code(row_of(it, mi), vcode);
+          ck[mi] = load_code(row_of(it + 1, mi), kcode);
+        }
 #pragma unroll
-      for (int mi = 0; mi < C::DMA; ++mi) dma(row_of(it + 1, mi), ksrd, kbuf(NB{}), C::KSLOT, mi);
+        for (int mi = 0; mi < C::DMA; ++mi) {
+          put_code(cv[mi], vbuf(B), C::VSLOT, mi);
+          put_code(ck[mi], kbuf(NB{}), C::KSLOT, mi);
+        }
+      } else {
+#pragma unroll
+        for (int mi = 0; mi < C::DMA; ++mi) dma(row_of(it, mi), vsrd, vbuf(B), C::VSLOT, mi);
+#pragma unroll
+        for (int mi = 0; mi < C::DMA; ++mi) dma(row_of(it + 1, mi), ksrd, kbuf(NB{}), C::KSLOT, mi);
+      }
     }
 
     // ---- matrix work: QK of tile it interleaved with PV of tile it - 1 ----
@@ -370,11 +429,11 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
       if constexpr (SOFTCAP) {
         // cap * tanh(y) - mu = (cap - mu) - 2 cap / (2^t + 1), t = 2y log2(e);
         // a masked score (t = -inf) gets -inf through t * 2^-120
-        const float tt = x * a.cap_in2;
+        const float tt = x * cap_in2;
         const float rc = __builtin_amdgcn_rcpf(exp2_fast(tt) + 1.0f);
         e = __builtin_fmaf(tt, 0x1p-120f, __builtin_fmaf(rc, -2.0f * a.cap_out, a.cap_out - mu));
       } else {
-        e = __builtin_fmaf(x, a.score_scale, -mu);
+        e = __builtin_fmaf(x, score_scale, -mu);
       }
       const float p = exp2_fast(e);
       part += p;
@@ -389,7 +448,12 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
     stage_table(max(kt_begin, lo));
     if (loader) {
 #pragma unroll
-      for (int mi = 0; mi < C::DMA; ++mi) dma(row_of(0, mi), ksrd, K0, C::KSLOT, mi);
+      for (int mi = 0; mi < C::DMA; ++mi) {
+        if constexpr (kCodes)
+          put_code(load_code(row_of(0, mi), kcode), K0, C::KSLOT, mi);
+        else
+          dma(row_of(0, mi), ksrd, K0, C::KSLOT, mi);
+      }
     }
     for (int i = tid; i < C::SLOTS * C::VSLOT / 16; i += 64 * C::WAVES)
       reinterpret_cast<u32x4*>(V1)[i] = u32x4{0, 0, 0, 0};
@@ -418,6 +482,20 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
   }
 
   const float lt = xor32_sum(lsum);
+  if constexpr (kCodes) {
+    // the V scale of channels 32 db + 8 q4 + 4 hf + (0..3): output = scale * sum p code
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * hf;
+        const f4 vs = a.v_quant == kQuantChannel
+                          ? *reinterpret_cast<const f4*>(a.v_scale + (int64_t)kvh * D + d0)
+                          : f4{a.v_scale[0], a.v_scale[0], a.v_scale[0], a.v_scale[0]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[db][4 * q4 + e] *= vs[e];
+      }
+  }
   if (pieces > 1) {
     // ---- one piece of several: store (m, l, unnormalised O) ----
     const int64_t pr = ((int64_t)t * a.num_heads + head) * a.chunks;
@@ -459,13 +537,23 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
 
 }  // namespace
 
-hipError_t launch_prefill32(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st) {
-  if (head_size != Rows32Cfg::D || a.cache_dtype != kCacheF16 || !a.pool32)
-    return hipErrorInvalidValue;
+namespace {
+template <int CT>
+void launch_prefill32_cache(const PrefillArgs& a, dim3 grid, hipStream_t st) {
   if (a.use_softcap)
-    launch_kernel(prefill32_kernel<true>, grid, dim3(512), st, a);
+    launch_kernel(prefill32_kernel<true, CT>, grid, dim3(512), st, a);
   else
-    launch_kernel(prefill32_kernel<false>, grid, dim3(512), st, a);
+    launch_kernel(prefill32_kernel<false, CT>, grid, dim3(512), st, a);
+}
+}  // namespace
+
+hipError_t launch_prefill32(const PrefillArgs& a, int head_size, dim3 grid, hipStream_t st) {
+  if (head_size != Rows32Cfg::D || !a.pool32) return hipErrorInvalidValue;
+  switch (a.cache_dtype) {
+    case kCacheI8: launch_prefill32_cache<kCacheI8>(a, grid, st); break;
+    case kCacheF8: launch_prefill32_cache<kCacheF8>(a, grid, st); break;
+    default: launch_prefill32_cache<kCacheF16>(a, grid, st); break;
+  }
   return hipGetLastError();
 }
 

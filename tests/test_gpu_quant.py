@@ -83,12 +83,12 @@ def test_quantized_multi_token_routes(case, path):
     check_quant(wl.scaled_down(name), cd, kq, vq, path=path)
 
 
-@pytest.mark.parametrize("kernel", [1, 2])
+@pytest.mark.parametrize("kernel", [1, 2, 3])
 @pytest.mark.parametrize("pieces", [0, 3])
 def test_quantized_prefill_kernels_pieces_and_holes(kernel, pieces):
-    """Both prefill kernels over codes (the 4-wave and the 8-wave one at head
-    size 256), whole and with the key range cut into pieces, with unmapped
-    blocks inside the window (their blocks hold the NaN code)."""
+    """The prefill kernels over codes (the 4-wave one and both 8-wave ones at
+    head size 256), whole and with the key range cut into pieces, with
+    unmapped blocks inside the window (their blocks hold the NaN code)."""
     w = wl.scaled_down("gemma2_prefill_window")
     ent = set(wl.random_unmapped_entries(w, 21, 0.2)) | {(0, 7), (0, 9)}
     w = wl.with_unmapped_blocks(w, sorted(ent))
