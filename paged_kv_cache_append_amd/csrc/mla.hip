@@ -15,15 +15,18 @@
 // rotating latent channels would rotate V as well.
 //
 // Per tile of 32 keys a wave
-//   - copies the rows (36 KB) straight into its own LDS tile with buffer
-//     loads to LDS, no registers on the way (the Q fragments and the
-//     512-channel accumulator already take 200 registers): one instruction
-//     per row for channels 0..511 (1 KB; rows 1056 B apart, 32 mod 64), and
-//     one per 8 rows for the rotary channels 512..575 (a 128-byte-per-row
-//     tail region whose 16-byte slots are XOR-swizzled by row).  Keys that
-//     are masked or past the split read offsets beyond the buffer's end,
-//     which load zeros.  The next tile's copy goes out once the tile's last
-//     LDS read has returned; the four waves of a CU overlap each other's;
+//   - writes the rows (36 KB), which it loaded into registers while the
+//     previous tile was computed, into its own LDS tile, and issues the loads
+//     of the next tile (one wave per SIMD, so the Q fragments, the
+//     512-channel accumulator and the 144 registers of a staged tile fit):
+//     one 1 KB load per row for channels 0..511 (rows 1056 B apart in LDS,
+//     32 mod 64), and one per 8 rows for the rotary channels 512..575 (a
+//     128-byte-per-row tail region whose 16-byte slots are XOR-swizzled by
+//     row).  Keys that are masked or past the split read offsets beyond the
+//     buffer's end, which load zeros.  (Direct loads into LDS, with the next
+//     copy issued once the tile's last read returned, measured 3.5 % slower
+//     on a 16-head batch: a wave then had no load in flight while it
+//     computed.);
 //   - computes S^T = K . Q^T on the matrix cores (18 k-steps of
 //     v_mfma_f32_16x16x32_f16 per 16-key block, Q fragments in registers);
 //   - runs the online softmax in registers (log2 units);
@@ -247,19 +250,44 @@ void mla_kernel(const DecodeArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
       const int ntile = (seg_hi - seg_lo + C::KT - 1) / C::KT;
-      // this wave's copy of tile `t` into its LDS tile
-      auto copy = [&](int t, char* buf) {
-        mla_copy_rows<C::KT / 8>(srd, buf, tbl, first_bi, shift, seg_lo + t * C::KT, seg_hi,
-                                 lane, 0);
+      // Tile `t`'s rows into registers (main parts: one 1 KB load per row;
+      // rotary tails: one per 8 rows), then into this wave's LDS tile: the
+      // next tile's loads stay in flight while this one is computed.
+      u32x4 stg[C::KT + C::KT / 8];
+      auto stage_load = [&](int t) {
+        const int k0 = seg_lo + t * C::KT;
+        const uint32_t mine = mla_row_offset(tbl, first_bi, shift, k0 + (lane & (C::KT - 1)), seg_hi);
+#pragma unroll
+        for (int r = 0; r < C::KT; ++r) {
+          const uint32_t base = __builtin_amdgcn_readlane(mine, r);
+          stg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(srd, base + 16 * lane, 0, 0));
+        }
+        const int rr = lane >> 3, cc = (lane & 7) ^ (rr & 7);
+#pragma unroll
+        for (int g = 0; g < C::KT / 8; ++g) {
+          const uint32_t base = (uint32_t)__shfl((int)mine, 8 * g + rr, 64);
+          stg[C::KT + g] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(srd, base + 2 * (C::DV + 8 * cc), 0, 0));
+        }
       };
-      copy(0, s_k[wave]);
+      auto stage_store = [&](char* buf) {
+#pragma unroll
+        for (int r = 0; r < C::KT; ++r)
+          *reinterpret_cast<u32x4*>(buf + r * C::MAIN + 16 * lane) = stg[r];
+#pragma unroll
+        for (int g = 0; g < C::KT / 8; ++g)
+          *reinterpret_cast<u32x4*>(buf + C::KT * C::MAIN + 8 * g * C::TAIL + 16 * lane) =
+              stg[C::KT + g];
+      };
+      stage_load(0);
       for (int it = 0; it < ntile; ++it) {
         const int k0 = seg_lo + it * C::KT;
         const bool more = it + 1 < ntile;
         char* tile = s_k[wave];
         const uint16_t* kmain = reinterpret_cast<const uint16_t*>(tile);
         const uint16_t* ktail = reinterpret_cast<const uint16_t*>(tile + C::KT * C::MAIN);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this tile's copy has landed
+        stage_store(tile);                    // (waits for this tile's loads)
+        if (more) stage_load(it + 1);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -354,12 +382,11 @@ void mla_kernel(const DecodeArgs a) {
           }
         }
         // every read of the tile has returned (the products above consumed
-        // them): a later tile's copy may overwrite it
+        // them): the next tile's stores may overwrite it
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (more) copy(it + 1, tile);
       }
       seg_lo = seg_hi;
       __builtin_amdgcn_wave_barrier();
