@@ -167,36 +167,7 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
   const int wpos_min = past + wj0;
   const int wpos_max = past + wj1;
 
-  // Q fragments (B operand of QK): row l32, channels 16 ks + 8 hf .. +7
-  h8 qf[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (row_ok) {
-      const uint16_t* qrow = a.query + (int64_t)t * HD + (int64_t)head * D;
-      const int c = 2 * ks + hf;
-      v = load16(qrow + 8 * c);
-      const bool rot = chunk_rotated(c, a.rotary_offset, a.rotary_dim);
-      if (rot || k_per_channel) {
-        const int off = rot ? a.rotary_offset : 0;
-        float rr[8];
-        rotate_chunk(qrow + off, v, c - off / 8, pos, a.cos, a.sin, rot ? a.rotary_dim : 0,
-                     a.rotary_interleaved, a.rotary_rows, rr);
-        if (k_per_channel) {
-          float ks[8];
-          channel_scales(a.k_scale, kQuantChannel, kvh, D, 8 * c, ks);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) rr[e] *= ks[e];
-        }
-        v = pack8(rr);
-      }
-    }
-    qf[ks] = as_h8(v);
-  }
-  // the query loads land here, so no later wait on the tile loads has to
-  // count them
-  wait_vmem();
-
+  h8 qf[C::KS];   // Q fragments, loaded in the prologue
   f16v acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
@@ -444,8 +415,44 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
     __syncthreads();   // ... and everyone's; K buffer B and V buffer 1 - B are free
   };
 
+  // Q fragments (B operand of QK): row l32, channels 16 ks + 8 hf .. +7.
+  // Their loads go out with the first K tile's, after the table slice is
+  // staged, so the prologue waits on memory twice; chunks that RoPE rotates
+  // or a per-channel K scale multiplies are transformed once they landed.
+  if (ntiles > 0) stage_table(max(kt_begin, lo));
+  const uint16_t* qrow = a.query + (int64_t)t * HD + (int64_t)head * D;
+  if (row_ok) {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_h8(load16(qrow + 8 * (2 * ks + hf)));
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_h8(u32x4{0, 0, 0, 0});
+  }
+  auto finish_q = [&]() {
+    if (!row_ok || (a.rotary_dim <= 0 && !k_per_channel)) return;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int c = 2 * ks + hf;
+      const bool rot = chunk_rotated(c, a.rotary_offset, a.rotary_dim);
+      if (rot || k_per_channel) {
+        const int off = rot ? a.rotary_offset : 0;
+        u32x4 v;
+        __builtin_memcpy(&v, &qf[ks], 16);
+        float rr[8];
+        rotate_chunk(qrow + off, v, c - off / 8, pos, a.cos, a.sin, rot ? a.rotary_dim : 0,
+                     a.rotary_interleaved, a.rotary_rows, rr);
+        if (k_per_channel) {
+          float ks8[8];
+          channel_scales(a.k_scale, kQuantChannel, kvh, D, 8 * c, ks8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rr[e] *= ks8[e];
+        }
+        qf[ks] = as_h8(pack8(rr));
+      }
+    }
+  };
+
   if (ntiles > 0) {
-    stage_table(max(kt_begin, lo));
     if (loader) {
 #pragma unroll
       for (int mi = 0; mi < C::DMA; ++mi) {
@@ -458,6 +465,7 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
     for (int i = tid; i < C::SLOTS * C::VSLOT / 16; i += 64 * C::WAVES)
       reinterpret_cast<u32x4*>(V1)[i] = u32x4{0, 0, 0, 0};
     wait_vmem();
+    finish_q();
     __syncthreads();
     for (int it = 0; it < ntiles; it += 2) {
       step(it, Buf0{});
@@ -516,21 +524,42 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
   }
 
   // ---- normalise and store: lane (l32, hf) holds channels 32 db + 8 q4 +
-  // 4 hf + (0..3) of its row ----
+  // 4 hf + (0..3) of its row.  The K buffers are free once the loop has
+  // ended; each wave passes its rows through 4 KB of them, 64 channels at a
+  // time (16-byte slots XOR-swizzled by row), so every store writes whole
+  // 128-byte segments of 8 rows.  Lane i stores slot i % 8 of rows
+  // i / 8 + 8 k. ----
   const float den = sink_denominator(lt, m, a.use_sink, a.head_sink, head);
   const float inv = den > 0.f ? 1.0f / den : 0.f;
-  if (row_ok) {
-    uint16_t* orow = a.out + (int64_t)t * HD + (int64_t)head * D;
+  char* stg = (wave < 4 ? K0 : K1) + (wave & 3) * 4096;
+  uint16_t* orow_k[4];
+  bool rok[4];
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
+  for (int k = 0; k < 4; ++k) {
+    const int Rk = tile * C::ROWS + wave * 32 + lane / 8 + 8 * k;
+    const int jk = Rk / g;
+    rok[k] = jk < q_len && t_begin + jk < sl.tokens;
+    orow_k[k] = a.out + (int64_t)(t_begin + jk) * HD + (int64_t)(kvh * g + Rk - jk * g) * D +
+                8 * (lane % 8);
+  }
+#pragma unroll
+  for (int rd = 0; rd < C::DB / 2; ++rd) {
+#pragma unroll
+    for (int dl = 0; dl < 2; ++dl) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = db * 32 + 8 * q4 + 4 * hf;
+        const f16v& o = acc[2 * rd + dl];
         uint2 w;
-        w.x = (uint32_t)f2h(acc[db][4 * q4 + 0] * inv) | ((uint32_t)f2h(acc[db][4 * q4 + 1] * inv) << 16);
-        w.y = (uint32_t)f2h(acc[db][4 * q4 + 2] * inv) | ((uint32_t)f2h(acc[db][4 * q4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + d0) = w;
+        w.x = (uint32_t)f2h(o[4 * q4 + 0] * inv) | ((uint32_t)f2h(o[4 * q4 + 1] * inv) << 16);
+        w.y = (uint32_t)f2h(o[4 * q4 + 2] * inv) | ((uint32_t)f2h(o[4 * q4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(stg + l32 * 128 + (((4 * dl + q4) ^ (l32 & 7)) * 16) + 8 * hf) = w;
       }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int rr = lane / 8 + 8 * k;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rr * 128 + (((lane % 8) ^ (rr & 7)) * 16));
+      if (rok[k]) store16(orow_k[k] + 64 * rd, v);
     }
   }
 }
