@@ -72,39 +72,100 @@ __device__ __forceinline__ void pipeline_order() {
 }
 
 // Tile slot -> (request b, tile) over requests with q_len >= 2, tiles of
-// `rows` rows (token x head-in-group) each; later (longer) tiles of a request
-// come first.  b = -1 past the last tile.  Called by a whole wave; the results
-// are the same in every lane.
+// `rows` rows (token x head-in-group) each.  b = -1 past the last tile.
+// Called by a whole wave; the results are the same in every lane.
+//
+// Order (the hardware starts the workgroups of an XCD in slot order, each on
+// the next CU that frees): request b is in group S_b / kGroupTiles, S_b being
+// the number of tiles of the requests before it, so a group spans at least
+// the CUs of one XCD.  A group's slots hold its tiles by rank -- rank 0 is
+// every request's last (longest) tile, then rank 1, ..., requests in order
+// within a rank -- so long and short tiles pair up on the CUs, and the
+// requests of a group walk their keys together.
+constexpr int kGroupTiles = 32;   // CUs per XCD
+__device__ __forceinline__ int tiles_of(const SeqLayout& sl, int b, int g, int rows) {
+  const int ql = sl.cum[b + 1] - sl.cum[b];
+  return ql >= 2 ? (ql * g + rows - 1) / rows : 0;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
 __device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, int lane, int& fb,
                                           int& ft, int rows = kPrefillRows) {
-  int base = 0;
+  __shared__ int s_member[2 * kGroupTiles];   // (request, tiles) of the group's requests
   fb = -1;
   ft = 0;
-  for (int b0 = 0; b0 < sl.batch; b0 += 64) {
+  // pass 1: the request whose tiles hold `slot` in request order, and its group
+  int base = 0, group = -1;
+  for (int b0 = 0; b0 < sl.batch && group < 0; b0 += 64) {
     const int bb = b0 + lane;
-    int nt = 0;
-    if (bb < sl.batch) {
-      const int ql = sl.cum[bb + 1] - sl.cum[bb];
-      if (ql >= 2) nt = (ql * g + rows - 1) / rows;
-    }
+    const int nt = bb < sl.batch ? tiles_of(sl, bb, g, rows) : 0;
     int incl = nt;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(incl, off, 64);
       if (lane >= off) incl += y;
     }
-    const int total = __shfl(incl, 63, 64);
-    if (slot < base + total) {
-      const bool mine = nt > 0 && slot >= base + incl - nt && slot < base + incl;
-      const unsigned long long bal = __ballot(mine);
-      const int src = __builtin_ctzll(bal);
-      fb = b0 + src;
-      const int fn = __shfl(nt, src, 64);
-      ft = fn - 1 - (slot - (base + __shfl(incl - nt, src, 64)));
-      return;
-    }
-    base += total;
+    const bool mine = nt > 0 && slot >= base + incl - nt && slot < base + incl;
+    const unsigned long long bal = __ballot(mine);
+    if (bal) group = (base + __shfl(incl - nt, __builtin_ctzll(bal), 64)) / kGroupTiles;
+    base += __shfl(incl, 63, 64);
   }
+  if (group < 0) return;
+  // pass 2: the group's requests (at most kGroupTiles: each starts at a
+  // distinct slot of the group's range), in order, into s_member
+  int members = 0, first = -1;
+  base = 0;
+  for (int b0 = 0; b0 < sl.batch; b0 += 64) {
+    const int bb = b0 + lane;
+    const int nt = bb < sl.batch ? tiles_of(sl, bb, g, rows) : 0;
+    int incl = nt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const int start = base + incl - nt;
+    const bool in = nt > 0 && start / kGroupTiles == group;
+    const unsigned long long bal = __ballot(in);
+    if (bal) {
+      if (first < 0) first = __shfl(start, __builtin_ctzll(bal), 64);
+      if (in) {
+        const int m = members + __builtin_popcountll(bal & ((1ull << lane) - 1));
+        s_member[2 * m] = bb;
+        s_member[2 * m + 1] = nt;
+      }
+      members += __builtin_popcountll(bal);
+    }
+    base += __shfl(incl, 63, 64);
+    if (base / kGroupTiles > group) break;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes above are visible to the wave
+  __builtin_amdgcn_wave_barrier();
+  const int mb = lane < members ? s_member[2 * lane] : 0;
+  const int mn = lane < members ? s_member[2 * lane + 1] : 0;
+  // rank-major position: P(r) = sum over members of min(n, r) slots precede rank r
+  const int k = slot - first;
+  int r_lo = 0, r_hi = 0;
+  {
+    int mx = mn;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+    r_hi = mx;   // P(r_hi) = group size > k
+  }
+  while (r_hi - r_lo > 1) {   // invariant: P(r_lo) <= k < P(r_hi)
+    const int mid = (r_lo + r_hi) >> 1;
+    if (wave_sum(min(mn, mid)) <= k) r_lo = mid; else r_hi = mid;
+  }
+  const int idx = k - wave_sum(min(mn, r_lo));
+  // the idx-th member (in order) that has a tile of rank r_lo
+  unsigned long long bal = __ballot(lane < members && mn > r_lo);
+  for (int i = 0; i < idx; ++i) bal &= bal - 1;
+  const int src = __builtin_ctzll(bal);
+  fb = __shfl(mb, src, 64);
+  ft = __shfl(mn, src, 64) - 1 - r_lo;
 }
 
 // Key range [lo, hi) that tile `tile` (of `rows` rows) of a request (q_len,

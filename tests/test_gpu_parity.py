@@ -177,6 +177,26 @@ def test_wide_head_prefill_kernels_with_pieces(kernel):
     check(w, 2, prefill_kernel=kernel, prefill_pieces=3)
 
 
+def many_requests_case(D, seed):
+    # 40 requests: decode rows between prefill chunks of 2..200 tokens, so the
+    # prefill tile order groups several requests with unequal tile counts
+    rng = np.random.default_rng(seed)
+    q_lens = [int(x) if rng.random() < 0.7 else 1 for x in rng.integers(2, 201, size=40)]
+    past = [int(x) for x in rng.integers(0, 501, size=40)]
+    return wl.build_case(f"many{D}", seed, q_lens=q_lens, past=past, num_heads=8,
+                         kv_num_heads=2, head_size=D, block_size=16,
+                         **(dict(local_window_size=300, softcap=30.0) if D == 256 else {}))
+
+
+@pytest.mark.parametrize("kernel", [1, 2, 3])
+def test_prefill_tile_order_over_many_requests(kernel):
+    check(many_requests_case(256, 960), 2, prefill_kernel=kernel)
+
+
+def test_prefill_tile_order_over_many_requests_d128():
+    check(many_requests_case(128, 961), 2)
+
+
 SLOT_CASES = [
     # q_lens, past, H, Hkv, D, bs, extra kwargs, fraction of tokens with -1
     ([1, 1, 40, 3], [50, 900, 0, 64], 8, 2, 64, 16, {}, 0.25),
