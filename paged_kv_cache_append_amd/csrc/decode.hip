@@ -301,30 +301,38 @@ void decode_kernel(const DecodeArgs a) {
     const bool head_ok = l16 < a.chunk_heads;
     h8 qf[C::KS];
     {
+      // all chunk loads first (one memory round trip), then the chunks that
+      // RoPE rotates or a per-channel K scale multiplies
       const uint16_t* qrow = a.query + (int64_t)r.t * HD + (int64_t)(h0 + l16) * D;
+      if (head_ok) {
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        u32x4 v = u32x4{0, 0, 0, 0};
-        const int c = 4 * ks + q;
-        if (head_ok) {
-          v = load16(qrow + 8 * c);
+        for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_h8(load16(qrow + 8 * (4 * ks + q)));
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_h8(u32x4{0, 0, 0, 0});
+      }
+      if (head_ok && (a.rotary_dim > 0 || k_per_channel)) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const int c = 4 * ks + q;
           const bool rot = chunk_rotated(c, a.rotary_offset, a.rotary_dim);
           if (rot || k_per_channel) {
             const int off = rot ? a.rotary_offset : 0;
+            u32x4 v;
+            __builtin_memcpy(&v, &qf[ks], 16);
             float rr[8];
             rotate_chunk(qrow + off, v, c - off / 8, r.pos, a.cos, a.sin, rot ? a.rotary_dim : 0,
                          a.rotary_interleaved, a.rotary_rows, rr);
             if (k_per_channel) {
-              float ks[8];
-              channel_scales(a.k_scale, kQuantChannel, kvh, D, 8 * c, ks);
+              float ks8[8];
+              channel_scales(a.k_scale, kQuantChannel, kvh, D, 8 * c, ks8);
 #pragma unroll
-              for (int e = 0; e < 8; ++e) rr[e] *= ks[e];
+              for (int e = 0; e < 8; ++e) rr[e] *= ks8[e];
             }
-            v = pack8(rr);
+            qf[ks] = as_h8(pack8(rr));
           }
+          __builtin_amdgcn_sched_barrier(0);   // one chunk at a time: keeps the prologue small
         }
-        qf[ks] = as_h8(v);
-        __builtin_amdgcn_sched_barrier(0);   // one chunk at a time: keeps the prologue small
       }
     }
 

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char V0[C::SLOTS * C::VSLOT];
   __shared__ __attribute__((aligned(1024))) char V1[C::SLOTS * C::VSLOT];
   __shared__ int32_t s_tbl[C::SEGT];
-  __shared__ int sh_b, sh_tile;
+  __shared__ int sh_b, sh_tile, sh_tb, sh_ql, sh_past;
 
   const SeqLayout& sl = a.s;
   const int tid = threadIdx.x;
@@ -108,11 +108,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 
   // Map this workgroup to (request, tile) over requests with q_len >= 2.
   if (wave == 0) {
-    int fb, ft;
-    find_tile(sl, g, lb.x / a.chunks, lane, fb, ft);
+    int fb, ft, tb, ql, ps;
+    find_tile(sl, g, lb.x / a.chunks, lane, fb, ft, tb, ql, ps);
     if (lane == 0) {
       sh_b = fb;
       sh_tile = ft;
+      sh_tb = tb;
+      sh_ql = ql;
+      sh_past = ps;
     }
   }
   __syncthreads();
@@ -120,9 +123,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   if (b < 0) return;
   const int tile = __builtin_amdgcn_readfirstlane(sh_tile);
 
-  const int t_begin = sl.cum[b];
-  const int q_len = sl.cum[b + 1] - t_begin;
-  const int past = sl.past[b];
+  const int t_begin = __builtin_amdgcn_readfirstlane(sh_tb);
+  const int q_len = __builtin_amdgcn_readfirstlane(sh_ql);
+  const int past = __builtin_amdgcn_readfirstlane(sh_past);
   const int cap = sl.maxblk << sl.block_shift;
   const int shift = sl.block_shift;
   const int bmask = (1 << shift) - 1;
@@ -178,30 +181,38 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const int wpos_max = past + wj1;
 
   // Q fragments (B operand): row l32, channels 16*ks + 8*hf .. +7
+  // all chunk loads first (one memory round trip), then the chunks that
+  // RoPE rotates or a per-channel K scale multiplies
   h8 qf[C::KS];
+  const uint16_t* qrow = a.query + (int64_t)t * HD + (int64_t)head * D;
+  if (row_ok) {
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (row_ok) {
-      const uint16_t* qrow = a.query + (int64_t)t * HD + (int64_t)head * D;
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_h8(load16(qrow + 8 * (2 * ks + hf)));
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_h8(u32x4{0, 0, 0, 0});
+  }
+  if (row_ok && (a.rotary_dim > 0 || k_per_channel)) {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
       const int c = 2 * ks + hf;
-      v = load16(qrow + 8 * c);
       const bool rot = chunk_rotated(c, a.rotary_offset, a.rotary_dim);
       if (rot || k_per_channel) {
         const int off = rot ? a.rotary_offset : 0;
+        u32x4 v;
+        __builtin_memcpy(&v, &qf[ks], 16);
         float rr[8];
         rotate_chunk(qrow + off, v, c - off / 8, pos, a.cos, a.sin, rot ? a.rotary_dim : 0,
                      a.rotary_interleaved, a.rotary_rows, rr);
         if (k_per_channel) {
-          float ks[8];
-          channel_scales(a.k_scale, kQuantChannel, kvh, D, 8 * c, ks);
+          float ks8[8];
+          channel_scales(a.k_scale, kQuantChannel, kvh, D, 8 * c, ks8);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) rr[e] *= ks[e];
+          for (int e = 0; e < 8; ++e) rr[e] *= ks8[e];
         }
-        v = pack8(rr);
+        qf[ks] = as_h8(pack8(rr));
       }
     }
-    qf[ks] = as_h8(v);
   }
   // Let the query loads land here: otherwise the first MFMA of every tile
   // would wait for them with a full vmcnt(0), i.e. also for the next tile's

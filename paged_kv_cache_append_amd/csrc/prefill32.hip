@@ -72,7 +72,7 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char V0[C::SLOTS * C::VSLOT];
   __shared__ __attribute__((aligned(1024))) char V1[C::SLOTS * C::VSLOT];
   __shared__ int32_t s_tbl[C::SEGT];
-  __shared__ int sh_b, sh_tile;
+  __shared__ int sh_b, sh_tile, sh_tb, sh_ql, sh_past;
 
   const SeqLayout& sl = a.s;
   const int tid = threadIdx.x;
@@ -99,11 +99,14 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
   }
 
   if (wave == 0) {
-    int fb, ft;
-    find_tile(sl, g, lb.x / a.chunks, lane, fb, ft, C::ROWS);
+    int fb, ft, tb, ql, ps;
+    find_tile(sl, g, lb.x / a.chunks, lane, fb, ft, tb, ql, ps, C::ROWS);
     if (lane == 0) {
       sh_b = fb;
       sh_tile = ft;
+      sh_tb = tb;
+      sh_ql = ql;
+      sh_past = ps;
     }
   }
   __syncthreads();
@@ -111,9 +114,9 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
   if (b < 0) return;
   const int tile = __builtin_amdgcn_readfirstlane(sh_tile);
 
-  const int t_begin = sl.cum[b];
-  const int q_len = sl.cum[b + 1] - t_begin;
-  const int past = sl.past[b];
+  const int t_begin = __builtin_amdgcn_readfirstlane(sh_tb);
+  const int q_len = __builtin_amdgcn_readfirstlane(sh_ql);
+  const int past = __builtin_amdgcn_readfirstlane(sh_past);
   const int cap = sl.maxblk << sl.block_shift;
   const int shift = sl.block_shift;
   const int bmask = (1 << shift) - 1;

@@ -83,34 +83,51 @@ __device__ __forceinline__ void pipeline_order() {
 // within a rank -- so long and short tiles pair up on the CUs, and the
 // requests of a group walk their keys together.
 constexpr int kGroupTiles = 32;   // CUs per XCD
-__device__ __forceinline__ int tiles_of(const SeqLayout& sl, int b, int g, int rows) {
-  const int ql = sl.cum[b + 1] - sl.cum[b];
-  return ql >= 2 ? (ql * g + rows - 1) / rows : 0;
-}
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
+// The request's first token, query length and past length come back too
+// (tb, ql, ps), so the caller need not read them again.
 __device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, int lane, int& fb,
-                                          int& ft, int rows = kPrefillRows) {
+                                          int& ft, int& tb, int& ql, int& ps,
+                                          int rows = kPrefillRows) {
   __shared__ int s_member[2 * kGroupTiles];   // (request, tiles) of the group's requests
   fb = -1;
   ft = 0;
-  // pass 1: the request whose tiles hold `slot` in request order, and its group
-  int base = 0, group = -1;
-  for (int b0 = 0; b0 < sl.batch && group < 0; b0 += 64) {
+  tb = ql = ps = 0;
+  // per-lane tiles and inclusive tile prefix of requests b0 + lane (the
+  // first chunk is kept: batches of up to 64 requests are scanned once)
+  auto scan = [&](int b0, int& nt, int& incl, int& cb, int& cq, int& cp) {
     const int bb = b0 + lane;
-    const int nt = bb < sl.batch ? tiles_of(sl, bb, g, rows) : 0;
-    int incl = nt;
+    cb = cq = cp = 0;
+    if (bb < sl.batch) {
+      cb = sl.cum[bb];
+      cq = sl.cum[bb + 1] - cb;
+      cp = sl.past[bb];
+    }
+    nt = cq >= 2 ? (cq * g + rows - 1) / rows : 0;
+    incl = nt;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(incl, off, 64);
       if (lane >= off) incl += y;
     }
+  };
+  int nt0, incl0, cb0, cq0, cp0;
+  scan(0, nt0, incl0, cb0, cq0, cp0);
+  // pass 1: the request whose tiles hold `slot` in request order, and its group
+  int base = 0, group = -1;
+  for (int b0 = 0; b0 < sl.batch && group < 0; b0 += 64) {
+    int nt = nt0, incl = incl0, cb = cb0, cq = cq0, cp = cp0;
+    if (b0 > 0) scan(b0, nt, incl, cb, cq, cp);
     const bool mine = nt > 0 && slot >= base + incl - nt && slot < base + incl;
     const unsigned long long bal = __ballot(mine);
-    if (bal) group = (base + __shfl(incl - nt, __builtin_ctzll(bal), 64)) / kGroupTiles;
+    if (bal) {
+      const int src = __builtin_ctzll(bal);
+      group = (base + __shfl(incl - nt, src, 64)) / kGroupTiles;
+    }
     base += __shfl(incl, 63, 64);
   }
   if (group < 0) return;
@@ -119,14 +136,9 @@ __device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, 
   int members = 0, first = -1;
   base = 0;
   for (int b0 = 0; b0 < sl.batch; b0 += 64) {
+    int nt = nt0, incl = incl0, cb = cb0, cq = cq0, cp = cp0;
+    if (b0 > 0) scan(b0, nt, incl, cb, cq, cp);
     const int bb = b0 + lane;
-    const int nt = bb < sl.batch ? tiles_of(sl, bb, g, rows) : 0;
-    int incl = nt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
     const int start = base + incl - nt;
     const bool in = nt > 0 && start / kGroupTiles == group;
     const unsigned long long bal = __ballot(in);
@@ -166,6 +178,22 @@ __device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, 
   const int src = __builtin_ctzll(bal);
   fb = __shfl(mb, src, 64);
   ft = __shfl(mn, src, 64) - 1 - r_lo;
+  // the chosen request's token range and past: from the first chunk's
+  // registers when it lies there, else read
+  if (fb < 64) {
+    tb = __shfl(cb0, fb, 64);
+    ql = __shfl(cq0, fb, 64);
+    ps = __shfl(cp0, fb, 64);
+  } else {
+    tb = sl.cum[fb];
+    ql = sl.cum[fb + 1] - tb;
+    ps = sl.past[fb];
+  }
+}
+__device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, int lane, int& fb,
+                                          int& ft, int rows = kPrefillRows) {
+  int tb, ql, ps;
+  find_tile(sl, g, slot, lane, fb, ft, tb, ql, ps, rows);
 }
 
 // Key range [lo, hi) that tile `tile` (of `rows` rows) of a request (q_len,
