@@ -81,7 +81,11 @@ __device__ __forceinline__ void pipeline_order() {
 // the CUs of one XCD.  A group's slots hold its tiles by rank -- rank 0 is
 // every request's last (longest) tile, then rank 1, ..., requests in order
 // within a rank -- so long and short tiles pair up on the CUs, and the
-// requests of a group walk their keys together.
+// requests of a group walk their keys together.  When all tiles fit one XCD's
+// CUs at once, no tile waits for another to finish and every request is a
+// group of its own (its tiles longest first): the tiles of one request then
+// start together, and a decode running beside a small prefill keeps more of
+// the chip.
 constexpr int kGroupTiles = 32;   // CUs per XCD
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
@@ -117,20 +121,20 @@ __device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, 
   };
   int nt0, incl0, cb0, cq0, cp0;
   scan(0, nt0, incl0, cb0, cq0, cp0);
-  // pass 1: the request whose tiles hold `slot` in request order, and its group
-  int base = 0, group = -1;
-  for (int b0 = 0; b0 < sl.batch && group < 0; b0 += 64) {
+  // pass 1: the request whose tiles hold `slot` in request order (its start
+  // `mine_start`), and the total number of tiles
+  int base = 0, mine_start = -1;
+  for (int b0 = 0; b0 < sl.batch; b0 += 64) {
     int nt = nt0, incl = incl0, cb = cb0, cq = cq0, cp = cp0;
     if (b0 > 0) scan(b0, nt, incl, cb, cq, cp);
     const bool mine = nt > 0 && slot >= base + incl - nt && slot < base + incl;
     const unsigned long long bal = __ballot(mine);
-    if (bal) {
-      const int src = __builtin_ctzll(bal);
-      group = (base + __shfl(incl - nt, src, 64)) / kGroupTiles;
-    }
+    if (bal) mine_start = base + __shfl(incl - nt, __builtin_ctzll(bal), 64);
     base += __shfl(incl, 63, 64);
   }
-  if (group < 0) return;
+  if (mine_start < 0) return;
+  const int gt = base <= kGroupTiles ? 1 : kGroupTiles;   // tiles per group (at least)
+  const int group = mine_start / gt;
   // pass 2: the group's requests (at most kGroupTiles: each starts at a
   // distinct slot of the group's range), in order, into s_member
   int members = 0, first = -1;
@@ -140,7 +144,7 @@ __device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, 
     if (b0 > 0) scan(b0, nt, incl, cb, cq, cp);
     const int bb = b0 + lane;
     const int start = base + incl - nt;
-    const bool in = nt > 0 && start / kGroupTiles == group;
+    const bool in = nt > 0 && start / gt == group;
     const unsigned long long bal = __ballot(in);
     if (bal) {
       if (first < 0) first = __shfl(start, __builtin_ctzll(bal), 64);
@@ -152,7 +156,7 @@ __device__ __forceinline__ void find_tile(const SeqLayout& sl, int g, int slot, 
       members += __builtin_popcountll(bal);
     }
     base += __shfl(incl, 63, 64);
-    if (base / kGroupTiles > group) break;
+    if (base / gt > group) break;
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes above are visible to the wave
   __builtin_amdgcn_wave_barrier();
