@@ -344,10 +344,31 @@ __global__ __launch_bounds__(512) void prefill32_kernel(const PrefillArgs a) {
           put_code(ck[mi], kbuf(NB{}), C::KSLOT, mi);
         }
       } else {
+        // every slot's table lookup first (a direct load writes LDS, so a
+        // lookup after it would wait for the one before), then the loads
+        // back to back
+        int tv[2 * C::DMA];
 #pragma unroll
-        for (int mi = 0; mi < C::DMA; ++mi) dma(row_of(it, mi), vsrd, vbuf(B), C::VSLOT, mi);
+        for (int q = 0; q < 2 * C::DMA; ++q) {
+          const int tt = it + (q & 1);
+          const int tau = kt_of(tt) + wave + C::LOADERS * (q >> 1) + 16 * (lane / C::CH);
+          const bool in = (tt < ntiles) & (tau >= lo) & (tau < hi);
+          tv[q] = s_tbl[in ? (tau >> shift) - seg_first : 0];
+        }
+        __builtin_amdgcn_sched_barrier(0);   // the lookups go out together
+        uint32_t rv[C::DMA], rk[C::DMA];
 #pragma unroll
-        for (int mi = 0; mi < C::DMA; ++mi) dma(row_of(it + 1, mi), ksrd, kbuf(NB{}), C::KSLOT, mi);
+        for (int q = 0; q < 2 * C::DMA; ++q) {
+          const int tt = it + (q & 1);
+          const int tau = kt_of(tt) + wave + C::LOADERS * (q >> 1) + 16 * (lane / C::CH);
+          const bool in = (tt < ntiles) & (tau >= lo) & (tau < hi);
+          const uint32_t r = !in || tv[q] < 0 ? ~0u : ((uint32_t)tv[q] << shift) | (uint32_t)(tau & bmask);
+          if (q & 1) rk[q >> 1] = r; else rv[q >> 1] = r;
+        }
+#pragma unroll
+        for (int mi = 0; mi < C::DMA; ++mi) dma(rv[mi], vsrd, vbuf(B), C::VSLOT, mi);
+#pragma unroll
+        for (int mi = 0; mi < C::DMA; ++mi) dma(rk[mi], ksrd, kbuf(NB{}), C::KSLOT, mi);
       }
     }
 
